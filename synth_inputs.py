@@ -1,0 +1,127 @@
+"""Seeded synthetic inputs shared by the oracle tests, the GPU parity tests and the bench.
+
+This module only draws random numbers and stores them as bfloat16 bit patterns; it holds
+none of the attention arithmetic.  Every tensor gets its own PCG64 substream
+(seed * 16 + slot) so any tensor can be regenerated alone, in chunks, with identical bits.
+
+Value recipe (the pages measure on activations of trained models, which are not available;
+these i.i.d. draws stand in for them):
+  * Q, K, V, KV caches ~ N(0, 1), rounded to bf16 (round to nearest even);
+  * compressor weights ~ N(0, std = 1/sqrt(l * D)), rounded to bf16;
+  * gates = sigmoid(N(0, 1)) as fp32 (the gate network itself is outside the layer);
+  * planted long-context decode: per KV head, 16 distinct blocks drawn from [1, nblk - 3];
+    every key of those blocks gets + 2 * unit(sum of the group's query vectors), re-rounded.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SLOT = {"q": 0, "k": 1, "v": 2, "wk": 3, "wv": 4, "gate": 5, "plant": 6, "seqlen": 7}
+
+
+def _gen(seed: int, slot: str) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed * 16 + SLOT[slot]))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest, ties to even. Finite inputs only."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = ((u >> 16) & 1) + np.uint32(0x7FFF)
+    return ((u + r) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def normal_bf16(seed: int, slot: str, shape, std: float = 1.0, chunk: int = 1 << 26) -> np.ndarray:
+    """N(0, std^2) draws in fp32, rounded to bf16 bits.  Drawn in chunks to bound host memory;
+    chunked draws from one PCG64 stream equal a single draw."""
+    g = _gen(seed, slot)
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        x = g.standard_normal(e - s, dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        out[s:e] = f32_to_bf16_bits(x)
+    return out.reshape(shape)
+
+
+def gates(seed: int, shape) -> np.ndarray:
+    g = _gen(seed, "gate")
+    x = g.standard_normal(int(np.prod(shape)), dtype=np.float32).astype(np.float64)
+    return (1.0 / (1.0 + np.exp(-x))).astype(np.float32).reshape(shape)
+
+
+def nsa_prefill_inputs(seed: int, B: int, T: int, Hkv: int, G: int, D: int, l: int = 32):
+    Hq = Hkv * G
+    wstd = 1.0 / np.sqrt(l * D)
+    return dict(
+        q=normal_bf16(seed, "q", (B, T, Hq, D)),
+        k=normal_bf16(seed, "k", (B, Hkv, T, D)),
+        v=normal_bf16(seed, "v", (B, Hkv, T, D)),
+        wk=normal_bf16(seed, "wk", (l, D, D), std=wstd),
+        wv=normal_bf16(seed, "wv", (l, D, D), std=wstd),
+        gate=gates(seed, (B, T, Hq, 3)),
+    )
+
+
+def nsa_decode_inputs(seed: int, B: int, L: int, Hkv: int, G: int, D: int, l: int = 32,
+                      seqlens=None):
+    """Decode inputs: one query per sequence, a K/V cache of capacity L (all positions filled),
+    compressor weights for building the compressed cache, gates.  seqlens defaults to L."""
+    Hq = Hkv * G
+    wstd = 1.0 / np.sqrt(l * D)
+    if seqlens is None:
+        seqlens = np.full(B, L, dtype=np.int32)
+    return dict(
+        q=normal_bf16(seed, "q", (B, Hq, D)),
+        kcache=normal_bf16(seed, "k", (B, Hkv, L, D)),
+        vcache=normal_bf16(seed, "v", (B, Hkv, L, D)),
+        wk=normal_bf16(seed, "wk", (l, D, D), std=wstd),
+        wv=normal_bf16(seed, "wv", (l, D, D), std=wstd),
+        gate=gates(seed, (B, Hq, 3)),
+        seqlens=np.asarray(seqlens, dtype=np.int32),
+    )
+
+
+def mean_pool_weights(l: int, D: int) -> np.ndarray:
+    """W[j] = I / l as bf16 bits (1/l is a power of two for l = 32, so exact)."""
+    w = np.zeros((l, D, D), dtype=np.float32)
+    for j in range(l):
+        w[j] = np.eye(D, dtype=np.float32) / l
+    return f32_to_bf16_bits(w)
+
+
+def plant_blocks(seed: int, kcache: np.ndarray, q: np.ndarray, G: int, sel_block: int = 64,
+                 n_plant: int = 16, shift: float = 2.0):
+    """Shift every key of n_plant random blocks per KV head toward the group's query direction.
+
+    kcache: bf16 bits [B, Hkv, L, D] (modified in place); q: bf16 bits [B, Hq, D].
+    Returns the planted block ids, int64 [B, Hkv, n_plant] (sorted)."""
+    B, Hkv, L, D = kcache.shape
+    nblk = L // sel_block
+    g = _gen(seed, "plant")
+    planted = np.empty((B, Hkv, n_plant), dtype=np.int64)
+    qf = bf16_bits_to_f32(q).reshape(B, Hkv, G, D).astype(np.float64)
+    for b in range(B):
+        for h in range(Hkv):
+            blocks = np.sort(g.choice(np.arange(1, nblk - 2), size=n_plant, replace=False))
+            planted[b, h] = blocks
+            dirn = qf[b, h].sum(axis=0)
+            dirn /= np.linalg.norm(dirn)
+            for j in blocks:
+                s = slice(j * sel_block, (j + 1) * sel_block)
+                kk = bf16_bits_to_f32(kcache[b, h, s]).astype(np.float64) + shift * dirn
+                kcache[b, h, s] = f32_to_bf16_bits(kk.astype(np.float32))
+    return planted
+
+
+def moba_inputs(seed: int, B: int, T: int, H: int, D: int):
+    return dict(
+        q=normal_bf16(seed, "q", (B, T, H, D)),
+        k=normal_bf16(seed, "k", (B, H, T, D)),
+        v=normal_bf16(seed, "v", (B, H, T, D)),
+    )

@@ -1,0 +1,57 @@
+"""Build libnsa.so (all HIP sources, gfx950) in-tree with hipcc."""
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB = os.path.join(PKG, "libnsa.so")
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # never let the compiler form packed fp32 ops
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every kernel source and the C-ABI layer into one shared library."""
+    objs = []
+    tmpdir = os.path.join(PKG, "_build")
+    os.makedirs(tmpdir, exist_ok=True)
+    procs = []
+    for src in sources():
+        obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+        cmd = ["hipcc", *HIPCC_FLAGS, "-c", "-I", os.path.join(ROOT, "include"), src, "-o", obj]
+        cmd.remove("-shared")
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((subprocess.Popen(cmd, stderr=subprocess.PIPE, text=True), src))
+        objs.append(obj)
+    failed = False
+    for p, src in procs:
+        _, err = p.communicate()
+        lines = [ln for ln in err.splitlines() if "packed-fp32-ops" not in ln]
+        if lines:
+            print("\n".join(lines), file=sys.stderr)
+        if p.returncode != 0:
+            failed = True
+            print("hipcc failed on %s" % src, file=sys.stderr)
+    if failed:
+        raise RuntimeError("HIP build failed")
+    tmp = LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,45 @@
+// Internal launcher interface between the C-ABI layer (api.hip) and the kernel files.
+// Every launcher only enqueues work on `stream`; shapes were validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nsa {
+
+struct PrefillArgs {
+  const uint16_t* q;    // [B, T, Hq, D]
+  const uint16_t* k;    // [B, Hkv, T, D]
+  const uint16_t* vt;   // [B, Hkv, D, TP]  values, keys contiguous, zero past T
+  const uint16_t* kc;   // [B, Hkv, NCP, D] compressed keys, zero rows past n_cmp
+  const uint16_t* vct;  // [B, Hkv, D, NCP] compressed values (transposed), zero past n_cmp
+  const float* gate;    // [B, T, Hq, 3]
+  float* out;           // [B, T, Hq, D]
+  int32_t* idx;         // [B, T, Hkv, top_n]
+  int B, T, Hkv, G, D;
+  int l, d, beta, top_n, n_local, window;
+  int ncmp, NCP, TP, nblk;
+  float scale_log2;     // softmax scale * log2(e)
+};
+
+// x [BH, rows, cols] -> xt [BH, cols, rows_pad] (bf16), zero-filled for rows..rows_pad-1.
+void launch_transpose(const uint16_t* x, uint16_t* xt, int BH, int rows, int cols, int rows_pad,
+                      hipStream_t s);
+
+// Compressed tokens of x [BH, T, D] with the transposed weight wt [D, l*D]:
+//   xc  (nullable) [BH, rows_alloc, D] row-major, rows n_cmp..rows_alloc-1 zero;
+//   xct (nullable) [BH, D, ncp] transposed, columns n_cmp..ncp-1 zero.
+void launch_compress(const uint16_t* x, const uint16_t* wt, uint16_t* xc, uint16_t* xct, int BH,
+                     int T, int D, int l, int d, int ncmp, int rows_alloc, int ncp,
+                     hipStream_t s);
+
+// Compressed attention (lse pass + probability pass), block importance, group selection;
+// writes out = gate_cmp * o_cmp and idx.
+void launch_cmp_select(const PrefillArgs& a, hipStream_t s);
+// out += gate_win * o_win.
+void launch_window(const PrefillArgs& a, hipStream_t s);
+// out += gate_slc * o_slc over the blocks in idx.
+void launch_selected(const PrefillArgs& a, hipStream_t s);
+
+size_t cmp_select_lds_bytes(int G, int nblk);
+
+}  // namespace nsa

@@ -1,0 +1,133 @@
+// Layout kernels: bf16 transpose (values with keys contiguous, compressor weights) and the
+// block compression of K/V ("Native Sparse Attention" article, token compression: a learnable
+// linear layer maps each l-token block, taken every d tokens, to one representative).
+#include "dev_common.h"
+#include "kernels.h"
+
+namespace nsa {
+
+// x [BH, rows, cols] -> xt [BH, cols, rows_pad]; one 64x64 tile per workgroup.
+__global__ __launch_bounds__(256) void transpose_kernel(const u16* __restrict__ x,
+                                                        u16* __restrict__ xt, int rows,
+                                                        int cols, int rows_pad) {
+  __shared__ u16 tile[64][66];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const long bh = blockIdx.z;
+  const int tid = threadIdx.x;
+  {
+    const int r = tid >> 2, cc = (tid & 3) * 16;
+    const int row = r0 + r;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int col = c0 + cc + e;
+      u16 v = 0;
+      if (row < rows && col < cols) v = x[(bh * rows + row) * cols + col];
+      tile[r][cc + e] = v;
+    }
+  }
+  __syncthreads();
+  {
+    const int c = tid >> 2, rr = (tid & 3) * 16;
+    const int col = c0 + c;
+    if (col < cols) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = r0 + rr + e;
+        if (row < rows_pad) xt[(bh * cols + col) * rows_pad + row] = tile[rr + e][c];
+      }
+    }
+  }
+}
+
+void launch_transpose(const uint16_t* x, uint16_t* xt, int BH, int rows, int cols, int rows_pad,
+                      hipStream_t s) {
+  dim3 grid((rows_pad + 63) / 64, (cols + 63) / 64, BH);
+  transpose_kernel<<<grid, 256, 0, s>>>(x, xt, rows, cols, rows_pad);
+}
+
+// Computes the transposed tile  C^T[c][i] = sum_k Wt[c][k] * X_i[k]  where X_i is the l*D
+// contiguous elements of x starting at token i*d (the l tokens of compressed token i), so the
+// A operand is the weight and the B operand the token window; both are 16-byte loads.
+// Workgroup: 64 compressed tokens x D features; wave w owns features [w*D/4, (w+1)*D/4).
+template <int D>
+__global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x,
+                                                       const u16* __restrict__ wt,
+                                                       u16* __restrict__ xc, u16* __restrict__ xct,
+                                                       int T, int l, int d, int ncmp,
+                                                       int rows_alloc, int ncp) {
+  constexpr int CT = D / 64;  // 16-wide feature tiles per wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const long bh = blockIdx.y;
+  const int i0 = blockIdx.x * 64;
+  const int K = l * D;
+  const u16* xb = x + bh * (long)T * D;
+
+  f32x4 acc[CT][4];
+#pragma unroll
+  for (int a = 0; a < CT; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = zero4();
+
+  if (ncmp > 0) {
+    long xrow[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      int i = i0 + it * 16 + r16;
+      i = i < ncmp ? i : ncmp - 1;  // clamp: rows past n_cmp are computed and discarded
+      xrow[it] = (long)i * d * D;
+    }
+    const u16* wrow[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) wrow[ct] = wt + (long)(wave * (D / 4) + ct * 16 + r16) * K;
+    for (int k0 = 0; k0 < K; k0 += 32) {
+      const int ko = k0 + 8 * g4;
+      bf16x8 bx[4], aw[CT];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) bx[it] = load8(xb + xrow[it] + ko);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) aw[ct] = load8(wrow[ct] + ko);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) acc[ct][it] = mfma16x16x32(aw[ct], bx[it], acc[ct][it]);
+    }
+  }
+  // lane holds C^T[c = base + 4*g4 + e][i = i0 + it*16 + r16]
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int c = wave * (D / 4) + ct * 16 + 4 * g4;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = i0 + it * 16 + r16;
+      const bool live = i < ncmp;
+      u16 h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = live ? f32_to_bf16(acc[ct][it][e]) : (u16)0;
+      if (xc != nullptr && i < rows_alloc) {
+        uint2 pk;
+        pk.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+        pk.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+        *reinterpret_cast<uint2*>(xc + (bh * rows_alloc + i) * D + c) = pk;
+      }
+      if (xct != nullptr && i < ncp) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xct[(bh * D + c + e) * (long)ncp + i] = h[e];
+      }
+    }
+  }
+}
+
+void launch_compress(const uint16_t* x, const uint16_t* wt, uint16_t* xc, uint16_t* xct, int BH,
+                     int T, int D, int l, int d, int ncmp, int rows_alloc, int ncp,
+                     hipStream_t s) {
+  int rows = rows_alloc > ncp ? rows_alloc : ncp;
+  if (rows <= 0) return;
+  dim3 grid((rows + 63) / 64, BH);
+  if (D == 128)
+    compress_kernel<128><<<grid, 256, 0, s>>>(x, wt, xc, xct, T, l, d, ncmp, rows_alloc, ncp);
+  else
+    compress_kernel<64><<<grid, 256, 0, s>>>(x, wt, xc, xct, T, l, d, ncmp, rows_alloc, ncp);
+}
+
+}  // namespace nsa

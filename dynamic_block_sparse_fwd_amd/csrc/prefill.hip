@@ -1,0 +1,566 @@
+// NSA prefill kernels ("Zhang Xiaojun podcast EP94 notes", sections 5 and 6):
+//   cmp_select_kernel: compressed attention + block importance + group top-n selection;
+//   window_kernel:     sliding-window attention;
+//   selected_kernel:   attention over the selected blocks, the group's heads stacked into the
+//                      matrix-core M dimension (section 6: heads of a GQA group share one
+//                      selection, so their queries form one tile against each block).
+// The gate mix is folded into the three output writes: cmp stores g0*o_cmp, window and
+// selected add g2*o_win and g1*o_slc.
+#include "dev_common.h"
+#include "kernels.h"
+
+namespace nsa {
+
+// Query tile geometry shared by the compressed and window kernels: TQ positions x G heads
+// = ROWS matrix rows, 16 rows per MFMA tile, up to two tiles per wave.
+template <int G>
+struct QTile {
+  static constexpr int TQ = (16 / G > 8) ? 16 / G : 8;
+  static constexpr int ROWS = TQ * G;
+  static constexpr int RT_ALL = ROWS / 16;
+  static constexpr int NW = RT_ALL >= 2 ? RT_ALL / 2 : 1;
+  static constexpr int RTW = RT_ALL / NW;
+};
+
+constexpr int KPAD = 8;  // bf16 padding of LDS rows (16 bytes)
+
+__device__ __forceinline__ int n_visible(int t, int l, int d, int ncmp) {
+  if (t < l - 1) return 0;
+  int n = (t - l + 1) / d + 1;
+  return n < ncmp ? n : ncmp;
+}
+
+// Cooperative copy of a 64-row x D tile (row-major, 16-byte rows chunks) into LDS [64][D+KPAD].
+template <int D, int NT>
+__device__ __forceinline__ void load_rows_tile(u16 (*dst)[D + KPAD], const u16* src, long row0,
+                                               int row_limit) {
+  constexpr int CH = D / 8;  // 16-byte chunks per row
+  for (int c = threadIdx.x; c < 64 * CH; c += NT) {
+    const int r = c / CH, o = (c % CH) * 8;
+    long row = row0 + r;
+    if (row > row_limit) row = row_limit;
+    store8(&dst[r][o], load8(src + row * D + o));
+  }
+}
+
+// Cooperative copy of a D x 64 tile of a transposed tensor (keys contiguous, row pitch `pitch`).
+template <int D, int NT>
+__device__ __forceinline__ void load_cols_tile(u16 (*dst)[64 + KPAD], const u16* src, long pitch,
+                                               long col0) {
+  for (int c = threadIdx.x; c < D * 8; c += NT) {
+    const int r = c >> 3, o = (c & 7) * 8;
+    store8(&dst[r][o], load8(src + r * pitch + col0 + o));
+  }
+}
+
+// S^T sub-tile: 16 keys (chunk kc, sub-tile s of the LDS tile) x 16 query rows.
+template <int D>
+__device__ __forceinline__ f32x4 score_subtile(const u16 (*Ks)[D + KPAD], const bf16x8* qf,
+                                               int kc, int s, int g4, int r16) {
+  f32x4 acc = zero4();
+  const u16* krow = Ks[32 * kc + perm_key(r16, s)];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) acc = mfma16x16x32(load8(krow + 32 * c + 8 * g4), qf[c], acc);
+  return acc;
+}
+
+// O^T += V^T P^T for one 32-key chunk; pb holds this lane's row probabilities for keys
+// 32*kc + 8*g4 .. +7.
+template <int D>
+__device__ __forceinline__ void pv_chunk(const u16 (*Vs)[64 + KPAD], const bf16x8& pb, int kc,
+                                         int g4, int r16, f32x4* O) {
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n)
+    O[n] = mfma16x16x32(load8(&Vs[16 * n + r16][32 * kc + 8 * g4]), pb, O[n]);
+}
+
+template <int D, int G>
+__device__ __forceinline__ void load_q_frags(const PrefillArgs& a, int b, int kvh, int t0,
+                                             int wave, int lane, bf16x8 (*qf)[D / 32],
+                                             int* row_t, int* row_h) {
+  using QT = QTile<G>;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const int Hq = a.Hkv * G;
+#pragma unroll
+  for (int rt = 0; rt < QT::RTW; ++rt) {
+    const int r = (wave * QT::RTW + rt) * 16 + r16;
+    const int t = t0 + r / G, hh = r % G;
+    row_t[rt] = t;
+    row_h[rt] = kvh * G + hh;
+    const bool live = t < a.T;
+    const u16* qp = a.q + (((long)b * a.T + (live ? t : 0)) * Hq + kvh * G + hh) * D;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) qf[rt][c] = live ? load8(qp + 32 * c + 8 * g4) : zero8();
+  }
+}
+
+// ------------------------------------------------------------------ compressed + selection
+
+template <int D, int G>
+__global__ __launch_bounds__(QTile<G>::NW * 64) void cmp_select_kernel(PrefillArgs a) {
+  using QT = QTile<G>;
+  constexpr int NT = QT::NW * 64, TQ = QT::TQ, RTW = QT::RTW, DT = D / 16;
+  __shared__ u16 Ks[64][D + KPAD];
+  __shared__ u16 Vs[D][64 + KPAD];
+  __shared__ float Mb[TQ][64];
+  extern __shared__ float Sb[];  // [TQ][nblk]
+
+  const int tile = gridDim.x - 1 - blockIdx.x;  // longest rows first
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int t0 = tile * TQ;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const long bkv = (long)b * a.Hkv + kvh;
+  const int nblk = a.nblk;
+
+  bf16x8 qf[RTW][D / 32];
+  int row_t[RTW], row_h[RTW], nvis[RTW];
+  load_q_frags<D, G>(a, b, kvh, t0, wave, lane, qf, row_t, row_h);
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt)
+    nvis[rt] = row_t[rt] < a.T ? n_visible(row_t[rt], a.l, a.d, a.ncmp) : 0;
+
+  const int tlast = (t0 + TQ - 1 < a.T - 1) ? t0 + TQ - 1 : a.T - 1;
+  const int nvis_max = n_visible(tlast, a.l, a.d, a.ncmp);
+  const int nkt = (nvis_max + 63) / 64;
+  const u16* kc = a.kc + bkv * (long)a.NCP * D;
+  const u16* vct = a.vct + bkv * (long)D * a.NCP;
+
+  for (int e = threadIdx.x; e < TQ * nblk; e += NT) Sb[e] = 0.f;
+
+  // Pass 1: per-row log-sum-exp (base 2) of the visible compressed logits.
+  float mrun[RTW], lrun[RTW];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) { mrun[rt] = kNegInf; lrun[rt] = 0.f; }
+  for (int kt = 0; kt < nkt; ++kt) {
+    __syncthreads();
+    load_rows_tile<D, NT>(Ks, kc, (long)kt * 64, a.NCP - 1);
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      float z[16];
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          f32x4 acc = score_subtile<D>(Ks, qf[rt], kc2, s, g4, r16);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kt * 64 + 32 * kc2 + 8 * g4 + 4 * s + i;
+            z[kc2 * 8 + s * 4 + i] = key < nvis[rt] ? acc[i] * a.scale_log2 : kNegInf;
+          }
+        }
+      float tm = z[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) tm = fmaxf(tm, z[e]);
+      const float mn = fmaxf(mrun[rt], tm);
+      if (mn != kNegInf) {
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sum += fast_exp2(z[e] - mn);
+        lrun[rt] = lrun[rt] * fast_exp2(mrun[rt] - mn) + sum;
+        mrun[rt] = mn;
+      }
+    }
+  }
+  float lse[RTW];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) {
+    const float M = col_max4(mrun[rt]);
+    const float part = (mrun[rt] == kNegInf) ? 0.f : lrun[rt] * fast_exp2(mrun[rt] - M);
+    const float L = col_sum4(part);
+    lse[rt] = (M == kNegInf) ? __builtin_inff() : M + __log2f(L);  // +inf -> every p = 0
+  }
+
+  // Pass 2: normalised probabilities -> o_cmp and per-(t, key) group mass -> block scores.
+  f32x4 O[RTW][DT];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+    for (int n = 0; n < DT; ++n) O[rt][n] = zero4();
+  const float inv_l = 1.0f / (float)a.l;
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    __syncthreads();
+    load_rows_tile<D, NT>(Ks, kc, (long)kt * 64, a.NCP - 1);
+    load_cols_tile<D, NT>(Vs, vct, a.NCP, (long)kt * 64);
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2) {
+        float pv[8];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          f32x4 acc = score_subtile<D>(Ks, qf[rt], kc2, s, g4, r16);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kt * 64 + 32 * kc2 + 8 * g4 + 4 * s + i;
+            pv[4 * s + i] = key < nvis[rt] ? fast_exp2(acc[i] * a.scale_log2 - lse[rt]) : 0.f;
+          }
+        }
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pv[e];
+        pv_chunk<D>(Vs, pb, kc2, g4, r16, O[rt]);
+        // group mass: sum over the G heads (adjacent rows) of the same position
+        const int r = (wave * RTW + rt) * 16 + r16;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float hs = group_sum<(G < 16 ? G : 16)>(pv[e]);
+          if ((r16 % G) == 0) Mb[r / G][32 * kc2 + 8 * g4 + e] = hs;
+        }
+      }
+    }
+    __syncthreads();
+    // Block importance: compressed token i covers tokens [i*d, i*d + l); its mass is spread
+    // evenly over those tokens and summed per block of `beta` tokens.
+    const int k0 = kt * 64;
+    const int jlo = (k0 * a.d) / a.beta;
+    int jhi = ((k0 + 63) * a.d + a.l - 1) / a.beta;
+    if (jhi > nblk - 1) jhi = nblk - 1;
+    const int nj = jhi - jlo + 1;
+    for (int pr = threadIdx.x; pr < TQ * nj; pr += NT) {
+      const int tq = pr / nj, j = jlo + pr % nj;
+      if (t0 + tq >= a.T) continue;
+      const int bs = j * a.beta, be = bs + a.beta;  // block tokens [bs, be)
+      int ilo = bs - a.l + 1 <= 0 ? 0 : (bs - a.l + 1 + a.d - 1) / a.d;
+      if (ilo < k0) ilo = k0;
+      int ihi = (be - 1) / a.d;
+      if (ihi > k0 + 63) ihi = k0 + 63;
+      // terms are added one by one in key order, so every block sees the same sequence of
+      // fp32 operations whether or not its keys straddle two key tiles (exact ties stay exact)
+      float sv = Sb[tq * nblk + j];
+      for (int i = ilo; i <= ihi; ++i) {
+        const int s0 = i * a.d, s1 = s0 + a.l;
+        const int ov = (s1 < be ? s1 : be) - (s0 > bs ? s0 : bs);
+        if (ov > 0) sv += Mb[tq][i - k0] * ((float)ov * inv_l);
+      }
+      Sb[tq * nblk + j] = sv;
+    }
+  }
+
+  // o_cmp epilogue: out = g0 * o_cmp.  Lane holds O^T[d = 16n + 4*g4 + e][row r16].
+  const int Hq = a.Hkv * G;
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) {
+    const int t = row_t[rt];
+    if (t < a.T) {
+      const long rowoff = ((long)b * a.T + t) * Hq + row_h[rt];
+      const float g0 = a.gate[rowoff * 3 + 0];
+      float* op = a.out + rowoff * D;
+#pragma unroll
+      for (int n = 0; n < DT; ++n) {
+        float4 v = make_float4(g0 * O[rt][n][0], g0 * O[rt][n][1], g0 * O[rt][n][2],
+                               g0 * O[rt][n][3]);
+        *reinterpret_cast<float4*>(op + 16 * n + 4 * g4) = v;
+      }
+    }
+  }
+  __syncthreads();
+
+  // Selection: one wave per position.  Free candidates are ranked by a 64-bit key
+  // (score bits << 32 | ~index): larger score first, then lower index.
+  for (int tq = wave; tq < TQ; tq += QT::NW) {
+    const int t = t0 + tq;
+    if (t >= a.T) break;
+    const int bcur = t / a.beta, nb = bcur + 1;
+    int32_t* orow = a.idx + (((long)b * a.T + t) * a.Hkv + kvh) * a.top_n;
+    if (nb <= a.top_n) {
+      for (int e = lane; e < a.top_n; e += 64) orow[e] = e < nb ? e : -1;
+      continue;
+    }
+    const int flo = bcur - a.n_local + 1;  // forced local blocks flo..bcur (flo >= 2 here)
+    const int nforced = 1 + a.n_local;
+    const int kfree = a.top_n - nforced;
+    float* srow = Sb + tq * nblk;
+    uint32_t removed = 0;  // bit m: candidate j = 1 + lane + 64 m already chosen
+    int mine = -1;         // lane e < kfree keeps the e-th winner
+    for (int it = 0; it < kfree; ++it) {
+      uint64_t best = 0;
+      for (int m = 0, j = 1 + lane; j < flo; ++m, j += 64) {
+        if (removed & (1u << m)) continue;
+        const uint64_t key = ((uint64_t)__float_as_uint(srow[j]) << 32) | (0xFFFFFFFFu - (uint32_t)j);
+        best = u64_max(best, key);
+      }
+      best = wave_max_u64(best);
+      const int jw = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+      if (((jw - 1) & 63) == lane) removed |= 1u << ((jw - 1) >> 6);
+      if (lane == it) mine = jw;
+    }
+    // the set: lanes 0..kfree-1 hold winners; next lanes hold block 0 and flo..bcur
+    int el = mine;
+    if (lane == kfree) el = 0;
+    if (lane > kfree && lane < a.top_n) el = flo + (lane - kfree - 1);
+    int rank = 0;
+    for (int o = 0; o < a.top_n; ++o) {
+      const int other = __shfl(el, o);
+      rank += (other < el) ? 1 : 0;
+    }
+    if (lane < a.top_n) orow[rank] = el;
+  }
+}
+
+// ------------------------------------------------------------------ sliding window
+
+template <int D, int G>
+__global__ __launch_bounds__(QTile<G>::NW * 64) void window_kernel(PrefillArgs a) {
+  using QT = QTile<G>;
+  constexpr int NT = QT::NW * 64, TQ = QT::TQ, RTW = QT::RTW, DT = D / 16;
+  __shared__ u16 Ks[64][D + KPAD];
+  __shared__ u16 Vs[D][64 + KPAD];
+
+  const int tile = blockIdx.x;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int t0 = tile * TQ;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const long bkv = (long)b * a.Hkv + kvh;
+
+  bf16x8 qf[RTW][D / 32];
+  int row_t[RTW], row_h[RTW];
+  load_q_frags<D, G>(a, b, kvh, t0, wave, lane, qf, row_t, row_h);
+
+  const int tlast = (t0 + TQ - 1 < a.T - 1) ? t0 + TQ - 1 : a.T - 1;
+  const int kstart = t0 - a.window + 1 > 0 ? t0 - a.window + 1 : 0;
+  const int kt0 = kstart / 64, kt1 = tlast / 64;
+  const u16* kb = a.k + bkv * (long)a.T * D;
+  const u16* vtb = a.vt + bkv * (long)D * a.TP;
+
+  float mrun[RTW], lrun[RTW];
+  f32x4 O[RTW][DT];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) {
+    mrun[rt] = kNegInf;
+    lrun[rt] = 0.f;
+#pragma unroll
+    for (int n = 0; n < DT; ++n) O[rt][n] = zero4();
+  }
+
+  for (int kt = kt0; kt <= kt1; ++kt) {
+    __syncthreads();
+    load_rows_tile<D, NT>(Ks, kb, (long)kt * 64, a.T - 1);
+    load_cols_tile<D, NT>(Vs, vtb, a.TP, (long)kt * 64);
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const int t = row_t[rt];
+      const int lo = t - a.window + 1;
+      float z[16];
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          f32x4 acc = score_subtile<D>(Ks, qf[rt], kc2, s, g4, r16);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kt * 64 + 32 * kc2 + 8 * g4 + 4 * s + i;
+            const bool ok = key <= t && key >= lo && t < a.T;
+            z[kc2 * 8 + s * 4 + i] = ok ? acc[i] * a.scale_log2 : kNegInf;
+          }
+        }
+      float tm = z[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) tm = fmaxf(tm, z[e]);
+      tm = col_max4(tm);
+      const float mn = fmaxf(mrun[rt], tm);
+      // A row with no visible key yet keeps m = -inf; exponentials then use 0 as reference
+      // so every p is exactly 0 (no branch: the MFMAs below need the whole wave).
+      const float ms = (mn == kNegInf) ? 0.f : mn;
+      const float alpha = fast_exp2(mrun[rt] - ms);
+      mrun[rt] = mn;
+      float p[16], sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { p[e] = fast_exp2(z[e] - ms); sum += p[e]; }
+      lrun[rt] = lrun[rt] * alpha + sum;
+#pragma unroll
+      for (int n = 0; n < DT; ++n) O[rt][n] *= alpha;
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[kc2 * 8 + e];
+        pv_chunk<D>(Vs, pb, kc2, g4, r16, O[rt]);
+      }
+    }
+  }
+
+  const int Hq = a.Hkv * G;
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) {
+    const float L = col_sum4(lrun[rt]);
+    const int t = row_t[rt];
+    if (t < a.T) {
+      const long rowoff = ((long)b * a.T + t) * Hq + row_h[rt];
+      const float gs = a.gate[rowoff * 3 + 2] / L;
+      float* op = a.out + rowoff * D;
+#pragma unroll
+      for (int n = 0; n < DT; ++n) {
+        float4* dst = reinterpret_cast<float4*>(op + 16 * n + 4 * g4);
+        float4 v = *dst;
+        v.x += gs * O[rt][n][0];
+        v.y += gs * O[rt][n][1];
+        v.z += gs * O[rt][n][2];
+        v.w += gs * O[rt][n][3];
+        *dst = v;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ selected blocks
+
+// One wave per (position, KV group): the group's heads form the 16 MFMA rows; K and V
+// fragments are read straight from global memory (16-byte loads), no LDS.
+template <int D, int G>
+__global__ __launch_bounds__(256) void selected_kernel(PrefillArgs a) {
+  constexpr int DT = D / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const int t = blockIdx.x * 4 + wave;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  if (t >= a.T) return;
+  const long bkv = (long)b * a.Hkv + kvh;
+  const int Hq = a.Hkv * G;
+  const bool hlive = r16 < G;
+  const int head = kvh * G + (hlive ? r16 : 0);
+
+  bf16x8 qf[D / 32];
+  {
+    const u16* qp = a.q + (((long)b * a.T + t) * Hq + head) * D;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) qf[c] = hlive ? load8(qp + 32 * c + 8 * g4) : zero8();
+  }
+  const u16* kb = a.k + bkv * (long)a.T * D;
+  const u16* vtb = a.vt + bkv * (long)D * a.TP;
+  const int32_t* irow = a.idx + (((long)b * a.T + t) * a.Hkv + kvh) * a.top_n;
+
+  float mrun = kNegInf, lrun = 0.f;
+  f32x4 O[DT];
+#pragma unroll
+  for (int n = 0; n < DT; ++n) O[n] = zero4();
+
+  for (int ai = 0; ai < a.top_n; ++ai) {
+    const int j = irow[ai];
+    if (j < 0) break;
+    for (int key0 = j * a.beta; key0 < (j + 1) * a.beta && key0 <= t; key0 += 64) {
+      float z[16];
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          int krow = key0 + 32 * kc2 + perm_key(r16, s);
+          krow = krow < a.T ? krow : a.T - 1;
+          const u16* kp = kb + (long)krow * D + 8 * g4;
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c) acc = mfma16x16x32(load8(kp + 32 * c), qf[c], acc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = key0 + 32 * kc2 + 8 * g4 + 4 * s + i;
+            z[kc2 * 8 + s * 4 + i] = key <= t ? acc[i] * a.scale_log2 : kNegInf;
+          }
+        }
+      float tm = z[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) tm = fmaxf(tm, z[e]);
+      tm = col_max4(tm);
+      const float mn = fmaxf(mrun, tm);
+      const float alpha = fast_exp2(mrun - mn);
+      mrun = mn;
+      float p[16], sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { p[e] = fast_exp2(z[e] - mn); sum += p[e]; }
+      lrun = lrun * alpha + sum;
+#pragma unroll
+      for (int n = 0; n < DT; ++n) O[n] *= alpha;
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[kc2 * 8 + e];
+#pragma unroll
+        for (int n = 0; n < DT; ++n) {
+          const u16* vp = vtb + (long)(16 * n + r16) * a.TP + key0 + 32 * kc2 + 8 * g4;
+          O[n] = mfma16x16x32(load8(vp), pb, O[n]);
+        }
+      }
+    }
+  }
+
+  const float L = col_sum4(lrun);
+  if (hlive) {
+    const long rowoff = ((long)b * a.T + t) * Hq + head;
+    const float gs = a.gate[rowoff * 3 + 1] / L;
+    float* op = a.out + rowoff * D;
+#pragma unroll
+    for (int n = 0; n < DT; ++n) {
+      float4* dst = reinterpret_cast<float4*>(op + 16 * n + 4 * g4);
+      float4 v = *dst;
+      v.x += gs * O[n][0];
+      v.y += gs * O[n][1];
+      v.z += gs * O[n][2];
+      v.w += gs * O[n][3];
+      *dst = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+
+template <int G>
+static size_t cmp_lds(int nblk) {
+  return (size_t)QTile<G>::TQ * nblk * sizeof(float);
+}
+
+size_t cmp_select_lds_bytes(int G, int nblk) {
+  switch (G) {
+    case 1: return cmp_lds<1>(nblk);
+    case 2: return cmp_lds<2>(nblk);
+    case 4: return cmp_lds<4>(nblk);
+    case 8: return cmp_lds<8>(nblk);
+    default: return cmp_lds<16>(nblk);
+  }
+}
+
+template <int D, int G>
+static void launch_prefill_all(const PrefillArgs& a, int which, hipStream_t s) {
+  using QT = QTile<G>;
+  const int ntile = (a.T + QT::TQ - 1) / QT::TQ;
+  if (which == 0) {
+    const size_t lds = cmp_lds<G>(a.nblk);
+    static bool attr_set = false;  // opt in to the largest dynamic LDS the kernel may use
+    if (!attr_set) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cmp_select_kernel<D, G>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
+      attr_set = true;
+    }
+    cmp_select_kernel<D, G><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, lds, s>>>(a);
+  } else if (which == 1) {
+    window_kernel<D, G><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, 0, s>>>(a);
+  } else {
+    selected_kernel<D, G><<<dim3((a.T + 3) / 4, a.Hkv, a.B), 256, 0, s>>>(a);
+  }
+}
+
+template <int D>
+static void dispatch_g(const PrefillArgs& a, int which, hipStream_t s) {
+  switch (a.G) {
+    case 1: launch_prefill_all<D, 1>(a, which, s); break;
+    case 2: launch_prefill_all<D, 2>(a, which, s); break;
+    case 4: launch_prefill_all<D, 4>(a, which, s); break;
+    case 8: launch_prefill_all<D, 8>(a, which, s); break;
+    default: launch_prefill_all<D, 16>(a, which, s); break;
+  }
+}
+
+static void dispatch(const PrefillArgs& a, int which, hipStream_t s) {
+  if (a.D == 128) dispatch_g<128>(a, which, s);
+  else dispatch_g<64>(a, which, s);
+}
+
+void launch_cmp_select(const PrefillArgs& a, hipStream_t s) { dispatch(a, 0, s); }
+void launch_window(const PrefillArgs& a, hipStream_t s) { dispatch(a, 1, s); }
+void launch_selected(const PrefillArgs& a, hipStream_t s) { dispatch(a, 2, s); }
+
+}  // namespace nsa

@@ -1,0 +1,158 @@
+/*
+ * nsa.h -- C ABI of the MI355X (gfx950) Native Sparse Attention / MoBA forward library.
+ *
+ * The method (cited by page title and section):
+ *   "Zhang Xiaojun podcast EP94 notes", section 5: an NSA layer runs three branches on every
+ *   query -- attention over compressed block representatives of K/V, attention over the
+ *   top-N selected 64-token blocks (chosen from the compressed branch's scores), and attention
+ *   over a sliding window of recent tokens -- and a learned per-query gate mixes the three
+ *   outputs.  Section 6: the heads of one GQA group sum their scores and share one selection.
+ *   Sections 9-10: MoBA keeps only the selection branch, with mean-pooled block keys, top-k
+ *   blocks per head, and (podcast transcript "Late Talk #103") always the query's own block.
+ *   Section 16: NSA block 64 / top-16; MoBA block 512 / top-3.
+ *   "Native Sparse Attention" article (lchairun): learnable linear compressor; importance from
+ *   the compressed representatives and the query, then top-K; first block always selected;
+ *   decode loads only the needed KV, saving HBM bandwidth rather than memory.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers, 16-byte aligned, densely packed (row-major) in the
+ *     layouts stated below; bf16 tensors are IEEE bfloat16 bit patterns (uint16 storage).
+ *   - Work is enqueued on `stream`; nothing synchronises the host.  The library allocates,
+ *     frees and retains nothing: the caller owns every buffer, including the workspace, and
+ *     may reuse it once the stream has passed the call.
+ *   - All argument checks run on the host before any launch; on error nothing is enqueued and
+ *     a negative status is returned.  Nothing is thrown across the ABI.
+ *   - Calls that overlap on one workspace race; calls on distinct workspaces are independent.
+ *
+ * Readings of what the pages leave open (the same ones the CPU oracle takes):
+ *   compression is linear with one weight W[l, D, D] shared by all KV heads,
+ *     xc[i] = bf16_round( sum_{j<l} x[i*d + j] . W[j] ), i in [0, n_cmp), n_cmp = (T-l)/d + 1;
+ *   compressed token i is visible to query t once i*d + l - 1 <= t;
+ *   block importance = compressed attention probability spread evenly over the l tokens of
+ *     each compressed token and summed per selection block, then summed over the group's heads;
+ *   selection takes every visible block if they fit in top_n, else block 0, the n_local most
+ *     recent blocks (b - n_local + 1 .. b, b = t / sel_block) and the best remaining blocks by
+ *     (score desc, index asc); selected and window branches are causal (keys s <= t), the
+ *     window being the `window` most recent tokens including t;
+ *   out = gate[...,0] * o_cmp + gate[...,1] * o_slc + gate[...,2] * o_win (gates already
+ *     passed through the sigmoid by the caller).
+ */
+#ifndef NSA_MI355X_H
+#define NSA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define NSA_OK 0
+#define NSA_ERR_INVALID_ARG (-1) /* null pointer, misaligned pointer, non-positive size     */
+#define NSA_ERR_UNSUPPORTED (-2) /* valid but outside what the kernels implement (see below) */
+#define NSA_ERR_WORKSPACE (-3)   /* ws_bytes smaller than the *_workspace_bytes() figure     */
+#define NSA_ERR_HIP (-4)         /* a HIP launch or runtime error                            */
+
+/* One NSA layer call.  Hq = Hkv * G query heads; query head h reads KV head h / G. */
+typedef struct nsa_config {
+  int32_t B;          /* batch (sequences)                                            */
+  int32_t T;          /* prefill: sequence length; decode: cache capacity Lmax         */
+  int32_t Hkv;        /* KV heads                                                      */
+  int32_t G;          /* query heads per KV head (GQA group): 1, 2, 4, 8 or 16         */
+  int32_t D;          /* head dimension: 64 or 128                                     */
+  int32_t cmp_len;    /* l, tokens per compressed token (32)                           */
+  int32_t cmp_stride; /* d, stride between compressed tokens (16)                      */
+  int32_t sel_block;  /* selection block size, a multiple of 64 (64)                   */
+  int32_t top_n;      /* blocks selected per (query, group), forced ones included (16) */
+  int32_t n_local;    /* most recent blocks always selected besides block 0 (2)        */
+  int32_t window;     /* sliding-window length (512)                                   */
+  float scale;        /* softmax scale applied to q.k (1/sqrt(D))                      */
+} nsa_config;
+
+/* One MoBA call (no GQA: H heads with their own K/V). */
+typedef struct moba_config {
+  int32_t B, T, H, D; /* D: 64 or 128; T a multiple of `block`                          */
+  int32_t block;      /* block size, a multiple of 64 (512)                              */
+  int32_t top_k;      /* past blocks chosen per (query, head), own block added (3)      */
+  float scale;        /* softmax scale (1/sqrt(D))                                       */
+} moba_config;
+
+/* Human-readable text for a status code (static storage). */
+const char* nsa_status_string(int status);
+
+/* Host-only checks; no device is touched.  NSA_ERR_UNSUPPORTED when: D not 64/128;
+ * G not in {1,2,4,8,16}; sel_block not a positive multiple of 64; top_n < 1 + n_local or
+ * top_n > 64; T / sel_block > 2048 (prefill selection buffer); cmp_len < cmp_stride. */
+int nsa_validate(const nsa_config* cfg);
+int moba_validate(const moba_config* cfg);
+
+/* Workspace sizes in bytes for the calls below (0 on an invalid config). */
+size_t nsa_compress_workspace_bytes(const nsa_config* cfg);
+size_t nsa_prefill_workspace_bytes(const nsa_config* cfg);
+size_t nsa_decode_workspace_bytes(const nsa_config* cfg);
+size_t moba_prefill_workspace_bytes(const moba_config* cfg);
+
+/* Number of compressed tokens for a length: (T - l) / d + 1, or 0 when T < l. */
+int32_t nsa_num_compressed(int32_t T, int32_t cmp_len, int32_t cmp_stride);
+
+/*
+ * Block compression (the compressed branch's learnable linear map; "Native Sparse Attention"
+ * article, token compression), also the way to build the decode-time compressed cache.
+ *   x  bf16 [B, Hkv, T, D]  keys or values
+ *   w  bf16 [l, D, D]       W[j, e, c] maps input feature e of in-block token j to feature c
+ *   xc bf16 [B, Hkv, n_cmp, D] output, n_cmp = nsa_num_compressed(T, l, d)
+ *   ws at least nsa_compress_workspace_bytes(cfg) bytes (holds the transposed weight)
+ * fp32 accumulation, one round-to-nearest-even to bf16.  Uses cfg B, T, Hkv, D, l, d only.
+ */
+int nsa_compress(const nsa_config* cfg, const void* x, const void* w, void* xc, void* ws,
+                 size_t ws_bytes, hipStream_t stream);
+
+/*
+ * NSA prefill (three branches + gate; podcast notes EP94 sections 5-6).
+ *   q      bf16 [B, T, Hq, D]
+ *   k, v   bf16 [B, Hkv, T, D]
+ *   wk, wv bf16 [l, D, D]      compressor weights for K and V
+ *   gate   fp32 [B, T, Hq, 3]  (cmp, slc, win) gate values
+ *   out    fp32 [B, T, Hq, D]
+ *   sel_idx int32 [B, T, Hkv, top_n] or NULL: selected blocks per (t, group), ascending,
+ *           -1 padded
+ *   ws     device workspace of at least nsa_prefill_workspace_bytes(cfg) bytes
+ */
+int nsa_prefill(const nsa_config* cfg, const void* q, const void* k, const void* v,
+                const void* wk, const void* wv, const float* gate, float* out,
+                int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * NSA decode: one new query per sequence; the caches already hold the new token, so query b
+ * sits at position t = seqlens[b] - 1 (lchairun article: decode loads only the compressed,
+ * selected and window KV).
+ *   q              bf16 [B, Hq, D]
+ *   kcache, vcache bf16 [B, Hkv, Lmax, D]    (Lmax = cfg->T)
+ *   kcmp, vcmp     bf16 [B, Hkv, n_cmp(Lmax), D]  compressed caches (nsa_compress of the
+ *                  caches); rows i with i*d + l <= seqlens[b] must be valid
+ *   seqlens        int32 [B], 1 <= seqlens[b] <= Lmax (device memory)
+ *   gate           fp32 [B, Hq, 3];  out fp32 [B, Hq, D]
+ *   sel_idx        int32 [B, Hkv, top_n] or NULL
+ */
+int nsa_decode(const nsa_config* cfg, const void* q, const void* kcache, const void* vcache,
+               const void* kcmp, const void* vcmp, const int32_t* seqlens, const float* gate,
+               float* out, int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * MoBA prefill (podcast notes EP94 sections 9-10): per head, block keys are the mean of the
+ * block's keys, the query scores past blocks by q . kbar, keeps the top_k (ties to the lower
+ * index) plus its own block, and attends causally over their union with one softmax.
+ *   q bf16 [B, T, H, D]; k, v bf16 [B, H, T, D]; out fp32 [B, T, H, D]
+ *   sel_idx int32 [B, T, H, top_k + 1] or NULL: chosen blocks incl. the own block,
+ *           ascending, -1 padded
+ */
+int moba_prefill(const moba_config* cfg, const void* q, const void* k, const void* v,
+                 float* out, int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSA_MI355X_H */

@@ -1,0 +1,121 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad arguments on the
+host before touching a device (CPU only: no compute call reaches a kernel here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dynamic_block_sparse_fwd_amd as nsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "nsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                                 src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return nsa.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert {"nsa_prefill", "nsa_decode", "moba_prefill", "nsa_compress"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(nsa.EXPORTS), "binding and header disagree"
+
+
+def cfgB():
+    return nsa.NsaConfig(1, 65536, 4, 16, 128)
+
+
+def test_validate_accepts_the_workloads(lib):
+    for c in (nsa.NsaConfig(1, 2048, 1, 4, 64), cfgB(), nsa.NsaConfig(32, 65536, 4, 16, 128),
+              nsa.NsaConfig(1, 1 << 20, 8, 8, 128)):
+        st = lib.nsa_validate(ctypes.byref(c.c()))
+        if c.T > 65536 * 2:  # 1M tokens: prefill selection buffer too large, decode only
+            assert st == nsa.NSA_ERR_UNSUPPORTED
+        else:
+            assert st == nsa.NSA_OK
+    assert lib.moba_validate(ctypes.byref(nsa.MobaConfig(1, 131072, 32, 128).c())) == nsa.NSA_OK
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("D", 96, nsa.NSA_ERR_UNSUPPORTED), ("G", 3, nsa.NSA_ERR_UNSUPPORTED),
+    ("G", 0, nsa.NSA_ERR_INVALID_ARG), ("T", 0, nsa.NSA_ERR_INVALID_ARG),
+    ("sel_block", 48, nsa.NSA_ERR_UNSUPPORTED), ("top_n", 2, nsa.NSA_ERR_UNSUPPORTED),
+    ("top_n", 65, nsa.NSA_ERR_UNSUPPORTED), ("window", 0, nsa.NSA_ERR_INVALID_ARG),
+    ("cmp_stride", 64, nsa.NSA_ERR_UNSUPPORTED), ("scale", -1.0, nsa.NSA_ERR_INVALID_ARG),
+    ("T", 64 * 4096, nsa.NSA_ERR_UNSUPPORTED),
+])
+def test_validate_rejects(lib, field, value, code):
+    c = cfgB()
+    setattr(c, field, value)
+    assert lib.nsa_validate(ctypes.byref(c.c())) == code
+    assert lib.nsa_prefill_workspace_bytes(ctypes.byref(c.c())) == 0
+
+
+def test_moba_validate_rejects(lib):
+    for kw, code in ((dict(D=80), nsa.NSA_ERR_UNSUPPORTED), (dict(block=100), nsa.NSA_ERR_UNSUPPORTED),
+                     (dict(T=1000), nsa.NSA_ERR_UNSUPPORTED), (dict(H=0), nsa.NSA_ERR_INVALID_ARG)):
+        c = nsa.MobaConfig(1, 131072, 32, 128)
+        for k, v in kw.items():
+            setattr(c, k, v)
+        assert lib.moba_validate(ctypes.byref(c.c())) == code
+
+
+def test_null_config_and_status_strings(lib):
+    assert lib.nsa_validate(None) == nsa.NSA_ERR_INVALID_ARG
+    assert lib.nsa_prefill_workspace_bytes(None) == 0
+    for code in (0, -1, -2, -3, -4, 7):
+        assert len(nsa.status_string(code)) > 0
+
+
+def test_workspace_sizes_are_plausible(lib):
+    c = cfgB()
+    ws = lib.nsa_prefill_workspace_bytes(ctypes.byref(c.c()))
+    # transposed V (64 MiB) + compressed caches + weights + indices, well under 1 GiB
+    assert 64 << 20 < ws < 1 << 30
+    assert lib.nsa_num_compressed(65536, 32, 16) == 4095
+    assert lib.nsa_num_compressed(31, 32, 16) == 0
+    assert lib.nsa_compress_workspace_bytes(ctypes.byref(c.c())) >= 32 * 128 * 128 * 2
+
+
+def test_entry_points_reject_before_any_launch(lib):
+    c = nsa.NsaConfig(1, 2048, 1, 4, 64).c()
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: the calls must fail on host checks first
+    # null tensor pointers
+    assert lib.nsa_prefill(ctypes.byref(c), None, fake, fake, fake, fake, fake, fake, None, fake,
+                           1 << 30, None) == nsa.NSA_ERR_INVALID_ARG
+    # workspace too small
+    assert lib.nsa_prefill(ctypes.byref(c), fake, fake, fake, fake, fake, fake, fake, None, fake,
+                           16, None) == nsa.NSA_ERR_WORKSPACE
+    # misaligned pointer
+    assert lib.nsa_prefill(ctypes.byref(c), P(0x1001), fake, fake, fake, fake, fake, fake, None,
+                           fake, 1 << 40, None) == nsa.NSA_ERR_INVALID_ARG
+    assert lib.nsa_compress(ctypes.byref(c), None, fake, fake, fake, 1 << 20, None) == \
+        nsa.NSA_ERR_INVALID_ARG
+    assert lib.nsa_compress(ctypes.byref(c), fake, fake, fake, fake, 8, None) == nsa.NSA_ERR_WORKSPACE
+    bad = nsa.NsaConfig(1, 2048, 1, 3, 64).c()
+    assert lib.nsa_decode(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, fake, fake, None,
+                          fake, 1 << 30, None) == nsa.NSA_ERR_UNSUPPORTED
+    m = nsa.MobaConfig(1, 1024, 2, 64, block=128).c()
+    assert lib.moba_prefill(ctypes.byref(m), None, fake, fake, fake, None, fake, 1 << 30, None) == \
+        nsa.NSA_ERR_INVALID_ARG
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The binding and kernels never import or link the CPU oracle."""
+    pkg = os.path.join(ROOT, "dynamic_block_sparse_fwd_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in txt.lower().replace("oracles", ""), f

@@ -125,11 +125,11 @@ int nsa_compress(const nsa_config* c, const void* x, const void* w, void* xc, vo
                  size_t ws_bytes, hipStream_t stream) {
   int st = check_compress(c);
   if (st != NSA_OK) return st;
-  if (!x || !w || !xc || !ws) return NSA_ERR_INVALID_ARG;
+  const int ncmp = nsa_num_compressed(c->T, c->cmp_len, c->cmp_stride);
+  if (!x || !w || !ws || (!xc && ncmp > 0)) return NSA_ERR_INVALID_ARG;  // empty output may be null
   if (!aligned16(x) || !aligned16(w) || !aligned16(xc) || !aligned16(ws))
     return NSA_ERR_INVALID_ARG;
   if (ws_bytes < nsa_compress_workspace_bytes(c)) return NSA_ERR_WORKSPACE;
-  const int ncmp = nsa_num_compressed(c->T, c->cmp_len, c->cmp_stride);
   if (ncmp == 0) return NSA_OK;
   const int LD = c->cmp_len * c->D;
   uint16_t* wt = static_cast<uint16_t*>(ws);

@@ -49,6 +49,11 @@ void launch_transpose(const uint16_t* x, uint16_t* xt, int BH, int rows, int col
 // contiguous elements of x starting at token i*d (the l tokens of compressed token i), so the
 // A operand is the weight and the B operand the token window; both are 16-byte loads.
 // Workgroup: 64 compressed tokens x D features; wave w owns features [w*D/4, (w+1)*D/4).
+// Half-width of the band around a bf16 rounding midpoint inside which an fp32 accumulation is
+// re-done in fp64 (absolute below 1, relative above).  fp32 accumulation errors of these sums
+// are around 1e-6 of the operand scale; 2^-16 leaves a wide margin and flags about 1% of outputs.
+constexpr float kMidTol = 1.0f / 65536.0f;
+
 template <int D>
 __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x,
                                                        const u16* __restrict__ wt,
@@ -92,6 +97,43 @@ __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x
 #pragma unroll
         for (int it = 0; it < 4; ++it) acc[ct][it] = mfma16x16x32(aw[ct], bx[it], acc[ct][it]);
     }
+  }
+  // Exact rounding.  The fp32 sum of l*D products carries a small accumulation error; where
+  // it lies within kMidTol of a bf16 rounding midpoint the rounding direction is not settled
+  // by fp32, so the whole wave recomputes that element in fp64 (exact products, fp64 sum) and
+  // replaces it by its round-to-odd fp32 image, whose bf16 rounding equals the correctly
+  // rounded fp64 value.  Every other element already rounds like the exact sum.
+  if (ncmp > 0) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = acc[ct][it][e];
+          const float mid = __uint_as_float((__float_as_uint(v) & 0xFFFF0000u) | 0x8000u);
+          const float tol = kMidTol * fmaxf(1.f, fabsf(v));
+          uint64_t pending = __ballot(fabsf(v - mid) < tol && (i0 + it * 16 + r16) < ncmp);
+          while (pending) {
+            const int src = __builtin_ctzll(pending);
+            pending &= pending - 1;
+            const int c = wave * (D / 4) + ct * 16 + 4 * (src >> 4) + e;
+            const int i = i0 + it * 16 + (src & 15);
+            const u16* xp = xb + (long)i * d * D;
+            const u16* wp = wt + (long)c * K;
+            double s = 0.0;
+            for (int k = 8 * lane; k < K; k += 512) {
+              const bf16x8 xv = load8(xp + k), wv = load8(wp + k);
+#pragma unroll
+              for (int q = 0; q < 8; ++q) s += (double)(float)xv[q] * (double)(float)wv[q];
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+            float f = __double2float_rz(s);
+            if ((double)f != s) f = __uint_as_float(__float_as_uint(f) | 1u);  // round to odd
+            if (lane == src) acc[ct][it][e] = f;
+          }
+        }
   }
   // lane holds C^T[c = base + 4*g4 + e][i = i0 + it*16 + r16]
 #pragma unroll

@@ -163,13 +163,16 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void cmp_select_kernel(PrefillAr
       }
     }
   }
-  float lse[RTW];
+  // Row maximum and 1 / (sum of exp2(z - max)).  Pass 2 feeds the matrix core with
+  // p' = exp2(z - max) (largest term exactly 1 in bf16) and applies the normalisation in fp32.
+  float rmax[RTW], rinv[RTW];
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
     const float M = col_max4(mrun[rt]);
     const float part = (mrun[rt] == kNegInf) ? 0.f : lrun[rt] * fast_exp2(mrun[rt] - M);
     const float L = col_sum4(part);
-    lse[rt] = (M == kNegInf) ? __builtin_inff() : M + __log2f(L);  // +inf -> every p = 0
+    rmax[rt] = (M == kNegInf) ? 0.f : M;  // no visible key: every p' is masked to 0
+    rinv[rt] = (M == kNegInf) ? 0.f : 1.0f / L;
   }
 
   // Pass 2: normalised probabilities -> o_cmp and per-(t, key) group mass -> block scores.
@@ -196,18 +199,18 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void cmp_select_kernel(PrefillAr
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = kt * 64 + 32 * kc2 + 8 * g4 + 4 * s + i;
-            pv[4 * s + i] = key < nvis[rt] ? fast_exp2(acc[i] * a.scale_log2 - lse[rt]) : 0.f;
+            pv[4 * s + i] = key < nvis[rt] ? fast_exp2(acc[i] * a.scale_log2 - rmax[rt]) : 0.f;
           }
         }
         bf16x8 pb;
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pv[e];
         pv_chunk<D>(Vs, pb, kc2, g4, r16, O[rt]);
-        // group mass: sum over the G heads (adjacent rows) of the same position
+        // group mass: normalised probabilities summed over the G heads (adjacent rows)
         const int r = (wave * RTW + rt) * 16 + r16;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float hs = group_sum<(G < 16 ? G : 16)>(pv[e]);
+          const float hs = group_sum<(G < 16 ? G : 16)>(pv[e] * rinv[rt]);
           if ((r16 % G) == 0) Mb[r / G][32 * kc2 + 8 * g4 + e] = hs;
         }
       }
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void cmp_select_kernel(PrefillAr
     const int t = row_t[rt];
     if (t < a.T) {
       const long rowoff = ((long)b * a.T + t) * Hq + row_h[rt];
-      const float g0 = a.gate[rowoff * 3 + 0];
+      const float g0 = a.gate[rowoff * 3 + 0] * rinv[rt];
       float* op = a.out + rowoff * D;
 #pragma unroll
       for (int n = 0; n < DT; ++n) {

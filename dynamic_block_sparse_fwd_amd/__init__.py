@@ -53,6 +53,9 @@ EXPORTS = {
     "moba_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
     "nsa_compress": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p]),
     "nsa_prefill": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "nsa_prefill_timed": (ctypes.c_int,
+                          [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p,
+                                                     ctypes.c_void_p]),
     "nsa_decode": (ctypes.c_int, [ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p]),
     "moba_prefill": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p]),
 }
@@ -202,9 +205,14 @@ def nsa_compress(cfg: NsaConfig, x, w, out=None, ws=None, stream=None):
     return out
 
 
+PREFILL_STAGES = ("layout", "compress", "cmp_select", "window", "selected")
+
+
 def nsa_prefill(cfg: NsaConfig, q, k, v, wk, wv, gate, out=None, sel_idx=None, ws=None,
-                want_idx=True, stream=None):
-    """Returns (out fp32 [B,T,Hq,D], sel_idx int32 [B,T,Hkv,top_n] or None)."""
+                want_idx=True, stream=None, events=None):
+    """Returns (out fp32 [B,T,Hq,D], sel_idx int32 [B,T,Hkv,top_n] or None).
+    events: optional ctypes array of len(PREFILL_STAGES) + 1 hipEvent_t handles, recorded
+    around every stage (nsa_prefill_timed)."""
     torch = _torch()
     lib = load_library()
     c = cfg.c()
@@ -216,14 +224,16 @@ def nsa_prefill(cfg: NsaConfig, q, k, v, wk, wv, gate, out=None, sel_idx=None, w
         sel_idx = torch.empty((B, T, Hkv, cfg.top_n), dtype=torch.int32, device=dev)
     ws = _workspace(lib.nsa_prefill_workspace_bytes(ctypes.byref(c)), dev, ws)
     bt = _bf16_types()
-    st = lib.nsa_prefill(
+    fn = lib.nsa_prefill if events is None else lib.nsa_prefill_timed
+    extra = () if events is None else (ctypes.cast(events, ctypes.c_void_p),)
+    st = fn(
         ctypes.byref(c), _dev(q, "q", bt, (B, T, Hq, D)), _dev(k, "k", bt, (B, Hkv, T, D)),
         _dev(v, "v", bt, (B, Hkv, T, D)), _dev(wk, "wk", bt, (cfg.cmp_len, D, D)),
         _dev(wv, "wv", bt, (cfg.cmp_len, D, D)),
         _dev(gate, "gate", (torch.float32,), (B, T, Hq, 3)),
         _dev(out, "out", (torch.float32,), (B, T, Hq, D)),
         None if sel_idx is None else _dev(sel_idx, "sel_idx", (torch.int32,), (B, T, Hkv, cfg.top_n)),
-        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream))
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream), *extra)
     _check(st, "nsa_prefill")
     return out, sel_idx
 

@@ -140,9 +140,10 @@ int nsa_compress(const nsa_config* c, const void* x, const void* w, void* xc, vo
   return hip_status();
 }
 
-int nsa_prefill(const nsa_config* c, const void* q, const void* k, const void* v, const void* wk,
-                const void* wv, const float* gate, float* out, int32_t* sel_idx, void* ws,
-                size_t ws_bytes, hipStream_t stream) {
+static int prefill_impl(const nsa_config* c, const void* q, const void* k, const void* v,
+                        const void* wk, const void* wv, const float* gate, float* out,
+                        int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream,
+                        hipEvent_t* ev) {
   int st = check_nsa(c);
   if (st != NSA_OK) return st;
   if (!q || !k || !v || !wk || !wv || !gate || !out || !ws) return NSA_ERR_INVALID_ARG;
@@ -163,10 +164,17 @@ int nsa_prefill(const nsa_config* c, const void* q, const void* k, const void* v
   const int LD = c->cmp_len * c->D;
 
   (void)hipGetLastError();
+  auto mark = [&](int sidx) {
+    if (ev != nullptr) (void)hipEventRecord(ev[sidx], stream);
+  };
+  mark(0);
   launch_transpose(static_cast<const uint16_t*>(v), vt, BH, c->T, c->D, p.TP, stream);
   if (p.ncmp > 0) {
     launch_transpose(static_cast<const uint16_t*>(wk), wkt, 1, LD, c->D, LD, stream);
     launch_transpose(static_cast<const uint16_t*>(wv), wvt, 1, LD, c->D, LD, stream);
+  }
+  mark(1);
+  if (p.ncmp > 0) {
     launch_compress(static_cast<const uint16_t*>(k), wkt, kcb, nullptr, BH, c->T, c->D,
                     c->cmp_len, c->cmp_stride, p.ncmp, p.NCP, p.NCP, stream);
     launch_compress(static_cast<const uint16_t*>(v), wvt, nullptr, vct, BH, c->T, c->D,
@@ -186,10 +194,30 @@ int nsa_prefill(const nsa_config* c, const void* q, const void* k, const void* v
   a.n_local = c->n_local; a.window = c->window;
   a.ncmp = p.ncmp; a.NCP = p.NCP; a.TP = p.TP; a.nblk = p.nblk;
   a.scale_log2 = c->scale * 1.4426950408889634f;
+  mark(2);
   launch_cmp_select(a, stream);
+  mark(3);
   launch_window(a, stream);
+  mark(4);
   launch_selected(a, stream);
+  mark(5);
   return hip_status();
+}
+
+int nsa_prefill(const nsa_config* c, const void* q, const void* k, const void* v, const void* wk,
+                const void* wv, const float* gate, float* out, int32_t* sel_idx, void* ws,
+                size_t ws_bytes, hipStream_t stream) {
+  return prefill_impl(c, q, k, v, wk, wv, gate, out, sel_idx, ws, ws_bytes, stream, nullptr);
+}
+
+int nsa_prefill_timed(const nsa_config* c, const void* q, const void* k, const void* v,
+                      const void* wk, const void* wv, const float* gate, float* out,
+                      int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream,
+                      hipEvent_t* events) {
+  if (events == nullptr) return NSA_ERR_INVALID_ARG;
+  for (int i = 0; i <= NSA_PREFILL_NSTAGES; ++i)
+    if (events[i] == nullptr) return NSA_ERR_INVALID_ARG;
+  return prefill_impl(c, q, k, v, wk, wv, gate, out, sel_idx, ws, ws_bytes, stream, events);
 }
 
 }  // extern "C"

@@ -125,6 +125,19 @@ int nsa_prefill(const nsa_config* cfg, const void* q, const void* k, const void*
                 int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Instrumented nsa_prefill: identical work, plus events[s] recorded on `stream` before stage s
+ * and events[NSA_PREFILL_NSTAGES] after the last stage.  Stages: 0 layout (value and weight
+ * transposes), 1 block compression of K and V, 2 compressed attention + block importance +
+ * selection, 3 sliding window, 4 selected blocks.  `events` holds NSA_PREFILL_NSTAGES + 1
+ * caller-created events (hipEventCreate); for measurement only.
+ */
+#define NSA_PREFILL_NSTAGES 5
+int nsa_prefill_timed(const nsa_config* cfg, const void* q, const void* k, const void* v,
+                      const void* wk, const void* wv, const float* gate, float* out,
+                      int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream,
+                      hipEvent_t* events);
+
+/*
  * NSA decode: one new query per sequence; the caches already hold the new token, so query b
  * sits at position t = seqlens[b] - 1 (lchairun article: decode loads only the compressed,
  * selected and window KV).

@@ -22,7 +22,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 bool g_ok(int G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
 
-int check_nsa(const nsa_config* c) {
+int check_nsa_base(const nsa_config* c) {
   if (c == nullptr) return NSA_ERR_INVALID_ARG;
   if (c->B <= 0 || c->T <= 0 || c->Hkv <= 0 || c->G <= 0 || c->D <= 0 || c->cmp_len <= 0 ||
       c->cmp_stride <= 0 || c->sel_block <= 0 || c->top_n <= 0 || c->n_local < 0 ||
@@ -33,10 +33,28 @@ int check_nsa(const nsa_config* c) {
   if (c->sel_block % 64 != 0) return NSA_ERR_UNSUPPORTED;
   if (c->top_n < 1 + c->n_local || c->top_n > 64) return NSA_ERR_UNSUPPORTED;
   if (c->cmp_len < c->cmp_stride) return NSA_ERR_UNSUPPORTED;
+  if ((long)c->B * c->Hkv * c->G > (1L << 30)) return NSA_ERR_UNSUPPORTED;
+  return NSA_OK;
+}
+
+// Prefill keeps one query tile's block scores in LDS.
+int check_nsa(const nsa_config* c) {
+  int st = check_nsa_base(c);
+  if (st != NSA_OK) return st;
   const long nblk = ((long)c->T + c->sel_block - 1) / c->sel_block;
   if (nblk > 2048) return NSA_ERR_UNSUPPORTED;
   if (cmp_select_lds_bytes(c->G, (int)nblk) > kMaxDynLds) return NSA_ERR_UNSUPPORTED;
-  if ((long)c->B * c->Hkv * c->G > (1L << 30)) return NSA_ERR_UNSUPPORTED;
+  return NSA_OK;
+}
+
+// Decode builds each group's list of selected/window tiles in a fixed 160-entry table.
+int decode_max_tiles(const nsa_config* c) {
+  return c->top_n * (c->sel_block / 64) + (c->window + 63) / 64 + 1;
+}
+int check_nsa_decode(const nsa_config* c) {
+  int st = check_nsa_base(c);
+  if (st != NSA_OK) return st;
+  if (decode_max_tiles(c) > 160) return NSA_ERR_UNSUPPORTED;
   return NSA_OK;
 }
 
@@ -70,6 +88,36 @@ PrefillPlan plan_prefill(const nsa_config* c) {
   p.wkt = off; off += align_up((size_t)c->cmp_len * c->D * c->D * 2);
   p.wvt = off; off += align_up((size_t)c->cmp_len * c->D * c->D * 2);
   p.idx = off; off += align_up((size_t)c->B * c->T * c->Hkv * c->top_n * 4);
+  p.total = off;
+  return p;
+}
+
+struct DecodePlan {
+  size_t cm, cl, co, cb, lse, S, idx, pm, pl, po, total;
+  int ncmp, nblk, NCH, NBC, NSLICE, NSPLIT;
+};
+
+DecodePlan plan_decode(const nsa_config* c) {
+  DecodePlan p{};
+  const size_t BKV = (size_t)c->B * c->Hkv;
+  p.ncmp = nsa_num_compressed(c->T, c->cmp_len, c->cmp_stride);
+  p.nblk = (c->T + c->sel_block - 1) / c->sel_block;
+  p.NCH = (p.ncmp + 255) / 256;
+  p.NBC = (255 * c->cmp_stride + c->cmp_len - 1) / c->sel_block + 2;
+  p.NSLICE = (p.nblk + 511) / 512;
+  p.NSPLIT = (decode_max_tiles(c) + 3) / 4;
+  const size_t F = sizeof(float);
+  size_t off = 0;
+  p.cm = off;  off += align_up(BKV * p.NCH * 16 * F);
+  p.cl = off;  off += align_up(BKV * p.NCH * 16 * F);
+  p.co = off;  off += align_up(BKV * p.NCH * 16 * c->D * F);
+  p.cb = off;  off += align_up(BKV * p.NCH * 16 * p.NBC * F);
+  p.lse = off; off += align_up(BKV * 16 * F);
+  p.S = off;   off += align_up(BKV * p.nblk * F);
+  p.idx = off; off += align_up(BKV * c->top_n * 4);
+  p.pm = off;  off += align_up(BKV * p.NSPLIT * 2 * 16 * F);
+  p.pl = off;  off += align_up(BKV * p.NSPLIT * 2 * 16 * F);
+  p.po = off;  off += align_up(BKV * p.NSPLIT * 2 * 16 * c->D * F);
   p.total = off;
   return p;
 }
@@ -220,20 +268,60 @@ int nsa_prefill_timed(const nsa_config* c, const void* q, const void* k, const v
   return prefill_impl(c, q, k, v, wk, wv, gate, out, sel_idx, ws, ws_bytes, stream, events);
 }
 
+size_t nsa_decode_workspace_bytes(const nsa_config* cfg) {
+  if (check_nsa_decode(cfg) != NSA_OK) return 0;
+  return plan_decode(cfg).total;
+}
+
+int nsa_decode(const nsa_config* c, const void* q, const void* kcache, const void* vcache,
+               const void* kcmp, const void* vcmp, const int32_t* seqlens, const float* gate,
+               float* out, int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_nsa_decode(c);
+  if (st != NSA_OK) return st;
+  const DecodePlan p = plan_decode(c);
+  if (!q || !kcache || !vcache || !seqlens || !gate || !out || !ws ||
+      (p.ncmp > 0 && (!kcmp || !vcmp)))
+    return NSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(kcmp) ||
+      !aligned16(vcmp) || !aligned16(seqlens) || !aligned16(gate) || !aligned16(out) ||
+      !aligned16(ws) || (sel_idx && !aligned16(sel_idx)))
+    return NSA_ERR_INVALID_ARG;
+  if (ws_bytes < p.total) return NSA_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kcache = static_cast<const uint16_t*>(kcache);
+  a.vcache = static_cast<const uint16_t*>(vcache);
+  a.kc = static_cast<const uint16_t*>(kcmp);
+  a.vc = static_cast<const uint16_t*>(vcmp);
+  a.seqlens = seqlens;
+  a.gate = gate;
+  a.out = out;
+  a.idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(base + p.idx);
+  a.cm = reinterpret_cast<float*>(base + p.cm);
+  a.cl = reinterpret_cast<float*>(base + p.cl);
+  a.co = reinterpret_cast<float*>(base + p.co);
+  a.cb = reinterpret_cast<float*>(base + p.cb);
+  a.lse = reinterpret_cast<float*>(base + p.lse);
+  a.S = reinterpret_cast<float*>(base + p.S);
+  a.pm = reinterpret_cast<float*>(base + p.pm);
+  a.pl = reinterpret_cast<float*>(base + p.pl);
+  a.po = reinterpret_cast<float*>(base + p.po);
+  a.B = c->B; a.L = c->T; a.Hkv = c->Hkv; a.G = c->G; a.D = c->D;
+  a.l = c->cmp_len; a.d = c->cmp_stride; a.beta = c->sel_block; a.top_n = c->top_n;
+  a.n_local = c->n_local; a.window = c->window;
+  a.ncmp = p.ncmp; a.nblk = p.nblk; a.NCH = p.NCH; a.NBC = p.NBC; a.NSLICE = p.NSLICE;
+  a.NSPLIT = p.NSPLIT;
+  a.scale_log2 = c->scale * 1.4426950408889634f;
+  (void)hipGetLastError();
+  launch_decode(a, stream);
+  return hip_status();
+}
+
 }  // extern "C"
 
-// ---- decode and MoBA: kernels land in decode.hip / moba.hip
+// ---- MoBA: kernels land in moba.hip
 extern "C" {
-size_t nsa_decode_workspace_bytes(const nsa_config* cfg) {
-  if (check_nsa(cfg) != NSA_OK) return 0;
-  return 0;
-}
-int nsa_decode(const nsa_config* c, const void*, const void*, const void*, const void*,
-               const void*, const int32_t*, const float*, float*, int32_t*, void*, size_t,
-               hipStream_t) {
-  int st = check_nsa(c);
-  return st != NSA_OK ? st : NSA_ERR_UNSUPPORTED;
-}
 size_t moba_prefill_workspace_bytes(const moba_config* cfg) {
   if (check_moba(cfg) != NSA_OK) return 0;
   return 0;

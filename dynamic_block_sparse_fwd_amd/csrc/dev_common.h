@@ -92,7 +92,26 @@ __device__ __forceinline__ float group_sum(float v) {
 // Key offset (inside a 32-key chunk) of C-row r of sub-tile s, per the ordering above.
 __device__ __forceinline__ int perm_key(int r, int s) { return 8 * (r >> 2) + 4 * s + (r & 3); }
 
+// bf16 padding of LDS rows (16 bytes) against bank conflicts.
+constexpr int KPAD = 8;
+
+// Compressed tokens visible to query position t: token i covers [i*d, i*d + l) and is
+// visible once its whole span is in the past.
+__device__ __forceinline__ int n_visible(int t, int l, int d, int ncmp) {
+  if (t < l - 1) return 0;
+  const int n = (t - l + 1) / d + 1;
+  return n < ncmp ? n : ncmp;
+}
+
 __device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Ranking key of a non-negative score: larger score first, then lower index.
+__device__ __forceinline__ uint64_t rank_key(float score, int j) {
+  return (static_cast<uint64_t>(__float_as_uint(score)) << 32) | (0xFFFFFFFFu - (uint32_t)j);
+}
+__device__ __forceinline__ int rank_key_index(uint64_t key) {
+  return (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
+}
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
   uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o);

@@ -21,6 +21,35 @@ struct PrefillArgs {
   float scale_log2;     // softmax scale * log2(e)
 };
 
+struct DecodeArgs {
+  const uint16_t* q;       // [B, Hq, D]
+  const uint16_t* kcache;  // [B, Hkv, L, D]
+  const uint16_t* vcache;  // [B, Hkv, L, D]
+  const uint16_t* kc;      // [B, Hkv, ncmp, D]
+  const uint16_t* vc;      // [B, Hkv, ncmp, D]
+  const int32_t* seqlens;  // [B]
+  const float* gate;       // [B, Hq, 3]
+  float* out;              // [B, Hq, D]
+  int32_t* idx;            // [B, Hkv, top_n]
+  // workspace: per 256-token chunk of the compressed cache (16 row slots per group)
+  float* cm;  // [B*Hkv, NCH, 16] chunk max (log2 units)
+  float* cl;  // [B*Hkv, NCH, 16] sum of exp2(z - max)
+  float* co;  // [B*Hkv, NCH, 16, D] unnormalised output
+  float* cb;  // [B*Hkv, NCH, 16, NBC] block mass relative to the chunk max
+  float* lse; // [B*Hkv, 16]
+  float* S;   // [B*Hkv, nblk] group block scores
+  // per split of the selected/window tile list: [.., NSPLIT, 2 (slc, win), 16 (, D)]
+  float* pm;
+  float* pl;
+  float* po;
+  int B, L, Hkv, G, D;
+  int l, d, beta, top_n, n_local, window;
+  int ncmp, nblk, NCH, NBC, NSLICE, NSPLIT;
+  float scale_log2;
+};
+
+void launch_decode(const DecodeArgs& a, hipStream_t s);
+
 // x [BH, rows, cols] -> xt [BH, cols, rows_pad] (bf16), zero-filled for rows..rows_pad-1.
 void launch_transpose(const uint16_t* x, uint16_t* xt, int BH, int rows, int cols, int rows_pad,
                       hipStream_t s);

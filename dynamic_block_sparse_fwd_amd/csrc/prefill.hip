@@ -22,14 +22,6 @@ struct QTile {
   static constexpr int RTW = RT_ALL / NW;
 };
 
-constexpr int KPAD = 8;  // bf16 padding of LDS rows (16 bytes)
-
-__device__ __forceinline__ int n_visible(int t, int l, int d, int ncmp) {
-  if (t < l - 1) return 0;
-  int n = (t - l + 1) / d + 1;
-  return n < ncmp ? n : ncmp;
-}
-
 // Cooperative copy of a 64-row x D tile (row-major, 16-byte rows chunks) into LDS [64][D+KPAD].
 template <int D, int NT>
 __device__ __forceinline__ void load_rows_tile(u16 (*dst)[D + KPAD], const u16* src, long row0,

@@ -85,6 +85,9 @@ void onsa_compress(int B, int H, int T, int D, int l, int d, const uint16_t* x,
                    const uint16_t* w, uint16_t* xc_bits, double* xc_exact) {
   int n = onsa_n_cmp(T, l, d);
   long total = (long)B * H * n;
+  /* the weight as fp64, converted once (exact) */
+  double* wd = (double*)malloc(sizeof(double) * (size_t)l * D * D);
+  for (long a = 0; a < (long)l * D * D; ++a) wd[a] = bf(w[a]);
 #pragma omp parallel for schedule(dynamic, 4)
   for (long r = 0; r < total; ++r) {
     long bh = r / n;
@@ -94,8 +97,8 @@ void onsa_compress(int B, int H, int T, int D, int l, int d, const uint16_t* x,
       const uint16_t* xr = x + (bh * T + (long)i * d + j) * D;
       for (int e = 0; e < D; ++e) {
         double xv = bf(xr[e]);
-        const uint16_t* wr = w + ((long)j * D + e) * D;
-        for (int c = 0; c < D; ++c) acc[c] += xv * bf(wr[c]);
+        const double* wr = wd + ((long)j * D + e) * D;
+        for (int c = 0; c < D; ++c) acc[c] += xv * wr[c];
       }
     }
     for (int c = 0; c < D; ++c) {
@@ -104,6 +107,7 @@ void onsa_compress(int B, int H, int T, int D, int l, int d, const uint16_t* x,
     }
     free(acc);
   }
+  free(wd);
 }
 
 /* softmax attention of one query over an explicit key list; writes o[D], returns lse.

@@ -177,6 +177,112 @@ def cpu_baseline_prefill(x, T, rows=1024):
                       % (t_cmp, len(rt), step, t_rows)}
 
 
+# ----------------------------------------------------------------------------- decode
+
+def decode_kv_bytes(idx, seqlens, L, D, l=32, d=16, beta=64, w=512):
+    """Unique K+V bytes one decode step must read: every visible compressed token, and the
+    union of the selected blocks' and the window's tokens (causal), per (sequence, KV group)."""
+    B, Hkv, _ = idx.shape
+    cmp_b = 0
+    tok_b = 0
+    for b in range(B):
+        t = int(seqlens[b]) - 1
+        nvis = (t - l + 1) // d + 1 if t >= l - 1 else 0
+        for h in range(Hkv):
+            toks = set(range(max(0, t - w + 1), t + 1))
+            for j in idx[b, h]:
+                if j >= 0:
+                    toks.update(range(j * beta, min((j + 1) * beta, t + 1)))
+            tok_b += len(toks)
+            cmp_b += nvis
+    per_tok = 2 * D * 2  # K and V, bf16
+    return cmp_b * per_tok, tok_b * per_tok
+
+
+def bench_decode(args, B=32, L=65536, Hkv=4, G=16, D=128, seed=3, calls=20):
+    import torch
+
+    import dynamic_block_sparse_fwd_amd as nsa
+    import synth_inputs as S
+
+    cfg = nsa.NsaConfig(B, L, Hkv, G, D)
+    t0 = time.time()
+    x = S.nsa_decode_inputs(seed, B, L, Hkv, G, D)
+    print("[bench] decode inputs generated in %.1fs" % (time.time() - t0), file=sys.stderr,
+          flush=True)
+    dev = torch.device("cuda:0")
+    d = {k: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).to(dev)
+         for k, v in x.items()}
+    kc = nsa.nsa_compress(cfg, d["kcache"], d["wk"])
+    vc = nsa.nsa_compress(cfg, d["vcache"], d["wv"])
+    out = torch.empty((B, Hkv * G, D), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, Hkv, cfg.top_n), dtype=torch.int32, device=dev)
+    ws = torch.empty(nsa.decode_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    nst = len(nsa.DECODE_STAGES)
+
+    def call(events=None):
+        nsa.nsa_decode(cfg, d["q"], d["kcache"], d["vcache"], kc, vc, d["seqlens"], d["gate"],
+                       out=out, sel_idx=idx, ws=ws, events=events)
+
+    for _ in range(3):
+        call()
+    ev = HipEvents(calls * (nst + 1))
+    torch.cuda.synchronize()
+    for c in range(calls):
+        flush.zero_()  # evict the 256 MB Infinity Cache between calls (outside the events)
+        call(ev.group(c * (nst + 1), nst + 1))
+    torch.cuda.synchronize()
+    per_call = []
+    stage_ms = {nm: [] for nm in nsa.DECODE_STAGES}
+    for c in range(calls):
+        base = c * (nst + 1)
+        per_call.append(ev.elapsed_ms(base, base + nst))
+        for i, nm in enumerate(nsa.DECODE_STAGES):
+            stage_ms[nm].append(ev.elapsed_ms(base + i, base + i + 1))
+    ms = float(np.median(per_call))
+    cmp_bytes, tok_bytes = decode_kv_bytes(idx.cpu().numpy(), x["seqlens"], L, D)
+    kv = cmp_bytes + tok_bytes
+    med = {nm: float(np.median(v)) for nm, v in stage_ms.items()}
+    res = {
+        "workload": "nsa_decode B=%d L=%d Hkv=%d G=%d D=%d top16 window512" % (B, L, Hkv, G, D),
+        "us_per_step": round(ms * 1e3, 2),
+        "tok_s": round(B / (ms * 1e-3), 1),
+        "kv_bytes": kv,
+        "kv_gbs": round(kv / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(kv / (ms * 1e-3) / HBM_PEAK, 4),
+        "stages_us": {nm: round(v * 1e3, 2) for nm, v in med.items()},
+        "roofline": {"bound": "hbm", "kernel": "dec_cmp (compressed-cache stream)",
+                     "achieved": round(cmp_bytes / (med["cmp_stream"] * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": round(cmp_bytes / (med["cmp_stream"] * 1e-3) / HBM_PEAK, 4),
+                     "traffic": None},
+        "timing": "median of %d calls, HIP events around each call, 1 GiB written between "
+                  "calls to evict the Infinity Cache" % calls,
+    }
+    del d, kc, vc, out, idx, ws, flush
+    torch.cuda.empty_cache()
+    return res, x
+
+
+def cpu_baseline_decode(x, B=32, L=65536, Hkv=4, G=16, D=128, nseq=4):
+    """fp64 oracle decode of `nseq` of the B sequences (their compressed caches built by the
+    oracle, not timed: the decode call takes them as inputs), scaled to tokens/s."""
+    import oracle as O
+
+    sub = {k: (v[:nseq] if k in ("q", "kcache", "vcache", "gate", "seqlens") else v)
+           for k, v in x.items()}
+    kc = O.compress(sub["kcache"], x["wk"], 32, 16)
+    vc = O.compress(sub["vcache"], x["wv"], 32, 16)
+    cfg = O.NsaCfg(nseq, L, Hkv, G, D)
+    t0 = time.perf_counter()
+    O.nsa_decode(cfg, sub["q"], sub["kcache"], sub["vcache"], kc, vc, sub["seqlens"], sub["gate"])
+    dt = time.perf_counter() - t0
+    return {"value": nseq / dt, "unit": "tok/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle", "sample": "fp64 oracle decode of %d of the %d sequences "
+                                        "(compressed caches precomputed, untimed)" % (nseq, B)}
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -186,7 +292,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seq", type=int, default=65536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--no-decode", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the NSA/MoBA forward on a single "
@@ -220,6 +327,13 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(x, args.seq, args.cpu_rows)
+    del x
+    if not args.no_decode:
+        dec, xd = bench_decode(args)
+        if not args.no_cpu_baseline:
+            dec["cpu_baseline"] = cpu_baseline_decode(xd)
+        del xd
+        line["decode"] = dec
     print(json.dumps(line), flush=True)
 
 

@@ -57,6 +57,8 @@ EXPORTS = {
                           [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p,
                                                      ctypes.c_void_p]),
     "nsa_decode": (ctypes.c_int, [ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "nsa_decode_timed": (ctypes.c_int, [ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p,
+                                                                 ctypes.c_void_p]),
     "moba_prefill": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p]),
 }
 
@@ -238,9 +240,13 @@ def nsa_prefill(cfg: NsaConfig, q, k, v, wk, wv, gate, out=None, sel_idx=None, w
     return out, sel_idx
 
 
+DECODE_STAGES = ("cmp_stream", "scores", "select", "tiles", "combine")
+
+
 def nsa_decode(cfg: NsaConfig, q, kcache, vcache, kcmp, vcmp, seqlens, gate, out=None,
-               sel_idx=None, ws=None, want_idx=True, stream=None):
-    """cfg.T is the cache capacity.  Returns (out fp32 [B,Hq,D], sel_idx [B,Hkv,top_n])."""
+               sel_idx=None, ws=None, want_idx=True, stream=None, events=None):
+    """cfg.T is the cache capacity.  Returns (out fp32 [B,Hq,D], sel_idx [B,Hkv,top_n]).
+    events: optional ctypes array of len(DECODE_STAGES) + 1 hipEvent_t (nsa_decode_timed)."""
     torch = _torch()
     lib = load_library()
     c = cfg.c()
@@ -252,7 +258,9 @@ def nsa_decode(cfg: NsaConfig, q, kcache, vcache, kcmp, vcmp, seqlens, gate, out
         sel_idx = torch.empty((B, Hkv, cfg.top_n), dtype=torch.int32, device=dev)
     ws = _workspace(lib.nsa_decode_workspace_bytes(ctypes.byref(c)), dev, ws)
     bt = _bf16_types()
-    st = lib.nsa_decode(
+    fn = lib.nsa_decode if events is None else lib.nsa_decode_timed
+    extra = () if events is None else (ctypes.cast(events, ctypes.c_void_p),)
+    st = fn(
         ctypes.byref(c), _dev(q, "q", bt, (B, Hq, D)), _dev(kcache, "kcache", bt, (B, Hkv, L, D)),
         _dev(vcache, "vcache", bt, (B, Hkv, L, D)), _dev(kcmp, "kcmp", bt, (B, Hkv, cfg.ncmp, D)),
         _dev(vcmp, "vcmp", bt, (B, Hkv, cfg.ncmp, D)),
@@ -260,7 +268,7 @@ def nsa_decode(cfg: NsaConfig, q, kcache, vcache, kcmp, vcmp, seqlens, gate, out
         _dev(gate, "gate", (torch.float32,), (B, Hq, 3)),
         _dev(out, "out", (torch.float32,), (B, Hq, D)),
         None if sel_idx is None else _dev(sel_idx, "sel_idx", (torch.int32,), (B, Hkv, cfg.top_n)),
-        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream))
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream), *extra)
     _check(st, "nsa_decode")
     return out, sel_idx
 

@@ -65,8 +65,37 @@ int check_moba(const moba_config* c) {
     return NSA_ERR_INVALID_ARG;
   if (c->D != 64 && c->D != 128) return NSA_ERR_UNSUPPORTED;
   if (c->block % 64 != 0 || c->T % c->block != 0) return NSA_ERR_UNSUPPORTED;
-  if (c->top_k > 15) return NSA_ERR_UNSUPPORTED;
+  if (c->top_k > 8) return NSA_ERR_UNSUPPORTED;
+  if ((long)c->T > (1L << 27)) return NSA_ERR_UNSUPPORTED;
   return NSA_OK;
+}
+
+struct MobaPlan {
+  size_t vt, hi, lo, count, cursor, offset, tstart, ntiles, idx, list, po, pml, total;
+  int nb, max_tiles;
+};
+
+MobaPlan plan_moba(const moba_config* c) {
+  MobaPlan p{};
+  const size_t BH = (size_t)c->B * c->H, rows = BH * c->T;
+  p.nb = c->T / c->block;
+  const size_t entries = rows * c->top_k;
+  p.max_tiles = (int)(entries / 128 + BH * p.nb + 1);
+  size_t off = 0;
+  p.vt = off;     off += align_up(BH * c->D * c->T * 2);
+  p.hi = off;     off += align_up(BH * p.nb * c->D * 2);
+  p.lo = off;     off += align_up(BH * p.nb * c->D * 2);
+  p.count = off;  off += align_up(BH * p.nb * 4);
+  p.cursor = off; off += align_up(BH * p.nb * 4);
+  p.offset = off; off += align_up(BH * p.nb * 4);
+  p.tstart = off; off += align_up(BH * p.nb * 4);
+  p.ntiles = off; off += align_up(4);
+  p.idx = off;    off += align_up(rows * (c->top_k + 1) * 4);
+  p.list = off;   off += align_up(entries * 4 + 4);
+  p.po = off;     off += align_up(entries * c->D * 4 + 4);
+  p.pml = off;    off += align_up(entries * 2 * 4 + 4);
+  p.total = off;
+  return p;
 }
 
 struct PrefillPlan {
@@ -273,9 +302,10 @@ size_t nsa_decode_workspace_bytes(const nsa_config* cfg) {
   return plan_decode(cfg).total;
 }
 
-int nsa_decode(const nsa_config* c, const void* q, const void* kcache, const void* vcache,
-               const void* kcmp, const void* vcmp, const int32_t* seqlens, const float* gate,
-               float* out, int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+static int decode_impl(const nsa_config* c, const void* q, const void* kcache,
+                       const void* vcache, const void* kcmp, const void* vcmp,
+                       const int32_t* seqlens, const float* gate, float* out, int32_t* sel_idx,
+                       void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* ev) {
   int st = check_nsa_decode(c);
   if (st != NSA_OK) return st;
   const DecodePlan p = plan_decode(c);
@@ -314,23 +344,73 @@ int nsa_decode(const nsa_config* c, const void* q, const void* kcache, const voi
   a.NSPLIT = p.NSPLIT;
   a.scale_log2 = c->scale * 1.4426950408889634f;
   (void)hipGetLastError();
-  launch_decode(a, stream);
+  launch_decode(a, stream, ev);
   return hip_status();
+}
+
+int nsa_decode(const nsa_config* c, const void* q, const void* kcache, const void* vcache,
+               const void* kcmp, const void* vcmp, const int32_t* seqlens, const float* gate,
+               float* out, int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_impl(c, q, kcache, vcache, kcmp, vcmp, seqlens, gate, out, sel_idx, ws,
+                     ws_bytes, stream, nullptr);
+}
+
+int nsa_decode_timed(const nsa_config* c, const void* q, const void* kcache, const void* vcache,
+                     const void* kcmp, const void* vcmp, const int32_t* seqlens,
+                     const float* gate, float* out, int32_t* sel_idx, void* ws, size_t ws_bytes,
+                     hipStream_t stream, hipEvent_t* events) {
+  if (events == nullptr) return NSA_ERR_INVALID_ARG;
+  for (int i = 0; i <= NSA_DECODE_NSTAGES; ++i)
+    if (events[i] == nullptr) return NSA_ERR_INVALID_ARG;
+  return decode_impl(c, q, kcache, vcache, kcmp, vcmp, seqlens, gate, out, sel_idx, ws,
+                     ws_bytes, stream, events);
 }
 
 }  // extern "C"
 
-// ---- MoBA: kernels land in moba.hip
+// ---- MoBA
 extern "C" {
+
 size_t moba_prefill_workspace_bytes(const moba_config* cfg) {
   if (check_moba(cfg) != NSA_OK) return 0;
-  return 0;
+  return plan_moba(cfg).total;
 }
+
 int moba_prefill(const moba_config* c, const void* q, const void* k, const void* v, float* out,
-                 int32_t*, void* ws, size_t, hipStream_t) {
+                 int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_moba(c);
   if (st != NSA_OK) return st;
   if (!q || !k || !v || !out || !ws) return NSA_ERR_INVALID_ARG;
-  return NSA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(ws) ||
+      (sel_idx && !aligned16(sel_idx)))
+    return NSA_ERR_INVALID_ARG;
+  const MobaPlan p = plan_moba(c);
+  if (ws_bytes < p.total) return NSA_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  MobaArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.vt = reinterpret_cast<const uint16_t*>(base + p.vt);
+  a.out = out;
+  a.kb_hi = reinterpret_cast<uint16_t*>(base + p.hi);
+  a.kb_lo = reinterpret_cast<uint16_t*>(base + p.lo);
+  a.count = reinterpret_cast<int32_t*>(base + p.count);
+  a.cursor = reinterpret_cast<int32_t*>(base + p.cursor);
+  a.offset = reinterpret_cast<int32_t*>(base + p.offset);
+  a.tstart = reinterpret_cast<int32_t*>(base + p.tstart);
+  a.ntiles = reinterpret_cast<int32_t*>(base + p.ntiles);
+  a.list = reinterpret_cast<int32_t*>(base + p.list);
+  a.po = reinterpret_cast<float*>(base + p.po);
+  a.pml = reinterpret_cast<float*>(base + p.pml);
+  a.idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(base + p.idx);
+  a.B = c->B; a.T = c->T; a.H = c->H; a.D = c->D; a.block = c->block; a.top_k = c->top_k;
+  a.nb = p.nb; a.max_tiles = p.max_tiles;
+  a.scale_log2 = c->scale * 1.4426950408889634f;
+  (void)hipGetLastError();
+  launch_transpose(static_cast<const uint16_t*>(v), reinterpret_cast<uint16_t*>(base + p.vt),
+                   c->B * c->H, c->T, c->D, c->T, stream);
+  launch_moba(a, stream);
+  return hip_status();
 }
-}
+
+}  // extern "C"

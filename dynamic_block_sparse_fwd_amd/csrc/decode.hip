@@ -467,18 +467,27 @@ __global__ __launch_bounds__(256) void dec_combine_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------------ launcher
 
-void launch_decode(const DecodeArgs& a, hipStream_t s) {
+void launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
+  auto mark = [&](int i) {
+    if (ev != nullptr) (void)hipEventRecord(ev[i], s);
+  };
   const dim3 g1(a.NCH, a.Hkv, a.B);
+  mark(0);
   if (a.NCH > 0) {
     if (a.D == 128) dec_cmp_kernel<128><<<g1, 256, 0, s>>>(a);
     else dec_cmp_kernel<64><<<g1, 256, 0, s>>>(a);
   }
+  mark(1);
   dec_scores_kernel<<<dim3(a.NSLICE, a.Hkv, a.B), 256, 0, s>>>(a);
+  mark(2);
   dec_select_kernel<<<dim3(a.Hkv, a.B), 64, 0, s>>>(a);
+  mark(3);
   const dim3 g4(a.NSPLIT, a.Hkv, a.B);
   if (a.D == 128) dec_tiles_kernel<128><<<g4, 256, 0, s>>>(a);
   else dec_tiles_kernel<64><<<g4, 256, 0, s>>>(a);
+  mark(4);
   dec_combine_kernel<<<dim3((16 * a.D + 255) / 256, a.Hkv, a.B), 256, 0, s>>>(a);
+  mark(5);
 }
 
 }  // namespace nsa

@@ -48,7 +48,30 @@ struct DecodeArgs {
   float scale_log2;
 };
 
-void launch_decode(const DecodeArgs& a, hipStream_t s);
+// ev: nullptr or NSA_DECODE_NSTAGES + 1 events recorded around the stages.
+void launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev);
+
+struct MobaArgs {
+  const uint16_t* q;   // [B, T, H, D]
+  const uint16_t* k;   // [B, H, T, D]
+  const uint16_t* vt;  // [B*H, D, T] values, keys contiguous
+  float* out;          // [B, T, H, D]
+  int32_t* idx;        // [B, T, H, top_k + 1]
+  uint16_t* kb_hi;     // [B*H, nb, D] block key mean, bf16 high part
+  uint16_t* kb_lo;     // [B*H, nb, D] bf16 of the remainder
+  int32_t* count;      // [B*H*nb] queries that chose each block
+  int32_t* cursor;     // [B*H*nb] fill cursors
+  int32_t* offset;     // [B*H*nb] list offsets (exclusive prefix of count)
+  int32_t* tstart;     // [B*H*nb] first 128-row tile of each list
+  int32_t* ntiles;     // [1] total tiles
+  int32_t* list;       // [B*T*H*top_k] (t << 4 | slot)
+  float* po;           // [B*T*H, top_k, D] partial outputs (relative to the partial max)
+  float* pml;          // [B*T*H, top_k, 2] partial (max, sum), log2 units
+  int B, T, H, D, block, top_k, nb, max_tiles;
+  float scale_log2;
+};
+
+void launch_moba(const MobaArgs& a, hipStream_t s);
 
 // x [BH, rows, cols] -> xt [BH, cols, rows_pad] (bf16), zero-filled for rows..rows_pad-1.
 void launch_transpose(const uint16_t* x, uint16_t* xt, int BH, int rows, int cols, int rows_pad,

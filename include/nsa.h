@@ -154,6 +154,17 @@ int nsa_decode(const nsa_config* cfg, const void* q, const void* kcache, const v
                float* out, int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Instrumented nsa_decode: identical work, plus events[s] recorded before stage s and
+ * events[NSA_DECODE_NSTAGES] after the last.  Stages: 0 compressed-cache stream, 1 block
+ * scores, 2 selection, 3 selected + window tiles, 4 merge and gate.  For measurement only.
+ */
+#define NSA_DECODE_NSTAGES 5
+int nsa_decode_timed(const nsa_config* cfg, const void* q, const void* kcache,
+                     const void* vcache, const void* kcmp, const void* vcmp,
+                     const int32_t* seqlens, const float* gate, float* out, int32_t* sel_idx,
+                     void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* events);
+
+/*
  * MoBA prefill (podcast notes EP94 sections 9-10): per head, block keys are the mean of the
  * block's keys, the query scores past blocks by q . kbar, keeps the top_k (ties to the lower
  * index) plus its own block, and attends causally over their union with one softmax.

@@ -412,9 +412,11 @@ int omoba_prefill_rows(const omoba_cfg* cf, const uint16_t* q, const uint16_t* k
         } else {
           qsort(cs, (size_t)bcur, sizeof(cand), cand_cmp);
           for (int a = 0; a < cf->top_k; ++a) I[nI++] = cs[a].j;
-          double den = qn * kmax;
-          double sk = cs[cf->top_k - 1].s, sk1 = cs[cf->top_k].s;
-          gp = sk == sk1 ? 0.0 : (den > 0 ? (sk - sk1) / den : INFINITY);
+          if (cf->top_k > 0) { /* top_k = 0: nothing ranked, no gap */
+            double den = qn * kmax;
+            double sk = cs[cf->top_k - 1].s, sk1 = cs[cf->top_k].s;
+            gp = sk == sk1 ? 0.0 : (den > 0 ? (sk - sk1) / den : INFINITY);
+          }
         }
         I[nI++] = bcur;
       }

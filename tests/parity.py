@@ -66,3 +66,30 @@ def check_close(got, ref, what=""):
         what, mx, MAX_ABS, np.unravel_index(int(err.argmax()), err.shape))
     assert mean <= MEAN_ABS, "%s: mean-abs error %.3g > %g" % (what, mean, MEAN_ABS)
     return mx, mean
+
+
+def check_moba_idx(gpu_idx, ora, rows_t, block, top_k, den):
+    """MoBA indices: bit-exact, except near ties (oracle gap < 1e-4, the gap being normalised
+    by den = |q| * max_j |kbar_j| of the row/head) where every GPU-chosen past block must score
+    within 1e-4 * den of the oracle's k-th score.  Returns rows to re-run with GPU indices."""
+    gpu_idx = np.asarray(gpu_idx)
+    rerun, accepted = [], 0
+    for r in range(gpu_idx.shape[0]):
+        bad = np.nonzero((gpu_idx[r] != ora["idx"][r]).any(axis=-1))[0]
+        if len(bad) == 0:
+            continue
+        t = int(rows_t[r])
+        b = t // block
+        for h in bad:
+            msg = "row t=%d head %d: gpu %s oracle %s gap %.3g" % (
+                t, h, gpu_idx[r, h].tolist(), ora["idx"][r, h].tolist(), ora["gap"][r, h])
+            assert ora["gap"][r, h] < GAP_TOL, "index mismatch outside near-tie: " + msg
+            sc = ora["scores"][r, h, :b]
+            sk = np.sort(sc)[::-1][top_k - 1]
+            chosen = [j for j in gpu_idx[r, h] if j >= 0]
+            assert chosen[-1] == b and chosen == sorted(chosen) and len(chosen) == top_k + 1, msg
+            for j in chosen[:-1]:
+                assert sc[j] >= sk - GAP_TOL * den[r, h], "weak pick: " + msg
+            accepted += 1
+        rerun.append(r)
+    return rerun, accepted

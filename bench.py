@@ -283,6 +283,87 @@ def cpu_baseline_decode(x, B=32, L=65536, Hkv=4, G=16, D=128, nseq=4):
                                         "(compressed caches precomputed, untimed)" % (nseq, B)}
 
 
+# ----------------------------------------------------------------------------- MoBA
+
+def moba_work(T, H, D, block=512, top_k=3):
+    t = np.arange(T, dtype=np.int64)
+    b = t // block
+    pairs = (t - b * block + 1) + block * np.minimum(b, top_k)
+    gate = np.where(b > top_k, b, 0)
+    return 4.0 * D * H * pairs.sum(), 2.0 * D * H * gate.sum(), int(pairs.sum())
+
+
+def bench_moba(args, B=1, T=131072, H=32, D=128, seed=4, calls=5):
+    import torch
+
+    import dynamic_block_sparse_fwd_amd as nsa
+    import synth_inputs as S
+
+    cfg = nsa.MobaConfig(B, T, H, D, block=512, top_k=3)
+    t0 = time.time()
+    x = S.moba_inputs(seed, B, T, H, D)
+    print("[bench] MoBA inputs generated in %.1fs" % (time.time() - t0), file=sys.stderr,
+          flush=True)
+    dev = torch.device("cuda:0")
+    d = {k: torch.from_numpy(v.view(np.int16)).to(dev) for k, v in x.items()}
+    out = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, T, H, cfg.top_k + 1), dtype=torch.int32, device=dev)
+    ws = torch.empty(nsa.moba_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    nst = len(nsa.MOBA_STAGES)
+
+    def call(events=None):
+        nsa.moba_prefill(cfg, d["q"], d["k"], d["v"], out=out, sel_idx=idx, ws=ws, events=events)
+
+    call()
+    ev = HipEvents(calls * (nst + 1))
+    torch.cuda.synchronize()
+    for c in range(calls):
+        call(ev.group(c * (nst + 1), nst + 1))
+    torch.cuda.synchronize()
+    tot = [ev.elapsed_ms(c * (nst + 1), c * (nst + 1) + nst) for c in range(calls)]
+    stg = {nm: float(np.median([ev.elapsed_ms(c * (nst + 1) + i, c * (nst + 1) + i + 1)
+                                for c in range(calls)]))
+           for i, nm in enumerate(nsa.MOBA_STAGES)}
+    ms = float(np.median(tot))
+    f_att, f_gate, pairs = moba_work(T, H, D)
+    res = {
+        "workload": "moba_prefill B=%d T=%d H=%d D=%d block 512 top-3 + own" % (B, T, H, D),
+        "ms_per_step": round(ms, 4),
+        "tok_s": round(B * T / (ms * 1e-3), 1),
+        "algorithmic_tflop": round((f_att + f_gate) / 1e12, 4),
+        "mfma_frac_total": round((f_att + f_gate) / (ms * 1e-3) / MFMA_PEAK_BF16, 4),
+        "stages_ms": {k: round(v, 4) for k, v in stg.items()},
+        "roofline": {"bound": "mfma", "kernel": "block_attn + own_merge (attention)",
+                     "achieved": round(f_att / ((stg["block_attn"] + stg["own_merge"]) * 1e-3) / 1e12, 2),
+                     "peak": MFMA_PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                     "frac": round(f_att / ((stg["block_attn"] + stg["own_merge"]) * 1e-3) / MFMA_PEAK_BF16, 4),
+                     "traffic": None},
+        "timing": "median of %d calls, HIP events around each stage" % calls,
+    }
+    del d, out, idx, ws
+    torch.cuda.empty_cache()
+    return res, x
+
+
+def cpu_baseline_moba(x, T=131072, H=32, D=128, rows=1024):
+    import oracle as O
+
+    cfg = O.MobaCfg(1, T, H, D, block=512, top_k=3)
+    t0 = time.perf_counter()
+    kbar = O.moba_pool(cfg, x["k"])
+    t_pool = time.perf_counter() - t0
+    step = T // rows
+    rt = np.arange(step // 2, T, step, dtype=np.int32)
+    t0 = time.perf_counter()
+    O.moba_prefill_rows(cfg, x["q"], x["k"], x["v"], np.zeros_like(rt), rt, kbar=kbar)
+    t_rows = time.perf_counter() - t0
+    est = t_pool + t_rows * T / len(rt)
+    return {"value": T / est, "unit": "tok/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle", "sample": "fp64 oracle: block-key pooling (%.1fs) + %d positions "
+                                        "every %d-th, all 32 heads (%.1fs), scaled to %d"
+                                        % (t_pool, len(rt), step, t_rows, T)}
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -294,6 +375,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-moba", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the NSA/MoBA forward on a single "
@@ -334,6 +416,12 @@ def main():
             dec["cpu_baseline"] = cpu_baseline_decode(xd)
         del xd
         line["decode"] = dec
+    if not args.no_moba:
+        mo, xm = bench_moba(args)
+        if not args.no_cpu_baseline:
+            mo["cpu_baseline"] = cpu_baseline_moba(xm)
+        del xm
+        line["moba"] = mo
     print(json.dumps(line), flush=True)
 
 

@@ -60,6 +60,8 @@ EXPORTS = {
     "nsa_decode_timed": (ctypes.c_int, [ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p,
                                                                  ctypes.c_void_p]),
     "moba_prefill": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "moba_prefill_timed": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p,
+                                                                  ctypes.c_void_p]),
 }
 
 
@@ -273,9 +275,13 @@ def nsa_decode(cfg: NsaConfig, q, kcache, vcache, kcmp, vcmp, seqlens, gate, out
     return out, sel_idx
 
 
+MOBA_STAGES = ("pool_gate", "lists", "block_attn", "own_merge")
+
+
 def moba_prefill(cfg: MobaConfig, q, k, v, out=None, sel_idx=None, ws=None, want_idx=True,
-                 stream=None):
-    """Returns (out fp32 [B,T,H,D], sel_idx int32 [B,T,H,top_k+1])."""
+                 stream=None, events=None):
+    """Returns (out fp32 [B,T,H,D], sel_idx int32 [B,T,H,top_k+1]).
+    events: optional ctypes array of len(MOBA_STAGES) + 1 hipEvent_t (moba_prefill_timed)."""
     torch = _torch()
     lib = load_library()
     c = cfg.c()
@@ -287,10 +293,12 @@ def moba_prefill(cfg: MobaConfig, q, k, v, out=None, sel_idx=None, ws=None, want
         sel_idx = torch.empty((B, T, H, cfg.top_k + 1), dtype=torch.int32, device=dev)
     ws = _workspace(lib.moba_prefill_workspace_bytes(ctypes.byref(c)), dev, ws)
     bt = _bf16_types()
-    st = lib.moba_prefill(
+    fn = lib.moba_prefill if events is None else lib.moba_prefill_timed
+    extra = () if events is None else (ctypes.cast(events, ctypes.c_void_p),)
+    st = fn(
         ctypes.byref(c), _dev(q, "q", bt, (B, T, H, D)), _dev(k, "k", bt, (B, H, T, D)),
         _dev(v, "v", bt, (B, H, T, D)), _dev(out, "out", (torch.float32,), (B, T, H, D)),
         None if sel_idx is None else _dev(sel_idx, "sel_idx", (torch.int32,), (B, T, H, cfg.top_k + 1)),
-        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream))
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream), *extra)
     _check(st, "moba_prefill")
     return out, sel_idx

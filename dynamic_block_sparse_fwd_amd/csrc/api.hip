@@ -376,8 +376,9 @@ size_t moba_prefill_workspace_bytes(const moba_config* cfg) {
   return plan_moba(cfg).total;
 }
 
-int moba_prefill(const moba_config* c, const void* q, const void* k, const void* v, float* out,
-                 int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+static int moba_impl(const moba_config* c, const void* q, const void* k, const void* v,
+                     float* out, int32_t* sel_idx, void* ws, size_t ws_bytes,
+                     hipStream_t stream, hipEvent_t* ev) {
   int st = check_moba(c);
   if (st != NSA_OK) return st;
   if (!q || !k || !v || !out || !ws) return NSA_ERR_INVALID_ARG;
@@ -407,10 +408,25 @@ int moba_prefill(const moba_config* c, const void* q, const void* k, const void*
   a.nb = p.nb; a.max_tiles = p.max_tiles;
   a.scale_log2 = c->scale * 1.4426950408889634f;
   (void)hipGetLastError();
+  if (ev != nullptr) (void)hipEventRecord(ev[0], stream);
   launch_transpose(static_cast<const uint16_t*>(v), reinterpret_cast<uint16_t*>(base + p.vt),
                    c->B * c->H, c->T, c->D, c->T, stream);
-  launch_moba(a, stream);
+  launch_moba(a, stream, ev);
   return hip_status();
+}
+
+int moba_prefill(const moba_config* c, const void* q, const void* k, const void* v, float* out,
+                 int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return moba_impl(c, q, k, v, out, sel_idx, ws, ws_bytes, stream, nullptr);
+}
+
+int moba_prefill_timed(const moba_config* c, const void* q, const void* k, const void* v,
+                       float* out, int32_t* sel_idx, void* ws, size_t ws_bytes,
+                       hipStream_t stream, hipEvent_t* events) {
+  if (events == nullptr) return NSA_ERR_INVALID_ARG;
+  for (int i = 0; i <= NSA_MOBA_NSTAGES; ++i)
+    if (events[i] == nullptr) return NSA_ERR_INVALID_ARG;
+  return moba_impl(c, q, k, v, out, sel_idx, ws, ws_bytes, stream, events);
 }
 
 }  // extern "C"

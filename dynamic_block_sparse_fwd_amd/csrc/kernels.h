@@ -71,7 +71,8 @@ struct MobaArgs {
   float scale_log2;
 };
 
-void launch_moba(const MobaArgs& a, hipStream_t s);
+// ev: nullptr or NSA_MOBA_NSTAGES + 1 events; ev[0] is recorded by the caller.
+void launch_moba(const MobaArgs& a, hipStream_t s, hipEvent_t* ev);
 
 // x [BH, rows, cols] -> xt [BH, cols, rows_pad] (bf16), zero-filled for rows..rows_pad-1.
 void launch_transpose(const uint16_t* x, uint16_t* xt, int BH, int rows, int cols, int rows_pad,

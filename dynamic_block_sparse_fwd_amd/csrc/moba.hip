@@ -420,7 +420,10 @@ __global__ __launch_bounds__(128) void moba_own_kernel(MobaArgs a) {
   }
 }
 
-void launch_moba(const MobaArgs& a, hipStream_t s) {
+void launch_moba(const MobaArgs& a, hipStream_t s, hipEvent_t* ev) {
+  auto mark = [&](int i) {
+    if (ev != nullptr) (void)hipEventRecord(ev[i], s);
+  };
   const int n = a.B * a.H * a.nb;
   moba_zero_kernel<<<(n + 255) / 256, 256, 0, s>>>(a.count, a.cursor, n);
   const long rows = (long)a.B * a.T * a.H;
@@ -432,14 +435,18 @@ void launch_moba(const MobaArgs& a, hipStream_t s) {
     moba_pool_kernel<64><<<gp, 256, 0, s>>>(a);
     moba_gate_kernel<64><<<gq, 256, 0, s>>>(a);
   }
+  mark(1);
   moba_scan_kernel<<<1, 1024, 0, s>>>(a);
   moba_fill_kernel<<<(int)((rows + 255) / 256), 256, 0, s>>>(a);
+  mark(2);
   if (a.max_tiles > 0) {
     if (a.D == 128) moba_block_kernel<128><<<a.max_tiles, 256, 0, s>>>(a);
     else moba_block_kernel<64><<<a.max_tiles, 256, 0, s>>>(a);
   }
+  mark(3);
   if (a.D == 128) moba_own_kernel<128><<<gq, 128, 0, s>>>(a);
   else moba_own_kernel<64><<<gq, 128, 0, s>>>(a);
+  mark(4);
 }
 
 }  // namespace nsa

@@ -175,6 +175,16 @@ int nsa_decode_timed(const nsa_config* cfg, const void* q, const void* kcache,
 int moba_prefill(const moba_config* cfg, const void* q, const void* k, const void* v,
                  float* out, int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Instrumented moba_prefill: identical work, plus events[s] recorded before stage s and
+ * events[NSA_MOBA_NSTAGES] after the last.  Stages: 0 value transpose, pooling and gating,
+ * 1 per-block query lists, 2 block-major attention, 3 own block and merge.
+ */
+#define NSA_MOBA_NSTAGES 4
+int moba_prefill_timed(const moba_config* cfg, const void* q, const void* k, const void* v,
+                       float* out, int32_t* sel_idx, void* ws, size_t ws_bytes,
+                       hipStream_t stream, hipEvent_t* events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -134,3 +134,17 @@ def test_prefill_deterministic():
     o2, i2 = run_gpu_prefill(cfg, x)
     np.testing.assert_array_equal(i1, i2)
     np.testing.assert_array_equal(o1, o2)
+
+
+def test_prefill_64k_sampled_rows():
+    """The 64k prefill workload (B=1, T=65536, 4 KV heads x group 16, D=128), run exactly as
+    bench.py runs it; checked on 4096 positions: all t < 1024 (every visible block selected),
+    the last 64, and a seeded random remainder."""
+    B, T, Hkv, G, D = 1, 65536, 4, 16, 128
+    cfg = O.NsaCfg(B, T, Hkv, G, D)
+    x = S.nsa_prefill_inputs(2, B, T, Hkv, G, D)
+    gout, gidx = run_gpu_prefill(cfg, x)
+    rng = np.random.default_rng(2)
+    rest = rng.choice(np.arange(1024, T - 64), 4096 - 1024 - 64, replace=False)
+    rt = np.unique(np.concatenate([np.arange(1024), np.arange(T - 64, T), rest])).astype(np.int32)
+    compare_prefill(cfg, x, np.zeros_like(rt), rt, gout, gidx, "prefill 64k")

@@ -203,8 +203,8 @@ __global__ __launch_bounds__(256) void moba_fill_kernel(MobaArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) void moba_block_kernel(MobaArgs a) {
   constexpr int RTW = 2, DT = D / 16;
-  __shared__ u16 Ks[64][D + KPAD];
-  __shared__ u16 Vs[D][64 + KPAD];
+  __shared__ u16 Ks[64][D];
+  __shared__ u16 Vs[D][64];
   __shared__ int ent;
   const int tile = blockIdx.x;
   if (tile >= a.ntiles[0]) return;
@@ -312,8 +312,8 @@ __global__ __launch_bounds__(256) void moba_block_kernel(MobaArgs a) {
 template <int D>
 __global__ __launch_bounds__(128) void moba_own_kernel(MobaArgs a) {
   constexpr int RTW = 2, DT = D / 16;
-  __shared__ u16 Ks[64][D + KPAD];
-  __shared__ u16 Vs[D][64 + KPAD];
+  __shared__ u16 Ks[64][D];
+  __shared__ u16 Vs[D][64];
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;

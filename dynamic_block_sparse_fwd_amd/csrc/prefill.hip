@@ -45,14 +45,29 @@ __device__ __forceinline__ void load_q_frags(const PrefillArgs& a, int b, int kv
 
 // ------------------------------------------------------------------ compressed + selection
 
-template <int D, int G>
+// Block importance, fast geometry (sel_block = 4 * stride, cmp_len = 2 * stride): block j
+// receives p(4j-1)/2 + p(4j) + p(4j+1) + p(4j+2) + p(4j+3)/2.  A lane holds the 8 keys
+// 8*g4 .. 8*g4+7 of a 32-key chunk, i.e. the "core" p(4j) + p(4j+1) + p(4j+2) + p(4j+3)/2 of
+// two blocks and the half-key carries p(4j+3)/2 into the next block; cores and carries are
+// summed over the group's heads, and every block is assembled as core + carry in the same
+// order (exact ties stay exact).
+template <int G>
+__device__ __forceinline__ float head_sum(float v) {
+  if constexpr (G >= 16) return row16_sum(v);
+  else return group_sum<G>(v);
+}
+
+template <int D, int G, bool FAST>
 __global__ __launch_bounds__(QTile<G>::NW * 64) void cmp_select_kernel(PrefillArgs a) {
   using QT = QTile<G>;
   constexpr int NT = QT::NW * 64, TQ = QT::TQ, RTW = QT::RTW, DT = D / 16;
-  __shared__ u16 Ks[64][D + KPAD];
-  __shared__ u16 Vs[D][64 + KPAD];
-  __shared__ float Mb[TQ][64];
-  extern __shared__ float Sb[];  // [TQ][nblk]
+  __shared__ u16 Ks[64][D];
+  __shared__ u16 Vs[D][64];
+  __shared__ float Mb[FAST ? 1 : TQ][64];   // generic path: group mass per (t, key)
+  __shared__ float Cb[FAST ? TQ : 1][16];   // fast path: block cores of the tile
+  __shared__ float Hb[FAST ? TQ : 1][17];   // fast path: half-key carries into blocks 0..16
+  __shared__ float Pc[TQ];                  // fast path: carry into the tile's first block
+  extern __shared__ float Sb[];             // [TQ][nblk] group block scores
 
   const int tile = gridDim.x - 1 - blockIdx.x;  // longest rows first
   const int kvh = blockIdx.y, b = blockIdx.z;
@@ -61,6 +76,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void cmp_select_kernel(PrefillAr
   const int g4 = lane >> 4, r16 = lane & 15;
   const long bkv = (long)b * a.Hkv + kvh;
   const int nblk = a.nblk;
+  const float sl = a.scale_log2;
 
   bf16x8 qf[RTW][D / 32];
   int row_t[RTW], row_h[RTW], nvis[RTW];
@@ -71,125 +87,181 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void cmp_select_kernel(PrefillAr
 
   const int tlast = (t0 + TQ - 1 < a.T - 1) ? t0 + TQ - 1 : a.T - 1;
   const int nvis_max = n_visible(tlast, a.l, a.d, a.ncmp);
+  // keys below nvis_lo are visible to every row of the tile (rows past T see none)
+  const int nvis_lo = (t0 + TQ - 1 < a.T) ? n_visible(t0, a.l, a.d, a.ncmp) : 0;
   const int nkt = (nvis_max + 63) / 64;
   const u16* kc = a.kc + bkv * (long)a.NCP * D;
   const u16* vct = a.vct + bkv * (long)D * a.NCP;
 
   for (int e = threadIdx.x; e < TQ * nblk; e += NT) Sb[e] = 0.f;
+  if (threadIdx.x < TQ) Pc[threadIdx.x] = 0.f;
 
-  // Pass 1: per-row log-sum-exp (base 2) of the visible compressed logits.
+  // Pass 1: per-row max and sum of exp2 (per lane; merged over the row's four lanes below).
   float mrun[RTW], lrun[RTW];
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) { mrun[rt] = kNegInf; lrun[rt] = 0.f; }
+  KTileRegs<D, NT> kr;
+  VTileRegs<D, NT> vr;
+  if (nkt > 0) kr.load(kc, 0, a.NCP - 1);
   for (int kt = 0; kt < nkt; ++kt) {
     __syncthreads();
-    load_rows_tile<D, NT>(Ks, kc, (long)kt * 64, a.NCP - 1);
+    kr.store(Ks);
     __syncthreads();
+    if (kt + 1 < nkt) kr.load(kc, (long)(kt + 1) * 64, a.NCP - 1);
+    const bool full = (kt + 1) * 64 <= nvis_lo;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
-      float z[16];
+      float raw[16];
 #pragma unroll
       for (int kc2 = 0; kc2 < 2; ++kc2)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          f32x4 acc = score_subtile<D>(Ks, qf[rt], kc2, s, g4, r16);
+          const f32x4 acc = score_subtile<D>(Ks, qf[rt], kc2, s, g4, r16);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kt * 64 + 32 * kc2 + 8 * g4 + 4 * s + i;
-            z[kc2 * 8 + s * 4 + i] = key < nvis[rt] ? acc[i] * a.scale_log2 : kNegInf;
-          }
+          for (int i = 0; i < 4; ++i) raw[kc2 * 8 + s * 4 + i] = acc[i];
         }
-      float tm = z[0];
+      if (!full) {  // a real (uniform) branch: full tiles skip the masking arithmetic
+        __asm__ volatile("" ::: "memory");
 #pragma unroll
-      for (int e = 1; e < 16; ++e) tm = fmaxf(tm, z[e]);
+        for (int e = 0; e < 16; ++e) {
+          const int key = kt * 64 + 32 * (e >> 3) + 8 * g4 + (e & 7);
+          raw[e] = key < nvis[rt] ? raw[e] : kNegInf;
+        }
+      }
+      float tm = raw[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) tm = fmaxf(tm, raw[e]);
       const float mn = fmaxf(mrun[rt], tm);
       if (mn != kNegInf) {
+        const float msl = mn * sl;
         float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sum += fast_exp2(z[e] - mn);
-        lrun[rt] = lrun[rt] * fast_exp2(mrun[rt] - mn) + sum;
+        for (int e = 0; e < 16; ++e) sum += fast_exp2(fmaf(raw[e], sl, -msl));
+        lrun[rt] = lrun[rt] * fast_exp2(fmaf(mrun[rt], sl, -msl)) + sum;
         mrun[rt] = mn;
       }
     }
   }
-  // Row maximum and 1 / (sum of exp2(z - max)).  Pass 2 feeds the matrix core with
-  // p' = exp2(z - max) (largest term exactly 1 in bf16) and applies the normalisation in fp32.
+  // Row maximum (scaled, log2 units) and 1 / sum: pass 2 feeds the matrix core with
+  // p' = exp2(z - max) (largest term exactly 1 in bf16) and normalises in fp32.
   float rmax[RTW], rinv[RTW];
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
     const float M = col_max4(mrun[rt]);
-    const float part = (mrun[rt] == kNegInf) ? 0.f : lrun[rt] * fast_exp2(mrun[rt] - M);
+    const float part = (mrun[rt] == kNegInf) ? 0.f : lrun[rt] * fast_exp2((mrun[rt] - M) * sl);
     const float L = col_sum4(part);
-    rmax[rt] = (M == kNegInf) ? 0.f : M;  // no visible key: every p' is masked to 0
+    rmax[rt] = (M == kNegInf) ? 0.f : M * sl;  // no visible key: every p' is masked to 0
     rinv[rt] = (M == kNegInf) ? 0.f : 1.0f / L;
   }
 
-  // Pass 2: normalised probabilities -> o_cmp and per-(t, key) group mass -> block scores.
+  // Pass 2: normalised probabilities -> o_cmp and group block scores.
   f32x4 O[RTW][DT];
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
     for (int n = 0; n < DT; ++n) O[rt][n] = zero4();
   const float inv_l = 1.0f / (float)a.l;
-
+  if (nkt > 0) {
+    kr.load(kc, 0, a.NCP - 1);
+    vr.load(vct, a.NCP, 0);
+  }
   for (int kt = 0; kt < nkt; ++kt) {
     __syncthreads();
-    load_rows_tile<D, NT>(Ks, kc, (long)kt * 64, a.NCP - 1);
-    load_cols_tile<D, NT>(Vs, vct, a.NCP, (long)kt * 64);
+    kr.store(Ks);
+    vr.store(Vs);
     __syncthreads();
+    if (kt + 1 < nkt) {
+      kr.load(kc, (long)(kt + 1) * 64, a.NCP - 1);
+      vr.load(vct, a.NCP, (long)(kt + 1) * 64);
+    }
+    const bool full = (kt + 1) * 64 <= nvis_lo;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
+      const int r = (wave * RTW + rt) * 16 + r16;
 #pragma unroll
       for (int kc2 = 0; kc2 < 2; ++kc2) {
         float pv[8];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          f32x4 acc = score_subtile<D>(Ks, qf[rt], kc2, s, g4, r16);
+          const f32x4 acc = score_subtile<D>(Ks, qf[rt], kc2, s, g4, r16);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kt * 64 + 32 * kc2 + 8 * g4 + 4 * s + i;
-            pv[4 * s + i] = key < nvis[rt] ? fast_exp2(acc[i] * a.scale_log2 - rmax[rt]) : 0.f;
+          for (int i = 0; i < 4; ++i) pv[4 * s + i] = fast_exp2(fmaf(acc[i], sl, -rmax[rt]));
+        }
+        if (!full) {
+          __asm__ volatile("" ::: "memory");
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int key = kt * 64 + 32 * kc2 + 8 * g4 + e;
+            pv[e] = key < nvis[rt] ? pv[e] : 0.f;
           }
         }
         bf16x8 pb;
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pv[e];
         pv_chunk<D>(Vs, pb, kc2, g4, r16, O[rt]);
-        // group mass: normalised probabilities summed over the G heads (adjacent rows)
-        const int r = (wave * RTW + rt) * 16 + r16;
+        if constexpr (FAST) {
+          const float cA = head_sum<G>(((pv[0] + pv[1]) + pv[2] + 0.5f * pv[3]) * rinv[rt]);
+          const float cB = head_sum<G>(((pv[4] + pv[5]) + pv[6] + 0.5f * pv[7]) * rinv[rt]);
+          const float h3 = head_sum<G>((0.5f * pv[3]) * rinv[rt]);
+          const float h7 = head_sum<G>((0.5f * pv[7]) * rinv[rt]);
+          if ((r16 % G) == 0) {
+            const int tq = r / G, jl = 8 * kc2 + 2 * g4;
+            Cb[tq][jl] = cA;
+            Cb[tq][jl + 1] = cB;
+            Hb[tq][jl + 1] = h3;
+            Hb[tq][jl + 2] = h7;
+          }
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float hs = group_sum<(G < 16 ? G : 16)>(pv[e] * rinv[rt]);
-          if ((r16 % G) == 0) Mb[r / G][32 * kc2 + 8 * g4 + e] = hs;
+          for (int e = 0; e < 8; ++e) {
+            const float hs = head_sum<G>(pv[e] * rinv[rt]);
+            if ((r16 % G) == 0) Mb[r / G][32 * kc2 + 8 * g4 + e] = hs;
+          }
         }
       }
     }
     __syncthreads();
-    // Block importance: compressed token i covers tokens [i*d, i*d + l); its mass is spread
-    // evenly over those tokens and summed per block of `beta` tokens.
-    const int k0 = kt * 64;
-    const int jlo = (k0 * a.d) / a.beta;
-    int jhi = ((k0 + 63) * a.d + a.l - 1) / a.beta;
-    if (jhi > nblk - 1) jhi = nblk - 1;
-    const int nj = jhi - jlo + 1;
-    for (int pr = threadIdx.x; pr < TQ * nj; pr += NT) {
-      const int tq = pr / nj, j = jlo + pr % nj;
-      if (t0 + tq >= a.T) continue;
-      const int bs = j * a.beta, be = bs + a.beta;  // block tokens [bs, be)
-      int ilo = bs - a.l + 1 <= 0 ? 0 : (bs - a.l + 1 + a.d - 1) / a.d;
-      if (ilo < k0) ilo = k0;
-      int ihi = (be - 1) / a.d;
-      if (ihi > k0 + 63) ihi = k0 + 63;
-      // terms are added one by one in key order, so every block sees the same sequence of
-      // fp32 operations whether or not its keys straddle two key tiles (exact ties stay exact)
-      float sv = Sb[tq * nblk + j];
-      for (int i = ilo; i <= ihi; ++i) {
-        const int s0 = i * a.d, s1 = s0 + a.l;
-        const int ov = (s1 < be ? s1 : be) - (s0 > bs ? s0 : bs);
-        if (ov > 0) sv += Mb[tq][i - k0] * ((float)ov * inv_l);
+    if constexpr (FAST) {
+      // blocks 16*kt .. 16*kt + 15 are complete: core + carry (the carry of the first block
+      // comes from the previous tile)
+      for (int pr = threadIdx.x; pr < TQ * 16; pr += NT) {
+        const int tq = pr >> 4, jl = pr & 15, j = 16 * kt + jl;
+        if (t0 + tq >= a.T || j >= nblk) continue;
+        const float carry = jl == 0 ? Pc[tq] : Hb[tq][jl];
+        Sb[tq * nblk + j] = Cb[tq][jl] + carry;
+        if (jl == 0) Pc[tq] = Hb[tq][16];
       }
-      Sb[tq * nblk + j] = sv;
+    } else {
+      // compressed token i covers tokens [i*d, i*d + l); its mass is spread evenly over those
+      // tokens and summed per block of `beta` tokens; terms are added one by one in key order
+      const int k0 = kt * 64;
+      const int jlo = (k0 * a.d) / a.beta;
+      int jhi = ((k0 + 63) * a.d + a.l - 1) / a.beta;
+      if (jhi > nblk - 1) jhi = nblk - 1;
+      const int nj = jhi - jlo + 1;
+      for (int pr = threadIdx.x; pr < TQ * nj; pr += NT) {
+        const int tq = pr / nj, j = jlo + pr % nj;
+        if (t0 + tq >= a.T) continue;
+        const int bs = j * a.beta, be = bs + a.beta;
+        int ilo = bs - a.l + 1 <= 0 ? 0 : (bs - a.l + 1 + a.d - 1) / a.d;
+        if (ilo < k0) ilo = k0;
+        int ihi = (be - 1) / a.d;
+        if (ihi > k0 + 63) ihi = k0 + 63;
+        float sv = Sb[tq * nblk + j];
+        for (int i = ilo; i <= ihi; ++i) {
+          const int s0 = i * a.d, s1 = s0 + a.l;
+          const int ov = (s1 < be ? s1 : be) - (s0 > bs ? s0 : bs);
+          if (ov > 0) sv += Mb[tq][i - k0] * ((float)ov * inv_l);
+        }
+        Sb[tq * nblk + j] = sv;
+      }
     }
+  }
+  if constexpr (FAST) {
+    __syncthreads();
+    // the block after the last tile only has its carry
+    if (threadIdx.x < TQ && t0 + (int)threadIdx.x < a.T && 16 * nkt < nblk && nkt > 0)
+      Sb[threadIdx.x * nblk + 16 * nkt] = 0.f + Pc[threadIdx.x];
   }
 
   // o_cmp epilogue: out = g0 * o_cmp.  Lane holds O^T[d = 16n + 4*g4 + e][row r16].
@@ -232,11 +304,10 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void cmp_select_kernel(PrefillAr
       uint64_t best = 0;
       for (int m = 0, j = 1 + lane; j < flo; ++m, j += 64) {
         if (removed & (1u << m)) continue;
-        const uint64_t key = ((uint64_t)__float_as_uint(srow[j]) << 32) | (0xFFFFFFFFu - (uint32_t)j);
-        best = u64_max(best, key);
+        best = u64_max(best, rank_key(srow[j], j));
       }
       best = wave_max_u64(best);
-      const int jw = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+      const int jw = rank_key_index(best);
       if (((jw - 1) & 63) == lane) removed |= 1u << ((jw - 1) >> 6);
       if (lane == it) mine = jw;
     }
@@ -259,8 +330,8 @@ template <int D, int G>
 __global__ __launch_bounds__(QTile<G>::NW * 64) void window_kernel(PrefillArgs a) {
   using QT = QTile<G>;
   constexpr int NT = QT::NW * 64, TQ = QT::TQ, RTW = QT::RTW, DT = D / 16;
-  __shared__ u16 Ks[64][D + KPAD];
-  __shared__ u16 Vs[D][64 + KPAD];
+  __shared__ u16 Ks[64][D];
+  __shared__ u16 Vs[D][64];
 
   const int tile = blockIdx.x;
   const int kvh = blockIdx.y, b = blockIdx.z;
@@ -268,6 +339,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void window_kernel(PrefillArgs a
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
   const long bkv = (long)b * a.Hkv + kvh;
+  const float sl = a.scale_log2;
 
   bf16x8 qf[RTW][D / 32];
   int row_t[RTW], row_h[RTW];
@@ -276,6 +348,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void window_kernel(PrefillArgs a
   const int tlast = (t0 + TQ - 1 < a.T - 1) ? t0 + TQ - 1 : a.T - 1;
   const int kstart = t0 - a.window + 1 > 0 ? t0 - a.window + 1 : 0;
   const int kt0 = kstart / 64, kt1 = tlast / 64;
+  const bool alive = t0 + TQ - 1 < a.T;
   const u16* kb = a.k + bkv * (long)a.T * D;
   const u16* vtb = a.vt + bkv * (long)D * a.TP;
 
@@ -289,41 +362,55 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void window_kernel(PrefillArgs a
     for (int n = 0; n < DT; ++n) O[rt][n] = zero4();
   }
 
+  KTileRegs<D, NT> kr;
+  VTileRegs<D, NT> vr;
+  kr.load(kb, (long)kt0 * 64, a.T - 1);
+  vr.load(vtb, a.TP, (long)kt0 * 64);
   for (int kt = kt0; kt <= kt1; ++kt) {
     __syncthreads();
-    load_rows_tile<D, NT>(Ks, kb, (long)kt * 64, a.T - 1);
-    load_cols_tile<D, NT>(Vs, vtb, a.TP, (long)kt * 64);
+    kr.store(Ks);
+    vr.store(Vs);
     __syncthreads();
+    if (kt < kt1) {
+      kr.load(kb, (long)(kt + 1) * 64, a.T - 1);
+      vr.load(vtb, a.TP, (long)(kt + 1) * 64);
+    }
+    // keys of this tile are inside every row's window unless the tile touches either end
+    const bool full = alive && kt * 64 >= tlast - a.window + 1 && kt * 64 + 63 <= t0;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
       const int t = row_t[rt];
       const int lo = t - a.window + 1;
-      float z[16];
+      float raw[16];
 #pragma unroll
       for (int kc2 = 0; kc2 < 2; ++kc2)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          f32x4 acc = score_subtile<D>(Ks, qf[rt], kc2, s, g4, r16);
+          const f32x4 acc = score_subtile<D>(Ks, qf[rt], kc2, s, g4, r16);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kt * 64 + 32 * kc2 + 8 * g4 + 4 * s + i;
-            const bool ok = key <= t && key >= lo && t < a.T;
-            z[kc2 * 8 + s * 4 + i] = ok ? acc[i] * a.scale_log2 : kNegInf;
-          }
+          for (int i = 0; i < 4; ++i) raw[kc2 * 8 + s * 4 + i] = acc[i];
         }
-      float tm = z[0];
+      if (!full) {
+        __asm__ volatile("" ::: "memory");
 #pragma unroll
-      for (int e = 1; e < 16; ++e) tm = fmaxf(tm, z[e]);
+        for (int e = 0; e < 16; ++e) {
+          const int key = kt * 64 + 32 * (e >> 3) + 8 * g4 + (e & 7);
+          raw[e] = (key <= t && key >= lo && t < a.T) ? raw[e] : kNegInf;
+        }
+      }
+      float tm = raw[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) tm = fmaxf(tm, raw[e]);
       tm = col_max4(tm);
       const float mn = fmaxf(mrun[rt], tm);
       // A row with no visible key yet keeps m = -inf; exponentials then use 0 as reference
       // so every p is exactly 0 (no branch: the MFMAs below need the whole wave).
-      const float ms = (mn == kNegInf) ? 0.f : mn;
-      const float alpha = fast_exp2(mrun[rt] - ms);
+      const float msl = (mn == kNegInf) ? 0.f : mn * sl;
+      const float alpha = fast_exp2(fmaf(mrun[rt], sl, -msl));
       mrun[rt] = mn;
       float p[16], sum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) { p[e] = fast_exp2(z[e] - ms); sum += p[e]; }
+      for (int e = 0; e < 16; ++e) { p[e] = fast_exp2(fmaf(raw[e], sl, -msl)); sum += p[e]; }
       lrun[rt] = lrun[rt] * alpha + sum;
 #pragma unroll
       for (int n = 0; n < DT; ++n) O[rt][n] *= alpha;
@@ -481,13 +568,19 @@ static void launch_prefill_all(const PrefillArgs& a, int which, hipStream_t s) {
   const int ntile = (a.T + QT::TQ - 1) / QT::TQ;
   if (which == 0) {
     const size_t lds = cmp_lds<G>(a.nblk);
+    const bool fast = a.beta == 4 * a.d && a.l == 2 * a.d;
     static bool attr_set = false;  // opt in to the largest dynamic LDS the kernel may use
     if (!attr_set) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cmp_select_kernel<D, G>),
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cmp_select_kernel<D, G, true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cmp_select_kernel<D, G, false>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
       attr_set = true;
     }
-    cmp_select_kernel<D, G><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, lds, s>>>(a);
+    if (fast)
+      cmp_select_kernel<D, G, true><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, lds, s>>>(a);
+    else
+      cmp_select_kernel<D, G, false><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, lds, s>>>(a);
   } else if (which == 1) {
     window_kernel<D, G><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, 0, s>>>(a);
   } else {

@@ -242,7 +242,7 @@ def nsa_prefill(cfg: NsaConfig, q, k, v, wk, wv, gate, out=None, sel_idx=None, w
     return out, sel_idx
 
 
-DECODE_STAGES = ("cmp_stream", "scores", "select", "tiles", "combine")
+DECODE_STAGES = ("cmp_stream", "scores_select", "tiles", "combine")
 
 
 def nsa_decode(cfg: NsaConfig, q, kcache, vcache, kcmp, vcmp, seqlens, gate, out=None,

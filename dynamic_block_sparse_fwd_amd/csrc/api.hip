@@ -2,6 +2,7 @@
 // Everything is enqueued on the caller's stream; no host synchronisation, no allocation.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -51,10 +52,33 @@ int check_nsa(const nsa_config* c) {
 int decode_max_tiles(const nsa_config* c) {
   return c->top_n * (c->sel_block / 64) + (c->window + 63) / 64 + 1;
 }
+
+struct DecodeShape {
+  int ncmp, nblk, NCH, NT, NBT, NSPLIT;
+};
+
+DecodeShape decode_shape(const nsa_config* c) {
+  DecodeShape p{};
+  p.ncmp = nsa_num_compressed(c->T, c->cmp_len, c->cmp_stride);
+  p.nblk = (c->T + c->sel_block - 1) / c->sel_block;
+  const int chunk = decode_chunk_tokens();
+  p.NCH = (p.ncmp + chunk - 1) / chunk;
+  p.NT = (p.ncmp + 63) / 64;
+  p.NBT = (63 * c->cmp_stride + c->cmp_len - 1) / c->sel_block + 2;
+  p.NSPLIT = (decode_max_tiles(c) + 3) / 4;
+  return p;
+}
+
+// Decode stages per-chunk statistics and the group's block scores in LDS (160 KB) and
+// addresses a cache row with 32-bit offsets.
 int check_nsa_decode(const nsa_config* c) {
   int st = check_nsa_base(c);
   if (st != NSA_OK) return st;
-  if (decode_max_tiles(c) > 160) return NSA_ERR_UNSUPPORTED;
+  if (c->T > (1 << 24)) return NSA_ERR_UNSUPPORTED;
+  if (decode_max_tiles(c) > decode_max_tile_list()) return NSA_ERR_UNSUPPORTED;
+  const DecodeShape p = decode_shape(c);
+  if (p.NSPLIT > decode_max_splits()) return NSA_ERR_UNSUPPORTED;
+  if (decode_select_lds_bytes(p.NCH, p.nblk) > 160 * 1024) return NSA_ERR_UNSUPPORTED;
   return NSA_OK;
 }
 
@@ -122,31 +146,29 @@ PrefillPlan plan_prefill(const nsa_config* c) {
 }
 
 struct DecodePlan {
-  size_t cm, cl, co, cb, lse, S, idx, pm, pl, po, total;
-  int ncmp, nblk, NCH, NBC, NSLICE, NSPLIT;
+  size_t cm, cl, co, tref, cb, lse, idx, tl, tn, pm, pl, po, total;
+  DecodeShape sh;
 };
 
 DecodePlan plan_decode(const nsa_config* c) {
   DecodePlan p{};
+  p.sh = decode_shape(c);
+  const DecodeShape& d = p.sh;
   const size_t BKV = (size_t)c->B * c->Hkv;
-  p.ncmp = nsa_num_compressed(c->T, c->cmp_len, c->cmp_stride);
-  p.nblk = (c->T + c->sel_block - 1) / c->sel_block;
-  p.NCH = (p.ncmp + 255) / 256;
-  p.NBC = (255 * c->cmp_stride + c->cmp_len - 1) / c->sel_block + 2;
-  p.NSLICE = (p.nblk + 511) / 512;
-  p.NSPLIT = (decode_max_tiles(c) + 3) / 4;
   const size_t F = sizeof(float);
   size_t off = 0;
-  p.cm = off;  off += align_up(BKV * p.NCH * 16 * F);
-  p.cl = off;  off += align_up(BKV * p.NCH * 16 * F);
-  p.co = off;  off += align_up(BKV * p.NCH * 16 * c->D * F);
-  p.cb = off;  off += align_up(BKV * p.NCH * 16 * p.NBC * F);
-  p.lse = off; off += align_up(BKV * 16 * F);
-  p.S = off;   off += align_up(BKV * p.nblk * F);
-  p.idx = off; off += align_up(BKV * c->top_n * 4);
-  p.pm = off;  off += align_up(BKV * p.NSPLIT * 2 * 16 * F);
-  p.pl = off;  off += align_up(BKV * p.NSPLIT * 2 * 16 * F);
-  p.po = off;  off += align_up(BKV * p.NSPLIT * 2 * 16 * c->D * F);
+  p.cm = off;   off += align_up(BKV * d.NCH * 16 * F);
+  p.cl = off;   off += align_up(BKV * d.NCH * 16 * F);
+  p.co = off;   off += align_up(BKV * d.NCH * 16 * c->D * F);
+  p.tref = off; off += align_up(BKV * d.NT * 16 * F);
+  p.cb = off;   off += align_up(BKV * d.NT * d.NBT * 16 * F);
+  p.lse = off;  off += align_up(BKV * 16 * F);
+  p.idx = off;  off += align_up(BKV * c->top_n * 4);
+  p.tl = off;   off += align_up(BKV * decode_max_tile_list() * 4);
+  p.tn = off;   off += align_up(BKV * 4);
+  p.pm = off;   off += align_up(BKV * d.NSPLIT * 2 * 16 * F);
+  p.pl = off;   off += align_up(BKV * d.NSPLIT * 2 * 16 * F);
+  p.po = off;   off += align_up(BKV * d.NSPLIT * 2 * 16 * c->D * F);
   p.total = off;
   return p;
 }
@@ -310,7 +332,7 @@ static int decode_impl(const nsa_config* c, const void* q, const void* kcache,
   if (st != NSA_OK) return st;
   const DecodePlan p = plan_decode(c);
   if (!q || !kcache || !vcache || !seqlens || !gate || !out || !ws ||
-      (p.ncmp > 0 && (!kcmp || !vcmp)))
+      (p.sh.ncmp > 0 && (!kcmp || !vcmp)))
     return NSA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(kcmp) ||
       !aligned16(vcmp) || !aligned16(seqlens) || !aligned16(gate) || !aligned16(out) ||
@@ -331,17 +353,19 @@ static int decode_impl(const nsa_config* c, const void* q, const void* kcache,
   a.cm = reinterpret_cast<float*>(base + p.cm);
   a.cl = reinterpret_cast<float*>(base + p.cl);
   a.co = reinterpret_cast<float*>(base + p.co);
+  a.tref = reinterpret_cast<float*>(base + p.tref);
   a.cb = reinterpret_cast<float*>(base + p.cb);
   a.lse = reinterpret_cast<float*>(base + p.lse);
-  a.S = reinterpret_cast<float*>(base + p.S);
+  a.tl = reinterpret_cast<int32_t*>(base + p.tl);
+  a.tn = reinterpret_cast<int32_t*>(base + p.tn);
   a.pm = reinterpret_cast<float*>(base + p.pm);
   a.pl = reinterpret_cast<float*>(base + p.pl);
   a.po = reinterpret_cast<float*>(base + p.po);
   a.B = c->B; a.L = c->T; a.Hkv = c->Hkv; a.G = c->G; a.D = c->D;
   a.l = c->cmp_len; a.d = c->cmp_stride; a.beta = c->sel_block; a.top_n = c->top_n;
   a.n_local = c->n_local; a.window = c->window;
-  a.ncmp = p.ncmp; a.nblk = p.nblk; a.NCH = p.NCH; a.NBC = p.NBC; a.NSLICE = p.NSLICE;
-  a.NSPLIT = p.NSPLIT;
+  a.ncmp = p.sh.ncmp; a.nblk = p.sh.nblk; a.NCH = p.sh.NCH; a.NT = p.sh.NT; a.NBT = p.sh.NBT;
+  a.NSPLIT = p.sh.NSPLIT;
   a.scale_log2 = c->scale * 1.4426950408889634f;
   (void)hipGetLastError();
   launch_decode(a, stream, ev);

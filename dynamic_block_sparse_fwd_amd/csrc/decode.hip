@@ -4,67 +4,94 @@
 // serves the group's heads).  Every phase streams HBM; the matrix core does the contractions
 // with the group's heads as the 16 MFMA rows.
 //
-//   dec_cmp_kernel     split-K over the compressed cache: per 256-token chunk, per head,
-//                      (max, sum, unnormalised output) and per-block probability mass
-//   dec_scores_kernel  per-head log-sum-exp, then group block scores for a slice of blocks
-//   dec_select_kernel  top-n with forced block 0 + local blocks (one wave)
-//   dec_tiles_kernel   selected blocks and window as one de-duplicated list of 64-token
-//                      tiles; each tile is read once and feeds whichever branches use it
-//   dec_combine_kernel merges all partials and applies the gate
+//   dec_cmp_kernel     split-K over the compressed cache: each wave streams TPW 64-token tiles
+//                      with register prefetch and an online softmax; per 1024-token chunk, per
+//                      head, (max, sum, unnormalised output); per tile, the probability mass of
+//                      every selection block it touches, relative to a per-tile reference
+//   dec_select_kernel  per (sequence, group): per-head log-sum-exp, every group block score,
+//                      the top-n (forced block 0 + local blocks) and the list of selected and
+//                      window tiles, each tile once
+//   dec_tiles_kernel   one wave per listed tile: the tile is read once and feeds whichever of
+//                      the selected and window branches use it
+//   dec_combine_kernel normalises the compressed output, merges all partials, applies the gate
+#include "attn_tile.h"
 #include "dev_common.h"
 #include "kernels.h"
 
 namespace nsa {
 
-constexpr int CHUNK = 256;  // compressed tokens per dec_cmp workgroup (4 waves x 64)
+constexpr int TPW = 4;               // 64-token tiles per wave in dec_cmp
+constexpr int CHUNK = 4 * TPW * 64;  // compressed tokens per dec_cmp workgroup
+constexpr int kMaxTiles = 160;       // selected + window tiles per group
+constexpr int kMaxSplits = 64;       // 4-tile splits of that list
 
-// Loads this wave's 64-key tile of a [rows, D] bf16 matrix (rows clamped to `last`) into LDS
-// transposed, Vt[d][key], four keys per 8-byte store.
+// One 64-key tile of a [rows, D] K/V cache pair in registers: K in MFMA A-operand order, V in
+// the gather order of the transposing LDS store.  Rows past `last` are clamped to it.
 template <int D>
-__device__ __forceinline__ void stage_vt(u16 (*Vt)[64 + KPAD], const u16* src, int k0, int last,
-                                         int lane) {
-  constexpr int DC = D / 8;
-  for (int it = lane; it < 16 * DC; it += 64) {
-    const int kq = it / DC, dc = it % DC;
-    uint32_t v[4][4];  // four keys x 8 features, as 32-bit words (2 features each)
+struct DecTile {
+  static constexpr int NK = D / 8, NV = D / 8, DC = D / 8;
+  u32x4 k[NK], v[NV];
+
+  __device__ __forceinline__ void load(const u16* kb, const u16* vb, int k0, int last,
+                                       int lane) {
+    const int g4 = lane >> 4, r16 = lane & 15;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int row = k0 + 4 * kq + r;
-      row = row < last ? row : last;
-      const uint4 w = *reinterpret_cast<const uint4*>(src + (long)row * D + 8 * dc);
-      v[r][0] = w.x; v[r][1] = w.y; v[r][2] = w.z; v[r][3] = w.w;
-    }
+    for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int sh = (e & 1) * 16;
-      const uint32_t h0 = (v[0][e >> 1] >> sh) & 0xFFFFu, h1 = (v[1][e >> 1] >> sh) & 0xFFFFu;
-      const uint32_t h2 = (v[2][e >> 1] >> sh) & 0xFFFFu, h3 = (v[3][e >> 1] >> sh) & 0xFFFFu;
-      uint2 pk;
-      pk.x = h0 | (h1 << 16);
-      pk.y = h2 | (h3 << 16);
-      *reinterpret_cast<uint2*>(&Vt[8 * dc + e][4 * kq]) = pk;
+      for (int s = 0; s < 2; ++s) {
+        int row = k0 + 32 * kc + perm_key(r16, s);
+        row = row < last ? row : last;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+          k[(kc * 2 + s) * (D / 32) + c] = *reinterpret_cast<const u32x4*>(
+              kb + ((uint32_t)row * D + 8 * g4 + 32 * c));
+      }
+#pragma unroll
+    for (int it = 0; it < DC / 4; ++it) {
+      const int x = it * 64 + lane, kq = x & 15, dc = x >> 4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int row = k0 + 4 * kq + r;
+        row = row < last ? row : last;
+        v[it * 4 + r] = *reinterpret_cast<const u32x4*>(vb + ((uint32_t)row * D + 8 * dc));
+      }
     }
   }
-}
 
-// S^T for a 64-key tile whose K rows are read straight from global memory (16-byte loads);
-// z[kc*8 + s*4 + i] belongs to key k0 + 32*kc + 8*g4 + 4*s + i.
-template <int D>
-__device__ __forceinline__ void tile_scores(const u16* kb, int k0, int last, const bf16x8* qf,
-                                            int g4, int r16, f32x4* acc) {
+  // S^T = K Q^T; acc[kc*2 + s][i] belongs to key 32*kc + 8*g4 + 4*s + i of the tile.
+  __device__ __forceinline__ void scores(const bf16x8* qf, f32x4* acc) const {
 #pragma unroll
-  for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      int row = k0 + 32 * kc + perm_key(r16, s);
-      row = row < last ? row : last;
-      const u16* kp = kb + (long)row * D + 8 * g4;
+    for (int q = 0; q < 4; ++q) {
       f32x4 a = zero4();
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) a = mfma16x16x32(load8(kp + 32 * c), qf[c], a);
-      acc[kc * 2 + s] = a;
+      for (int c = 0; c < D / 32; ++c)
+        a = mfma16x16x32(__builtin_bit_cast(bf16x8, k[q * (D / 32) + c]), qf[c], a);
+      acc[q] = a;
     }
-}
+  }
+
+  // V^T into LDS, Vt[d][key], in the V-tile swizzle of attn_tile.h (8-key chunk c of feature
+  // row d at chunk c ^ (d & 7)), four keys per 8-byte store.  The 16 lanes of a row hold 16
+  // key quads of one feature octet, so each store instruction covers whole LDS rows.
+  __device__ __forceinline__ void stage(u16 (*Vt)[64], int lane) const {
+#pragma unroll
+    for (int it = 0; it < DC / 4; ++it) {
+      const int x = it * 64 + lane, kq = x & 15, dc = x >> 4;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) * 16, d = 8 * dc + e;
+        const uint32_t h0 = (v[it * 4 + 0][e >> 1] >> sh) & 0xFFFFu;
+        const uint32_t h1 = (v[it * 4 + 1][e >> 1] >> sh) & 0xFFFFu;
+        const uint32_t h2 = (v[it * 4 + 2][e >> 1] >> sh) & 0xFFFFu;
+        const uint32_t h3 = (v[it * 4 + 3][e >> 1] >> sh) & 0xFFFFu;
+        uint2 pk;
+        pk.x = h0 | (h1 << 16);
+        pk.y = h2 | (h3 << 16);
+        *reinterpret_cast<uint2*>(&Vt[d][(((kq >> 1) ^ (d & 7)) * 8) + (kq & 1) * 4]) = pk;
+      }
+    }
+  }
+};
 
 template <int D>
 __device__ __forceinline__ void load_q_decode(const DecodeArgs& a, int b, int kvh, int lane,
@@ -76,173 +103,184 @@ __device__ __forceinline__ void load_q_decode(const DecodeArgs& a, int b, int kv
   for (int c = 0; c < D / 32; ++c) qf[c] = hlive ? load8(qp + 32 * c + 8 * g4) : zero8();
 }
 
-// ------------------------------------------------------------------ phase 1: compressed stream
+// Key (tile-relative) of this lane's score e = 4*q4 + i.
+__device__ __forceinline__ int lane_key(int q4, int i, int g4) {
+  return 32 * (q4 >> 1) + 8 * g4 + 4 * (q4 & 1) + i;
+}
 
+// O^T += V^T P^T over one 64-key tile staged in Vt (16 probabilities per lane).
 template <int D>
-__global__ __launch_bounds__(256) void dec_cmp_kernel(DecodeArgs a) {
-  __shared__ u16 Vt[4][D][64 + KPAD];
-  __shared__ float Pw[4][16][64];
-  __shared__ float Wm[4][16], Wl[4][16];
-  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int t = a.seqlens[b] - 1;
-  const int nvis = n_visible(t, a.l, a.d, a.ncmp);
-  const int c0 = chunk * CHUNK;
-  if (c0 >= nvis) return;  // uniform across the workgroup
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g4 = lane >> 4, r16 = lane & 15;
-  const long bkv = (long)b * a.Hkv + kvh;
-  const int k0 = c0 + 64 * wave;
-  const u16* kcb = a.kc + bkv * a.ncmp * D;
-  const u16* vcb = a.vc + bkv * a.ncmp * D;
-
-  bf16x8 qf[D / 32];
-  load_q_decode<D>(a, b, kvh, lane, qf);
-  f32x4 acc[4];
-  tile_scores<D>(kcb, k0, nvis - 1, qf, g4, r16, acc);
-  stage_vt<D>(Vt[wave], vcb, k0, nvis - 1, lane);
-
-  float z[16];
-#pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = k0 + 32 * (q4 >> 1) + 8 * g4 + 4 * (q4 & 1) + i;
-      z[q4 * 4 + i] = key < nvis ? acc[q4][i] * a.scale_log2 : kNegInf;
-    }
-  float tm = z[0];
-#pragma unroll
-  for (int e = 1; e < 16; ++e) tm = fmaxf(tm, z[e]);
-  tm = col_max4(tm);
-  const float ms = tm == kNegInf ? 0.f : tm;
-  float p[16], ls = 0.f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) { p[e] = fast_exp2(z[e] - ms); ls += p[e]; }
-  ls = col_sum4(ls);
-  __syncthreads();  // Vt staged by the whole wave
-
-  constexpr int DT = D / 16;
-  f32x4 O[DT];
-#pragma unroll
-  for (int n = 0; n < DT; ++n) O[n] = zero4();
+__device__ __forceinline__ void tile_pv(const u16 (*Vt)[64], const float* p, int g4, int r16,
+                                        f32x4* O) {
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc) {
     bf16x8 pb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[kc * 8 + e];
-#pragma unroll
-    for (int n = 0; n < DT; ++n)
-      O[n] = mfma16x16x32(load8(&Vt[wave][16 * n + r16][32 * kc + 8 * g4]), pb, O[n]);
+    pv_chunk<D>(Vt, pb, kc, g4, r16, O);
   }
-#pragma unroll
-  for (int e = 0; e < 16; ++e) Pw[wave][r16][32 * (e >> 3) + 8 * g4 + (e & 7)] = p[e];
-  if (g4 == 0) { Wm[wave][r16] = tm; Wl[wave][r16] = ls; }
-  __syncthreads();
+}
 
-  // merge the four tiles: chunk max, rescaled sums and outputs
-  float sc[4];
+// First and last compressed token whose span [i*d, i*d + l) overlaps block j.
+__device__ __forceinline__ int block_tok_lo(int j, int beta, int l, int d) {
+  const int x = j * beta - l + 1;
+  return x <= 0 ? 0 : (x + d - 1) / d;
+}
+__device__ __forceinline__ int block_tok_hi(int j, int beta, int d) {
+  return ((j + 1) * beta - 1) / d;
+}
+
+// ------------------------------------------------------------------ phase 1: compressed stream
+
+// FAST: sel_block = 4 * stride and cmp_len = 2 * stride, where block j receives
+// p(4j-1)/2 + p(4j) + p(4j+1) + p(4j+2) + p(4j+3)/2: the lane holding keys 4jl..4jl+3 of a
+// tile forms the block's core, and the half-token carries cross lanes by shuffles.
+template <int D, bool FAST>
+__global__ __launch_bounds__(256, FAST ? 2 : 1) void dec_cmp_kernel(DecodeArgs a) {
+  constexpr int DT = D / 16, OP = D + 4;
+  __shared__ __align__(16) u16 Vt[4][D][64];
+  __shared__ float Wm[4][16], Wl[4][16];
+  __shared__ float Pw[FAST ? 1 : 4][FAST ? 1 : 16][64];
+  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int t = a.seqlens[b] - 1;
+  const int nvis = n_visible(t, a.l, a.d, a.ncmp);
+  const int c0 = chunk * CHUNK;
+  const long bkv = (long)b * a.Hkv + kvh;
+  if (c0 >= nvis) return;  // uniform across the workgroup
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const u16* kcb = a.kc + bkv * a.ncmp * D;
+  const u16* vcb = a.vc + bkv * a.ncmp * D;
+  const float sl = a.scale_log2;
+
+  bf16x8 qf[D / 32];
+  load_q_decode<D>(a, b, kvh, lane, qf);
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 O[DT];
+#pragma unroll
+  for (int n = 0; n < DT; ++n) O[n] = zero4();
+
+  // wave w takes tiles c0/64 + w, + 4, + 8, ... (the four waves read adjacent tiles together)
+  const int tile0 = (c0 >> 6) + wave;
+  DecTile<D> cur;
+  if (tile0 * 64 < nvis) cur.load(kcb, vcb, tile0 * 64, nvis - 1, lane);
+#pragma unroll 1
+  for (int it = 0; it < TPW; ++it) {
+    const int tile = tile0 + 4 * it;
+    const int k0 = tile * 64;
+    if (k0 >= nvis) break;  // wave-uniform
+    f32x4 acc[4];
+    cur.scores(qf, acc);
+    __asm__ volatile("" ::: "memory");  // the previous tile's Vt reads stay before these writes
+    cur.stage(Vt[wave], lane);
+    if (it + 1 < TPW && k0 + 256 < nvis) cur.load(kcb, vcb, k0 + 256, nvis - 1, lane);
+
+    float p[16];
+    float tm = kNegInf;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float r = k0 + lane_key(q4, i, g4) < nvis ? acc[q4][i] : kNegInf;
+        p[q4 * 4 + i] = r;
+        tm = fmaxf(tm, r);
+      }
+    tm = col_max4(tm);
+    const float m_new = fmaxf(m_run, tm);  // finite: the tile holds a visible key
+    const float ms = m_new * sl;
+    const float alpha = fast_exp2(fmaf(m_run, sl, -ms));
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = fast_exp2(fmaf(p[e], sl, -ms));
+      ls += p[e];
+    }
+    ls = col_sum4(ls);
+    l_run = fmaf(l_run, alpha, ls);
+    m_run = m_new;
+#pragma unroll
+    for (int n = 0; n < DT; ++n) O[n] *= alpha;
+    __asm__ volatile("" ::: "memory");  // Vt written by this wave before its reads
+    tile_pv<D>(Vt[wave], p, g4, r16, O);
+
+    // block masses of this tile, relative to exp2(ms)
+    const long tix = bkv * a.NT + tile;
+    if (g4 == 0) a.tref[tix * 16 + r16] = ms;
+    float* cbt = a.cb + tix * a.NBT * 16;
+    if constexpr (FAST) {
+      float core[2][2], cout[2][2];
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const float* q = p + 8 * kc + 4 * s;
+          core[kc][s] = (q[0] + q[1]) + q[2] + 0.5f * q[3];
+          cout[kc][s] = 0.5f * q[3];
+        }
+      // lane (g4, kc, s) holds block 8kc + 2g4 + s; its carry-in comes from block - 1
+      const int src = (lane + 48) & 63;
+      const float y = __shfl(cout[0][1], src), z = __shfl(cout[1][1], src);
+      cbt[(2 * g4) * 16 + r16] = core[0][0] + (g4 > 0 ? y : 0.f);
+      cbt[(2 * g4 + 1) * 16 + r16] = core[0][1] + cout[0][0];
+      cbt[(8 + 2 * g4) * 16 + r16] = core[1][0] + (g4 > 0 ? z : y);
+      cbt[(9 + 2 * g4) * 16 + r16] = core[1][1] + cout[1][0];
+      if (g4 == 3) cbt[16 * 16 + r16] = cout[1][1];  // into the next tile's first block
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) Pw[wave][r16][32 * (e >> 3) + 8 * g4 + (e & 7)] = p[e];
+      __asm__ volatile("" ::: "memory");
+      const int jb0 = (k0 * a.d) / a.beta;
+      for (int pr = lane; pr < 16 * a.NBT; pr += 64) {
+        const int h = pr & 15, jj = pr >> 4;
+        const int j = jb0 + jj;
+        const int bs = j * a.beta, be = bs + a.beta;
+        int ilo = block_tok_lo(j, a.beta, a.l, a.d), ihi = block_tok_hi(j, a.beta, a.d);
+        ilo = ilo > k0 ? ilo : k0;
+        ihi = ihi < k0 + 63 ? ihi : k0 + 63;
+        ihi = ihi < nvis - 1 ? ihi : nvis - 1;
+        float sv = 0.f;
+        for (int i = ilo; i <= ihi; ++i) {
+          const int s0 = i * a.d, s1 = s0 + a.l;
+          const int ov = (s1 < be ? s1 : be) - (s0 > bs ? s0 : bs);
+          sv += Pw[wave][h][i - k0] * ((float)ov / (float)a.l);
+        }
+        cbt[pr] = sv;
+      }
+      __asm__ volatile("" ::: "memory");  // Pw reads stay before the next tile's writes
+    }
+  }
+
+  // merge the four waves: outputs rescaled to the chunk max, summed through LDS
+  if (g4 == 0) { Wm[wave][r16] = m_run; Wl[wave][r16] = l_run; }
+  __syncthreads();  // every wave done with Vt; statistics posted
   float M = kNegInf;
 #pragma unroll
   for (int w = 0; w < 4; ++w) M = fmaxf(M, Wm[w][r16]);
+  const float sc = fast_exp2((Wm[wave][r16] - M) * sl);
+  float* Ob = reinterpret_cast<float*>(&Vt[0][0][0]);  // [4][16][OP] fp32
 #pragma unroll
-  for (int w = 0; w < 4; ++w) sc[w] = Wm[w][r16] == kNegInf ? 0.f : fast_exp2(Wm[w][r16] - M);
+  for (int n = 0; n < DT; ++n)
+    *reinterpret_cast<f32x4*>(&Ob[(wave * 16 + r16) * OP + 16 * n + 4 * g4]) = sc * O[n];
+  __syncthreads();
   const long cidx = bkv * a.NCH + chunk;
-  // each wave adds its scaled output into LDS (reusing Vt storage as [16][D] fp32)
-  float* Ob = reinterpret_cast<float*>(&Vt[0][0][0]);
-  __syncthreads();
-  for (int e = threadIdx.x; e < 16 * D; e += 256) Ob[e] = 0.f;
-  __syncthreads();
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int n = 0; n < DT; ++n)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Ob[r16 * D + 16 * n + 4 * g4 + e] += sc[w] * O[n][e];
-    }
-    __syncthreads();
+  for (int e = threadIdx.x; e < 16 * D; e += 256) {
+    const int o = (e / D) * OP + e % D;
+    a.co[cidx * 16 * D + e] = (Ob[o] + Ob[16 * OP + o]) + (Ob[32 * OP + o] + Ob[48 * OP + o]);
   }
-  for (int e = threadIdx.x; e < 16 * D; e += 256) a.co[cidx * 16 * D + e] = Ob[e];
   if (threadIdx.x < 16) {
     const int h = threadIdx.x;
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) L += Wl[w][h] * (Wm[w][h] == kNegInf ? 0.f : fast_exp2(Wm[w][h] - M));
-    a.cm[cidx * 16 + h] = M;
-    a.cl[cidx * 16 + h] = L;
-  }
-  // per-head block mass (relative to the chunk max) of the blocks this chunk touches
-  const int jb0 = (c0 * a.d) / a.beta;
-  for (int pr = threadIdx.x; pr < 16 * a.NBC; pr += 256) {
-    const int h = pr / a.NBC, j = jb0 + pr % a.NBC;
     float Mh = kNegInf;
 #pragma unroll
     for (int w = 0; w < 4; ++w) Mh = fmaxf(Mh, Wm[w][h]);
-    const int bs = j * a.beta, be = bs + a.beta;
-    int ilo = bs - a.l + 1 <= 0 ? 0 : (bs - a.l + 1 + a.d - 1) / a.d;
-    if (ilo < c0) ilo = c0;
-    int ihi = (be - 1) / a.d;
-    if (ihi > c0 + CHUNK - 1) ihi = c0 + CHUNK - 1;
-    if (ihi > nvis - 1) ihi = nvis - 1;
-    float sv = 0.f;
-    for (int i = ilo; i <= ihi; ++i) {
-      const int w = (i - c0) >> 6;
-      const float f = Wm[w][h] == kNegInf ? 0.f : fast_exp2(Wm[w][h] - Mh);
-      const int s0 = i * a.d, s1 = s0 + a.l;
-      const int ov = (s1 < be ? s1 : be) - (s0 > bs ? s0 : bs);
-      if (ov > 0) sv += Pw[w][h][(i - c0) & 63] * f * ((float)ov / (float)a.l);
-    }
-    a.cb[cidx * 16 * a.NBC + pr] = sv;
-  }
-}
-
-// ------------------------------------------------------------------ phase 2: block scores
-
-__global__ __launch_bounds__(256) void dec_scores_kernel(DecodeArgs a) {
-  __shared__ float lse[16];
-  const int slice = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const long bkv = (long)b * a.Hkv + kvh;
-  const int t = a.seqlens[b] - 1;
-  const int nvis = n_visible(t, a.l, a.d, a.ncmp);
-  const int nch = (nvis + CHUNK - 1) / CHUNK;
-  const int nb = t / a.beta + 1;
-  if (threadIdx.x < 16) {
-    const int h = threadIdx.x;
-    float M = kNegInf;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, a.cm[(bkv * a.NCH + c) * 16 + h]);
     float L = 0.f;
-    for (int c = 0; c < nch; ++c) {
-      const float mc = a.cm[(bkv * a.NCH + c) * 16 + h];
-      if (mc != kNegInf) L += a.cl[(bkv * a.NCH + c) * 16 + h] * fast_exp2(mc - M);
-    }
-    const float v = (M == kNegInf) ? __builtin_inff() : M + __log2f(L);
-    lse[h] = v;
-    if (slice == 0) a.lse[bkv * 16 + h] = v;
-  }
-  __syncthreads();
-  const int per = (nb + gridDim.x - 1) / gridDim.x;
-  const int j0 = slice * per, j1 = (j0 + per < nb) ? j0 + per : nb;
-  for (int j = j0 + threadIdx.x; j < j1; j += blockDim.x) {
-    const int bs = j * a.beta, be = bs + a.beta;
-    int ilo = bs - a.l + 1 <= 0 ? 0 : (bs - a.l + 1 + a.d - 1) / a.d;
-    int ihi = (be - 1) / a.d;
-    if (ihi > nvis - 1) ihi = nvis - 1;
-    float S = 0.f;
-    if (ilo <= ihi) {
-      const int clo = ilo / CHUNK, chi = ihi / CHUNK;
-      for (int h = 0; h < a.G; ++h) {
-        for (int c = clo; c <= chi; ++c) {
-          const long cidx = bkv * a.NCH + c;
-          const float mc = a.cm[cidx * 16 + h];
-          const int jb0 = (c * CHUNK * a.d) / a.beta;
-          if (mc != kNegInf)
-            S += a.cb[(cidx * 16 + h) * a.NBC + (j - jb0)] * fast_exp2(mc - lse[h]);
-        }
-      }
-    }
-    a.S[bkv * a.nblk + j] = S;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) L += Wl[w][h] * fast_exp2((Wm[w][h] - Mh) * sl);
+    a.cm[cidx * 16 + h] = Mh * sl;
+    a.cl[cidx * 16 + h] = L;
   }
 }
 
-// ------------------------------------------------------------------ phase 3: selection
+// ------------------------------------------------------------------ phase 2: scores + selection
 
 // Top-k of S[first, last) by (score desc, index asc) for non-negative scores.  Every lane keeps
 // its four best candidates; the wave repeatedly takes the best head, and a lane that runs out
@@ -274,145 +312,216 @@ __device__ int wave_topk(const float* S, int first, int last, int k, int lane) {
   return mine;
 }
 
-__global__ __launch_bounds__(64) void dec_select_kernel(DecodeArgs a) {
-  const int kvh = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x;
-  const long bkv = (long)b * a.Hkv + kvh;
-  const int t = a.seqlens[b] - 1;
-  const int bcur = t / a.beta, nb = bcur + 1;
-  int32_t* orow = a.idx + bkv * a.top_n;
-  if (nb <= a.top_n) {
-    for (int e = lane; e < a.top_n; e += 64) orow[e] = e < nb ? e : -1;
-    return;
-  }
-  const int flo = bcur - a.n_local + 1;
-  const int kfree = a.top_n - 1 - a.n_local;
-  int el = wave_topk(a.S + bkv * a.nblk, 1, flo, kfree, lane);
-  if (lane == kfree) el = 0;
-  if (lane > kfree && lane < a.top_n) el = flo + (lane - kfree - 1);
-  int rank = 0;
-  for (int o = 0; o < a.top_n; ++o) rank += (__shfl(el, o) < el) ? 1 : 0;
-  if (lane < a.top_n) orow[rank] = el;
+// Group score contribution of tile T to block j for heads 4*hq .. 4*hq + 3: masses times
+// exp2(tref - lse), the per-head normalisation of the compressed softmax.
+__device__ __forceinline__ float tile_block_score(const DecodeArgs& a, long bkv, int T, int j,
+                                                  int hq, const float* wl) {
+  const int jj = j - (T * 64 * a.d) / a.beta;
+  const f32x4 m =
+      *reinterpret_cast<const f32x4*>(a.cb + ((bkv * a.NT + T) * a.NBT + jj) * 16 + 4 * hq);
+  const f32x4 r = *reinterpret_cast<const f32x4*>(a.tref + (bkv * a.NT + T) * 16 + 4 * hq);
+  return (m[0] * fast_exp2(r[0] - wl[0]) + m[1] * fast_exp2(r[1] - wl[1])) +
+         (m[2] * fast_exp2(r[2] - wl[2]) + m[3] * fast_exp2(r[3] - wl[3]));
 }
 
-// ------------------------------------------------------------------ phase 4: selected + window
+constexpr int kSelThreads = 512;
 
-// Tile list of one (sequence, group): selected-block tiles and window tiles, ascending, each
-// tile once.  Returns the count; tiles[] gets the tile numbers (64 tokens each).
-__device__ int tile_list(const DecodeArgs& a, const int32_t* irow, int t, int* tiles) {
-  const int w0 = t - a.window + 1 > 0 ? t - a.window + 1 : 0;
-  const int wt0 = w0 / 64, wt1 = t / 64;
-  const int per = a.beta / 64;
-  int n = 0, wnext = wt0;
-  for (int e = 0; e < a.top_n; ++e) {
-    const int j = irow[e];
-    if (j < 0) break;
-    for (int u = 0; u < per; ++u) {
-      const int tile = j * per + u;
-      if (tile * 64 > t) break;
-      while (wnext <= wt1 && wnext < tile) tiles[n++] = wnext++;
-      if (wnext == tile) ++wnext;
-      tiles[n++] = tile;
+// One workgroup per (sequence, group): per-head log-sum-exp of the compressed softmax, every
+// group block score (four lanes per block, four heads each), the top-n with forced block 0 +
+// local blocks, and the group's tile list: tl[e] = tile | (1 << 30) for a tile of a selected
+// block, then the window tiles outside the selected blocks.
+__global__ __launch_bounds__(kSelThreads) void dec_select_kernel(DecodeArgs a) {
+  extern __shared__ float sh[];  // cm[NCH * 16] | cl[NCH * 16] | S[nblk]
+  __shared__ float lse[16];
+  __shared__ int sidx[64];
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const long bkv = (long)b * a.Hkv + kvh;
+  const int t = a.seqlens[b] - 1;
+  const int nb = t / a.beta + 1;
+  const int nvis = n_visible(t, a.l, a.d, a.ncmp);
+  const int nch = (nvis + CHUNK - 1) / CHUNK;
+  float* scm = sh;
+  float* scl = sh + a.NCH * 16;
+  float* Ss = sh + 2 * a.NCH * 16;
+  for (int e = threadIdx.x; e < nch * 16; e += kSelThreads) {
+    scm[e] = a.cm[bkv * a.NCH * 16 + e];
+    scl[e] = a.cl[bkv * a.NCH * 16 + e];
+  }
+  __syncthreads();
+  if (threadIdx.x < 256) {  // 16 lanes per head
+    const int h = threadIdx.x >> 4, sub = threadIdx.x & 15;
+    float M = kNegInf;
+    for (int c = sub; c < nch; c += 16) M = fmaxf(M, scm[c * 16 + h]);
+    M = group_max<16>(M);
+    float L = 0.f;
+    for (int c = sub; c < nch; c += 16) L += scl[c * 16 + h] * fast_exp2(scm[c * 16 + h] - M);
+    L = group_sum<16>(L);
+    if (sub == 0) {
+      // heads past G get +inf: their weights vanish
+      const float v = (M == kNegInf || h >= a.G) ? __builtin_inff() : M + __log2f(L);
+      lse[h] = v;
+      a.lse[bkv * 16 + h] = v;
     }
   }
-  while (wnext <= wt1) tiles[n++] = wnext++;
-  return n;
+  __syncthreads();
+  const bool all = nb <= a.top_n;  // uniform: every block is selected, no scores needed
+  if (!all) {
+    const int hq = threadIdx.x & 3;
+    float wl[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wl[k] = lse[4 * hq + k];
+    for (int j = threadIdx.x >> 2; j < nb; j += kSelThreads / 4) {
+      const int ilo = block_tok_lo(j, a.beta, a.l, a.d);
+      int ihi = block_tok_hi(j, a.beta, a.d);
+      ihi = ihi < nvis - 1 ? ihi : nvis - 1;
+      float S = 0.f;
+      if (ilo <= ihi)
+        for (int T = ilo / 64; T <= ihi / 64; ++T) S += tile_block_score(a, bkv, T, j, hq, wl);
+      S = group_sum<4>(S);
+      if (hq == 0) Ss[j] = S;
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int bcur = nb - 1;
+  if (threadIdx.x < 64) {
+    int32_t* orow = a.idx + bkv * a.top_n;
+    if (all) {
+      if (lane < a.top_n) {
+        const int el = lane < nb ? lane : -1;
+        orow[lane] = el;
+        sidx[lane] = el;
+      }
+    } else {
+      const int flo = bcur - a.n_local + 1;
+      const int kfree = a.top_n - 1 - a.n_local;
+      int el = wave_topk(Ss, 1, flo, kfree, lane);
+      if (lane == kfree) el = 0;
+      if (lane > kfree && lane < a.top_n) el = flo + (lane - kfree - 1);
+      int rank = 0;
+      for (int o = 0; o < a.top_n; ++o) rank += (__shfl(el, o) < el) ? 1 : 0;
+      if (lane < a.top_n) {
+        orow[rank] = el;
+        sidx[rank] = el;
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int per = a.beta / 64;
+    const int w0 = t - a.window + 1 > 0 ? t - a.window + 1 : 0;
+    const int wt0 = w0 / 64, wt1 = t / 64;
+    const int nsel = a.top_n * per, ncand = nsel + (wt1 - wt0 + 1);
+    int base = 0;
+    for (int i0 = 0; i0 < ncand; i0 += 64) {
+      const int i = i0 + lane;
+      int code = -1;
+      if (i < nsel) {
+        const int jb = sidx[i / per], tile = jb * per + i % per;
+        if (jb >= 0 && tile * 64 <= t) code = tile | (1 << 30);
+      } else if (i < ncand) {
+        const int tile = wt0 + (i - nsel), jw = tile / per;
+        bool in = false;
+        for (int e = 0; e < a.top_n; ++e) in |= sidx[e] == jw;
+        if (!in) code = tile;
+      }
+      const uint64_t m = __ballot(code >= 0);
+      const int pos = base + (int)__popcll(m & ((1ull << lane) - 1ull));
+      if (code >= 0) a.tl[bkv * kMaxTiles + pos] = code;
+      base += (int)__popcll(m);
+    }
+    if (lane == 0) a.tn[bkv] = base;
+  }
 }
 
+// ------------------------------------------------------------------ phase 3: selected + window
+
+// One wave per listed tile; four tiles per workgroup, merged into one partial per branch.
 template <int D>
 __global__ __launch_bounds__(256) void dec_tiles_kernel(DecodeArgs a) {
-  __shared__ u16 Vt[4][D][64 + KPAD];
-  __shared__ int tiles[160];
-  __shared__ int ntiles;
+  constexpr int DT = D / 16, OP = D + 4;
+  constexpr int VT_U16 = 4 * D * 64, OB_U16 = 4 * 2 * 16 * OP * 2;
+  __shared__ __align__(16) u16 smem[VT_U16 > OB_U16 ? VT_U16 : OB_U16];
   __shared__ float Wm[2][4][16], Wl[2][4][16];
+  u16(*Vt)[D][64] = reinterpret_cast<u16(*)[D][64]>(smem);
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g4 = lane >> 4, r16 = lane & 15;
   const long bkv = (long)b * a.Hkv + kvh;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int my = split * 4 + wave;  // < NSPLIT * 4 <= kMaxTiles
+  const int tn = a.tn[bkv];
+  const int code_raw = a.tl[bkv * kMaxTiles + my];
+  if (split * 4 >= tn) return;  // uniform
+  const int g4 = lane >> 4, r16 = lane & 15;
   const int t = a.seqlens[b] - 1;
-  const int32_t* irow = a.idx + bkv * a.top_n;
-  if (threadIdx.x == 0) ntiles = tile_list(a, irow, t, tiles);
-  __syncthreads();
-  const int my = split * 4 + wave;
-  const bool have = my < ntiles;
-  const int tile = have ? tiles[my] : 0;
-  const int k0 = tile * 64;
-  // branch membership of this tile
-  const int jblk = k0 / a.beta;
-  bool in_slc = false;
-  for (int e = 0; e < a.top_n; ++e) in_slc |= (irow[e] == jblk);
+  const float sl = a.scale_log2;
+  const bool have = my < tn;
+  const int code = have ? code_raw : 0;
+  const int k0 = (code & 0x3FFFFFFF) * 64;
+  const bool in_slc = have && ((code >> 30) & 1);
   const int w0 = t - a.window + 1;
   const bool in_win = have && (k0 + 63 >= w0);
-  in_slc = in_slc && have;
 
-  const u16* kb = a.kcache + bkv * (long)a.L * D;
-  const u16* vb = a.vcache + bkv * (long)a.L * D;
   bf16x8 qf[D / 32];
   load_q_decode<D>(a, b, kvh, lane, qf);
+  DecTile<D> kv;
+  kv.load(a.kcache + bkv * (long)a.L * D, a.vcache + bkv * (long)a.L * D, k0, t, lane);
   f32x4 acc[4];
-  tile_scores<D>(kb, k0, t, qf, g4, r16, acc);
-  stage_vt<D>(Vt[wave], vb, k0, t, lane);
+  kv.scores(qf, acc);
+  kv.stage(Vt[wave], lane);
   __syncthreads();
 
-  constexpr int DT = D / 16;
   f32x4 O[2][DT];
 #pragma unroll
   for (int br = 0; br < 2; ++br) {
-    float z[16];
+    float p[16];
+    float tm = kNegInf;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = k0 + 32 * (q4 >> 1) + 8 * g4 + 4 * (q4 & 1) + i;
+        const int key = k0 + lane_key(q4, i, g4);
         const bool ok = br == 0 ? (in_slc && key <= t) : (in_win && key <= t && key >= w0);
-        z[q4 * 4 + i] = ok ? acc[q4][i] * a.scale_log2 : kNegInf;
+        const float r = ok ? acc[q4][i] : kNegInf;
+        p[q4 * 4 + i] = r;
+        tm = fmaxf(tm, r);
       }
-    float tm = z[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) tm = fmaxf(tm, z[e]);
     tm = col_max4(tm);
-    const float ms = tm == kNegInf ? 0.f : tm;
-    float p[16], ls = 0.f;
+    const float ms = tm == kNegInf ? 0.f : tm * sl;
+    float ls = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) { p[e] = fast_exp2(z[e] - ms); ls += p[e]; }
+    for (int e = 0; e < 16; ++e) {
+      p[e] = fast_exp2(fmaf(p[e], sl, -ms));
+      ls += p[e];
+    }
     ls = col_sum4(ls);
 #pragma unroll
     for (int n = 0; n < DT; ++n) O[br][n] = zero4();
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[kc * 8 + e];
-#pragma unroll
-      for (int n = 0; n < DT; ++n)
-        O[br][n] = mfma16x16x32(load8(&Vt[wave][16 * n + r16][32 * kc + 8 * g4]), pb, O[br][n]);
-    }
+    tile_pv<D>(Vt[wave], p, g4, r16, O[br]);
     if (g4 == 0) { Wm[br][wave][r16] = tm; Wl[br][wave][r16] = ls; }
   }
-  __syncthreads();
-  // merge the four waves per branch into one partial of this split
-  float* Ob = reinterpret_cast<float*>(&Vt[0][0][0]);  // [2][16][D] fp32
-  for (int e = threadIdx.x; e < 2 * 16 * D; e += 256) Ob[e] = 0.f;
+  __syncthreads();  // Vt reads done; maxima posted
+  // merge the four waves per branch into this split's partial, summed through LDS
+  float* Ob = reinterpret_cast<float*>(smem);  // [4][2][16][OP] fp32
+#pragma unroll
+  for (int br = 0; br < 2; ++br) {
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, Wm[br][w][r16]);
+    const float f =
+        Wm[br][wave][r16] == kNegInf ? 0.f : fast_exp2((Wm[br][wave][r16] - M) * sl);
+#pragma unroll
+    for (int n = 0; n < DT; ++n)
+      *reinterpret_cast<f32x4*>(&Ob[((wave * 2 + br) * 16 + r16) * OP + 16 * n + 4 * g4]) =
+          f * O[br][n];
+  }
   __syncthreads();
   const long sidx = bkv * a.NSPLIT + split;
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int br = 0; br < 2; ++br) {
-        float M = kNegInf;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) M = fmaxf(M, Wm[br][v][r16]);
-        const float f = Wm[br][w][r16] == kNegInf ? 0.f : fast_exp2(Wm[br][w][r16] - M);
-#pragma unroll
-        for (int n = 0; n < DT; ++n)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            Ob[(br * 16 + r16) * D + 16 * n + 4 * g4 + e] += f * O[br][n][e];
-      }
-    }
-    __syncthreads();
+  for (int e = threadIdx.x; e < 2 * 16 * D; e += 256) {
+    const int br = e / (16 * D), rest = e % (16 * D);
+    const int o = (br * 16 + rest / D) * OP + rest % D;
+    a.po[sidx * 2 * 16 * D + e] =
+        (Ob[o] + Ob[2 * 16 * OP + o]) + (Ob[4 * 16 * OP + o] + Ob[6 * 16 * OP + o]);
   }
-  for (int e = threadIdx.x; e < 2 * 16 * D; e += 256) a.po[sidx * 2 * 16 * D + e] = Ob[e];
   if (threadIdx.x < 32) {
     const int br = threadIdx.x >> 4, h = threadIdx.x & 15;
     float M = kNegInf;
@@ -421,42 +530,52 @@ __global__ __launch_bounds__(256) void dec_tiles_kernel(DecodeArgs a) {
     float L = 0.f;
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      L += Wm[br][v][h] == kNegInf ? 0.f : Wl[br][v][h] * fast_exp2(Wm[br][v][h] - M);
-    a.pm[(sidx * 2 + br) * 16 + h] = M;
+      if (Wm[br][v][h] != kNegInf) L += Wl[br][v][h] * fast_exp2((Wm[br][v][h] - M) * sl);
+    a.pm[(sidx * 2 + br) * 16 + h] = M == kNegInf ? kNegInf : M * sl;
     a.pl[(sidx * 2 + br) * 16 + h] = L;
   }
 }
 
-// ------------------------------------------------------------------ phase 5: merge + gate
+// ------------------------------------------------------------------ phase 4: merge + gate
 
+// 256 (head, feature) outputs of one (sequence, group) per workgroup: the compressed output
+// normalised by the lse, the selected and window partials merged, then the gate.
 __global__ __launch_bounds__(256) void dec_combine_kernel(DecodeArgs a) {
+  extern __shared__ float wc[];  // [nch][16] chunk weights exp2(cm - lse)
+  __shared__ float pm[2][kMaxSplits][16], pl[2][kMaxSplits][16];
   const int kvh = blockIdx.y, b = blockIdx.z;
   const long bkv = (long)b * a.Hkv + kvh;
-  const int pair = blockIdx.x * 256 + threadIdx.x;
-  const int h = pair / a.D, dd = pair % a.D;
-  if (h >= a.G) return;
   const int t = a.seqlens[b] - 1;
   const int nvis = n_visible(t, a.l, a.d, a.ncmp);
   const int nch = (nvis + CHUNK - 1) / CHUNK;
-  float ocmp = 0.f;
-  const float lse = a.lse[bkv * 16 + h];
-  for (int c = 0; c < nch; ++c) {
-    const long cidx = bkv * a.NCH + c;
-    const float mc = a.cm[cidx * 16 + h];
-    if (mc != kNegInf) ocmp += a.co[(cidx * 16 + h) * a.D + dd] * fast_exp2(mc - lse);
+  const int nsp = (a.tn[bkv] + 3) / 4;
+  for (int e = threadIdx.x; e < nsp * 32; e += 256) {
+    const int s = e >> 5, br = (e >> 4) & 1, h = e & 15;
+    pm[br][s][h] = a.pm[(bkv * a.NSPLIT + s) * 32 + (e & 31)];
+    pl[br][s][h] = a.pl[(bkv * a.NSPLIT + s) * 32 + (e & 31)];
   }
+  for (int e = threadIdx.x; e < nch * 16; e += 256)
+    wc[e] = fast_exp2(a.cm[bkv * a.NCH * 16 + e] - a.lse[bkv * 16 + (e & 15)]);
+  __syncthreads();
+  const int pair = blockIdx.x * 256 + threadIdx.x;
+  const int h = pair / a.D, dd = pair % a.D;
+  if (h >= a.G) return;
+  float ocmp = 0.f;
+  const float* cop = a.co + bkv * a.NCH * 16 * a.D + pair;
+#pragma unroll 4
+  for (int c = 0; c < nch; ++c) ocmp += cop[(long)c * 16 * a.D] * wc[c * 16 + h];
   float ob[2];
+#pragma unroll
   for (int br = 0; br < 2; ++br) {
     float M = kNegInf;
-    for (int s = 0; s < a.NSPLIT; ++s) M = fmaxf(M, a.pm[((bkv * a.NSPLIT + s) * 2 + br) * 16 + h]);
+    for (int s = 0; s < nsp; ++s) M = fmaxf(M, pm[br][s][h]);
     float L = 0.f, o = 0.f;
-    for (int s = 0; s < a.NSPLIT; ++s) {
-      const long sidx = bkv * a.NSPLIT + s;
-      const float m = a.pm[(sidx * 2 + br) * 16 + h];
-      if (m == kNegInf) continue;
-      const float f = fast_exp2(m - M);
-      L += a.pl[(sidx * 2 + br) * 16 + h] * f;
-      o += a.po[((sidx * 2 + br) * 16 + h) * a.D + dd] * f;
+#pragma unroll 4
+    for (int s = 0; s < nsp; ++s) {
+      const float m = pm[br][s][h];
+      const float f = m == kNegInf ? 0.f : fast_exp2(m - M);
+      L += pl[br][s][h] * f;
+      o += a.po[((bkv * a.NSPLIT + s) * 2 + br) * 16 * a.D + pair] * f;
     }
     ob[br] = L > 0.f ? o / L : 0.f;
   }
@@ -467,27 +586,43 @@ __global__ __launch_bounds__(256) void dec_combine_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------------ launcher
 
+int decode_chunk_tokens() { return CHUNK; }
+int decode_max_splits() { return kMaxSplits; }
+int decode_max_tile_list() { return kMaxTiles; }
+size_t decode_select_lds_bytes(int nch, int nblk) {
+  return (size_t)(2 * nch * 16 + nblk) * sizeof(float);
+}
+
 void launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
   auto mark = [&](int i) {
     if (ev != nullptr) (void)hipEventRecord(ev[i], s);
   };
-  const dim3 g1(a.NCH, a.Hkv, a.B);
+  const bool fast = a.beta == 4 * a.d && a.l == 2 * a.d && a.NBT >= 17;
+  const size_t sel_lds = decode_select_lds_bytes(a.NCH, a.nblk);
+  if (sel_lds > 64 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(dec_select_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sel_lds);
   mark(0);
   if (a.NCH > 0) {
-    if (a.D == 128) dec_cmp_kernel<128><<<g1, 256, 0, s>>>(a);
-    else dec_cmp_kernel<64><<<g1, 256, 0, s>>>(a);
+    const dim3 g1(a.NCH, a.Hkv, a.B);
+    if (a.D == 128) {
+      if (fast) dec_cmp_kernel<128, true><<<g1, 256, 0, s>>>(a);
+      else dec_cmp_kernel<128, false><<<g1, 256, 0, s>>>(a);
+    } else {
+      if (fast) dec_cmp_kernel<64, true><<<g1, 256, 0, s>>>(a);
+      else dec_cmp_kernel<64, false><<<g1, 256, 0, s>>>(a);
+    }
   }
   mark(1);
-  dec_scores_kernel<<<dim3(a.NSLICE, a.Hkv, a.B), 256, 0, s>>>(a);
+  dec_select_kernel<<<dim3(a.Hkv, a.B), kSelThreads, sel_lds, s>>>(a);
   mark(2);
-  dec_select_kernel<<<dim3(a.Hkv, a.B), 64, 0, s>>>(a);
+  const dim3 g3(a.NSPLIT, a.Hkv, a.B);
+  if (a.D == 128) dec_tiles_kernel<128><<<g3, 256, 0, s>>>(a);
+  else dec_tiles_kernel<64><<<g3, 256, 0, s>>>(a);
   mark(3);
-  const dim3 g4(a.NSPLIT, a.Hkv, a.B);
-  if (a.D == 128) dec_tiles_kernel<128><<<g4, 256, 0, s>>>(a);
-  else dec_tiles_kernel<64><<<g4, 256, 0, s>>>(a);
+  dec_combine_kernel<<<dim3((16 * a.D + 255) / 256, a.Hkv, a.B), 256,
+                       (size_t)a.NCH * 16 * sizeof(float), s>>>(a);
   mark(4);
-  dec_combine_kernel<<<dim3((16 * a.D + 255) / 256, a.Hkv, a.B), 256, 0, s>>>(a);
-  mark(5);
 }
 
 }  // namespace nsa

@@ -90,6 +90,13 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+template <int GS>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = 1; o < GS; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
 // Key offset (inside a 32-key chunk) of C-row r of sub-tile s, per the ordering above.
 __device__ __forceinline__ int perm_key(int r, int s) { return 8 * (r >> 2) + 4 * s + (r & 3); }
 

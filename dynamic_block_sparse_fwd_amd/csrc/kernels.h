@@ -31,25 +31,31 @@ struct DecodeArgs {
   const float* gate;       // [B, Hq, 3]
   float* out;              // [B, Hq, D]
   int32_t* idx;            // [B, Hkv, top_n]
-  // workspace: per 256-token chunk of the compressed cache (16 row slots per group)
-  float* cm;  // [B*Hkv, NCH, 16] chunk max (log2 units)
-  float* cl;  // [B*Hkv, NCH, 16] sum of exp2(z - max)
-  float* co;  // [B*Hkv, NCH, 16, D] unnormalised output
-  float* cb;  // [B*Hkv, NCH, 16, NBC] block mass relative to the chunk max
-  float* lse; // [B*Hkv, 16]
-  float* S;   // [B*Hkv, nblk] group block scores
-  // per split of the selected/window tile list: [.., NSPLIT, 2 (slc, win), 16 (, D)]
+  // workspace; 16 row slots (heads of a group) everywhere
+  float* cm;    // [B*Hkv, NCH, 16] chunk max (scaled log2 units)
+  float* cl;    // [B*Hkv, NCH, 16] sum of exp2(z - max)
+  float* co;    // [B*Hkv, NCH, 16, D] unnormalised output
+  float* tref;  // [B*Hkv, NT, 16] per 64-token tile: reference of its block masses (log2)
+  float* cb;    // [B*Hkv, NT, NBT, 16] block masses of each tile, relative to exp2(tref)
+  float* lse;   // [B*Hkv, 16]
+  int32_t* tl;  // [B*Hkv, 160] selected / window tile list
+  int32_t* tn;  // [B*Hkv] its length
+  // per 4-tile split of the tile list: [.., NSPLIT, 2 (slc, win), 16 (, D)]
   float* pm;
   float* pl;
   float* po;
   int B, L, Hkv, G, D;
   int l, d, beta, top_n, n_local, window;
-  int ncmp, nblk, NCH, NBC, NSLICE, NSPLIT;
+  int ncmp, nblk, NCH, NT, NBT, NSPLIT;
   float scale_log2;
 };
 
 // ev: nullptr or NSA_DECODE_NSTAGES + 1 events recorded around the stages.
 void launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev);
+int decode_chunk_tokens();
+int decode_max_splits();
+int decode_max_tile_list();
+size_t decode_select_lds_bytes(int nch, int nblk);
 
 struct MobaArgs {
   const uint16_t* q;   // [B, T, H, D]

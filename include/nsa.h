@@ -148,6 +148,8 @@ int nsa_prefill_timed(const nsa_config* cfg, const void* q, const void* k, const
  *   seqlens        int32 [B], 1 <= seqlens[b] <= Lmax (device memory)
  *   gate           fp32 [B, Hq, 3];  out fp32 [B, Hq, D]
  *   sel_idx        int32 [B, Hkv, top_n] or NULL
+ * Returns NSA_ERR_UNSUPPORTED when top_n * sel_block / 64 + ceil(window / 64) + 1 > 160
+ * (tile table), Lmax > 2^24, or the block scores of a group outgrow 160 KB of LDS.
  */
 int nsa_decode(const nsa_config* cfg, const void* q, const void* kcache, const void* vcache,
                const void* kcmp, const void* vcmp, const int32_t* seqlens, const float* gate,
@@ -156,9 +158,9 @@ int nsa_decode(const nsa_config* cfg, const void* q, const void* kcache, const v
 /*
  * Instrumented nsa_decode: identical work, plus events[s] recorded before stage s and
  * events[NSA_DECODE_NSTAGES] after the last.  Stages: 0 compressed-cache stream, 1 block
- * scores, 2 selection, 3 selected + window tiles, 4 merge and gate.  For measurement only.
+ * scores and selection, 2 selected + window tiles, 3 merge and gate.  For measurement only.
  */
-#define NSA_DECODE_NSTAGES 5
+#define NSA_DECODE_NSTAGES 4
 int nsa_decode_timed(const nsa_config* cfg, const void* q, const void* kcache,
                      const void* vcache, const void* kcmp, const void* vcmp,
                      const int32_t* seqlens, const float* gate, float* out, int32_t* sel_idx,

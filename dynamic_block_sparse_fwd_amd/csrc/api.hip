@@ -38,13 +38,16 @@ int check_nsa_base(const nsa_config* c) {
   return NSA_OK;
 }
 
-// Prefill keeps one query tile's block scores in LDS.
+// Prefill keeps one query tile's block scores in LDS and lists a row's selected 64-key tiles
+// one per lane.
 int check_nsa(const nsa_config* c) {
   int st = check_nsa_base(c);
   if (st != NSA_OK) return st;
   const long nblk = ((long)c->T + c->sel_block - 1) / c->sel_block;
   if (nblk > 2048) return NSA_ERR_UNSUPPORTED;
   if (cmp_select_lds_bytes(c->G, (int)nblk) > kMaxDynLds) return NSA_ERR_UNSUPPORTED;
+  if (c->top_n * (c->sel_block / 64) > 64) return NSA_ERR_UNSUPPORTED;  // one tile per lane
+  if ((long)((c->T + 3) / 4) * c->B * c->Hkv > (1L << 31) - 8) return NSA_ERR_UNSUPPORTED;
   return NSA_OK;
 }
 

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256, FAST ? 2 : 1) void dec_cmp_kernel(DecodeArgs a
   const int tile0 = (c0 >> 6) + wave;
   DecTile<D> cur;
   if (tile0 * 64 < nvis) cur.load(kcb, vcb, tile0 * 64, nvis - 1, lane);
-#pragma unroll 1
+#pragma unroll
   for (int it = 0; it < TPW; ++it) {
     const int tile = tile0 + 4 * it;
     const int k0 = tile * 64;
@@ -173,7 +173,10 @@ __global__ __launch_bounds__(256, FAST ? 2 : 1) void dec_cmp_kernel(DecodeArgs a
     cur.scores(qf, acc);
     __asm__ volatile("" ::: "memory");  // the previous tile's Vt reads stay before these writes
     cur.stage(Vt[wave], lane);
-    if (it + 1 < TPW && k0 + 256 < nvis) cur.load(kcb, vcb, k0 + 256, nvis - 1, lane);
+    // the loop is unrolled, so this condition is resolved at compile time: a load under a
+    // run-time branch would make the join wait for every load in flight (rows past the last
+    // visible one clamp to it)
+    if (it + 1 < TPW) cur.load(kcb, vcb, k0 + 256, nvis - 1, lane);
 
     float p[16];
     float tm = kNegInf;

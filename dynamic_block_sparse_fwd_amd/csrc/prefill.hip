@@ -450,19 +450,43 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void window_kernel(PrefillArgs a
 // ------------------------------------------------------------------ selected blocks
 
 // One wave per (position, KV group): the group's heads form the 16 MFMA rows; K and V
-// fragments are read straight from global memory (16-byte loads), no LDS.
+// fragments are read straight from global memory (16-byte loads, no LDS).  The wave's tiles
+// (64 keys each, in selection order) are listed once, lane e holding the first key of tile e;
+// the selected blocks precede the -1 padding and a block's tiles past t come last, so the
+// valid tiles form a prefix.  Each tile's K and V are fetched while the previous tile computes.
+// Workgroups are dealt to the 8 XCDs round-robin; the linear index is remapped so that XCD x
+// runs a contiguous 1/8 of the (sequence, group, position) range: the waves that share an
+// XCD's L2 then read the same group's K/V at nearby positions.
 template <int D, int G>
-__global__ __launch_bounds__(256) void selected_kernel(PrefillArgs a) {
-  constexpr int DT = D / 16;
+__global__ __launch_bounds__(256, 2) void selected_kernel(PrefillArgs a) {
+  constexpr int DT = D / 16, NK = D / 8, NV = D / 8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
-  const int t = blockIdx.x * 4 + wave;
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int ntb = (a.T + 3) / 4;
+  const int per_xcd = gridDim.x / 8;  // the grid is padded to a multiple of 8
+  const int w = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  const int stream = w / ntb;
+  if (stream >= a.B * a.Hkv) return;
+  const int t = (w % ntb) * 4 + wave;
+  const int kvh = stream % a.Hkv, b = stream / a.Hkv;
   if (t >= a.T) return;
   const long bkv = (long)b * a.Hkv + kvh;
   const int Hq = a.Hkv * G;
   const bool hlive = r16 < G;
   const int head = kvh * G + (hlive ? r16 : 0);
+  const float sl = a.scale_log2;
+
+  int my_key0 = -1;
+  {
+    const int per = a.beta >> 6;
+    const int32_t* irow = a.idx + (((long)b * a.T + t) * a.Hkv + kvh) * a.top_n;
+    if (lane < a.top_n * per) {
+      const int j = irow[lane / per];
+      const int k0 = j * a.beta + 64 * (lane % per);
+      if (j >= 0 && k0 <= t) my_key0 = k0;
+    }
+  }
+  const int ntile = (int)__popcll(__ballot(my_key0 >= 0));
 
   bf16x8 qf[D / 32];
   {
@@ -472,65 +496,96 @@ __global__ __launch_bounds__(256) void selected_kernel(PrefillArgs a) {
   }
   const u16* kb = a.k + bkv * (long)a.T * D;
   const u16* vtb = a.vt + bkv * (long)D * a.TP;
-  const int32_t* irow = a.idx + (((long)b * a.T + t) * a.Hkv + kvh) * a.top_n;
+  const int tmax = a.T - 1;
+  u32x4 kr[NK], vr[NV];
+  auto load_k = [&](int key0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int row = key0 + 32 * (q >> 1) + perm_key(r16, q & 1);
+      row = row < tmax ? row : tmax;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+        kr[q * (D / 32) + c] =
+            *reinterpret_cast<const u32x4*>(kb + ((uint32_t)row * D + 8 * g4 + 32 * c));
+    }
+  };
+  auto load_v = [&](int key0) {
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int n = 0; n < DT; ++n)
+        vr[kc * DT + n] = *reinterpret_cast<const u32x4*>(
+            vtb + ((uint32_t)(16 * n + r16) * a.TP + key0 + 32 * kc + 8 * g4));
+  };
 
   float mrun = kNegInf, lrun = 0.f;
   f32x4 O[DT];
 #pragma unroll
   for (int n = 0; n < DT; ++n) O[n] = zero4();
-
-  for (int ai = 0; ai < a.top_n; ++ai) {
-    const int j = irow[ai];
-    if (j < 0) break;
-    for (int key0 = j * a.beta; key0 < (j + 1) * a.beta && key0 <= t; key0 += 64) {
-      float z[16];
+  if (ntile > 0) {
+    const int k00 = __builtin_amdgcn_readfirstlane(my_key0);
+    load_k(k00);
+    load_v(k00);
+  }
+  for (int i = 0; i < ntile; ++i) {
+    const int key0 = __builtin_amdgcn_readlane(my_key0, i);
+    // the last tile re-fetches itself: unconditional loads keep the wait counts exact (a load
+    // under a branch makes the join wait for every load in flight)
+    const int knext = (i + 1 < ntile) ? __builtin_amdgcn_readlane(my_key0, i + 1) : key0;
+    float z[16];
 #pragma unroll
-      for (int kc2 = 0; kc2 < 2; ++kc2)
+    for (int q = 0; q < 4; ++q) {
+      f32x4 acc = zero4();
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          int krow = key0 + 32 * kc2 + perm_key(r16, s);
-          krow = krow < a.T ? krow : a.T - 1;
-          const u16* kp = kb + (long)krow * D + 8 * g4;
-          f32x4 acc = zero4();
+      for (int c = 0; c < D / 32; ++c)
+        acc = mfma16x16x32(__builtin_bit_cast(bf16x8, kr[q * (D / 32) + c]), qf[c], acc);
 #pragma unroll
-          for (int c = 0; c < D / 32; ++c) acc = mfma16x16x32(load8(kp + 32 * c), qf[c], acc);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = key0 + 32 * kc2 + 8 * g4 + 4 * s + i;
-            z[kc2 * 8 + s * 4 + i] = key <= t ? acc[i] * a.scale_log2 : kNegInf;
-          }
-        }
-      float tm = z[0];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) tm = fmaxf(tm, z[e]);
-      tm = col_max4(tm);
-      const float mn = fmaxf(mrun, tm);
-      const float alpha = fast_exp2(mrun - mn);
-      mrun = mn;
-      float p[16], sum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) { p[e] = fast_exp2(z[e] - mn); sum += p[e]; }
-      lrun = lrun * alpha + sum;
-#pragma unroll
-      for (int n = 0; n < DT; ++n) O[n] *= alpha;
-#pragma unroll
-      for (int kc2 = 0; kc2 < 2; ++kc2) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[kc2 * 8 + e];
-#pragma unroll
-        for (int n = 0; n < DT; ++n) {
-          const u16* vp = vtb + (long)(16 * n + r16) * a.TP + key0 + 32 * kc2 + 8 * g4;
-          O[n] = mfma16x16x32(load8(vp), pb, O[n]);
-        }
-      }
+      for (int e = 0; e < 4; ++e) z[q * 4 + e] = acc[e];
     }
+    load_k(knext);
+    if (key0 + 63 > t) {  // the diagonal tile (uniform branch)
+      __asm__ volatile("" ::: "memory");
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = key0 + 32 * (q >> 1) + 8 * g4 + 4 * (q & 1) + e;
+          z[q * 4 + e] = key <= t ? z[q * 4 + e] : kNegInf;
+        }
+    }
+    float tm = z[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) tm = fmaxf(tm, z[e]);
+    tm = col_max4(tm);
+    const float mn = fmaxf(mrun, tm);  // finite: every listed tile holds key0 <= t
+    const float msl = mn * sl;
+    const float alpha = fast_exp2(fmaf(mrun, sl, -msl));
+    mrun = mn;
+    float p[16], sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = fast_exp2(fmaf(z[e], sl, -msl));
+      sum += p[e];
+    }
+    lrun = fmaf(lrun, alpha, sum);
+#pragma unroll
+    for (int n = 0; n < DT; ++n) O[n] *= alpha;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[kc * 8 + e];
+#pragma unroll
+      for (int n = 0; n < DT; ++n)
+        O[n] = mfma16x16x32(__builtin_bit_cast(bf16x8, vr[kc * DT + n]), pb, O[n]);
+    }
+    load_v(knext);
   }
 
   const float L = col_sum4(lrun);
   if (hlive) {
     const long rowoff = ((long)b * a.T + t) * Hq + head;
-    const float gs = a.gate[rowoff * 3 + 1] / L;
+    const float gs = L > 0.f ? a.gate[rowoff * 3 + 1] / L : 0.f;
     float* op = a.out + rowoff * D;
 #pragma unroll
     for (int n = 0; n < DT; ++n) {
@@ -584,7 +639,8 @@ static void launch_prefill_all(const PrefillArgs& a, int which, hipStream_t s) {
   } else if (which == 1) {
     window_kernel<D, G><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, 0, s>>>(a);
   } else {
-    selected_kernel<D, G><<<dim3((a.T + 3) / 4, a.Hkv, a.B), 256, 0, s>>>(a);
+    const long nwg = (long)((a.T + 3) / 4) * a.Hkv * a.B;
+    selected_kernel<D, G><<<dim3((unsigned)((nwg + 7) / 8 * 8)), 256, 0, s>>>(a);
   }
 }
 

@@ -84,7 +84,8 @@ const char* nsa_status_string(int status);
 
 /* Host-only checks; no device is touched.  NSA_ERR_UNSUPPORTED when: D not 64/128;
  * G not in {1,2,4,8,16}; sel_block not a positive multiple of 64; top_n < 1 + n_local or
- * top_n > 64; T / sel_block > 2048 (prefill selection buffer); cmp_len < cmp_stride. */
+ * top_n > 64; T / sel_block > 2048 (prefill selection buffer); top_n * sel_block / 64 > 64
+ * (prefill tiles of a row); cmp_len < cmp_stride. */
 int nsa_validate(const nsa_config* cfg);
 int moba_validate(const moba_config* cfg);
 

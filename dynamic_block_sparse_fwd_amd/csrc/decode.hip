@@ -315,19 +315,47 @@ __device__ int wave_topk(const float* S, int first, int last, int k, int lane) {
   return mine;
 }
 
-// Group score contribution of tile T to block j for heads 4*hq .. 4*hq + 3: masses times
-// exp2(tref - lse), the per-head normalisation of the compressed softmax.
-__device__ __forceinline__ float tile_block_score(const DecodeArgs& a, long bkv, int T, int j,
-                                                  int hq, const float* wl) {
-  const int jj = j - (T * 64 * a.d) / a.beta;
-  const f32x4 m =
-      *reinterpret_cast<const f32x4*>(a.cb + ((bkv * a.NT + T) * a.NBT + jj) * 16 + 4 * hq);
-  const f32x4 r = *reinterpret_cast<const f32x4*>(a.tref + (bkv * a.NT + T) * 16 + 4 * hq);
+// Masses and tile references of block j for heads 4*hq .. 4*hq + 3 over the (at most) first
+// two tiles it touches.  Every index is clamped so the loads are unconditional (no branch
+// around them); `ntile` is the number of tiles the block really touches (0 when none of its
+// compressed tokens is visible).
+struct BlockMass {
+  f32x4 m0, r0, m1, r1;
+  int ta, ntile;
+};
+
+__device__ __forceinline__ BlockMass fetch_block(const DecodeArgs& a, long bkv, int j, int nvis,
+                                                 int hq) {
+  const int lo = block_tok_lo(j, a.beta, a.l, a.d);
+  int hi = block_tok_hi(j, a.beta, a.d);
+  hi = hi < nvis - 1 ? hi : nvis - 1;
+  const int ta = (lo < nvis - 1 ? lo : nvis - 1) / 64;
+  const int tb = hi / 64 > ta ? ta + 1 : ta;
+  auto entry = [&](int T) {
+    int jj = j - (T * 64 * a.d) / a.beta;
+    jj = jj < 0 ? 0 : (jj < a.NBT ? jj : a.NBT - 1);
+    return ((bkv * a.NT + T) * a.NBT + jj) * 16 + 4 * hq;
+  };
+  BlockMass r;
+  r.m0 = *reinterpret_cast<const f32x4*>(a.cb + entry(ta));
+  r.r0 = *reinterpret_cast<const f32x4*>(a.tref + (bkv * a.NT + ta) * 16 + 4 * hq);
+  r.m1 = *reinterpret_cast<const f32x4*>(a.cb + entry(tb));
+  r.r1 = *reinterpret_cast<const f32x4*>(a.tref + (bkv * a.NT + tb) * 16 + 4 * hq);
+  r.ta = ta;
+  r.ntile = lo <= hi ? hi / 64 - lo / 64 + 1 : 0;
+  return r;
+}
+
+// Group score share of one tile: masses times exp2(tref - lse), the per-head normalisation of
+// the compressed softmax.
+__device__ __forceinline__ float mass_score(const f32x4& m, const f32x4& r, const float* wl) {
   return (m[0] * fast_exp2(r[0] - wl[0]) + m[1] * fast_exp2(r[1] - wl[1])) +
          (m[2] * fast_exp2(r[2] - wl[2]) + m[3] * fast_exp2(r[3] - wl[3]));
 }
 
-constexpr int kSelThreads = 512;
+constexpr int kSelThreads = 1024;
+constexpr int kSelLanes = kSelThreads / 4;  // blocks per pass (four lanes per block)
+constexpr int kSelUnroll = 4;              // passes whose loads are in flight together
 
 // One workgroup per (sequence, group): per-head log-sum-exp of the compressed softmax, every
 // group block score (four lanes per block, four heads each), the top-n with forced block 0 +
@@ -343,14 +371,36 @@ __global__ __launch_bounds__(kSelThreads) void dec_select_kernel(DecodeArgs a) {
   const int nb = t / a.beta + 1;
   const int nvis = n_visible(t, a.l, a.d, a.ncmp);
   const int nch = (nvis + CHUNK - 1) / CHUNK;
+  const bool all = nb <= a.top_n;            // uniform: every block is selected
+  const bool scored = !all && nvis > 0;      // uniform
+  const int hq = threadIdx.x & 3, jq = threadIdx.x >> 2;
   float* scm = sh;
   float* scl = sh + a.NCH * 16;
   float* Ss = sh + 2 * a.NCH * 16;
-  for (int e = threadIdx.x; e < nch * 16; e += kSelThreads) {
-    scm[e] = a.cm[bkv * a.NCH * 16 + e];
-    scl[e] = a.cl[bkv * a.NCH * 16 + e];
+
+  // Chunk statistics first, then the first pass of block masses: the wait for the former
+  // (vmcnt retires in order) leaves the latter in flight while the lse is formed.  The loads
+  // are unconditional, every index clamped into the workspace (which is never empty); values
+  // of a missing chunk or tile are never used.
+  const bool many = nch * 16 > kSelThreads;  // uniform: beyond 64 chunks, a plain loop
+  if (many)
+    for (int e = threadIdx.x; e < nch * 16; e += kSelThreads) {
+      scm[e] = a.cm[bkv * a.NCH * 16 + e];
+      scl[e] = a.cl[bkv * a.NCH * 16 + e];
+    }
+  const int ce = threadIdx.x < nch * 16 ? threadIdx.x : 0;
+  const float cmv = a.cm[bkv * a.NCH * 16 + ce], clv = a.cl[bkv * a.NCH * 16 + ce];
+  BlockMass bm[kSelUnroll];
+#pragma unroll
+  for (int u = 0; u < kSelUnroll; ++u) {
+    const int j = jq + kSelLanes * u;
+    bm[u] = fetch_block(a, bkv, j < nb ? j : nb - 1, nvis, hq);
   }
-  __syncthreads();
+  if (!many && threadIdx.x < nch * 16) {
+    scm[threadIdx.x] = cmv;
+    scl[threadIdx.x] = clv;
+  }
+  lds_barrier();
   if (threadIdx.x < 256) {  // 16 lanes per head
     const int h = threadIdx.x >> 4, sub = threadIdx.x & 15;
     float M = kNegInf;
@@ -366,23 +416,39 @@ __global__ __launch_bounds__(kSelThreads) void dec_select_kernel(DecodeArgs a) {
       a.lse[bkv * 16 + h] = v;
     }
   }
-  __syncthreads();
-  const bool all = nb <= a.top_n;  // uniform: every block is selected, no scores needed
-  if (!all) {
-    const int hq = threadIdx.x & 3;
+  lds_barrier();
+  if (scored) {
     float wl[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) wl[k] = lse[4 * hq + k];
-    for (int j = threadIdx.x >> 2; j < nb; j += kSelThreads / 4) {
-      const int ilo = block_tok_lo(j, a.beta, a.l, a.d);
-      int ihi = block_tok_hi(j, a.beta, a.d);
-      ihi = ihi < nvis - 1 ? ihi : nvis - 1;
-      float S = 0.f;
-      if (ilo <= ihi)
-        for (int T = ilo / 64; T <= ihi / 64; ++T) S += tile_block_score(a, bkv, T, j, hq, wl);
-      S = group_sum<4>(S);
-      if (hq == 0) Ss[j] = S;
+    for (int j0 = jq;; j0 += kSelLanes * kSelUnroll) {
+#pragma unroll
+      for (int u = 0; u < kSelUnroll; ++u) {
+        const int j = j0 + kSelLanes * u;
+        float S = 0.f;
+        if (bm[u].ntile >= 1) S = mass_score(bm[u].m0, bm[u].r0, wl);
+        if (bm[u].ntile >= 2) S += mass_score(bm[u].m1, bm[u].r1, wl);
+        for (int T = bm[u].ta + 2; T < bm[u].ta + bm[u].ntile; ++T) {  // wide blocks only
+          const int jj = j - (T * 64 * a.d) / a.beta;
+          const f32x4 m = *reinterpret_cast<const f32x4*>(
+              a.cb + ((bkv * a.NT + T) * a.NBT + jj) * 16 + 4 * hq);
+          const f32x4 r =
+              *reinterpret_cast<const f32x4*>(a.tref + (bkv * a.NT + T) * 16 + 4 * hq);
+          S += mass_score(m, r, wl);
+        }
+        S = group_sum<4>(S);
+        if (hq == 0 && j < nb) Ss[j] = S;
+      }
+      const int jn = j0 + kSelLanes * kSelUnroll;
+      if (jn - jq >= nb) break;  // uniform
+#pragma unroll
+      for (int u = 0; u < kSelUnroll; ++u) {
+        const int j = jn + kSelLanes * u;
+        bm[u] = fetch_block(a, bkv, j < nb ? j : nb - 1, nvis, hq);
+      }
     }
+  } else if (!all) {
+    for (int j = threadIdx.x; j < nb; j += kSelThreads) Ss[j] = 0.f;
   }
   __syncthreads();
   const int lane = threadIdx.x & 63;
@@ -471,7 +537,7 @@ __global__ __launch_bounds__(256) void dec_tiles_kernel(DecodeArgs a) {
   f32x4 acc[4];
   kv.scores(qf, acc);
   kv.stage(Vt[wave], lane);
-  __syncthreads();
+  __asm__ volatile("" ::: "memory");  // Vt[wave] is this wave's own: LDS keeps its order
 
   f32x4 O[2][DT];
 #pragma unroll

@@ -90,6 +90,14 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Workgroup barrier that orders LDS only: unlike __syncthreads it does not wait for global
+// loads in flight, so prefetches issued before it stay outstanding.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int GS>
 __device__ __forceinline__ float group_max(float v) {
 #pragma unroll

@@ -28,6 +28,56 @@ sys.path.insert(0, ROOT)
 METRIC = "NSA prefill tok/s @64k (MFMA % peak); decode tok/s + KV GB/s @64k (HBM % peak)"
 MFMA_PEAK_BF16 = 2.5e15   # dense bf16 matrix peak, FLOP/s
 HBM_PEAK = 8.0e12         # bytes/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "dynamic_block_sparse_fwd_amd", "csrc")
+# the sources a kernel's code object depends on (its translation unit, shared headers, flags)
+KERNEL_SOURCES = {
+    "selected_kernel": ["prefill.hip", "attn_tile.h", "dev_common.h", "kernels.h", "../build.py"],
+    "dec_cmp_kernel": ["decode.hip", "attn_tile.h", "dev_common.h", "kernels.h", "../build.py"],
+    "moba_block_kernel": ["moba.hip", "attn_tile.h", "dev_common.h", "kernels.h", "../build.py"],
+}
+
+
+def source_digest(kernel):
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each divided by what the same counter reads per byte of a
+    plain copy of known size.  None when there is no summary or the kernel's sources changed
+    since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        k = tr["kernels"][kernel]
+        cal = tr["copy_calibration"]
+    except (OSError, KeyError, ValueError):
+        return None
+    if k.get("source_sha256") != source_digest(kernel):
+        return None
+    fetch = k["fetch_kib_per_dispatch"] * 1024.0 / cal["fetch_counter_bytes_per_byte"]
+    write = k["write_kib_per_dispatch"] * 1024.0 / cal["write_counter_bytes_per_byte"]
+    return int(round(fetch + write))
+
+
+def copy_calibration():
+    """A plain device copy of known size (256 MiB read + 256 MiB written per dispatch, three
+    dispatches) for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    x = torch.ones(1 << 26, dtype=torch.int32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_dispatch": x.numel() * 4}), flush=True)
 
 
 # ----------------------------------------------------------------------------- HIP events
@@ -68,6 +118,13 @@ class HipEvents:
 
 
 # ----------------------------------------------------------------------------- work counts
+
+def gather_bytes(B, T, Hkv, D, beta=64, n=16):
+    """K+V bytes the selected branch gathers: one bf16 K and V row per (position, KV group,
+    selected key), causal keys of the selected blocks only."""
+    _, slc, _ = prefill_pairs(T, beta=beta, n=n)
+    return B * Hkv * slc * 2 * D * 2
+
 
 def prefill_pairs(T, l=32, d=16, beta=64, n=16, n_local=2, w=512):
     """Query-key pairs per head performed by each branch (the method's algorithmic work)."""
@@ -152,7 +209,11 @@ def bench_prefill(args):
                   "achieved": flops[dom] / (stage_ms[dom] * 1e-3) / 1e12,
                   "peak": MFMA_PEAK_BF16 / 1e12, "unit": "TFLOP/s",
                   "frac": flops[dom] / (stage_ms[dom] * 1e-3) / MFMA_PEAK_BF16,
-                  "traffic": None},
+                  "traffic": measured_traffic("selected_kernel") if dom == "selected" else None},
+        # the selected branch gathers a 64-key K+V tile per (position, group, selected block):
+        # its bound is the cache hierarchy's gather bandwidth, reported beside the MFMA figure
+        selected_gather={"bytes": gather_bytes(B, T, Hkv, D),
+                         "gbs": gather_bytes(B, T, Hkv, D) / (stage_ms["selected"] * 1e-3) / 1e9},
     )
     del d, out, idx, ws
     torch.cuda.empty_cache()
@@ -275,7 +336,7 @@ def bench_decode(args, B=32, L=65536, Hkv=4, G=16, D=128, seed=3, calls=20):
                      "achieved": round(cmp_bytes / (med["cmp_stream"] * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(cmp_bytes / (med["cmp_stream"] * 1e-3) / HBM_PEAK, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic("dec_cmp_kernel")},
         "timing": "median of %d calls, HIP events around each call, 1 GiB read between "
                   "calls to evict the Infinity Cache" % calls,
     }
@@ -395,13 +456,28 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-moba", action="store_true")
+    ap.add_argument("--only", choices=("prefill", "decode", "moba"),
+                    help="run one workload and print its result alone (for profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run the plain copy used to scale the traffic counters, then exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the NSA/MoBA forward on a single "
               "MI355X (multi-GPU sharding is a design note, not implemented); use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
+    if args.only == "decode":
+        dec, _ = bench_decode(args)
+        print(json.dumps({"decode": dec}), flush=True)
+        return
+    if args.only == "moba":
+        mo, _ = bench_moba(args)
+        print(json.dumps({"moba": mo}), flush=True)
+        return
     pre, x = bench_prefill(args)
     line = {
         "metric": METRIC,
@@ -424,8 +500,13 @@ def main():
         "prefill": {"mfma_frac_total": round(pre["mfma_frac"], 4),
                     "algorithmic_tflop": round(pre["algorithmic_tflop"], 4),
                     "events_ms_per_step": round(pre["events_ms_per_step"], 4),
-                    "stages": pre["stages"]},
+                    "stages": pre["stages"],
+                    "selected_gather": {"bytes": pre["selected_gather"]["bytes"],
+                                        "gbs": round(pre["selected_gather"]["gbs"], 1)}},
     }
+    if args.only == "prefill":
+        print(json.dumps(line), flush=True)
+        return
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(x, args.seq, args.cpu_rows)
     del x

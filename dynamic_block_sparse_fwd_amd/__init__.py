@@ -53,6 +53,8 @@ EXPORTS = {
     "moba_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
     "nsa_compress": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p]),
     "nsa_prefill": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "nsa_prefill_stages": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint] + [ctypes.c_void_p] * 9
+                           + [ctypes.c_size_t, ctypes.c_void_p]),
     "nsa_prefill_timed": (ctypes.c_int,
                           [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p,
                                                      ctypes.c_void_p]),
@@ -239,6 +241,39 @@ def nsa_prefill(cfg: NsaConfig, q, k, v, wk, wv, gate, out=None, sel_idx=None, w
         None if sel_idx is None else _dev(sel_idx, "sel_idx", (torch.int32,), (B, T, Hkv, cfg.top_n)),
         ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream), *extra)
     _check(st, "nsa_prefill")
+    return out, sel_idx
+
+
+STAGE_CMP_SELECT, STAGE_WINDOW, STAGE_SELECTED = 1, 2, 4
+STAGE_ALL = STAGE_CMP_SELECT | STAGE_WINDOW | STAGE_SELECTED
+
+
+def nsa_prefill_stages(cfg: NsaConfig, stages: int, q, k, v, wk, wv, gate, out=None,
+                       sel_idx=None, ws=None, stream=None):
+    """The prefill branches selected by `stages` (STAGE_* bits), same kernels as nsa_prefill.
+    With STAGE_SELECTED but not STAGE_CMP_SELECT, sel_idx is the input selection.  wk, wv may be
+    None without STAGE_CMP_SELECT.  Returns (out, sel_idx)."""
+    torch = _torch()
+    lib = load_library()
+    c = cfg.c()
+    B, T, Hkv, Hq, D = cfg.B, cfg.T, cfg.Hkv, cfg.Hq, cfg.D
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
+    if sel_idx is None and stages & STAGE_CMP_SELECT:
+        sel_idx = torch.empty((B, T, Hkv, cfg.top_n), dtype=torch.int32, device=dev)
+    ws = _workspace(lib.nsa_prefill_workspace_bytes(ctypes.byref(c)), dev, ws)
+    bt = _bf16_types()
+    st = lib.nsa_prefill_stages(
+        ctypes.byref(c), int(stages), _dev(q, "q", bt, (B, T, Hq, D)),
+        _dev(k, "k", bt, (B, Hkv, T, D)), _dev(v, "v", bt, (B, Hkv, T, D)),
+        None if wk is None else _dev(wk, "wk", bt, (cfg.cmp_len, D, D)),
+        None if wv is None else _dev(wv, "wv", bt, (cfg.cmp_len, D, D)),
+        _dev(gate, "gate", (torch.float32,), (B, T, Hq, 3)),
+        _dev(out, "out", (torch.float32,), (B, T, Hq, D)),
+        None if sel_idx is None else _dev(sel_idx, "sel_idx", (torch.int32,), (B, T, Hkv, cfg.top_n)),
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream))
+    _check(st, "nsa_prefill_stages")
     return out, sel_idx
 
 

@@ -242,15 +242,23 @@ int nsa_compress(const nsa_config* c, const void* x, const void* w, void* xc, vo
   return hip_status();
 }
 
-static int prefill_impl(const nsa_config* c, const void* q, const void* k, const void* v,
-                        const void* wk, const void* wv, const float* gate, float* out,
-                        int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream,
-                        hipEvent_t* ev) {
+// Runs the requested prefill stages (NSA_STAGE_* bits) on the stream.  Without the compressed
+// stage, `out` is cleared first and the window / selected stages add into it; the selected
+// stage alone reads its block indices from `sel_idx`.
+static int prefill_run(const nsa_config* c, unsigned stages, const void* q, const void* k,
+                       const void* v, const void* wk, const void* wv, const float* gate,
+                       float* out, int32_t* sel_idx, void* ws, size_t ws_bytes,
+                       hipStream_t stream, hipEvent_t* ev) {
   int st = check_nsa(c);
   if (st != NSA_OK) return st;
-  if (!q || !k || !v || !wk || !wv || !gate || !out || !ws) return NSA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(wk) || !aligned16(wv) ||
-      !aligned16(gate) || !aligned16(out) || !aligned16(ws) ||
+  if (stages == 0 || (stages & ~(unsigned)NSA_STAGE_ALL) != 0) return NSA_ERR_INVALID_ARG;
+  const bool s_cmp = stages & NSA_STAGE_CMP_SELECT, s_win = stages & NSA_STAGE_WINDOW;
+  const bool s_slc = stages & NSA_STAGE_SELECTED;
+  if (!q || !k || !v || !gate || !out || !ws) return NSA_ERR_INVALID_ARG;
+  if (s_cmp && (!wk || !wv)) return NSA_ERR_INVALID_ARG;
+  if (s_slc && !s_cmp && !sel_idx) return NSA_ERR_INVALID_ARG;  // indices are an input then
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (wk && !aligned16(wk)) ||
+      (wv && !aligned16(wv)) || !aligned16(gate) || !aligned16(out) || !aligned16(ws) ||
       (sel_idx && !aligned16(sel_idx)))
     return NSA_ERR_INVALID_ARG;
   const PrefillPlan p = plan_prefill(c);
@@ -270,13 +278,15 @@ static int prefill_impl(const nsa_config* c, const void* q, const void* k, const
     if (ev != nullptr) (void)hipEventRecord(ev[sidx], stream);
   };
   mark(0);
-  launch_transpose(static_cast<const uint16_t*>(v), vt, BH, c->T, c->D, p.TP, stream);
-  if (p.ncmp > 0) {
+  if (s_win || s_slc)
+    launch_transpose(static_cast<const uint16_t*>(v), vt, BH, c->T, c->D, p.TP, stream);
+  if (s_cmp && p.ncmp > 0) {
     launch_transpose(static_cast<const uint16_t*>(wk), wkt, 1, LD, c->D, LD, stream);
     launch_transpose(static_cast<const uint16_t*>(wv), wvt, 1, LD, c->D, LD, stream);
   }
+  if (!s_cmp) launch_fill_zero(out, (size_t)c->B * c->T * c->Hkv * c->G * c->D, stream);
   mark(1);
-  if (p.ncmp > 0) {
+  if (s_cmp && p.ncmp > 0) {
     launch_compress(static_cast<const uint16_t*>(k), wkt, kcb, nullptr, BH, c->T, c->D,
                     c->cmp_len, c->cmp_stride, p.ncmp, p.NCP, p.NCP, stream);
     launch_compress(static_cast<const uint16_t*>(v), wvt, nullptr, vct, BH, c->T, c->D,
@@ -297,13 +307,29 @@ static int prefill_impl(const nsa_config* c, const void* q, const void* k, const
   a.ncmp = p.ncmp; a.NCP = p.NCP; a.TP = p.TP; a.nblk = p.nblk;
   a.scale_log2 = c->scale * 1.4426950408889634f;
   mark(2);
-  launch_cmp_select(a, stream);
+  if (s_cmp) launch_cmp_select(a, stream);
   mark(3);
-  launch_window(a, stream);
+  if (s_win) launch_window(a, stream);
   mark(4);
-  launch_selected(a, stream);
+  if (s_slc) launch_selected(a, stream);
   mark(5);
   return hip_status();
+}
+
+static int prefill_impl(const nsa_config* c, const void* q, const void* k, const void* v,
+                        const void* wk, const void* wv, const float* gate, float* out,
+                        int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream,
+                        hipEvent_t* ev) {
+  return prefill_run(c, NSA_STAGE_ALL, q, k, v, wk, wv, gate, out, sel_idx, ws, ws_bytes,
+                     stream, ev);
+}
+
+int nsa_prefill_stages(const nsa_config* c, unsigned stages, const void* q, const void* k,
+                       const void* v, const void* wk, const void* wv, const float* gate,
+                       float* out, int32_t* sel_idx, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  return prefill_run(c, stages, q, k, v, wk, wv, gate, out, sel_idx, ws, ws_bytes, stream,
+                     nullptr);
 }
 
 int nsa_prefill(const nsa_config* c, const void* q, const void* k, const void* v, const void* wk,

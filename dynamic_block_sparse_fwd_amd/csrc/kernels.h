@@ -80,6 +80,9 @@ struct MobaArgs {
 // ev: nullptr or NSA_MOBA_NSTAGES + 1 events; ev[0] is recorded by the caller.
 void launch_moba(const MobaArgs& a, hipStream_t s, hipEvent_t* ev);
 
+// p[0 .. n) = 0 (n a multiple of 4, p 16-byte aligned); a kernel, so it may be captured.
+void launch_fill_zero(float* p, size_t n, hipStream_t s);
+
 // x [BH, rows, cols] -> xt [BH, cols, rows_pad] (bf16), zero-filled for rows..rows_pad-1.
 void launch_transpose(const uint16_t* x, uint16_t* xt, int BH, int rows, int cols, int rows_pad,
                       hipStream_t s);

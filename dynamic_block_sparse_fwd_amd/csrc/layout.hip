@@ -39,6 +39,20 @@ __global__ __launch_bounds__(256) void transpose_kernel(const u16* __restrict__ 
   }
 }
 
+__global__ __launch_bounds__(256) void fill_zero_kernel(float4* __restrict__ p, long n4) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+void launch_fill_zero(float* p, size_t n, hipStream_t s) {
+  const long n4 = (long)(n / 4);
+  if (n4 > 0) {
+    const long want = (n4 + 255) / 256;
+    fill_zero_kernel<<<(unsigned)(want < 8192 ? want : 8192), 256, 0, s>>>(
+        reinterpret_cast<float4*>(p), n4);
+  }
+}
+
 void launch_transpose(const uint16_t* x, uint16_t* xt, int BH, int rows, int cols, int rows_pad,
                       hipStream_t s) {
   dim3 grid((rows_pad + 63) / 64, (cols + 63) / 64, BH);

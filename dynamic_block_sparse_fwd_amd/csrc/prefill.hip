@@ -451,9 +451,10 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void window_kernel(PrefillArgs a
 
 // One wave per (position, KV group): the group's heads form the 16 MFMA rows; K and V
 // fragments are read straight from global memory (16-byte loads, no LDS).  The wave's tiles
-// (64 keys each, in selection order) are listed once, lane e holding the first key of tile e;
-// the selected blocks precede the -1 padding and a block's tiles past t come last, so the
-// valid tiles form a prefix.  Each tile's K and V are fetched while the previous tile computes.
+// (64 keys each, in index-list order) are listed once, lane e holding the first key of tile e
+// or -1 (padding, a block outside [0, nblk), a tile past t); the valid lanes are visited in
+// order through the ballot mask.  Each tile's K and V are fetched while the previous tile
+// computes.
 // Workgroups are dealt to the 8 XCDs round-robin; the linear index is remapped so that XCD x
 // runs a contiguous 1/8 of the (sequence, group, position) range: the waves that share an
 // XCD's L2 then read the same group's K/V at nearby positions.
@@ -483,10 +484,11 @@ __global__ __launch_bounds__(256, 2) void selected_kernel(PrefillArgs a) {
     if (lane < a.top_n * per) {
       const int j = irow[lane / per];
       const int k0 = j * a.beta + 64 * (lane % per);
-      if (j >= 0 && k0 <= t) my_key0 = k0;
+      if (j >= 0 && j < a.nblk && k0 <= t) my_key0 = k0;
     }
   }
-  const int ntile = (int)__popcll(__ballot(my_key0 >= 0));
+  uint64_t todo = __ballot(my_key0 >= 0);  // wave-uniform: valid lanes still to visit
+  const int ntile = (int)__popcll(todo);
 
   bf16x8 qf[D / 32];
   {
@@ -522,16 +524,18 @@ __global__ __launch_bounds__(256, 2) void selected_kernel(PrefillArgs a) {
   f32x4 O[DT];
 #pragma unroll
   for (int n = 0; n < DT; ++n) O[n] = zero4();
+  int key0 = 0;
   if (ntile > 0) {
-    const int k00 = __builtin_amdgcn_readfirstlane(my_key0);
-    load_k(k00);
-    load_v(k00);
+    key0 = __builtin_amdgcn_readlane(my_key0, __builtin_ctzll(todo));
+    todo &= todo - 1;
+    load_k(key0);
+    load_v(key0);
   }
   for (int i = 0; i < ntile; ++i) {
-    const int key0 = __builtin_amdgcn_readlane(my_key0, i);
     // the last tile re-fetches itself: unconditional loads keep the wait counts exact (a load
     // under a branch makes the join wait for every load in flight)
-    const int knext = (i + 1 < ntile) ? __builtin_amdgcn_readlane(my_key0, i + 1) : key0;
+    const int knext = todo ? __builtin_amdgcn_readlane(my_key0, __builtin_ctzll(todo)) : key0;
+    todo &= todo - 1;
     float z[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -580,6 +584,7 @@ __global__ __launch_bounds__(256, 2) void selected_kernel(PrefillArgs a) {
         O[n] = mfma16x16x32(__builtin_bit_cast(bf16x8, vr[kc * DT + n]), pb, O[n]);
     }
     load_v(knext);
+    key0 = knext;
   }
 
   const float L = col_sum4(lrun);

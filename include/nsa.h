@@ -126,6 +126,34 @@ int nsa_prefill(const nsa_config* cfg, const void* q, const void* k, const void*
                 int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The prefill branches one at a time (the kernels nsa_prefill runs, same code path), for
+ * per-branch checks (podcast notes EP94 section 5: compressed, selected and sliding-window
+ * branches, mixed by the gate).  `stages` ORs:
+ *   NSA_STAGE_CMP_SELECT  compression of K and V, compressed attention, block importance, group
+ *                         sum and top-n: out = g0 * o_cmp, selection written to sel_idx (or
+ *                         kept in ws when sel_idx is NULL)
+ *   NSA_STAGE_WINDOW      out (+)= g2 * o_win
+ *   NSA_STAGE_SELECTED    out (+)= g1 * o_slc over the blocks in sel_idx; without
+ *                         NSA_STAGE_CMP_SELECT sel_idx is an INPUT (required): per (t, group)
+ *                         top_n block indices; entries outside [0, ceil(T/sel_block)) (e.g. the
+ *                         -1 padding) are skipped, tiles past t are skipped
+ * Without NSA_STAGE_CMP_SELECT out is cleared first.  The stages accumulate in nsa_prefill's
+ * order (compressed, window, selected), so NSA_STAGE_ALL reproduces nsa_prefill bit for bit and
+ * the sum of separately computed stages equals it to fp32 rounding.  There is no
+ * separate combine stage: each branch adds its gated output.  wk, wv may be NULL without
+ * NSA_STAGE_CMP_SELECT.  Same workspace and errors as nsa_prefill; NSA_ERR_INVALID_ARG for an
+ * empty or unknown stage mask.
+ */
+#define NSA_STAGE_CMP_SELECT 1u
+#define NSA_STAGE_WINDOW 2u
+#define NSA_STAGE_SELECTED 4u
+#define NSA_STAGE_ALL 7u
+int nsa_prefill_stages(const nsa_config* cfg, unsigned stages, const void* q, const void* k,
+                       const void* v, const void* wk, const void* wv, const float* gate,
+                       float* out, int32_t* sel_idx, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/*
  * Instrumented nsa_prefill: identical work, plus events[s] recorded on `stream` before stage s
  * and events[NSA_PREFILL_NSTAGES] after the last stage.  Stages: 0 layout (value and weight
  * transposes), 1 block compression of K and V, 2 compressed attention + block importance +

@@ -111,6 +111,26 @@ def test_entry_points_reject_before_any_launch(lib):
         nsa.NSA_ERR_INVALID_ARG
 
 
+def test_prefill_stages_reject_before_any_launch(lib):
+    c = nsa.NsaConfig(1, 2048, 1, 4, 64).c()
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced
+    ws = 1 << 40
+    # empty and unknown stage masks
+    for mask in (0, 8, 15):
+        assert lib.nsa_prefill_stages(ctypes.byref(c), mask, fake, fake, fake, fake, fake, fake,
+                                      fake, fake, fake, ws, None) == nsa.NSA_ERR_INVALID_ARG
+    # the selected stage alone needs the index list as input
+    assert lib.nsa_prefill_stages(ctypes.byref(c), nsa.STAGE_SELECTED, fake, fake, fake, None,
+                                  None, fake, fake, None, fake, ws, None) == nsa.NSA_ERR_INVALID_ARG
+    # the compressed stage needs the compressor weights
+    assert lib.nsa_prefill_stages(ctypes.byref(c), nsa.STAGE_CMP_SELECT, fake, fake, fake, None,
+                                  fake, fake, fake, fake, fake, ws, None) == nsa.NSA_ERR_INVALID_ARG
+    # workspace too small
+    assert lib.nsa_prefill_stages(ctypes.byref(c), nsa.STAGE_WINDOW, fake, fake, fake, None, None,
+                                  fake, fake, None, fake, 16, None) == nsa.NSA_ERR_WORKSPACE
+
+
 def test_product_path_does_not_touch_the_oracle():
     """The binding and kernels never import or link the CPU oracle."""
     pkg = os.path.join(ROOT, "dynamic_block_sparse_fwd_amd")

@@ -148,3 +148,68 @@ def test_prefill_64k_sampled_rows():
     rest = rng.choice(np.arange(1024, T - 64), 4096 - 1024 - 64, replace=False)
     rt = np.unique(np.concatenate([np.arange(1024), np.arange(T - 64, T), rest])).astype(np.int32)
     compare_prefill(cfg, x, np.zeros_like(rt), rt, gout, gidx, "prefill 64k")
+
+
+def _stage_inputs(cfg, x):
+    nsa = _nsa()
+    c = nsa.NsaConfig(cfg.B, cfg.T, cfg.Hkv, cfg.G, cfg.D, cfg.cmp_len, cfg.cmp_stride,
+                      cfg.sel_block, cfg.top_n, cfg.n_local, cfg.window, cfg.scale)
+    return nsa, c, {k: to_dev(v) for k, v in x.items()}
+
+
+def test_prefill_stages_compose_bit_exact():
+    """nsa_prefill_stages runs the same kernels: all stages at once equal nsa_prefill bit for
+    bit, and the three stages run separately add up to it to fp32 rounding (inside a kernel the
+    gated add is one fused multiply-add, so summing finished stages rounds once more)."""
+    cfg = O.NsaCfg(2, 1300, 2, 16, 128)
+    x = S.nsa_prefill_inputs(11, 2, 1300, 2, 16, 128)
+    nsa, c, d = _stage_inputs(cfg, x)
+    full, fidx = nsa.nsa_prefill(c, d["q"], d["k"], d["v"], d["wk"], d["wv"], d["gate"])
+    allst, aidx = nsa.nsa_prefill_stages(c, nsa.STAGE_ALL, d["q"], d["k"], d["v"], d["wk"],
+                                         d["wv"], d["gate"])
+    o_c, cidx = nsa.nsa_prefill_stages(c, nsa.STAGE_CMP_SELECT, d["q"], d["k"], d["v"], d["wk"],
+                                       d["wv"], d["gate"])
+    o_w, _ = nsa.nsa_prefill_stages(c, nsa.STAGE_WINDOW, d["q"], d["k"], d["v"], None, None,
+                                    d["gate"])
+    o_s, _ = nsa.nsa_prefill_stages(c, nsa.STAGE_SELECTED, d["q"], d["k"], d["v"], None, None,
+                                    d["gate"], sel_idx=cidx)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(allst.cpu().numpy(), full.cpu().numpy())
+    np.testing.assert_array_equal(aidx.cpu().numpy(), fidx.cpu().numpy())
+    np.testing.assert_array_equal(cidx.cpu().numpy(), fidx.cpu().numpy())
+    summed = (o_c + o_w) + o_s
+    np.testing.assert_allclose(summed.cpu().numpy(), full.cpu().numpy(), rtol=2e-6, atol=2e-6)
+
+
+def test_prefill_window_and_selected_stages_against_oracle():
+    """Window stage = g2 * o_win; selected stage with the ORACLE's indices (no near-tie
+    question) = g1 * o_slc; then the same with an index list holding -1 holes in the middle,
+    an out-of-range block and a repeated block, which the oracle treats identically."""
+    cfg = O.NsaCfg(1, 1500, 2, 8, 128, top_n=6, n_local=1, window=300)
+    x = S.nsa_prefill_inputs(12, 1, 1500, 2, 8, 128)
+    kc = O.compress(x["k"], x["wk"], 32, 16)
+    vc = O.compress(x["v"], x["wv"], 32, 16)
+    rb, rt = all_rows(cfg)
+    ora = O.nsa_prefill_rows(cfg, x["q"], x["k"], x["v"], kc, vc, x["gate"], rb, rt,
+                             branches=True)
+    nsa, c, d = _stage_inputs(cfg, x)
+    g = x["gate"][0]
+    o_w, _ = nsa.nsa_prefill_stages(c, nsa.STAGE_WINDOW, d["q"], d["k"], d["v"], None, None,
+                                    d["gate"])
+    check_close(o_w.cpu().numpy()[0], g[..., 2:3] * ora["o_win"], "window stage")
+    idx = ora["idx"].reshape(1, cfg.T, cfg.Hkv, cfg.top_n).astype(np.int32)
+    o_s, _ = nsa.nsa_prefill_stages(c, nsa.STAGE_SELECTED, d["q"], d["k"], d["v"], None, None,
+                                    d["gate"], sel_idx=to_dev(idx))
+    check_close(o_s.cpu().numpy()[0], g[..., 1:2] * ora["o_slc"], "selected stage")
+    # holes, an out-of-range block and a repeat
+    rng = np.random.default_rng(12)
+    idx2 = idx.copy()
+    holes = rng.random(idx2.shape) < 0.2
+    idx2[holes] = -1
+    idx2[..., 0] = np.where(rng.random(idx2.shape[:-1]) < 0.1, cfg.nblk + 3, idx2[..., 0])
+    idx2[..., 1] = np.where(rng.random(idx2.shape[:-1]) < 0.1, idx2[..., 2], idx2[..., 1])
+    ora2 = O.nsa_prefill_rows(cfg, x["q"], x["k"], x["v"], kc, vc, x["gate"], rb, rt,
+                              idx_in=idx2[0], branches=True)
+    o_s2, _ = nsa.nsa_prefill_stages(c, nsa.STAGE_SELECTED, d["q"], d["k"], d["v"], None, None,
+                                     d["gate"], sel_idx=to_dev(idx2))
+    check_close(o_s2.cpu().numpy()[0], g[..., 1:2] * ora2["o_slc"], "selected stage, holes")

@@ -93,12 +93,13 @@ int check_moba(const moba_config* c) {
   if (c->D != 64 && c->D != 128) return NSA_ERR_UNSUPPORTED;
   if (c->block % 64 != 0 || c->T % c->block != 0) return NSA_ERR_UNSUPPORTED;
   if (c->top_k > 8) return NSA_ERR_UNSUPPORTED;
+  if (c->T / c->block > 16384) return NSA_ERR_UNSUPPORTED;  // per-head block counts in LDS
   if ((long)c->T > (1L << 27)) return NSA_ERR_UNSUPPORTED;
   return NSA_OK;
 }
 
 struct MobaPlan {
-  size_t vt, hi, lo, count, cursor, offset, tstart, ntiles, idx, list, po, pml, total;
+  size_t vt, hi, lo, count, rank, offset, tstart, ntiles, tile_entry, idx, list, po, pml, total;
   int nb, max_tiles;
 };
 
@@ -112,15 +113,17 @@ MobaPlan plan_moba(const moba_config* c) {
   p.vt = off;     off += align_up(BH * c->D * c->T * 2);
   p.hi = off;     off += align_up(BH * p.nb * c->D * 2);
   p.lo = off;     off += align_up(BH * p.nb * c->D * 2);
-  p.count = off;  off += align_up(BH * p.nb * 4);
-  p.cursor = off; off += align_up(BH * p.nb * 4);
-  p.offset = off; off += align_up(BH * p.nb * 4);
+  p.count = off;  off += align_up(BH * p.nb * kMobaChunks * 4);
+  p.rank = off;   off += align_up(entries * 4 + 4);
+  p.offset = off; off += align_up((BH * p.nb + 1) * 4);
   p.tstart = off; off += align_up(BH * p.nb * 4);
   p.ntiles = off; off += align_up(4);
+  p.tile_entry = off; off += align_up((size_t)p.max_tiles * 4);
   p.idx = off;    off += align_up(rows * (c->top_k + 1) * 4);
   p.list = off;   off += align_up(entries * 4 + 4);
-  p.po = off;     off += align_up(entries * c->D * 4 + 4);
-  p.pml = off;    off += align_up(entries * 2 * 4 + 4);
+  // one spare slot each: the merge loads slot 0 unconditionally, also when top_k = 0
+  p.po = off;     off += align_up((entries + 1) * c->D * 4);
+  p.pml = off;    off += align_up((entries + 1) * 2 * 4);
   p.total = off;
   return p;
 }
@@ -449,10 +452,11 @@ static int moba_impl(const moba_config* c, const void* q, const void* k, const v
   a.kb_hi = reinterpret_cast<uint16_t*>(base + p.hi);
   a.kb_lo = reinterpret_cast<uint16_t*>(base + p.lo);
   a.count = reinterpret_cast<int32_t*>(base + p.count);
-  a.cursor = reinterpret_cast<int32_t*>(base + p.cursor);
+  a.rank = reinterpret_cast<int32_t*>(base + p.rank);
   a.offset = reinterpret_cast<int32_t*>(base + p.offset);
   a.tstart = reinterpret_cast<int32_t*>(base + p.tstart);
   a.ntiles = reinterpret_cast<int32_t*>(base + p.ntiles);
+  a.tile_entry = reinterpret_cast<int32_t*>(base + p.tile_entry);
   a.list = reinterpret_cast<int32_t*>(base + p.list);
   a.po = reinterpret_cast<float*>(base + p.po);
   a.pml = reinterpret_cast<float*>(base + p.pml);

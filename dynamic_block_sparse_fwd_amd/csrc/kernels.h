@@ -57,6 +57,8 @@ int decode_max_splits();
 int decode_max_tile_list();
 size_t decode_select_lds_bytes(int nch, int nblk);
 
+constexpr int kMobaChunks = 8;  // T-chunks per head counted by separate workgroups
+
 struct MobaArgs {
   const uint16_t* q;   // [B, T, H, D]
   const uint16_t* k;   // [B, H, T, D]
@@ -65,11 +67,13 @@ struct MobaArgs {
   int32_t* idx;        // [B, T, H, top_k + 1]
   uint16_t* kb_hi;     // [B*H, nb, D] block key mean, bf16 high part
   uint16_t* kb_lo;     // [B*H, nb, D] bf16 of the remainder
-  int32_t* count;      // [B*H*nb] queries that chose each block
-  int32_t* cursor;     // [B*H*nb] fill cursors
-  int32_t* offset;     // [B*H*nb] list offsets (exclusive prefix of count)
+  int32_t* count;      // [B*H*nb, kMobaChunks] queries of each T-chunk that chose each block,
+                       // turned into chunk offsets inside the block's list by the scan
+  int32_t* rank;       // [B*T*H, top_k] position of each (query, slot) in its block's list
+  int32_t* offset;     // [B*H*nb + 1] list offsets (exclusive prefix of the list lengths)
   int32_t* tstart;     // [B*H*nb] first 128-row tile of each list
   int32_t* ntiles;     // [1] total tiles
+  int32_t* tile_entry; // [max_tiles] the list each 128-row tile belongs to
   int32_t* list;       // [B*T*H*top_k] (t << 4 | slot)
   float* po;           // [B*T*H, top_k, D] partial outputs (relative to the partial max)
   float* pml;          // [B*T*H, top_k, 2] partial (max, sum), log2 units
@@ -83,7 +87,8 @@ void launch_moba(const MobaArgs& a, hipStream_t s, hipEvent_t* ev);
 // p[0 .. n) = 0 (n a multiple of 4, p 16-byte aligned); a kernel, so it may be captured.
 void launch_fill_zero(float* p, size_t n, hipStream_t s);
 
-// x [BH, rows, cols] -> xt [BH, cols, rows_pad] (bf16), zero-filled for rows..rows_pad-1.
+// x [BH, rows, cols] -> xt [BH, cols, rows_pad] (bf16), zero-filled for rows..rows_pad-1;
+// cols and rows_pad multiples of 64, x and xt 16-byte aligned.
 void launch_transpose(const uint16_t* x, uint16_t* xt, int BH, int rows, int cols, int rows_pad,
                       hipStream_t s);
 

@@ -6,36 +6,37 @@
 
 namespace nsa {
 
-// x [BH, rows, cols] -> xt [BH, cols, rows_pad]; one 64x64 tile per workgroup.
+// x [BH, rows, cols] -> xt [BH, cols, rows_pad]; one 64x64 tile per workgroup, 16-byte
+// global loads and stores (cols and rows_pad multiples of 64, 16-byte aligned bases); rows past
+// `rows` are written as zero.
+constexpr int kTP = 72;  // LDS row pitch in bf16 (16-byte aligned rows)
+
 __global__ __launch_bounds__(256) void transpose_kernel(const u16* __restrict__ x,
                                                         u16* __restrict__ xt, int rows,
                                                         int cols, int rows_pad) {
-  __shared__ u16 tile[64][66];
+  __shared__ __align__(16) u16 tile[64][kTP];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const long bh = blockIdx.z;
   const int tid = threadIdx.x;
-  {
-    const int r = tid >> 2, cc = (tid & 3) * 16;
-    const int row = r0 + r;
+  const int ch = tid & 7;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int col = c0 + cc + e;
-      u16 v = 0;
-      if (row < rows && col < cols) v = x[(bh * rows + row) * cols + col];
-      tile[r][cc + e] = v;
-    }
+  for (int pass = 0; pass < 2; ++pass) {
+    const int r = (tid >> 3) + 32 * pass, row = r0 + r;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < rows)
+      v = *reinterpret_cast<const u32x4*>(x + (bh * rows + row) * cols + c0 + 8 * ch);
+    *reinterpret_cast<u32x4*>(&tile[r][8 * ch]) = v;
   }
   __syncthreads();
-  {
-    const int c = tid >> 2, rr = (tid & 3) * 16;
-    const int col = c0 + c;
-    if (col < cols) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = r0 + rr + e;
-        if (row < rows_pad) xt[(bh * cols + col) * rows_pad + row] = tile[rr + e][c];
-      }
-    }
+  for (int pass = 0; pass < 2; ++pass) {
+    const int c = (tid >> 3) + 32 * pass;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)tile[8 * ch + 2 * e][c] | ((uint32_t)tile[8 * ch + 2 * e + 1][c] << 16);
+    *reinterpret_cast<u32x4*>(xt + (bh * cols + c0 + c) * rows_pad + r0 + 8 * ch) =
+        u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -55,7 +56,7 @@ void launch_fill_zero(float* p, size_t n, hipStream_t s) {
 
 void launch_transpose(const uint16_t* x, uint16_t* xt, int BH, int rows, int cols, int rows_pad,
                       hipStream_t s) {
-  dim3 grid((rows_pad + 63) / 64, (cols + 63) / 64, BH);
+  dim3 grid(rows_pad / 64, cols / 64, BH);
   transpose_kernel<<<grid, 256, 0, s>>>(x, xt, rows, cols, rows_pad);
 }
 

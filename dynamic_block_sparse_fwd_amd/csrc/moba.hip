@@ -8,12 +8,12 @@
 // kernel (gathered query rows x one block's keys, partial max/sum/output per query and slot)
 // and one query-major kernel that attends the causal own block and merges the partials.
 //
-//   moba_zero_kernel   clears per-block counters
 //   moba_pool_kernel   kbar = mean of block keys, kept as bf16 hi + lo (kbar ~ hi + lo)
 //   moba_gate_kernel   scores q . kbar on the matrix core (hi and lo), top-k per query,
-//                      ascending index list, per-block query counts
+//                      ascending index list
+//   moba_count_kernel  per-block query counts and each entry's rank in its block's list
 //   moba_scan_kernel   offsets of the per-block query lists and of their 128-row tiles
-//   moba_fill_kernel   places every (query, slot) into its block's list
+//   moba_fill_kernel   places every (query, slot) into its block's list (no atomics)
 //   moba_block_kernel  gathered queries x block keys -> partial (max, sum, output)
 //   moba_own_kernel    own block (causal) + merge of the partials -> out
 #include "attn_tile.h"
@@ -23,27 +23,32 @@
 namespace nsa {
 
 constexpr int MOBA_ROWS = 128;  // gathered queries per block-major tile
-constexpr int MOBA_KMAX = 8;    // largest top_k kept in registers
 
-__global__ void moba_zero_kernel(int32_t* a, int32_t* b, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) { a[i] = 0; b[i] = 0; }
-}
-
+// kbar of one block: 16-byte loads, each thread sums 8 features over a stride of rows; the
+// row groups are then added in a fixed order (fp32), and kbar is split into bf16 hi + lo.
 template <int D>
 __global__ __launch_bounds__(256) void moba_pool_kernel(MobaArgs a) {
-  constexpr int NP = 256 / D;
+  constexpr int DC = D / 8, NP = 256 / DC;
   __shared__ float part[NP][D];
   const int j = blockIdx.x;
   const long bh = blockIdx.y;
-  const int d = threadIdx.x % D, p = threadIdx.x / D;
-  const int per = a.block / NP;
-  const u16* src = a.k + (bh * a.T + (long)j * a.block + p * per) * D + d;
-  float s = 0.f;
-  for (int r = 0; r < per; ++r) s += bf16_to_f32(src[(long)r * D]);
-  part[p][d] = s;
+  const int dc = threadIdx.x % DC, p = threadIdx.x / DC;
+  const u16* src = a.k + (bh * a.T + (long)j * a.block) * D + 8 * dc;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int r = p; r < a.block; r += NP) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(src + (long)r * D);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s[2 * e] += __uint_as_float(w[e] << 16);
+      s[2 * e + 1] += __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[p][8 * dc + e] = s[e];
   __syncthreads();
   if (threadIdx.x < D) {
+    const int d = threadIdx.x;
     float tot = 0.f;
 #pragma unroll
     for (int q = 0; q < NP; ++q) tot += part[q][d];
@@ -56,99 +61,195 @@ __global__ __launch_bounds__(256) void moba_pool_kernel(MobaArgs a) {
   }
 }
 
-// Order-preserving ranking key of a signed score: larger score first, then lower index.
+// Order-preserving ranking key of a signed score: larger score first, then lower index
+// (-0 and +0 compare equal, as in the scores' arithmetic).
 __device__ __forceinline__ uint64_t signed_rank_key(float s, int j) {
-  const uint32_t u = __float_as_uint(s);
+  const uint32_t u = __float_as_uint(s + 0.0f);
   const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return (static_cast<uint64_t>(o) << 32) | (0xFFFFFFFFu - (uint32_t)j);
 }
 
-template <int D>
+// The KS best (score, block) pairs seen by one lane for one query, largest first.  Candidates
+// arrive in increasing block order and displace only on a strictly larger score, so of two
+// equal scores the lower block stays ahead.
+template <int KS>
+struct TopList {
+  float v[KS];
+  int j[KS];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) { v[s] = kNegInf; j[s] = 0; }
+  }
+  __device__ __forceinline__ void insert(float x, int jj) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bool gt = x > v[s];
+      const float tv = v[s];
+      const int tj = j[s];
+      v[s] = gt ? x : tv;
+      j[s] = gt ? jj : tj;
+      x = gt ? tv : x;
+      jj = gt ? tj : jj;
+    }
+  }
+  __device__ __forceinline__ void pop() {
+#pragma unroll
+    for (int s = 0; s + 1 < KS; ++s) { v[s] = v[s + 1]; j[s] = j[s + 1]; }
+    v[KS - 1] = kNegInf;
+  }
+};
+
+// One wave scores 64 queries (four 16-query sub-tiles, one query block) against every past
+// block key on the matrix core: each 16-block tile of kbar (bf16 hi and lo parts) is loaded
+// once and multiplies all four sub-tiles.  Every lane keeps the top KS of its four blocks per
+// tile for its queries; the four lanes of a query then merge.  The ascending index list is
+// written.
+template <int D, int KS>
 __global__ __launch_bounds__(256) void moba_gate_kernel(MobaArgs a) {
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  constexpr int NU = 4;
+  const int h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
-  const int t0 = tile * 64;
-  const int bq = t0 / a.block;  // every query of the tile sits in this block
-  const int t = t0 + 16 * wave + r16;
+  const int t0 = (blockIdx.x * 4 + wave) * 64;
+  if (t0 >= a.T) return;
+  const int bq = t0 / a.block;  // the wave's 64 queries share one block (block % 64 == 0)
   const long bh = (long)b * a.H + h;
   const int K = a.top_k;
   const int nsel = bq < K ? bq : K;
-  int chosen[MOBA_KMAX];
+  int chosen[NU][KS];
 #pragma unroll
-  for (int s = 0; s < MOBA_KMAX; ++s) chosen[s] = s;  // the b <= top_k case: blocks 0..b-1
-  if (bq > K) {
-    bf16x8 qf[D / 32];
-    const u16* qp = a.q + (((long)b * a.T + t) * a.H + h) * D + 8 * g4;
+  for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) qf[c] = load8(qp + 32 * c);
-    uint64_t cand[MOBA_KMAX];
+    for (int s = 0; s < KS; ++s) chosen[u][s] = s;  // bq <= top_k: blocks 0 .. bq-1
+  if (K > 0 && bq > K) {
+    bf16x8 qf[NU][D / 32];
 #pragma unroll
-    for (int s = 0; s < MOBA_KMAX; ++s) cand[s] = 0;
+    for (int u = 0; u < NU; ++u) {
+      const u16* qp = a.q + (((long)b * a.T + t0 + 16 * u + r16) * a.H + h) * D + 8 * g4;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) qf[u][c] = load8(qp + 32 * c);
+    }
+    TopList<KS> lst[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) lst[u].init();
     const u16* hib = a.kb_hi + bh * a.nb * D + 8 * g4;
     const u16* lob = a.kb_lo + bh * a.nb * D + 8 * g4;
     for (int jt = 0; jt * 16 < bq; ++jt) {
       int jr = jt * 16 + r16;
       jr = jr < bq ? jr : bq - 1;
-      f32x4 acc = zero4();
+      bf16x8 kh[D / 32], kl[D / 32];
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) {
-        acc = mfma16x16x32(load8(hib + (long)jr * D + 32 * c), qf[c], acc);
-        acc = mfma16x16x32(load8(lob + (long)jr * D + 32 * c), qf[c], acc);
+        kh[c] = load8(hib + (long)jr * D + 32 * c);
+        kl[c] = load8(lob + (long)jr * D + 32 * c);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = jt * 16 + 4 * g4 + i;
-        uint64_t key = j < bq ? signed_rank_key(acc[i], j) : 0;
+      for (int u = 0; u < NU; ++u) {
+        f32x4 acc = zero4();
 #pragma unroll
-        for (int s = 0; s < MOBA_KMAX; ++s) {
-          const uint64_t c0 = cand[s];
-          const bool gt = key > c0;
-          cand[s] = gt ? key : c0;
-          key = gt ? c0 : key;
+        for (int c = 0; c < D / 32; ++c) {
+          acc = mfma16x16x32(kh[c], qf[u][c], acc);
+          acc = mfma16x16x32(kl[c], qf[u][c], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = jt * 16 + 4 * g4 + i;
+          lst[u].insert(j < bq ? acc[i] : kNegInf, j);
         }
       }
     }
-    // merge the four lanes that hold this query's candidates
+    // merge the four lanes (L, L^16, L^32, L^48) that hold one query's candidates
 #pragma unroll
-    for (int s = 0; s < MOBA_KMAX; ++s) {
-      if (s < K) {
-        uint64_t m = cand[0];
-        m = u64_max(m, shfl_xor_u64(m, 16));
-        m = u64_max(m, shfl_xor_u64(m, 32));
-        if (cand[0] == m) {
+    for (int u = 0; u < NU; ++u) {
 #pragma unroll
-          for (int q = 0; q + 1 < MOBA_KMAX; ++q) cand[q] = cand[q + 1];
-          cand[MOBA_KMAX - 1] = 0;
+      for (int s = 0; s < KS; ++s) {
+        if (s < K) {
+          const uint64_t mine =
+              lst[u].v[0] == kNegInf ? 0 : signed_rank_key(lst[u].v[0], lst[u].j[0]);
+          uint64_t m = u64_max(mine, shfl_xor_u64(mine, 16));
+          m = u64_max(m, shfl_xor_u64(m, 32));
+          if (mine == m) lst[u].pop();
+          chosen[u][s] = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFu));
         }
-        chosen[s] = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFu));
       }
+      // ascending order of the K chosen blocks
+#pragma unroll
+      for (int x = 0; x < KS; ++x)
+#pragma unroll
+        for (int y = 0; y + 1 < KS; ++y)
+          if (y + 1 < K && chosen[u][y] > chosen[u][y + 1]) {
+            const int tmp = chosen[u][y];
+            chosen[u][y] = chosen[u][y + 1];
+            chosen[u][y + 1] = tmp;
+          }
     }
-    // ascending order of the K chosen blocks
-#pragma unroll
-    for (int x = 0; x < MOBA_KMAX; ++x)
-#pragma unroll
-      for (int y = 0; y + 1 < MOBA_KMAX; ++y)
-        if (y + 1 < K && chosen[y] > chosen[y + 1]) {
-          const int tmp = chosen[y];
-          chosen[y] = chosen[y + 1];
-          chosen[y + 1] = tmp;
-        }
   }
   if (g4 == 0) {
-    int32_t* orow = a.idx + (((long)b * a.T + t) * a.H + h) * (K + 1);
 #pragma unroll
-    for (int s = 0; s < MOBA_KMAX; ++s)
-      if (s < nsel) {
-        orow[s] = chosen[s];
-        atomicAdd(&a.count[bh * a.nb + chosen[s]], 1);
-      }
-    orow[nsel] = bq;
-    for (int s = nsel + 1; s <= K; ++s) orow[s] = -1;
+    for (int u = 0; u < NU; ++u) {
+      const long row = ((long)b * a.T + t0 + 16 * u + r16) * a.H + h;
+      int32_t* orow = a.idx + row * (K + 1);
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        if (s < nsel) orow[s] = chosen[u][s];
+      orow[nsel] = bq;
+      for (int s = nsel + 1; s <= K; ++s) orow[s] = -1;
+    }
   }
 }
 
-// Exclusive prefix sums of the list lengths and of their 128-row tile counts (one workgroup).
+// Per (sequence, head, T-chunk): how many of the chunk's queries chose each block, and every
+// (query, slot)'s rank among them, counted with LDS atomics (no global atomics).  Each thread
+// takes kCountRows rows per pass with every index load issued before the atomics.
+constexpr int kCountThreads = 1024, kCountRows = 8;
+
+template <int KS>
+__global__ __launch_bounds__(kCountThreads) void moba_count_kernel(MobaArgs a) {
+  extern __shared__ int cnt[];  // [nb]
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const long bh = (long)b * a.H + h;
+  const int K = a.top_k;
+  const int slast = K > 0 ? K - 1 : 0;
+  const int cl = (a.T + kMobaChunks - 1) / kMobaChunks;
+  const int tbeg = chunk * cl, tend = tbeg + cl < a.T ? tbeg + cl : a.T;
+  for (int j = threadIdx.x; j < a.nb; j += kCountThreads) cnt[j] = 0;
+  __syncthreads();
+  for (int t0 = tbeg + threadIdx.x; t0 < tend; t0 += kCountThreads * kCountRows) {
+    int jb[kCountRows][KS];
+#pragma unroll
+    for (int u = 0; u < kCountRows; ++u) {
+      int t = t0 + u * kCountThreads;
+      t = t < tend ? t : tend - 1;
+      const int32_t* orow = a.idx + (((long)b * a.T + t) * a.H + h) * (K + 1);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) jb[u][s] = orow[s < slast ? s : slast];
+    }
+#pragma unroll
+    for (int u = 0; u < kCountRows; ++u) {
+      const int t = t0 + u * kCountThreads;
+      const int bq = t / a.block;
+      const int nsel = t < tend ? (bq < K ? bq : K) : 0;
+      const long row = ((long)b * a.T + t) * a.H + h;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        if (s < nsel) a.rank[row * K + s] = atomicAdd(&cnt[jb[u][s]], 1);
+    }
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < a.nb; j += kCountThreads)
+    a.count[(bh * a.nb + j) * kMobaChunks + chunk] = cnt[j];
+}
+
+// Exclusive prefix sums of the list lengths and of their 128-row tile counts (one workgroup);
+// each list's chunk counts become the chunk offsets inside the list, and every tile records
+// its list.
+__device__ __forceinline__ int list_len(const MobaArgs& a, int e) {
+  int v = 0;
+#pragma unroll
+  for (int c = 0; c < kMobaChunks; ++c) v += a.count[(long)e * kMobaChunks + c];
+  return v;
+}
+
 __global__ __launch_bounds__(1024) void moba_scan_kernel(MobaArgs a) {
   __shared__ int sc[1024], st[1024];
   const int n = a.B * a.H * a.nb;
@@ -156,7 +257,7 @@ __global__ __launch_bounds__(1024) void moba_scan_kernel(MobaArgs a) {
   const int lo = threadIdx.x * per, hi = lo + per < n ? lo + per : n;
   int c = 0, tl = 0;
   for (int e = lo; e < hi; ++e) {
-    const int v = a.count[e];
+    const int v = list_len(a, e);
     c += v;
     tl += (v + MOBA_ROWS - 1) / MOBA_ROWS;
   }
@@ -173,15 +274,29 @@ __global__ __launch_bounds__(1024) void moba_scan_kernel(MobaArgs a) {
   }
   int co = sc[threadIdx.x] - c, to = st[threadIdx.x] - tl;  // exclusive
   for (int e = lo; e < hi; ++e) {
-    const int v = a.count[e];
+    int run = 0;
+#pragma unroll
+    for (int ch = 0; ch < kMobaChunks; ++ch) {
+      int32_t* cc = a.count + (long)e * kMobaChunks + ch;
+      const int v = *cc;
+      *cc = run;
+      run += v;
+    }
     a.offset[e] = co;
     a.tstart[e] = to;
-    co += v;
-    to += (v + MOBA_ROWS - 1) / MOBA_ROWS;
+    const int nt = (run + MOBA_ROWS - 1) / MOBA_ROWS;
+    for (int k = 0; k < nt; ++k) a.tile_entry[to + k] = e;
+    co += run;
+    to += nt;
   }
-  if (threadIdx.x == 1023) a.ntiles[0] = st[1023];
+  if (threadIdx.x == 1023) {
+    a.ntiles[0] = st[1023];
+    a.offset[n] = sc[1023];  // end of the last list
+  }
 }
 
+// Places every (query, slot) at its block's list offset + its chunk's offset in the list + its
+// rank among the chunk's queries.
 __global__ __launch_bounds__(256) void moba_fill_kernel(MobaArgs a) {
   const long row = (long)blockIdx.x * 256 + threadIdx.x;  // (b, t, h)
   if (row >= (long)a.B * a.T * a.H) return;
@@ -190,13 +305,13 @@ __global__ __launch_bounds__(256) void moba_fill_kernel(MobaArgs a) {
   const int t = (int)(bt % a.T), b = (int)(bt / a.T);
   const int bq = t / a.block;
   const int nsel = bq < a.top_k ? bq : a.top_k;
+  const int chunk = t / ((a.T + kMobaChunks - 1) / kMobaChunks);
   const long bh = (long)b * a.H + h;
   const int32_t* irow = a.idx + row * (a.top_k + 1);
   for (int s = 0; s < nsel; ++s) {
-    const int j = irow[s];
-    const long e = bh * a.nb + j;
-    const int pos = a.offset[e] + atomicAdd(&a.cursor[e], 1);
-    a.list[pos] = (t << 4) | s;
+    const long e = bh * a.nb + irow[s];
+    a.list[a.offset[e] + a.count[e * kMobaChunks + chunk] + a.rank[row * a.top_k + s]] =
+        (t << 4) | s;
   }
 }
 
@@ -205,26 +320,15 @@ __global__ __launch_bounds__(256) void moba_block_kernel(MobaArgs a) {
   constexpr int RTW = 2, DT = D / 16;
   __shared__ u16 Ks[64][D];
   __shared__ u16 Vs[D][64];
-  __shared__ int ent;
   const int tile = blockIdx.x;
   if (tile >= a.ntiles[0]) return;
-  const int n = a.B * a.H * a.nb;
-  if (threadIdx.x == 0) {  // last list whose first tile is <= this tile
-    int lo = 0, hi = n - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.tstart[mid] <= tile) lo = mid; else hi = mid - 1;
-    }
-    ent = lo;
-  }
-  __syncthreads();
-  const int e = ent;
+  const int e = a.tile_entry[tile];
   const long bh = e / a.nb;
   const int j = e % a.nb;
   const int b = (int)(bh / a.H), h = (int)(bh % a.H);
   const int kt_in = tile - a.tstart[e];
   const int base = a.offset[e] + kt_in * MOBA_ROWS;
-  const int rem = a.count[e] - kt_in * MOBA_ROWS;
+  const int rem = a.offset[e + 1] - base;
   const int cnt = rem < MOBA_ROWS ? rem : MOBA_ROWS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
@@ -253,11 +357,21 @@ __global__ __launch_bounds__(256) void moba_block_kernel(MobaArgs a) {
     for (int nn = 0; nn < DT; ++nn) O[rt][nn] = zero4();
   }
   const long key0 = (long)j * a.block;
-  for (int kt = 0; kt < a.block / 64; ++kt) {
+  const int nkt = a.block / 64;
+  KTileRegs<D, 256> kr;
+  VTileRegs<D, 256> vr;
+  kr.load(kb, key0, a.T - 1);
+  vr.load(vtb, a.T, key0);
+  for (int kt = 0; kt < nkt; ++kt) {
     __syncthreads();
-    load_rows_tile<D, 256>(Ks, kb, key0 + kt * 64, a.T - 1);
-    load_cols_tile<D, 256>(Vs, vtb, a.T, key0 + kt * 64);
+    kr.store(Ks);
+    vr.store(Vs);
     __syncthreads();
+    {  // next tile in flight while this one computes (the last re-fetches itself: no branch)
+      const long nxt = key0 + 64L * (kt + 1 < nkt ? kt + 1 : kt);
+      kr.load(kb, nxt, a.T - 1);
+      vr.load(vtb, a.T, nxt);
+    }
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
       float z[16];
@@ -309,9 +423,11 @@ __global__ __launch_bounds__(256) void moba_block_kernel(MobaArgs a) {
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(128) void moba_own_kernel(MobaArgs a) {
-  constexpr int RTW = 2, DT = D / 16;
+// Own block (causal) of 64 queries, then the merge with the KS partials of their chosen blocks
+// (slots past the row's count are masked by selects, never multiplied in).
+template <int D, int KS>
+__global__ __launch_bounds__(256) void moba_own_kernel(MobaArgs a) {
+  constexpr int RTW = 1, DT = D / 16;
   __shared__ u16 Ks[64][D];
   __shared__ u16 Vs[D][64];
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -341,11 +457,21 @@ __global__ __launch_bounds__(128) void moba_own_kernel(MobaArgs a) {
     for (int nn = 0; nn < DT; ++nn) O[rt][nn] = zero4();
   }
   const int kt0 = (bq * a.block) / 64, kt1 = (t0 + 63) / 64;
+  KTileRegs<D, 256> kr;
+  VTileRegs<D, 256> vr;
+  kr.load(kb, (long)kt0 * 64, a.T - 1);
+  vr.load(vtb, a.T, (long)kt0 * 64);
   for (int kt = kt0; kt <= kt1; ++kt) {
     __syncthreads();
-    load_rows_tile<D, 128>(Ks, kb, (long)kt * 64, a.T - 1);
-    load_cols_tile<D, 128>(Vs, vtb, a.T, (long)kt * 64);
+    kr.store(Ks);
+    vr.store(Vs);
     __syncthreads();
+    {
+      const long nxt = 64L * (kt < kt1 ? kt + 1 : kt);
+      kr.load(kb, nxt, a.T - 1);
+      vr.load(vtb, a.T, nxt);
+    }
+    const bool diag = kt == kt1;  // uniform: only the last tile needs the causal mask
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
       float z[16];
@@ -355,22 +481,26 @@ __global__ __launch_bounds__(128) void moba_own_kernel(MobaArgs a) {
         for (int s = 0; s < 2; ++s) {
           const f32x4 acc = score_subtile<D>(Ks, qf[rt], kc, s, g4, r16);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kt * 64 + 32 * kc + 8 * g4 + 4 * s + i;
-            z[kc * 8 + s * 4 + i] = key <= row_t[rt] ? acc[i] * a.scale_log2 : kNegInf;
-          }
+          for (int i = 0; i < 4; ++i) z[kc * 8 + s * 4 + i] = acc[i] * a.scale_log2;
         }
+      if (diag) {
+        __asm__ volatile("" ::: "memory");
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kt * 64 + 32 * (e >> 3) + 8 * g4 + 4 * ((e >> 2) & 1) + (e & 3);
+          z[e] = key <= row_t[rt] ? z[e] : kNegInf;
+        }
+      }
       float tm = z[0];
 #pragma unroll
       for (int q = 1; q < 16; ++q) tm = fmaxf(tm, z[q]);
       tm = col_max4(tm);
-      const float mn = fmaxf(mrun[rt], tm);
-      const float ms = mn == kNegInf ? 0.f : mn;
-      const float alpha = fast_exp2(mrun[rt] - ms);
+      const float mn = fmaxf(mrun[rt], tm);  // finite: every row sees its block's first key
+      const float alpha = fast_exp2(mrun[rt] - mn);
       mrun[rt] = mn;
       float p[16], sum = 0.f;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) { p[q] = fast_exp2(z[q] - ms); sum += p[q]; }
+      for (int q = 0; q < 16; ++q) { p[q] = fast_exp2(z[q] - mn); sum += p[q]; }
       lrun[rt] = lrun[rt] * alpha + sum;
 #pragma unroll
       for (int nn = 0; nn < DT; ++nn) O[rt][nn] *= alpha;
@@ -383,13 +513,27 @@ __global__ __launch_bounds__(128) void moba_own_kernel(MobaArgs a) {
       }
     }
   }
-  const int nsel = bq < a.top_k ? bq : a.top_k;
+  const int K = a.top_k;
+  const int nsel = bq < K ? bq : K;
+  const int slast = K > 0 ? K - 1 : 0;
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
-    const int t = row_t[rt];
-    const long row = ((long)b * a.T + t) * a.H + h;
+    const long row = ((long)b * a.T + row_t[rt]) * a.H + h;
+    float pm[KS], pl[KS];
+    float4 pv[KS][DT];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {  // every load unconditional (slot index clamped)
+      const long slot = row * K + (s < slast ? s : slast);
+      pm[s] = a.pml[slot * 2];
+      pl[s] = a.pml[slot * 2 + 1];
+      const float* op = a.po + slot * D;
+#pragma unroll
+      for (int nn = 0; nn < DT; ++nn)
+        pv[s][nn] = *reinterpret_cast<const float4*>(op + 16 * nn + 4 * g4);
+    }
     float M = mrun[rt];
-    for (int s = 0; s < nsel; ++s) M = fmaxf(M, a.pml[(row * a.top_k + s) * 2]);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) M = s < nsel ? fmaxf(M, pm[s]) : M;
     const float fo = fast_exp2(mrun[rt] - M);
     float L = col_sum4(lrun[rt]) * fo;
     float4 acc[DT];
@@ -397,18 +541,17 @@ __global__ __launch_bounds__(128) void moba_own_kernel(MobaArgs a) {
     for (int nn = 0; nn < DT; ++nn)
       acc[nn] = make_float4(O[rt][nn][0] * fo, O[rt][nn][1] * fo, O[rt][nn][2] * fo,
                             O[rt][nn][3] * fo);
-    for (int s = 0; s < nsel; ++s) {
-      const long slot = row * a.top_k + s;
-      const float f = fast_exp2(a.pml[slot * 2] - M);
-      L += a.pml[slot * 2 + 1] * f;
-      const float* op = a.po + slot * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bool ok = s < nsel;
+      const float f = ok ? fast_exp2(pm[s] - M) : 0.f;
+      L += ok ? pl[s] * f : 0.f;
 #pragma unroll
       for (int nn = 0; nn < DT; ++nn) {
-        const float4 v = *reinterpret_cast<const float4*>(op + 16 * nn + 4 * g4);
-        acc[nn].x += f * v.x;
-        acc[nn].y += f * v.y;
-        acc[nn].z += f * v.z;
-        acc[nn].w += f * v.w;
+        acc[nn].x += ok ? f * pv[s][nn].x : 0.f;
+        acc[nn].y += ok ? f * pv[s][nn].y : 0.f;
+        acc[nn].z += ok ? f * pv[s][nn].z : 0.f;
+        acc[nn].w += ok ? f * pv[s][nn].w : 0.f;
       }
     }
     const float inv = 1.0f / L;
@@ -420,33 +563,39 @@ __global__ __launch_bounds__(128) void moba_own_kernel(MobaArgs a) {
   }
 }
 
-void launch_moba(const MobaArgs& a, hipStream_t s, hipEvent_t* ev) {
+template <int D, int KS>
+static void launch_moba_k(const MobaArgs& a, hipStream_t s, hipEvent_t* ev) {
   auto mark = [&](int i) {
     if (ev != nullptr) (void)hipEventRecord(ev[i], s);
   };
-  const int n = a.B * a.H * a.nb;
-  moba_zero_kernel<<<(n + 255) / 256, 256, 0, s>>>(a.count, a.cursor, n);
   const long rows = (long)a.B * a.T * a.H;
-  const dim3 gp(a.nb, a.B * a.H), gq(a.T / 64, a.H, a.B);
-  if (a.D == 128) {
-    moba_pool_kernel<128><<<gp, 256, 0, s>>>(a);
-    moba_gate_kernel<128><<<gq, 256, 0, s>>>(a);
-  } else {
-    moba_pool_kernel<64><<<gp, 256, 0, s>>>(a);
-    moba_gate_kernel<64><<<gq, 256, 0, s>>>(a);
-  }
+  const dim3 gp(a.nb, a.B * a.H), gq(a.T / 64, a.H, a.B), gg((a.T / 64 + 3) / 4, a.H, a.B);
+  moba_pool_kernel<D><<<gp, 256, 0, s>>>(a);
+  moba_gate_kernel<D, KS><<<gg, 256, 0, s>>>(a);
   mark(1);
+  moba_count_kernel<KS><<<dim3(kMobaChunks, a.H, a.B), kCountThreads,
+                          (size_t)a.nb * sizeof(int), s>>>(a);
   moba_scan_kernel<<<1, 1024, 0, s>>>(a);
   moba_fill_kernel<<<(int)((rows + 255) / 256), 256, 0, s>>>(a);
   mark(2);
-  if (a.max_tiles > 0) {
-    if (a.D == 128) moba_block_kernel<128><<<a.max_tiles, 256, 0, s>>>(a);
-    else moba_block_kernel<64><<<a.max_tiles, 256, 0, s>>>(a);
-  }
+  if (a.max_tiles > 0) moba_block_kernel<D><<<a.max_tiles, 256, 0, s>>>(a);
   mark(3);
-  if (a.D == 128) moba_own_kernel<128><<<gq, 128, 0, s>>>(a);
-  else moba_own_kernel<64><<<gq, 128, 0, s>>>(a);
+  moba_own_kernel<D, KS><<<gq, 256, 0, s>>>(a);
   mark(4);
+}
+
+template <int D>
+static void launch_moba_d(const MobaArgs& a, hipStream_t s, hipEvent_t* ev) {
+  if (a.top_k <= 1) launch_moba_k<D, 1>(a, s, ev);
+  else if (a.top_k == 2) launch_moba_k<D, 2>(a, s, ev);
+  else if (a.top_k == 3) launch_moba_k<D, 3>(a, s, ev);
+  else if (a.top_k == 4) launch_moba_k<D, 4>(a, s, ev);
+  else launch_moba_k<D, 8>(a, s, ev);
+}
+
+void launch_moba(const MobaArgs& a, hipStream_t s, hipEvent_t* ev) {
+  if (a.D == 128) launch_moba_d<128>(a, s, ev);
+  else launch_moba_d<64>(a, s, ev);
 }
 
 }  // namespace nsa

@@ -202,6 +202,8 @@ int nsa_decode_timed(const nsa_config* cfg, const void* q, const void* kcache,
  *   q bf16 [B, T, H, D]; k, v bf16 [B, H, T, D]; out fp32 [B, T, H, D]
  *   sel_idx int32 [B, T, H, top_k + 1] or NULL: chosen blocks incl. the own block,
  *           ascending, -1 padded
+ * NSA_ERR_UNSUPPORTED (moba_validate) unless D is 64 or 128, block is a multiple of 64 that
+ * divides T, top_k <= 8, T <= 2^27 and T / block <= 16384.
  */
 int moba_prefill(const moba_config* cfg, const void* q, const void* k, const void* v,
                  float* out, int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream);

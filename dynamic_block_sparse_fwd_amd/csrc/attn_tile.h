@@ -117,6 +117,47 @@ __device__ __forceinline__ void pv_chunk(const u16 (*Vs)[64], const bf16x8& pb, 
   for (int n = 0; n < D / 16; ++n) O[n] = mfma16x16x32(load8(&Vs[16 * n + r16][ch]), pb, O[n]);
 }
 
+// S^T for RTW row tiles against the 64-key LDS tile: each K fragment is read from LDS once
+// and multiplies every row tile (LDS bandwidth, not the matrix core, is the scarcer resource
+// when each fragment feeds one MFMA).  raw[rt][kc*8 + s*4 + i] = score of key
+// 32*kc + 8*g4 + 4*s + i for row tile rt.
+template <int D, int RTW>
+__device__ __forceinline__ void score_tiles(const u16 (*Ks)[D], const bf16x8 (*qf)[D / 32],
+                                            int g4, int r16, float (*raw)[16]) {
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 kf[D / 32];
+      k_frags<D>(Ks, kc, s, g4, r16, kf);
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) acc = mfma16x16x32(kf[c], qf[rt][c], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[rt][kc * 8 + s * 4 + i] = acc[i];
+      }
+    }
+}
+
+// O^T += V^T P^T for RTW row tiles: each V fragment is read from LDS once.  pb[rt][kc] holds
+// row tile rt's probabilities of keys 32*kc + 8*g4 .. +7.
+template <int D, int RTW>
+__device__ __forceinline__ void pv_tiles(const u16 (*Vs)[64], const bf16x8 (*pb)[2], int g4,
+                                         int r16, f32x4 (*O)[D / 16]) {
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    const int ch = ((4 * kc + g4) ^ (r16 & 7)) * 8;
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) {
+      const bf16x8 vf = load8(&Vs[16 * n + r16][ch]);
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt) O[rt][n] = mfma16x16x32(vf, pb[rt][kc], O[rt][n]);
+    }
+  }
+}
+
 // Sum over the 16 lanes of a DPP row (row rotations 8, 4, 2, 1); every lane ends with a sum,
 // lane 0 of the row with a fixed association.
 __device__ __forceinline__ float row16_sum(float v) {

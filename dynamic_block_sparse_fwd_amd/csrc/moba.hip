@@ -372,38 +372,31 @@ __global__ __launch_bounds__(256) void moba_block_kernel(MobaArgs a) {
       kr.load(kb, nxt, a.T - 1);
       vr.load(vtb, a.T, nxt);
     }
+    float z[RTW][16];
+    score_tiles<D, RTW>(Ks, qf, g4, r16, z);
+    bf16x8 pb[RTW][2];
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
-      float z[16];
+      float tm = z[rt][0];
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const f32x4 acc = score_subtile<D>(Ks, qf[rt], kc, s, g4, r16);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) z[kc * 8 + s * 4 + i] = acc[i] * a.scale_log2;
-        }
-      float tm = z[0];
-#pragma unroll
-      for (int q = 1; q < 16; ++q) tm = fmaxf(tm, z[q]);
+      for (int q = 1; q < 16; ++q) tm = fmaxf(tm, z[rt][q]);
       tm = col_max4(tm);
       const float mn = fmaxf(mrun[rt], tm);
-      const float alpha = fast_exp2(mrun[rt] - mn);
+      const float msl = mn * a.scale_log2;
+      const float alpha = fast_exp2(fmaf(mrun[rt], a.scale_log2, -msl));
       mrun[rt] = mn;
-      float p[16], sum = 0.f;
+      float sum = 0.f;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) { p[q] = fast_exp2(z[q] - mn); sum += p[q]; }
+      for (int q = 0; q < 16; ++q) {
+        const float p = fast_exp2(fmaf(z[rt][q], a.scale_log2, -msl));
+        sum += p;
+        pb[rt][q >> 3][q & 7] = (__bf16)p;
+      }
       lrun[rt] = lrun[rt] * alpha + sum;
 #pragma unroll
       for (int nn = 0; nn < DT; ++nn) O[rt][nn] *= alpha;
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        bf16x8 pb;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) pb[q] = (__bf16)p[kc * 8 + q];
-        pv_chunk<D>(Vs, pb, kc, g4, r16, O[rt]);
-      }
     }
+    pv_tiles<D, RTW>(Vs, pb, g4, r16, O);
   }
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
@@ -416,7 +409,7 @@ __global__ __launch_bounds__(256) void moba_block_kernel(MobaArgs a) {
         *reinterpret_cast<float4*>(op + 16 * nn + 4 * g4) =
             make_float4(O[rt][nn][0], O[rt][nn][1], O[rt][nn][2], O[rt][nn][3]);
       if (g4 == 0) {
-        a.pml[slot * 2 + 0] = mrun[rt];
+        a.pml[slot * 2 + 0] = mrun[rt] * a.scale_log2;
         a.pml[slot * 2 + 1] = L;
       }
     }

@@ -109,34 +109,27 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void cmp_select_kernel(PrefillAr
     __syncthreads();
     if (kt + 1 < nkt) kr.load(kc, (long)(kt + 1) * 64, a.NCP - 1);
     const bool full = (kt + 1) * 64 <= nvis_lo;
+    float raw[RTW][16];
+    score_tiles<D, RTW>(Ks, qf, g4, r16, raw);
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
-      float raw[16];
-#pragma unroll
-      for (int kc2 = 0; kc2 < 2; ++kc2)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const f32x4 acc = score_subtile<D>(Ks, qf[rt], kc2, s, g4, r16);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) raw[kc2 * 8 + s * 4 + i] = acc[i];
-        }
       if (!full) {  // a real (uniform) branch: full tiles skip the masking arithmetic
         __asm__ volatile("" ::: "memory");
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kt * 64 + 32 * (e >> 3) + 8 * g4 + (e & 7);
-          raw[e] = key < nvis[rt] ? raw[e] : kNegInf;
+          raw[rt][e] = key < nvis[rt] ? raw[rt][e] : kNegInf;
         }
       }
-      float tm = raw[0];
+      float tm = raw[rt][0];
 #pragma unroll
-      for (int e = 1; e < 16; ++e) tm = fmaxf(tm, raw[e]);
+      for (int e = 1; e < 16; ++e) tm = fmaxf(tm, raw[rt][e]);
       const float mn = fmaxf(mrun[rt], tm);
       if (mn != kNegInf) {
         const float msl = mn * sl;
         float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sum += fast_exp2(fmaf(raw[e], sl, -msl));
+        for (int e = 0; e < 16; ++e) sum += fast_exp2(fmaf(raw[rt][e], sl, -msl));
         lrun[rt] = lrun[rt] * fast_exp2(fmaf(mrun[rt], sl, -msl)) + sum;
         mrun[rt] = mn;
       }
@@ -175,6 +168,9 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void cmp_select_kernel(PrefillAr
       vr.load(vct, a.NCP, (long)(kt + 1) * 64);
     }
     const bool full = (kt + 1) * 64 <= nvis_lo;
+    float raw[RTW][16];
+    score_tiles<D, RTW>(Ks, qf, g4, r16, raw);
+    bf16x8 pbt[RTW][2];
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
       const int r = (wave * RTW + rt) * 16 + r16;
@@ -182,11 +178,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void cmp_select_kernel(PrefillAr
       for (int kc2 = 0; kc2 < 2; ++kc2) {
         float pv[8];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const f32x4 acc = score_subtile<D>(Ks, qf[rt], kc2, s, g4, r16);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pv[4 * s + i] = fast_exp2(fmaf(acc[i], sl, -rmax[rt]));
-        }
+        for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(raw[rt][kc2 * 8 + e], sl, -rmax[rt]));
         if (!full) {
           __asm__ volatile("" ::: "memory");
 #pragma unroll
@@ -195,10 +187,8 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void cmp_select_kernel(PrefillAr
             pv[e] = key < nvis[rt] ? pv[e] : 0.f;
           }
         }
-        bf16x8 pb;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pv[e];
-        pv_chunk<D>(Vs, pb, kc2, g4, r16, O[rt]);
+        for (int e = 0; e < 8; ++e) pbt[rt][kc2][e] = (__bf16)pv[e];
         if constexpr (FAST) {
           const float cA = head_sum<G>(((pv[0] + pv[1]) + pv[2] + 0.5f * pv[3]) * rinv[rt]);
           const float cB = head_sum<G>(((pv[4] + pv[5]) + pv[6] + 0.5f * pv[7]) * rinv[rt]);
@@ -220,6 +210,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void cmp_select_kernel(PrefillAr
         }
       }
     }
+    pv_tiles<D, RTW>(Vs, pbt, g4, r16, O);
     __syncthreads();
     if constexpr (FAST) {
       // blocks 16*kt .. 16*kt + 15 are complete: core + carry (the carry of the first block
@@ -377,30 +368,24 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void window_kernel(PrefillArgs a
     }
     // keys of this tile are inside every row's window unless the tile touches either end
     const bool full = alive && kt * 64 >= tlast - a.window + 1 && kt * 64 + 63 <= t0;
+    float raw[RTW][16];
+    score_tiles<D, RTW>(Ks, qf, g4, r16, raw);
+    bf16x8 pb[RTW][2];
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
       const int t = row_t[rt];
       const int lo = t - a.window + 1;
-      float raw[16];
-#pragma unroll
-      for (int kc2 = 0; kc2 < 2; ++kc2)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const f32x4 acc = score_subtile<D>(Ks, qf[rt], kc2, s, g4, r16);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) raw[kc2 * 8 + s * 4 + i] = acc[i];
-        }
       if (!full) {
         __asm__ volatile("" ::: "memory");
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kt * 64 + 32 * (e >> 3) + 8 * g4 + (e & 7);
-          raw[e] = (key <= t && key >= lo && t < a.T) ? raw[e] : kNegInf;
+          raw[rt][e] = (key <= t && key >= lo && t < a.T) ? raw[rt][e] : kNegInf;
         }
       }
-      float tm = raw[0];
+      float tm = raw[rt][0];
 #pragma unroll
-      for (int e = 1; e < 16; ++e) tm = fmaxf(tm, raw[e]);
+      for (int e = 1; e < 16; ++e) tm = fmaxf(tm, raw[rt][e]);
       tm = col_max4(tm);
       const float mn = fmaxf(mrun[rt], tm);
       // A row with no visible key yet keeps m = -inf; exponentials then use 0 as reference
@@ -408,20 +393,18 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void window_kernel(PrefillArgs a
       const float msl = (mn == kNegInf) ? 0.f : mn * sl;
       const float alpha = fast_exp2(fmaf(mrun[rt], sl, -msl));
       mrun[rt] = mn;
-      float p[16], sum = 0.f;
+      float sum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) { p[e] = fast_exp2(fmaf(raw[e], sl, -msl)); sum += p[e]; }
+      for (int e = 0; e < 16; ++e) {
+        const float p = fast_exp2(fmaf(raw[rt][e], sl, -msl));
+        sum += p;
+        pb[rt][e >> 3][e & 7] = (__bf16)p;
+      }
       lrun[rt] = lrun[rt] * alpha + sum;
 #pragma unroll
       for (int n = 0; n < DT; ++n) O[rt][n] *= alpha;
-#pragma unroll
-      for (int kc2 = 0; kc2 < 2; ++kc2) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[kc2 * 8 + e];
-        pv_chunk<D>(Vs, pb, kc2, g4, r16, O[rt]);
-      }
     }
+    pv_tiles<D, RTW>(Vs, pb, g4, r16, O);
   }
 
   const int Hq = a.Hkv * G;
@@ -449,36 +432,60 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void window_kernel(PrefillArgs a
 
 // ------------------------------------------------------------------ selected blocks
 
-// One wave per (position, KV group): the group's heads form the 16 MFMA rows; K and V
-// fragments are read straight from global memory (16-byte loads, no LDS).  The wave's tiles
-// (64 keys each, in index-list order) are listed once, lane e holding the first key of tile e
-// or -1 (padding, a block outside [0, nblk), a tile past t); the valid lanes are visited in
-// order through the ballot mask.  Each tile's K and V are fetched while the previous tile
-// computes.
+// One wave per (position, KV group), eight consecutive positions of one group per workgroup:
+// the group's heads form the 16 MFMA rows.  The forced blocks (block 0 and the local blocks,
+// one 64-key tile each at the benchmark geometry) are common to the eight positions, so up to
+// three of their tiles are staged in LDS once per workgroup; every other selected tile is
+// gathered straight from global memory (16-byte loads), the next tile's K and V in flight
+// while the current one computes.  A wave's tiles (in index-list order) are listed once, lane
+// e holding the first key of tile e or -1 (padding, a block outside [0, nblk), a tile past t);
+// tiles it shares with the workgroup are taken from LDS (as often as they occur), the rest
+// are visited in order through the ballot mask.
 // Workgroups are dealt to the 8 XCDs round-robin; the linear index is remapped so that XCD x
 // runs a contiguous 1/8 of the (sequence, group, position) range: the waves that share an
 // XCD's L2 then read the same group's K/V at nearby positions.
+constexpr int kSelWaves = 8;   // positions per workgroup
+constexpr int kSelShared = 3;  // tiles staged in LDS per workgroup
+
 template <int D, int G>
-__global__ __launch_bounds__(256, 2) void selected_kernel(PrefillArgs a) {
-  constexpr int DT = D / 16, NK = D / 8, NV = D / 8;
+__global__ __launch_bounds__(kSelWaves * 64, 1) void selected_kernel(PrefillArgs a) {
+  constexpr int DT = D / 16, NK = D / 8, NV = D / 8, NT = kSelWaves * 64;
+  __shared__ __align__(16) u16 Ksh[kSelShared][64][D];
+  __shared__ __align__(16) u16 Vsh[kSelShared][D][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
-  const int ntb = (a.T + 3) / 4;
+  const int ntb = (a.T + kSelWaves - 1) / kSelWaves;
   const int per_xcd = gridDim.x / 8;  // the grid is padded to a multiple of 8
   const int w = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   const int stream = w / ntb;
-  if (stream >= a.B * a.Hkv) return;
-  const int t = (w % ntb) * 4 + wave;
+  if (stream >= a.B * a.Hkv) return;  // uniform
+  const int t0 = (w % ntb) * kSelWaves;
+  const int t = t0 + wave;
+  const bool act = t < a.T;
   const int kvh = stream % a.Hkv, b = stream / a.Hkv;
-  if (t >= a.T) return;
   const long bkv = (long)b * a.Hkv + kvh;
   const int Hq = a.Hkv * G;
   const bool hlive = r16 < G;
   const int head = kvh * G + (hlive ? r16 : 0);
   const float sl = a.scale_log2;
+  const u16* kb = a.k + bkv * (long)a.T * D;
+  const u16* vtb = a.vt + bkv * (long)D * a.TP;
+
+  // The workgroup's shared tiles: tiles of the current block up to t0, of the other local
+  // blocks, then block 0's first tile (uniform; t0 .. t0+7 share one block since the block
+  // size is a multiple of 64 and t0 of 8).
+  int sh[kSelShared];
+  int nsh = 0;
+  {
+    const int bcur = t0 / a.beta, per = a.beta >> 6;
+    for (int f = bcur; f >= 0 && f > bcur - a.n_local && nsh < kSelShared; --f)
+      for (int u = 0; u < per && nsh < kSelShared; ++u)
+        if (f * a.beta + 64 * u <= t0) sh[nsh++] = f * a.beta + 64 * u;
+    if (nsh < kSelShared && bcur - a.n_local >= 0) sh[nsh++] = 0;
+  }
 
   int my_key0 = -1;
-  {
+  if (act) {
     const int per = a.beta >> 6;
     const int32_t* irow = a.idx + (((long)b * a.T + t) * a.Hkv + kvh) * a.top_n;
     if (lane < a.top_n * per) {
@@ -487,23 +494,28 @@ __global__ __launch_bounds__(256, 2) void selected_kernel(PrefillArgs a) {
       if (j >= 0 && j < a.nblk && k0 <= t) my_key0 = k0;
     }
   }
-  uint64_t todo = __ballot(my_key0 >= 0);  // wave-uniform: valid lanes still to visit
+  uint64_t todo = __ballot(my_key0 >= 0);  // wave-uniform: gathered tiles still to visit
+  int shcnt[kSelShared];
+#pragma unroll
+  for (int i = 0; i < kSelShared; ++i) {
+    const uint64_t m = i < nsh ? __ballot(my_key0 == sh[i]) : 0ull;
+    shcnt[i] = (int)__popcll(m);
+    todo &= ~m;
+  }
   const int ntile = (int)__popcll(todo);
 
   bf16x8 qf[D / 32];
   {
-    const u16* qp = a.q + (((long)b * a.T + t) * Hq + head) * D;
+    const u16* qp = a.q + (((long)b * a.T + (act ? t : 0)) * Hq + head) * D;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) qf[c] = hlive ? load8(qp + 32 * c + 8 * g4) : zero8();
   }
-  const u16* kb = a.k + bkv * (long)a.T * D;
-  const u16* vtb = a.vt + bkv * (long)D * a.TP;
   const int tmax = a.T - 1;
   u32x4 kr[NK], vr[NV];
-  auto load_k = [&](int key0) {
+  auto load_k = [&](int k0) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      int row = key0 + 32 * (q >> 1) + perm_key(r16, q & 1);
+      int row = k0 + 32 * (q >> 1) + perm_key(r16, q & 1);
       row = row < tmax ? row : tmax;
 #pragma unroll
       for (int c = 0; c < D / 32; ++c)
@@ -511,27 +523,89 @@ __global__ __launch_bounds__(256, 2) void selected_kernel(PrefillArgs a) {
             *reinterpret_cast<const u32x4*>(kb + ((uint32_t)row * D + 8 * g4 + 32 * c));
     }
   };
-  auto load_v = [&](int key0) {
+  auto load_v = [&](int k0) {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int n = 0; n < DT; ++n)
         vr[kc * DT + n] = *reinterpret_cast<const u32x4*>(
-            vtb + ((uint32_t)(16 * n + r16) * a.TP + key0 + 32 * kc + 8 * g4));
+            vtb + ((uint32_t)(16 * n + r16) * a.TP + k0 + 32 * kc + 8 * g4));
   };
+  for (int i = 0; i < nsh; ++i) {  // uniform
+    KTileRegs<D, NT> sk;
+    VTileRegs<D, NT> sv;
+    sk.load(kb, sh[i], tmax);
+    sv.load(vtb, a.TP, sh[i]);
+    sk.store(Ksh[i]);
+    sv.store(Vsh[i]);
+  }
+  __syncthreads();
+  if (!act) return;  // after the workgroup's only barrier
+  // the first gathered tile's K is in flight while the shared tiles compute (its V follows:
+  // both at once would not fit the register budget)
+  int key0 = 0;
+  if (ntile > 0) {
+    key0 = __builtin_amdgcn_readlane(my_key0, __builtin_ctzll(todo));
+    todo &= todo - 1;
+  }
+  load_k(key0);
 
   float mrun = kNegInf, lrun = 0.f;
   f32x4 O[DT];
 #pragma unroll
   for (int n = 0; n < DT; ++n) O[n] = zero4();
-  int key0 = 0;
-  if (ntile > 0) {
-    key0 = __builtin_amdgcn_readlane(my_key0, __builtin_ctzll(todo));
-    todo &= todo - 1;
-    load_k(key0);
-    load_v(key0);
-  }
-  for (int i = 0; i < ntile; ++i) {
+  // masking, online softmax and the rescale of O; returns P^T fragments for the P V product
+  auto softmax_step = [&](float* z, int k0, bf16x8* pb) {
+    if (k0 + 63 > t) {  // the diagonal tile (uniform branch)
+      __asm__ volatile("" ::: "memory");
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = k0 + 32 * (q >> 1) + 8 * g4 + 4 * (q & 1) + e;
+          z[q * 4 + e] = key <= t ? z[q * 4 + e] : kNegInf;
+        }
+    }
+    float tm = z[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) tm = fmaxf(tm, z[e]);
+    tm = col_max4(tm);
+    const float mn = fmaxf(mrun, tm);  // finite: every tile used holds a key <= t
+    const float msl = mn * sl;
+    const float alpha = fast_exp2(fmaf(mrun, sl, -msl));
+    mrun = mn;
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = fast_exp2(fmaf(z[e], sl, -msl));
+      sum += p;
+      pb[e >> 3][e & 7] = (__bf16)p;
+    }
+    lrun = fmaf(lrun, alpha, sum);
+#pragma unroll
+    for (int n = 0; n < DT; ++n) O[n] *= alpha;
+  };
+
+  // shared tiles, from LDS
+  for (int i = 0; i < nsh; ++i)
+    for (int c = 0; c < shcnt[i]; ++c) {
+      float z[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 acc = score_subtile<D>(Ksh[i], qf, q >> 1, q & 1, g4, r16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[q * 4 + e] = acc[e];
+      }
+      bf16x8 pb[2];
+      softmax_step(z, sh[i], pb);
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) pv_chunk<D>(Vsh[i], pb[kc], kc, g4, r16, O);
+    }
+
+  load_v(key0);
+
+  // gathered tiles
+  for (int it = 0; it < ntile; ++it) {
     // the last tile re-fetches itself: unconditional loads keep the wait counts exact (a load
     // under a branch makes the join wait for every load in flight)
     const int knext = todo ? __builtin_amdgcn_readlane(my_key0, __builtin_ctzll(todo)) : key0;
@@ -547,42 +621,13 @@ __global__ __launch_bounds__(256, 2) void selected_kernel(PrefillArgs a) {
       for (int e = 0; e < 4; ++e) z[q * 4 + e] = acc[e];
     }
     load_k(knext);
-    if (key0 + 63 > t) {  // the diagonal tile (uniform branch)
-      __asm__ volatile("" ::: "memory");
+    bf16x8 pb[2];
+    softmax_step(z, key0, pb);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = key0 + 32 * (q >> 1) + 8 * g4 + 4 * (q & 1) + e;
-          z[q * 4 + e] = key <= t ? z[q * 4 + e] : kNegInf;
-        }
-    }
-    float tm = z[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) tm = fmaxf(tm, z[e]);
-    tm = col_max4(tm);
-    const float mn = fmaxf(mrun, tm);  // finite: every listed tile holds key0 <= t
-    const float msl = mn * sl;
-    const float alpha = fast_exp2(fmaf(mrun, sl, -msl));
-    mrun = mn;
-    float p[16], sum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      p[e] = fast_exp2(fmaf(z[e], sl, -msl));
-      sum += p[e];
-    }
-    lrun = fmaf(lrun, alpha, sum);
-#pragma unroll
-    for (int n = 0; n < DT; ++n) O[n] *= alpha;
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[kc * 8 + e];
+    for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int n = 0; n < DT; ++n)
-        O[n] = mfma16x16x32(__builtin_bit_cast(bf16x8, vr[kc * DT + n]), pb, O[n]);
-    }
+        O[n] = mfma16x16x32(__builtin_bit_cast(bf16x8, vr[kc * DT + n]), pb[kc], O[n]);
     load_v(knext);
     key0 = knext;
   }
@@ -644,8 +689,8 @@ static void launch_prefill_all(const PrefillArgs& a, int which, hipStream_t s) {
   } else if (which == 1) {
     window_kernel<D, G><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, 0, s>>>(a);
   } else {
-    const long nwg = (long)((a.T + 3) / 4) * a.Hkv * a.B;
-    selected_kernel<D, G><<<dim3((unsigned)((nwg + 7) / 8 * 8)), 256, 0, s>>>(a);
+    const long nwg = (long)((a.T + kSelWaves - 1) / kSelWaves) * a.Hkv * a.B;
+    selected_kernel<D, G><<<dim3((unsigned)((nwg + 7) / 8 * 8)), kSelWaves * 64, 0, s>>>(a);
   }
 }
 

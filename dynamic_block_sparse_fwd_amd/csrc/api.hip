@@ -309,10 +309,11 @@ static int prefill_run(const nsa_config* c, unsigned stages, const void* q, cons
   a.n_local = c->n_local; a.window = c->window;
   a.ncmp = p.ncmp; a.NCP = p.NCP; a.TP = p.TP; a.nblk = p.nblk;
   a.scale_log2 = c->scale * 1.4426950408889634f;
+  a.fuse_window = s_cmp && s_win;  // one query tile, out written once
   mark(2);
   if (s_cmp) launch_cmp_select(a, stream);
   mark(3);
-  if (s_win) launch_window(a, stream);
+  if (s_win && !s_cmp) launch_window(a, stream);
   mark(4);
   if (s_slc) launch_selected(a, stream);
   mark(5);

@@ -19,6 +19,7 @@ struct PrefillArgs {
   int l, d, beta, top_n, n_local, window;
   int ncmp, NCP, TP, nblk;
   float scale_log2;     // softmax scale * log2(e)
+  int fuse_window;      // cmp_select also runs the window branch and writes out once
 };
 
 struct DecodeArgs {
@@ -100,7 +101,7 @@ void launch_compress(const uint16_t* x, const uint16_t* wt, uint16_t* xc, uint16
                      hipStream_t s);
 
 // Compressed attention (lse pass + probability pass), block importance, group selection;
-// writes out = gate_cmp * o_cmp and idx.
+// writes out = gate_cmp * o_cmp (+ gate_win * o_win when a.fuse_window) and idx.
 void launch_cmp_select(const PrefillArgs& a, hipStream_t s);
 // out += gate_win * o_win.
 void launch_window(const PrefillArgs& a, hipStream_t s);

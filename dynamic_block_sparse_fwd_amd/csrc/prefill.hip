@@ -58,7 +58,7 @@ __device__ __forceinline__ float head_sum(float v) {
 }
 
 template <int D, int G, bool FAST>
-__global__ __launch_bounds__(QTile<G>::NW * 64) void cmp_select_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select_kernel(PrefillArgs a) {
   using QT = QTile<G>;
   constexpr int NT = QT::NW * 64, TQ = QT::TQ, RTW = QT::RTW, DT = D / 16;
   __shared__ u16 Ks[64][D];
@@ -147,12 +147,99 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void cmp_select_kernel(PrefillAr
     rinv[rt] = (M == kNegInf) ? 0.f : 1.0f / L;
   }
 
-  // Pass 2: normalised probabilities -> o_cmp and group block scores.
   f32x4 O[RTW][DT];
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
     for (int n = 0; n < DT; ++n) O[rt][n] = zero4();
+  const int Hq = a.Hkv * G;
+  // The epilogue multiplies O by ef = g0 / L (L the compressed softmax sum), and pass 2 feeds
+  // the matrix core with p' = exp2(z - max) unscaled (its largest term exactly 1 in bf16).
+  // Fused, O first receives the window output times g2 / ef, so that out = g0 * o_cmp +
+  // g2 * o_win is written once and never read; a row with ef = 0 keeps the window output as is
+  // (ef taken as 1) and drops p' from the P V product (ps = 0).
+  float ps[RTW], ef[RTW];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) {
+    const int t = row_t[rt];
+    const float g0 =
+        t < a.T ? a.gate[(((long)b * a.T + t) * Hq + row_h[rt]) * 3 + 0] * rinv[rt] : 0.f;
+    const bool zero = a.fuse_window && g0 == 0.f;
+    ps[rt] = zero ? 0.f : 1.f;
+    ef[rt] = zero ? 1.f : g0;
+  }
+  if (a.fuse_window) {  // uniform: sliding window over the raw K/V, same query tile
+    const int tlast = (t0 + TQ - 1 < a.T - 1) ? t0 + TQ - 1 : a.T - 1;
+    const int kstart = t0 - a.window + 1 > 0 ? t0 - a.window + 1 : 0;
+    const int kw0 = kstart / 64, kw1 = tlast / 64;
+    const bool alive = t0 + TQ - 1 < a.T;
+    const u16* kb = a.k + bkv * (long)a.T * D;
+    const u16* vtb = a.vt + bkv * (long)D * a.TP;
+    float wm[RTW], wl[RTW];
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) { wm[rt] = kNegInf; wl[rt] = 0.f; }
+    kr.load(kb, (long)kw0 * 64, a.T - 1);
+    vr.load(vtb, a.TP, (long)kw0 * 64);
+    for (int kt = kw0; kt <= kw1; ++kt) {
+      __syncthreads();
+      kr.store(Ks);
+      vr.store(Vs);
+      __syncthreads();
+      if (kt < kw1) {
+        kr.load(kb, (long)(kt + 1) * 64, a.T - 1);
+        vr.load(vtb, a.TP, (long)(kt + 1) * 64);
+      }
+      // keys of this tile are inside every row's window unless the tile touches either end
+      const bool wfull = alive && kt * 64 >= tlast - a.window + 1 && kt * 64 + 63 <= t0;
+      float raw[RTW][16];
+      score_tiles<D, RTW>(Ks, qf, g4, r16, raw);
+      bf16x8 pb[RTW][2];
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt) {
+        const int t = row_t[rt];
+        const int lo = t - a.window + 1;
+        if (!wfull) {
+          __asm__ volatile("" ::: "memory");
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = kt * 64 + 32 * (e >> 3) + 8 * g4 + (e & 7);
+            raw[rt][e] = (key <= t && key >= lo && t < a.T) ? raw[rt][e] : kNegInf;
+          }
+        }
+        float tm = raw[rt][0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) tm = fmaxf(tm, raw[rt][e]);
+        tm = col_max4(tm);
+        const float mn = fmaxf(wm[rt], tm);
+        const float msl = (mn == kNegInf) ? 0.f : mn * sl;
+        const float alpha = fast_exp2(fmaf(wm[rt], sl, -msl));
+        wm[rt] = mn;
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = fast_exp2(fmaf(raw[rt][e], sl, -msl));
+          sum += p;
+          pb[rt][e >> 3][e & 7] = (__bf16)p;
+        }
+        wl[rt] = wl[rt] * alpha + sum;
+#pragma unroll
+        for (int n = 0; n < DT; ++n) O[rt][n] *= alpha;
+      }
+      pv_tiles<D, RTW>(Vs, pb, g4, r16, O);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const float L = col_sum4(wl[rt]);
+      const int t = row_t[rt];
+      const float g2 =
+          t < a.T ? a.gate[(((long)b * a.T + t) * Hq + row_h[rt]) * 3 + 2] : 0.f;
+      const float f = L > 0.f ? g2 / (L * ef[rt]) : 0.f;
+#pragma unroll
+      for (int n = 0; n < DT; ++n) O[rt][n] *= f;
+    }
+  }
+
+  // Pass 2: normalised probabilities -> o_cmp and group block scores.
   const float inv_l = 1.0f / (float)a.l;
   if (nkt > 0) {
     kr.load(kc, 0, a.NCP - 1);
@@ -188,7 +275,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void cmp_select_kernel(PrefillAr
           }
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pbt[rt][kc2][e] = (__bf16)pv[e];
+        for (int e = 0; e < 8; ++e) pbt[rt][kc2][e] = (__bf16)(pv[e] * ps[rt]);
         if constexpr (FAST) {
           const float cA = head_sum<G>(((pv[0] + pv[1]) + pv[2] + 0.5f * pv[3]) * rinv[rt]);
           const float cB = head_sum<G>(((pv[4] + pv[5]) + pv[6] + 0.5f * pv[7]) * rinv[rt]);
@@ -255,14 +342,14 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void cmp_select_kernel(PrefillAr
       Sb[threadIdx.x * nblk + 16 * nkt] = 0.f + Pc[threadIdx.x];
   }
 
-  // o_cmp epilogue: out = g0 * o_cmp.  Lane holds O^T[d = 16n + 4*g4 + e][row r16].
-  const int Hq = a.Hkv * G;
+  // epilogue: out = g0 * o_cmp (+ g2 * o_win fused).  Lane holds O^T[d = 16n + 4*g4 + e][row
+  // r16].
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
     const int t = row_t[rt];
     if (t < a.T) {
       const long rowoff = ((long)b * a.T + t) * Hq + row_h[rt];
-      const float g0 = a.gate[rowoff * 3 + 0] * rinv[rt];
+      const float g0 = ef[rt];
       float* op = a.out + rowoff * D;
 #pragma unroll
       for (int n = 0; n < DT; ++n) {

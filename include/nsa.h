@@ -137,9 +137,11 @@ int nsa_prefill(const nsa_config* cfg, const void* q, const void* k, const void*
  *                         NSA_STAGE_CMP_SELECT sel_idx is an INPUT (required): per (t, group)
  *                         top_n block indices; entries outside [0, ceil(T/sel_block)) (e.g. the
  *                         -1 padding) are skipped, tiles past t are skipped
- * Without NSA_STAGE_CMP_SELECT out is cleared first.  The stages accumulate in nsa_prefill's
- * order (compressed, window, selected), so NSA_STAGE_ALL reproduces nsa_prefill bit for bit and
- * the sum of separately computed stages equals it to fp32 rounding.  There is no
+ * Without NSA_STAGE_CMP_SELECT out is cleared first.  With NSA_STAGE_CMP_SELECT and
+ * NSA_STAGE_WINDOW together the window branch runs inside the compressed kernel on the same
+ * query tile (out is written once), as in nsa_prefill, so NSA_STAGE_ALL reproduces nsa_prefill
+ * bit for bit; separately computed stages add up to it to within the bf16 rounding of the
+ * attention probabilities fed to the matrix core.  There is no
  * separate combine stage: each branch adds its gated output.  wk, wv may be NULL without
  * NSA_STAGE_CMP_SELECT.  Same workspace and errors as nsa_prefill; NSA_ERR_INVALID_ARG for an
  * empty or unknown stage mask.
@@ -156,8 +158,8 @@ int nsa_prefill_stages(const nsa_config* cfg, unsigned stages, const void* q, co
 /*
  * Instrumented nsa_prefill: identical work, plus events[s] recorded on `stream` before stage s
  * and events[NSA_PREFILL_NSTAGES] after the last stage.  Stages: 0 layout (value and weight
- * transposes), 1 block compression of K and V, 2 compressed attention + block importance +
- * selection, 3 sliding window, 4 selected blocks.  `events` holds NSA_PREFILL_NSTAGES + 1
+ * transposes), 1 block compression of K and V, 2 compressed attention + sliding window + block
+ * importance + selection, 3 (empty: the window runs inside stage 2), 4 selected blocks.  `events` holds NSA_PREFILL_NSTAGES + 1
  * caller-created events (hipEventCreate); for measurement only.
  */
 #define NSA_PREFILL_NSTAGES 5

@@ -159,8 +159,9 @@ def _stage_inputs(cfg, x):
 
 def test_prefill_stages_compose_bit_exact():
     """nsa_prefill_stages runs the same kernels: all stages at once equal nsa_prefill bit for
-    bit, and the three stages run separately add up to it to fp32 rounding (inside a kernel the
-    gated add is one fused multiply-add, so summing finished stages rounds once more)."""
+    bit; the three stages run separately (the window then in its own kernel, not fused into the
+    compressed one) add up to it within the bf16 rounding of the probabilities that feed the
+    matrix core."""
     cfg = O.NsaCfg(2, 1300, 2, 16, 128)
     x = S.nsa_prefill_inputs(11, 2, 1300, 2, 16, 128)
     nsa, c, d = _stage_inputs(cfg, x)
@@ -178,7 +179,7 @@ def test_prefill_stages_compose_bit_exact():
     np.testing.assert_array_equal(aidx.cpu().numpy(), fidx.cpu().numpy())
     np.testing.assert_array_equal(cidx.cpu().numpy(), fidx.cpu().numpy())
     summed = (o_c + o_w) + o_s
-    np.testing.assert_allclose(summed.cpu().numpy(), full.cpu().numpy(), rtol=2e-6, atol=2e-6)
+    np.testing.assert_allclose(summed.cpu().numpy(), full.cpu().numpy(), rtol=0, atol=2e-3)
 
 
 def test_prefill_window_and_selected_stages_against_oracle():

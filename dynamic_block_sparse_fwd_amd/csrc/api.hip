@@ -68,7 +68,7 @@ DecodeShape decode_shape(const nsa_config* c) {
   p.NCH = (p.ncmp + chunk - 1) / chunk;
   p.NT = (p.ncmp + 63) / 64;
   p.NBT = (63 * c->cmp_stride + c->cmp_len - 1) / c->sel_block + 2;
-  p.NSPLIT = (decode_max_tiles(c) + 3) / 4;
+  p.NSPLIT = (decode_max_tiles(c) + decode_tiles_per_split() - 1) / decode_tiles_per_split();
   return p;
 }
 

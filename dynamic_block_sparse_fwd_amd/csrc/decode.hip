@@ -23,7 +23,7 @@ namespace nsa {
 constexpr int TPW = 4;               // 64-token tiles per wave in dec_cmp
 constexpr int CHUNK = 4 * TPW * 64;  // compressed tokens per dec_cmp workgroup
 constexpr int kMaxTiles = 160;       // selected + window tiles per group
-constexpr int kMaxSplits = 64;       // 4-tile splits of that list
+constexpr int kMaxSplits = 64;       // splits of that list (8 tiles each)
 
 // One 64-key tile of a [rows, D] K/V cache pair in registers: K in MFMA A-operand order, V in
 // the gather order of the transposing LDS store.  Rows past `last` are clamped to it.
@@ -34,6 +34,11 @@ struct DecTile {
 
   __device__ __forceinline__ void load(const u16* kb, const u16* vb, int k0, int last,
                                        int lane) {
+    load_k(kb, k0, last, lane);
+    load_v(vb, k0, last, lane);
+  }
+
+  __device__ __forceinline__ void load_k(const u16* kb, int k0, int last, int lane) {
     const int g4 = lane >> 4, r16 = lane & 15;
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
@@ -46,6 +51,9 @@ struct DecTile {
           k[(kc * 2 + s) * (D / 32) + c] = *reinterpret_cast<const u32x4*>(
               kb + ((uint32_t)row * D + 8 * g4 + 32 * c));
       }
+  }
+
+  __device__ __forceinline__ void load_v(const u16* vb, int k0, int last, int lane) {
 #pragma unroll
     for (int it = 0; it < DC / 4; ++it) {
       const int x = it * 64 + lane, kq = x & 15, dc = x >> 4;
@@ -453,6 +461,8 @@ __global__ __launch_bounds__(kSelThreads) void dec_select_kernel(DecodeArgs a) {
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int bcur = nb - 1;
+  const int flo = bcur - a.n_local + 1;
+  const int kfree = a.top_n - 1 - a.n_local;
   if (threadIdx.x < 64) {
     int32_t* orow = a.idx + bkv * a.top_n;
     if (all) {
@@ -462,8 +472,6 @@ __global__ __launch_bounds__(kSelThreads) void dec_select_kernel(DecodeArgs a) {
         sidx[lane] = el;
       }
     } else {
-      const int flo = bcur - a.n_local + 1;
-      const int kfree = a.top_n - 1 - a.n_local;
       int el = wave_topk(Ss, 1, flo, kfree, lane);
       if (lane == kfree) el = 0;
       if (lane > kfree && lane < a.top_n) el = flo + (lane - kfree - 1);
@@ -505,9 +513,13 @@ __global__ __launch_bounds__(kSelThreads) void dec_select_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------------ phase 3: selected + window
 
-// One wave per listed tile; four tiles per workgroup, merged into one partial per branch.
+// Two listed tiles per wave (the second in flight while the first computes), eight per
+// workgroup, merged into one partial per branch; the first four tiles of a split go to the four
+// waves, then the next four.
+constexpr int kTilesPerWave = 2;
+
 template <int D>
-__global__ __launch_bounds__(256) void dec_tiles_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void dec_tiles_kernel(DecodeArgs a) {
   constexpr int DT = D / 16, OP = D + 4;
   constexpr int VT_U16 = 4 * D * 64, OB_U16 = 4 * 2 * 16 * OP * 2;
   __shared__ __align__(16) u16 smem[VT_U16 > OB_U16 ? VT_U16 : OB_U16];
@@ -516,57 +528,92 @@ __global__ __launch_bounds__(256) void dec_tiles_kernel(DecodeArgs a) {
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const long bkv = (long)b * a.Hkv + kvh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int my = split * 4 + wave;  // < NSPLIT * 4 <= kMaxTiles
   const int tn = a.tn[bkv];
-  const int code_raw = a.tl[bkv * kMaxTiles + my];
-  if (split * 4 >= tn) return;  // uniform
+  int code_raw[kTilesPerWave];
+#pragma unroll
+  for (int u = 0; u < kTilesPerWave; ++u) {
+    const int my = split * 4 * kTilesPerWave + 4 * u + wave;
+    code_raw[u] = a.tl[bkv * kMaxTiles + (my < kMaxTiles ? my : 0)];
+  }
+  if (split * 4 * kTilesPerWave >= tn) return;  // uniform
   const int g4 = lane >> 4, r16 = lane & 15;
   const int t = a.seqlens[b] - 1;
   const float sl = a.scale_log2;
-  const bool have = my < tn;
-  const int code = have ? code_raw : 0;
-  const int k0 = (code & 0x3FFFFFFF) * 64;
-  const bool in_slc = have && ((code >> 30) & 1);
   const int w0 = t - a.window + 1;
-  const bool in_win = have && (k0 + 63 >= w0);
+  const u16* kcb = a.kcache + bkv * (long)a.L * D;
+  const u16* vcb = a.vcache + bkv * (long)a.L * D;
 
   bf16x8 qf[D / 32];
   load_q_decode<D>(a, b, kvh, lane, qf);
-  DecTile<D> kv;
-  kv.load(a.kcache + bkv * (long)a.L * D, a.vcache + bkv * (long)a.L * D, k0, t, lane);
-  f32x4 acc[4];
-  kv.scores(qf, acc);
-  kv.stage(Vt[wave], lane);
-  __asm__ volatile("" ::: "memory");  // Vt[wave] is this wave's own: LDS keeps its order
-
+  float mrun[2] = {kNegInf, kNegInf}, lrun[2] = {0.f, 0.f};
   f32x4 O[2][DT];
 #pragma unroll
-  for (int br = 0; br < 2; ++br) {
-    float p[16];
-    float tm = kNegInf;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + lane_key(q4, i, g4);
-        const bool ok = br == 0 ? (in_slc && key <= t) : (in_win && key <= t && key >= w0);
-        const float r = ok ? acc[q4][i] : kNegInf;
-        p[q4 * 4 + i] = r;
-        tm = fmaxf(tm, r);
-      }
-    tm = col_max4(tm);
-    const float ms = tm == kNegInf ? 0.f : tm * sl;
-    float ls = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      p[e] = fast_exp2(fmaf(p[e], sl, -ms));
-      ls += p[e];
-    }
-    ls = col_sum4(ls);
+  for (int br = 0; br < 2; ++br)
 #pragma unroll
     for (int n = 0; n < DT; ++n) O[br][n] = zero4();
-    tile_pv<D>(Vt[wave], p, g4, r16, O[br]);
-    if (g4 == 0) { Wm[br][wave][r16] = tm; Wl[br][wave][r16] = ls; }
+
+  auto tile_of = [&](int u, bool* have, bool* in_slc, bool* in_win) {
+    const int my = split * 4 * kTilesPerWave + 4 * u + wave;
+    *have = my < tn;
+    const int code = *have ? code_raw[u] : 0;
+    const int k0 = (code & 0x3FFFFFFF) * 64;
+    *in_slc = *have && ((code >> 30) & 1);
+    *in_win = *have && (k0 + 63 >= w0);
+    return k0;
+  };
+  DecTile<D> kv;
+  bool have0, slc0, win0;
+  int k0 = tile_of(0, &have0, &slc0, &win0);
+  kv.load(kcb, vcb, k0, t, lane);
+#pragma unroll
+  for (int u = 0; u < kTilesPerWave; ++u) {
+    bool have, in_slc, in_win;
+    k0 = tile_of(u, &have, &in_slc, &in_win);
+    f32x4 acc[4];
+    kv.scores(qf, acc);
+    __asm__ volatile("" ::: "memory");  // the previous tile's Vt reads stay before these writes
+    kv.stage(Vt[wave], lane);
+    __asm__ volatile("" ::: "memory");  // Vt[wave] is this wave's own: LDS keeps its order
+    bool h1, s1, w1;
+    const int k1 = u + 1 < kTilesPerWave ? tile_of(u + 1, &h1, &s1, &w1) : 0;
+    // the next tile's K is in flight during this tile's softmax and P V, its V after them
+    // (compile-time conditions: the loop is unrolled)
+    if (u + 1 < kTilesPerWave) kv.load_k(kcb, k1, t, lane);
+#pragma unroll
+    for (int br = 0; br < 2; ++br) {
+      float p[16];
+      float tm = kNegInf;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + lane_key(q4, i, g4);
+          const bool ok = br == 0 ? (in_slc && key <= t) : (in_win && key <= t && key >= w0);
+          const float r = ok ? acc[q4][i] : kNegInf;
+          p[q4 * 4 + i] = r;
+          tm = fmaxf(tm, r);
+        }
+      tm = col_max4(tm);
+      const float mn = fmaxf(mrun[br], tm);
+      const float ms = mn == kNegInf ? 0.f : mn * sl;
+      const float alpha = fast_exp2(fmaf(mrun[br], sl, -ms));
+      mrun[br] = mn;
+      float ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        p[e] = fast_exp2(fmaf(p[e], sl, -ms));
+        ls += p[e];
+      }
+      lrun[br] = fmaf(lrun[br], alpha, col_sum4(ls));
+#pragma unroll
+      for (int n = 0; n < DT; ++n) O[br][n] *= alpha;
+      tile_pv<D>(Vt[wave], p, g4, r16, O[br]);
+    }
+    if (u + 1 < kTilesPerWave) kv.load_v(vcb, k1, t, lane);
+  }
+  if (g4 == 0) {
+#pragma unroll
+    for (int br = 0; br < 2; ++br) { Wm[br][wave][r16] = mrun[br]; Wl[br][wave][r16] = lrun[br]; }
   }
   __syncthreads();  // Vt reads done; maxima posted
   // merge the four waves per branch into this split's partial, summed through LDS
@@ -617,7 +664,7 @@ __global__ __launch_bounds__(256) void dec_combine_kernel(DecodeArgs a) {
   const int t = a.seqlens[b] - 1;
   const int nvis = n_visible(t, a.l, a.d, a.ncmp);
   const int nch = (nvis + CHUNK - 1) / CHUNK;
-  const int nsp = (a.tn[bkv] + 3) / 4;
+  const int nsp = (a.tn[bkv] + 4 * kTilesPerWave - 1) / (4 * kTilesPerWave);
   for (int e = threadIdx.x; e < nsp * 32; e += 256) {
     const int s = e >> 5, br = (e >> 4) & 1, h = e & 15;
     pm[br][s][h] = a.pm[(bkv * a.NSPLIT + s) * 32 + (e & 31)];
@@ -657,6 +704,7 @@ __global__ __launch_bounds__(256) void dec_combine_kernel(DecodeArgs a) {
 
 int decode_chunk_tokens() { return CHUNK; }
 int decode_max_splits() { return kMaxSplits; }
+int decode_tiles_per_split() { return 4 * kTilesPerWave; }
 int decode_max_tile_list() { return kMaxTiles; }
 size_t decode_select_lds_bytes(int nch, int nblk) {
   return (size_t)(2 * nch * 16 + nblk) * sizeof(float);

@@ -41,7 +41,8 @@ struct DecodeArgs {
   float* lse;   // [B*Hkv, 16]
   int32_t* tl;  // [B*Hkv, 160] selected / window tile list
   int32_t* tn;  // [B*Hkv] its length
-  // per 4-tile split of the tile list: [.., NSPLIT, 2 (slc, win), 16 (, D)]
+  // per split of the tile list (decode_tiles_per_split() tiles): [.., NSPLIT, 2 (slc, win),
+  // 16 (, D)]
   float* pm;
   float* pl;
   float* po;
@@ -55,6 +56,7 @@ struct DecodeArgs {
 void launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev);
 int decode_chunk_tokens();
 int decode_max_splits();
+int decode_tiles_per_split();
 int decode_max_tile_list();
 size_t decode_select_lds_bytes(int nch, int nblk);
 

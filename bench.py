@@ -243,8 +243,7 @@ def cpu_baseline_prefill(x, T, rows=1024):
     O.nsa_prefill_rows(cfg, x["q"], x["k"], x["v"], kc, vc, x["gate"], rb, rt)
     t_rows = time.perf_counter() - t0
     est = t_cmp + t_rows * T / len(rt)
-    cores = len(os.sched_getaffinity(0))
-    return {"value": T / est, "unit": "tok/s", "cores": cores, "kind": "oracle",
+    return {"value": T / est, "unit": "tok/s", "cores": O.threads(), "kind": "oracle",
             "sample": "fp64 oracle: full K/V compression (%.1fs) + %d positions every %d-th of "
                       "the 64k prefill, all 64 heads (%.1fs), scaled to 65536 positions"
                       % (t_cmp, len(rt), step, t_rows)}
@@ -351,7 +350,7 @@ def bench_decode(args, B=32, L=65536, Hkv=4, G=16, D=128, seed=3, calls=20):
     return res, x
 
 
-def cpu_baseline_decode(x, B=32, L=65536, Hkv=4, G=16, D=128, nseq=4):
+def cpu_baseline_decode(x, B=32, L=65536, Hkv=4, G=16, D=128, nseq=4, reps=15):
     """fp64 oracle decode of `nseq` of the B sequences (their compressed caches built by the
     oracle, not timed: the decode call takes them as inputs), scaled to tokens/s."""
     import oracle as O
@@ -361,12 +360,17 @@ def cpu_baseline_decode(x, B=32, L=65536, Hkv=4, G=16, D=128, nseq=4):
     kc = O.compress(sub["kcache"], x["wk"], 32, 16)
     vc = O.compress(sub["vcache"], x["wv"], 32, 16)
     cfg = O.NsaCfg(nseq, L, Hkv, G, D)
-    t0 = time.perf_counter()
-    O.nsa_decode(cfg, sub["q"], sub["kcache"], sub["vcache"], kc, vc, sub["seqlens"], sub["gate"])
-    dt = time.perf_counter() - t0
-    return {"value": nseq / dt, "unit": "tok/s", "cores": len(os.sched_getaffinity(0)),
-            "kind": "oracle", "sample": "fp64 oracle decode of %d of the %d sequences "
-                                        "(compressed caches precomputed, untimed)" % (nseq, B)}
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        O.nsa_decode(cfg, sub["q"], sub["kcache"], sub["vcache"], kc, vc, sub["seqlens"],
+                     sub["gate"])
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    return {"value": nseq / dt, "unit": "tok/s", "cores": O.threads(),
+            "kind": "oracle", "sample": "fp64 oracle decode of %d of the %d sequences, median of "
+                                        "%d runs (compressed caches precomputed, untimed)"
+                                        % (nseq, B, reps)}
 
 
 # ----------------------------------------------------------------------------- MoBA
@@ -431,7 +435,7 @@ def bench_moba(args, B=1, T=131072, H=32, D=128, seed=4, calls=5):
     return res, x
 
 
-def cpu_baseline_moba(x, T=131072, H=32, D=128, rows=1024):
+def cpu_baseline_moba(x, T=131072, H=32, D=128, rows=24576):
     import oracle as O
 
     cfg = O.MobaCfg(1, T, H, D, block=512, top_k=3)
@@ -444,7 +448,7 @@ def cpu_baseline_moba(x, T=131072, H=32, D=128, rows=1024):
     O.moba_prefill_rows(cfg, x["q"], x["k"], x["v"], np.zeros_like(rt), rt, kbar=kbar)
     t_rows = time.perf_counter() - t0
     est = t_pool + t_rows * T / len(rt)
-    return {"value": T / est, "unit": "tok/s", "cores": len(os.sched_getaffinity(0)),
+    return {"value": T / est, "unit": "tok/s", "cores": O.threads(),
             "kind": "oracle", "sample": "fp64 oracle: block-key pooling (%.1fs) + %d positions "
                                         "every %d-th, all 32 heads (%.1fs), scaled to %d"
                                         % (t_pool, len(rt), step, t_rows, T)}
@@ -459,7 +463,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seq", type=int, default=65536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-moba", action="store_true")
     ap.add_argument("--only", choices=("prefill", "decode", "moba"),

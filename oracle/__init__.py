@@ -57,7 +57,14 @@ def _load():
         _lib.omoba_pool.restype = None
         _lib.omoba_prefill_rows.argtypes = [P] * 5 + [ctypes.c_int] + [P] * 7
         _lib.omoba_prefill_rows.restype = ctypes.c_int
+        _lib.onsa_threads.argtypes = []
+        _lib.onsa_threads.restype = ctypes.c_int
     return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops run on."""
+    return int(_load().onsa_threads())
 
 
 def _p(a):

@@ -37,6 +37,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 typedef struct {
   int B, T, Hkv, G, D;
@@ -431,4 +434,13 @@ int omoba_prefill_rows(const omoba_cfg* cf, const uint16_t* q, const uint16_t* k
     free(qd); free(z); free(keys); free(cs); free(I);
   }
   return 0;
+}
+
+/* Threads the parallel loops above use (for reporting the CPU baseline). */
+int onsa_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }

@@ -286,7 +286,7 @@ def bench_decode(args, B=32, L=65536, Hkv=4, G=16, D=128, seed=3, calls=20):
     d = {k: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).to(dev)
          for k, v in x.items()}
     kc = nsa.nsa_compress(cfg, d["kcache"], d["wk"])
-    vc = nsa.nsa_compress(cfg, d["vcache"], d["wv"])
+    vc = nsa.nsa_compress_tiles(cfg, d["vcache"], d["wv"])
     out = torch.empty((B, Hkv * G, D), dtype=torch.float32, device=dev)
     idx = torch.empty((B, Hkv, cfg.top_n), dtype=torch.int32, device=dev)
     ws = torch.empty(nsa.decode_workspace_bytes(cfg), dtype=torch.uint8, device=dev)

@@ -47,11 +47,13 @@ EXPORTS = {
     "nsa_validate": (ctypes.c_int, [ctypes.c_void_p]),
     "moba_validate": (ctypes.c_int, [ctypes.c_void_p]),
     "nsa_num_compressed": (ctypes.c_int32, [ctypes.c_int32] * 3),
+    "nsa_num_compressed_tiles": (ctypes.c_int32, [ctypes.c_int32] * 3),
     "nsa_compress_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
     "nsa_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
     "nsa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
     "moba_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
     "nsa_compress": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "nsa_compress_tiles": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p]),
     "nsa_prefill": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p]),
     "nsa_prefill_stages": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint] + [ctypes.c_void_p] * 9
                            + [ctypes.c_size_t, ctypes.c_void_p]),
@@ -108,6 +110,11 @@ class NsaConfig:
     @property
     def ncmp(self):
         return (self.T - self.cmp_len) // self.cmp_stride + 1 if self.T >= self.cmp_len else 0
+
+    @property
+    def ncmp_tiles(self):
+        """64-token tiles of compressed tokens: ceil(ncmp / 64)."""
+        return (self.ncmp + 63) // 64
 
     def c(self):
         s = self.scale if self.scale is not None else self.D ** -0.5
@@ -211,6 +218,26 @@ def nsa_compress(cfg: NsaConfig, x, w, out=None, ws=None, stream=None):
     return out
 
 
+def nsa_compress_tiles(cfg: NsaConfig, x, w, out=None, ws=None, stream=None):
+    """x bf16 [B, Hkv, T, D], w bf16 [l, D, D] -> compressed bf16 bits in feature-major 64-token
+    tiles [B, Hkv, ncmp_tiles, D, 64] (tokens past n_cmp zero); the compressed-value layout of
+    nsa_decode."""
+    torch = _torch()
+    lib = load_library()
+    c = cfg.c()
+    shape = (cfg.B, cfg.Hkv, cfg.ncmp_tiles, cfg.D, 64)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.int16, device=x.device)
+    ws = _workspace(lib.nsa_compress_workspace_bytes(ctypes.byref(c)), x.device, ws)
+    bt = _bf16_types()
+    st = lib.nsa_compress_tiles(
+        ctypes.byref(c), _dev(x, "x", bt, (cfg.B, cfg.Hkv, cfg.T, cfg.D)),
+        _dev(w, "w", bt, (cfg.cmp_len, cfg.D, cfg.D)), _dev(out, "out", bt, shape),
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream))
+    _check(st, "nsa_compress_tiles")
+    return out
+
+
 PREFILL_STAGES = ("layout", "compress", "cmp_select", "window", "selected")
 
 
@@ -282,7 +309,9 @@ DECODE_STAGES = ("cmp_stream", "scores_select", "tiles", "combine")
 
 def nsa_decode(cfg: NsaConfig, q, kcache, vcache, kcmp, vcmp, seqlens, gate, out=None,
                sel_idx=None, ws=None, want_idx=True, stream=None, events=None):
-    """cfg.T is the cache capacity.  Returns (out fp32 [B,Hq,D], sel_idx [B,Hkv,top_n]).
+    """cfg.T is the cache capacity; kcmp is [B,Hkv,ncmp,D] (nsa_compress), vcmp is
+    [B,Hkv,ncmp_tiles,D,64] (nsa_compress_tiles).  Returns (out fp32 [B,Hq,D], sel_idx
+    [B,Hkv,top_n]).
     events: optional ctypes array of len(DECODE_STAGES) + 1 hipEvent_t (nsa_decode_timed)."""
     torch = _torch()
     lib = load_library()
@@ -300,7 +329,7 @@ def nsa_decode(cfg: NsaConfig, q, kcache, vcache, kcmp, vcmp, seqlens, gate, out
     st = fn(
         ctypes.byref(c), _dev(q, "q", bt, (B, Hq, D)), _dev(kcache, "kcache", bt, (B, Hkv, L, D)),
         _dev(vcache, "vcache", bt, (B, Hkv, L, D)), _dev(kcmp, "kcmp", bt, (B, Hkv, cfg.ncmp, D)),
-        _dev(vcmp, "vcmp", bt, (B, Hkv, cfg.ncmp, D)),
+        _dev(vcmp, "vcmp", bt, (B, Hkv, cfg.ncmp_tiles, D, 64)),
         _dev(seqlens, "seqlens", (torch.int32,), (B,)),
         _dev(gate, "gate", (torch.float32,), (B, Hq, 3)),
         _dev(out, "out", (torch.float32,), (B, Hq, D)),

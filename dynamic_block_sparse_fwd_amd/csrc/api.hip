@@ -204,6 +204,10 @@ int32_t nsa_num_compressed(int32_t T, int32_t cmp_len, int32_t cmp_stride) {
   return (T - cmp_len) / cmp_stride + 1;
 }
 
+int32_t nsa_num_compressed_tiles(int32_t T, int32_t cmp_len, int32_t cmp_stride) {
+  return (nsa_num_compressed(T, cmp_len, cmp_stride) + 63) / 64;
+}
+
 int nsa_validate(const nsa_config* cfg) { return check_nsa(cfg); }
 int moba_validate(const moba_config* cfg) { return check_moba(cfg); }
 
@@ -226,23 +230,36 @@ size_t nsa_compress_workspace_bytes(const nsa_config* c) {
   return align_up((size_t)c->cmp_len * c->D * c->D * 2);
 }
 
-int nsa_compress(const nsa_config* c, const void* x, const void* w, void* xc, void* ws,
-                 size_t ws_bytes, hipStream_t stream) {
+static int compress_impl(const nsa_config* c, const void* x, const void* w, void* xc, void* xct,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_compress(c);
   if (st != NSA_OK) return st;
   const int ncmp = nsa_num_compressed(c->T, c->cmp_len, c->cmp_stride);
-  if (!x || !w || !ws || (!xc && ncmp > 0)) return NSA_ERR_INVALID_ARG;  // empty output may be null
-  if (!aligned16(x) || !aligned16(w) || !aligned16(xc) || !aligned16(ws))
+  void* dst = xc ? xc : xct;
+  if (!x || !w || !ws || (!dst && ncmp > 0)) return NSA_ERR_INVALID_ARG;  // empty output may be null
+  if (!aligned16(x) || !aligned16(w) || !aligned16(dst) || !aligned16(ws))
     return NSA_ERR_INVALID_ARG;
   if (ws_bytes < nsa_compress_workspace_bytes(c)) return NSA_ERR_WORKSPACE;
   if (ncmp == 0) return NSA_OK;
   const int LD = c->cmp_len * c->D;
   uint16_t* wt = static_cast<uint16_t*>(ws);
+  const int ncp = xct ? 64 * ((ncmp + 63) / 64) : 0;
   (void)hipGetLastError();
   launch_transpose(static_cast<const uint16_t*>(w), wt, 1, LD, c->D, LD, stream);
-  launch_compress(static_cast<const uint16_t*>(x), wt, static_cast<uint16_t*>(xc), nullptr,
-                  c->B * c->Hkv, c->T, c->D, c->cmp_len, c->cmp_stride, ncmp, ncmp, 0, stream);
+  launch_compress(static_cast<const uint16_t*>(x), wt, static_cast<uint16_t*>(xc),
+                  static_cast<uint16_t*>(xct), c->B * c->Hkv, c->T, c->D, c->cmp_len,
+                  c->cmp_stride, ncmp, xc ? ncmp : 0, ncp, true, stream);
   return hip_status();
+}
+
+int nsa_compress(const nsa_config* c, const void* x, const void* w, void* xc, void* ws,
+                 size_t ws_bytes, hipStream_t stream) {
+  return compress_impl(c, x, w, xc, nullptr, ws, ws_bytes, stream);
+}
+
+int nsa_compress_tiles(const nsa_config* c, const void* x, const void* w, void* xct,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  return compress_impl(c, x, w, nullptr, xct, ws, ws_bytes, stream);
 }
 
 // Runs the requested prefill stages (NSA_STAGE_* bits) on the stream.  Without the compressed
@@ -291,9 +308,9 @@ static int prefill_run(const nsa_config* c, unsigned stages, const void* q, cons
   mark(1);
   if (s_cmp && p.ncmp > 0) {
     launch_compress(static_cast<const uint16_t*>(k), wkt, kcb, nullptr, BH, c->T, c->D,
-                    c->cmp_len, c->cmp_stride, p.ncmp, p.NCP, p.NCP, stream);
+                    c->cmp_len, c->cmp_stride, p.ncmp, p.NCP, p.NCP, false, stream);
     launch_compress(static_cast<const uint16_t*>(v), wvt, nullptr, vct, BH, c->T, c->D,
-                    c->cmp_len, c->cmp_stride, p.ncmp, p.NCP, p.NCP, stream);
+                    c->cmp_len, c->cmp_stride, p.ncmp, p.NCP, p.NCP, false, stream);
   }
   PrefillArgs a{};
   a.q = static_cast<const uint16_t*>(q);
@@ -378,7 +395,7 @@ static int decode_impl(const nsa_config* c, const void* q, const void* kcache,
   a.kcache = static_cast<const uint16_t*>(kcache);
   a.vcache = static_cast<const uint16_t*>(vcache);
   a.kc = static_cast<const uint16_t*>(kcmp);
-  a.vc = static_cast<const uint16_t*>(vcmp);
+  a.vct = static_cast<const uint16_t*>(vcmp);
   a.seqlens = seqlens;
   a.gate = gate;
   a.out = out;

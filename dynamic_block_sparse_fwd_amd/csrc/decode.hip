@@ -101,6 +101,88 @@ struct DecTile {
   }
 };
 
+// One 64-token tile of the compressed caches in registers: K rows in MFMA A-operand order
+// (rows past `last` clamp to it) and V^T fragments read straight from the tiled feature-major
+// value cache (one contiguous [D][64] block per tile) as the A operand of O^T += V^T P^T, so no
+// LDS staging is needed.
+template <int D>
+struct CmpTile {
+  static constexpr int DT = D / 16;
+  u32x4 k[D / 8], vt[2 * DT];
+
+  __device__ __forceinline__ void load_k(const u16* kb, int k0, int last, int lane) {
+    const int g4 = lane >> 4, r16 = lane & 15;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        int row = k0 + 32 * kc + perm_key(r16, s);
+        row = row < last ? row : last;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+          k[(kc * 2 + s) * (D / 32) + c] = *reinterpret_cast<const u32x4*>(
+              kb + ((uint32_t)row * D + 8 * g4 + 32 * c));
+      }
+  }
+
+  // Lane (g4, r16) of fragment (kc, n) holds V^T[16n + r16][k0 + 32kc + 8g4 .. + 7].  `k0`
+  // clamps to `last0`, the last visible tile, so a prefetch past the end stays in bounds.
+  __device__ __forceinline__ void load_vt(const u16* vtb, int k0, int last0, int lane) {
+    const int g4 = lane >> 4, r16 = lane & 15;
+    k0 = k0 < last0 ? k0 : last0;
+    const u16* tb = vtb + (uint32_t)k0 * D;  // tile k0 / 64 starts at (k0 / 64) * D * 64
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int n = 0; n < DT; ++n)
+        vt[kc * DT + n] = *reinterpret_cast<const u32x4*>(
+            tb + ((16 * n + r16) * 64 + 32 * kc + 8 * g4));
+  }
+
+  // Zero the V^T columns from `nvis` on: the cache past the visible tokens is arbitrary, and a
+  // zero probability times a NaN is still NaN.
+  __device__ __forceinline__ void mask_tail(int k0, int nvis, int lane) {
+    const int g4 = lane >> 4;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const int lim = nvis - (k0 + 32 * kc + 8 * g4);  // valid columns among this lane's 8
+      uint32_t m[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        m[w] = (2 * w < lim ? 0xFFFFu : 0u) | (2 * w + 1 < lim ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int n = 0; n < DT; ++n)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) vt[kc * DT + n][w] &= m[w];
+    }
+  }
+
+  // S^T = K Q^T; acc[kc*2 + s][i] belongs to key 32*kc + 8*g4 + 4*s + i of the tile.
+  __device__ __forceinline__ void scores(const bf16x8* qf, f32x4* acc) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 a = zero4();
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+        a = mfma16x16x32(__builtin_bit_cast(bf16x8, k[q * (D / 32) + c]), qf[c], a);
+      acc[q] = a;
+    }
+  }
+
+  // O^T += V^T P^T; p[kc*8 + e] is the probability of key 32kc + 8g4 + e.
+  __device__ __forceinline__ void pv(const float* p, f32x4* O) const {
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[kc * 8 + e];
+#pragma unroll
+      for (int n = 0; n < DT; ++n)
+        O[n] = mfma16x16x32(__builtin_bit_cast(bf16x8, vt[kc * DT + n]), pb, O[n]);
+    }
+  }
+};
+
 template <int D>
 __device__ __forceinline__ void load_q_decode(const DecodeArgs& a, int b, int kvh, int lane,
                                               bf16x8* qf) {
@@ -146,7 +228,7 @@ __device__ __forceinline__ int block_tok_hi(int j, int beta, int d) {
 template <int D, bool FAST>
 __global__ __launch_bounds__(256, FAST ? 2 : 1) void dec_cmp_kernel(DecodeArgs a) {
   constexpr int DT = D / 16, OP = D + 4;
-  __shared__ __align__(16) u16 Vt[4][D][64];
+  __shared__ __align__(16) float Ob[4 * 16 * OP];
   __shared__ float Wm[4][16], Wl[4][16];
   __shared__ float Pw[FAST ? 1 : 4][FAST ? 1 : 16][64];
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -158,7 +240,8 @@ __global__ __launch_bounds__(256, FAST ? 2 : 1) void dec_cmp_kernel(DecodeArgs a
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
   const u16* kcb = a.kc + bkv * a.ncmp * D;
-  const u16* vcb = a.vc + bkv * a.ncmp * D;
+  const u16* vtb = a.vct + bkv * (long)a.NT * D * 64;
+  const int last0 = (nvis - 1) & ~63;  // first key of the last visible tile
   const float sl = a.scale_log2;
 
   bf16x8 qf[D / 32];
@@ -170,8 +253,11 @@ __global__ __launch_bounds__(256, FAST ? 2 : 1) void dec_cmp_kernel(DecodeArgs a
 
   // wave w takes tiles c0/64 + w, + 4, + 8, ... (the four waves read adjacent tiles together)
   const int tile0 = (c0 >> 6) + wave;
-  DecTile<D> cur;
-  if (tile0 * 64 < nvis) cur.load(kcb, vcb, tile0 * 64, nvis - 1, lane);
+  CmpTile<D> cur;
+  if (tile0 * 64 < nvis) {
+    cur.load_k(kcb, tile0 * 64, nvis - 1, lane);
+    cur.load_vt(vtb, tile0 * 64, last0, lane);
+  }
 #pragma unroll
   for (int it = 0; it < TPW; ++it) {
     const int tile = tile0 + 4 * it;
@@ -179,12 +265,10 @@ __global__ __launch_bounds__(256, FAST ? 2 : 1) void dec_cmp_kernel(DecodeArgs a
     if (k0 >= nvis) break;  // wave-uniform
     f32x4 acc[4];
     cur.scores(qf, acc);
-    __asm__ volatile("" ::: "memory");  // the previous tile's Vt reads stay before these writes
-    cur.stage(Vt[wave], lane);
     // the loop is unrolled, so this condition is resolved at compile time: a load under a
     // run-time branch would make the join wait for every load in flight (rows past the last
     // visible one clamp to it)
-    if (it + 1 < TPW) cur.load(kcb, vcb, k0 + 256, nvis - 1, lane);
+    if (it + 1 < TPW) cur.load_k(kcb, k0 + 256, nvis - 1, lane);
 
     float p[16];
     float tm = kNegInf;
@@ -211,8 +295,9 @@ __global__ __launch_bounds__(256, FAST ? 2 : 1) void dec_cmp_kernel(DecodeArgs a
     m_run = m_new;
 #pragma unroll
     for (int n = 0; n < DT; ++n) O[n] *= alpha;
-    __asm__ volatile("" ::: "memory");  // Vt written by this wave before its reads
-    tile_pv<D>(Vt[wave], p, g4, r16, O);
+    if (k0 + 64 > nvis) cur.mask_tail(k0, nvis, lane);  // wave-uniform; no load inside
+    cur.pv(p, O);
+    if (it + 1 < TPW) cur.load_vt(vtb, k0 + 256, last0, lane);
 
     // block masses of this tile, relative to exp2(ms)
     const long tix = bkv * a.NT + tile;
@@ -263,12 +348,11 @@ __global__ __launch_bounds__(256, FAST ? 2 : 1) void dec_cmp_kernel(DecodeArgs a
 
   // merge the four waves: outputs rescaled to the chunk max, summed through LDS
   if (g4 == 0) { Wm[wave][r16] = m_run; Wl[wave][r16] = l_run; }
-  __syncthreads();  // every wave done with Vt; statistics posted
+  __syncthreads();  // statistics posted
   float M = kNegInf;
 #pragma unroll
   for (int w = 0; w < 4; ++w) M = fmaxf(M, Wm[w][r16]);
   const float sc = fast_exp2((Wm[wave][r16] - M) * sl);
-  float* Ob = reinterpret_cast<float*>(&Vt[0][0][0]);  // [4][16][OP] fp32
 #pragma unroll
   for (int n = 0; n < DT; ++n)
     *reinterpret_cast<f32x4*>(&Ob[(wave * 16 + r16) * OP + 16 * n + 4 * g4]) = sc * O[n];
@@ -476,7 +560,8 @@ __global__ __launch_bounds__(kSelThreads) void dec_select_kernel(DecodeArgs a) {
       if (lane == kfree) el = 0;
       if (lane > kfree && lane < a.top_n) el = flo + (lane - kfree - 1);
       int rank = 0;
-      for (int o = 0; o < a.top_n; ++o) rank += (__shfl(el, o) < el) ? 1 : 0;
+      for (int o = 0; o < a.top_n; ++o)  // the whole wave is active here
+        rank += (__builtin_amdgcn_readlane(el, o) < el) ? 1 : 0;
       if (lane < a.top_n) {
         orow[rank] = el;
         sidx[rank] = el;

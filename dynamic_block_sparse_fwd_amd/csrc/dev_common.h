@@ -60,34 +60,90 @@ __device__ __forceinline__ u16 f32_to_bf16(float f) {
   return *reinterpret_cast<u16*>(&h);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+// Cross-lane exchanges done in the VALU, without the LDS round trip of a bpermute shuffle.
+// DPP inside 16-lane rows: quad_perm [1,0,3,2] reads lane ^ 1, [2,3,0,1] lane ^ 2,
+// row_half_mirror lane 7 - i of its 8-lane half, row_mirror lane 15 - i of its row.  Once a
+// value is uniform over aligned groups of 4 (8), the half mirror (mirror) reads the partner
+// group exactly as lane ^ 4 (lane ^ 8) would.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+// Partner read for step o = 1, 2, 4, 8 of a butterfly over aligned lane groups.
+template <int O>
+__device__ __forceinline__ float xor_lane_f(float v) {
+  static_assert(O == 1 || O == 2 || O == 4 || O == 8, "DPP butterfly step");
+  return dpp_f<O == 1 ? kDppXor1 : O == 2 ? kDppXor2 : O == 4 ? kDppHalfMirror : kDppMirror>(v);
+}
+template <int O>
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v) {
+  return dpp_u32<O == 1 ? kDppXor1 : O == 2 ? kDppXor2 : O == 4 ? kDppHalfMirror : kDppMirror>(v);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+// gfx950 row swaps, both operands the same value: .x gets the even (lower) row or half of each
+// pair, .y the odd (upper) one, in every lane of the pair.  x + y and max(x, y) therefore equal
+// v + v[lane ^ 16] (swap16) or v + v[lane ^ 32] (swap32) exactly.
+struct U32Pair { uint32_t x, y; };
+__device__ __forceinline__ U32Pair swap16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return {r[0], r[1]};
+}
+__device__ __forceinline__ U32Pair swap32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return {r[0], r[1]};
 }
 
-// Max over the four lanes that hold one C-layout column (lanes L, L^16, L^32, L^48).
+// Max / sum over the four lanes that hold one C-layout column (lanes L, L^16, L^32, L^48).
 __device__ __forceinline__ float col_max4(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+  U32Pair p = swap16(__float_as_uint(v));
+  v = fmaxf(__uint_as_float(p.x), __uint_as_float(p.y));
+  p = swap32(__float_as_uint(v));
+  return fmaxf(__uint_as_float(p.x), __uint_as_float(p.y));
 }
 __device__ __forceinline__ float col_sum4(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  U32Pair p = swap16(__float_as_uint(v));
+  v = __uint_as_float(p.x) + __uint_as_float(p.y);
+  p = swap32(__float_as_uint(v));
+  return __uint_as_float(p.x) + __uint_as_float(p.y);
 }
 
-// Sum over aligned groups of GS consecutive lanes inside each 16-lane row (GS = 1..16).
+// Sum / max over aligned groups of GS consecutive lanes inside each 16-lane row (GS = 1, 2, 4,
+// 8 or 16).
 template <int GS>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < GS; o <<= 1) v += __shfl_xor(v, o);
+  static_assert(GS == 1 || GS == 2 || GS == 4 || GS == 8 || GS == 16, "group size");
+  if constexpr (GS > 1) v += xor_lane_f<1>(v);
+  if constexpr (GS > 2) v += xor_lane_f<2>(v);
+  if constexpr (GS > 4) v += xor_lane_f<4>(v);
+  if constexpr (GS > 8) v += xor_lane_f<8>(v);
   return v;
+}
+template <int GS>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(GS == 1 || GS == 2 || GS == 4 || GS == 8 || GS == 16, "group size");
+  if constexpr (GS > 1) v = fmaxf(v, xor_lane_f<1>(v));
+  if constexpr (GS > 2) v = fmaxf(v, xor_lane_f<2>(v));
+  if constexpr (GS > 4) v = fmaxf(v, xor_lane_f<4>(v));
+  if constexpr (GS > 8) v = fmaxf(v, xor_lane_f<8>(v));
+  return v;
+}
+
+// Unsigned max over the whole wave, returned in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, xor_lane_u32<1>(v));
+  v = max(v, xor_lane_u32<2>(v));
+  v = max(v, xor_lane_u32<4>(v));
+  v = max(v, xor_lane_u32<8>(v));
+  U32Pair p = swap16(v);
+  v = max(p.x, p.y);
+  p = swap32(v);
+  return max(p.x, p.y);
 }
 
 // Workgroup barrier that orders LDS only: unlike __syncthreads it does not wait for global
@@ -96,13 +152,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-template <int GS>
-__device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int o = 1; o < GS; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
 }
 
 // Key offset (inside a 32-key chunk) of C-row r of sub-tile s, per the ordering above.
@@ -129,15 +178,25 @@ __device__ __forceinline__ int rank_key_index(uint64_t key) {
   return (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
-  uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o);
-  uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
+// Max of 64-bit keys over the whole wave (high words first, then the low words of the lanes
+// that hold the top high word), returned in every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  const uint32_t hi = static_cast<uint32_t>(v >> 32);
+  const uint32_t top = wave_max_u32(hi);
+  const uint32_t lo = wave_max_u32(hi == top ? static_cast<uint32_t>(v) : 0u);
+  return (static_cast<uint64_t>(top) << 32) | lo;
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+// Max of v over lanes L, L^16, L^32, L^48 (one C-layout column), for 64-bit keys.
+__device__ __forceinline__ uint64_t col_max4_u64(uint64_t v) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = u64_max(v, shfl_xor_u64(v, o));
+  for (int step = 0; step < 2; ++step) {
+    const uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+    const U32Pair pl = step == 0 ? swap16(lo) : swap32(lo);
+    const U32Pair ph = step == 0 ? swap16(hi) : swap32(hi);
+    v = u64_max((static_cast<uint64_t>(ph.x) << 32) | pl.x,
+                (static_cast<uint64_t>(ph.y) << 32) | pl.y);
+  }
   return v;
 }
 

@@ -27,7 +27,7 @@ struct DecodeArgs {
   const uint16_t* kcache;  // [B, Hkv, L, D]
   const uint16_t* vcache;  // [B, Hkv, L, D]
   const uint16_t* kc;      // [B, Hkv, ncmp, D]
-  const uint16_t* vc;      // [B, Hkv, ncmp, D]
+  const uint16_t* vct;     // [B, Hkv, NT, D, 64] feature-major 64-token tiles
   const int32_t* seqlens;  // [B]
   const float* gate;       // [B, Hq, 3]
   float* out;              // [B, Hq, D]
@@ -97,9 +97,10 @@ void launch_transpose(const uint16_t* x, uint16_t* xt, int BH, int rows, int col
 
 // Compressed tokens of x [BH, T, D] with the transposed weight wt [D, l*D]:
 //   xc  (nullable) [BH, rows_alloc, D] row-major, rows n_cmp..rows_alloc-1 zero;
-//   xct (nullable) [BH, D, ncp] transposed, columns n_cmp..ncp-1 zero.
+//   xct (nullable) [BH, D, ncp] transposed, or with `tiled` [BH, ncp / 64, D, 64] (64-token
+//       tiles, each feature-major); columns n_cmp..ncp-1 zero.
 void launch_compress(const uint16_t* x, const uint16_t* wt, uint16_t* xc, uint16_t* xct, int BH,
-                     int T, int D, int l, int d, int ncmp, int rows_alloc, int ncp,
+                     int T, int D, int l, int d, int ncmp, int rows_alloc, int ncp, bool tiled,
                      hipStream_t s);
 
 // Compressed attention (lse pass + probability pass), block importance, group selection;

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x
                                                        const u16* __restrict__ wt,
                                                        u16* __restrict__ xc, u16* __restrict__ xct,
                                                        int T, int l, int d, int ncmp,
-                                                       int rows_alloc, int ncp) {
+                                                       int rows_alloc, int ncp, int tiled) {
   constexpr int CT = D / 64;  // 16-wide feature tiles per wave
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
@@ -168,23 +168,29 @@ __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x
         *reinterpret_cast<uint2*>(xc + (bh * rows_alloc + i) * D + c) = pk;
       }
       if (xct != nullptr && i < ncp) {
+        // feature-major [D, ncp], or in 64-token tiles [ncp / 64, D, 64]
+        const long o = tiled ? ((bh * (ncp >> 6) + (i >> 6)) * D + c) * 64 + (i & 63)
+                             : (bh * D + c) * (long)ncp + i;
+        const long es = tiled ? 64 : ncp;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) xct[(bh * D + c + e) * (long)ncp + i] = h[e];
+        for (int e = 0; e < 4; ++e) xct[o + e * es] = h[e];
       }
     }
   }
 }
 
 void launch_compress(const uint16_t* x, const uint16_t* wt, uint16_t* xc, uint16_t* xct, int BH,
-                     int T, int D, int l, int d, int ncmp, int rows_alloc, int ncp,
+                     int T, int D, int l, int d, int ncmp, int rows_alloc, int ncp, bool tiled,
                      hipStream_t s) {
   int rows = rows_alloc > ncp ? rows_alloc : ncp;
   if (rows <= 0) return;
   dim3 grid((rows + 63) / 64, BH);
   if (D == 128)
-    compress_kernel<128><<<grid, 256, 0, s>>>(x, wt, xc, xct, T, l, d, ncmp, rows_alloc, ncp);
+    compress_kernel<128><<<grid, 256, 0, s>>>(x, wt, xc, xct, T, l, d, ncmp, rows_alloc, ncp,
+                                              tiled ? 1 : 0);
   else
-    compress_kernel<64><<<grid, 256, 0, s>>>(x, wt, xc, xct, T, l, d, ncmp, rows_alloc, ncp);
+    compress_kernel<64><<<grid, 256, 0, s>>>(x, wt, xc, xct, T, l, d, ncmp, rows_alloc, ncp,
+                                             tiled ? 1 : 0);
 }
 
 }  // namespace nsa

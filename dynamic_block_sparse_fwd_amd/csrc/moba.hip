@@ -166,8 +166,7 @@ __global__ __launch_bounds__(256) void moba_gate_kernel(MobaArgs a) {
         if (s < K) {
           const uint64_t mine =
               lst[u].v[0] == kNegInf ? 0 : signed_rank_key(lst[u].v[0], lst[u].j[0]);
-          uint64_t m = u64_max(mine, shfl_xor_u64(mine, 16));
-          m = u64_max(m, shfl_xor_u64(m, 32));
+          const uint64_t m = col_max4_u64(mine);
           if (mine == m) lst[u].pop();
           chosen[u][s] = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFu));
         }

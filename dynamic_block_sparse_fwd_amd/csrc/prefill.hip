@@ -395,7 +395,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
     if (lane > kfree && lane < a.top_n) el = flo + (lane - kfree - 1);
     int rank = 0;
     for (int o = 0; o < a.top_n; ++o) {
-      const int other = __shfl(el, o);
+      const int other = __builtin_amdgcn_readlane(el, o);  // the whole wave is active here
       rank += (other < el) ? 1 : 0;
     }
     if (lane < a.top_n) orow[rank] = el;

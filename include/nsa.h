@@ -98,6 +98,9 @@ size_t moba_prefill_workspace_bytes(const moba_config* cfg);
 /* Number of compressed tokens for a length: (T - l) / d + 1, or 0 when T < l. */
 int32_t nsa_num_compressed(int32_t T, int32_t cmp_len, int32_t cmp_stride);
 
+/* Number of 64-token tiles of compressed tokens: ceil(nsa_num_compressed / 64). */
+int32_t nsa_num_compressed_tiles(int32_t T, int32_t cmp_len, int32_t cmp_stride);
+
 /*
  * Block compression (the compressed branch's learnable linear map; "Native Sparse Attention"
  * article, token compression), also the way to build the decode-time compressed cache.
@@ -109,6 +112,19 @@ int32_t nsa_num_compressed(int32_t T, int32_t cmp_len, int32_t cmp_stride);
  */
 int nsa_compress(const nsa_config* cfg, const void* x, const void* w, void* xc, void* ws,
                  size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The same block compression written in 64-token tiles, each tile feature-major: the layout
+ * nsa_decode takes for the compressed values (its probability-times-value product reads 64
+ * consecutive compressed tokens of one feature at a time, and a tile is one contiguous 16 KB
+ * (D = 128) read):
+ *   xt bf16 [B, Hkv, nt, D, 64], nt = nsa_num_compressed_tiles(T, l, d);
+ *      xt[.., i / 64, c, i % 64] is feature c of compressed token i; tokens n_cmp <= i < 64 * nt
+ *      are written as zero
+ * Values, rounding, workspace and errors as nsa_compress.
+ */
+int nsa_compress_tiles(const nsa_config* cfg, const void* x, const void* w, void* xt, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
 
 /*
  * NSA prefill (three branches + gate; podcast notes EP94 sections 5-6).
@@ -174,8 +190,11 @@ int nsa_prefill_timed(const nsa_config* cfg, const void* q, const void* k, const
  * selected and window KV).
  *   q              bf16 [B, Hq, D]
  *   kcache, vcache bf16 [B, Hkv, Lmax, D]    (Lmax = cfg->T)
- *   kcmp, vcmp     bf16 [B, Hkv, n_cmp(Lmax), D]  compressed caches (nsa_compress of the
- *                  caches); rows i with i*d + l <= seqlens[b] must be valid
+ *   kcmp           bf16 [B, Hkv, n_cmp(Lmax), D]  compressed keys (nsa_compress of kcache)
+ *   vcmp           bf16 [B, Hkv, nt(Lmax), D, 64]  compressed values in feature-major 64-token
+ *                  tiles (nsa_compress_tiles of vcache; nt = nsa_num_compressed_tiles)
+ *                  compressed token i must be valid in both when i*d + l <= seqlens[b]; the
+ *                  rest (and the pad tokens of the last tile) may hold anything, NaN included
  *   seqlens        int32 [B], 1 <= seqlens[b] <= Lmax (device memory)
  *   gate           fp32 [B, Hq, 3];  out fp32 [B, Hq, D]
  *   sel_idx        int32 [B, Hkv, top_n] or NULL

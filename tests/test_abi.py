@@ -84,6 +84,9 @@ def test_workspace_sizes_are_plausible(lib):
     assert 64 << 20 < ws < 1 << 30
     assert lib.nsa_num_compressed(65536, 32, 16) == 4095
     assert lib.nsa_num_compressed(31, 32, 16) == 0
+    assert lib.nsa_num_compressed_tiles(65536, 32, 16) == 64
+    assert lib.nsa_num_compressed_tiles(32 + 16 * 64, 32, 16) == 2  # 65 tokens
+    assert lib.nsa_num_compressed_tiles(31, 32, 16) == 0
     assert lib.nsa_compress_workspace_bytes(ctypes.byref(c.c())) >= 32 * 128 * 128 * 2
 
 
@@ -103,6 +106,10 @@ def test_entry_points_reject_before_any_launch(lib):
     assert lib.nsa_compress(ctypes.byref(c), None, fake, fake, fake, 1 << 20, None) == \
         nsa.NSA_ERR_INVALID_ARG
     assert lib.nsa_compress(ctypes.byref(c), fake, fake, fake, fake, 8, None) == nsa.NSA_ERR_WORKSPACE
+    assert lib.nsa_compress_tiles(ctypes.byref(c), fake, fake, None, fake, 1 << 20,
+                                  None) == nsa.NSA_ERR_INVALID_ARG
+    assert lib.nsa_compress_tiles(ctypes.byref(c), fake, fake, fake, fake, 8,
+                                  None) == nsa.NSA_ERR_WORKSPACE
     bad = nsa.NsaConfig(1, 2048, 1, 3, 64).c()
     assert lib.nsa_decode(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, fake, fake, None,
                           fake, 1 << 30, None) == nsa.NSA_ERR_UNSUPPORTED

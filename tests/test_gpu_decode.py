@@ -1,7 +1,10 @@
 """GPU parity of nsa_decode (through the C ABI) against the fp64 oracle.
 
 The compressed caches fed to both sides are the oracle's compression of the KV cache (the
-decode call takes them as inputs); nsa_compress itself is checked bit-exact elsewhere."""
+decode call takes them as inputs; the GPU gets the values in feature-major 64-token tiles, as
+nsa_decode wants); nsa_compress and nsa_compress_tiles are checked bit-exact elsewhere.  Every
+compressed token a sequence may not see, and the pad tokens of the last value tile, hold NaN on
+the GPU side: the kernels must never let them into a result."""
 import numpy as np
 import pytest
 
@@ -19,13 +22,34 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+BF16_NAN = np.uint16(0x7FC0)
+
+
+def poisoned_caches(cfg, kc, vc, seqlens):
+    """kc [B,Hkv,ncmp,D] and vc in feature-major 64-token tiles [B,Hkv,nt,D,64], with NaN in
+    every compressed token that the sequence's query may not see (i*d + l > seqlen) and in the
+    pad tokens of the last tile."""
+    B, Hkv, ncmp, D = kc.shape
+    nt = (ncmp + 63) // 64
+    kp = kc.copy()
+    vp = np.full((B, Hkv, nt * 64, D), BF16_NAN, dtype=np.uint16)
+    vp[:, :, :ncmp] = vc
+    for b, L in enumerate(seqlens):
+        nvis = (L - cfg.cmp_len) // cfg.cmp_stride + 1 if L >= cfg.cmp_len else 0
+        kp[b, :, nvis:] = BF16_NAN
+        vp[b, :, nvis:] = BF16_NAN
+    vt = np.ascontiguousarray(vp.reshape(B, Hkv, nt, 64, D).transpose(0, 1, 2, 4, 3))
+    return kp, vt
+
+
 def gpu_decode(cfg, x, kc, vc, seqlens):
     import dynamic_block_sparse_fwd_amd as nsa
     nsa.load_library()
     c = nsa.NsaConfig(cfg.B, cfg.T, cfg.Hkv, cfg.G, cfg.D, cfg.cmp_len, cfg.cmp_stride,
                       cfg.sel_block, cfg.top_n, cfg.n_local, cfg.window, cfg.scale)
+    kp, vt = poisoned_caches(cfg, kc, vc, seqlens)
     out, idx = nsa.nsa_decode(c, to_dev(x["q"]), to_dev(x["kcache"]), to_dev(x["vcache"]),
-                              to_dev(kc), to_dev(vc), to_dev(np.asarray(seqlens, np.int32)),
+                              to_dev(kp), to_dev(vt), to_dev(np.asarray(seqlens, np.int32)),
                               to_dev(x["gate"]))
     torch.cuda.synchronize()
     return out.cpu().numpy(), idx.cpu().numpy()
@@ -78,7 +102,7 @@ def test_decode_equals_prefill_last_row_on_gpu():
     d = {k: to_dev(v) for k, v in x.items()}
     pout, pidx = nsa.nsa_prefill(c, d["q"], d["k"], d["v"], d["wk"], d["wv"], d["gate"])
     kc = nsa.nsa_compress(c, d["k"], d["wk"])
-    vc = nsa.nsa_compress(c, d["v"], d["wv"])
+    vc = nsa.nsa_compress_tiles(c, d["v"], d["wv"])
     dout, didx = nsa.nsa_decode(c, d["q"][:, L - 1].contiguous(), d["k"], d["v"], kc, vc,
                                 torch.tensor([L], dtype=torch.int32, device="cuda"),
                                 d["gate"][:, L - 1].contiguous())

@@ -304,7 +304,7 @@ def nsa_prefill_stages(cfg: NsaConfig, stages: int, q, k, v, wk, wv, gate, out=N
     return out, sel_idx
 
 
-DECODE_STAGES = ("cmp_stream", "scores_select", "tiles", "combine")
+DECODE_STAGES = ("cmp_stream", "select_attend")
 
 
 def nsa_decode(cfg: NsaConfig, q, kcache, vcache, kcmp, vcmp, seqlens, gate, out=None,

@@ -57,7 +57,7 @@ int decode_max_tiles(const nsa_config* c) {
 }
 
 struct DecodeShape {
-  int ncmp, nblk, NCH, NT, NBT, NSPLIT;
+  int ncmp, nblk, NCH, NT, NBT;
 };
 
 DecodeShape decode_shape(const nsa_config* c) {
@@ -68,7 +68,6 @@ DecodeShape decode_shape(const nsa_config* c) {
   p.NCH = (p.ncmp + chunk - 1) / chunk;
   p.NT = (p.ncmp + 63) / 64;
   p.NBT = (63 * c->cmp_stride + c->cmp_len - 1) / c->sel_block + 2;
-  p.NSPLIT = (decode_max_tiles(c) + decode_tiles_per_split() - 1) / decode_tiles_per_split();
   return p;
 }
 
@@ -80,8 +79,8 @@ int check_nsa_decode(const nsa_config* c) {
   if (c->T > (1 << 24)) return NSA_ERR_UNSUPPORTED;
   if (decode_max_tiles(c) > decode_max_tile_list()) return NSA_ERR_UNSUPPORTED;
   const DecodeShape p = decode_shape(c);
-  if (p.NSPLIT > decode_max_splits()) return NSA_ERR_UNSUPPORTED;
-  if (decode_select_lds_bytes(p.NCH, p.nblk) > 160 * 1024) return NSA_ERR_UNSUPPORTED;
+  // 160 KB of LDS per workgroup, 4 KB of it static
+  if (decode_group_lds_bytes(c->D, p.NCH, p.NT, p.nblk) > 156 * 1024) return NSA_ERR_UNSUPPORTED;
   return NSA_OK;
 }
 
@@ -152,7 +151,7 @@ PrefillPlan plan_prefill(const nsa_config* c) {
 }
 
 struct DecodePlan {
-  size_t cm, cl, co, tref, cb, lse, idx, tl, tn, pm, pl, po, total;
+  size_t cm, cl, co, tref, cb, idx, total;
   DecodeShape sh;
 };
 
@@ -162,19 +161,14 @@ DecodePlan plan_decode(const nsa_config* c) {
   const DecodeShape& d = p.sh;
   const size_t BKV = (size_t)c->B * c->Hkv;
   const size_t F = sizeof(float);
+  const size_t nch = d.NCH > 0 ? d.NCH : 1, nt = d.NT > 0 ? d.NT : 1;  // never empty
   size_t off = 0;
-  p.cm = off;   off += align_up(BKV * d.NCH * 16 * F);
-  p.cl = off;   off += align_up(BKV * d.NCH * 16 * F);
-  p.co = off;   off += align_up(BKV * d.NCH * 16 * c->D * F);
-  p.tref = off; off += align_up(BKV * d.NT * 16 * F);
-  p.cb = off;   off += align_up(BKV * d.NT * d.NBT * 16 * F);
-  p.lse = off;  off += align_up(BKV * 16 * F);
+  p.cm = off;   off += align_up(BKV * nch * 16 * F);
+  p.cl = off;   off += align_up(BKV * nch * 16 * F);
+  p.co = off;   off += align_up(BKV * nch * 16 * c->D * F);
+  p.tref = off; off += align_up(BKV * nt * 16 * F);
+  p.cb = off;   off += align_up(BKV * nt * d.NBT * 16 * F);
   p.idx = off;  off += align_up(BKV * c->top_n * 4);
-  p.tl = off;   off += align_up(BKV * decode_max_tile_list() * 4);
-  p.tn = off;   off += align_up(BKV * 4);
-  p.pm = off;   off += align_up(BKV * d.NSPLIT * 2 * 16 * F);
-  p.pl = off;   off += align_up(BKV * d.NSPLIT * 2 * 16 * F);
-  p.po = off;   off += align_up(BKV * d.NSPLIT * 2 * 16 * c->D * F);
   p.total = off;
   return p;
 }
@@ -405,17 +399,10 @@ static int decode_impl(const nsa_config* c, const void* q, const void* kcache,
   a.co = reinterpret_cast<float*>(base + p.co);
   a.tref = reinterpret_cast<float*>(base + p.tref);
   a.cb = reinterpret_cast<float*>(base + p.cb);
-  a.lse = reinterpret_cast<float*>(base + p.lse);
-  a.tl = reinterpret_cast<int32_t*>(base + p.tl);
-  a.tn = reinterpret_cast<int32_t*>(base + p.tn);
-  a.pm = reinterpret_cast<float*>(base + p.pm);
-  a.pl = reinterpret_cast<float*>(base + p.pl);
-  a.po = reinterpret_cast<float*>(base + p.po);
   a.B = c->B; a.L = c->T; a.Hkv = c->Hkv; a.G = c->G; a.D = c->D;
   a.l = c->cmp_len; a.d = c->cmp_stride; a.beta = c->sel_block; a.top_n = c->top_n;
   a.n_local = c->n_local; a.window = c->window;
   a.ncmp = p.sh.ncmp; a.nblk = p.sh.nblk; a.NCH = p.sh.NCH; a.NT = p.sh.NT; a.NBT = p.sh.NBT;
-  a.NSPLIT = p.sh.NSPLIT;
   a.scale_log2 = c->scale * 1.4426950408889634f;
   (void)hipGetLastError();
   launch_decode(a, stream, ev);

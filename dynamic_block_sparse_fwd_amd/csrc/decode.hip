@@ -8,12 +8,10 @@
 //                      with register prefetch and an online softmax; per 1024-token chunk, per
 //                      head, (max, sum, unnormalised output); per tile, the probability mass of
 //                      every selection block it touches, relative to a per-tile reference
-//   dec_select_kernel  per (sequence, group): per-head log-sum-exp, every group block score,
-//                      the top-n (forced block 0 + local blocks) and the list of selected and
-//                      window tiles, each tile once
-//   dec_tiles_kernel   one wave per listed tile: the tile is read once and feeds whichever of
-//                      the selected and window branches use it
-//   dec_combine_kernel normalises the compressed output, merges all partials, applies the gate
+//   dec_group_kernel   one workgroup per (sequence, group): per-head log-sum-exp, every group
+//                      block score, the top-n (forced block 0 + local blocks), the list of
+//                      selected and window tiles (each tile read once, feeding whichever branch
+//                      uses it), the merge of all partials and the gate
 #include "attn_tile.h"
 #include "dev_common.h"
 #include "kernels.h"
@@ -23,7 +21,6 @@ namespace nsa {
 constexpr int TPW = 4;               // 64-token tiles per wave in dec_cmp
 constexpr int CHUNK = 4 * TPW * 64;  // compressed tokens per dec_cmp workgroup
 constexpr int kMaxTiles = 160;       // selected + window tiles per group
-constexpr int kMaxSplits = 64;       // splits of that list (8 tiles each)
 
 // One 64-key tile of a [rows, D] K/V cache pair in registers: K in MFMA A-operand order, V in
 // the gather order of the transposing LDS store.  Rows past `last` are clamped to it.
@@ -375,12 +372,15 @@ __global__ __launch_bounds__(256, FAST ? 2 : 1) void dec_cmp_kernel(DecodeArgs a
   }
 }
 
-// ------------------------------------------------------------------ phase 2: scores + selection
+// ------------------------------------------------------------------ phase 2: one workgroup per group
 
-// Top-k of S[first, last) by (score desc, index asc) for non-negative scores.  Every lane keeps
-// its four best candidates; the wave repeatedly takes the best head, and a lane that runs out
-// rescans below its last popped key.  Lane e < k receives the e-th winner.
-__device__ int wave_topk(const float* S, int first, int last, int k, int lane) {
+// Top-k by (key desc) of keyof(first) .. keyof(last - 1), 64-bit keys (score bits << 32 |
+// ~index, 0 = none).  Every lane keeps its four best candidates; the wave repeatedly takes the
+// best head, and a lane that runs out rescans below its last popped key (unless it never had
+// more than four).  Lane e < k receives
+// the e-th winner's key (0 when there are fewer than k candidates).
+template <class KeyOf>
+__device__ uint64_t wave_topk(KeyOf keyof, int first, int last, int k, int lane) {
   uint64_t c[4] = {0, 0, 0, 0};
   auto insert = [&](uint64_t key) {
     if (key <= c[3]) return;
@@ -389,16 +389,17 @@ __device__ int wave_topk(const float* S, int first, int last, int k, int lane) {
     else if (key > c[2]) { c[3] = c[2]; c[2] = key; }
     else c[3] = key;
   };
-  for (int j = first + lane; j < last; j += 64) insert(rank_key(S[j], j));
-  int mine = -1;
+  int n = 0;
+  for (int j = first + lane; j < last; j += 64, ++n) insert(keyof(j));
+  uint64_t mine = 0;
   for (int it = 0; it < k; ++it) {
     const uint64_t best = wave_max_u64(c[0]);
-    if (lane == it) mine = rank_key_index(best);
+    if (lane == it) mine = best;
     if (c[0] == best && best != 0) {
       c[0] = c[1]; c[1] = c[2]; c[2] = c[3]; c[3] = 0;
-      if (c[0] == 0) {  // cache exhausted: rescan strictly below the popped key
+      if (c[0] == 0 && n > 4) {  // cache exhausted: rescan strictly below the popped key
         for (int j = first + lane; j < last; j += 64) {
-          const uint64_t key = rank_key(S[j], j);
+          const uint64_t key = keyof(j);
           if (key < best) insert(key);
         }
       }
@@ -407,147 +408,267 @@ __device__ int wave_topk(const float* S, int first, int last, int k, int lane) {
   return mine;
 }
 
-// Masses and tile references of block j for heads 4*hq .. 4*hq + 3 over the (at most) first
-// two tiles it touches.  Every index is clamped so the loads are unconditional (no branch
-// around them); `ntile` is the number of tiles the block really touches (0 when none of its
-// compressed tokens is visible).
+// Masses of block j for heads 4*hq .. 4*hq + 3.  Every index is clamped so the loads are
+// unconditional (no branch around them).
+//  generic: the (at most) first two tiles the block touches, from tile ta; `ntile` is the
+//    number of tiles it really touches (0 when none of its compressed tokens is visible);
+//  FAST (sel_block = 4 * stride, cmp_len = 2 * stride): block j spans compressed tokens
+//    4j - 1 .. 4j + 3, all in tile T = j / 16 except for j = 16 T, whose half-weight first token
+//    is the previous tile's carry slot 16.  m0 = tile T's slot j - 16 T, m1 = tile T - 1's carry:
+//    the 16 blocks of one wave instruction share that address, so it costs one 64-byte request.
 struct BlockMass {
-  f32x4 m0, r0, m1, r1;
-  int ta, ntile;
+  f32x4 m0, m1;
+  int ta, tb, ntile;  // generic: first tile, -, tiles touched; FAST: tile of m0, tile of m1,
+                      // (m0 used) | 2 (m1 used)
 };
 
+template <bool FAST>
 __device__ __forceinline__ BlockMass fetch_block(const DecodeArgs& a, long bkv, int j, int nvis,
                                                  int hq) {
-  const int lo = block_tok_lo(j, a.beta, a.l, a.d);
-  int hi = block_tok_hi(j, a.beta, a.d);
-  hi = hi < nvis - 1 ? hi : nvis - 1;
-  const int ta = (lo < nvis - 1 ? lo : nvis - 1) / 64;
-  const int tb = hi / 64 > ta ? ta + 1 : ta;
-  auto entry = [&](int T) {
-    int jj = j - (T * 64 * a.d) / a.beta;
-    jj = jj < 0 ? 0 : (jj < a.NBT ? jj : a.NBT - 1);
-    return ((bkv * a.NT + T) * a.NBT + jj) * 16 + 4 * hq;
-  };
   BlockMass r;
-  r.m0 = *reinterpret_cast<const f32x4*>(a.cb + entry(ta));
-  r.r0 = *reinterpret_cast<const f32x4*>(a.tref + (bkv * a.NT + ta) * 16 + 4 * hq);
-  r.m1 = *reinterpret_cast<const f32x4*>(a.cb + entry(tb));
-  r.r1 = *reinterpret_cast<const f32x4*>(a.tref + (bkv * a.NT + tb) * 16 + 4 * hq);
-  r.ta = ta;
-  r.ntile = lo <= hi ? hi / 64 - lo / 64 + 1 : 0;
+  if constexpr (FAST) {
+    const int T = j >> 4;
+    const int tmax = a.NT > 0 ? a.NT - 1 : 0;
+    const int Tm = T < tmax ? T : tmax, Tc = T > 0 ? (T - 1 < tmax ? T - 1 : tmax) : 0;
+    const bool first = (j & 15) == 0;
+    const bool main_ok = (first ? 4 * j : 4 * j - 1) <= nvis - 1;
+    const bool carry_ok = first && j > 0 && 4 * j - 1 <= nvis - 1;
+    r.m0 = *reinterpret_cast<const f32x4*>(a.cb + ((bkv * a.NT + Tm) * a.NBT + (j - 16 * T)) * 16 +
+                                           4 * hq);
+    r.m1 = *reinterpret_cast<const f32x4*>(a.cb + ((bkv * a.NT + Tc) * a.NBT + 16) * 16 + 4 * hq);
+    r.ta = Tm;
+    r.tb = Tc;
+    r.ntile = (main_ok ? 1 : 0) | (carry_ok ? 2 : 0);
+  } else {
+    const int lo = block_tok_lo(j, a.beta, a.l, a.d);
+    int hi = block_tok_hi(j, a.beta, a.d);
+    hi = hi < nvis - 1 ? hi : nvis - 1;
+    const int ta = (lo < nvis - 1 ? lo : nvis - 1) / 64;
+    const int tb = hi / 64 > ta ? ta + 1 : ta;
+    auto entry = [&](int T) {
+      int jj = j - (T * 64 * a.d) / a.beta;
+      jj = jj < 0 ? 0 : (jj < a.NBT ? jj : a.NBT - 1);
+      return ((bkv * a.NT + T) * a.NBT + jj) * 16 + 4 * hq;
+    };
+    r.m0 = *reinterpret_cast<const f32x4*>(a.cb + entry(ta));
+    r.m1 = *reinterpret_cast<const f32x4*>(a.cb + entry(tb));
+    r.ta = ta;
+    r.tb = tb;
+    r.ntile = lo <= hi ? hi / 64 - lo / 64 + 1 : 0;
+  }
   return r;
 }
 
-// Group score share of one tile: masses times exp2(tref - lse), the per-head normalisation of
-// the compressed softmax.
-__device__ __forceinline__ float mass_score(const f32x4& m, const f32x4& r, const float* wl) {
-  return (m[0] * fast_exp2(r[0] - wl[0]) + m[1] * fast_exp2(r[1] - wl[1])) +
-         (m[2] * fast_exp2(r[2] - wl[2]) + m[3] * fast_exp2(r[3] - wl[3]));
+// Group score share of one tile: masses times w = exp2(tref - lse), the per-head normalisation
+// of the compressed softmax (w per tile and head, computed once).
+__device__ __forceinline__ float mass_score(const f32x4& m, const float* w) {
+  return (m[0] * w[0] + m[1] * w[1]) + (m[2] * w[2] + m[3] * w[3]);
 }
 
-constexpr int kSelThreads = 1024;
-constexpr int kSelLanes = kSelThreads / 4;  // blocks per pass (four lanes per block)
-constexpr int kSelUnroll = 4;              // passes whose loads are in flight together
+constexpr int kGrpWaves = 8;
+constexpr int kGrpThreads = 64 * kGrpWaves;
+constexpr int kGrpLanes = kGrpThreads / 4;  // blocks per pass (four lanes per block)
+constexpr int kGrpUnroll = 8;               // passes whose loads are in flight together
+constexpr int kCoRegs = 4;                  // compressed-output chunks prefetched in registers
 
-// One workgroup per (sequence, group): per-head log-sum-exp of the compressed softmax, every
-// group block score (four lanes per block, four heads each), the top-n with forced block 0 +
-// local blocks, and the group's tile list: tl[e] = tile | (1 << 30) for a tile of a selected
-// block, then the window tiles outside the selected blocks.
-__global__ __launch_bounds__(kSelThreads) void dec_select_kernel(DecodeArgs a) {
-  extern __shared__ float sh[];  // cm[NCH * 16] | cl[NCH * 16] | S[nblk]
-  __shared__ float lse[16];
+// Dynamic LDS of dec_group_kernel: one region reused by the three phases (selection state,
+// per-wave V^T tiles, per-wave partial outputs), then the compressed chunk weights.
+struct GroupLds {
+  size_t cm, cl, tr, S, keys, region, wc, total;
+};
+__host__ __device__ inline GroupLds group_lds(int D, int nch, int nt, int nblk) {
+  auto up = [](size_t x) { return (x + 15) & ~(size_t)15; };
+  GroupLds g{};
+  size_t o = 0;
+  g.cm = o;   o = up(o + (size_t)nch * 16 * 4);
+  g.cl = o;   o = up(o + (size_t)nch * 16 * 4);
+  g.tr = o;   o = up(o + (size_t)nt * 16 * 4);
+  g.S = o;    o = up(o + (size_t)nblk * 4);
+  g.keys = o; o = up(o + (size_t)kGrpWaves * 64 * 8);
+  const size_t tiles = (size_t)kGrpWaves * D * 64 * 2;
+  const size_t merge = (size_t)2 * kGrpWaves * 16 * (D + 4) * 4;
+  g.region = o > tiles ? o : tiles;
+  g.region = g.region > merge ? g.region : merge;
+  g.wc = g.region;
+  g.total = up(g.wc + (size_t)nch * 16 * 4);
+  return g;
+}
+
+// One workgroup per (sequence, group), after the compressed stream:
+//  1. the window's tiles (known before any selection) are requested at once, one per wave;
+//  2. per-head log-sum-exp of the compressed softmax, every group block score (the tile masses
+//     of the compressed stream rescaled by exp2(tref - lse), summed over the group's heads), the
+//     top-n with block 0 and the local blocks forced (each wave ranks an eighth of the blocks,
+//     one wave merges), the compressed output normalised and weighted;
+//  3. the tile list: window tiles first, then selected tiles outside the window, each tile once
+//     and marked with the branches it feeds; the waves take turns over it (the next tile's K in
+//     flight during this tile's softmax and P V, its V after them);
+//  4. the waves' partials merged per branch in LDS and the gate applied:
+//     out = g0 * o_cmp + g1 * o_slc + g2 * o_win.
+template <int D, bool FAST>
+__global__ __launch_bounds__(kGrpThreads, 1) void dec_group_kernel(DecodeArgs a) {
+  constexpr int DT = D / 16, OP = D + 4;
+  extern __shared__ __align__(16) unsigned char gsm[];
+  __shared__ float lse_s[16];
   __shared__ int sidx[64];
+  __shared__ int tl_s[kMaxTiles];
+  __shared__ int tn_s, next_s;
+  __shared__ float Wm[2][kGrpWaves][16], Wl[2][kGrpWaves][16];
+  __shared__ __align__(16) u16 Qs[16][D + 8];  // the group's queries (MFMA B operand rows)
+  const GroupLds L = group_lds(D, a.NCH, a.NT, a.nblk);
+  float* scm = reinterpret_cast<float*>(gsm + L.cm);
+  float* scl = reinterpret_cast<float*>(gsm + L.cl);
+  float* trs = reinterpret_cast<float*>(gsm + L.tr);
+  float* Ss = reinterpret_cast<float*>(gsm + L.S);
+  uint64_t* Kw = reinterpret_cast<uint64_t*>(gsm + L.keys);
+  u16(*Vt)[D][64] = reinterpret_cast<u16(*)[D][64]>(gsm);
+  float* Ob = reinterpret_cast<float*>(gsm);  // [2][waves][16][OP]
+  float* wc = reinterpret_cast<float*>(gsm + L.wc);
+
   const int kvh = blockIdx.x, b = blockIdx.y;
   const long bkv = (long)b * a.Hkv + kvh;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
+  const int g4 = lane >> 4, r16 = lane & 15;
   const int t = a.seqlens[b] - 1;
   const int nb = t / a.beta + 1;
   const int nvis = n_visible(t, a.l, a.d, a.ncmp);
   const int nch = (nvis + CHUNK - 1) / CHUNK;
-  const bool all = nb <= a.top_n;            // uniform: every block is selected
-  const bool scored = !all && nvis > 0;      // uniform
-  const int hq = threadIdx.x & 3, jq = threadIdx.x >> 2;
-  float* scm = sh;
-  float* scl = sh + a.NCH * 16;
-  float* Ss = sh + 2 * a.NCH * 16;
+  const int ntv = (nvis + 63) / 64;
+  const bool all = nb <= a.top_n;        // uniform: every block is selected
+  const bool scored = !all && nvis > 0;  // uniform
+  const float sl = a.scale_log2;
+  const int w0 = t - a.window + 1;
+  const int wt0 = (w0 > 0 ? w0 : 0) / 64, wt1 = t / 64, nwin = wt1 - wt0 + 1;
+  const u16* kcb = a.kcache + bkv * (long)a.L * D;
+  const u16* vcb = a.vcache + bkv * (long)a.L * D;
 
-  // Chunk statistics first, then the first pass of block masses: the wait for the former
-  // (vmcnt retires in order) leaves the latter in flight while the lse is formed.  The loads
-  // are unconditional, every index clamped into the workspace (which is never empty); values
-  // of a missing chunk or tile are never used.
-  const bool many = nch * 16 > kSelThreads;  // uniform: beyond 64 chunks, a plain loop
+  // the group's queries, one 16-byte octet per thread (16 heads x D / 8 octets <= 512 threads),
+  // stored to LDS with the first statistics: the waves re-read their fragments per tile
+  // instead of holding them in registers
+  const int qh = tid / (D / 8), qc = (tid % (D / 8)) * 8;
+  const bool qlive = tid < 16 * (D / 8) && qh < a.G;
+  const bf16x8 qv =
+      load8(a.q + ((long)b * a.Hkv * a.G + kvh * a.G + (qlive ? qh : 0)) * D + (qlive ? qc : 0));
+
+  // 2. selection.  Loads first (chunk statistics, tile references, compressed outputs of the
+  // first chunks, the first block masses), then the LDS stores that wait for them.
+  const int hq = tid & 3, jq = tid >> 2;
+  const bool many = nch * 16 > kGrpThreads;  // uniform: beyond 32 chunks, a loop below
+  const int ce = tid < nch * 16 ? tid : 0;
+  const float cmv = a.cm[bkv * a.NCH * 16 + ce], clv = a.cl[bkv * a.NCH * 16 + ce];
+  // tile references: one f32x4 per thread up to 128 tiles (clamped, stored below), a loop beyond
+  const bool tr_loop = ntv * 4 > kGrpThreads;  // uniform
+  const f32x4 trv = *reinterpret_cast<const f32x4*>(
+      a.tref + bkv * a.NT * 16 + 4 * (tid < ntv * 4 ? tid : 0));
+  // the loads above are waited for first: keep them ahead of the prefetches below (the counter
+  // of loads in flight retires in order, so waiting for a later load waits for every earlier one)
+  __asm__ volatile("" ::: "memory");
+  BlockMass bm[kGrpUnroll];
+#pragma unroll
+  for (int u = 0; u < kGrpUnroll; ++u) {
+    const int j = jq + kGrpLanes * u;
+    bm[u] = fetch_block<FAST>(a, bkv, j < nb ? j : nb - 1, nvis, hq);
+  }
+  __asm__ volatile("" ::: "memory");
+  if (!many && tid < nch * 16) {
+    scm[tid] = cmv;
+    scl[tid] = clv;
+  }
+  if (tid < 16 * (D / 8)) *reinterpret_cast<bf16x8*>(&Qs[qh][qc]) = qlive ? qv : zero8();
   if (many)
-    for (int e = threadIdx.x; e < nch * 16; e += kSelThreads) {
+    for (int e = tid; e < nch * 16; e += kGrpThreads) {
       scm[e] = a.cm[bkv * a.NCH * 16 + e];
       scl[e] = a.cl[bkv * a.NCH * 16 + e];
     }
-  const int ce = threadIdx.x < nch * 16 ? threadIdx.x : 0;
-  const float cmv = a.cm[bkv * a.NCH * 16 + ce], clv = a.cl[bkv * a.NCH * 16 + ce];
-  BlockMass bm[kSelUnroll];
-#pragma unroll
-  for (int u = 0; u < kSelUnroll; ++u) {
-    const int j = jq + kSelLanes * u;
-    bm[u] = fetch_block(a, bkv, j < nb ? j : nb - 1, nvis, hq);
-  }
-  if (!many && threadIdx.x < nch * 16) {
-    scm[threadIdx.x] = cmv;
-    scl[threadIdx.x] = clv;
+  if (tr_loop) {
+    for (int e = tid; e < ntv * 4; e += kGrpThreads)
+      *reinterpret_cast<f32x4*>(trs + 4 * e) =
+          *reinterpret_cast<const f32x4*>(a.tref + bkv * a.NT * 16 + 4 * e);
+  } else if (tid < ntv * 4) {
+    *reinterpret_cast<f32x4*>(trs + 4 * tid) = trv;
   }
   lds_barrier();
-  if (threadIdx.x < 256) {  // 16 lanes per head
-    const int h = threadIdx.x >> 4, sub = threadIdx.x & 15;
+  if (tid < 256) {  // 16 lanes per head
+    const int h = tid >> 4, sub = tid & 15;
     float M = kNegInf;
     for (int c = sub; c < nch; c += 16) M = fmaxf(M, scm[c * 16 + h]);
     M = group_max<16>(M);
-    float L = 0.f;
-    for (int c = sub; c < nch; c += 16) L += scl[c * 16 + h] * fast_exp2(scm[c * 16 + h] - M);
-    L = group_sum<16>(L);
-    if (sub == 0) {
-      // heads past G get +inf: their weights vanish
-      const float v = (M == kNegInf || h >= a.G) ? __builtin_inff() : M + __log2f(L);
-      lse[h] = v;
-      a.lse[bkv * 16 + h] = v;
-    }
+    float Ls = 0.f;
+    for (int c = sub; c < nch; c += 16) Ls += scl[c * 16 + h] * fast_exp2(scm[c * 16 + h] - M);
+    Ls = group_sum<16>(Ls);
+    // heads past G get +inf: their weights vanish
+    if (sub == 0) lse_s[h] = (M == kNegInf || h >= a.G) ? __builtin_inff() : M + __log2f(Ls);
   }
   lds_barrier();
+  // chunk weights exp2(cm - lse); tile weights exp2(tref - lse) in place of the references
+  for (int e = tid; e < nch * 16; e += kGrpThreads) wc[e] = fast_exp2(scm[e] - lse_s[e & 15]);
+  for (int e = tid; e < ntv * 16; e += kGrpThreads) trs[e] = fast_exp2(trs[e] - lse_s[e & 15]);
+  lds_barrier();
   if (scored) {
-    float wl[4];
+    for (int j0 = jq;; j0 += kGrpLanes * kGrpUnroll) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) wl[k] = lse[4 * hq + k];
-    for (int j0 = jq;; j0 += kSelLanes * kSelUnroll) {
-#pragma unroll
-      for (int u = 0; u < kSelUnroll; ++u) {
-        const int j = j0 + kSelLanes * u;
+      for (int u = 0; u < kGrpUnroll; ++u) {
+        const int j = j0 + kGrpLanes * u;
         float S = 0.f;
-        if (bm[u].ntile >= 1) S = mass_score(bm[u].m0, bm[u].r0, wl);
-        if (bm[u].ntile >= 2) S += mass_score(bm[u].m1, bm[u].r1, wl);
-        for (int T = bm[u].ta + 2; T < bm[u].ta + bm[u].ntile; ++T) {  // wide blocks only
-          const int jj = j - (T * 64 * a.d) / a.beta;
-          const f32x4 m = *reinterpret_cast<const f32x4*>(
-              a.cb + ((bkv * a.NT + T) * a.NBT + jj) * 16 + 4 * hq);
-          const f32x4 r =
-              *reinterpret_cast<const f32x4*>(a.tref + (bkv * a.NT + T) * 16 + 4 * hq);
-          S += mass_score(m, r, wl);
+        if constexpr (FAST) {
+          // main + carry equals the generic carry + main bit for bit (one commutative add)
+          if (bm[u].ntile & 1) S = mass_score(bm[u].m0, trs + bm[u].ta * 16 + 4 * hq);
+          if (bm[u].ntile & 2) S += mass_score(bm[u].m1, trs + bm[u].tb * 16 + 4 * hq);
+        } else {
+          if (bm[u].ntile >= 1) S = mass_score(bm[u].m0, trs + bm[u].ta * 16 + 4 * hq);
+          if (bm[u].ntile >= 2) S += mass_score(bm[u].m1, trs + (bm[u].ta + 1) * 16 + 4 * hq);
+          for (int T = bm[u].ta + 2; T < bm[u].ta + bm[u].ntile; ++T) {  // wide blocks only
+            const int jj = j - (T * 64 * a.d) / a.beta;
+            const f32x4 m = *reinterpret_cast<const f32x4*>(
+                a.cb + ((bkv * a.NT + T) * a.NBT + jj) * 16 + 4 * hq);
+            S += mass_score(m, trs + T * 16 + 4 * hq);
+          }
         }
         S = group_sum<4>(S);
         if (hq == 0 && j < nb) Ss[j] = S;
       }
-      const int jn = j0 + kSelLanes * kSelUnroll;
+      const int jn = j0 + kGrpLanes * kGrpUnroll;
       if (jn - jq >= nb) break;  // uniform
 #pragma unroll
-      for (int u = 0; u < kSelUnroll; ++u) {
-        const int j = jn + kSelLanes * u;
-        bm[u] = fetch_block(a, bkv, j < nb ? j : nb - 1, nvis, hq);
+      for (int u = 0; u < kGrpUnroll; ++u) {
+        const int j = jn + kGrpLanes * u;
+        bm[u] = fetch_block<FAST>(a, bkv, j < nb ? j : nb - 1, nvis, hq);
       }
     }
   } else if (!all) {
-    for (int j = threadIdx.x; j < nb; j += kSelThreads) Ss[j] = 0.f;
+    for (int j = tid; j < nb; j += kGrpThreads) Ss[j] = 0.f;
   }
-  __syncthreads();
-  const int lane = threadIdx.x & 63;
+  // compressed outputs of the first chunks for this thread's output pairs p = tid + 512 i
+  // (head p / D, feature p % D), in flight during the top-n.  (The window's K/V tiles are not
+  // requested here: with every group doing so at once, a wave stalls issuing them while memory
+  // is busy, and the whole workgroup waits for it at the next barrier.)
+  constexpr int PPT = 16 * D / kGrpThreads;
+  float cov[PPT][kCoRegs];
+#pragma unroll
+  for (int i = 0; i < PPT; ++i)
+#pragma unroll
+    for (int c = 0; c < kCoRegs; ++c) {
+      const int cc = c < a.NCH ? c : 0;
+      cov[i][c] = a.co[(bkv * a.NCH + cc) * 16 * D + tid + kGrpThreads * i];
+    }
+  lds_barrier();  // scores and chunk weights in LDS (the loads stay in flight)
   const int bcur = nb - 1;
   const int flo = bcur - a.n_local + 1;
   const int kfree = a.top_n - 1 - a.n_local;
-  if (threadIdx.x < 64) {
+  // top-n in two levels: waves 0-3 (one per SIMD) each rank a quarter of the free blocks
+  // 1 .. flo-1, then wave 0 ranks their 4 * kfree winners
+  constexpr int kRankWaves = 4;
+  if (!all && wave < kRankWaves) {  // uniform
+    const int span = (flo - 1 + kRankWaves - 1) / kRankWaves;
+    const int lo = 1 + wave * span;
+    const int hi = lo + span < flo ? lo + span : flo;
+    const uint64_t key =
+        wave_topk([&](int j) { return rank_key(Ss[j], j); }, lo, hi, kfree, lane);
+    if (lane < kfree) Kw[wave * kfree + lane] = key;
+  }
+  lds_barrier();
+  if (wave == 0) {
     int32_t* orow = a.idx + bkv * a.top_n;
     if (all) {
       if (lane < a.top_n) {
@@ -556,7 +677,9 @@ __global__ __launch_bounds__(kSelThreads) void dec_select_kernel(DecodeArgs a) {
         sidx[lane] = el;
       }
     } else {
-      int el = wave_topk(Ss, 1, flo, kfree, lane);
+      const uint64_t key =
+          wave_topk([&](int i) { return Kw[i]; }, 0, kRankWaves * kfree, kfree, lane);
+      int el = rank_key_index(key);
       if (lane == kfree) el = 0;
       if (lane > kfree && lane < a.top_n) el = flo + (lane - kfree - 1);
       int rank = 0;
@@ -567,232 +690,170 @@ __global__ __launch_bounds__(kSelThreads) void dec_select_kernel(DecodeArgs a) {
         sidx[rank] = el;
       }
     }
-  }
-  __syncthreads();
-  if (threadIdx.x < 64) {
+    __asm__ volatile("" ::: "memory");  // sidx written by this wave before its reads
+    // 3. tile list: the window tiles, flagged when their block is selected, then the tiles of
+    // selected blocks outside the window, at or before t
     const int per = a.beta / 64;
-    const int w0 = t - a.window + 1 > 0 ? t - a.window + 1 : 0;
-    const int wt0 = w0 / 64, wt1 = t / 64;
-    const int nsel = a.top_n * per, ncand = nsel + (wt1 - wt0 + 1);
-    int base = 0;
-    for (int i0 = 0; i0 < ncand; i0 += 64) {
+    for (int i = lane; i < nwin; i += 64) {
+      const int tile = wt0 + i, jw = tile / per;
+      bool in = false;
+      for (int e = 0; e < a.top_n; ++e) in |= sidx[e] == jw;
+      tl_s[i] = tile | (in ? 1 << 30 : 0);
+    }
+    const int nsel = a.top_n * per;
+    int base = nwin;
+    for (int i0 = 0; i0 < nsel; i0 += 64) {
       const int i = i0 + lane;
       int code = -1;
       if (i < nsel) {
         const int jb = sidx[i / per], tile = jb * per + i % per;
-        if (jb >= 0 && tile * 64 <= t) code = tile | (1 << 30);
-      } else if (i < ncand) {
-        const int tile = wt0 + (i - nsel), jw = tile / per;
-        bool in = false;
-        for (int e = 0; e < a.top_n; ++e) in |= sidx[e] == jw;
-        if (!in) code = tile;
+        if (jb >= 0 && tile * 64 <= t && (tile < wt0 || tile > wt1)) code = tile | (1 << 30);
       }
       const uint64_t m = __ballot(code >= 0);
       const int pos = base + (int)__popcll(m & ((1ull << lane) - 1ull));
-      if (code >= 0) a.tl[bkv * kMaxTiles + pos] = code;
+      if (code >= 0) tl_s[pos] = code;
       base += (int)__popcll(m);
     }
-    if (lane == 0) a.tn[bkv] = base;
+    if (lane == 0) {
+      tn_s = base;
+      next_s = kGrpWaves;  // entries 0..7 go to waves 0..7, the rest to whichever wave asks
+    }
   }
-}
-
-// ------------------------------------------------------------------ phase 3: selected + window
-
-// Two listed tiles per wave (the second in flight while the first computes), eight per
-// workgroup, merged into one partial per branch; the first four tiles of a split go to the four
-// waves, then the next four.
-constexpr int kTilesPerWave = 2;
-
-template <int D>
-__global__ __launch_bounds__(256, 2) void dec_tiles_kernel(DecodeArgs a) {
-  constexpr int DT = D / 16, OP = D + 4;
-  constexpr int VT_U16 = 4 * D * 64, OB_U16 = 4 * 2 * 16 * OP * 2;
-  __shared__ __align__(16) u16 smem[VT_U16 > OB_U16 ? VT_U16 : OB_U16];
-  __shared__ float Wm[2][4][16], Wl[2][4][16];
-  u16(*Vt)[D][64] = reinterpret_cast<u16(*)[D][64]>(smem);
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const long bkv = (long)b * a.Hkv + kvh;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tn = a.tn[bkv];
-  int code_raw[kTilesPerWave];
+  lds_barrier();  // tile list ready; the selection state in the shared region is dead
+  // compressed output of this thread's pairs: sum over chunks of co * exp2(cm - lse)
+  float ocmp[PPT];
 #pragma unroll
-  for (int u = 0; u < kTilesPerWave; ++u) {
-    const int my = split * 4 * kTilesPerWave + 4 * u + wave;
-    code_raw[u] = a.tl[bkv * kMaxTiles + (my < kMaxTiles ? my : 0)];
+  for (int i = 0; i < PPT; ++i) {
+    const int h = (tid + kGrpThreads * i) / D;
+    float o = 0.f;
+#pragma unroll
+    for (int c = 0; c < kCoRegs; ++c) o += c < nch ? cov[i][c] * wc[c * 16 + h] : 0.f;
+    for (int c = kCoRegs; c < nch; ++c)  // long contexts only
+      o += a.co[(bkv * a.NCH + c) * 16 * D + tid + kGrpThreads * i] * wc[c * 16 + h];
+    ocmp[i] = o;
   }
-  if (split * 4 * kTilesPerWave >= tn) return;  // uniform
-  const int g4 = lane >> 4, r16 = lane & 15;
-  const int t = a.seqlens[b] - 1;
-  const float sl = a.scale_log2;
-  const int w0 = t - a.window + 1;
-  const u16* kcb = a.kcache + bkv * (long)a.L * D;
-  const u16* vcb = a.vcache + bkv * (long)a.L * D;
 
-  bf16x8 qf[D / 32];
-  load_q_decode<D>(a, b, kvh, lane, qf);
+  // 3. the tiles: wave w starts on list entry w and takes the next unclaimed entry (an LDS
+  // counter) when it requests its next tile, so a wave held up by slow loads takes fewer
+  const int tn = __builtin_amdgcn_readfirstlane(tn_s);
   float mrun[2] = {kNegInf, kNegInf}, lrun[2] = {0.f, 0.f};
   f32x4 O[2][DT];
 #pragma unroll
   for (int br = 0; br < 2; ++br)
 #pragma unroll
     for (int n = 0; n < DT; ++n) O[br][n] = zero4();
-
-  auto tile_of = [&](int u, bool* have, bool* in_slc, bool* in_win) {
-    const int my = split * 4 * kTilesPerWave + 4 * u + wave;
-    *have = my < tn;
-    const int code = *have ? code_raw[u] : 0;
-    const int k0 = (code & 0x3FFFFFFF) * 64;
-    *in_slc = *have && ((code >> 30) & 1);
-    *in_win = *have && (k0 + 63 >= w0);
-    return k0;
-  };
-  DecTile<D> kv;
-  bool have0, slc0, win0;
-  int k0 = tile_of(0, &have0, &slc0, &win0);
-  kv.load(kcb, vcb, k0, t, lane);
+  if (wave < tn) {  // uniform per wave
+    int e = wave;
+    DecTile<D> kv;
+    kv.load(kcb, vcb, (tl_s[e] & 0x3FFFFFFF) * 64, t, lane);
+    for (;;) {
+      const int code = __builtin_amdgcn_readfirstlane(tl_s[e]);
+      const int k0 = (code & 0x3FFFFFFF) * 64;
+      const bool in_slc = (code >> 30) & 1, in_win = k0 + 63 >= w0;
+      // the next tile; after the last one every row of the "next" load is row t (one line)
+      int en = 0;
+      if (lane == 0) en = atomicAdd(&next_s, 1);
+      en = __builtin_amdgcn_readfirstlane(en);
+      const bool more = en < tn;
+      const int k1 =
+          more ? (__builtin_amdgcn_readfirstlane(tl_s[en]) & 0x3FFFFFFF) * 64 : t;
+      const int last1 = more ? t : k1;
+      f32x4 acc[4];
+      {
+        bf16x8 qf[D / 32];
 #pragma unroll
-  for (int u = 0; u < kTilesPerWave; ++u) {
-    bool have, in_slc, in_win;
-    k0 = tile_of(u, &have, &in_slc, &in_win);
-    f32x4 acc[4];
-    kv.scores(qf, acc);
-    __asm__ volatile("" ::: "memory");  // the previous tile's Vt reads stay before these writes
-    kv.stage(Vt[wave], lane);
-    __asm__ volatile("" ::: "memory");  // Vt[wave] is this wave's own: LDS keeps its order
-    bool h1, s1, w1;
-    const int k1 = u + 1 < kTilesPerWave ? tile_of(u + 1, &h1, &s1, &w1) : 0;
-    // the next tile's K is in flight during this tile's softmax and P V, its V after them
-    // (compile-time conditions: the loop is unrolled)
-    if (u + 1 < kTilesPerWave) kv.load_k(kcb, k1, t, lane);
-#pragma unroll
-    for (int br = 0; br < 2; ++br) {
-      float p[16];
-      float tm = kNegInf;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = k0 + lane_key(q4, i, g4);
-          const bool ok = br == 0 ? (in_slc && key <= t) : (in_win && key <= t && key >= w0);
-          const float r = ok ? acc[q4][i] : kNegInf;
-          p[q4 * 4 + i] = r;
-          tm = fmaxf(tm, r);
-        }
-      tm = col_max4(tm);
-      const float mn = fmaxf(mrun[br], tm);
-      const float ms = mn == kNegInf ? 0.f : mn * sl;
-      const float alpha = fast_exp2(fmaf(mrun[br], sl, -ms));
-      mrun[br] = mn;
-      float ls = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p[e] = fast_exp2(fmaf(p[e], sl, -ms));
-        ls += p[e];
+        for (int c = 0; c < D / 32; ++c) qf[c] = load8(&Qs[r16][32 * c + 8 * g4]);
+        kv.scores(qf, acc);
       }
-      lrun[br] = fmaf(lrun[br], alpha, col_sum4(ls));
+      __asm__ volatile("" ::: "memory");  // the previous tile's Vt reads stay before these writes
+      kv.stage(Vt[wave], lane);
+      __asm__ volatile("" ::: "memory");  // Vt[wave] is this wave's own: LDS keeps its order
+      kv.load_k(kcb, k1, last1, lane);
 #pragma unroll
-      for (int n = 0; n < DT; ++n) O[br][n] *= alpha;
-      tile_pv<D>(Vt[wave], p, g4, r16, O[br]);
+      for (int br = 0; br < 2; ++br) {
+        float p[16];
+        float tm = kNegInf;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = k0 + lane_key(q4, i, g4);
+            const bool ok = br == 0 ? (in_slc && key <= t) : (in_win && key <= t && key >= w0);
+            const float r = ok ? acc[q4][i] : kNegInf;
+            p[q4 * 4 + i] = r;
+            tm = fmaxf(tm, r);
+          }
+        tm = col_max4(tm);
+        const float mn = fmaxf(mrun[br], tm);
+        const float ms = mn == kNegInf ? 0.f : mn * sl;
+        const float alpha = fast_exp2(fmaf(mrun[br], sl, -ms));
+        mrun[br] = mn;
+        float ls = 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          p[q] = fast_exp2(fmaf(p[q], sl, -ms));
+          ls += p[q];
+        }
+        lrun[br] = fmaf(lrun[br], alpha, col_sum4(ls));
+#pragma unroll
+        for (int n = 0; n < DT; ++n) O[br][n] *= alpha;
+        tile_pv<D>(Vt[wave], p, g4, r16, O[br]);
+      }
+      kv.load_v(vcb, k1, last1, lane);
+      if (!more) break;
+      e = en;
     }
-    if (u + 1 < kTilesPerWave) kv.load_v(vcb, k1, t, lane);
   }
   if (g4 == 0) {
 #pragma unroll
     for (int br = 0; br < 2; ++br) { Wm[br][wave][r16] = mrun[br]; Wl[br][wave][r16] = lrun[br]; }
   }
   __syncthreads();  // Vt reads done; maxima posted
-  // merge the four waves per branch into this split's partial, summed through LDS
-  float* Ob = reinterpret_cast<float*>(smem);  // [4][2][16][OP] fp32
+  // 4. partials rescaled to the workgroup maximum of each branch, summed through LDS
 #pragma unroll
   for (int br = 0; br < 2; ++br) {
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, Wm[br][w][r16]);
+    for (int w = 0; w < kGrpWaves; ++w) M = fmaxf(M, Wm[br][w][r16]);
     const float f =
         Wm[br][wave][r16] == kNegInf ? 0.f : fast_exp2((Wm[br][wave][r16] - M) * sl);
 #pragma unroll
     for (int n = 0; n < DT; ++n)
-      *reinterpret_cast<f32x4*>(&Ob[((wave * 2 + br) * 16 + r16) * OP + 16 * n + 4 * g4]) =
+      *reinterpret_cast<f32x4*>(&Ob[((br * kGrpWaves + wave) * 16 + r16) * OP + 16 * n + 4 * g4]) =
           f * O[br][n];
   }
   __syncthreads();
-  const long sidx = bkv * a.NSPLIT + split;
-  for (int e = threadIdx.x; e < 2 * 16 * D; e += 256) {
-    const int br = e / (16 * D), rest = e % (16 * D);
-    const int o = (br * 16 + rest / D) * OP + rest % D;
-    a.po[sidx * 2 * 16 * D + e] =
-        (Ob[o] + Ob[2 * 16 * OP + o]) + (Ob[4 * 16 * OP + o] + Ob[6 * 16 * OP + o]);
-  }
-  if (threadIdx.x < 32) {
-    const int br = threadIdx.x >> 4, h = threadIdx.x & 15;
-    float M = kNegInf;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) M = fmaxf(M, Wm[br][v][h]);
-    float L = 0.f;
+  for (int i = 0; i < PPT; ++i) {
+    const int pr = tid + kGrpThreads * i;
+    const int h = pr / D, dd = pr % D;
+    if (h >= a.G) continue;
+    float ob[2];
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      if (Wm[br][v][h] != kNegInf) L += Wl[br][v][h] * fast_exp2((Wm[br][v][h] - M) * sl);
-    a.pm[(sidx * 2 + br) * 16 + h] = M == kNegInf ? kNegInf : M * sl;
-    a.pl[(sidx * 2 + br) * 16 + h] = L;
-  }
-}
-
-// ------------------------------------------------------------------ phase 4: merge + gate
-
-// 256 (head, feature) outputs of one (sequence, group) per workgroup: the compressed output
-// normalised by the lse, the selected and window partials merged, then the gate.
-__global__ __launch_bounds__(256) void dec_combine_kernel(DecodeArgs a) {
-  extern __shared__ float wc[];  // [nch][16] chunk weights exp2(cm - lse)
-  __shared__ float pm[2][kMaxSplits][16], pl[2][kMaxSplits][16];
-  const int kvh = blockIdx.y, b = blockIdx.z;
-  const long bkv = (long)b * a.Hkv + kvh;
-  const int t = a.seqlens[b] - 1;
-  const int nvis = n_visible(t, a.l, a.d, a.ncmp);
-  const int nch = (nvis + CHUNK - 1) / CHUNK;
-  const int nsp = (a.tn[bkv] + 4 * kTilesPerWave - 1) / (4 * kTilesPerWave);
-  for (int e = threadIdx.x; e < nsp * 32; e += 256) {
-    const int s = e >> 5, br = (e >> 4) & 1, h = e & 15;
-    pm[br][s][h] = a.pm[(bkv * a.NSPLIT + s) * 32 + (e & 31)];
-    pl[br][s][h] = a.pl[(bkv * a.NSPLIT + s) * 32 + (e & 31)];
-  }
-  for (int e = threadIdx.x; e < nch * 16; e += 256)
-    wc[e] = fast_exp2(a.cm[bkv * a.NCH * 16 + e] - a.lse[bkv * 16 + (e & 15)]);
-  __syncthreads();
-  const int pair = blockIdx.x * 256 + threadIdx.x;
-  const int h = pair / a.D, dd = pair % a.D;
-  if (h >= a.G) return;
-  float ocmp = 0.f;
-  const float* cop = a.co + bkv * a.NCH * 16 * a.D + pair;
-#pragma unroll 4
-  for (int c = 0; c < nch; ++c) ocmp += cop[(long)c * 16 * a.D] * wc[c * 16 + h];
-  float ob[2];
+    for (int br = 0; br < 2; ++br) {
+      float M = kNegInf;
 #pragma unroll
-  for (int br = 0; br < 2; ++br) {
-    float M = kNegInf;
-    for (int s = 0; s < nsp; ++s) M = fmaxf(M, pm[br][s][h]);
-    float L = 0.f, o = 0.f;
-#pragma unroll 4
-    for (int s = 0; s < nsp; ++s) {
-      const float m = pm[br][s][h];
-      const float f = m == kNegInf ? 0.f : fast_exp2(m - M);
-      L += pl[br][s][h] * f;
-      o += a.po[((bkv * a.NSPLIT + s) * 2 + br) * 16 * a.D + pair] * f;
+      for (int w = 0; w < kGrpWaves; ++w) M = fmaxf(M, Wm[br][w][h]);
+      float Lb = 0.f, o = 0.f;
+#pragma unroll
+      for (int w = 0; w < kGrpWaves; ++w) {
+        if (Wm[br][w][h] != kNegInf) Lb += Wl[br][w][h] * fast_exp2((Wm[br][w][h] - M) * sl);
+        o += Ob[((br * kGrpWaves + w) * 16 + h) * OP + dd];
+      }
+      ob[br] = Lb > 0.f ? o / Lb : 0.f;
     }
-    ob[br] = L > 0.f ? o / L : 0.f;
+    const long head = (long)b * a.Hkv * a.G + kvh * a.G + h;
+    const float* g = a.gate + head * 3;
+    a.out[head * D + dd] = g[0] * ocmp[i] + g[1] * ob[0] + g[2] * ob[1];
   }
-  const int head = kvh * a.G + h;
-  const float* g = a.gate + ((long)b * a.Hkv * a.G + head) * 3;
-  a.out[((long)b * a.Hkv * a.G + head) * a.D + dd] = g[0] * ocmp + g[1] * ob[0] + g[2] * ob[1];
 }
 
 // ------------------------------------------------------------------ launcher
 
 int decode_chunk_tokens() { return CHUNK; }
-int decode_max_splits() { return kMaxSplits; }
-int decode_tiles_per_split() { return 4 * kTilesPerWave; }
 int decode_max_tile_list() { return kMaxTiles; }
-size_t decode_select_lds_bytes(int nch, int nblk) {
-  return (size_t)(2 * nch * 16 + nblk) * sizeof(float);
+size_t decode_group_lds_bytes(int D, int nch, int nt, int nblk) {
+  return group_lds(D, nch, nt, nblk).total;
 }
 
 void launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
@@ -800,10 +861,14 @@ void launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
     if (ev != nullptr) (void)hipEventRecord(ev[i], s);
   };
   const bool fast = a.beta == 4 * a.d && a.l == 2 * a.d && a.NBT >= 17;
-  const size_t sel_lds = decode_select_lds_bytes(a.NCH, a.nblk);
-  if (sel_lds > 64 * 1024)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(dec_select_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sel_lds);
+  const size_t lds = decode_group_lds_bytes(a.D, a.NCH, a.NT, a.nblk);
+  const void* gk =
+      a.D == 128 ? (fast ? reinterpret_cast<const void*>(dec_group_kernel<128, true>)
+                         : reinterpret_cast<const void*>(dec_group_kernel<128, false>))
+                 : (fast ? reinterpret_cast<const void*>(dec_group_kernel<64, true>)
+                         : reinterpret_cast<const void*>(dec_group_kernel<64, false>));
+  if (lds > 64 * 1024)
+    (void)hipFuncSetAttribute(gk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   mark(0);
   if (a.NCH > 0) {
     const dim3 g1(a.NCH, a.Hkv, a.B);
@@ -816,15 +881,15 @@ void launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
     }
   }
   mark(1);
-  dec_select_kernel<<<dim3(a.Hkv, a.B), kSelThreads, sel_lds, s>>>(a);
+  const dim3 g2(a.Hkv, a.B);
+  if (a.D == 128) {
+    if (fast) dec_group_kernel<128, true><<<g2, kGrpThreads, lds, s>>>(a);
+    else dec_group_kernel<128, false><<<g2, kGrpThreads, lds, s>>>(a);
+  } else {
+    if (fast) dec_group_kernel<64, true><<<g2, kGrpThreads, lds, s>>>(a);
+    else dec_group_kernel<64, false><<<g2, kGrpThreads, lds, s>>>(a);
+  }
   mark(2);
-  const dim3 g3(a.NSPLIT, a.Hkv, a.B);
-  if (a.D == 128) dec_tiles_kernel<128><<<g3, 256, 0, s>>>(a);
-  else dec_tiles_kernel<64><<<g3, 256, 0, s>>>(a);
-  mark(3);
-  dec_combine_kernel<<<dim3((16 * a.D + 255) / 256, a.Hkv, a.B), 256,
-                       (size_t)a.NCH * 16 * sizeof(float), s>>>(a);
-  mark(4);
 }
 
 }  // namespace nsa

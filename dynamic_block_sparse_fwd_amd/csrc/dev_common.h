@@ -178,12 +178,19 @@ __device__ __forceinline__ int rank_key_index(uint64_t key) {
   return (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
 }
 
-// Max of 64-bit keys over the whole wave (high words first, then the low words of the lanes
-// that hold the top high word), returned in every lane.
+// Max of 64-bit keys over the whole (fully active) wave: high words first; the low word is read
+// from the one lane holding the top high word, or reduced over the lanes that tie on it.
+// Returned in every lane.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   const uint32_t hi = static_cast<uint32_t>(v >> 32);
   const uint32_t top = wave_max_u32(hi);
-  const uint32_t lo = wave_max_u32(hi == top ? static_cast<uint32_t>(v) : 0u);
+  const uint64_t eq = __ballot(hi == top);
+  uint32_t lo;
+  if (__popcll(eq) == 1)  // uniform
+    lo = (uint32_t)__builtin_amdgcn_readlane((int)static_cast<uint32_t>(v),
+                                             (int)__builtin_ctzll(eq));
+  else
+    lo = wave_max_u32(hi == top ? static_cast<uint32_t>(v) : 0u);
   return (static_cast<uint64_t>(top) << 32) | lo;
 }
 

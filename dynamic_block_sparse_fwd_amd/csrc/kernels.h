@@ -32,33 +32,25 @@ struct DecodeArgs {
   const float* gate;       // [B, Hq, 3]
   float* out;              // [B, Hq, D]
   int32_t* idx;            // [B, Hkv, top_n]
-  // workspace; 16 row slots (heads of a group) everywhere
+  // workspace; 16 row slots (heads of a group) everywhere; every array holds at least one
+  // chunk / tile per group, so clamped indices stay inside it when nothing is visible
   float* cm;    // [B*Hkv, NCH, 16] chunk max (scaled log2 units)
   float* cl;    // [B*Hkv, NCH, 16] sum of exp2(z - max)
   float* co;    // [B*Hkv, NCH, 16, D] unnormalised output
   float* tref;  // [B*Hkv, NT, 16] per 64-token tile: reference of its block masses (log2)
   float* cb;    // [B*Hkv, NT, NBT, 16] block masses of each tile, relative to exp2(tref)
-  float* lse;   // [B*Hkv, 16]
-  int32_t* tl;  // [B*Hkv, 160] selected / window tile list
-  int32_t* tn;  // [B*Hkv] its length
-  // per split of the tile list (decode_tiles_per_split() tiles): [.., NSPLIT, 2 (slc, win),
-  // 16 (, D)]
-  float* pm;
-  float* pl;
-  float* po;
   int B, L, Hkv, G, D;
   int l, d, beta, top_n, n_local, window;
-  int ncmp, nblk, NCH, NT, NBT, NSPLIT;
+  int ncmp, nblk, NCH, NT, NBT;
   float scale_log2;
 };
 
 // ev: nullptr or NSA_DECODE_NSTAGES + 1 events recorded around the stages.
 void launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev);
 int decode_chunk_tokens();
-int decode_max_splits();
-int decode_tiles_per_split();
 int decode_max_tile_list();
-size_t decode_select_lds_bytes(int nch, int nblk);
+// dynamic LDS of the per-group kernel (selection state, per-wave tiles, partials)
+size_t decode_group_lds_bytes(int D, int nch, int nt, int nblk);
 
 constexpr int kMobaChunks = 8;  // T-chunks per head counted by separate workgroups
 

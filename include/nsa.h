@@ -199,7 +199,8 @@ int nsa_prefill_timed(const nsa_config* cfg, const void* q, const void* k, const
  *   gate           fp32 [B, Hq, 3];  out fp32 [B, Hq, D]
  *   sel_idx        int32 [B, Hkv, top_n] or NULL
  * Returns NSA_ERR_UNSUPPORTED when top_n * sel_block / 64 + ceil(window / 64) + 1 > 160
- * (tile table), Lmax > 2^24, or the block scores of a group outgrow 160 KB of LDS.
+ * (tile table), Lmax > 2^24, or the per-group selection state (chunk statistics, tile
+ * references, block scores) outgrows the 160 KB of LDS of one workgroup.
  */
 int nsa_decode(const nsa_config* cfg, const void* q, const void* kcache, const void* vcache,
                const void* kcmp, const void* vcmp, const int32_t* seqlens, const float* gate,
@@ -207,10 +208,10 @@ int nsa_decode(const nsa_config* cfg, const void* q, const void* kcache, const v
 
 /*
  * Instrumented nsa_decode: identical work, plus events[s] recorded before stage s and
- * events[NSA_DECODE_NSTAGES] after the last.  Stages: 0 compressed-cache stream, 1 block
- * scores and selection, 2 selected + window tiles, 3 merge and gate.  For measurement only.
+ * events[NSA_DECODE_NSTAGES] after the last.  Stages: 0 compressed-cache stream, 1 per group:
+ * block scores, selection, selected + window tiles, merge and gate.  For measurement only.
  */
-#define NSA_DECODE_NSTAGES 4
+#define NSA_DECODE_NSTAGES 2
 int nsa_decode_timed(const nsa_config* cfg, const void* q, const void* kcache,
                      const void* vcache, const void* kcmp, const void* vcmp,
                      const int32_t* seqlens, const float* gate, float* out, int32_t* sel_idx,

@@ -79,6 +79,9 @@ DECODE_CASES = [
     ("G4_D64", 3, 3000, 3, 4, 64, [3000, 2999, 1025], {}),
     ("G1_D64_block128", 2, 2500, 2, 1, 64, [2500, 1300], dict(sel_block=128, top_n=6, window=200)),
     ("G2_D128_top5", 2, 4100, 1, 2, 128, [4100, 4096], dict(top_n=5, n_local=1, window=64)),
+    # 128 compressed tokens fill two tiles exactly; the last block's only visible token is the
+    # carry out of the last tile
+    ("G4_D128_tile_edge", 2, 2064, 1, 4, 128, [2064, 2063], {}),
 ]
 
 

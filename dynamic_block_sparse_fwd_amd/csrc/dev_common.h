@@ -207,4 +207,38 @@ __device__ __forceinline__ uint64_t col_max4_u64(uint64_t v) {
   return v;
 }
 
+// Top-k by (key desc) of keyof(first) .. keyof(last - 1), 64-bit keys (score bits << 32 |
+// ~index, 0 = none).  Every lane keeps its four best candidates; the wave repeatedly takes the
+// best head, and a lane that runs out rescans below its last popped key (unless it never had
+// more than four).  Lane e < k receives
+// the e-th winner's key (0 when there are fewer than k candidates).
+template <class KeyOf>
+__device__ uint64_t wave_topk(KeyOf keyof, int first, int last, int k, int lane) {
+  uint64_t c[4] = {0, 0, 0, 0};
+  auto insert = [&](uint64_t key) {
+    if (key <= c[3]) return;
+    if (key > c[0]) { c[3] = c[2]; c[2] = c[1]; c[1] = c[0]; c[0] = key; }
+    else if (key > c[1]) { c[3] = c[2]; c[2] = c[1]; c[1] = key; }
+    else if (key > c[2]) { c[3] = c[2]; c[2] = key; }
+    else c[3] = key;
+  };
+  int n = 0;
+  for (int j = first + lane; j < last; j += 64, ++n) insert(keyof(j));
+  uint64_t mine = 0;
+  for (int it = 0; it < k; ++it) {
+    const uint64_t best = wave_max_u64(c[0]);
+    if (lane == it) mine = best;
+    if (c[0] == best && best != 0) {
+      c[0] = c[1]; c[1] = c[2]; c[2] = c[3]; c[3] = 0;
+      if (c[0] == 0 && n > 4) {  // cache exhausted: rescan strictly below the popped key
+        for (int j = first + lane; j < last; j += 64) {
+          const uint64_t key = keyof(j);
+          if (key < best) insert(key);
+        }
+      }
+    }
+  }
+  return mine;
+}
+
 }  // namespace nsa

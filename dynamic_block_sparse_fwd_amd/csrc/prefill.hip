@@ -375,22 +375,12 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
     const int flo = bcur - a.n_local + 1;  // forced local blocks flo..bcur (flo >= 2 here)
     const int nforced = 1 + a.n_local;
     const int kfree = a.top_n - nforced;
-    float* srow = Sb + tq * nblk;
-    uint32_t removed = 0;  // bit m: candidate j = 1 + lane + 64 m already chosen
-    int mine = -1;         // lane e < kfree keeps the e-th winner
-    for (int it = 0; it < kfree; ++it) {
-      uint64_t best = 0;
-      for (int m = 0, j = 1 + lane; j < flo; ++m, j += 64) {
-        if (removed & (1u << m)) continue;
-        best = u64_max(best, rank_key(srow[j], j));
-      }
-      best = wave_max_u64(best);
-      const int jw = rank_key_index(best);
-      if (((jw - 1) & 63) == lane) removed |= 1u << ((jw - 1) >> 6);
-      if (lane == it) mine = jw;
-    }
+    const float* srow = Sb + tq * nblk;
+    // lane e < kfree receives the e-th winner among the free blocks 1 .. flo-1
+    const uint64_t key =
+        wave_topk([&](int j) { return rank_key(srow[j], j); }, 1, flo, kfree, lane);
     // the set: lanes 0..kfree-1 hold winners; next lanes hold block 0 and flo..bcur
-    int el = mine;
+    int el = rank_key_index(key);
     if (lane == kfree) el = 0;
     if (lane > kfree && lane < a.top_n) el = flo + (lane - kfree - 1);
     int rank = 0;

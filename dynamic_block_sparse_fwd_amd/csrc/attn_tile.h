@@ -159,12 +159,13 @@ __device__ __forceinline__ void pv_tiles(const u16 (*Vs)[64], const bf16x8 (*pb)
 }
 
 // Sum over the 16 lanes of a DPP row (row rotations 8, 4, 2, 1); every lane ends with a sum,
-// lane 0 of the row with a fixed association.
+// lane 0 of the row with a fixed association.  A rotation never leaves the row, so bound_ctrl
+// is moot and set, which lets the compiler fold each move into the add (v_add_f32_dpp).
 __device__ __forceinline__ float row16_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xF, 0xF, true));
   return v;
 }
 

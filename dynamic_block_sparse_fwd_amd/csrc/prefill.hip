@@ -239,6 +239,10 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
     }
   }
 
+  bool ps_zero = false;
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) ps_zero |= ps[rt] == 0.f;
+  ps_zero = __ballot(ps_zero) != 0;  // wave-uniform
   // Pass 2: normalised probabilities -> o_cmp and group block scores.
   const float inv_l = 1.0f / (float)a.l;
   if (nkt > 0) {
@@ -274,8 +278,13 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
             pv[e] = key < nvis[rt] ? pv[e] : 0.f;
           }
         }
+        if (ps_zero) {  // uniform: a row of this wave drops p' from P V (rare)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pbt[rt][kc2][e] = (__bf16)(pv[e] * ps[rt]);
+          for (int e = 0; e < 8; ++e) pbt[rt][kc2][e] = (__bf16)(pv[e] * ps[rt]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pbt[rt][kc2][e] = (__bf16)pv[e];
+        }
         if constexpr (FAST) {
           const float cA = head_sum<G>(((pv[0] + pv[1]) + pv[2] + 0.5f * pv[3]) * rinv[rt]);
           const float cB = head_sum<G>(((pv[4] + pv[5]) + pv[6] + 0.5f * pv[7]) * rinv[rt]);

@@ -94,6 +94,7 @@ int check_moba(const moba_config* c) {
   if (c->top_k > 8) return NSA_ERR_UNSUPPORTED;
   if (c->T / c->block > 16384) return NSA_ERR_UNSUPPORTED;  // per-head block counts in LDS
   if ((long)c->T > (1L << 27)) return NSA_ERR_UNSUPPORTED;
+  if ((long)c->B * c->H * (c->T / 64) > (1L << 31) - 8) return NSA_ERR_UNSUPPORTED;  // 1-D grid
   return NSA_OK;
 }
 

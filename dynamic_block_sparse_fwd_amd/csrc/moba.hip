@@ -319,8 +319,13 @@ __global__ __launch_bounds__(256) void moba_block_kernel(MobaArgs a) {
   constexpr int RTW = 2, DT = D / 16;
   __shared__ u16 Ks[64][D];
   __shared__ u16 Vs[D][64];
-  const int tile = blockIdx.x;
-  if (tile >= a.ntiles[0]) return;
+  // XCD-contiguous order: workgroup i runs on XCD i % 8, so logical tiles are dealt out in eight
+  // contiguous runs, one per XCD; the tiles of one (head, block) then share that XCD's L2 for
+  // the block's K/V
+  const int ntiles = a.ntiles[0];
+  const int per = (ntiles + 7) / 8;
+  const int tile = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if ((int)(blockIdx.x / 8) >= per || tile >= ntiles) return;
   const int e = a.tile_entry[tile];
   const long bh = e / a.nb;
   const int j = e % a.nb;
@@ -422,7 +427,13 @@ __global__ __launch_bounds__(256) void moba_own_kernel(MobaArgs a) {
   constexpr int RTW = 1, DT = D / 16;
   __shared__ u16 Ks[64][D];
   __shared__ u16 Vs[D][64];
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // XCD-contiguous order (workgroup i runs on XCD i % 8): the 64-query tiles of one own block
+  // run on one XCD and share its L2 for the block's K/V
+  const int ntq = a.T / 64, n = ntq * a.H * a.B;
+  const int per = (n + 7) / 8;
+  const int lin = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if ((int)(blockIdx.x / 8) >= per || lin >= n) return;
+  const int tile = lin % ntq, h = (lin / ntq) % a.H, b = lin / (ntq * a.H);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
   const int t0 = tile * 64;
@@ -561,7 +572,7 @@ static void launch_moba_k(const MobaArgs& a, hipStream_t s, hipEvent_t* ev) {
     if (ev != nullptr) (void)hipEventRecord(ev[i], s);
   };
   const long rows = (long)a.B * a.T * a.H;
-  const dim3 gp(a.nb, a.B * a.H), gq(a.T / 64, a.H, a.B), gg((a.T / 64 + 3) / 4, a.H, a.B);
+  const dim3 gp(a.nb, a.B * a.H), gg((a.T / 64 + 3) / 4, a.H, a.B);
   moba_pool_kernel<D><<<gp, 256, 0, s>>>(a);
   moba_gate_kernel<D, KS><<<gg, 256, 0, s>>>(a);
   mark(1);
@@ -570,9 +581,9 @@ static void launch_moba_k(const MobaArgs& a, hipStream_t s, hipEvent_t* ev) {
   moba_scan_kernel<<<1, 1024, 0, s>>>(a);
   moba_fill_kernel<<<(int)((rows + 255) / 256), 256, 0, s>>>(a);
   mark(2);
-  if (a.max_tiles > 0) moba_block_kernel<D><<<a.max_tiles, 256, 0, s>>>(a);
+  if (a.max_tiles > 0) moba_block_kernel<D><<<(a.max_tiles + 7) / 8 * 8, 256, 0, s>>>(a);
   mark(3);
-  moba_own_kernel<D, KS><<<gq, 256, 0, s>>>(a);
+  moba_own_kernel<D, KS><<<(int)((rows / 64 + 7) / 8 * 8), 256, 0, s>>>(a);
   mark(4);
 }
 

@@ -22,6 +22,10 @@
 
 namespace nsa {
 
+// Lazy softmax rescaling: headroom of the reference max, in log2 units (probabilities fed to the
+// matrix core stay below 2^8; bf16 keeps its relative precision there).
+constexpr float kLazyLog2 = 8.f;
+
 constexpr int MOBA_ROWS = 128;  // gathered queries per block-major tile
 
 // kbar of one block: 16-byte loads, each thread sums 8 features over a stride of rows; the
@@ -385,10 +389,19 @@ __global__ __launch_bounds__(256) void moba_block_kernel(MobaArgs a) {
 #pragma unroll
       for (int q = 1; q < 16; ++q) tm = fmaxf(tm, z[rt][q]);
       tm = col_max4(tm);
-      const float mn = fmaxf(mrun[rt], tm);
-      const float msl = mn * a.scale_log2;
-      const float alpha = fast_exp2(fmaf(mrun[rt], a.scale_log2, -msl));
-      mrun[rt] = mn;
+      // The reference max moves only when a score exceeds it by more than kLazyLog2 (log2
+      // units): probabilities then stay below 2^kLazyLog2, and the rescale of O (a multiply
+      // per accumulator) is skipped by the whole wave in the usual case.
+      const bool move = tm * a.scale_log2 > mrun[rt] * a.scale_log2 + kLazyLog2;
+      if (__ballot(move) != 0) {  // uniform
+        const float mn = move ? tm : mrun[rt];
+        const float alpha = move ? fast_exp2((mrun[rt] - mn) * a.scale_log2) : 1.f;
+        mrun[rt] = mn;
+        lrun[rt] *= alpha;
+#pragma unroll
+        for (int nn = 0; nn < DT; ++nn) O[rt][nn] *= alpha;
+      }
+      const float msl = mrun[rt] * a.scale_log2;
       float sum = 0.f;
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
@@ -396,9 +409,7 @@ __global__ __launch_bounds__(256) void moba_block_kernel(MobaArgs a) {
         sum += p;
         pb[rt][q >> 3][q & 7] = (__bf16)p;
       }
-      lrun[rt] = lrun[rt] * alpha + sum;
-#pragma unroll
-      for (int nn = 0; nn < DT; ++nn) O[rt][nn] *= alpha;
+      lrun[rt] += sum;
     }
     pv_tiles<D, RTW>(Vs, pb, g4, r16, O);
   }
@@ -497,16 +508,21 @@ __global__ __launch_bounds__(256) void moba_own_kernel(MobaArgs a) {
       float tm = z[0];
 #pragma unroll
       for (int q = 1; q < 16; ++q) tm = fmaxf(tm, z[q]);
-      tm = col_max4(tm);
-      const float mn = fmaxf(mrun[rt], tm);  // finite: every row sees its block's first key
-      const float alpha = fast_exp2(mrun[rt] - mn);
-      mrun[rt] = mn;
+      tm = col_max4(tm);  // finite: every row sees a key of every tile it reaches
+      const bool move = tm > mrun[rt] + kLazyLog2;  // lazy rescale, as in the block kernel
+      if (__ballot(move) != 0) {  // uniform
+        const float mn = move ? tm : mrun[rt];
+        const float alpha = move ? fast_exp2(mrun[rt] - mn) : 1.f;
+        mrun[rt] = mn;
+        lrun[rt] *= alpha;
+#pragma unroll
+        for (int nn = 0; nn < DT; ++nn) O[rt][nn] *= alpha;
+      }
+      const float mn = mrun[rt];
       float p[16], sum = 0.f;
 #pragma unroll
       for (int q = 0; q < 16; ++q) { p[q] = fast_exp2(z[q] - mn); sum += p[q]; }
-      lrun[rt] = lrun[rt] * alpha + sum;
-#pragma unroll
-      for (int nn = 0; nn < DT; ++nn) O[rt][nn] *= alpha;
+      lrun[rt] += sum;
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         bf16x8 pb;

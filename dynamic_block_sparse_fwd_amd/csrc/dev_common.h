@@ -146,6 +146,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(p.x, p.y);
 }
 
+// Lazy online-softmax rescaling: headroom of a row's reference max, in log2 units.  The
+// reference moves (and the accumulators are rescaled) only when a score exceeds it by more than
+// this, so probabilities fed to the matrix core stay below 2^8 (bf16 keeps its relative
+// precision there) and most tiles skip the rescale.
+constexpr float kLazyLog2 = 8.f;
+
 // Workgroup barrier that orders LDS only: unlike __syncthreads it does not wait for global
 // loads in flight, so prefetches issued before it stay outstanding.
 __device__ __forceinline__ void lds_barrier() {

@@ -22,10 +22,6 @@
 
 namespace nsa {
 
-// Lazy softmax rescaling: headroom of the reference max, in log2 units (probabilities fed to the
-// matrix core stay below 2^8; bf16 keeps its relative precision there).
-constexpr float kLazyLog2 = 8.f;
-
 constexpr int MOBA_ROWS = 128;  // gathered queries per block-major tile
 
 // kbar of one block: 16-byte loads, each thread sums 8 features over a stride of rows; the

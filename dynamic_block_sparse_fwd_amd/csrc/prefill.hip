@@ -210,10 +210,18 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
 #pragma unroll
         for (int e = 1; e < 16; ++e) tm = fmaxf(tm, raw[rt][e]);
         tm = col_max4(tm);
-        const float mn = fmaxf(wm[rt], tm);
-        const float msl = (mn == kNegInf) ? 0.f : mn * sl;
-        const float alpha = fast_exp2(fmaf(wm[rt], sl, -msl));
-        wm[rt] = mn;
+        // lazy rescale: the reference moves only past kLazyLog2 of headroom (a row with no key
+        // yet has reference -inf and moves on its first key)
+        const bool move = tm * sl > wm[rt] * sl + kLazyLog2;
+        if (__ballot(move) != 0) {  // uniform
+          const float mn = move ? tm : wm[rt];
+          const float alpha = move ? fast_exp2((wm[rt] - mn) * sl) : 1.f;
+          wm[rt] = mn;
+          wl[rt] *= alpha;
+#pragma unroll
+          for (int n = 0; n < DT; ++n) O[rt][n] *= alpha;
+        }
+        const float msl = (wm[rt] == kNegInf) ? 0.f : wm[rt] * sl;
         float sum = 0.f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -221,9 +229,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
           sum += p;
           pb[rt][e >> 3][e & 7] = (__bf16)p;
         }
-        wl[rt] = wl[rt] * alpha + sum;
-#pragma unroll
-        for (int n = 0; n < DT; ++n) O[rt][n] *= alpha;
+        wl[rt] += sum;
       }
       pv_tiles<D, RTW>(Vs, pb, g4, r16, O);
     }
@@ -473,12 +479,19 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void window_kernel(PrefillArgs a
 #pragma unroll
       for (int e = 1; e < 16; ++e) tm = fmaxf(tm, raw[rt][e]);
       tm = col_max4(tm);
-      const float mn = fmaxf(mrun[rt], tm);
+      // lazy rescale: the reference moves only past kLazyLog2 of headroom
+      const bool move = tm * sl > mrun[rt] * sl + kLazyLog2;
+      if (__ballot(move) != 0) {  // uniform
+        const float mn = move ? tm : mrun[rt];
+        const float alpha = move ? fast_exp2((mrun[rt] - mn) * sl) : 1.f;
+        mrun[rt] = mn;
+        lrun[rt] *= alpha;
+#pragma unroll
+        for (int n = 0; n < DT; ++n) O[rt][n] *= alpha;
+      }
       // A row with no visible key yet keeps m = -inf; exponentials then use 0 as reference
       // so every p is exactly 0 (no branch: the MFMAs below need the whole wave).
-      const float msl = (mn == kNegInf) ? 0.f : mn * sl;
-      const float alpha = fast_exp2(fmaf(mrun[rt], sl, -msl));
-      mrun[rt] = mn;
+      const float msl = (mrun[rt] == kNegInf) ? 0.f : mrun[rt] * sl;
       float sum = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -486,9 +499,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void window_kernel(PrefillArgs a
         sum += p;
         pb[rt][e >> 3][e & 7] = (__bf16)p;
       }
-      lrun[rt] = lrun[rt] * alpha + sum;
-#pragma unroll
-      for (int n = 0; n < DT; ++n) O[rt][n] *= alpha;
+      lrun[rt] += sum;
     }
     pv_tiles<D, RTW>(Vs, pb, g4, r16, O);
   }
@@ -655,11 +666,17 @@ __global__ __launch_bounds__(kSelWaves * 64, 1) void selected_kernel(PrefillArgs
     float tm = z[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) tm = fmaxf(tm, z[e]);
-    tm = col_max4(tm);
-    const float mn = fmaxf(mrun, tm);  // finite: every tile used holds a key <= t
-    const float msl = mn * sl;
-    const float alpha = fast_exp2(fmaf(mrun, sl, -msl));
-    mrun = mn;
+    tm = col_max4(tm);  // finite: every tile used holds a key <= t
+    const bool move = tm * sl > mrun * sl + kLazyLog2;
+    if (__ballot(move) != 0) {  // uniform: lazy rescale
+      const float mn = move ? tm : mrun;
+      const float alpha = move ? fast_exp2((mrun - mn) * sl) : 1.f;
+      mrun = mn;
+      lrun *= alpha;
+#pragma unroll
+      for (int n = 0; n < DT; ++n) O[n] *= alpha;
+    }
+    const float msl = mrun * sl;
     float sum = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -667,9 +684,7 @@ __global__ __launch_bounds__(kSelWaves * 64, 1) void selected_kernel(PrefillArgs
       sum += p;
       pb[e >> 3][e & 7] = (__bf16)p;
     }
-    lrun = fmaf(lrun, alpha, sum);
-#pragma unroll
-    for (int n = 0; n < DT; ++n) O[n] *= alpha;
+    lrun += sum;
   };
 
   // shared tiles, from LDS

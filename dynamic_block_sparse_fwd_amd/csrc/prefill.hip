@@ -135,16 +135,15 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
       }
     }
   }
-  // Row maximum (scaled, log2 units) and 1 / sum: pass 2 feeds the matrix core with
-  // p' = exp2(z - max) (largest term exactly 1 in bf16) and normalises in fp32.
-  float rmax[RTW], rinv[RTW];
+  // Row log-sum-exp (scaled, log2 units): pass 2 computes the normalised probabilities
+  // p = exp2(z - lse) directly, for the block importance (fp32) and the P V product (bf16).
+  float rlse[RTW];
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
     const float M = col_max4(mrun[rt]);
     const float part = (mrun[rt] == kNegInf) ? 0.f : lrun[rt] * fast_exp2((mrun[rt] - M) * sl);
     const float L = col_sum4(part);
-    rmax[rt] = (M == kNegInf) ? 0.f : M * sl;  // no visible key: every p' is masked to 0
-    rinv[rt] = (M == kNegInf) ? 0.f : 1.0f / L;
+    rlse[rt] = (M == kNegInf) ? 0.f : M * sl + __log2f(L);  // no visible key: p masked to 0
   }
 
   f32x4 O[RTW][DT];
@@ -153,17 +152,16 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
 #pragma unroll
     for (int n = 0; n < DT; ++n) O[rt][n] = zero4();
   const int Hq = a.Hkv * G;
-  // The epilogue multiplies O by ef = g0 / L (L the compressed softmax sum), and pass 2 feeds
-  // the matrix core with p' = exp2(z - max) unscaled (its largest term exactly 1 in bf16).
-  // Fused, O first receives the window output times g2 / ef, so that out = g0 * o_cmp +
-  // g2 * o_win is written once and never read; a row with ef = 0 keeps the window output as is
-  // (ef taken as 1) and drops p' from the P V product (ps = 0).
+  // The epilogue multiplies O by ef = g0.  Fused, O first receives the window output times
+  // g2 / ef, so that out = g0 * o_cmp + g2 * o_win is written once and never read; a row with
+  // g0 = 0 keeps the window output as is (ef taken as 1) and drops p from the P V product
+  // (ps = 0).
   float ps[RTW], ef[RTW];
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
     const int t = row_t[rt];
     const float g0 =
-        t < a.T ? a.gate[(((long)b * a.T + t) * Hq + row_h[rt]) * 3 + 0] * rinv[rt] : 0.f;
+        t < a.T ? a.gate[(((long)b * a.T + t) * Hq + row_h[rt]) * 3 + 0] : 0.f;
     const bool zero = a.fuse_window && g0 == 0.f;
     ps[rt] = zero ? 0.f : 1.f;
     ef[rt] = zero ? 1.f : g0;
@@ -275,7 +273,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
       for (int kc2 = 0; kc2 < 2; ++kc2) {
         float pv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(raw[rt][kc2 * 8 + e], sl, -rmax[rt]));
+        for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(raw[rt][kc2 * 8 + e], sl, -rlse[rt]));
         if (!full) {
           __asm__ volatile("" ::: "memory");
 #pragma unroll
@@ -292,10 +290,10 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
           for (int e = 0; e < 8; ++e) pbt[rt][kc2][e] = (__bf16)pv[e];
         }
         if constexpr (FAST) {
-          const float cA = head_sum<G>(((pv[0] + pv[1]) + pv[2] + 0.5f * pv[3]) * rinv[rt]);
-          const float cB = head_sum<G>(((pv[4] + pv[5]) + pv[6] + 0.5f * pv[7]) * rinv[rt]);
-          const float h3 = head_sum<G>((0.5f * pv[3]) * rinv[rt]);
-          const float h7 = head_sum<G>((0.5f * pv[7]) * rinv[rt]);
+          const float cA = head_sum<G>((pv[0] + pv[1]) + pv[2] + 0.5f * pv[3]);
+          const float cB = head_sum<G>((pv[4] + pv[5]) + pv[6] + 0.5f * pv[7]);
+          const float h3 = head_sum<G>(0.5f * pv[3]);
+          const float h7 = head_sum<G>(0.5f * pv[7]);
           if ((r16 % G) == 0) {
             const int tq = r / G, jl = 8 * kc2 + 2 * g4;
             Cb[tq][jl] = cA;
@@ -306,7 +304,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float hs = head_sum<G>(pv[e] * rinv[rt]);
+            const float hs = head_sum<G>(pv[e]);
             if ((r16 % G) == 0) Mb[r / G][32 * kc2 + 8 * g4 + e] = hs;
           }
         }

@@ -3,16 +3,25 @@
 //
 // LDS tiles are unpadded and XOR-swizzled in 16-byte chunks so that the 16-byte operand reads
 // of a wave are free of bank conflicts:
-//   K tile  Ks[64][D]: chunk c of key row r is stored at chunk c ^ ((r & 3) | ((r & 8) >> 1));
+//   K tile  Ks[64][D]: chunk c of key row r is stored at chunk c ^ k_swz(r), where k_swz(r) is
+//           the lane index (lane & 15) that reads row r (4 bits for the 16 chunks of a D = 128
+//           row, 3 bits for D = 64);
 //   V tile  Vs[D][64]: chunk c of feature row r is stored at chunk c ^ (r & 7).
-// With the sub-tile row order of dev_common.h both swizzles reduce to (lane & 7) on the read
-// side, so a read of logical chunk c by lane L is at physical chunk c ^ (L & 7).
+// With the sub-tile row order of dev_common.h a read of logical K chunk c by lane L is at
+// physical chunk c ^ (L & 15) (D = 128), a V read at c ^ (L & 7).  (A 3-bit K swizzle at
+// D = 128 left lanes L and L + 8 on the same banks: the counters showed as many conflict cycles
+// as LDS instructions.)
 #pragma once
 #include "dev_common.h"
 
 namespace nsa {
 
-__device__ __forceinline__ int k_swz(int r) { return (r & 3) | ((r & 8) >> 1); }
+// Swizzle of K row r: the lane index r16 that reads the row (see perm_key), 4 bits wide when a
+// row has 16 chunks (D = 128), 3 bits otherwise.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  return D >= 128 ? ((r & 3) | ((r & 24) >> 1)) : ((r & 3) | ((r & 8) >> 1));
+}
 
 // Global -> register staging of one 64 x D K tile (row-major source) and one D x 64 V tile
 // (keys contiguous, row pitch `pitch`), NT threads; then register -> LDS with the swizzle.
@@ -39,7 +48,7 @@ struct KTileRegs {
     for (int i = 0; i < N; ++i) {
       const int c = threadIdx.x + i * NT;
       const int rr = c / (D / 8), o = c % (D / 8);
-      *reinterpret_cast<u32x4*>(&Ks[rr][(o ^ k_swz(rr)) * 8]) = r[i];
+      *reinterpret_cast<u32x4*>(&Ks[rr][(o ^ k_swz<D>(rr)) * 8]) = r[i];
     }
   }
 };
@@ -90,7 +99,7 @@ template <int D>
 __device__ __forceinline__ void k_frags(const u16 (*Ks)[D], int kc, int s, int g4, int r16,
                                         bf16x8* kf) {
   const u16* krow = Ks[32 * kc + perm_key(r16, s)];
-  const int x = r16 & 7;
+  const int x = D >= 128 ? r16 : (r16 & 7);
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) kf[c] = load8(krow + (((4 * c + g4) ^ x) * 8));
 }

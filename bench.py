@@ -384,6 +384,9 @@ def moba_work(T, H, D, block=512, top_k=3):
 
 
 def bench_moba(args, B=1, T=131072, H=32, D=128, seed=4, calls=5):
+    """MoBA prefill at T tokens.  Up to 128k the inputs come from synth_inputs (shared with the
+    oracle baseline); beyond, N(0,1) bf16 values are drawn on the device with a seeded torch
+    generator (the host generator would take minutes and tens of GB at 1M x 32 heads)."""
     import torch
 
     import dynamic_block_sparse_fwd_amd as nsa
@@ -391,11 +394,19 @@ def bench_moba(args, B=1, T=131072, H=32, D=128, seed=4, calls=5):
 
     cfg = nsa.MobaConfig(B, T, H, D, block=512, top_k=3)
     t0 = time.time()
-    x = S.moba_inputs(seed, B, T, H, D)
+    dev = torch.device("cuda:0")
+    if T <= 131072:
+        x = S.moba_inputs(seed, B, T, H, D)
+        d = {k: torch.from_numpy(v.view(np.int16)).to(dev) for k, v in x.items()}
+    else:
+        x = None
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        shapes = {"q": (B, T, H, D), "k": (B, H, T, D), "v": (B, H, T, D)}
+        d = {k: torch.randn(sh, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+             for k, sh in shapes.items()}
     print("[bench] MoBA inputs generated in %.1fs" % (time.time() - t0), file=sys.stderr,
           flush=True)
-    dev = torch.device("cuda:0")
-    d = {k: torch.from_numpy(v.view(np.int16)).to(dev) for k, v in x.items()}
     out = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
     idx = torch.empty((B, T, H, cfg.top_k + 1), dtype=torch.int32, device=dev)
     ws = torch.empty(nsa.moba_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
@@ -466,6 +477,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-moba", action="store_true")
+    ap.add_argument("--moba-seq", type=int, default=131072,
+                    help="MoBA sequence length for --only moba (beyond 128k: device-drawn inputs)")
     ap.add_argument("--only", choices=("prefill", "decode", "moba"),
                     help="run one workload and print its result alone (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -485,7 +498,7 @@ def main():
         print(json.dumps({"decode": dec}), flush=True)
         return
     if args.only == "moba":
-        mo, _ = bench_moba(args)
+        mo, _ = bench_moba(args, T=args.moba_seq)
         print(json.dumps({"moba": mo}), flush=True)
         return
     pre, x = bench_prefill(args)

@@ -91,3 +91,18 @@ def test_moba_128k_sampled_rows():
                                      rng.choice(np.arange(2048, T - 64), 4096 - 2048 - 64,
                                                 replace=False)])).astype(np.int32)
     check_moba(cfg, x, np.zeros_like(rows), rows, gout, gidx, "moba 128k")
+
+
+def test_moba_1m_sampled_rows():
+    """MoBA at 1M tokens (the next row after the 128k workload: 2048 blocks of 512 per head), 4
+    heads, D=128, top-3 + own: every row of the first 4 blocks, the last 64 rows and a seeded
+    random remainder (3072 rows in all)."""
+    B, T, H, D = 1, 1 << 20, 4, 128
+    cfg = O.MobaCfg(B, T, H, D, block=512, top_k=3)
+    x = S.moba_inputs(6, B, T, H, D)
+    gout, gidx = gpu_moba(cfg, x)
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([np.arange(2048), np.arange(T - 64, T),
+                                     rng.choice(np.arange(2048, T - 64), 3072 - 2048 - 64,
+                                                replace=False)])).astype(np.int32)
+    check_moba(cfg, x, np.zeros_like(rows), rows, gout, gidx, "moba 1M")

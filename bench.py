@@ -137,8 +137,23 @@ def prefill_pairs(T, l=32, d=16, beta=64, n=16, n_local=2, w=512):
     return int(vis.sum()), int(slc.sum()), int(win.sum())
 
 
-def prefill_flops(B, T, Hkv, G, D, l=32, d=16):
+def selected_keys(idx, beta=64):
+    """Causal keys of the selected blocks, summed over (sequence, position, KV group), from a
+    prefill index tensor [B, T, Hkv, n] (-1 = unused)."""
+    import torch
+
+    T = idx.shape[1]
+    t = torch.arange(T, device=idx.device).view(1, T, 1, 1)
+    k = (t + 1 - idx.long() * beta).clamp(0, beta)
+    return int(torch.where(idx >= 0, k, torch.zeros_like(k)).sum())
+
+
+def prefill_flops(B, T, Hkv, G, D, l=32, d=16, slc_keys=None):
+    """slc_keys: selected keys summed over (sequence, position, KV group) when the selection
+    is adaptive; None = the fixed top-16 count."""
     cmp_, slc, win = prefill_pairs(T, l, d)
+    if slc_keys is not None:
+        slc = slc_keys / (B * Hkv)
     Hq = Hkv * G
     ncmp = (T - l) // d + 1
     per = {
@@ -161,7 +176,7 @@ def bench_prefill(args):
 
     nsa.load_library()
     B, T, Hkv, G, D = 1, args.seq, 4, 16, 128
-    cfg = nsa.NsaConfig(B, T, Hkv, G, D)
+    cfg = nsa.NsaConfig(B, T, Hkv, G, D, top_p=args.top_p)
     t0 = time.time()
     x = S.nsa_prefill_inputs(2, B, T, Hkv, G, D)
     print("[bench] prefill inputs generated in %.1fs" % (time.time() - t0), file=sys.stderr,
@@ -196,13 +211,16 @@ def bench_prefill(args):
             stage_ms[nm] += ev.elapsed_ms(base + i, base + i + 1) / args.steps
         total_ev += ev.elapsed_ms(base, base + nst) / args.steps
     ms = wall * 1e3 / args.steps
-    flops = prefill_flops(B, T, Hkv, G, D)
+    slc_keys = selected_keys(idx) if args.top_p > 0 else None
+    blocks_per_row = float((idx >= 0).sum(-1).float().mean())
+    flops = prefill_flops(B, T, Hkv, G, D, slc_keys=slc_keys)
     F = sum(flops.values())
     # nsa_prefill runs the window branch inside the compressed-attention kernel (same query
     # tile, output written once): its stage interval is empty and its work counts there
     flops["cmp_select"] += flops["window"]
     flops["window"] = 0.0
     dom = max(stage_ms, key=lambda k: stage_ms[k])
+    gbytes = gather_bytes(B, T, Hkv, D) if slc_keys is None else slc_keys * 2 * D * 2
     stages = {nm: {"ms": round(stage_ms[nm], 4),
                    "tflops": round(flops[nm] / (stage_ms[nm] * 1e-3) / 1e12, 2)
                    if flops.get(nm, 0) > 0 and stage_ms[nm] > 0 else None}
@@ -218,8 +236,8 @@ def bench_prefill(args):
                   "traffic": measured_traffic("selected_kernel") if dom == "selected" else None},
         # the selected branch gathers a 64-key K+V tile per (position, group, selected block):
         # its bound is the cache hierarchy's gather bandwidth, reported beside the MFMA figure
-        selected_gather={"bytes": gather_bytes(B, T, Hkv, D),
-                         "gbs": gather_bytes(B, T, Hkv, D) / (stage_ms["selected"] * 1e-3) / 1e9},
+        selected_gather={"bytes": gbytes, "gbs": gbytes / (stage_ms["selected"] * 1e-3) / 1e9},
+        blocks_per_row=blocks_per_row,
     )
     del d, out, idx, ws
     torch.cuda.empty_cache()
@@ -277,7 +295,7 @@ def bench_decode(args, B=32, L=65536, Hkv=4, G=16, D=128, seed=3, calls=20):
     import dynamic_block_sparse_fwd_amd as nsa
     import synth_inputs as S
 
-    cfg = nsa.NsaConfig(B, L, Hkv, G, D)
+    cfg = nsa.NsaConfig(B, L, Hkv, G, D, top_p=args.top_p)
     t0 = time.time()
     x = S.nsa_decode_inputs(seed, B, L, Hkv, G, D)
     print("[bench] decode inputs generated in %.1fs" % (time.time() - t0), file=sys.stderr,
@@ -329,7 +347,9 @@ def bench_decode(args, B=32, L=65536, Hkv=4, G=16, D=128, seed=3, calls=20):
     kv = cmp_bytes + tok_bytes
     med = {nm: float(np.median(v)) for nm, v in stage_ms.items()}
     res = {
-        "workload": "nsa_decode B=%d L=%d Hkv=%d G=%d D=%d top16 window512" % (B, L, Hkv, G, D),
+        "workload": "nsa_decode B=%d L=%d Hkv=%d G=%d D=%d top16 window512%s" % (
+            B, L, Hkv, G, D, " top_p=%g" % args.top_p if args.top_p > 0 else ""),
+        "blocks_per_row": round(float((idx >= 0).sum(-1).float().mean()), 3),
         "us_per_step": round(ms * 1e3, 2),
         "us_per_step_with_stage_events": round(float(np.median(per_call)) * 1e3, 2),
         "tok_s": round(B / (ms * 1e-3), 1),
@@ -481,6 +501,8 @@ def main():
                     help="MoBA sequence length for --only moba (beyond 128k: device-drawn inputs)")
     ap.add_argument("--only", choices=("prefill", "decode", "moba"),
                     help="run one workload and print its result alone (for profiling runs)")
+    ap.add_argument("--top-p", type=float, default=0.0,
+                    help="adaptive top-p block selection for the NSA workloads (0: fixed top-16)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run the plain copy used to scale the traffic counters, then exit")
     args = ap.parse_args()
@@ -525,8 +547,11 @@ def main():
                     "events_ms_per_step": round(pre["events_ms_per_step"], 4),
                     "stages": pre["stages"],
                     "selected_gather": {"bytes": pre["selected_gather"]["bytes"],
-                                        "gbs": round(pre["selected_gather"]["gbs"], 1)}},
+                                        "gbs": round(pre["selected_gather"]["gbs"], 1)},
+                    "blocks_per_row": round(pre["blocks_per_row"], 3)},
     }
+    if args.top_p > 0:
+        line["config"]["top_p"] = args.top_p
     if args.only == "prefill":
         print(json.dumps(line), flush=True)
         return

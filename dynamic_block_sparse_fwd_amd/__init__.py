@@ -33,7 +33,7 @@ class NsaError(RuntimeError):
 class nsa_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("B", "T", "Hkv", "G", "D", "cmp_len", "cmp_stride",
                                                "sel_block", "top_n", "n_local", "window")] + \
-               [("scale", ctypes.c_float)]
+               [("scale", ctypes.c_float), ("top_p", ctypes.c_float)]
 
 
 class moba_config(ctypes.Structure):
@@ -102,6 +102,7 @@ class NsaConfig:
     n_local: int = 2
     window: int = 512
     scale: float = None
+    top_p: float = 0.0  # 0: fixed top_n; in (0, 1]: adaptive cut by cumulative importance
 
     @property
     def Hq(self):
@@ -120,7 +121,7 @@ class NsaConfig:
         s = self.scale if self.scale is not None else self.D ** -0.5
         return nsa_config(self.B, self.T, self.Hkv, self.G, self.D, self.cmp_len,
                           self.cmp_stride, self.sel_block, self.top_n, self.n_local,
-                          self.window, s)
+                          self.window, s, self.top_p)
 
 
 @dataclass

@@ -27,7 +27,8 @@ int check_nsa_base(const nsa_config* c) {
   if (c == nullptr) return NSA_ERR_INVALID_ARG;
   if (c->B <= 0 || c->T <= 0 || c->Hkv <= 0 || c->G <= 0 || c->D <= 0 || c->cmp_len <= 0 ||
       c->cmp_stride <= 0 || c->sel_block <= 0 || c->top_n <= 0 || c->n_local < 0 ||
-      c->window <= 0 || !(c->scale > 0.f) || !std::isfinite(c->scale))
+      c->window <= 0 || !(c->scale > 0.f) || !std::isfinite(c->scale) ||
+      !(c->top_p >= 0.f && c->top_p <= 1.f))
     return NSA_ERR_INVALID_ARG;
   if (c->D != 64 && c->D != 128) return NSA_ERR_UNSUPPORTED;
   if (!g_ok(c->G)) return NSA_ERR_UNSUPPORTED;
@@ -318,7 +319,7 @@ static int prefill_run(const nsa_config* c, unsigned stages, const void* q, cons
   a.idx = idx;
   a.B = c->B; a.T = c->T; a.Hkv = c->Hkv; a.G = c->G; a.D = c->D;
   a.l = c->cmp_len; a.d = c->cmp_stride; a.beta = c->sel_block; a.top_n = c->top_n;
-  a.n_local = c->n_local; a.window = c->window;
+  a.n_local = c->n_local; a.window = c->window; a.top_p = c->top_p;
   a.ncmp = p.ncmp; a.NCP = p.NCP; a.TP = p.TP; a.nblk = p.nblk;
   a.scale_log2 = c->scale * 1.4426950408889634f;
   a.fuse_window = s_cmp && s_win;  // one query tile, out written once
@@ -402,7 +403,7 @@ static int decode_impl(const nsa_config* c, const void* q, const void* kcache,
   a.cb = reinterpret_cast<float*>(base + p.cb);
   a.B = c->B; a.L = c->T; a.Hkv = c->Hkv; a.G = c->G; a.D = c->D;
   a.l = c->cmp_len; a.d = c->cmp_stride; a.beta = c->sel_block; a.top_n = c->top_n;
-  a.n_local = c->n_local; a.window = c->window;
+  a.n_local = c->n_local; a.window = c->window; a.top_p = c->top_p;
   a.ncmp = p.sh.ncmp; a.nblk = p.sh.nblk; a.NCH = p.sh.NCH; a.NT = p.sh.NT; a.NBT = p.sh.NBT;
   a.scale_log2 = c->scale * 1.4426950408889634f;
   (void)hipGetLastError();

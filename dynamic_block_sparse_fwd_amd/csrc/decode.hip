@@ -501,7 +501,8 @@ __global__ __launch_bounds__(kGrpThreads, 1) void dec_group_kernel(DecodeArgs a)
   const int nvis = n_visible(t, a.l, a.d, a.ncmp);
   const int nch = (nvis + CHUNK - 1) / CHUNK;
   const int ntv = (nvis + 63) / 64;
-  const bool all = nb <= a.top_n;        // uniform: every block is selected
+  const bool top_p = a.top_p > 0.f;
+  const bool all = nb <= a.top_n && !top_p;  // uniform: every block is selected
   const bool scored = !all && nvis > 0;  // uniform
   const float sl = a.scale_log2;
   const int w0 = t - a.window + 1;
@@ -620,7 +621,7 @@ __global__ __launch_bounds__(kGrpThreads, 1) void dec_group_kernel(DecodeArgs a)
     }
   lds_barrier();  // scores and chunk weights in LDS (the loads stay in flight)
   const int bcur = nb - 1;
-  const int flo = bcur - a.n_local + 1;
+  const int flo = bcur - a.n_local + 1 > 1 ? bcur - a.n_local + 1 : 1;  // forced: 0, flo..bcur
   const int kfree = a.top_n - 1 - a.n_local;
   // top-n in two levels: waves 0-3 (one per SIMD) each rank a quarter of the free blocks
   // 1 .. flo-1, then wave 0 ranks their 4 * kfree winners
@@ -643,17 +644,28 @@ __global__ __launch_bounds__(kGrpThreads, 1) void dec_group_kernel(DecodeArgs a)
         sidx[lane] = el;
       }
     } else {
-      const uint64_t key =
+      uint64_t key =
           wave_topk([&](int i) { return Kw[i]; }, 0, kRankWaves * kfree, kfree, lane);
-      int el = rank_key_index(key);
+      if (top_p) {
+        float forced = Ss[0];
+        for (int j = flo; j <= bcur; ++j) forced += Ss[j];
+        key = top_p_cut(key, kfree, forced, nvis > 0 ? a.top_p * (float)a.G : 0.f, lane);
+      }
+      int el = key != 0 ? rank_key_index(key) : 0x7FFFFFFF;
       if (lane == kfree) el = 0;
-      if (lane > kfree && lane < a.top_n) el = flo + (lane - kfree - 1);
+      if (lane > kfree && lane <= kfree + bcur - flo + 1) el = flo + (lane - kfree - 1);
       int rank = 0;
       for (int o = 0; o < a.top_n; ++o)  // the whole wave is active here
         rank += (__builtin_amdgcn_readlane(el, o) < el) ? 1 : 0;
-      if (lane < a.top_n) {
+      const bool valid = lane < a.top_n && el != 0x7FFFFFFF;
+      const int nsel = (int)__popcll(__ballot(valid));
+      if (valid) {
         orow[rank] = el;
         sidx[rank] = el;
+      }
+      if (lane >= nsel && lane < a.top_n) {
+        orow[lane] = -1;
+        sidx[lane] = -1;
       }
     }
     __asm__ volatile("" ::: "memory");  // sidx written by this wave before its reads

@@ -247,4 +247,19 @@ __device__ uint64_t wave_topk(KeyOf keyof, int first, int last, int k, int lane)
   return mine;
 }
 
+// Adaptive top-p cut of a ranked free list held one key per lane (lane e < k: the e-th best free
+// block's rank key, 0 = none).  Lane e keeps its key while the importance chosen before it --
+// the forced blocks' total, then the better free blocks added in rank order -- is below target,
+// and gets 0 otherwise; the kept lanes are a prefix.  Called by the whole wave.
+__device__ __forceinline__ uint64_t top_p_cut(uint64_t key, int k, float forced, float target,
+                                              int lane) {
+  const int sbits = (int)(uint32_t)(key >> 32);  // the score's bits (rank_key's high word)
+  float before = forced;
+  for (int o = 0; o < k; ++o) {
+    const float s = __int_as_float(__builtin_amdgcn_readlane(sbits, o));
+    if (o < lane) before += s;
+  }
+  return before < target ? key : 0;
+}
+
 }  // namespace nsa

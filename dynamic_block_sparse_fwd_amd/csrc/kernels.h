@@ -19,6 +19,7 @@ struct PrefillArgs {
   int l, d, beta, top_n, n_local, window;
   int ncmp, NCP, TP, nblk;
   float scale_log2;     // softmax scale * log2(e)
+  float top_p;          // 0: fixed top_n; else the adaptive cut at top_p * G
   int fuse_window;      // cmp_select also runs the window branch and writes out once
 };
 
@@ -43,6 +44,7 @@ struct DecodeArgs {
   int l, d, beta, top_n, n_local, window;
   int ncmp, nblk, NCH, NT, NBT;
   float scale_log2;
+  float top_p;  // 0: fixed top_n; else the adaptive cut at top_p * G
 };
 
 // ev: nullptr or NSA_DECODE_NSTAGES + 1 events recorded around the stages.

@@ -376,32 +376,41 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
 
   // Selection: one wave per position.  Free candidates are ranked by a 64-bit key
   // (score bits << 32 | ~index): larger score first, then lower index.
+  const bool top_p = a.top_p > 0.f;
   for (int tq = wave; tq < TQ; tq += QT::NW) {
     const int t = t0 + tq;
     if (t >= a.T) break;
     const int bcur = t / a.beta, nb = bcur + 1;
     int32_t* orow = a.idx + (((long)b * a.T + t) * a.Hkv + kvh) * a.top_n;
-    if (nb <= a.top_n) {
+    if (nb <= a.top_n && !top_p) {
       for (int e = lane; e < a.top_n; e += 64) orow[e] = e < nb ? e : -1;
       continue;
     }
-    const int flo = bcur - a.n_local + 1;  // forced local blocks flo..bcur (flo >= 2 here)
-    const int nforced = 1 + a.n_local;
-    const int kfree = a.top_n - nforced;
+    // forced: block 0 and the local blocks flo..bcur; free candidates 1 .. flo-1
+    const int flo = bcur - a.n_local + 1 > 1 ? bcur - a.n_local + 1 : 1;
+    const int kfree = a.top_n - 1 - a.n_local;
     const float* srow = Sb + tq * nblk;
-    // lane e < kfree receives the e-th winner among the free blocks 1 .. flo-1
-    const uint64_t key =
-        wave_topk([&](int j) { return rank_key(srow[j], j); }, 1, flo, kfree, lane);
+    // lane e < kfree receives the e-th winner among the free blocks (0 past the last one)
+    uint64_t key = wave_topk([&](int j) { return rank_key(srow[j], j); }, 1, flo, kfree, lane);
+    if (top_p) {
+      float forced = srow[0];
+      for (int j = flo; j <= bcur; ++j) forced += srow[j];
+      const bool seen = t >= a.l - 1;  // a compressed token is visible: total importance G
+      key = top_p_cut(key, kfree, forced, seen ? a.top_p * (float)a.G : 0.f, lane);
+    }
     // the set: lanes 0..kfree-1 hold winners; next lanes hold block 0 and flo..bcur
-    int el = rank_key_index(key);
+    int el = key != 0 ? rank_key_index(key) : 0x7FFFFFFF;
     if (lane == kfree) el = 0;
-    if (lane > kfree && lane < a.top_n) el = flo + (lane - kfree - 1);
+    if (lane > kfree && lane <= kfree + bcur - flo + 1) el = flo + (lane - kfree - 1);
     int rank = 0;
     for (int o = 0; o < a.top_n; ++o) {
       const int other = __builtin_amdgcn_readlane(el, o);  // the whole wave is active here
       rank += (other < el) ? 1 : 0;
     }
-    if (lane < a.top_n) orow[rank] = el;
+    const bool valid = lane < a.top_n && el != 0x7FFFFFFF;
+    const int nsel = (int)__popcll(__ballot(valid));
+    if (valid) orow[rank] = el;
+    if (lane >= nsel && lane < a.top_n) orow[lane] = -1;
   }
 }
 

@@ -69,6 +69,8 @@ typedef struct nsa_config {
   int32_t n_local;    /* most recent blocks always selected besides block 0 (2)        */
   int32_t window;     /* sliding-window length (512)                                   */
   float scale;        /* softmax scale applied to q.k (1/sqrt(D))                      */
+  float top_p;        /* 0: top_n blocks per (query, group); in (0, 1]: adaptive cut, see
+                       * below (top_n is then the cap)                                  */
 } nsa_config;
 
 /* One MoBA call (no GQA: H heads with their own K/V). */
@@ -81,6 +83,19 @@ typedef struct moba_config {
 
 /* Human-readable text for a status code (static storage). */
 const char* nsa_status_string(int status);
+
+/*
+ * Adaptive top-p block selection ("Native Sparse Attention" article, closing remarks on
+ * adaptive sparsity: choose the most important blocks first and stop once their share of the
+ * total importance reaches p).  With top_p > 0 the forced blocks (block 0 and the n_local most
+ * recent) are kept as before and their importance counts as chosen; the free blocks are then
+ * taken in rank order (importance descending, index ascending) while the importance chosen so
+ * far is below top_p * G, G being the total importance of a position that sees at least one
+ * compressed token (each of the group's heads spreads a probability mass of one), and 0 before
+ * that.  top_n caps the whole set; the rule also applies when every block would fit.  Index
+ * rows stay ascending with -1 padding.  top_p = 0 is the fixed top_n rule; NaN, negative or
+ * > 1 is NSA_ERR_INVALID_ARG.
+ */
 
 /* Host-only checks; no device is touched.  NSA_ERR_UNSUPPORTED when: D not 64/128;
  * G not in {1,2,4,8,16}; sel_block not a positive multiple of 64; top_n < 1 + n_local or

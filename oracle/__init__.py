@@ -33,7 +33,7 @@ def build(force: bool = True) -> str:
 class _NsaCfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("B", "T", "Hkv", "G", "D", "cmp_len", "cmp_stride",
                                              "sel_block", "top_n", "n_local", "window")] + \
-               [("scale", ctypes.c_double)]
+               [("scale", ctypes.c_double), ("top_p", ctypes.c_double)]
 
 
 class _MobaCfg(ctypes.Structure):
@@ -83,11 +83,12 @@ class NsaCfg:
     """Hyper-parameters of one NSA layer call (notation of the pages: block 64, top-16 ...)."""
 
     def __init__(self, B, T, Hkv, G, D, cmp_len=32, cmp_stride=16, sel_block=64, top_n=16,
-                 n_local=2, window=512, scale=None):
+                 n_local=2, window=512, scale=None, top_p=0.0):
         self.B, self.T, self.Hkv, self.G, self.D = B, T, Hkv, G, D
         self.cmp_len, self.cmp_stride = cmp_len, cmp_stride
         self.sel_block, self.top_n, self.n_local, self.window = sel_block, top_n, n_local, window
         self.scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+        self.top_p = float(top_p)  # 0: fixed top_n; in (0, 1]: adaptive cut (R9)
 
     @property
     def Hq(self):
@@ -103,7 +104,8 @@ class NsaCfg:
 
     def c(self):
         return _NsaCfg(self.B, self.T, self.Hkv, self.G, self.D, self.cmp_len, self.cmp_stride,
-                       self.sel_block, self.top_n, self.n_local, self.window, self.scale)
+                       self.sel_block, self.top_n, self.n_local, self.window, self.scale,
+                       self.top_p)
 
 
 class MobaCfg:

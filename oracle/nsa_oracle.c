@@ -31,6 +31,12 @@
  *   R8 MoBA: block key = mean of the block's keys (fp64, no rounding); score = q . kbar;
  *      past blocks j < b ranked by (score desc, index asc); own block always added; one softmax
  *      over the union, causal.
+ *   R9 adaptive top-p ([P4], closing remarks on adaptive sparsity: pick the most important
+ *      first and stop once the picked share of the total score reaches p): the forced blocks
+ *      of R5 are always kept and their importance counts as picked; free blocks are then taken
+ *      in the R5 ranking while the importance picked so far is below p * M, M = sum of S_j over
+ *      the visible blocks j <= b; top_n stays the cap on the whole set.  Applies whether or
+ *      not every visible block would fit.
  * Inputs are bf16 bit patterns, converted exactly to fp64; all arithmetic is fp64.
  */
 #include <math.h>
@@ -47,6 +53,7 @@ typedef struct {
   int sel_block, top_n, n_local;
   int window;
   double scale;
+  double top_p; /* R9: 0 = fixed top_n; in (0, 1] = adaptive cut by cumulative importance */
 } onsa_cfg;
 
 typedef struct {
@@ -162,7 +169,8 @@ static int int_cmp(const void* a, const void* b) {
  * Outputs per row (any may be NULL except out and idx_out):
  *   out, o_cmp, o_slc, o_win [Hq, D]; lse_cmp [Hq]; scores [Hkv, nblk_cap] (block j <= b);
  *   idx_out [Hkv, n] ascending, -1 padded; gap [Hkv] = (S_(k) - S_(k+1)) / S_(k) of the free
- *   ranking (INFINITY when no competitor is left out, 0 on an exact tie).
+ *   ranking at the number k of free blocks taken (INFINITY when no competitor is left out, 0 on
+ *   an exact tie); under top-p also at most min_a |cum_a - p M| / M over the mass decisions.
  */
 static void nsa_row(const onsa_cfg* cf, int t, const uint16_t* qrow, const uint16_t* kb,
                     const uint16_t* vb, long tstride, const uint16_t* kcb, const uint16_t* vcb,
@@ -227,7 +235,7 @@ static void nsa_row(const onsa_cfg* cf, int t, const uint16_t* qrow, const uint1
         int j = idx_in[(long)g * n + a];
         if (j >= 0) I[nI++] = j;
       }
-    } else if (nb <= n) {
+    } else if (cf->top_p <= 0 && nb <= n) {
       for (int j = 0; j < nb; ++j) I[nI++] = j;
     } else {
       memset(forced, 0, (size_t)nb);
@@ -241,10 +249,29 @@ static void nsa_row(const onsa_cfg* cf, int t, const uint16_t* qrow, const uint1
       }
       int k = n - nf;
       qsort(cs, (size_t)nc, sizeof(cand), cand_cmp);
-      for (int a = 0; a < k && a < nc; ++a) I[nI++] = cs[a].j;
+      if (cf->top_p > 0) { /* R9 */
+        double M = 0.0, cum = 0.0, close = INFINITY;
+        for (int j = 0; j < nb; ++j) M += S[j];
+        for (int j = 0; j < nb; ++j)
+          if (forced[j]) cum += S[j];
+        const double target = cf->top_p * M;
+        int a = 0;
+        for (; a < k && a < nc; ++a) {
+          double dist = fabs(cum - target);
+          if (dist < close) close = dist;
+          if (!(cum < target)) break;
+          I[nI++] = cs[a].j;
+          cum += cs[a].s;
+        }
+        if (M > 0) gp = close / M;
+        k = a; /* the ranking matters at the number actually taken */
+      } else {
+        for (int a = 0; a < k && a < nc; ++a) I[nI++] = cs[a].j;
+      }
       if (k > 0 && k < nc) {
         double sk = cs[k - 1].s, sk1 = cs[k].s;
-        gp = sk == sk1 ? 0.0 : (sk > 0 ? (sk - sk1) / sk : INFINITY);
+        double rg = sk == sk1 ? 0.0 : (sk > 0 ? (sk - sk1) / sk : INFINITY);
+        if (rg < gp) gp = rg;
       }
     }
     qsort(I, (size_t)nI, sizeof(int), int_cmp);

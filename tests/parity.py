@@ -5,6 +5,10 @@
     GPU's choice is accepted when every free block it picked scores at least
     S_(k) * (1 - 1e-4) in the oracle, and the oracle is then re-run with the GPU's indices
     before outputs are compared;
+  * under adaptive top-p the oracle's gap also covers the mass decisions (|cum - p M| / M);
+    a near-tie choice is accepted when, in the oracle's scores, its free blocks outrank the
+    rest within the same tolerance, the last one taken was still needed (mass before it below
+    p M + tol M) and it stopped only at the cap, with no block left, or with p M - tol M reached;
   * fp32 outputs within max-abs 1e-2 and mean-abs 1e-3 of the fp64 oracle.
 """
 import numpy as np
@@ -23,7 +27,29 @@ def free_kth_score(scores_row, t, beta, n, n_local):
     return free[k - 1] if 0 < k <= len(free) else None
 
 
-def check_nsa_idx(gpu_idx, ora, rows_t, beta, n, n_local):
+def check_top_p_choice(chosen, scores_row, t, beta, n, n_local, top_p, msg):
+    """Validity of one adaptive top-p index list against the oracle's fp64 scores."""
+    b = t // beta
+    forced = {0} | set(j for j in range(b - n_local + 1, b + 1) if j >= 0)
+    assert forced <= set(chosen), "forced block missing: " + msg
+    assert len(set(chosen)) == len(chosen) <= n, "bad index list: " + msg
+    assert sorted(chosen) == chosen, "indices not ascending: " + msg
+    s = scores_row
+    M = float(s[:b + 1].sum())
+    tol = GAP_TOL * M
+    free_in = sorted((s[j] for j in chosen if j not in forced), reverse=True)
+    free_out = [s[j] for j in range(b + 1) if j not in forced and j not in chosen]
+    if free_in and free_out:
+        assert free_in[-1] >= max(free_out) * (1 - GAP_TOL), "weak pick: " + msg
+    fm = float(sum(s[j] for j in forced))
+    total = fm + float(sum(free_in))
+    if free_in:
+        assert total - free_in[-1] < top_p * M + tol, "pick not needed: " + msg
+    if free_out and len(chosen) < n:
+        assert total >= top_p * M - tol, "stopped short of p: " + msg
+
+
+def check_nsa_idx(gpu_idx, ora, rows_t, beta, n, n_local, top_p=0.0):
     """Compare GPU indices with the oracle's.  Returns (rows needing an oracle re-run with the
     GPU indices, number of near-tie rows accepted).  Raises AssertionError on a real mismatch."""
     gpu_idx = np.asarray(gpu_idx)
@@ -39,6 +65,12 @@ def check_nsa_idx(gpu_idx, ora, rows_t, beta, n, n_local):
             msg = "row t=%d group %d: gpu %s oracle %s gap %.3g" % (
                 t, g, gpu_idx[r, g].tolist(), ora["idx"][r, g].tolist(), gap)
             assert gap < GAP_TOL, "index mismatch outside near-tie: " + msg
+            if top_p > 0:
+                chosen = [int(j) for j in gpu_idx[r, g] if j >= 0]
+                assert (gpu_idx[r, g, len(chosen):] == -1).all(), "bad padding: " + msg
+                check_top_p_choice(chosen, ora["scores"][r, g], t, beta, n, n_local, top_p, msg)
+                accepted += 1
+                continue
             sk = free_kth_score(ora["scores"][r, g], t, beta, n, n_local)
             assert sk is not None, msg
             b = t // beta

@@ -44,6 +44,10 @@ def test_validate_accepts_the_workloads(lib):
         else:
             assert st == nsa.NSA_OK
     assert lib.moba_validate(ctypes.byref(nsa.MobaConfig(1, 131072, 32, 128).c())) == nsa.NSA_OK
+    for p in (0.0, 1e-6, 0.5, 1.0):
+        c = cfgB()
+        c.top_p = p
+        assert lib.nsa_validate(ctypes.byref(c.c())) == nsa.NSA_OK
 
 
 @pytest.mark.parametrize("field,value,code", [
@@ -52,7 +56,8 @@ def test_validate_accepts_the_workloads(lib):
     ("sel_block", 48, nsa.NSA_ERR_UNSUPPORTED), ("top_n", 2, nsa.NSA_ERR_UNSUPPORTED),
     ("top_n", 65, nsa.NSA_ERR_UNSUPPORTED), ("window", 0, nsa.NSA_ERR_INVALID_ARG),
     ("cmp_stride", 64, nsa.NSA_ERR_UNSUPPORTED), ("scale", -1.0, nsa.NSA_ERR_INVALID_ARG),
-    ("T", 64 * 4096, nsa.NSA_ERR_UNSUPPORTED),
+    ("T", 64 * 4096, nsa.NSA_ERR_UNSUPPORTED), ("top_p", -0.1, nsa.NSA_ERR_INVALID_ARG),
+    ("top_p", 1.5, nsa.NSA_ERR_INVALID_ARG), ("top_p", float("nan"), nsa.NSA_ERR_INVALID_ARG),
 ])
 def test_validate_rejects(lib, field, value, code):
     c = cfgB()

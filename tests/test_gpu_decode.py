@@ -46,7 +46,8 @@ def gpu_decode(cfg, x, kc, vc, seqlens):
     import dynamic_block_sparse_fwd_amd as nsa
     nsa.load_library()
     c = nsa.NsaConfig(cfg.B, cfg.T, cfg.Hkv, cfg.G, cfg.D, cfg.cmp_len, cfg.cmp_stride,
-                      cfg.sel_block, cfg.top_n, cfg.n_local, cfg.window, cfg.scale)
+                      cfg.sel_block, cfg.top_n, cfg.n_local, cfg.window, cfg.scale,
+                      cfg.top_p)
     kp, vt = poisoned_caches(cfg, kc, vc, seqlens)
     out, idx = nsa.nsa_decode(c, to_dev(x["q"]), to_dev(x["kcache"]), to_dev(x["vcache"]),
                               to_dev(kp), to_dev(vt), to_dev(np.asarray(seqlens, np.int32)),
@@ -60,7 +61,8 @@ def check_decode(cfg, x, kc, vc, seqlens, what):
     ora = O.nsa_decode(cfg, x["q"], x["kcache"], x["vcache"], kc, vc, seqlens, x["gate"],
                        want_scores=True)
     rows_t = np.asarray(seqlens) - 1
-    rerun, acc = check_nsa_idx(gidx, ora, rows_t, cfg.sel_block, cfg.top_n, cfg.n_local)
+    rerun, acc = check_nsa_idx(gidx, ora, rows_t, cfg.sel_block, cfg.top_n, cfg.n_local,
+                               cfg.top_p)
     ref = ora["out"].copy()
     if rerun:
         idx_in = ora["idx"].copy()
@@ -82,6 +84,14 @@ DECODE_CASES = [
     # 128 compressed tokens fill two tiles exactly; the last block's only visible token is the
     # carry out of the last tile
     ("G4_D128_tile_edge", 2, 2064, 1, 4, 128, [2064, 2063], {}),
+    # adaptive top-p, also on sequences short enough for every block to fit
+    ("topp0.3_G16_D128", 4, 2000, 2, 16, 128, [2000, 1500, 777, 64], dict(top_p=0.3)),
+    ("topp0.5_G8_D128_short", 6, 700, 1, 8, 128, [1, 31, 32, 33, 65, 700], dict(top_p=0.5)),
+    ("topp0.9_G4_D64", 3, 3000, 3, 4, 64, [3000, 2999, 1025], dict(top_p=0.9)),
+    ("topp0.5_G2_D128_top5", 2, 4100, 1, 2, 128, [4100, 4096],
+     dict(top_p=0.5, top_n=5, n_local=1, window=64)),
+    ("topp1_G1_D64_block128", 2, 2500, 2, 1, 64, [2500, 1300],
+     dict(top_p=1.0, sel_block=128, top_n=6, window=200)),
 ]
 
 

@@ -29,7 +29,8 @@ def to_dev(a):
 def run_gpu_prefill(cfg, x):
     nsa = _nsa()
     c = nsa.NsaConfig(cfg.B, cfg.T, cfg.Hkv, cfg.G, cfg.D, cfg.cmp_len, cfg.cmp_stride,
-                      cfg.sel_block, cfg.top_n, cfg.n_local, cfg.window, cfg.scale)
+                      cfg.sel_block, cfg.top_n, cfg.n_local, cfg.window, cfg.scale,
+                      cfg.top_p)
     d = {k: to_dev(v) for k, v in x.items()}
     out, idx = nsa.nsa_prefill(c, d["q"], d["k"], d["v"], d["wk"], d["wv"], d["gate"])
     torch.cuda.synchronize()
@@ -42,7 +43,8 @@ def compare_prefill(cfg, x, rows_b, rows_t, gout, gidx, what):
     ora = O.nsa_prefill_rows(cfg, x["q"], x["k"], x["v"], kc, vc, x["gate"], rows_b, rows_t,
                              want_scores=True)
     gi = gidx[rows_b, rows_t]
-    rerun, accepted = check_nsa_idx(gi, ora, rows_t, cfg.sel_block, cfg.top_n, cfg.n_local)
+    rerun, accepted = check_nsa_idx(gi, ora, rows_t, cfg.sel_block, cfg.top_n, cfg.n_local,
+                                    cfg.top_p)
     ref = ora["out"].copy()
     if rerun:
         rr = np.array(rerun)
@@ -67,6 +69,13 @@ CASES = [
     ("G2_D64_top5", 1, 1100, 3, 2, 64, dict(top_n=5, n_local=1)),
     ("G1_D64_nolocal", 2, 700, 2, 1, 64, dict(top_n=4, n_local=0, window=100)),
     ("G16_D64_block128", 1, 1300, 1, 16, 64, dict(sel_block=128, top_n=6, window=200)),
+    # adaptive top-p: the number of blocks taken varies from the forced three to the cap
+    ("topp0.3_G4_D64", 1, 2048, 1, 4, 64, dict(top_p=0.3)),
+    ("topp0.5_G16_D128", 2, 1300, 2, 16, 128, dict(top_p=0.5)),
+    ("topp0.9_G8_D128", 1, 1500, 2, 8, 128, dict(top_p=0.9)),
+    ("topp0.5_G2_D64_block128", 1, 1500, 2, 2, 64, dict(top_p=0.5, sel_block=128, top_n=6,
+                                                        window=200)),
+    ("topp1_G1_D64_nolocal", 2, 700, 2, 1, 64, dict(top_p=1.0, top_n=4, n_local=0, window=100)),
 ]
 
 

@@ -307,6 +307,100 @@ def test_selection_with_integer_score_ties_brute_force():
         assert [j for j in r["idx"][a, 0] if j >= 0] == ref
 
 
+def brute_force_top_p(S_row, b, n, n_local, p):
+    """Adaptive cut by enumeration: among the sets of free blocks (at most n - |forced|) whose
+    importance together with the forced blocks' reaches p * M (M = total importance), the
+    smallest size wins, then the largest sum, then the smallest index list; when no set
+    reaches p * M, the cap-sized best set is taken."""
+    forced = {0} | {j for j in range(b - n_local + 1, b + 1) if j >= 0}
+    free = [j for j in range(b + 1) if j not in forced]
+    M = sum(S_row[:b + 1])
+    fm = sum(S_row[j] for j in forced)
+    cap = min(n - len(forced), len(free))
+    for size in range(cap + 1):
+        best = None
+        for comb in itertools.combinations(free, size):
+            sc = sum(S_row[j] for j in comb)
+            key = (-sc, sorted(comb))
+            if best is None or key < best[0]:
+                best = (key, comb)
+        if fm - best[0][0] >= p * M or size == cap:
+            return sorted(forced | set(best[1]))
+
+
+@pytest.mark.parametrize("p", [0.3, 0.6, 0.9, 1.0])
+def test_top_p_matches_brute_force_enumeration(p):
+    """Top-p selection against the enumeration of every candidate set (rows with few blocks,
+    so also the rows where every block would fit under the fixed rule)."""
+    cfg, x = small_nsa(seed=25, T=640, Hkv=2, G=2, D=16, top_n=6, n_local=1, top_p=p)
+    rows = np.array([63, 64, 200, 383, 450, 575, 639])
+    r = run_rows(cfg, x, rows=rows, want_scores=True)
+    for a, t in enumerate(rows):
+        b = t // cfg.sel_block
+        for g in range(cfg.Hkv):
+            ref = brute_force_top_p(r["scores"][a, g], b, cfg.top_n, cfg.n_local, p)
+            got = [j for j in r["idx"][a, g] if j >= 0]
+            assert got == ref, (p, t, g, got, ref)
+            assert (r["idx"][a, g, len(got):] == -1).all()
+
+
+def test_top_p_one_equals_fixed_top_n_and_sets_are_nested():
+    """p = 1 keeps taking blocks until the cap (every free block carries mass here), so it
+    equals the fixed top-n rule on rows with more blocks than top_n; the selected sets grow
+    with p; a tiny p keeps only the forced blocks."""
+    cfg0, x = small_nsa(seed=26, T=2000, Hkv=2, G=4, D=16)
+    rows = np.array([700, 1100, 1500, 1999])
+    fixed = run_rows(cfg0, x, rows=rows, want_scores=True)
+    prev = None
+    for p in [1e-9, 0.2, 0.5, 0.8, 0.95, 1.0]:
+        cfg = O.NsaCfg(1, cfg0.T, cfg0.Hkv, cfg0.G, cfg0.D, top_p=p)
+        r = run_rows(cfg, x, rows=rows)
+        sets = [[set(j for j in r["idx"][a, g] if j >= 0) for g in range(cfg.Hkv)]
+                for a in range(len(rows))]
+        if p == 1e-9:
+            for a, t in enumerate(rows):
+                b = t // 64
+                for g in range(cfg.Hkv):
+                    assert sets[a][g] == {0, b - 1, b}
+        if p == 1.0:
+            assert (fixed["scores"][:, :, :] >= 0).all()
+            assert np.array_equal(r["idx"], fixed["idx"])
+        if prev is not None:
+            for a in range(len(rows)):
+                for g in range(cfg.Hkv):
+                    assert prev[a][g] <= sets[a][g], (p, a, g)
+        prev = sets
+
+
+def test_top_p_concentrated_attention_takes_one_free_block():
+    """Compressed keys all zero except one whose span lies inside free block 5, which every
+    head's query matches strongly: nearly all importance lands on block 5, so p = 0.5 takes
+    exactly the forced blocks plus block 5, and the fixed rule still takes top_n blocks."""
+    T, D, G = 1500, 16, 2
+    cfg, x = small_nsa(seed=27, T=T, Hkv=1, G=G, D=D, top_p=0.5)
+    x = dict(x)
+    x["k"] = np.zeros_like(x["k"])
+    # compressed token i = 21 covers tokens 336..367, inside block 5 (320..383); a mean-pool
+    # compressor turns keys of value 8 on those tokens into a compressed key of 8 at i = 21
+    # (its neighbours i = 20, 22 overlap it by half and get 4)
+    kk = np.zeros((T, D), np.float32)
+    kk[336:368, 0] = 8.0
+    x["k"] = np.broadcast_to(S.f32_to_bf16_bits(kk), x["k"].shape).copy()
+    q = np.zeros((T, G, D), np.float32)
+    q[:, :, 0] = 8.0
+    x["q"] = S.f32_to_bf16_bits(q).reshape(x["q"].shape)
+    rows = np.array([1400, 1499])
+    wk = S.mean_pool_weights(cfg.cmp_len, D)
+    r = run_rows(cfg, x, rows=rows, wk=wk, want_scores=True)
+    for a, t in enumerate(rows):
+        b = t // 64
+        assert r["scores"][a, 0, 5] > 0.9 * G
+        assert [j for j in r["idx"][a, 0] if j >= 0] == [0, 5, b - 1, b]
+    cfg_fixed = O.NsaCfg(1, T, 1, G, D)
+    rf = run_rows(cfg_fixed, x, rows=rows, wk=wk)
+    assert (rf["idx"] >= 0).all()
+
+
 def test_head_permutation_inside_group_keeps_scores():
     cfg, x = small_nsa(seed=23, T=512, Hkv=2, G=4, D=16)
     r1 = run_rows(cfg, x, rows=np.array([511, 300]), want_scores=True)

@@ -63,6 +63,12 @@ EXPORTS = {
     "nsa_decode": (ctypes.c_int, [ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p]),
     "nsa_decode_timed": (ctypes.c_int, [ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p,
                                                                  ctypes.c_void_p]),
+    "nsa_cache_append_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
+    "nsa_cache_append": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 10
+                         + [ctypes.c_size_t, ctypes.c_void_p]),
+    "nsa_prefill_chunk_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
+    "nsa_prefill_chunk": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
+                          + [ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p]),
     "moba_prefill": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p]),
     "moba_prefill_timed": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p,
                                                                   ctypes.c_void_p]),
@@ -337,6 +343,63 @@ def nsa_decode(cfg: NsaConfig, q, kcache, vcache, kcmp, vcmp, seqlens, gate, out
         None if sel_idx is None else _dev(sel_idx, "sel_idx", (torch.int32,), (B, Hkv, cfg.top_n)),
         ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream), *extra)
     _check(st, "nsa_decode")
+    return out, sel_idx
+
+
+def nsa_cache_append(cfg: NsaConfig, k_new, v_new, seqlens, wk, wv, kcache, vcache, kcmp,
+                     vcmp, ws=None, stream=None):
+    """Append k_new/v_new [B,Hkv,C,D] at positions seqlens[b] .. seqlens[b]+C-1 (seqlens: the
+    lengths BEFORE the append, not updated) and emit the compressed tokens they complete into
+    kcmp [B,Hkv,ncmp,D] and vcmp [B,Hkv,ncmp_tiles,D,64].  cfg.T is the cache capacity."""
+    torch = _torch()
+    lib = load_library()
+    c = cfg.c()
+    B, L, Hkv, D = cfg.B, cfg.T, cfg.Hkv, cfg.D
+    if k_new.dim() != 4:
+        raise ValueError("k_new must be [B, Hkv, C, D]")
+    C = int(k_new.shape[2])
+    bt = _bf16_types()
+    ws = _workspace(lib.nsa_cache_append_workspace_bytes(ctypes.byref(c)), k_new.device, ws)
+    st = lib.nsa_cache_append(
+        ctypes.byref(c), C, _dev(k_new, "k_new", bt, (B, Hkv, C, D)),
+        _dev(v_new, "v_new", bt, (B, Hkv, C, D)), _dev(seqlens, "seqlens", (torch.int32,), (B,)),
+        _dev(wk, "wk", bt, (cfg.cmp_len, D, D)), _dev(wv, "wv", bt, (cfg.cmp_len, D, D)),
+        _dev(kcache, "kcache", bt, (B, Hkv, L, D)), _dev(vcache, "vcache", bt, (B, Hkv, L, D)),
+        _dev(kcmp, "kcmp", bt, (B, Hkv, cfg.ncmp, D)),
+        _dev(vcmp, "vcmp", bt, (B, Hkv, cfg.ncmp_tiles, D, 64)),
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream))
+    _check(st, "nsa_cache_append")
+
+
+def nsa_prefill_chunk(cfg: NsaConfig, P: int, q, kcache, vcache, kcmp, vcmp, gate, out=None,
+                      sel_idx=None, ws=None, want_idx=True, stream=None):
+    """Query positions P .. P+C-1 (C = q.shape[1]) against the caches (cfg.T = capacity).
+    Returns (out fp32 [B,C,Hq,D], sel_idx int32 [B,C,Hkv,top_n])."""
+    torch = _torch()
+    lib = load_library()
+    c = cfg.c()
+    B, L, Hkv, Hq, D = cfg.B, cfg.T, cfg.Hkv, cfg.Hq, cfg.D
+    if q.dim() != 4:
+        raise ValueError("q must be [B, C, Hq, D]")
+    C = int(q.shape[1])
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, C, Hq, D), dtype=torch.float32, device=dev)
+    if want_idx and sel_idx is None:
+        sel_idx = torch.empty((B, C, Hkv, cfg.top_n), dtype=torch.int32, device=dev)
+    ws = _workspace(lib.nsa_prefill_chunk_workspace_bytes(ctypes.byref(c)), dev, ws)
+    bt = _bf16_types()
+    st = lib.nsa_prefill_chunk(
+        ctypes.byref(c), int(P), C, _dev(q, "q", bt, (B, C, Hq, D)),
+        _dev(kcache, "kcache", bt, (B, Hkv, L, D)), _dev(vcache, "vcache", bt, (B, Hkv, L, D)),
+        _dev(kcmp, "kcmp", bt, (B, Hkv, cfg.ncmp, D)),
+        _dev(vcmp, "vcmp", bt, (B, Hkv, cfg.ncmp_tiles, D, 64)),
+        _dev(gate, "gate", (torch.float32,), (B, C, Hq, 3)),
+        _dev(out, "out", (torch.float32,), (B, C, Hq, D)),
+        None if sel_idx is None else _dev(sel_idx, "sel_idx", (torch.int32,),
+                                          (B, C, Hkv, cfg.top_n)),
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream))
+    _check(st, "nsa_prefill_chunk")
     return out, sel_idx
 
 

@@ -318,6 +318,7 @@ static int prefill_run(const nsa_config* c, unsigned stages, const void* q, cons
   a.out = out;
   a.idx = idx;
   a.B = c->B; a.T = c->T; a.Hkv = c->Hkv; a.G = c->G; a.D = c->D;
+  a.q0 = 0; a.nq = c->T; a.ldk = c->T;
   a.l = c->cmp_len; a.d = c->cmp_stride; a.beta = c->sel_block; a.top_n = c->top_n;
   a.n_local = c->n_local; a.window = c->window; a.top_p = c->top_p;
   a.ncmp = p.ncmp; a.NCP = p.NCP; a.TP = p.TP; a.nblk = p.nblk;
@@ -363,6 +364,101 @@ int nsa_prefill_timed(const nsa_config* c, const void* q, const void* k, const v
   for (int i = 0; i <= NSA_PREFILL_NSTAGES; ++i)
     if (events[i] == nullptr) return NSA_ERR_INVALID_ARG;
   return prefill_impl(c, q, k, v, wk, wv, gate, out, sel_idx, ws, ws_bytes, stream, events);
+}
+
+size_t nsa_prefill_chunk_workspace_bytes(const nsa_config* cfg) {
+  return nsa_prefill_workspace_bytes(cfg);  // sized for a chunk ending at the capacity
+}
+
+int nsa_prefill_chunk(const nsa_config* c, int32_t P, int32_t C, const void* q,
+                      const void* kcache, const void* vcache, const void* kcmp,
+                      const void* vcmp, const float* gate, float* out, int32_t* sel_idx,
+                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_nsa(c);
+  if (st != NSA_OK) return st;
+  if (P < 0 || C <= 0 || (long)P + C > c->T) return NSA_ERR_INVALID_ARG;
+  if (P % 64 != 0) return NSA_ERR_UNSUPPORTED;
+  const int Tend = P + C;
+  const int ncmp = nsa_num_compressed(Tend, c->cmp_len, c->cmp_stride);
+  if (!q || !kcache || !vcache || !gate || !out || !ws || (ncmp > 0 && (!kcmp || !vcmp)))
+    return NSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(kcmp) ||
+      !aligned16(vcmp) || !aligned16(gate) || !aligned16(out) || !aligned16(ws) ||
+      (sel_idx && !aligned16(sel_idx)))
+    return NSA_ERR_INVALID_ARG;
+  const PrefillPlan p = plan_prefill(c);
+  if (ws_bytes < p.total) return NSA_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(base + p.vt);
+  uint16_t* kcb = reinterpret_cast<uint16_t*>(base + p.kc);
+  uint16_t* vct = reinterpret_cast<uint16_t*>(base + p.vct);
+  const int BH = c->B * c->Hkv;
+  const int ncap = nsa_num_compressed(c->T, c->cmp_len, c->cmp_stride);
+  PrefillArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(kcache);
+  a.vt = vt;
+  a.kc = kcb;
+  a.vct = vct;
+  a.gate = gate;
+  a.out = out;
+  a.idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(base + p.idx);
+  a.B = c->B; a.T = Tend; a.Hkv = c->Hkv; a.G = c->G; a.D = c->D;
+  a.q0 = P; a.nq = C; a.ldk = c->T;
+  a.l = c->cmp_len; a.d = c->cmp_stride; a.beta = c->sel_block; a.top_n = c->top_n;
+  a.n_local = c->n_local; a.window = c->window; a.top_p = c->top_p;
+  a.ncmp = ncmp; a.NCP = round64(ncmp); a.TP = round64(Tend);
+  a.nblk = (Tend + c->sel_block - 1) / c->sel_block;
+  a.scale_log2 = c->scale * 1.4426950408889634f;
+  a.fuse_window = 1;
+  (void)hipGetLastError();
+  launch_transpose(static_cast<const uint16_t*>(vcache), vt, BH, Tend, c->D, a.TP, stream, c->T);
+  launch_cmp_cache_layout(static_cast<const uint16_t*>(kcmp), static_cast<const uint16_t*>(vcmp),
+                          kcb, vct, BH, c->D, ncap, (ncap + 63) / 64, ncmp, a.NCP, stream);
+  launch_cmp_select(a, stream);
+  launch_selected(a, stream);
+  return hip_status();
+}
+
+size_t nsa_cache_append_workspace_bytes(const nsa_config* c) {
+  if (check_compress(c) != NSA_OK) return 0;
+  return 2 * align_up((size_t)c->cmp_len * c->D * c->D * 2);
+}
+
+int nsa_cache_append(const nsa_config* c, int32_t C, const void* k_new, const void* v_new,
+                     const int32_t* seqlens, const void* wk, const void* wv, void* kcache,
+                     void* vcache, void* kcmp, void* vcmp, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  int st = check_compress(c);
+  if (st != NSA_OK) return st;
+  if (C <= 0 || C > c->T) return NSA_ERR_INVALID_ARG;
+  const int ncap = nsa_num_compressed(c->T, c->cmp_len, c->cmp_stride);
+  if (!k_new || !v_new || !seqlens || !kcache || !vcache ||
+      (ncap > 0 && (!wk || !wv || !kcmp || !vcmp || !ws)))
+    return NSA_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(seqlens) || !aligned16(kcache) ||
+      !aligned16(vcache) || !aligned16(wk) || !aligned16(wv) || !aligned16(kcmp) ||
+      !aligned16(vcmp) || !aligned16(ws))
+    return NSA_ERR_INVALID_ARG;
+  if (ncap > 0 && ws_bytes < nsa_cache_append_workspace_bytes(c)) return NSA_ERR_WORKSPACE;
+  const int BH = c->B * c->Hkv, LD = c->cmp_len * c->D;
+  uint16_t* kc16 = static_cast<uint16_t*>(kcache);
+  uint16_t* vc16 = static_cast<uint16_t*>(vcache);
+  (void)hipGetLastError();
+  launch_append_rows(static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                     kc16, vc16, seqlens, BH, c->Hkv, C, c->T, c->D, stream);
+  if (ncap > 0) {
+    uint16_t* wkt = static_cast<uint16_t*>(ws);
+    uint16_t* wvt = wkt + align_up((size_t)LD * c->D * 2) / 2;
+    launch_transpose(static_cast<const uint16_t*>(wk), wkt, 1, LD, c->D, LD, stream);
+    launch_transpose(static_cast<const uint16_t*>(wv), wvt, 1, LD, c->D, LD, stream);
+    launch_compress(kc16, wkt, static_cast<uint16_t*>(kcmp), nullptr, BH, c->T, c->D,
+                    c->cmp_len, c->cmp_stride, ncap, ncap, 0, false, stream, seqlens, C, c->Hkv);
+    launch_compress(vc16, wvt, nullptr, static_cast<uint16_t*>(vcmp), BH, c->T, c->D,
+                    c->cmp_len, c->cmp_stride, ncap, 0, 64 * ((ncap + 63) / 64), true, stream,
+                    seqlens, C, c->Hkv);
+  }
+  return hip_status();
 }
 
 size_t nsa_decode_workspace_bytes(const nsa_config* cfg) {

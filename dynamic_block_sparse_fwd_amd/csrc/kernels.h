@@ -7,21 +7,28 @@
 namespace nsa {
 
 struct PrefillArgs {
-  const uint16_t* q;    // [B, T, Hq, D]
-  const uint16_t* k;    // [B, Hkv, T, D]
+  const uint16_t* q;    // [B, nq, Hq, D]
+  const uint16_t* k;    // [B, Hkv, ldk, D]
   const uint16_t* vt;   // [B, Hkv, D, TP]  values, keys contiguous, zero past T
   const uint16_t* kc;   // [B, Hkv, NCP, D] compressed keys, zero rows past n_cmp
   const uint16_t* vct;  // [B, Hkv, D, NCP] compressed values (transposed), zero past n_cmp
-  const float* gate;    // [B, T, Hq, 3]
-  float* out;           // [B, T, Hq, D]
-  int32_t* idx;         // [B, T, Hkv, top_n]
-  int B, T, Hkv, G, D;
+  const float* gate;    // [B, nq, Hq, 3]
+  float* out;           // [B, nq, Hq, D]
+  int32_t* idx;         // [B, nq, Hkv, top_n]
+  int B, T, Hkv, G, D;  // T: end of the query rows (keys 0 .. T-1 exist)
+  int q0, nq;           // query rows q0 .. q0+nq-1 = T-1; q/gate/out/idx hold row t at t - q0
+  int ldk;              // rows per (sequence, KV head) slab of k (T, or a cache's capacity)
   int l, d, beta, top_n, n_local, window;
   int ncmp, NCP, TP, nblk;
   float scale_log2;     // softmax scale * log2(e)
   float top_p;          // 0: fixed top_n; else the adaptive cut at top_p * G
   int fuse_window;      // cmp_select also runs the window branch and writes out once
 };
+
+// Row of q/gate/out/idx holding query position t of sequence b.
+__device__ __forceinline__ long prow(const PrefillArgs& a, int b, int t) {
+  return (long)b * a.nq + (t - a.q0);
+}
 
 struct DecodeArgs {
   const uint16_t* q;       // [B, Hq, D]
@@ -84,18 +91,35 @@ void launch_moba(const MobaArgs& a, hipStream_t s, hipEvent_t* ev);
 // p[0 .. n) = 0 (n a multiple of 4, p 16-byte aligned); a kernel, so it may be captured.
 void launch_fill_zero(float* p, size_t n, hipStream_t s);
 
-// x [BH, rows, cols] -> xt [BH, cols, rows_pad] (bf16), zero-filled for rows..rows_pad-1;
-// cols and rows_pad multiples of 64, x and xt 16-byte aligned.
+// x [BH, ld_rows, cols] (first `rows` rows used) -> xt [BH, cols, rows_pad] (bf16),
+// zero-filled for rows..rows_pad-1; cols and rows_pad multiples of 64, x and xt 16-byte
+// aligned.  ld_rows < 0 means rows.
 void launch_transpose(const uint16_t* x, uint16_t* xt, int BH, int rows, int cols, int rows_pad,
-                      hipStream_t s);
+                      hipStream_t s, int ld_rows = -1);
 
 // Compressed tokens of x [BH, T, D] with the transposed weight wt [D, l*D]:
 //   xc  (nullable) [BH, rows_alloc, D] row-major, rows n_cmp..rows_alloc-1 zero;
 //   xct (nullable) [BH, D, ncp] transposed, or with `tiled` [BH, ncp / 64, D, 64] (64-token
 //       tiles, each feature-major); columns n_cmp..ncp-1 zero.
+// Append mode (seqlens non-null, Hkv heads per sequence): only the compressed tokens completed
+// by appending C tokens to sequence b, i.e. n_cmp(seqlens[b]) <= i < n_cmp(seqlens[b] + C)
+// (and i < ncmp), are computed and written; no other row is touched.
 void launch_compress(const uint16_t* x, const uint16_t* wt, uint16_t* xc, uint16_t* xct, int BH,
                      int T, int D, int l, int d, int ncmp, int rows_alloc, int ncp, bool tiled,
-                     hipStream_t s);
+                     hipStream_t s, const int32_t* seqlens = nullptr, int C = 0, int Hkv = 1);
+
+// Cache append: rows seqlens[b] .. seqlens[b]+C-1 of kc/vc [BH, L, D] <- k_new/v_new
+// [BH, C, D] (rows at or past L are dropped).
+void launch_append_rows(const uint16_t* k_new, const uint16_t* v_new, uint16_t* kcache,
+                        uint16_t* vcache, const int32_t* seqlens, int BH, int Hkv, int C, int L,
+                        int D, hipStream_t s);
+
+// Compressed caches to the prefill layouts: keys [BH, ncap, D] -> kco [BH, NCP, D]; values in
+// 64-token tiles [BH, ntcap, D, 64] -> vcto [BH, D, NCP]; tokens ncmp..NCP-1 written as zero
+// (whatever the caches hold there).
+void launch_cmp_cache_layout(const uint16_t* kc, const uint16_t* vtiles, uint16_t* kco,
+                             uint16_t* vcto, int BH, int D, int ncap, int ntcap, int ncmp,
+                             int NCP, hipStream_t s);
 
 // Compressed attention (lse pass + probability pass), block importance, group selection;
 // writes out = gate_cmp * o_cmp (+ gate_win * o_win when a.fuse_window) and idx.

@@ -13,7 +13,7 @@ constexpr int kTP = 72;  // LDS row pitch in bf16 (16-byte aligned rows)
 
 __global__ __launch_bounds__(256) void transpose_kernel(const u16* __restrict__ x,
                                                         u16* __restrict__ xt, int rows,
-                                                        int cols, int rows_pad) {
+                                                        int cols, int rows_pad, int ld_rows) {
   __shared__ __align__(16) u16 tile[64][kTP];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const long bh = blockIdx.z;
@@ -24,7 +24,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const u16* __restrict__ 
     const int r = (tid >> 3) + 32 * pass, row = r0 + r;
     u32x4 v = {0u, 0u, 0u, 0u};
     if (row < rows)
-      v = *reinterpret_cast<const u32x4*>(x + (bh * rows + row) * cols + c0 + 8 * ch);
+      v = *reinterpret_cast<const u32x4*>(x + (bh * ld_rows + row) * cols + c0 + 8 * ch);
     *reinterpret_cast<u32x4*>(&tile[r][8 * ch]) = v;
   }
   __syncthreads();
@@ -55,9 +55,76 @@ void launch_fill_zero(float* p, size_t n, hipStream_t s) {
 }
 
 void launch_transpose(const uint16_t* x, uint16_t* xt, int BH, int rows, int cols, int rows_pad,
-                      hipStream_t s) {
+                      hipStream_t s, int ld_rows) {
   dim3 grid(rows_pad / 64, cols / 64, BH);
-  transpose_kernel<<<grid, 256, 0, s>>>(x, xt, rows, cols, rows_pad);
+  transpose_kernel<<<grid, 256, 0, s>>>(x, xt, rows, cols, rows_pad, ld_rows < 0 ? rows : ld_rows);
+}
+
+// One thread per 16-byte octet of a new K row and of the matching V row.
+__global__ __launch_bounds__(256) void append_rows_kernel(const u16* __restrict__ k_new,
+                                                          const u16* __restrict__ v_new,
+                                                          u16* __restrict__ kcache,
+                                                          u16* __restrict__ vcache,
+                                                          const int32_t* __restrict__ seqlens,
+                                                          int Hkv, int C, int L, int D) {
+  const long bh = blockIdx.y;
+  const int oct = D / 8;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= C * oct) return;
+  const int r = e / oct, c = (e % oct) * 8;
+  const int pos = seqlens[bh / Hkv] + r;
+  if (pos < 0 || pos >= L) return;
+  const long src = (bh * C + r) * D + c, dst = (bh * L + pos) * D + c;
+  *reinterpret_cast<u32x4*>(kcache + dst) = *reinterpret_cast<const u32x4*>(k_new + src);
+  *reinterpret_cast<u32x4*>(vcache + dst) = *reinterpret_cast<const u32x4*>(v_new + src);
+}
+
+void launch_append_rows(const uint16_t* k_new, const uint16_t* v_new, uint16_t* kcache,
+                        uint16_t* vcache, const int32_t* seqlens, int BH, int Hkv, int C, int L,
+                        int D, hipStream_t s) {
+  const int n = C * (D / 8);
+  append_rows_kernel<<<dim3((n + 255) / 256, BH), 256, 0, s>>>(k_new, v_new, kcache, vcache,
+                                                               seqlens, Hkv, C, L, D);
+}
+
+// One workgroup per 64-token tile of one (sequence, head): the tile's key rows are copied
+// row-major, its value tile [D][64] lands in columns tile*64 .. tile*64+63 of [D, NCP].
+__global__ __launch_bounds__(256) void cmp_cache_layout_kernel(
+    const u16* __restrict__ kc, const u16* __restrict__ vtiles, u16* __restrict__ kco,
+    u16* __restrict__ vcto, int D, int ncap, int ntcap, int ncmp, int NCP) {
+  const int tile = blockIdx.x;
+  const long bh = blockIdx.y;
+  const int oct = D / 8;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int e = threadIdx.x; e < 64 * oct; e += 256) {
+    const int i = tile * 64 + e / oct, c = (e % oct) * 8;
+    u32x4 v = z;
+    if (i < ncmp) v = *reinterpret_cast<const u32x4*>(kc + (bh * ncap + i) * D + c);
+    *reinterpret_cast<u32x4*>(kco + (bh * NCP + i) * D + c) = v;
+  }
+  for (int e = threadIdx.x; e < D * 8; e += 256) {
+    const int c = e / 8, i0 = tile * 64 + (e % 8) * 8;
+    u32x4 v = z;
+    if (i0 < ncmp) {
+      v = *reinterpret_cast<const u32x4*>(vtiles + ((bh * ntcap + tile) * D + c) * 64 +
+                                          (e % 8) * 8);
+      // tokens past ncmp inside the last tile: zero, whatever the cache holds (NaN included)
+      uint32_t w[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+      for (int h = 0; h < 8; ++h)
+        if (i0 + h >= ncmp) w[h / 2] &= (h & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+      v = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    *reinterpret_cast<u32x4*>(vcto + (bh * D + c) * (long)NCP + i0) = v;
+  }
+}
+
+void launch_cmp_cache_layout(const uint16_t* kc, const uint16_t* vtiles, uint16_t* kco,
+                             uint16_t* vcto, int BH, int D, int ncap, int ntcap, int ncmp,
+                             int NCP, hipStream_t s) {
+  if (NCP <= 0) return;
+  cmp_cache_layout_kernel<<<dim3(NCP / 64, BH), 256, 0, s>>>(kc, vtiles, kco, vcto, D, ncap,
+                                                              ntcap, ncmp, NCP);
 }
 
 // Computes the transposed tile  C^T[c][i] = sum_k Wt[c][k] * X_i[k]  where X_i is the l*D
@@ -74,12 +141,25 @@ __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x
                                                        const u16* __restrict__ wt,
                                                        u16* __restrict__ xc, u16* __restrict__ xct,
                                                        int T, int l, int d, int ncmp,
-                                                       int rows_alloc, int ncp, int tiled) {
+                                                       int rows_alloc, int ncp, int tiled,
+                                                       const int32_t* __restrict__ seqlens,
+                                                       int C, int Hkv) {
   constexpr int CT = D / 64;  // 16-wide feature tiles per wave
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
   const long bh = blockIdx.y;
-  const int i0 = blockIdx.x * 64;
+  // rows computed: [ilo, ihi); everything else is only zero-filled, and not at all in append
+  // mode
+  int ilo = 0, ihi = ncmp;
+  const bool append = seqlens != nullptr;
+  if (append) {
+    const int s0 = seqlens[bh / Hkv], s1 = s0 + C;
+    ilo = s0 >= l ? (s0 - l) / d + 1 : 0;
+    ihi = s1 >= l ? (s1 - l) / d + 1 : 0;
+    ihi = ihi < ncmp ? ihi : ncmp;
+    if (ilo + (int)blockIdx.x * 64 >= ihi) return;  // uniform; nothing completed here
+  }
+  const int i0 = ilo + blockIdx.x * 64;
   const int K = l * D;
   const u16* xb = x + bh * (long)T * D;
 
@@ -89,12 +169,12 @@ __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = zero4();
 
-  if (ncmp > 0) {
+  if (ihi > 0) {
     long xrow[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       int i = i0 + it * 16 + r16;
-      i = i < ncmp ? i : ncmp - 1;  // clamp: rows past n_cmp are computed and discarded
+      i = i < ihi ? i : ihi - 1;  // clamp: rows past ihi are computed and discarded
       xrow[it] = (long)i * d * D;
     }
     const u16* wrow[CT];
@@ -118,7 +198,7 @@ __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x
   // by fp32, so the whole wave recomputes that element in fp64 (exact products, fp64 sum) and
   // replaces it by its round-to-odd fp32 image, whose bf16 rounding equals the correctly
   // rounded fp64 value.  Every other element already rounds like the exact sum.
-  if (ncmp > 0) {
+  if (ihi > 0) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -128,7 +208,7 @@ __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x
           const float v = acc[ct][it][e];
           const float mid = __uint_as_float((__float_as_uint(v) & 0xFFFF0000u) | 0x8000u);
           const float tol = kMidTol * fmaxf(1.f, fabsf(v));
-          uint64_t pending = __ballot(fabsf(v - mid) < tol && (i0 + it * 16 + r16) < ncmp);
+          uint64_t pending = __ballot(fabsf(v - mid) < tol && (i0 + it * 16 + r16) < ihi);
           while (pending) {
             const int src = __builtin_ctzll(pending);
             pending &= pending - 1;
@@ -157,17 +237,17 @@ __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int i = i0 + it * 16 + r16;
-      const bool live = i < ncmp;
+      const bool live = i < ihi;
       u16 h[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) h[e] = live ? f32_to_bf16(acc[ct][it][e]) : (u16)0;
-      if (xc != nullptr && i < rows_alloc) {
+      if (xc != nullptr && i < rows_alloc && (live || !append)) {
         uint2 pk;
         pk.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
         pk.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
         *reinterpret_cast<uint2*>(xc + (bh * rows_alloc + i) * D + c) = pk;
       }
-      if (xct != nullptr && i < ncp) {
+      if (xct != nullptr && i < ncp && (live || !append)) {
         // feature-major [D, ncp], or in 64-token tiles [ncp / 64, D, 64]
         const long o = tiled ? ((bh * (ncp >> 6) + (i >> 6)) * D + c) * 64 + (i & 63)
                              : (bh * D + c) * (long)ncp + i;
@@ -181,16 +261,18 @@ __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x
 
 void launch_compress(const uint16_t* x, const uint16_t* wt, uint16_t* xc, uint16_t* xct, int BH,
                      int T, int D, int l, int d, int ncmp, int rows_alloc, int ncp, bool tiled,
-                     hipStream_t s) {
+                     hipStream_t s, const int32_t* seqlens, int C, int Hkv) {
   int rows = rows_alloc > ncp ? rows_alloc : ncp;
+  // append mode: at most C / d + 1 tokens are completed per sequence
+  if (seqlens != nullptr) rows = C / d + 1 < ncmp ? C / d + 1 : ncmp;
   if (rows <= 0) return;
   dim3 grid((rows + 63) / 64, BH);
   if (D == 128)
     compress_kernel<128><<<grid, 256, 0, s>>>(x, wt, xc, xct, T, l, d, ncmp, rows_alloc, ncp,
-                                              tiled ? 1 : 0);
+                                              tiled ? 1 : 0, seqlens, C, Hkv);
   else
     compress_kernel<64><<<grid, 256, 0, s>>>(x, wt, xc, xct, T, l, d, ncmp, rows_alloc, ncp,
-                                             tiled ? 1 : 0);
+                                             tiled ? 1 : 0, seqlens, C, Hkv);
 }
 
 }  // namespace nsa

@@ -37,7 +37,7 @@ __device__ __forceinline__ void load_q_frags(const PrefillArgs& a, int b, int kv
     row_t[rt] = t;
     row_h[rt] = kvh * G + hh;
     const bool live = t < a.T;
-    const u16* qp = a.q + (((long)b * a.T + (live ? t : 0)) * Hq + kvh * G + hh) * D;
+    const u16* qp = a.q + (prow(a, b, live ? t : a.q0) * Hq + kvh * G + hh) * D;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) qf[rt][c] = live ? load8(qp + 32 * c + 8 * g4) : zero8();
   }
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
 
   const int tile = gridDim.x - 1 - blockIdx.x;  // longest rows first
   const int kvh = blockIdx.y, b = blockIdx.z;
-  const int t0 = tile * TQ;
+  const int t0 = a.q0 + tile * TQ;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
   const long bkv = (long)b * a.Hkv + kvh;
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
   for (int rt = 0; rt < RTW; ++rt) {
     const int t = row_t[rt];
     const float g0 =
-        t < a.T ? a.gate[(((long)b * a.T + t) * Hq + row_h[rt]) * 3 + 0] : 0.f;
+        t < a.T ? a.gate[(prow(a, b, t) * Hq + row_h[rt]) * 3 + 0] : 0.f;
     const bool zero = a.fuse_window && g0 == 0.f;
     ps[rt] = zero ? 0.f : 1.f;
     ef[rt] = zero ? 1.f : g0;
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
     const int kstart = t0 - a.window + 1 > 0 ? t0 - a.window + 1 : 0;
     const int kw0 = kstart / 64, kw1 = tlast / 64;
     const bool alive = t0 + TQ - 1 < a.T;
-    const u16* kb = a.k + bkv * (long)a.T * D;
+    const u16* kb = a.k + bkv * (long)a.ldk * D;
     const u16* vtb = a.vt + bkv * (long)D * a.TP;
     float wm[RTW], wl[RTW];
 #pragma unroll
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
       const float L = col_sum4(wl[rt]);
       const int t = row_t[rt];
       const float g2 =
-          t < a.T ? a.gate[(((long)b * a.T + t) * Hq + row_h[rt]) * 3 + 2] : 0.f;
+          t < a.T ? a.gate[(prow(a, b, t) * Hq + row_h[rt]) * 3 + 2] : 0.f;
       const float f = L > 0.f ? g2 / (L * ef[rt]) : 0.f;
 #pragma unroll
       for (int n = 0; n < DT; ++n) O[rt][n] *= f;
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
   for (int rt = 0; rt < RTW; ++rt) {
     const int t = row_t[rt];
     if (t < a.T) {
-      const long rowoff = ((long)b * a.T + t) * Hq + row_h[rt];
+      const long rowoff = prow(a, b, t) * Hq + row_h[rt];
       const float g0 = ef[rt];
       float* op = a.out + rowoff * D;
 #pragma unroll
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
     const int t = t0 + tq;
     if (t >= a.T) break;
     const int bcur = t / a.beta, nb = bcur + 1;
-    int32_t* orow = a.idx + (((long)b * a.T + t) * a.Hkv + kvh) * a.top_n;
+    int32_t* orow = a.idx + (prow(a, b, t) * a.Hkv + kvh) * a.top_n;
     if (nb <= a.top_n && !top_p) {
       for (int e = lane; e < a.top_n; e += 64) orow[e] = e < nb ? e : -1;
       continue;
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void window_kernel(PrefillArgs a
 
   const int tile = blockIdx.x;
   const int kvh = blockIdx.y, b = blockIdx.z;
-  const int t0 = tile * TQ;
+  const int t0 = a.q0 + tile * TQ;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
   const long bkv = (long)b * a.Hkv + kvh;
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void window_kernel(PrefillArgs a
   const int kstart = t0 - a.window + 1 > 0 ? t0 - a.window + 1 : 0;
   const int kt0 = kstart / 64, kt1 = tlast / 64;
   const bool alive = t0 + TQ - 1 < a.T;
-  const u16* kb = a.k + bkv * (long)a.T * D;
+  const u16* kb = a.k + bkv * (long)a.ldk * D;
   const u16* vtb = a.vt + bkv * (long)D * a.TP;
 
   float mrun[RTW], lrun[RTW];
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void window_kernel(PrefillArgs a
     const float L = col_sum4(lrun[rt]);
     const int t = row_t[rt];
     if (t < a.T) {
-      const long rowoff = ((long)b * a.T + t) * Hq + row_h[rt];
+      const long rowoff = prow(a, b, t) * Hq + row_h[rt];
       const float gs = a.gate[rowoff * 3 + 2] / L;
       float* op = a.out + rowoff * D;
 #pragma unroll
@@ -558,12 +558,12 @@ __global__ __launch_bounds__(kSelWaves * 64, 1) void selected_kernel(PrefillArgs
   __shared__ __align__(16) u16 Vsh[kSelShared][D][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
-  const int ntb = (a.T + kSelWaves - 1) / kSelWaves;
+  const int ntb = (a.nq + kSelWaves - 1) / kSelWaves;
   const int per_xcd = gridDim.x / 8;  // the grid is padded to a multiple of 8
   const int w = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   const int stream = w / ntb;
   if (stream >= a.B * a.Hkv) return;  // uniform
-  const int t0 = (w % ntb) * kSelWaves;
+  const int t0 = a.q0 + (w % ntb) * kSelWaves;
   const int t = t0 + wave;
   const bool act = t < a.T;
   const int kvh = stream % a.Hkv, b = stream / a.Hkv;
@@ -572,7 +572,7 @@ __global__ __launch_bounds__(kSelWaves * 64, 1) void selected_kernel(PrefillArgs
   const bool hlive = r16 < G;
   const int head = kvh * G + (hlive ? r16 : 0);
   const float sl = a.scale_log2;
-  const u16* kb = a.k + bkv * (long)a.T * D;
+  const u16* kb = a.k + bkv * (long)a.ldk * D;
   const u16* vtb = a.vt + bkv * (long)D * a.TP;
 
   // The workgroup's shared tiles: tiles of the current block up to t0, of the other local
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(kSelWaves * 64, 1) void selected_kernel(PrefillArgs
   int my_key0 = -1;
   if (act) {
     const int per = a.beta >> 6;
-    const int32_t* irow = a.idx + (((long)b * a.T + t) * a.Hkv + kvh) * a.top_n;
+    const int32_t* irow = a.idx + (prow(a, b, t) * a.Hkv + kvh) * a.top_n;
     if (lane < a.top_n * per) {
       const int j = irow[lane / per];
       const int k0 = j * a.beta + 64 * (lane % per);
@@ -610,7 +610,7 @@ __global__ __launch_bounds__(kSelWaves * 64, 1) void selected_kernel(PrefillArgs
 
   bf16x8 qf[D / 32];
   {
-    const u16* qp = a.q + (((long)b * a.T + (act ? t : 0)) * Hq + head) * D;
+    const u16* qp = a.q + (prow(a, b, act ? t : a.q0) * Hq + head) * D;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) qf[c] = hlive ? load8(qp + 32 * c + 8 * g4) : zero8();
   }
@@ -742,7 +742,7 @@ __global__ __launch_bounds__(kSelWaves * 64, 1) void selected_kernel(PrefillArgs
 
   const float L = col_sum4(lrun);
   if (hlive) {
-    const long rowoff = ((long)b * a.T + t) * Hq + head;
+    const long rowoff = prow(a, b, t) * Hq + head;
     const float gs = L > 0.f ? a.gate[rowoff * 3 + 1] / L : 0.f;
     float* op = a.out + rowoff * D;
 #pragma unroll
@@ -778,7 +778,7 @@ size_t cmp_select_lds_bytes(int G, int nblk) {
 template <int D, int G>
 static void launch_prefill_all(const PrefillArgs& a, int which, hipStream_t s) {
   using QT = QTile<G>;
-  const int ntile = (a.T + QT::TQ - 1) / QT::TQ;
+  const int ntile = (a.nq + QT::TQ - 1) / QT::TQ;
   if (which == 0) {
     const size_t lds = cmp_lds<G>(a.nblk);
     const bool fast = a.beta == 4 * a.d && a.l == 2 * a.d;
@@ -797,7 +797,7 @@ static void launch_prefill_all(const PrefillArgs& a, int which, hipStream_t s) {
   } else if (which == 1) {
     window_kernel<D, G><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, 0, s>>>(a);
   } else {
-    const long nwg = (long)((a.T + kSelWaves - 1) / kSelWaves) * a.Hkv * a.B;
+    const long nwg = (long)((a.nq + kSelWaves - 1) / kSelWaves) * a.Hkv * a.B;
     selected_kernel<D, G><<<dim3((unsigned)((nwg + 7) / 8 * 8)), kSelWaves * 64, 0, s>>>(a);
   }
 }

@@ -233,6 +233,59 @@ int nsa_decode_timed(const nsa_config* cfg, const void* q, const void* kcache,
                      void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t* events);
 
 /*
+ * Cache maintenance for generation ("Native Sparse Attention" article: the whole KV cache stays
+ * in memory while decoding reads only the compressed, selected and window parts of it; its
+ * token compression emits one compressed token per d tokens once all l of its tokens exist;
+ * podcast notes EP94 section 3: long chains of thought are long decodes).  Appends C tokens to
+ * every sequence and emits the compressed tokens those tokens complete.
+ *   cfg            B, T = Lmax (cache capacity), Hkv, D, cmp_len l, cmp_stride d are used
+ *   C              tokens appended per sequence, 1 <= C <= Lmax
+ *   k_new, v_new   bf16 [B, Hkv, C, D]
+ *   seqlens        int32 [B] (device memory): tokens each sequence holds BEFORE the append; the
+ *                  new tokens go to positions seqlens[b] .. seqlens[b] + C - 1 (positions at or
+ *                  past Lmax are not written: the caller keeps seqlens[b] + C <= Lmax).  Not
+ *                  updated here.
+ *   wk, wv         bf16 [l, D, D] compressor weights (as nsa_compress)
+ *   kcache, vcache bf16 [B, Hkv, Lmax, D]           updated in place
+ *   kcmp           bf16 [B, Hkv, n_cmp(Lmax), D]     compressed keys, updated in place
+ *   vcmp           bf16 [B, Hkv, nt(Lmax), D, 64]    compressed values in tiles, updated in place
+ *   ws             at least nsa_cache_append_workspace_bytes(cfg) bytes (transposed weights)
+ * Exactly the compressed tokens i with n_cmp(seqlens[b]) <= i < n_cmp(seqlens[b] + C) are
+ * written, each equal bit for bit to nsa_compress / nsa_compress_tiles of the full cache; no
+ * other compressed token and no cache row outside the appended positions is touched.  With
+ * n_cmp(Lmax) = 0, wk, wv, kcmp, vcmp and ws may be NULL.  Errors as nsa_compress, and
+ * NSA_ERR_INVALID_ARG for C outside [1, Lmax].
+ */
+size_t nsa_cache_append_workspace_bytes(const nsa_config* cfg);
+int nsa_cache_append(const nsa_config* cfg, int32_t C, const void* k_new, const void* v_new,
+                     const int32_t* seqlens, const void* wk, const void* wv, void* kcache,
+                     void* vcache, void* kcmp, void* vcmp, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/*
+ * Chunked prefill from an existing cache: query positions P .. P + C - 1 of every sequence
+ * (the same P and C for all), with keys 0 .. P + C - 1 read from the caches (podcast notes
+ * EP94 sections 5-6, as nsa_prefill).  Row t of the outputs equals row t of an nsa_prefill of
+ * the first P + C tokens.
+ *   cfg            T = Lmax, the capacity of the caches; every other field as nsa_prefill
+ *   P              first query position, a multiple of 64 (NSA_ERR_UNSUPPORTED otherwise)
+ *   C              chunk length, P + C <= Lmax
+ *   q              bf16 [B, C, Hq, D];  gate fp32 [B, C, Hq, 3];  out fp32 [B, C, Hq, D]
+ *   kcache, vcache bf16 [B, Hkv, Lmax, D], positions 0 .. P + C - 1 valid (nsa_cache_append)
+ *   kcmp, vcmp     compressed caches in the nsa_decode layouts; tokens i < n_cmp(P + C) valid,
+ *                  the rest may hold anything
+ *   sel_idx        int32 [B, C, Hkv, top_n] or NULL
+ *   ws             at least nsa_prefill_chunk_workspace_bytes(cfg) bytes
+ * Errors as nsa_prefill (validated at T = Lmax), NSA_ERR_INVALID_ARG for P < 0, C < 1 or
+ * P + C > Lmax.
+ */
+size_t nsa_prefill_chunk_workspace_bytes(const nsa_config* cfg);
+int nsa_prefill_chunk(const nsa_config* cfg, int32_t P, int32_t C, const void* q,
+                      const void* kcache, const void* vcache, const void* kcmp,
+                      const void* vcmp, const float* gate, float* out, int32_t* sel_idx,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * MoBA prefill (podcast notes EP94 sections 9-10): per head, block keys are the mean of the
  * block's keys, the query scores past blocks by q . kbar, keeps the top_k (ties to the lower
  * index) plus its own block, and attends causally over their union with one softmax.

@@ -151,3 +151,42 @@ def test_product_path_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in txt.lower().replace("oracles", ""), f
+
+
+def test_cache_append_and_chunk_reject_before_any_launch(lib):
+    c = nsa.NsaConfig(2, 4096, 2, 4, 64).c()
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced
+    ws = 1 << 40
+    wsb = lib.nsa_cache_append_workspace_bytes(ctypes.byref(c))
+    assert wsb >= 2 * 32 * 64 * 64 * 2
+    assert lib.nsa_prefill_chunk_workspace_bytes(ctypes.byref(c)) == \
+        lib.nsa_prefill_workspace_bytes(ctypes.byref(c))
+    args = [fake] * 10
+    # C outside [1, Lmax]
+    for C in (0, -3, 4097):
+        assert lib.nsa_cache_append(ctypes.byref(c), C, *args, ws, None) == nsa.NSA_ERR_INVALID_ARG
+    # null new rows, null seqlens, small workspace, misaligned cache
+    for i in (0, 2):
+        a = list(args)
+        a[i] = None
+        assert lib.nsa_cache_append(ctypes.byref(c), 1, *a, ws, None) == nsa.NSA_ERR_INVALID_ARG
+    assert lib.nsa_cache_append(ctypes.byref(c), 1, *args, wsb - 1, None) == nsa.NSA_ERR_WORKSPACE
+    a = list(args)
+    a[5] = P(0x1008)
+    assert lib.nsa_cache_append(ctypes.byref(c), 1, *a, ws, None) == nsa.NSA_ERR_INVALID_ARG
+    cargs = [fake] * 9
+    # chunk start not a multiple of 64; negative start; empty chunk; past the capacity
+    assert lib.nsa_prefill_chunk(ctypes.byref(c), 32, 64, *cargs, ws, None) == \
+        nsa.NSA_ERR_UNSUPPORTED
+    for (p0, C) in ((-64, 64), (0, 0), (4032, 128)):
+        assert lib.nsa_prefill_chunk(ctypes.byref(c), p0, C, *cargs, ws, None) == \
+            nsa.NSA_ERR_INVALID_ARG
+    a = list(cargs)
+    a[0] = None
+    assert lib.nsa_prefill_chunk(ctypes.byref(c), 0, 64, *a, ws, None) == nsa.NSA_ERR_INVALID_ARG
+    assert lib.nsa_prefill_chunk(ctypes.byref(c), 0, 64, *cargs, 16, None) == \
+        nsa.NSA_ERR_WORKSPACE
+    bad = nsa.NsaConfig(2, 4096, 2, 3, 64).c()
+    assert lib.nsa_prefill_chunk(ctypes.byref(bad), 0, 64, *cargs, ws, None) == \
+        nsa.NSA_ERR_UNSUPPORTED

@@ -343,6 +343,43 @@ def bench_decode(args, B=32, L=65536, Hkv=4, G=16, D=128, seed=3, calls=20):
     torch.cuda.synchronize()
     plain = [ev2.elapsed_ms(2 * c, 2 * c + 1) for c in range(calls)]
     ms = float(np.median(plain))
+    # a generation step: nsa_cache_append of the newest token (here the last cached one,
+    # rewritten with its own values at position L-1, which also completes compressed token
+    # n_cmp(L) - 1: the 1-in-16 steps that emit one), then the decode
+    k_last = d["kcache"][:, :, L - 1:L].contiguous()
+    v_last = d["vcache"][:, :, L - 1:L].contiguous()
+    before = (d["seqlens"] - 1).contiguous()
+    aws = torch.empty(nsa.cache_append_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+
+    def app():
+        nsa.nsa_cache_append(cfg, k_last, v_last, before, d["wk"], d["wv"], d["kcache"],
+                             d["vcache"], kc, vc, ws=aws)
+
+    ev3 = HipEvents(3 * calls)
+    for c in range(calls):
+        flush.sum()
+        ev3.record(3 * c, stream)
+        app()
+        ev3.record(3 * c + 1, stream)
+        call()
+        ev3.record(3 * c + 2, stream)
+    torch.cuda.synchronize()
+    app_ms = float(np.median([ev3.elapsed_ms(3 * c, 3 * c + 1) for c in range(calls)]))
+    gen_ms = float(np.median([ev3.elapsed_ms(3 * c, 3 * c + 2) for c in range(calls)]))
+    # the other 15 of 16 steps: the token at L-2 (rewritten with its own values) completes no
+    # compressed token
+    k_prev = d["kcache"][:, :, L - 2:L - 1].contiguous()
+    v_prev = d["vcache"][:, :, L - 2:L - 1].contiguous()
+    before2 = (d["seqlens"] - 2).contiguous()
+    ev4 = HipEvents(2 * calls)
+    for c in range(calls):
+        flush.sum()
+        ev4.record(2 * c, stream)
+        nsa.nsa_cache_append(cfg, k_prev, v_prev, before2, d["wk"], d["wv"], d["kcache"],
+                             d["vcache"], kc, vc, ws=aws)
+        ev4.record(2 * c + 1, stream)
+    torch.cuda.synchronize()
+    app0_ms = float(np.median([ev4.elapsed_ms(2 * c, 2 * c + 1) for c in range(calls)]))
     cmp_bytes, tok_bytes = decode_kv_bytes(idx.cpu().numpy(), x["seqlens"], L, D)
     kv = cmp_bytes + tok_bytes
     med = {nm: float(np.median(v)) for nm, v in stage_ms.items()}
@@ -357,6 +394,9 @@ def bench_decode(args, B=32, L=65536, Hkv=4, G=16, D=128, seed=3, calls=20):
         "kv_gbs": round(kv / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(kv / (ms * 1e-3) / HBM_PEAK, 4),
         "stages_us": {nm: round(v * 1e3, 2) for nm, v in med.items()},
+        "append_us": round(app_ms * 1e3, 2),
+        "append_us_no_emission": round(app0_ms * 1e3, 2),
+        "generation_step_us": round(gen_ms * 1e3, 2),
         "roofline": {"bound": "hbm", "kernel": "dec_cmp (compressed-cache stream)",
                      "achieved": round(cmp_bytes / (med["cmp_stream"] * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s",
@@ -365,9 +405,85 @@ def bench_decode(args, B=32, L=65536, Hkv=4, G=16, D=128, seed=3, calls=20):
         "timing": "median of %d calls, HIP events around each call, 1 GiB read between "
                   "calls to evict the Infinity Cache" % calls,
     }
-    del d, kc, vc, out, idx, ws, flush
+    del d, kc, vc, out, idx, ws, flush, aws
     torch.cuda.empty_cache()
     return res, x
+
+
+def bench_chunked(args, B=1, Hkv=4, G=16, D=128):
+    """The 64k prefill run as a sequence of chunks from the caches: per chunk,
+    nsa_cache_append of its K/V (cache rows and the compressed tokens they complete) and
+    nsa_prefill_chunk of its query rows."""
+    import torch
+
+    import dynamic_block_sparse_fwd_amd as nsa
+    import synth_inputs as S
+
+    T, C = args.seq, args.chunk
+    cfg = nsa.NsaConfig(B, T, Hkv, G, D, top_p=args.top_p)
+    x = S.nsa_prefill_inputs(2, B, T, Hkv, G, D)
+    dev = torch.device("cuda:0")
+    d = {k: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).to(dev)
+         for k, v in x.items()}
+    del x
+    kcache = torch.zeros((B, Hkv, T, D), dtype=torch.int16, device=dev)
+    vcache = torch.zeros_like(kcache)
+    kc = torch.zeros((B, Hkv, cfg.ncmp, D), dtype=torch.int16, device=dev)
+    vc = torch.zeros((B, Hkv, cfg.ncmp_tiles, D, 64), dtype=torch.int16, device=dev)
+    starts = list(range(0, T, C))
+    kn = [d["k"][:, :, P:P + C].contiguous() for P in starts]
+    vn = [d["v"][:, :, P:P + C].contiguous() for P in starts]
+    qn = [d["q"][:, P:P + C].contiguous() for P in starts]
+    gn = [d["gate"][:, P:P + C].contiguous() for P in starts]
+    sl = [torch.full((B,), P, dtype=torch.int32, device=dev) for P in starts]
+    out = [torch.empty((B, q.shape[1], Hkv * G, D), dtype=torch.float32, device=dev) for q in qn]
+    idx = [torch.empty((B, q.shape[1], Hkv, cfg.top_n), dtype=torch.int32, device=dev)
+           for q in qn]
+    aws = torch.empty(nsa.cache_append_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    pws = torch.empty(nsa.prefill_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    n = len(starts)
+
+    def step(ev=None, base=0):
+        for i, P in enumerate(starts):
+            if ev is not None:
+                ev.record(base + 2 * i, stream)
+            nsa.nsa_cache_append(cfg, kn[i], vn[i], sl[i], d["wk"], d["wv"], kcache, vcache, kc,
+                                 vc, ws=aws)
+            if ev is not None:
+                ev.record(base + 2 * i + 1, stream)
+            nsa.nsa_prefill_chunk(cfg, P, qn[i], kcache, vcache, kc, vc, gn[i], out=out[i],
+                                  sel_idx=idx[i], ws=pws)
+        if ev is not None:
+            ev.record(base + 2 * n, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = HipEvents(args.steps * (2 * n + 1))
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev, s * (2 * n + 1))
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    app = [0.0] * n
+    pre = [0.0] * n
+    tot = 0.0
+    for s in range(args.steps):
+        b0 = s * (2 * n + 1)
+        tot += ev.elapsed_ms(b0, b0 + 2 * n) / args.steps
+        for i in range(n):
+            app[i] += ev.elapsed_ms(b0 + 2 * i, b0 + 2 * i + 1) / args.steps
+            pre[i] += ev.elapsed_ms(b0 + 2 * i + 1, b0 + 2 * i + 2) / args.steps
+    return {
+        "workload": "nsa chunked prefill B=%d T=%d Hkv=%d G=%d D=%d, chunks of %d%s" % (
+            B, T, Hkv, G, D, C, " top_p=%g" % args.top_p if args.top_p > 0 else ""),
+        "ms_per_step": round(wall * 1e3, 3),
+        "events_ms_per_step": round(tot, 3),
+        "tok_s": round(B * T / wall, 1),
+        "append_ms": [round(v, 3) for v in app],
+        "prefill_chunk_ms": [round(v, 3) for v in pre],
+    }
 
 
 def cpu_baseline_decode(x, B=32, L=65536, Hkv=4, G=16, D=128, nseq=4, reps=15):
@@ -499,7 +615,9 @@ def main():
     ap.add_argument("--no-moba", action="store_true")
     ap.add_argument("--moba-seq", type=int, default=131072,
                     help="MoBA sequence length for --only moba (beyond 128k: device-drawn inputs)")
-    ap.add_argument("--only", choices=("prefill", "decode", "moba"),
+    ap.add_argument("--chunk", type=int, default=8192,
+                    help="chunk length for --only chunked (a multiple of 64)")
+    ap.add_argument("--only", choices=("prefill", "decode", "moba", "chunked"),
                     help="run one workload and print its result alone (for profiling runs)")
     ap.add_argument("--top-p", type=float, default=0.0,
                     help="adaptive top-p block selection for the NSA workloads (0: fixed top-16)")
@@ -518,6 +636,9 @@ def main():
     if args.only == "decode":
         dec, _ = bench_decode(args)
         print(json.dumps({"decode": dec}), flush=True)
+        return
+    if args.only == "chunked":
+        print(json.dumps({"chunked": bench_chunked(args)}), flush=True)
         return
     if args.only == "moba":
         mo, _ = bench_moba(args, T=args.moba_seq)

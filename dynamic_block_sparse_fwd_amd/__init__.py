@@ -200,6 +200,10 @@ def prefill_workspace_bytes(cfg: NsaConfig) -> int:
     return load_library().nsa_prefill_workspace_bytes(ctypes.byref(cfg.c()))
 
 
+def cache_append_workspace_bytes(cfg: NsaConfig) -> int:
+    return load_library().nsa_cache_append_workspace_bytes(ctypes.byref(cfg.c()))
+
+
 def decode_workspace_bytes(cfg: NsaConfig) -> int:
     return load_library().nsa_decode_workspace_bytes(ctypes.byref(cfg.c()))
 

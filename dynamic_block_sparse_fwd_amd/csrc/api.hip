@@ -420,9 +420,14 @@ int nsa_prefill_chunk(const nsa_config* c, int32_t P, int32_t C, const void* q,
   return hip_status();
 }
 
+// Appends that complete at most this many compressed tokens per sequence-head use one
+// workgroup per token; longer ones the 64-token tile compressor.
+constexpr int kFewTokens = 4;
+
 size_t nsa_cache_append_workspace_bytes(const nsa_config* c) {
   if (check_compress(c) != NSA_OK) return 0;
-  return 2 * align_up((size_t)c->cmp_len * c->D * c->D * 2);
+  return 2 * align_up((size_t)c->cmp_len * c->D * c->D * 2) +
+         align_up(few_part_bytes(c->B * c->Hkv, c->D, c->cmp_len, kFewTokens));
 }
 
 int nsa_cache_append(const nsa_config* c, int32_t C, const void* k_new, const void* v_new,
@@ -447,7 +452,23 @@ int nsa_cache_append(const nsa_config* c, int32_t C, const void* k_new, const vo
   (void)hipGetLastError();
   launch_append_rows(static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
                      kc16, vc16, seqlens, BH, c->Hkv, C, c->T, c->D, stream);
-  if (ncap > 0) {
+  // at most C / d + 1 compressed tokens per sequence-head are completed
+  const int per = C / c->cmp_stride + 1 < ncap ? C / c->cmp_stride + 1 : ncap;
+  if (ncap > 0 && per <= kFewTokens) {
+    char* base = static_cast<char*>(ws);
+    uint16_t* wkt = reinterpret_cast<uint16_t*>(base);
+    uint16_t* wvt = reinterpret_cast<uint16_t*>(base + align_up((size_t)LD * c->D * 2));
+    float* part = reinterpret_cast<float*>(base + 2 * align_up((size_t)LD * c->D * 2));
+    launch_transpose(static_cast<const uint16_t*>(wk), wkt, 1, LD, c->D, LD, stream);
+    launch_transpose(static_cast<const uint16_t*>(wv), wvt, 1, LD, c->D, LD, stream);
+    const uint16_t* xs[2] = {kc16, vc16};
+    const uint16_t* wts[2] = {wkt, wvt};
+    uint16_t* xcs[2] = {static_cast<uint16_t*>(kcmp), nullptr};
+    uint16_t* xcts[2] = {nullptr, static_cast<uint16_t*>(vcmp)};
+    launch_compress_few(xs, wts, xcs, xcts, part, BH, c->T, c->D, c->cmp_len,
+                        c->cmp_stride, ncap, ncap, 64 * ((ncap + 63) / 64), seqlens, C, c->Hkv,
+                        per, stream);
+  } else if (ncap > 0) {
     uint16_t* wkt = static_cast<uint16_t*>(ws);
     uint16_t* wvt = wkt + align_up((size_t)LD * c->D * 2) / 2;
     launch_transpose(static_cast<const uint16_t*>(wk), wkt, 1, LD, c->D, LD, stream);

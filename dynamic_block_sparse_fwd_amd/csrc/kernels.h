@@ -108,6 +108,17 @@ void launch_compress(const uint16_t* x, const uint16_t* wt, uint16_t* xc, uint16
                      int T, int D, int l, int d, int ncmp, int rows_alloc, int ncp, bool tiled,
                      hipStream_t s, const int32_t* seqlens = nullptr, int C = 0, int Hkv = 1);
 
+// Append mode for few tokens, keys and values in one go (index 0 keys, 1 values): the same
+// tokens as launch_compress's append mode, at most `per` per sequence-head, gathered over all
+// sequence-heads into one split-K GEMM; wt the transposed weights [D, l*D]; part a workspace
+// of few_part_bytes(BH, D, l, per) bytes.
+size_t few_part_bytes(int BH, int D, int l, int per);
+void launch_compress_few(const uint16_t* const x[2], const uint16_t* const wt[2],
+                         uint16_t* const xc[2],
+                         uint16_t* const xct[2], float* part, int BH, int T, int D, int l, int d,
+                         int ncmp, int rows_alloc, int ncp, const int32_t* seqlens, int C,
+                         int Hkv, int per, hipStream_t s);
+
 // Cache append: rows seqlens[b] .. seqlens[b]+C-1 of kc/vc [BH, L, D] <- k_new/v_new
 // [BH, C, D] (rows at or past L are dropped).
 void launch_append_rows(const uint16_t* k_new, const uint16_t* v_new, uint16_t* kcache,

@@ -259,6 +259,170 @@ __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x
   }
 }
 
+// Append-time compression of the few tokens an append completes (at most `per` per
+// sequence-head): a GEMM whose rows are the completed tokens gathered over all sequence-heads,
+// so the weight is read once per 64 tokens instead of once per token.  Slot s = bh * per + q
+// stands for token n_cmp(seqlens[b]) + q of sequence-head bh (b = bh / Hkv), live while below
+// n_cmp(seqlens[b] + C).  The l*D reduction is split in `ks`-long pieces over blockIdx.y, each
+// writing fp32 partials part[split][slot][D]; compress_finish_kernel sums them in split order
+// and rounds like compress_kernel.  blockIdx.z: 0 keys, 1 values.
+struct FewArgs {
+  const u16* x[2];   // caches [BH, T, D]
+  const u16* wt[2];  // transposed weights [D, l*D]
+  u16* xc[2];        // [BH, rows_alloc, D] or null
+  u16* xct[2];       // [BH, ncp / 64, D, 64] or null
+  float* part;       // [2][nsplit][nslots][D]
+  const int32_t* seqlens;
+  int T, l, d, ncmp, rows_alloc, ncp, C, Hkv, per, nslots, ks, nsplit;
+};
+
+__device__ __forceinline__ int few_token(const FewArgs& a, int slot, int* bh_out) {
+  const int bh = slot / a.per, q = slot % a.per;
+  const int s0 = a.seqlens[bh / a.Hkv], s1 = s0 + a.C;
+  const int ilo = s0 >= a.l ? (s0 - a.l) / a.d + 1 : 0;
+  int ihi = s1 >= a.l ? (s1 - a.l) / a.d + 1 : 0;
+  ihi = ihi < a.ncmp ? ihi : a.ncmp;
+  *bh_out = bh;
+  return ilo + q < ihi ? ilo + q : -1;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void compress_split_kernel(FewArgs a) {
+  constexpr int CT = D / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const int kv = blockIdx.z;
+  const int g0 = blockIdx.x * 64, sp = blockIdx.y;
+  const int K = a.l * D;
+  const int k_lo = sp * a.ks, k_hi = k_lo + a.ks < K ? k_lo + a.ks : K;
+  {  // every wave finds the same answer: a workgroup whose 64 slots are all dead leaves
+    int bh;
+    const bool live = g0 + lane < a.nslots && few_token(a, g0 + lane, &bh) >= 0;
+    if (__ballot(live) == 0ull) return;
+  }
+  long xrow[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int slot = g0 + it * 16 + r16;
+    int bh = 0, i = -1;
+    if (slot < a.nslots) i = few_token(a, slot, &bh);
+    if (i < 0) { bh = 0; i = 0; }  // dead slot: reads tokens 0 .. l-1 of head 0, discarded
+    xrow[it] = ((long)bh * a.T + (long)i * a.d) * D;
+  }
+  const u16* xb = a.x[kv];
+  const u16* wrow[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) wrow[ct] = a.wt[kv] + (long)(wave * (D / 4) + ct * 16 + r16) * K;
+  f32x4 acc[CT][4];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) acc[ct][it] = zero4();
+  for (int k0 = k_lo; k0 < k_hi; k0 += 32) {
+    const int ko = k0 + 8 * g4;
+    bf16x8 bx[4], aw[CT];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) bx[it] = load8(xb + xrow[it] + ko);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) aw[ct] = load8(wrow[ct] + ko);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int it = 0; it < 4; ++it) acc[ct][it] = mfma16x16x32(aw[ct], bx[it], acc[ct][it]);
+  }
+  // lane holds C^T[c = base + 4*g4 + e][slot = g0 + it*16 + r16]
+  float* pb = a.part + ((long)(kv * a.nsplit + sp) * a.nslots) * D;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int slot = g0 + it * 16 + r16;
+    if (slot >= a.nslots) continue;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int c = wave * (D / 4) + ct * 16 + 4 * g4;
+      *reinterpret_cast<f32x4*>(pb + (long)slot * D + c) = acc[ct][it];
+    }
+  }
+}
+
+// One wave per (slot, 64 features): sum of the split partials in split order, then the exact
+// rounding of compress_kernel (fp64 recomputation near a bf16 rounding midpoint).
+template <int D>
+__global__ __launch_bounds__(256) void compress_finish_kernel(FewArgs a) {
+  const int kv = blockIdx.y;
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  const int slot = (int)(e / D), c = (int)(e % D);
+  const int lane = threadIdx.x & 63;
+  if (slot >= a.nslots) return;  // uniform per wave (D is a multiple of 64)
+  int bh = 0;
+  const int i = few_token(a, slot, &bh);
+  if (i < 0) return;  // uniform per wave
+  const float* pb = a.part + ((long)kv * a.nsplit * a.nslots + slot) * D + c;
+  float v = 0.f;
+  for (int sp = 0; sp < a.nsplit; ++sp) v += pb[(long)sp * a.nslots * D];
+  const int K = a.l * D;
+  const u16* xp = a.x[kv] + ((long)bh * a.T + (long)i * a.d) * D;
+  const float mid = __uint_as_float((__float_as_uint(v) & 0xFFFF0000u) | 0x8000u);
+  uint64_t pending = __ballot(fabsf(v - mid) < kMidTol * fmaxf(1.f, fabsf(v)));
+  while (pending) {  // rare: the whole wave recomputes one flagged feature in fp64
+    const int src = __builtin_ctzll(pending);
+    pending &= pending - 1;
+    const u16* wp = a.wt[kv] + (long)(c - lane + src) * K;
+    double s = 0.0;
+    for (int k = 8 * lane; k < K; k += 512) {
+      const bf16x8 xv = load8(xp + k), wv = load8(wp + k);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s += (double)(float)xv[q] * (double)(float)wv[q];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    float f = __double2float_rz(s);
+    if ((double)f != s) f = __uint_as_float(__float_as_uint(f) | 1u);  // round to odd
+    if (lane == src) v = f;
+  }
+  const u16 h = f32_to_bf16(v);
+  if (a.xc[kv] != nullptr && i < a.rows_alloc) a.xc[kv][((long)bh * a.rows_alloc + i) * D + c] = h;
+  if (a.xct[kv] != nullptr && i < a.ncp)
+    a.xct[kv][(((long)bh * (a.ncp >> 6) + (i >> 6)) * D + c) * 64 + (i & 63)] = h;
+}
+
+int few_splits(int K, int* ks) {
+  int k = (K + 15) / 16;
+  k = (k + 31) / 32 * 32;
+  *ks = k;
+  return (K + k - 1) / k;
+}
+
+size_t few_part_bytes(int BH, int D, int l, int per) {
+  int ks;
+  const int nsplit = few_splits(l * D, &ks);
+  return (size_t)2 * nsplit * BH * per * D * sizeof(float);
+}
+
+void launch_compress_few(const uint16_t* const x[2], const uint16_t* const wt[2],
+                         uint16_t* const xc[2],
+                         uint16_t* const xct[2], float* part, int BH, int T, int D, int l, int d,
+                         int ncmp, int rows_alloc, int ncp, const int32_t* seqlens, int C,
+                         int Hkv, int per, hipStream_t s) {
+  if (per <= 0 || ncmp <= 0) return;
+  FewArgs a{};
+  for (int j = 0; j < 2; ++j) {
+    a.x[j] = x[j]; a.wt[j] = wt[j]; a.xc[j] = xc[j]; a.xct[j] = xct[j];
+  }
+  a.part = part; a.seqlens = seqlens;
+  a.T = T; a.l = l; a.d = d; a.ncmp = ncmp; a.rows_alloc = rows_alloc; a.ncp = ncp;
+  a.C = C; a.Hkv = Hkv; a.per = per; a.nslots = BH * per;
+  a.nsplit = few_splits(l * D, &a.ks);
+  const dim3 g1((a.nslots + 63) / 64, a.nsplit, 2);
+  const dim3 g2((unsigned)(((long)a.nslots * D + 255) / 256), 2);
+  if (D == 128) {
+    compress_split_kernel<128><<<g1, 256, 0, s>>>(a);
+    compress_finish_kernel<128><<<g2, 256, 0, s>>>(a);
+  } else {
+    compress_split_kernel<64><<<g1, 256, 0, s>>>(a);
+    compress_finish_kernel<64><<<g2, 256, 0, s>>>(a);
+  }
+}
+
 void launch_compress(const uint16_t* x, const uint16_t* wt, uint16_t* xc, uint16_t* xct, int BH,
                      int T, int D, int l, int d, int ncmp, int rows_alloc, int ncp, bool tiled,
                      hipStream_t s, const int32_t* seqlens, int C, int Hkv) {

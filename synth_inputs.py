@@ -16,7 +16,8 @@ from __future__ import annotations
 
 import numpy as np
 
-SLOT = {"q": 0, "k": 1, "v": 2, "wk": 3, "wv": 4, "gate": 5, "plant": 6, "seqlen": 7}
+SLOT = {"q": 0, "k": 1, "v": 2, "wk": 3, "wv": 4, "gate": 5, "plant": 6, "seqlen": 7,
+        "dout": 8}
 
 
 def _gen(seed: int, slot: str) -> np.random.Generator:
@@ -47,6 +48,12 @@ def normal_bf16(seed: int, slot: str, shape, std: float = 1.0, chunk: int = 1 <<
             x *= np.float32(std)
         out[s:e] = f32_to_bf16_bits(x)
     return out.reshape(shape)
+
+
+def upstream_grad(seed: int, shape) -> np.ndarray:
+    """Gradient of the loss with respect to the layer output: N(0, 1) in fp32."""
+    g = _gen(seed, "dout")
+    return g.standard_normal(int(np.prod(shape)), dtype=np.float32).reshape(shape)
 
 
 def gates(seed: int, shape) -> np.ndarray:

@@ -69,6 +69,11 @@ EXPORTS = {
     "nsa_prefill_chunk_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
     "nsa_prefill_chunk": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
                           + [ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "nsa_backward_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
+    "nsa_backward": (ctypes.c_int, [ctypes.c_void_p] * 16 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "nsa_backward_timed": (ctypes.c_int, [ctypes.c_void_p] * 16 + [ctypes.c_size_t,
+                                                                   ctypes.c_void_p,
+                                                                   ctypes.c_void_p]),
     "moba_prefill": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p]),
     "moba_prefill_timed": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_size_t, ctypes.c_void_p,
                                                                   ctypes.c_void_p]),
@@ -405,6 +410,44 @@ def nsa_prefill_chunk(cfg: NsaConfig, P: int, q, kcache, vcache, kcmp, vcmp, gat
         ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream))
     _check(st, "nsa_prefill_chunk")
     return out, sel_idx
+
+
+BACKWARD_STAGES = ("layout", "prep", "query_major", "key_major", "compressor")
+
+
+def backward_workspace_bytes(cfg: NsaConfig) -> int:
+    return load_library().nsa_backward_workspace_bytes(ctypes.byref(cfg.c()))
+
+
+def nsa_backward(cfg: NsaConfig, q, k, v, wk, wv, gate, sel_idx, dout, grads=None, ws=None,
+                 stream=None, events=None):
+    """Gradients of sum(dout * nsa_prefill(...)) with the selection sel_idx held fixed.
+    Returns dict(dq, dk, dv, dwk, dwv, dgate) (fp32; `grads` may supply the tensors).
+    events: optional ctypes array of len(BACKWARD_STAGES) + 1 hipEvent_t."""
+    torch = _torch()
+    lib = load_library()
+    c = cfg.c()
+    B, T, Hkv, Hq, D, l = cfg.B, cfg.T, cfg.Hkv, cfg.Hq, cfg.D, cfg.cmp_len
+    dev = q.device
+    shapes = dict(dq=(B, T, Hq, D), dk=(B, Hkv, T, D), dv=(B, Hkv, T, D), dwk=(l, D, D),
+                  dwv=(l, D, D), dgate=(B, T, Hq, 3))
+    if grads is None:
+        grads = {n: torch.empty(s, dtype=torch.float32, device=dev) for n, s in shapes.items()}
+    ws = _workspace(lib.nsa_backward_workspace_bytes(ctypes.byref(c)), dev, ws)
+    bt = _bf16_types()
+    f32 = (torch.float32,)
+    fn = lib.nsa_backward if events is None else lib.nsa_backward_timed
+    extra = () if events is None else (ctypes.cast(events, ctypes.c_void_p),)
+    st = fn(
+        ctypes.byref(c), _dev(q, "q", bt, (B, T, Hq, D)), _dev(k, "k", bt, (B, Hkv, T, D)),
+        _dev(v, "v", bt, (B, Hkv, T, D)), _dev(wk, "wk", bt, (l, D, D)),
+        _dev(wv, "wv", bt, (l, D, D)), _dev(gate, "gate", f32, (B, T, Hq, 3)),
+        _dev(sel_idx, "sel_idx", (torch.int32,), (B, T, Hkv, cfg.top_n)),
+        _dev(dout, "dout", f32, (B, T, Hq, D)),
+        *[_dev(grads[n], n, f32, shapes[n]) for n in ("dq", "dk", "dv", "dwk", "dwv", "dgate")],
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream), *extra)
+    _check(st, "nsa_backward")
+    return grads
 
 
 MOBA_STAGES = ("pool_gate", "lists", "block_attn", "own_merge")

@@ -152,6 +152,42 @@ PrefillPlan plan_prefill(const nsa_config* c) {
   return p;
 }
 
+struct BackwardPlan {
+  size_t kt, kc, kct, vc, wkt, wvt, dob, dot, qt, lse, dlt, pk, pv, dkc, dvc, total;
+  int ncmp, NCP, TP, nblk, PC, NPC;
+};
+
+BackwardPlan plan_backward(const nsa_config* c) {
+  BackwardPlan p{};
+  const size_t BH = (size_t)c->B * c->Hkv, rows = (size_t)c->B * c->T * c->Hkv * c->G;
+  p.ncmp = nsa_num_compressed(c->T, c->cmp_len, c->cmp_stride);
+  p.NCP = round64(p.ncmp);
+  p.TP = round64(c->T);
+  p.nblk = (c->T + c->sel_block - 1) / c->sel_block;
+  // positions per chunk of the compressed key pass: about 16 chunks, at least 256 positions
+  p.PC = std::max(256, round64((c->T + 15) / 16));
+  p.NPC = (c->T + p.PC - 1) / p.PC;
+  const size_t cmpn = BH * (size_t)std::max(p.NCP, 64) * c->D;
+  size_t off = 0;
+  p.kt = off;  off += align_up(BH * c->D * p.TP * 2);
+  p.kc = off;  off += align_up(cmpn * 2);
+  p.kct = off; off += align_up(cmpn * 2);
+  p.vc = off;  off += align_up(cmpn * 2);
+  p.wkt = off; off += align_up((size_t)c->cmp_len * c->D * c->D * 2);
+  p.wvt = off; off += align_up((size_t)c->cmp_len * c->D * c->D * 2);
+  p.dob = off; off += align_up(rows * c->D * 2);
+  p.dot = off; off += align_up(rows * c->D * 2);
+  p.qt = off;  off += align_up(rows * c->D * 2);
+  p.lse = off; off += align_up(3 * rows * 4);
+  p.dlt = off; off += align_up(3 * rows * 4);
+  p.pk = off;  off += align_up((size_t)p.NPC * cmpn * 4);
+  p.pv = off;  off += align_up((size_t)p.NPC * cmpn * 4);
+  p.dkc = off; off += align_up(cmpn * 4);
+  p.dvc = off; off += align_up(cmpn * 4);
+  p.total = off;
+  return p;
+}
+
 struct DecodePlan {
   size_t cm, cl, co, tref, cb, idx, total;
   DecodeShape sh;
@@ -480,6 +516,92 @@ int nsa_cache_append(const nsa_config* c, int32_t C, const void* k_new, const vo
                     seqlens, C, c->Hkv);
   }
   return hip_status();
+}
+
+// The backward runs a position's 16 heads as one matrix-core tile.
+static int check_nsa_backward(const nsa_config* c) {
+  int st = check_nsa(c);
+  if (st != NSA_OK) return st;
+  if (c->G != 16) return NSA_ERR_UNSUPPORTED;
+  return NSA_OK;
+}
+
+size_t nsa_backward_workspace_bytes(const nsa_config* cfg) {
+  if (check_nsa_backward(cfg) != NSA_OK) return 0;
+  return plan_backward(cfg).total;
+}
+
+static int backward_impl(const nsa_config* c, const void* q, const void* k, const void* v,
+                         const void* wk, const void* wv, const float* gate,
+                         const int32_t* sel_idx, const float* dout, float* dq, float* dk,
+                         float* dv, float* dwk, float* dwv, float* dgate, void* ws,
+                         size_t ws_bytes, hipStream_t stream, hipEvent_t* ev) {
+  int st = check_nsa_backward(c);
+  if (st != NSA_OK) return st;
+  if (!q || !k || !v || !wk || !wv || !gate || !sel_idx || !dout || !dq || !dk || !dv || !dwk ||
+      !dwv || !dgate || !ws)
+    return NSA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, wk, wv, gate, sel_idx, dout, dq, dk, dv, dwk, dwv, dgate, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return NSA_ERR_INVALID_ARG;
+  const BackwardPlan p = plan_backward(c);
+  if (ws_bytes < p.total) return NSA_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  auto u16p = [&](size_t o) { return reinterpret_cast<uint16_t*>(base + o); };
+  auto f32p = [&](size_t o) { return reinterpret_cast<float*>(base + o); };
+  BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.wk = static_cast<const uint16_t*>(wk);
+  a.wv = static_cast<const uint16_t*>(wv);
+  a.gate = gate;
+  a.idx = sel_idx;
+  a.dout = dout;
+  a.kt = u16p(p.kt); a.kc = u16p(p.kc); a.kct = u16p(p.kct); a.vc = u16p(p.vc);
+  a.dob = u16p(p.dob); a.dot = u16p(p.dot); a.qt = u16p(p.qt);
+  a.lse = f32p(p.lse); a.dlt = f32p(p.dlt); a.pk = f32p(p.pk); a.pv = f32p(p.pv);
+  a.dkc = f32p(p.dkc); a.dvc = f32p(p.dvc);
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dwk = dwk; a.dwv = dwv; a.dgate = dgate;
+  a.B = c->B; a.T = c->T; a.Hkv = c->Hkv; a.D = c->D; a.l = c->cmp_len; a.d = c->cmp_stride;
+  a.beta = c->sel_block; a.top_n = c->top_n; a.window = c->window;
+  a.ncmp = p.ncmp; a.NCP = p.NCP; a.TP = p.TP; a.nblk = p.nblk; a.PC = p.PC; a.NPC = p.NPC;
+  a.scale = c->scale;
+  a.scale_log2 = c->scale * 1.4426950408889634f;
+  const int BH = c->B * c->Hkv, LD = c->cmp_len * c->D;
+  (void)hipGetLastError();
+  if (ev != nullptr) (void)hipEventRecord(ev[0], stream);
+  launch_transpose(a.k, u16p(p.kt), BH, c->T, c->D, p.TP, stream);
+  if (p.ncmp > 0) {
+    launch_transpose(a.wk, u16p(p.wkt), 1, LD, c->D, LD, stream);
+    launch_transpose(a.wv, u16p(p.wvt), 1, LD, c->D, LD, stream);
+    launch_compress(a.k, u16p(p.wkt), u16p(p.kc), u16p(p.kct), BH, c->T, c->D, c->cmp_len,
+                    c->cmp_stride, p.ncmp, p.NCP, p.NCP, false, stream);
+    launch_compress(a.v, u16p(p.wvt), u16p(p.vc), nullptr, BH, c->T, c->D, c->cmp_len,
+                    c->cmp_stride, p.ncmp, p.NCP, 0, false, stream);
+  }
+  launch_backward(a, stream, ev);
+  return hip_status();
+}
+
+int nsa_backward(const nsa_config* c, const void* q, const void* k, const void* v,
+                 const void* wk, const void* wv, const float* gate, const int32_t* sel_idx,
+                 const float* dout, float* dq, float* dk, float* dv, float* dwk, float* dwv,
+                 float* dgate, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return backward_impl(c, q, k, v, wk, wv, gate, sel_idx, dout, dq, dk, dv, dwk, dwv, dgate, ws,
+                       ws_bytes, stream, nullptr);
+}
+
+int nsa_backward_timed(const nsa_config* c, const void* q, const void* k, const void* v,
+                       const void* wk, const void* wv, const float* gate,
+                       const int32_t* sel_idx, const float* dout, float* dq, float* dk,
+                       float* dv, float* dwk, float* dwv, float* dgate, void* ws,
+                       size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
+  if (events == nullptr) return NSA_ERR_INVALID_ARG;
+  for (int i = 0; i <= NSA_BACKWARD_NSTAGES; ++i)
+    if (events[i] == nullptr) return NSA_ERR_INVALID_ARG;
+  return backward_impl(c, q, k, v, wk, wv, gate, sel_idx, dout, dq, dk, dv, dwk, dwv, dgate, ws,
+                       ws_bytes, stream, events);
 }
 
 size_t nsa_decode_workspace_bytes(const nsa_config* cfg) {

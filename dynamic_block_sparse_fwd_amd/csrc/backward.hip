@@ -1,0 +1,541 @@
+// Backward of the NSA prefill layer ("Zhang Xiaojun podcast EP94" notes, section 5: three
+// attention branches mixed by a gate; the "Native Sparse Attention" article: the layer is
+// trained end to end and its compressor is a learnable linear map).  The forward's block
+// selection is an input: a discrete choice, it passes no gradient, and the bf16 rounding of a
+// compressed token passes the gradient unchanged.
+//
+// A position's 16 query heads (G = 16) form one 16-row matrix-core tile.  Per branch:
+//   bwd_q_kernel   query-major, one wave per position: a first pass over the branch's 64-key
+//                  tiles gives the log2-sum-exp2 of the scaled scores and <dO, o> (online
+//                  softmax), a second pass dq += scale * dS K;
+//   bwd_kv_kernel  key-major, one workgroup per 64-key tile (a wave per 16 keys): over the
+//                  positions that see the tile, two positions (32 rows) per step,
+//                  dV += (g P)^T dO and dK += scale * dS^T q;
+// the compressed branch's key gradients then go back through the compressor
+// (bwd_cmp_dx_kernel: dK, dV; bwd_cmp_dw_kernel: dWk, dWv).  No atomics: every output element
+// has one writer per launch, and launches that add to the same output run in order.
+// Operands reach the matrix core straight from global memory (no LDS), in the layouts the
+// preparation kernel writes: dO in bf16, and q and dO with the 16 heads of a position
+// contiguous per feature (the B operand of the key-major products).
+#include "dev_common.h"
+#include "kernels.h"
+
+namespace nsa {
+
+namespace {
+
+constexpr int kBrCmp = 0, kBrSlc = 1, kBrWin = 2;  // also the gate columns
+constexpr float kInf = __builtin_huge_valf();
+
+__device__ __forceinline__ bf16x8 pack8(const float* v) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)v[i];
+  return r;
+}
+
+// Key-set geometry of one branch for query position t.
+template <int BR>
+struct KeySet {
+  int lo, hi;  // valid keys: lo <= key <= hi (compressed: token indices)
+  __device__ __forceinline__ KeySet(const BwdArgs& a, int t) {
+    if constexpr (BR == kBrCmp) {
+      lo = 0;
+      hi = n_visible(t, a.l, a.d, a.ncmp) - 1;
+    } else if constexpr (BR == kBrSlc) {
+      lo = 0;
+      hi = t;
+    } else {
+      lo = t - a.window + 1 > 0 ? t - a.window + 1 : 0;
+      hi = t;
+    }
+  }
+  __device__ __forceinline__ bool valid(int key) const { return key >= lo && key <= hi; }
+};
+
+}  // namespace
+
+// dO -> bf16 rows; q and dO with the 16 heads of a (position, group) contiguous per feature.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  const long n = (long)a.B * a.T * a.Hkv * a.D;
+  if (e >= n) return;
+  const int D = a.D;
+  const int dd = (int)(e % D);
+  const long r = e / D;  // (b, t, g)
+  const long row0 = r * 16;  // first head row of [B, T, Hq] (Hq = 16 Hkv)
+  u16 qh[16], dh[16];
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    const float dv = a.dout[(row0 + h) * D + dd];
+    dh[h] = f32_to_bf16(dv);
+    qh[h] = a.q[(row0 + h) * D + dd];
+    a.dob[(row0 + h) * D + dd] = dh[h];
+  }
+  u16* dt = a.dot + (r * D + dd) * 16;
+  u16* qt = a.qt + (r * D + dd) * 16;
+#pragma unroll
+  for (int h = 0; h < 16; h += 8) {
+    u32x4 w1, w2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w1[i] = (uint32_t)dh[h + 2 * i] | ((uint32_t)dh[h + 2 * i + 1] << 16);
+      w2[i] = (uint32_t)qh[h + 2 * i] | ((uint32_t)qh[h + 2 * i + 1] << 16);
+    }
+    *reinterpret_cast<u32x4*>(dt + h) = w1;
+    *reinterpret_cast<u32x4*>(qt + h) = w2;
+  }
+}
+
+// Query-major pass of branch BR: lse and <dO, o> per (position, head), then dq.
+template <int D, int BR>
+__global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs a) {
+  constexpr int DC = D / 32, DT = D / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const int t = blockIdx.x * 4 + wave, g = blockIdx.y, b = blockIdx.z;
+  if (t >= a.T) return;  // uniform per wave; no barrier in this kernel
+  const int Hq = a.Hkv * 16;
+  const long bg = (long)b * a.Hkv + g;
+  const long rowq = ((long)b * a.T + t) * Hq + g * 16;  // head 0 of this position and group
+  const long myrow = rowq + r16;
+  bf16x8 qf[DC], df[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    qf[c] = load8(a.q + myrow * D + 32 * c + 8 * g4);
+    df[c] = load8(a.dob + myrow * D + 32 * c + 8 * g4);
+  }
+  const float gt = a.gate[myrow * 3 + BR];
+  const float sl = a.scale_log2;
+  const KeySet<BR> ks(a, t);
+
+  const u16* krows;
+  const u16* vrows;
+  const u16* kcols;
+  int pitch, klim;
+  if constexpr (BR == kBrCmp) {
+    krows = a.kc + bg * (long)a.NCP * D;
+    vrows = a.vc + bg * (long)a.NCP * D;
+    kcols = a.kct + bg * (long)D * a.NCP;
+    pitch = a.NCP;
+    klim = a.NCP - 1;
+  } else {
+    krows = a.k + bg * (long)a.T * D;
+    vrows = a.v + bg * (long)a.T * D;
+    kcols = a.kt + bg * (long)D * a.TP;
+    pitch = a.TP;
+    klim = a.T - 1;
+  }
+  // tiles: base key of tile e, or -1 to skip (uniform over the wave)
+  const int per = a.beta / 64;
+  int ntiles;
+  if constexpr (BR == kBrCmp) ntiles = (ks.hi + 1 + 63) / 64;
+  else if constexpr (BR == kBrSlc) ntiles = a.top_n * per;
+  else ntiles = t / 64 - ks.lo / 64 + 1;
+  const int32_t* irow = a.idx + (((long)b * a.T + t) * a.Hkv + g) * a.top_n;
+  auto tile_base = [&](int e) -> int {
+    if constexpr (BR == kBrCmp) return 64 * e;
+    else if constexpr (BR == kBrSlc) {
+      const int j = irow[e / per];
+      const int base = j * a.beta + 64 * (e % per);
+      return (j >= 0 && j < a.nblk && base <= t) ? base : -1;
+    } else return (ks.lo / 64 + e) * 64;
+  };
+  // S^T and dP'^T = V dO^T of one tile: raw[kc*8 + s*4 + i] / dp[..] belong to key
+  // base + 32 kc + 8 g4 + 4 s + i and query row (head) r16
+  auto tile = [&](int base, float* raw, float* dp) {
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        int key = base + 32 * kc + perm_key(r16, s);
+        key = key < klim ? key : klim;
+        f32x4 as = zero4(), ap = zero4();
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          as = mfma16x16x32(load8(krows + (long)key * D + 32 * c + 8 * g4), qf[c], as);
+          ap = mfma16x16x32(load8(vrows + (long)key * D + 32 * c + 8 * g4), df[c], ap);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = base + 32 * kc + 8 * g4 + 4 * s + i;
+          raw[kc * 8 + s * 4 + i] = ks.valid(kk) ? as[i] * sl : -kInf;
+          dp[kc * 8 + s * 4 + i] = ap[i];
+        }
+      }
+  };
+
+  // pass 1: online log2-sum-exp2 and sum of p * dP'
+  float m = -kInf, lsum = 0.f, acc = 0.f;
+  for (int e = 0; e < ntiles; ++e) {
+    const int base = tile_base(e);
+    if (base < 0) continue;
+    float raw[16], dp[16];
+    tile(base, raw, dp);
+    float mx = raw[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, raw[i]);
+    mx = col_max4(mx);
+    const float mn = fmaxf(m, mx);
+    if (mn == -kInf) continue;  // nothing visible yet (the same for every head)
+    const float sc = exp2f(m - mn);
+    float ls = 0.f, as = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = exp2f(raw[i] - mn);
+      ls += p;
+      as += p * dp[i];
+    }
+    lsum = lsum * sc + col_sum4(ls);
+    acc = acc * sc + col_sum4(as);
+    m = mn;
+  }
+  const bool any = lsum > 0.f;
+  const float lse2 = any ? m + __log2f(lsum) : kInf;  // no key: every p is 0
+  const float dl = any ? acc / lsum : 0.f;
+  if (g4 == 0) {
+    const long o = (long)BR * a.B * a.T * Hq + myrow;
+    a.lse[o] = lse2;
+    a.dlt[o] = dl;
+    a.dgate[myrow * 3 + BR] = dl;
+  }
+
+  // pass 2: dq^T += K^T dS^T
+  f32x4 dq[DT];
+#pragma unroll
+  for (int n = 0; n < DT; ++n) dq[n] = zero4();
+  if (any) {
+    for (int e = 0; e < ntiles; ++e) {
+      const int base = tile_base(e);
+      if (base < 0) continue;
+      float raw[16], dp[16];
+      tile(base, raw, dp);
+      float ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[i] = gt * exp2f(raw[i] - lse2) * (dp[i] - dl);
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const bf16x8 pb = pack8(ds + 8 * kc);
+#pragma unroll
+        for (int n = 0; n < DT; ++n)
+          dq[n] = mfma16x16x32(
+              load8(kcols + (long)(16 * n + r16) * pitch + base + 32 * kc + 8 * g4), pb, dq[n]);
+      }
+    }
+  }
+  // lane holds dq^T[feature 16 n + 4 g4 + i][head r16]
+  float* dqp = a.dq + myrow * D;
+#pragma unroll
+  for (int n = 0; n < DT; ++n) {
+    float4 v = make_float4(a.scale * dq[n][0], a.scale * dq[n][1], a.scale * dq[n][2],
+                           a.scale * dq[n][3]);
+    float4* dst = reinterpret_cast<float4*>(dqp + 16 * n + 4 * g4);
+    if constexpr (BR != kBrCmp) {
+      const float4 o = *dst;
+      v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+    }
+    *dst = v;
+  }
+}
+
+// Key-major pass of branch BR over one 64-key tile: dK and dV of its keys.
+template <int D, int BR>
+__global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs a) {
+  constexpr int DC = D / 32, DT = D / 16;
+  __shared__ int plist[256];
+  __shared__ int wcount[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const int kb = blockIdx.x * 64;
+  const long bg = blockIdx.y;
+  const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
+  const int Hq = a.Hkv * 16;
+  const float sl = a.scale_log2;
+  const u16* krows;
+  const u16* vrows;
+  int klim;
+  if constexpr (BR == kBrCmp) {
+    krows = a.kc + bg * (long)a.NCP * D;
+    vrows = a.vc + bg * (long)a.NCP * D;
+    klim = a.NCP - 1;
+  } else {
+    krows = a.k + bg * (long)a.T * D;
+    vrows = a.v + bg * (long)a.T * D;
+    klim = a.T - 1;
+  }
+  // B operands of S = Q K^T and dP' = dO V^T: key kb + 16 wave + r16, features 32 c + 8 g4 ..
+  const int mykey = kb + 16 * wave + r16;
+  const int kr = mykey < klim ? mykey : klim;
+  bf16x8 kf[DC], vf[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    kf[c] = load8(krows + (long)kr * D + 32 * c + 8 * g4);
+    vf[c] = load8(vrows + (long)kr * D + 32 * c + 8 * g4);
+  }
+  f32x4 dK[DT], dV[DT];
+#pragma unroll
+  for (int n = 0; n < DT; ++n) { dK[n] = zero4(); dV[n] = zero4(); }
+  // keys of this lane's accumulator rows: kb + 16 wave + 4 g4 + i
+  const long bto = (long)BR * a.B * a.T * Hq;
+
+  // one step: positions ta, tb (either may be invalid: < 0)
+  auto step = [&](int ta, int tb) {
+    // A operands: row perm_key(r16, s) of the 32 rows; rows 0-15 are position ta's heads,
+    // 16-31 position tb's
+    bf16x8 qa[2][DC], da[2][DC];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int row = perm_key(r16, s);
+      int pos = row < 16 ? ta : tb;
+      pos = pos >= 0 ? pos : (ta >= 0 ? ta : tb);
+      const long qrow = ((long)b * a.T + pos) * Hq + g * 16 + (row & 15);
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        qa[s][c] = load8(a.q + qrow * D + 32 * c + 8 * g4);
+        da[s][c] = load8(a.dob + qrow * D + 32 * c + 8 * g4);
+      }
+    }
+    // this lane's rows: 8 g4 + j (j = 4 s + i), all of position p, heads 8 (g4 & 1) + j
+    const int p = g4 < 2 ? ta : tb;
+    const int pr = p >= 0 ? p : (ta >= 0 ? ta : tb);
+    const long row0 = ((long)b * a.T + pr) * Hq + g * 16 + 8 * (g4 & 1);
+    float lse8[8], dl8[8], gt8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      lse8[j] = a.lse[bto + row0 + j];
+      dl8[j] = a.dlt[bto + row0 + j];
+      gt8[j] = a.gate[(row0 + j) * 3 + BR];
+    }
+    bool ok = p >= 0;
+    if (ok) {
+      const KeySet<BR> ks(a, p);
+      ok = ks.valid(mykey);
+    }
+    float gp[8], ds[8];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      f32x4 as = zero4(), ap = zero4();
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        as = mfma16x16x32(qa[s][c], kf[c], as);
+        ap = mfma16x16x32(da[s][c], vf[c], ap);
+      }
+      // C[m = 4 g4 + i][n = key r16]: row perm_key(4 g4 + i, s) = 8 g4 + 4 s + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 4 * s + i;
+        const float pv = ok ? exp2f(as[i] * sl - lse8[j]) : 0.f;
+        gp[j] = gt8[j] * pv;
+        ds[j] = gt8[j] * pv * (ap[i] - dl8[j]);
+      }
+    }
+    // A = (gP)^T and dS^T: key r16, rows 8 g4 .. 8 g4 + 7; B = dO^T, q^T of those rows
+    const bf16x8 ap8 = pack8(gp), as8 = pack8(ds);
+    const long tro = (((long)b * a.T + pr) * a.Hkv + g) * D;
+#pragma unroll
+    for (int n = 0; n < DT; ++n) {
+      const long o = (tro + 16 * n + r16) * 16 + 8 * (g4 & 1);
+      dV[n] = mfma16x16x32(ap8, load8(a.dot + o), dV[n]);
+      dK[n] = mfma16x16x32(as8, load8(a.qt + o), dK[n]);
+    }
+  };
+
+  if constexpr (BR == kBrWin) {
+    const int t0 = kb, t1 = kb + 63 + a.window - 1 < a.T - 1 ? kb + 63 + a.window - 1 : a.T - 1;
+    for (int t = t0; t <= t1; t += 2) step(t, t + 1 <= t1 ? t + 1 : -1);
+  } else if constexpr (BR == kBrCmp) {
+    const int tlo = kb * a.d + a.l - 1;  // first position that sees compressed token kb
+    int t0 = blockIdx.z * a.PC, t1 = t0 + a.PC - 1;
+    t0 = t0 > tlo ? t0 : tlo;
+    t1 = t1 < a.T - 1 ? t1 : a.T - 1;
+    for (int t = t0; t <= t1; t += 2) step(t, t + 1 <= t1 ? t + 1 : -1);
+  } else {
+    // positions t >= kb whose group selected the block of this tile, gathered 256 at a time
+    const int jb = kb / a.beta;
+    for (int c0 = kb; c0 < a.T; c0 += 256) {
+      const int t = c0 + (int)threadIdx.x;
+      bool sel = false;
+      if (t < a.T) {
+        const int32_t* ir = a.idx + (((long)b * a.T + t) * a.Hkv + g) * a.top_n;
+        for (int e = 0; e < a.top_n; ++e) sel |= ir[e] == jb;
+      }
+      const uint64_t bal = __ballot(sel);
+      if (lane == 0) wcount[wave] = (int)__popcll(bal);
+      __syncthreads();
+      int off = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        off += w < wave ? wcount[w] : 0;
+        tot += wcount[w];
+      }
+      if (sel) plist[off + (int)__popcll(bal & ((1ull << lane) - 1ull))] = t;
+      __syncthreads();
+      for (int e = 0; e < tot; e += 2) step(plist[e], e + 1 < tot ? plist[e + 1] : -1);
+      __syncthreads();  // plist and wcount are rewritten by the next round
+    }
+  }
+
+  // lane holds dK[key kb + 16 wave + 4 g4 + i][feature 16 n + r16]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = kb + 16 * wave + 4 * g4 + i;
+    if constexpr (BR == kBrCmp) {
+      if (key >= a.NCP) continue;
+      const long o = (((long)blockIdx.z * a.B * a.Hkv + bg) * a.NCP + key) * D;
+#pragma unroll
+      for (int n = 0; n < DT; ++n) {
+        a.pk[o + 16 * n + r16] = a.scale * dK[n][i];
+        a.pv[o + 16 * n + r16] = dV[n][i];
+      }
+    } else {
+      if (key >= a.T) continue;
+      const long o = (bg * a.T + key) * D;
+#pragma unroll
+      for (int n = 0; n < DT; ++n) {
+        float kv = a.scale * dK[n][i], vv = dV[n][i];
+        if constexpr (BR == kBrSlc) {
+          kv += a.dk[o + 16 * n + r16];
+          vv += a.dv[o + 16 * n + r16];
+        }
+        a.dk[o + 16 * n + r16] = kv;
+        a.dv[o + 16 * n + r16] = vv;
+      }
+    }
+  }
+}
+
+// dKc, dVc = sum of the position-chunk partials (chunk order).
+__global__ __launch_bounds__(256) void bwd_cmp_reduce_kernel(BwdArgs a) {
+  const long n = (long)a.B * a.Hkv * a.NCP * a.D;
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  float sk = 0.f, sv = 0.f;
+  for (int z = 0; z < a.NPC; ++z) {
+    sk += a.pk[(long)z * n + e];
+    sv += a.pv[(long)z * n + e];
+  }
+  a.dkc[e] = sk;
+  a.dvc[e] = sv;
+}
+
+// dK[s] += sum over the compressed tokens i covering s of dKc[i] W[s - i d]^T (same for V);
+// one thread per (sequence-head, token, feature).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_cmp_dx_kernel(BwdArgs a) {
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  const long n = (long)a.B * a.Hkv * a.T * D;
+  if (e >= n) return;
+  const int f = (int)(e % D);
+  const long r = e / D;
+  const int s = (int)(r % a.T);
+  const long bg = r / a.T;
+  int i0 = s - a.l + 1 <= 0 ? 0 : (s - a.l + 1 + a.d - 1) / a.d;
+  int i1 = s / a.d;
+  i1 = i1 < a.ncmp - 1 ? i1 : a.ncmp - 1;
+  float gk = 0.f, gv = 0.f;
+  for (int i = i0; i <= i1; ++i) {
+    const int j = s - i * a.d;
+    const float* ck = a.dkc + (bg * a.NCP + i) * D;
+    const float* cv = a.dvc + (bg * a.NCP + i) * D;
+    const u16* wkr = a.wk + ((long)j * D + f) * D;
+    const u16* wvr = a.wv + ((long)j * D + f) * D;
+    for (int c = 0; c < D; c += 8) {
+      const bf16x8 wk8 = load8(wkr + c), wv8 = load8(wvr + c);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        gk = fmaf(ck[c + u], (float)wk8[u], gk);
+        gv = fmaf(cv[c + u], (float)wv8[u], gv);
+      }
+    }
+  }
+  a.dk[r * D + f] += gk;
+  a.dv[r * D + f] += gv;
+}
+
+// dW[j][e][c] = sum over (sequence-head, token i) of x[i d + j][e] dXc[i][c]: 64 x 64 output
+// tiles, 16 reduction rows per step through LDS, 4 x 4 outputs per thread (fp32).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_cmp_dw_kernel(BwdArgs a) {
+  __shared__ float As[16][64];
+  __shared__ float Bs[16][64];
+  const int c0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int j = blockIdx.z % a.l, kv = blockIdx.z / a.l;
+  const u16* x = kv ? a.v : a.k;
+  const float* dxc = kv ? a.dvc : a.dkc;
+  float* dw = kv ? a.dwv : a.dwk;
+  const int tid = threadIdx.x;
+  const int te = (tid / 16) * 4, tc = (tid % 16) * 4;
+  float acc[4][4] = {};
+  const long N = (long)a.B * a.Hkv * a.ncmp;
+  for (long n0 = 0; n0 < N; n0 += 16) {
+    for (int q = tid; q < 16 * 64; q += 256) {
+      const int rr = q / 64, cc = q % 64;
+      const long nn = n0 + rr;
+      float av = 0.f, bv = 0.f;
+      if (nn < N) {
+        const long bg = nn / a.ncmp;
+        const int i = (int)(nn % a.ncmp);
+        const u16 xb = x[(bg * a.T + (long)i * a.d + j) * D + e0 + cc];
+        av = __uint_as_float((uint32_t)xb << 16);
+        bv = dxc[(bg * a.NCP + i) * D + c0 + cc];
+      }
+      As[rr][cc] = av;
+      Bs[rr][cc] = bv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { av[u] = As[rr][te + u]; bv[u] = Bs[rr][tc + u]; }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc[u][w] = fmaf(av[u], bv[w], acc[u][w]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    *reinterpret_cast<float4*>(dw + ((long)j * D + e0 + te + u) * D + c0 + tc) =
+        make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+}
+
+template <int D>
+static void launch_bwd_d(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) {
+  auto mark = [&](int i) {
+    if (ev != nullptr) (void)hipEventRecord(ev[i], s);
+  };
+  const long nprep = (long)a.B * a.T * a.Hkv * D;
+  bwd_prep_kernel<<<(unsigned)((nprep + 255) / 256), 256, 0, s>>>(a);
+  mark(1);
+  const dim3 gq((a.T + 3) / 4, a.Hkv, a.B);
+  bwd_q_kernel<D, kBrCmp><<<gq, 256, 0, s>>>(a);
+  bwd_q_kernel<D, kBrSlc><<<gq, 256, 0, s>>>(a);
+  bwd_q_kernel<D, kBrWin><<<gq, 256, 0, s>>>(a);
+  mark(2);
+  const int nkt = (a.T + 63) / 64;
+  bwd_kv_kernel<D, kBrWin><<<dim3(nkt, a.B * a.Hkv, 1), 256, 0, s>>>(a);
+  bwd_kv_kernel<D, kBrSlc><<<dim3(nkt, a.B * a.Hkv, 1), 256, 0, s>>>(a);
+  if (a.ncmp > 0)
+    bwd_kv_kernel<D, kBrCmp><<<dim3(a.NCP / 64, a.B * a.Hkv, a.NPC), 256, 0, s>>>(a);
+  mark(3);
+  if (a.ncmp > 0) {
+    const long nr = (long)a.B * a.Hkv * a.NCP * D;
+    bwd_cmp_reduce_kernel<<<(unsigned)((nr + 255) / 256), 256, 0, s>>>(a);
+    const long nx = (long)a.B * a.Hkv * a.T * D;
+    bwd_cmp_dx_kernel<D><<<(unsigned)((nx + 255) / 256), 256, 0, s>>>(a);
+    bwd_cmp_dw_kernel<D><<<dim3(D / 64, D / 64, 2 * a.l), 256, 0, s>>>(a);
+  } else {
+    launch_fill_zero(a.dwk, (size_t)a.l * D * D, s);
+    launch_fill_zero(a.dwv, (size_t)a.l * D * D, s);
+  }
+  mark(4);
+}
+
+void launch_backward(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) {
+  if (a.D == 128) launch_bwd_d<128>(a, s, ev);
+  else launch_bwd_d<64>(a, s, ev);
+}
+
+}  // namespace nsa

@@ -61,6 +61,45 @@ int decode_max_tile_list();
 // dynamic LDS of the per-group kernel (selection state, per-wave tiles, partials)
 size_t decode_group_lds_bytes(int D, int nch, int nt, int nblk);
 
+// Backward of the prefill layer (G = 16).
+struct BwdArgs {
+  const uint16_t* q;      // [B, T, Hq, D]
+  const uint16_t* k;      // [B, Hkv, T, D]
+  const uint16_t* v;      // [B, Hkv, T, D]
+  const uint16_t* wk;     // [l, D, D]
+  const uint16_t* wv;     // [l, D, D]
+  const float* gate;      // [B, T, Hq, 3]
+  const int32_t* idx;     // [B, T, Hkv, top_n] the forward's selection
+  const float* dout;      // [B, T, Hq, D]
+  // workspace
+  const uint16_t* kt;     // [B*Hkv, D, TP] keys, transposed, zero past T
+  const uint16_t* kc;     // [B*Hkv, NCP, D] compressed keys, zero past n_cmp
+  const uint16_t* kct;    // [B*Hkv, D, NCP] compressed keys, transposed
+  const uint16_t* vc;     // [B*Hkv, NCP, D] compressed values
+  uint16_t* dob;          // [B, T, Hq, D] dout in bf16
+  uint16_t* dot;          // [B, T, Hkv, D, 16] dout, the 16 heads contiguous per feature
+  uint16_t* qt;           // [B, T, Hkv, D, 16] q, the same
+  float* lse;             // [3, B, T, Hq] per branch: log2-sum-exp2 of the scaled scores
+  float* dlt;             // [3, B, T, Hq] per branch: <dout, o_branch>
+  float* pk;              // [NPC, B*Hkv, NCP, D] compressed-key gradient, per position chunk
+  float* pv;              // [NPC, B*Hkv, NCP, D] compressed-value gradient, the same
+  float* dkc;             // [B*Hkv, NCP, D]
+  float* dvc;             // [B*Hkv, NCP, D]
+  // outputs
+  float* dq;              // [B, T, Hq, D]
+  float* dk;              // [B, Hkv, T, D]
+  float* dv;              // [B, Hkv, T, D]
+  float* dwk;             // [l, D, D]
+  float* dwv;             // [l, D, D]
+  float* dgate;           // [B, T, Hq, 3]
+  int B, T, Hkv, D, l, d, beta, top_n, window;
+  int ncmp, NCP, TP, nblk, PC, NPC;  // PC positions per chunk of the compressed key pass
+  float scale, scale_log2;
+};
+
+// ev: nullptr or NSA_BACKWARD_NSTAGES + 1 events; ev[0] is recorded by the caller.
+void launch_backward(const BwdArgs& a, hipStream_t s, hipEvent_t* ev);
+
 constexpr int kMobaChunks = 8;  // T-chunks per head counted by separate workgroups
 
 struct MobaArgs {

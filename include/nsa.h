@@ -286,6 +286,43 @@ int nsa_prefill_chunk(const nsa_config* cfg, int32_t P, int32_t C, const void* q
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Backward of the NSA prefill layer (podcast notes EP94 section 5: three attention branches and
+ * a gate; "Native Sparse Attention" article: the layer is trained end to end, its compressor a
+ * learnable linear map).  Gradients of sum(dout * out) for q, k, v, the compressor weights and
+ * the gate, with the forward's block selection held fixed (a discrete choice: the
+ * block-importance path carries no gradient) and the bf16 rounding of compressed tokens passed
+ * through unchanged.
+ *   q, k, v, wk, wv, gate  the nsa_prefill inputs (same shapes)
+ *   sel_idx  int32 [B, T, Hkv, top_n]  the selection nsa_prefill returned (any index list in
+ *            that format is accepted; entries outside [0, ceil(T / sel_block)) are skipped)
+ *   dout     fp32 [B, T, Hq, D]
+ *   dq fp32 [B, T, Hq, D]; dk, dv fp32 [B, Hkv, T, D]; dwk, dwv fp32 [l, D, D];
+ *   dgate fp32 [B, T, Hq, 3]   outputs, overwritten
+ *   ws       at least nsa_backward_workspace_bytes(cfg) bytes
+ * Matrix-core operands are bf16 (q, k, v, the compressed tokens as given; dout, the
+ * probabilities and the score gradients rounded to bf16), accumulation fp32.  Requires G = 16
+ * (NSA_ERR_UNSUPPORTED otherwise); other checks as nsa_prefill.
+ */
+size_t nsa_backward_workspace_bytes(const nsa_config* cfg);
+int nsa_backward(const nsa_config* cfg, const void* q, const void* k, const void* v,
+                 const void* wk, const void* wv, const float* gate, const int32_t* sel_idx,
+                 const float* dout, float* dq, float* dk, float* dv, float* dwk, float* dwv,
+                 float* dgate, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Instrumented nsa_backward: events[s] recorded before stage s, events[NSA_BACKWARD_NSTAGES]
+ * after the last.  Stages: 0 layout (key transpose, compression), 1 dout/q layouts, 2
+ * query-major passes (dq, per-branch statistics, dgate), 3 key-major passes (dk, dv, compressed
+ * partials), 4 compressor backward.  For measurement only.
+ */
+#define NSA_BACKWARD_NSTAGES 4
+int nsa_backward_timed(const nsa_config* cfg, const void* q, const void* k, const void* v,
+                       const void* wk, const void* wv, const float* gate,
+                       const int32_t* sel_idx, const float* dout, float* dq, float* dk,
+                       float* dv, float* dwk, float* dwv, float* dgate, void* ws,
+                       size_t ws_bytes, hipStream_t stream, hipEvent_t* events);
+
+/*
  * MoBA prefill (podcast notes EP94 sections 9-10): per head, block keys are the mean of the
  * block's keys, the query scores past blocks by q . kbar, keeps the top_k (ties to the lower
  * index) plus its own block, and attends causally over their union with one softmax.

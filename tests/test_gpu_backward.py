@@ -1,0 +1,87 @@
+"""GPU parity of nsa_backward (through the C ABI) against the fp64 backward oracle.
+
+Both sides take the same seeded inputs and the same block selection, the C oracle forward's
+(the selection is an input of the backward).  The matrix core sees bf16 operands (dout, the
+probabilities and the score gradients rounded to bf16) with fp32 accumulation.  Rounding dout
+alone gives every term of every gradient a relative error of up to 2^-9 (about 2e-3), and
+sums of such terms keep that relative size, so each gradient is held to an error relative to
+its own scale: mean |err| <= 4e-3 * mean |ref| (2^-8) and max |err| <= 1e-2 * max |ref|
+(per tensor)."""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth_inputs as S
+from oracle import nsa_backward as NB
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+MAX_REL = 1e-2
+MEAN_REL = 4e-3
+
+
+def to_dev(a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def check_grad(name, got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.isfinite(got).all(), "%s %s: non-finite" % (what, name)
+    err = np.abs(got - ref)
+    scale_max = float(np.abs(ref).max())
+    scale_mean = float(np.abs(ref).mean())
+    if scale_max == 0.0:
+        assert float(err.max()) == 0.0, "%s %s: expected zeros" % (what, name)
+        return 0.0, 0.0
+    mx, mean = float(err.max()) / scale_max, float(err.mean()) / scale_mean
+    assert mx <= MAX_REL, "%s %s: max err %.3g of max |ref| at %s" % (
+        what, name, mx, np.unravel_index(int(err.argmax()), err.shape))
+    assert mean <= MEAN_REL, "%s %s: mean err %.3g of mean |ref|" % (what, name, mean)
+    return mx, mean
+
+
+CASES = [
+    # name, B, T, Hkv, D, extra
+    ("T700_Hkv2_D64", 1, 700, 2, 64, {}),
+    ("B2_T530_D128", 2, 530, 1, 128, {}),
+    ("block128_top6_win200_D64", 1, 900, 1, 64, dict(sel_block=128, top_n=6, window=200)),
+    ("top5_local1_win100_D128", 1, 1100, 1, 128, dict(top_n=5, n_local=1, window=100)),
+    ("short_T40", 1, 40, 2, 64, {}),
+    ("no_compressed_T20", 1, 20, 1, 128, {}),
+]
+
+
+@pytest.mark.parametrize("name,B,T,Hkv,D,extra", CASES, ids=[c[0] for c in CASES])
+def test_backward_parity(name, B, T, Hkv, D, extra):
+    import dynamic_block_sparse_fwd_amd as nsa
+    nsa.load_library()
+    print("case backward", name, flush=True)
+    G = 16
+    ocfg = O.NsaCfg(B, T, Hkv, G, D, **extra)
+    x = S.nsa_prefill_inputs(91 + len(name), B, T, Hkv, G, D)
+    dout = S.upstream_grad(92 + len(name), (B, T, Hkv * G, D))
+    kc = O.compress(x["k"], x["wk"], ocfg.cmp_len, ocfg.cmp_stride)
+    vc = O.compress(x["v"], x["wv"], ocfg.cmp_len, ocfg.cmp_stride)
+    rb, rt = np.meshgrid(np.arange(B), np.arange(T), indexing="ij")
+    ora = O.nsa_prefill_rows(ocfg, x["q"], x["k"], x["v"], kc, vc, x["gate"],
+                             rb.ravel().astype(np.int32), rt.ravel().astype(np.int32))
+    idx = ora["idx"].reshape(B, T, Hkv, ocfg.top_n)
+    f = NB.inputs_f64(x)
+    ref = NB.backward(ocfg, f["q"], f["k"], f["v"], f["wk"], f["wv"], f["gate"], idx,
+                      dout.astype(np.float64))
+    cfg = nsa.NsaConfig(B, T, Hkv, G, D, ocfg.cmp_len, ocfg.cmp_stride, ocfg.sel_block,
+                        ocfg.top_n, ocfg.n_local, ocfg.window, ocfg.scale)
+    d = {k_: to_dev(v_) for k_, v_ in x.items()}
+    got = nsa.nsa_backward(cfg, d["q"], d["k"], d["v"], d["wk"], d["wv"], d["gate"], to_dev(idx),
+                           to_dev(dout))
+    torch.cuda.synchronize()
+    msg = []
+    for n in ("dq", "dk", "dv", "dwk", "dwv", "dgate"):
+        mx, mean = check_grad(n, got[n].cpu().numpy(), ref[n], name)
+        msg.append("%s %.1e/%.1e" % (n, mx, mean))
+    print("%s: %s (max/mean error relative to the gradient's scale)" % (name, ", ".join(msg)),
+          flush=True)

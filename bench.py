@@ -410,6 +410,70 @@ def bench_decode(args, B=32, L=65536, Hkv=4, G=16, D=128, seed=3, calls=20):
     return res, x
 
 
+def backward_flops(B, T, Hkv, G, D, l=32, d=16):
+    """Algorithmic work of the backward: per (row, key) pair of a branch, the scores, dP, dq, dK
+    and dV products (5 x 2 D flop); per compressed token the two products of the compressor
+    backward (dX and dW) for K and V."""
+    cmp_, slc, win = prefill_pairs(T, l, d)
+    ncmp = (T - l) // d + 1
+    attn = 10.0 * D * Hkv * G * (cmp_ + slc + win) * B
+    comp = 2 * 2 * (2.0 * ncmp * l * D * D * Hkv * B)
+    return attn, comp
+
+
+def bench_backward(args, B=1, Hkv=4, G=16, D=128):
+    """nsa_backward at the 64k prefill shape: gradients for q, k, v, the compressor weights
+    and the gate, the selection taken from nsa_prefill on the same inputs."""
+    import torch
+
+    import dynamic_block_sparse_fwd_amd as nsa
+    import synth_inputs as S
+
+    T = args.seq
+    cfg = nsa.NsaConfig(B, T, Hkv, G, D)
+    x = S.nsa_prefill_inputs(2, B, T, Hkv, G, D)
+    dev = torch.device("cuda:0")
+    d = {k: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).to(dev)
+         for k, v in x.items()}
+    del x
+    dout = torch.from_numpy(S.upstream_grad(6, (B, T, Hkv * G, D))).to(dev)
+    _, idx = nsa.nsa_prefill(cfg, d["q"], d["k"], d["v"], d["wk"], d["wv"], d["gate"])
+    ws = torch.empty(nsa.backward_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    grads = None
+    nst = len(nsa.BACKWARD_STAGES)
+
+    def step(events=None):
+        nonlocal grads
+        grads = nsa.nsa_backward(cfg, d["q"], d["k"], d["v"], d["wk"], d["wv"], d["gate"], idx,
+                                 dout, grads=grads, ws=ws, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = HipEvents(args.steps * (nst + 1))
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev.group(s * (nst + 1), nst + 1))
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    stage = {nm: 0.0 for nm in nsa.BACKWARD_STAGES}
+    for s in range(args.steps):
+        b0 = s * (nst + 1)
+        for i, nm in enumerate(nsa.BACKWARD_STAGES):
+            stage[nm] += ev.elapsed_ms(b0 + i, b0 + i + 1) / args.steps
+    attn, comp = backward_flops(B, T, Hkv, G, D)
+    F = attn + comp
+    return {
+        "workload": "nsa backward B=%d T=%d Hkv=%d G=%d D=%d top16 window512" % (B, T, Hkv, G, D),
+        "ms_per_step": round(wall * 1e3, 3),
+        "tok_s": round(B * T / wall, 1),
+        "algorithmic_tflop": round(F / 1e12, 3),
+        "tflops": round(F / wall / 1e12, 1),
+        "mfma_frac": round(F / wall / MFMA_PEAK_BF16, 4),
+        "stages_ms": {k: round(v, 3) for k, v in stage.items()},
+    }
+
+
 def bench_chunked(args, B=1, Hkv=4, G=16, D=128):
     """The 64k prefill run as a sequence of chunks from the caches: per chunk,
     nsa_cache_append of its K/V (cache rows and the compressed tokens they complete) and
@@ -617,7 +681,7 @@ def main():
                     help="MoBA sequence length for --only moba (beyond 128k: device-drawn inputs)")
     ap.add_argument("--chunk", type=int, default=8192,
                     help="chunk length for --only chunked (a multiple of 64)")
-    ap.add_argument("--only", choices=("prefill", "decode", "moba", "chunked"),
+    ap.add_argument("--only", choices=("prefill", "decode", "moba", "chunked", "backward"),
                     help="run one workload and print its result alone (for profiling runs)")
     ap.add_argument("--top-p", type=float, default=0.0,
                     help="adaptive top-p block selection for the NSA workloads (0: fixed top-16)")
@@ -636,6 +700,9 @@ def main():
     if args.only == "decode":
         dec, _ = bench_decode(args)
         print(json.dumps({"decode": dec}), flush=True)
+        return
+    if args.only == "backward":
+        print(json.dumps({"backward": bench_backward(args)}), flush=True)
         return
     if args.only == "chunked":
         print(json.dumps({"chunked": bench_chunked(args)}), flush=True)

@@ -580,6 +580,7 @@ static int backward_impl(const nsa_config* c, const void* q, const void* k, cons
     launch_compress(a.v, u16p(p.wvt), u16p(p.vc), nullptr, BH, c->T, c->D, c->cmp_len,
                     c->cmp_stride, p.ncmp, p.NCP, 0, false, stream);
   }
+  if (ev != nullptr) (void)hipEventRecord(ev[1], stream);
   launch_backward(a, stream, ev);
   return hip_status();
 }

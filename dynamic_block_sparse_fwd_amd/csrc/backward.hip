@@ -13,7 +13,8 @@
 //                  dV += (g P)^T dO and dK += scale * dS^T q;
 // the compressed branch's key gradients then go back through the compressor
 // (bwd_cmp_dx_kernel: dK, dV; bwd_cmp_dw_kernel: dWk, dWv).  No atomics: every output element
-// has one writer per launch, and launches that add to the same output run in order.
+// has one writer per launch, and launches that add to the same output run in order, except
+// the selected branch's key-major pass, whose position chunks add into dK, dV atomically.
 // Operands reach the matrix core straight from global memory (no LDS), in the layouts the
 // preparation kernel writes: dO in bf16, and q and dO with the 16 heads of a position
 // contiguous per feature (the B operand of the key-major products).
@@ -275,6 +276,7 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs a) {
   f32x4 dK[DT], dV[DT];
 #pragma unroll
   for (int n = 0; n < DT; ++n) { dK[n] = zero4(); dV[n] = zero4(); }
+  int seen = 0;  // selected branch: positions gathered by this workgroup (uniform)
   // keys of this lane's accumulator rows: kb + 16 wave + 4 g4 + i
   const long bto = (long)BR * a.B * a.T * Hq;
 
@@ -350,12 +352,16 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs a) {
     t1 = t1 < a.T - 1 ? t1 : a.T - 1;
     for (int t = t0; t <= t1; t += 2) step(t, t + 1 <= t1 ? t + 1 : -1);
   } else {
-    // positions t >= kb whose group selected the block of this tile, gathered 256 at a time
+    // positions of chunk blockIdx.z at or after kb whose group selected the block of this
+    // tile, gathered 256 at a time (block 0 is selected by every position: without the chunks
+    // its tile alone would walk the whole sequence)
     const int jb = kb / a.beta;
-    for (int c0 = kb; c0 < a.T; c0 += 256) {
+    const int c_lo = (int)blockIdx.z * a.PC > kb ? (int)blockIdx.z * a.PC : kb;
+    const int c_hi = ((int)blockIdx.z + 1) * a.PC < a.T ? ((int)blockIdx.z + 1) * a.PC : a.T;
+    for (int c0 = c_lo; c0 < c_hi; c0 += 256) {
       const int t = c0 + (int)threadIdx.x;
       bool sel = false;
-      if (t < a.T) {
+      if (t < c_hi) {
         const int32_t* ir = a.idx + (((long)b * a.T + t) * a.Hkv + g) * a.top_n;
         for (int e = 0; e < a.top_n; ++e) sel |= ir[e] == jb;
       }
@@ -371,10 +377,13 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs a) {
       if (sel) plist[off + (int)__popcll(bal & ((1ull << lane) - 1ull))] = t;
       __syncthreads();
       for (int e = 0; e < tot; e += 2) step(plist[e], e + 1 < tot ? plist[e + 1] : -1);
+      seen += tot;
       __syncthreads();  // plist and wcount are rewritten by the next round
     }
   }
 
+  if constexpr (BR == kBrSlc)
+    if (seen == 0) return;  // uniform: nothing to add
   // lane holds dK[key kb + 16 wave + 4 g4 + i][feature 16 n + r16]
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -392,13 +401,14 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs a) {
       const long o = (bg * a.T + key) * D;
 #pragma unroll
       for (int n = 0; n < DT; ++n) {
-        float kv = a.scale * dK[n][i], vv = dV[n][i];
-        if constexpr (BR == kBrSlc) {
-          kv += a.dk[o + 16 * n + r16];
-          vv += a.dv[o + 16 * n + r16];
+        const float kv = a.scale * dK[n][i], vv = dV[n][i];
+        if constexpr (BR == kBrSlc) {  // position chunks of one tile add concurrently
+          unsafeAtomicAdd(a.dk + o + 16 * n + r16, kv);
+          unsafeAtomicAdd(a.dv + o + 16 * n + r16, vv);
+        } else {
+          a.dk[o + 16 * n + r16] = kv;
+          a.dv[o + 16 * n + r16] = vv;
         }
-        a.dk[o + 16 * n + r16] = kv;
-        a.dv[o + 16 * n + r16] = vv;
       }
     }
   }
@@ -508,18 +518,18 @@ static void launch_bwd_d(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) {
   };
   const long nprep = (long)a.B * a.T * a.Hkv * D;
   bwd_prep_kernel<<<(unsigned)((nprep + 255) / 256), 256, 0, s>>>(a);
-  mark(1);
+  mark(2);
   const dim3 gq((a.T + 3) / 4, a.Hkv, a.B);
   bwd_q_kernel<D, kBrCmp><<<gq, 256, 0, s>>>(a);
   bwd_q_kernel<D, kBrSlc><<<gq, 256, 0, s>>>(a);
   bwd_q_kernel<D, kBrWin><<<gq, 256, 0, s>>>(a);
-  mark(2);
+  mark(3);
   const int nkt = (a.T + 63) / 64;
   bwd_kv_kernel<D, kBrWin><<<dim3(nkt, a.B * a.Hkv, 1), 256, 0, s>>>(a);
-  bwd_kv_kernel<D, kBrSlc><<<dim3(nkt, a.B * a.Hkv, 1), 256, 0, s>>>(a);
+  bwd_kv_kernel<D, kBrSlc><<<dim3(nkt, a.B * a.Hkv, a.NPC), 256, 0, s>>>(a);
   if (a.ncmp > 0)
     bwd_kv_kernel<D, kBrCmp><<<dim3(a.NCP / 64, a.B * a.Hkv, a.NPC), 256, 0, s>>>(a);
-  mark(3);
+  mark(4);
   if (a.ncmp > 0) {
     const long nr = (long)a.B * a.Hkv * a.NCP * D;
     bwd_cmp_reduce_kernel<<<(unsigned)((nr + 255) / 256), 256, 0, s>>>(a);
@@ -530,7 +540,7 @@ static void launch_bwd_d(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) {
     launch_fill_zero(a.dwk, (size_t)a.l * D * D, s);
     launch_fill_zero(a.dwv, (size_t)a.l * D * D, s);
   }
-  mark(4);
+  mark(5);
 }
 
 void launch_backward(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) {

@@ -97,7 +97,7 @@ struct BwdArgs {
   float scale, scale_log2;
 };
 
-// ev: nullptr or NSA_BACKWARD_NSTAGES + 1 events; ev[0] is recorded by the caller.
+// ev: nullptr or NSA_BACKWARD_NSTAGES + 1 events; ev[0] and ev[1] are recorded by the caller.
 void launch_backward(const BwdArgs& a, hipStream_t s, hipEvent_t* ev);
 
 constexpr int kMobaChunks = 8;  // T-chunks per head counted by separate workgroups

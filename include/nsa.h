@@ -315,7 +315,7 @@ int nsa_backward(const nsa_config* cfg, const void* q, const void* k, const void
  * query-major passes (dq, per-branch statistics, dgate), 3 key-major passes (dk, dv, compressed
  * partials), 4 compressor backward.  For measurement only.
  */
-#define NSA_BACKWARD_NSTAGES 4
+#define NSA_BACKWARD_NSTAGES 5
 int nsa_backward_timed(const nsa_config* cfg, const void* q, const void* k, const void* v,
                        const void* wk, const void* wv, const float* gate,
                        const int32_t* sel_idx, const float* dout, float* dq, float* dk,

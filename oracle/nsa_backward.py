@@ -107,25 +107,28 @@ def forward(cfg, q, k, v, wk, wv, gate, idx, round_cmp=True):
     return out
 
 
-def backward(cfg, q, k, v, wk, wv, gate, idx, dout, round_cmp=True):
+def backward(cfg, q, k, v, wk, wv, gate, idx, dout, round_cmp=True, rows=None):
     """Gradients of sum(dout * out) for the inputs of forward(): dict with dq, dk, dv, dwk, dwv,
-    dgate (same shapes as the inputs)."""
+    dgate (same shapes as the inputs).  rows: None, or the positions whose terms are summed (the
+    others count as dout = 0): dq and dgate are then exact on those rows, and dk, dv on keys
+    that only they can see (keys s with every position >= s in rows)."""
     B, T, Hq, D = q.shape
     G, l, d, sc = cfg.G, cfg.cmp_len, cfg.cmp_stride, cfg.scale
-    dq = np.zeros_like(q)
-    dk = np.zeros_like(k)
-    dv = np.zeros_like(v)
-    dwk = np.zeros_like(wk)
-    dwv = np.zeros_like(wv)
-    dgate = np.zeros_like(gate)
+    # fp64 results whatever the input dtype (bf16 inputs may come as exact fp32 arrays)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    dwk = np.zeros(wk.shape)
+    dwv = np.zeros(wv.shape)
+    dgate = np.zeros(gate.shape)
     for b in range(B):
         for g in range(cfg.Hkv):
-            kc = compress_f64(k[b, g], wk, l, d, round_cmp)
-            vc = compress_f64(v[b, g], wv, l, d, round_cmp)
+            kc = compress_f64(k[b, g].astype(np.float64), wk, l, d, round_cmp)
+            vc = compress_f64(v[b, g].astype(np.float64), wv, l, d, round_cmp)
             dkc = np.zeros_like(kc)
             dvc = np.zeros_like(vc)
             hs = slice(g * G, (g + 1) * G)
-            for t in range(T):
+            for t in (range(T) if rows is None else rows):
                 nvis = n_cmp(t + 1, l, d)
                 c_keys, s_keys, w_keys = _key_sets(t, nvis, idx[b, t, g], cfg.sel_block,
                                                    cfg.window)
@@ -149,13 +152,13 @@ def backward(cfg, q, k, v, wk, wv, gate, idx, dout, round_cmp=True):
             # through the compressor (the rounding passes the gradient unchanged, B2)
             n = kc.shape[0]
             for j in range(l):
-                rows = slice(j, j + d * (n - 1) + 1, d)
+                toks = slice(j, j + d * (n - 1) + 1, d)
                 if n == 0:
                     continue
-                dk[b, g, rows] += dkc @ wk[j].T
-                dv[b, g, rows] += dvc @ wv[j].T
-                dwk[j] += k[b, g, rows].T @ dkc
-                dwv[j] += v[b, g, rows].T @ dvc
+                dk[b, g, toks] += dkc @ wk[j].T
+                dv[b, g, toks] += dvc @ wv[j].T
+                dwk[j] += k[b, g, toks].T @ dkc
+                dwv[j] += v[b, g, toks].T @ dvc
     return dict(dq=dq, dk=dk, dv=dv, dwk=dwk, dwv=dwv, dgate=dgate)
 
 

@@ -56,6 +56,34 @@ def upstream_grad(seed: int, shape) -> np.ndarray:
     return g.standard_normal(int(np.prod(shape)), dtype=np.float32).reshape(shape)
 
 
+def block_selection(B: int, T: int, Hkv: int, top_n: int = 16, beta: int = 64,
+                    n_local: int = 2) -> np.ndarray:
+    """A deterministic, valid block-index list [B, T, Hkv, top_n] (ascending, -1 padded) for
+    inputs of the backward: block 0, the n_local most recent blocks, and top_n - 1 - n_local
+    distinct other blocks spread by a fixed stride (all blocks while they fit).  No scores are
+    involved: any selection is a legal input of the backward."""
+    t = np.arange(T, dtype=np.int64)
+    b = t // beta
+    out = np.full((B, T, Hkv, top_n), -1, dtype=np.int32)
+    kfree = top_n - 1 - n_local
+    for g in range(Hkv):
+        for bb in range(B):
+            rows = np.full((T, top_n), -1, dtype=np.int64)
+            fit = b + 1 <= top_n
+            ar = np.arange(top_n)
+            rows[fit] = np.where(ar[None, :] <= b[fit, None], ar[None, :], -1)
+            nf = ~fit
+            bn = b[nf]
+            span = bn - n_local  # free candidates 1 .. bn - n_local
+            off = (t[nf] * 7919 + g * 31 + bb * 17) % span
+            free = 1 + (off[:, None] + np.arange(kfree)[None, :] * 104729) % span[:, None]
+            local = bn[:, None] - np.arange(n_local)[None, :]
+            sel = np.concatenate([np.zeros((nf.sum(), 1), np.int64), free, local], axis=1)
+            rows[nf] = np.sort(sel, axis=1)
+            out[bb, :, g] = rows
+    return out
+
+
 def gates(seed: int, shape) -> np.ndarray:
     g = _gen(seed, "gate")
     x = g.standard_normal(int(np.prod(shape)), dtype=np.float32).astype(np.float64)

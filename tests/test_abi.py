@@ -190,3 +190,24 @@ def test_cache_append_and_chunk_reject_before_any_launch(lib):
     bad = nsa.NsaConfig(2, 4096, 2, 3, 64).c()
     assert lib.nsa_prefill_chunk(ctypes.byref(bad), 0, 64, *cargs, ws, None) == \
         nsa.NSA_ERR_UNSUPPORTED
+
+
+def test_backward_rejects_before_any_launch(lib):
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced
+    c = nsa.NsaConfig(1, 2048, 2, 16, 128).c()
+    assert lib.nsa_backward_workspace_bytes(ctypes.byref(c)) > 0
+    args = [fake] * 15
+    # G other than 16
+    bad = nsa.NsaConfig(1, 2048, 2, 8, 128).c()
+    assert lib.nsa_backward_workspace_bytes(ctypes.byref(bad)) == 0
+    assert lib.nsa_backward(ctypes.byref(bad), *args, 1 << 40, None) == nsa.NSA_ERR_UNSUPPORTED
+    # a null input or output, a misaligned pointer, a small workspace
+    for i in (0, 6, 7, 13):
+        a = list(args)
+        a[i] = None
+        assert lib.nsa_backward(ctypes.byref(c), *a, 1 << 40, None) == nsa.NSA_ERR_INVALID_ARG
+    a = list(args)
+    a[8] = P(0x1004)
+    assert lib.nsa_backward(ctypes.byref(c), *a, 1 << 40, None) == nsa.NSA_ERR_INVALID_ARG
+    assert lib.nsa_backward(ctypes.byref(c), *args, 16, None) == nsa.NSA_ERR_WORKSPACE

@@ -98,3 +98,19 @@ def test_special_cases_equal_sdpa_autograd(branch):
     np.testing.assert_allclose(g["dv"][0, 0], rv, rtol=0, atol=1e-11)
     if branch != "compressed":
         assert not g["dwk"].any() and not g["dwv"].any()
+
+
+def test_row_restricted_backward_is_exact_where_claimed():
+    """rows=[...]: dq and dgate on those rows, and dk/dv on keys only those rows see, equal the
+    full backward's."""
+    cfg, x, idx, _ = setup(T=260, G=2, D=16, window=40)
+    f = NB.inputs_f64(x)
+    dout = S.upstream_grad(55, f["q"].shape).astype(np.float64)
+    full = NB.backward(cfg, f["q"], f["k"], f["v"], f["wk"], f["wv"], f["gate"], idx, dout)
+    rows = [3, 77, 150] + list(range(200, 260))
+    part = NB.backward(cfg, f["q"], f["k"], f["v"], f["wk"], f["wv"], f["gate"], idx, dout,
+                       rows=rows)
+    np.testing.assert_allclose(part["dq"][:, rows], full["dq"][:, rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(part["dgate"][:, rows], full["dgate"][:, rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(part["dk"][:, :, 200:], full["dk"][:, :, 200:], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(part["dv"][:, :, 200:], full["dv"][:, :, 200:], rtol=0, atol=1e-12)

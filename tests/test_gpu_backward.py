@@ -85,3 +85,44 @@ def test_backward_parity(name, B, T, Hkv, D, extra):
         msg.append("%s %.1e/%.1e" % (n, mx, mean))
     print("%s: %s (max/mean error relative to the gradient's scale)" % (name, ", ".join(msg)),
           flush=True)
+
+
+def test_backward_64k_sampled_rows():
+    """The 64k prefill shape (1 x 65536, 4 KV heads x 16, D = 128) with a synthetic selection:
+    dq and dgate on 60 sampled positions (the first rows, block edges, random ones) and dk, dv
+    on the last 128 keys, which only the last 128 positions can see, against the oracle summed
+    over exactly those positions."""
+    import dynamic_block_sparse_fwd_amd as nsa
+    nsa.load_library()
+    B, T, Hkv, G, D = 1, 65536, 4, 16, 128
+    print("case backward 64k", flush=True)
+    ocfg = O.NsaCfg(B, T, Hkv, G, D)
+    x = S.nsa_prefill_inputs(2, B, T, Hkv, G, D)
+    dout = S.upstream_grad(7, (B, T, Hkv * G, D))
+    idx = S.block_selection(B, T, Hkv)
+    cfg = nsa.NsaConfig(B, T, Hkv, G, D)
+    d = {k_: to_dev(v_) for k_, v_ in x.items()}
+    got = nsa.nsa_backward(cfg, d["q"], d["k"], d["v"], d["wk"], d["wv"], d["gate"], to_dev(idx),
+                           to_dev(dout))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    sample = sorted(set([0, 1, 31, 32, 63, 64, 511, 512, 1023, 1024, 4095, 4096]) |
+                    set(rng.integers(1025, T - 128, 48).tolist()))
+    tail = list(range(T - 128, T))
+    rows = sample + tail
+    ri = torch.tensor(rows, device="cuda")
+    gdq = got["dq"][:, ri].cpu().numpy()
+    gdg = got["dgate"][:, ri].cpu().numpy()
+    gdk = got["dk"][:, :, T - 128:].cpu().numpy()
+    gdv = got["dv"][:, :, T - 128:].cpu().numpy()
+    del got, d
+    f = dict(q=S.bf16_bits_to_f32(x["q"]), k=NB.bf16_to_f64(x["k"]), v=NB.bf16_to_f64(x["v"]),
+             wk=NB.bf16_to_f64(x["wk"]), wv=NB.bf16_to_f64(x["wv"]), gate=x["gate"])
+    ref = NB.backward(ocfg, f["q"], f["k"], f["v"], f["wk"], f["wv"], f["gate"], idx, dout,
+                      rows=rows)
+    msg = []
+    for n, gv, rv in (("dq", gdq, ref["dq"][:, rows]), ("dgate", gdg, ref["dgate"][:, rows]),
+                      ("dk", gdk, ref["dk"][:, :, T - 128:]), ("dv", gdv, ref["dv"][:, :, T - 128:])):
+        mx, mean = check_grad(n, gv, rv, "64k")
+        msg.append("%s %.1e/%.1e" % (n, mx, mean))
+    print("backward 64k sampled: %s" % ", ".join(msg), flush=True)

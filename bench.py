@@ -196,13 +196,18 @@ def bench_prefill(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # the timed region: the production call, bracketed by device synchronisations
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    # per-stage times from the instrumented call (the same kernels, events between them)
     ev = HipEvents(args.steps * (nst + 1))
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
     for s in range(args.steps):
         step(ev.group(s * (nst + 1), nst + 1))
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
     stage_ms = {nm: 0.0 for nm in nsa.PREFILL_STAGES}
     total_ev = 0.0
     for s in range(args.steps):
@@ -732,7 +737,7 @@ def main():
                      for k, v in pre["roofline"].items()},
         "prefill": {"mfma_frac_total": round(pre["mfma_frac"], 4),
                     "algorithmic_tflop": round(pre["algorithmic_tflop"], 4),
-                    "events_ms_per_step": round(pre["events_ms_per_step"], 4),
+                    "instrumented_ms_per_step": round(pre["events_ms_per_step"], 4),
                     "stages": pre["stages"],
                     "selected_gather": {"bytes": pre["selected_gather"]["bytes"],
                                         "gbs": round(pre["selected_gather"]["gbs"], 1)},

@@ -14,6 +14,7 @@ using namespace nsa;
 
 namespace {
 
+
 constexpr size_t kAlign = 256;
 constexpr size_t kMaxDynLds = 64 * 1024;
 
@@ -354,7 +355,7 @@ static int prefill_run(const nsa_config* c, unsigned stages, const void* q, cons
   a.out = out;
   a.idx = idx;
   a.B = c->B; a.T = c->T; a.Hkv = c->Hkv; a.G = c->G; a.D = c->D;
-  a.q0 = 0; a.nq = c->T; a.ldk = c->T;
+  a.q0 = 0; a.nq = c->T; a.ldq = c->T; a.qs = 0; a.ldk = c->T;
   a.l = c->cmp_len; a.d = c->cmp_stride; a.beta = c->sel_block; a.top_n = c->top_n;
   a.n_local = c->n_local; a.window = c->window; a.top_p = c->top_p;
   a.ncmp = p.ncmp; a.NCP = p.NCP; a.TP = p.TP; a.nblk = p.nblk;
@@ -440,7 +441,7 @@ int nsa_prefill_chunk(const nsa_config* c, int32_t P, int32_t C, const void* q,
   a.out = out;
   a.idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(base + p.idx);
   a.B = c->B; a.T = Tend; a.Hkv = c->Hkv; a.G = c->G; a.D = c->D;
-  a.q0 = P; a.nq = C; a.ldk = c->T;
+  a.q0 = P; a.nq = C; a.ldq = C; a.qs = P; a.ldk = c->T;
   a.l = c->cmp_len; a.d = c->cmp_stride; a.beta = c->sel_block; a.top_n = c->top_n;
   a.n_local = c->n_local; a.window = c->window; a.top_p = c->top_p;
   a.ncmp = ncmp; a.NCP = round64(ncmp); a.TP = round64(Tend);

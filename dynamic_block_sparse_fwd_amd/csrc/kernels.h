@@ -16,7 +16,8 @@ struct PrefillArgs {
   float* out;           // [B, nq, Hq, D]
   int32_t* idx;         // [B, nq, Hkv, top_n]
   int B, T, Hkv, G, D;  // T: end of the query rows (keys 0 .. T-1 exist)
-  int q0, nq;           // query rows q0 .. q0+nq-1 = T-1; q/gate/out/idx hold row t at t - q0
+  int q0, nq;           // query rows processed: q0 .. q0+nq-1 (<= T-1)
+  int ldq, qs;          // q/gate/out/idx hold row t of sequence b at b * ldq + t - qs
   int ldk;              // rows per (sequence, KV head) slab of k (T, or a cache's capacity)
   int l, d, beta, top_n, n_local, window;
   int ncmp, NCP, TP, nblk;
@@ -27,7 +28,7 @@ struct PrefillArgs {
 
 // Row of q/gate/out/idx holding query position t of sequence b.
 __device__ __forceinline__ long prow(const PrefillArgs& a, int b, int t) {
-  return (long)b * a.nq + (t - a.q0);
+  return (long)b * a.ldq + (t - a.qs);
 }
 
 struct DecodeArgs {

@@ -239,13 +239,35 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs a) {
   }
 }
 
-// Key-major pass of branch BR over one 64-key tile: dK and dV of its keys.
+// LDS copy of one position pair's operands for the key-major pass (rows 0-15: position ta's
+// heads, 16-31: tb's).  q and dO rows are chunk-swizzled (chunk c of row r at c ^ pair_swz(r):
+// the 16 rows one operand read touches land on 16 distinct chunks); the heads-contiguous
+// copies have a 40-element pitch (80 bytes: 16 consecutive features on distinct banks).
+template <int D>
+struct PairStage {
+  u16 qr[32][D];
+  u16 dr[32][D];
+  u16 qt[D][40];
+  u16 dt[D][40];
+  float lse[32], dlt[32], gt[32];
+};
+
+template <int D>
+__device__ __forceinline__ int pair_swz(int r) {
+  return ((r & 3) | ((r >> 3) << 2)) & (D / 8 - 1);
+}
+
+// Key-major pass of branch BR over one 64-key tile: dK and dV of its keys.  The workgroup
+// stages each position pair's q, dO (both layouts) and row statistics in LDS once for its four
+// waves, the next pair's global loads in flight while the current one is computed.
 template <int D, int BR>
 __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs a) {
   constexpr int DC = D / 32, DT = D / 16;
+  constexpr int NCH = 16 * D / 256;  // 16-byte chunks per thread per pair (4 arrays of 4D)
+  __shared__ PairStage<D> st;
   __shared__ int plist[256];
   __shared__ int wcount[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
   const int kb = blockIdx.x * 64;
   const long bg = blockIdx.y;
@@ -277,37 +299,72 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
   for (int n = 0; n < DT; ++n) { dK[n] = zero4(); dV[n] = zero4(); }
   int seen = 0;  // selected branch: positions gathered by this workgroup (uniform)
-  // keys of this lane's accumulator rows: kb + 16 wave + 4 g4 + i
   const long bto = (long)BR * a.B * a.T * Hq;
 
-  // one step: positions ta, tb (either may be invalid: < 0)
-  auto step = [&](int ta, int tb) {
-    // A operands: row perm_key(r16, s) of the 32 rows; rows 0-15 are position ta's heads,
-    // 16-31 position tb's
+  // global -> registers for the pair (ta, tb); tb < 0: rows 16-31 repeat ta's (masked later)
+  u32x4 pre[NCH];
+  float pst = 0.f;
+  auto fetch = [&](int ta, int tb) {
+    const int tb2 = tb >= 0 ? tb : ta;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + 256 * i;
+      const int region = c / (4 * D), w = c % (4 * D);
+      const u16* src;
+      if (region < 2) {
+        const int row = w / (D / 8), ch = w % (D / 8);
+        const int pos = row < 16 ? ta : tb2;
+        const long qrow = ((long)b * a.T + pos) * Hq + g * 16 + (row & 15);
+        src = (region == 0 ? a.q : a.dob) + qrow * D + 8 * ch;
+      } else {
+        const int f = w / 4, part = w % 4;
+        const int pos = (part >> 1) ? tb2 : ta;
+        src = (region == 2 ? a.qt : a.dot) + ((((long)b * a.T + pos) * a.Hkv + g) * D + f) * 16 +
+              8 * (part & 1);
+      }
+      pre[i] = *reinterpret_cast<const u32x4*>(src);
+    }
+    if (tid < 96) {
+      const int kind = tid / 32, row = tid % 32;
+      const int pos = row < 16 ? ta : tb2;
+      const long hrow = ((long)b * a.T + pos) * Hq + g * 16 + (row & 15);
+      pst = kind == 0 ? a.lse[bto + hrow] : kind == 1 ? a.dlt[bto + hrow] : a.gate[hrow * 3 + BR];
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + 256 * i;
+      const int region = c / (4 * D), w = c % (4 * D);
+      u16* dst;
+      if (region < 2) {
+        const int row = w / (D / 8), ch = w % (D / 8);
+        dst = (region == 0 ? &st.qr[row][0] : &st.dr[row][0]) + 8 * (ch ^ pair_swz<D>(row));
+      } else {
+        const int f = w / 4, part = w % 4;
+        dst = (region == 2 ? &st.qt[f][0] : &st.dt[f][0]) + 8 * part;
+      }
+      *reinterpret_cast<u32x4*>(dst) = pre[i];
+    }
+    if (tid < 96) {
+      const int kind = tid / 32, row = tid % 32;
+      (kind == 0 ? st.lse : kind == 1 ? st.dlt : st.gt)[row] = pst;
+    }
+  };
+  // one pair from the staged operands
+  auto compute = [&](int ta, int tb) {
     bf16x8 qa[2][DC], da[2][DC];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int row = perm_key(r16, s);
-      int pos = row < 16 ? ta : tb;
-      pos = pos >= 0 ? pos : (ta >= 0 ? ta : tb);
-      const long qrow = ((long)b * a.T + pos) * Hq + g * 16 + (row & 15);
+      const int row = perm_key(r16, s), sw = pair_swz<D>(row);
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        qa[s][c] = load8(a.q + qrow * D + 32 * c + 8 * g4);
-        da[s][c] = load8(a.dob + qrow * D + 32 * c + 8 * g4);
+        qa[s][c] = load8(&st.qr[row][8 * ((4 * c + g4) ^ sw)]);
+        da[s][c] = load8(&st.dr[row][8 * ((4 * c + g4) ^ sw)]);
       }
     }
-    // this lane's rows: 8 g4 + j (j = 4 s + i), all of position p, heads 8 (g4 & 1) + j
+    // this lane's rows: 8 g4 + j (j = 4 s + i), all of position p
     const int p = g4 < 2 ? ta : tb;
-    const int pr = p >= 0 ? p : (ta >= 0 ? ta : tb);
-    const long row0 = ((long)b * a.T + pr) * Hq + g * 16 + 8 * (g4 & 1);
-    float lse8[8], dl8[8], gt8[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      lse8[j] = a.lse[bto + row0 + j];
-      dl8[j] = a.dlt[bto + row0 + j];
-      gt8[j] = a.gate[(row0 + j) * 3 + BR];
-    }
     bool ok = p >= 0;
     if (ok) {
       const KeySet<BR> ks(a, p);
@@ -325,32 +382,55 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs a) {
       // C[m = 4 g4 + i][n = key r16]: row perm_key(4 g4 + i, s) = 8 g4 + 4 s + i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = 4 * s + i;
-        const float pv = ok ? exp2f(as[i] * sl - lse8[j]) : 0.f;
-        gp[j] = gt8[j] * pv;
-        ds[j] = gt8[j] * pv * (ap[i] - dl8[j]);
+        const int j = 4 * s + i, row = 8 * g4 + j;
+        const float gt = st.gt[row];
+        const float pv = ok ? exp2f(as[i] * sl - st.lse[row]) : 0.f;
+        gp[j] = gt * pv;
+        ds[j] = gt * pv * (ap[i] - st.dlt[row]);
       }
     }
     // A = (gP)^T and dS^T: key r16, rows 8 g4 .. 8 g4 + 7; B = dO^T, q^T of those rows
     const bf16x8 ap8 = pack8(gp), as8 = pack8(ds);
-    const long tro = (((long)b * a.T + pr) * a.Hkv + g) * D;
 #pragma unroll
     for (int n = 0; n < DT; ++n) {
-      const long o = (tro + 16 * n + r16) * 16 + 8 * (g4 & 1);
-      dV[n] = mfma16x16x32(ap8, load8(a.dot + o), dV[n]);
-      dK[n] = mfma16x16x32(as8, load8(a.qt + o), dK[n]);
+      dV[n] = mfma16x16x32(ap8, load8(&st.dt[16 * n + r16][8 * g4]), dV[n]);
+      dK[n] = mfma16x16x32(as8, load8(&st.qt[16 * n + r16][8 * g4]), dK[n]);
+    }
+  };
+  // the pairs pair(0 .. np-1), software-pipelined through the LDS stage
+  auto run = [&](int np, auto pair) {
+    if (np <= 0) return;
+    int ta, tb;
+    pair(0, ta, tb);
+    fetch(ta, tb);
+    for (int e = 0; e < np; ++e) {
+      stash();
+      lds_barrier();
+      const int ca = ta, cb = tb;
+      if (e + 1 < np) {
+        pair(e + 1, ta, tb);
+        fetch(ta, tb);  // in flight during this pair's products
+      }
+      compute(ca, cb);
+      lds_barrier();  // the stage is rewritten next
     }
   };
 
   if constexpr (BR == kBrWin) {
     const int t0 = kb, t1 = kb + 63 + a.window - 1 < a.T - 1 ? kb + 63 + a.window - 1 : a.T - 1;
-    for (int t = t0; t <= t1; t += 2) step(t, t + 1 <= t1 ? t + 1 : -1);
+    run((t1 - t0 + 2) / 2, [&](int e, int& x, int& y) {
+      x = t0 + 2 * e;
+      y = x + 1 <= t1 ? x + 1 : -1;
+    });
   } else if constexpr (BR == kBrCmp) {
     const int tlo = kb * a.d + a.l - 1;  // first position that sees compressed token kb
     int t0 = blockIdx.z * a.PC, t1 = t0 + a.PC - 1;
     t0 = t0 > tlo ? t0 : tlo;
     t1 = t1 < a.T - 1 ? t1 : a.T - 1;
-    for (int t = t0; t <= t1; t += 2) step(t, t + 1 <= t1 ? t + 1 : -1);
+    run((t1 - t0 + 2) / 2, [&](int e, int& x, int& y) {
+      x = t0 + 2 * e;
+      y = x + 1 <= t1 ? x + 1 : -1;
+    });
   } else {
     // positions of chunk blockIdx.z at or after kb whose group selected the block of this
     // tile, gathered 256 at a time (block 0 is selected by every position: without the chunks
@@ -359,7 +439,7 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs a) {
     const int c_lo = (int)blockIdx.z * a.PC > kb ? (int)blockIdx.z * a.PC : kb;
     const int c_hi = ((int)blockIdx.z + 1) * a.PC < a.T ? ((int)blockIdx.z + 1) * a.PC : a.T;
     for (int c0 = c_lo; c0 < c_hi; c0 += 256) {
-      const int t = c0 + (int)threadIdx.x;
+      const int t = c0 + tid;
       bool sel = false;
       if (t < c_hi) {
         const int32_t* ir = a.idx + (((long)b * a.T + t) * a.Hkv + g) * a.top_n;
@@ -376,7 +456,10 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs a) {
       }
       if (sel) plist[off + (int)__popcll(bal & ((1ull << lane) - 1ull))] = t;
       __syncthreads();
-      for (int e = 0; e < tot; e += 2) step(plist[e], e + 1 < tot ? plist[e + 1] : -1);
+      run((tot + 1) / 2, [&](int e, int& x, int& y) {
+        x = plist[2 * e];
+        y = 2 * e + 1 < tot ? plist[2 * e + 1] : -1;
+      });
       seen += tot;
       __syncthreads();  // plist and wcount are rewritten by the next round
     }

@@ -18,7 +18,7 @@
 // Operands reach the matrix core straight from global memory (no LDS), in the layouts the
 // preparation kernel writes: dO in bf16, and q and dO with the 16 heads of a position
 // contiguous per feature (the B operand of the key-major products).
-#include "dev_common.h"
+#include "attn_tile.h"
 #include "kernels.h"
 
 namespace nsa {
@@ -225,6 +225,188 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs a) {
     }
   }
   // lane holds dq^T[feature 16 n + 4 g4 + i][head r16]
+  float* dqp = a.dq + myrow * D;
+#pragma unroll
+  for (int n = 0; n < DT; ++n) {
+    float4 v = make_float4(a.scale * dq[n][0], a.scale * dq[n][1], a.scale * dq[n][2],
+                           a.scale * dq[n][3]);
+    float4* dst = reinterpret_cast<float4*>(dqp + 16 * n + 4 * g4);
+    if constexpr (BR != kBrCmp) {
+      const float4 o = *dst;
+      v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+    }
+    *dst = v;
+  }
+}
+
+// Query-major pass of the compressed or window branch with the workgroup's four positions
+// (consecutive, one per wave) sharing every key tile: K and V rows and the transposed keys are
+// staged once in LDS (the swizzled tile layouts of the forward), the next tile's loads in flight
+// during the current one.  The four positions' key sets differ by at most a token at either
+// end, so the workgroup walks the union of their tiles and each wave masks its own keys.
+template <int D, int BR>
+__global__ __launch_bounds__(256) void bwd_q_shared_kernel(BwdArgs a) {
+  static_assert(BR != kBrSlc, "the selected branch's key sets differ per position");
+  constexpr int DC = D / 32, DT = D / 16;
+  __shared__ __align__(16) u16 Ks[64][D];
+  __shared__ __align__(16) u16 Vr[64][D];
+  __shared__ __align__(16) u16 Kt[D][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const int tfirst = blockIdx.x * 4, g = blockIdx.y, b = blockIdx.z;
+  const int t = tfirst + wave;
+  const bool live = t < a.T;  // dead waves still pass the barriers
+  const int tq = live ? t : a.T - 1;
+  const int tlastw = tfirst + 3 < a.T - 1 ? tfirst + 3 : a.T - 1;
+  const int Hq = a.Hkv * 16;
+  const long bg = (long)b * a.Hkv + g;
+  const long myrow = ((long)b * a.T + tq) * Hq + g * 16 + r16;
+  bf16x8 qf[DC], df[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    qf[c] = load8(a.q + myrow * D + 32 * c + 8 * g4);
+    df[c] = load8(a.dob + myrow * D + 32 * c + 8 * g4);
+  }
+  const float gt = a.gate[myrow * 3 + BR];
+  const float sl = a.scale_log2;
+  const KeySet<BR> ks(a, tq);
+
+  const u16* krows;
+  const u16* vrows;
+  const u16* kcols;
+  int pitch, klim, kt0, kt1;
+  if constexpr (BR == kBrCmp) {
+    krows = a.kc + bg * (long)a.NCP * D;
+    vrows = a.vc + bg * (long)a.NCP * D;
+    kcols = a.kct + bg * (long)D * a.NCP;
+    pitch = a.NCP;
+    klim = a.NCP - 1;
+    kt0 = 0;
+    kt1 = (n_visible(tlastw, a.l, a.d, a.ncmp) + 63) / 64 - 1;
+  } else {
+    krows = a.k + bg * (long)a.T * D;
+    vrows = a.v + bg * (long)a.T * D;
+    kcols = a.kt + bg * (long)D * a.TP;
+    pitch = a.TP;
+    klim = a.T - 1;
+    kt0 = (tfirst - a.window + 1 > 0 ? tfirst - a.window + 1 : 0) / 64;
+    kt1 = tlastw / 64;
+  }
+  // scores and dP'^T of the staged tile: raw[kc*8 + s*4 + i] / dp[..] belong to key
+  // base + 32 kc + 8 g4 + 4 s + i and query row (head) r16
+  auto tile = [&](int base, float* raw, float* dp) {
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 kf[DC], vf[DC];
+        k_frags<D>(Ks, kc, s, g4, r16, kf);
+        k_frags<D>(Vr, kc, s, g4, r16, vf);
+        f32x4 as = zero4(), ap = zero4();
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          as = mfma16x16x32(kf[c], qf[c], as);
+          ap = mfma16x16x32(vf[c], df[c], ap);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = base + 32 * kc + 8 * g4 + 4 * s + i;
+          raw[kc * 8 + s * 4 + i] = live && ks.valid(kk) ? as[i] * sl : -kInf;
+          dp[kc * 8 + s * 4 + i] = ap[i];
+        }
+      }
+  };
+
+  // pass 1: online log2-sum-exp2 and sum of p * dP'
+  float m = -kInf, lsum = 0.f, acc = 0.f;
+  {
+    KTileRegs<D, 256> kr, vr;
+    if (kt0 <= kt1) {
+      kr.load(krows, (long)kt0 * 64, klim);
+      vr.load(vrows, (long)kt0 * 64, klim);
+    }
+    for (int kt = kt0; kt <= kt1; ++kt) {
+      kr.store(Ks);
+      vr.store(Vr);
+      lds_barrier();
+      if (kt < kt1) {
+        kr.load(krows, (long)(kt + 1) * 64, klim);
+        vr.load(vrows, (long)(kt + 1) * 64, klim);
+      }
+      float raw[16], dp[16];
+      tile(kt * 64, raw, dp);
+      float mx = raw[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, raw[i]);
+      mx = col_max4(mx);
+      const float mn = fmaxf(m, mx);
+      if (mn != -kInf) {  // uniform per wave (every head shares the key mask)
+        const float sc = exp2f(m - mn);
+        float ls = 0.f, as = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = exp2f(raw[i] - mn);
+          ls += p;
+          as += p * dp[i];
+        }
+        lsum = lsum * sc + col_sum4(ls);
+        acc = acc * sc + col_sum4(as);
+        m = mn;
+      }
+      lds_barrier();
+    }
+  }
+  const bool any = lsum > 0.f;
+  const float lse2 = any ? m + __log2f(lsum) : kInf;
+  const float dl = any ? acc / lsum : 0.f;
+  if (live && g4 == 0) {
+    const long o = (long)BR * a.B * a.T * Hq + myrow;
+    a.lse[o] = lse2;
+    a.dlt[o] = dl;
+    a.dgate[myrow * 3 + BR] = dl;
+  }
+
+  // pass 2: dq^T += K^T dS^T
+  f32x4 dq[DT];
+#pragma unroll
+  for (int n = 0; n < DT; ++n) dq[n] = zero4();
+  {
+    KTileRegs<D, 256> kr, vr;
+    VTileRegs<D, 256> tr;
+    if (kt0 <= kt1) {
+      kr.load(krows, (long)kt0 * 64, klim);
+      vr.load(vrows, (long)kt0 * 64, klim);
+      tr.load(kcols, pitch, (long)kt0 * 64);
+    }
+    for (int kt = kt0; kt <= kt1; ++kt) {
+      kr.store(Ks);
+      vr.store(Vr);
+      tr.store(Kt);
+      lds_barrier();
+      if (kt < kt1) {
+        kr.load(krows, (long)(kt + 1) * 64, klim);
+        vr.load(vrows, (long)(kt + 1) * 64, klim);
+        tr.load(kcols, pitch, (long)(kt + 1) * 64);
+      }
+      if (any) {
+        float raw[16], dp[16];
+        tile(kt * 64, raw, dp);
+        float ds[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ds[i] = gt * exp2f(raw[i] - lse2) * (dp[i] - dl);
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const bf16x8 pb = pack8(ds + 8 * kc);
+          const int ch = ((4 * kc + g4) ^ (r16 & 7)) * 8;
+#pragma unroll
+          for (int n = 0; n < DT; ++n)
+            dq[n] = mfma16x16x32(load8(&Kt[16 * n + r16][ch]), pb, dq[n]);
+        }
+      }
+      lds_barrier();
+    }
+  }
+  if (!live) return;
   float* dqp = a.dq + myrow * D;
 #pragma unroll
   for (int n = 0; n < DT; ++n) {
@@ -603,9 +785,9 @@ static void launch_bwd_d(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) {
   bwd_prep_kernel<<<(unsigned)((nprep + 255) / 256), 256, 0, s>>>(a);
   mark(2);
   const dim3 gq((a.T + 3) / 4, a.Hkv, a.B);
-  bwd_q_kernel<D, kBrCmp><<<gq, 256, 0, s>>>(a);
+  bwd_q_shared_kernel<D, kBrCmp><<<gq, 256, 0, s>>>(a);
   bwd_q_kernel<D, kBrSlc><<<gq, 256, 0, s>>>(a);
-  bwd_q_kernel<D, kBrWin><<<gq, 256, 0, s>>>(a);
+  bwd_q_shared_kernel<D, kBrWin><<<gq, 256, 0, s>>>(a);
   mark(3);
   const int nkt = (a.T + 63) / 64;
   bwd_kv_kernel<D, kBrWin><<<dim3(nkt, a.B * a.Hkv, 1), 256, 0, s>>>(a);

@@ -239,25 +239,25 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs a) {
   }
 }
 
-// Query-major pass of the compressed or window branch with the workgroup's four positions
+// Query-major pass of the compressed or window branch with the workgroup's NW positions
 // (consecutive, one per wave) sharing every key tile: K and V rows and the transposed keys are
 // staged once in LDS (the swizzled tile layouts of the forward), the next tile's loads in flight
-// during the current one.  The four positions' key sets differ by at most a token at either
+// during the current one.  Neighbouring positions' key sets differ by a few tokens at either
 // end, so the workgroup walks the union of their tiles and each wave masks its own keys.
-template <int D, int BR>
-__global__ __launch_bounds__(256) void bwd_q_shared_kernel(BwdArgs a) {
+template <int D, int BR, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_q_shared_kernel(BwdArgs a) {
   static_assert(BR != kBrSlc, "the selected branch's key sets differ per position");
-  constexpr int DC = D / 32, DT = D / 16;
+  constexpr int DC = D / 32, DT = D / 16, NT = NW * 64;
   __shared__ __align__(16) u16 Ks[64][D];
   __shared__ __align__(16) u16 Vr[64][D];
   __shared__ __align__(16) u16 Kt[D][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
-  const int tfirst = blockIdx.x * 4, g = blockIdx.y, b = blockIdx.z;
+  const int tfirst = blockIdx.x * NW, g = blockIdx.y, b = blockIdx.z;
   const int t = tfirst + wave;
   const bool live = t < a.T;  // dead waves still pass the barriers
   const int tq = live ? t : a.T - 1;
-  const int tlastw = tfirst + 3 < a.T - 1 ? tfirst + 3 : a.T - 1;
+  const int tlastw = tfirst + NW - 1 < a.T - 1 ? tfirst + NW - 1 : a.T - 1;
   const int Hq = a.Hkv * 16;
   const long bg = (long)b * a.Hkv + g;
   const long myrow = ((long)b * a.T + tq) * Hq + g * 16 + r16;
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(256) void bwd_q_shared_kernel(BwdArgs a) {
   // pass 1: online log2-sum-exp2 and sum of p * dP'
   float m = -kInf, lsum = 0.f, acc = 0.f;
   {
-    KTileRegs<D, 256> kr, vr;
+    KTileRegs<D, NT> kr, vr;
     if (kt0 <= kt1) {
       kr.load(krows, (long)kt0 * 64, klim);
       vr.load(vrows, (long)kt0 * 64, klim);
@@ -371,8 +371,8 @@ __global__ __launch_bounds__(256) void bwd_q_shared_kernel(BwdArgs a) {
 #pragma unroll
   for (int n = 0; n < DT; ++n) dq[n] = zero4();
   {
-    KTileRegs<D, 256> kr, vr;
-    VTileRegs<D, 256> tr;
+    KTileRegs<D, NT> kr, vr;
+    VTileRegs<D, NT> tr;
     if (kt0 <= kt1) {
       kr.load(krows, (long)kt0 * 64, klim);
       vr.load(vrows, (long)kt0 * 64, klim);
@@ -442,16 +442,17 @@ __device__ __forceinline__ int pair_swz(int r) {
 // Key-major pass of branch BR over one 64-key tile: dK and dV of its keys.  The workgroup
 // stages each position pair's q, dO (both layouts) and row statistics in LDS once for its four
 // waves, the next pair's global loads in flight while the current one is computed.
-template <int D, int BR>
-__global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs a) {
-  constexpr int DC = D / 32, DT = D / 16;
-  constexpr int NCH = 16 * D / 256;  // 16-byte chunks per thread per pair (4 arrays of 4D)
+template <int D, int BR, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(BwdArgs a) {
+  static_assert(BR != kBrSlc || NW == 4, "a selected tile is one 64-key piece of one block");
+  constexpr int DC = D / 32, DT = D / 16, NT = NW * 64;
+  constexpr int NCH = 16 * D / NT;  // 16-byte chunks per thread per pair (4 arrays of 4D)
   __shared__ PairStage<D> st;
   __shared__ int plist[256];
   __shared__ int wcount[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
-  const int kb = blockIdx.x * 64;
+  const int kb = blockIdx.x * 16 * NW;
   const long bg = blockIdx.y;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
   const int Hq = a.Hkv * 16;
@@ -490,7 +491,7 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs a) {
     const int tb2 = tb >= 0 ? tb : ta;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       const int region = c / (4 * D), w = c % (4 * D);
       const u16* src;
       if (region < 2) {
@@ -516,7 +517,7 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs a) {
   auto stash = [&]() {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       const int region = c / (4 * D), w = c % (4 * D);
       u16* dst;
       if (region < 2) {
@@ -599,7 +600,8 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs a) {
   };
 
   if constexpr (BR == kBrWin) {
-    const int t0 = kb, t1 = kb + 63 + a.window - 1 < a.T - 1 ? kb + 63 + a.window - 1 : a.T - 1;
+    const int klast = kb + 16 * NW - 1;
+    const int t0 = kb, t1 = klast + a.window - 1 < a.T - 1 ? klast + a.window - 1 : a.T - 1;
     run((t1 - t0 + 2) / 2, [&](int e, int& x, int& y) {
       x = t0 + 2 * e;
       y = x + 1 <= t1 ? x + 1 : -1;
@@ -654,7 +656,7 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdArgs a) {
   for (int i = 0; i < 4; ++i) {
     const int key = kb + 16 * wave + 4 * g4 + i;
     if constexpr (BR == kBrCmp) {
-      if (key >= a.NCP) continue;
+      if (key >= a.NCP) continue;  // NCP is a multiple of 64, the workgroup may span 128
       const long o = (((long)blockIdx.z * a.B * a.Hkv + bg) * a.NCP + key) * D;
 #pragma unroll
       for (int n = 0; n < DT; ++n) {
@@ -785,15 +787,16 @@ static void launch_bwd_d(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) {
   bwd_prep_kernel<<<(unsigned)((nprep + 255) / 256), 256, 0, s>>>(a);
   mark(2);
   const dim3 gq((a.T + 3) / 4, a.Hkv, a.B);
-  bwd_q_shared_kernel<D, kBrCmp><<<gq, 256, 0, s>>>(a);
+  const dim3 gq8((a.T + 7) / 8, a.Hkv, a.B);
+  bwd_q_shared_kernel<D, kBrCmp, 8><<<gq8, 512, 0, s>>>(a);
   bwd_q_kernel<D, kBrSlc><<<gq, 256, 0, s>>>(a);
-  bwd_q_shared_kernel<D, kBrWin><<<gq, 256, 0, s>>>(a);
+  bwd_q_shared_kernel<D, kBrWin, 8><<<gq8, 512, 0, s>>>(a);
   mark(3);
   const int nkt = (a.T + 63) / 64;
-  bwd_kv_kernel<D, kBrWin><<<dim3(nkt, a.B * a.Hkv, 1), 256, 0, s>>>(a);
-  bwd_kv_kernel<D, kBrSlc><<<dim3(nkt, a.B * a.Hkv, a.NPC), 256, 0, s>>>(a);
+  bwd_kv_kernel<D, kBrWin, 8><<<dim3((a.T + 127) / 128, a.B * a.Hkv, 1), 512, 0, s>>>(a);
+  bwd_kv_kernel<D, kBrSlc, 4><<<dim3(nkt, a.B * a.Hkv, a.NPC), 256, 0, s>>>(a);
   if (a.ncmp > 0)
-    bwd_kv_kernel<D, kBrCmp><<<dim3(a.NCP / 64, a.B * a.Hkv, a.NPC), 256, 0, s>>>(a);
+    bwd_kv_kernel<D, kBrCmp, 8><<<dim3((a.NCP + 127) / 128, a.B * a.Hkv, a.NPC), 512, 0, s>>>(a);
   mark(4);
   if (a.ncmp > 0) {
     const long nr = (long)a.B * a.Hkv * a.NCP * D;

@@ -293,8 +293,9 @@ int nsa_prefill_chunk(const nsa_config* cfg, int32_t P, int32_t C, const void* q
  * block-importance path carries no gradient) and the bf16 rounding of compressed tokens passed
  * through unchanged.
  *   q, k, v, wk, wv, gate  the nsa_prefill inputs (same shapes)
- *   sel_idx  int32 [B, T, Hkv, top_n]  the selection nsa_prefill returned (any index list in
- *            that format is accepted; entries outside [0, ceil(T / sel_block)) are skipped)
+ *   sel_idx  int32 [B, T, Hkv, top_n]  the selection nsa_prefill returned, or any list in that
+ *            format whose valid entries are distinct (a repeated block is not supported);
+ *            entries outside [0, ceil(T / sel_block)) are skipped
  *   dout     fp32 [B, T, Hq, D]
  *   dq fp32 [B, T, Hq, D]; dk, dv fp32 [B, Hkv, T, D]; dwk, dwv fp32 [l, D, D];
  *   dgate fp32 [B, T, Hq, 3]   outputs, overwritten

@@ -52,6 +52,8 @@ CASES = [
     ("top5_local1_win100_D128", 1, 1100, 1, 128, dict(top_n=5, n_local=1, window=100)),
     ("short_T40", 1, 40, 2, 64, {}),
     ("no_compressed_T20", 1, 20, 1, 128, {}),
+    # an adaptive top-p selection: index rows of varying length, -1 padded
+    ("topp0.4_T800_D128", 1, 800, 2, 128, dict(top_p=0.4)),
 ]
 
 

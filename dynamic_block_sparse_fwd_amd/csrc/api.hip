@@ -124,7 +124,7 @@ MobaPlan plan_moba(const moba_config* c) {
   p.idx = off;    off += align_up(rows * (c->top_k + 1) * 4);
   p.list = off;   off += align_up(entries * 4 + 4);
   // one spare slot each: the merge loads slot 0 unconditionally, also when top_k = 0
-  p.po = off;     off += align_up((entries + 1) * c->D * 4);
+  p.po = off;     off += align_up((entries + 1) * c->D * 2);  // fp16
   p.pml = off;    off += align_up((entries + 1) * 2 * 4);
   p.total = off;
   return p;
@@ -706,7 +706,7 @@ static int moba_impl(const moba_config* c, const void* q, const void* k, const v
   a.ntiles = reinterpret_cast<int32_t*>(base + p.ntiles);
   a.tile_entry = reinterpret_cast<int32_t*>(base + p.tile_entry);
   a.list = reinterpret_cast<int32_t*>(base + p.list);
-  a.po = reinterpret_cast<float*>(base + p.po);
+  a.po = reinterpret_cast<_Float16*>(base + p.po);
   a.pml = reinterpret_cast<float*>(base + p.pml);
   a.idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(base + p.idx);
   a.B = c->B; a.T = c->T; a.H = c->H; a.D = c->D; a.block = c->block; a.top_k = c->top_k;

@@ -119,7 +119,7 @@ struct MobaArgs {
   int32_t* ntiles;     // [1] total tiles
   int32_t* tile_entry; // [max_tiles] the list each 128-row tile belongs to
   int32_t* list;       // [B*T*H*top_k] (t << 4 | slot)
-  float* po;           // [B*T*H, top_k, D] partial outputs (relative to the partial max)
+  _Float16* po;        // [B*T*H, top_k, D] partial outputs, normalised by their own sum (fp16)
   float* pml;          // [B*T*H, top_k, 2] partial (max, sum), log2 units
   int B, T, H, D, block, top_k, nb, max_tiles;
   float scale_log2;

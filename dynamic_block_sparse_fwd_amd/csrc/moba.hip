@@ -414,11 +414,16 @@ __global__ __launch_bounds__(256) void moba_block_kernel(MobaArgs a) {
     const float L = col_sum4(lrun[rt]);
     if (rt_t[rt] >= 0) {
       const long slot = (((long)b * a.T + rt_t[rt]) * a.H + h) * a.top_k + rt_s[rt];
-      float* op = a.po + slot * D;
+      // stored normalised by the partial's own sum: a convex combination of value rows, well
+      // inside fp16's range whatever the headroom of the lazily rescaled sum
+      _Float16* op = a.po + slot * D;
+      const float inv = 1.0f / L;  // a chosen past block always has visible keys: L > 0
 #pragma unroll
-      for (int nn = 0; nn < DT; ++nn)
-        *reinterpret_cast<float4*>(op + 16 * nn + 4 * g4) =
-            make_float4(O[rt][nn][0], O[rt][nn][1], O[rt][nn][2], O[rt][nn][3]);
+      for (int nn = 0; nn < DT; ++nn) {
+        const h16x4 v = {(_Float16)(O[rt][nn][0] * inv), (_Float16)(O[rt][nn][1] * inv),
+                         (_Float16)(O[rt][nn][2] * inv), (_Float16)(O[rt][nn][3] * inv)};
+        *reinterpret_cast<h16x4*>(op + 16 * nn + 4 * g4) = v;
+      }
       if (g4 == 0) {
         a.pml[slot * 2 + 0] = mrun[rt] * a.scale_log2;
         a.pml[slot * 2 + 1] = L;
@@ -541,10 +546,12 @@ __global__ __launch_bounds__(256) void moba_own_kernel(MobaArgs a) {
       const long slot = row * K + (s < slast ? s : slast);
       pm[s] = a.pml[slot * 2];
       pl[s] = a.pml[slot * 2 + 1];
-      const float* op = a.po + slot * D;
+      const _Float16* op = a.po + slot * D;
 #pragma unroll
-      for (int nn = 0; nn < DT; ++nn)
-        pv[s][nn] = *reinterpret_cast<const float4*>(op + 16 * nn + 4 * g4);
+      for (int nn = 0; nn < DT; ++nn) {
+        const h16x4 v = *reinterpret_cast<const h16x4*>(op + 16 * nn + 4 * g4);
+        pv[s][nn] = make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+      }
     }
     float M = mrun[rt];
 #pragma unroll
@@ -559,8 +566,9 @@ __global__ __launch_bounds__(256) void moba_own_kernel(MobaArgs a) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const bool ok = s < nsel;
-      const float f = ok ? fast_exp2(pm[s] - M) : 0.f;
-      L += ok ? pl[s] * f : 0.f;
+      // the partials are normalised: weight = their sum relative to the common max
+      const float f = ok ? pl[s] * fast_exp2(pm[s] - M) : 0.f;
+      L += f;
 #pragma unroll
       for (int nn = 0; nn < DT; ++nn) {
         acc[nn].x += ok ? f * pv[s][nn].x : 0.f;

@@ -82,7 +82,10 @@ int check_nsa_decode(const nsa_config* c) {
   if (decode_max_tiles(c) > decode_max_tile_list()) return NSA_ERR_UNSUPPORTED;
   const DecodeShape p = decode_shape(c);
   // 160 KB of LDS per workgroup, 4 KB of it static
-  if (decode_group_lds_bytes(c->D, p.NCH, p.NT, p.nblk) > 156 * 1024) return NSA_ERR_UNSUPPORTED;
+  // dynamic LDS of the per-group workgroup; with its static LDS (under 8 KB) it must fit the
+  // 160 KB of a workgroup
+  if (decode_group_lds_bytes(c->D, p.NCH, p.NT, p.nblk) > kMaxDecodeDynLds)
+    return NSA_ERR_UNSUPPORTED;
   return NSA_OK;
 }
 

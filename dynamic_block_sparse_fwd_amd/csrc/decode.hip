@@ -845,8 +845,11 @@ void launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
                          : reinterpret_cast<const void*>(dec_group_kernel<128, false>))
                  : (fast ? reinterpret_cast<const void*>(dec_group_kernel<64, true>)
                          : reinterpret_cast<const void*>(dec_group_kernel<64, false>));
+  // opt in to the accepted maximum (not this launch's size: concurrent calls on other host
+  // threads may need more); the attribute is per device, so it is set on every launch
   if (lds > 64 * 1024)
-    (void)hipFuncSetAttribute(gk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute(gk, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kMaxDecodeDynLds);
   mark(0);
   if (a.NCH > 0) {
     const dim3 g1(a.NCH, a.Hkv, a.B);

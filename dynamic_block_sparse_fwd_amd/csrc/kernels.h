@@ -61,6 +61,7 @@ int decode_chunk_tokens();
 int decode_max_tile_list();
 // dynamic LDS of the per-group kernel (selection state, per-wave tiles, partials)
 size_t decode_group_lds_bytes(int D, int nch, int nt, int nblk);
+constexpr size_t kMaxDecodeDynLds = 152 * 1024;  // accepted maximum of the above
 
 // Backward of the prefill layer (G = 16).
 struct BwdArgs {

@@ -782,14 +782,11 @@ static void launch_prefill_all(const PrefillArgs& a, int which, hipStream_t s) {
   if (which == 0) {
     const size_t lds = cmp_lds<G>(a.nblk);
     const bool fast = a.beta == 4 * a.d && a.l == 2 * a.d;
-    static bool attr_set = false;  // opt in to the largest dynamic LDS the kernel may use
-    if (!attr_set) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cmp_select_kernel<D, G, true>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&cmp_select_kernel<D, G, false>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
-      attr_set = true;
-    }
+    // opt in to the largest dynamic LDS any launch may use (64 KB, the validated limit); the
+    // attribute is per device, so it is set on every launch rather than once per process
+    (void)hipFuncSetAttribute(fast ? reinterpret_cast<const void*>(&cmp_select_kernel<D, G, true>)
+                                   : reinterpret_cast<const void*>(&cmp_select_kernel<D, G, false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
     if (fast)
       cmp_select_kernel<D, G, true><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, lds, s>>>(a);
     else

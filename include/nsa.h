@@ -215,7 +215,8 @@ int nsa_prefill_timed(const nsa_config* cfg, const void* q, const void* k, const
  *   sel_idx        int32 [B, Hkv, top_n] or NULL
  * Returns NSA_ERR_UNSUPPORTED when top_n * sel_block / 64 + ceil(window / 64) + 1 > 160
  * (tile table), Lmax > 2^24, or the per-group selection state (chunk statistics, tile
- * references, block scores) outgrows the 160 KB of LDS of one workgroup.
+ * references, block scores) outgrows 152 KB of LDS (the workgroup's other LDS and it share
+ * 160 KB).
  */
 int nsa_decode(const nsa_config* cfg, const void* q, const void* kcache, const void* vcache,
                const void* kcmp, const void* vcmp, const int32_t* seqlens, const float* gate,

@@ -92,6 +92,7 @@ DECODE_CASES = [
      dict(top_p=0.5, top_n=5, n_local=1, window=64)),
     ("topp1_G1_D64_block128", 2, 2500, 2, 1, 64, [2500, 1300],
      dict(top_p=1.0, sel_block=128, top_n=6, window=200)),
+    ("topp_tiny_G16_D128", 3, 3000, 2, 16, 128, [3000, 1000, 40], dict(top_p=1e-6)),
 ]
 
 

@@ -76,6 +76,8 @@ CASES = [
     ("topp0.5_G2_D64_block128", 1, 1500, 2, 2, 64, dict(top_p=0.5, sel_block=128, top_n=6,
                                                         window=200)),
     ("topp1_G1_D64_nolocal", 2, 700, 2, 1, 64, dict(top_p=1.0, top_n=4, n_local=0, window=100)),
+    # p below any forced mass: only block 0 and the local blocks are kept
+    ("topp_tiny_G4_D128", 1, 1300, 2, 4, 128, dict(top_p=1e-6)),
 ]
 
 

@@ -344,9 +344,8 @@ static int prefill_run(const nsa_config* c, unsigned stages, const void* q, cons
   mark(1);
   if (s_cmp && p.ncmp > 0) {
     launch_compress(static_cast<const uint16_t*>(k), wkt, kcb, nullptr, BH, c->T, c->D,
-                    c->cmp_len, c->cmp_stride, p.ncmp, p.NCP, p.NCP, false, stream);
-    launch_compress(static_cast<const uint16_t*>(v), wvt, nullptr, vct, BH, c->T, c->D,
-                    c->cmp_len, c->cmp_stride, p.ncmp, p.NCP, p.NCP, false, stream);
+                    c->cmp_len, c->cmp_stride, p.ncmp, p.NCP, p.NCP, false, stream, nullptr, 0, 1,
+                    static_cast<const uint16_t*>(v), wvt, nullptr, vct);
   }
   PrefillArgs a{};
   a.q = static_cast<const uint16_t*>(q);
@@ -513,11 +512,10 @@ int nsa_cache_append(const nsa_config* c, int32_t C, const void* k_new, const vo
     uint16_t* wvt = wkt + align_up((size_t)LD * c->D * 2) / 2;
     launch_transpose(static_cast<const uint16_t*>(wk), wkt, 1, LD, c->D, LD, stream);
     launch_transpose(static_cast<const uint16_t*>(wv), wvt, 1, LD, c->D, LD, stream);
+    // keys (row-major) and values (tiles) in one launch
     launch_compress(kc16, wkt, static_cast<uint16_t*>(kcmp), nullptr, BH, c->T, c->D,
-                    c->cmp_len, c->cmp_stride, ncap, ncap, 0, false, stream, seqlens, C, c->Hkv);
-    launch_compress(vc16, wvt, nullptr, static_cast<uint16_t*>(vcmp), BH, c->T, c->D,
-                    c->cmp_len, c->cmp_stride, ncap, 0, 64 * ((ncap + 63) / 64), true, stream,
-                    seqlens, C, c->Hkv);
+                    c->cmp_len, c->cmp_stride, ncap, ncap, 64 * ((ncap + 63) / 64), true, stream,
+                    seqlens, C, c->Hkv, vc16, wvt, nullptr, static_cast<uint16_t*>(vcmp));
   }
   return hip_status();
 }
@@ -580,9 +578,8 @@ static int backward_impl(const nsa_config* c, const void* q, const void* k, cons
     launch_transpose(a.wk, u16p(p.wkt), 1, LD, c->D, LD, stream);
     launch_transpose(a.wv, u16p(p.wvt), 1, LD, c->D, LD, stream);
     launch_compress(a.k, u16p(p.wkt), u16p(p.kc), u16p(p.kct), BH, c->T, c->D, c->cmp_len,
-                    c->cmp_stride, p.ncmp, p.NCP, p.NCP, false, stream);
-    launch_compress(a.v, u16p(p.wvt), u16p(p.vc), nullptr, BH, c->T, c->D, c->cmp_len,
-                    c->cmp_stride, p.ncmp, p.NCP, 0, false, stream);
+                    c->cmp_stride, p.ncmp, p.NCP, p.NCP, false, stream, nullptr, 0, 1, a.v,
+                    u16p(p.wvt), u16p(p.vc), nullptr);
   }
   if (ev != nullptr) (void)hipEventRecord(ev[1], stream);
   launch_backward(a, stream, ev);

@@ -145,9 +145,13 @@ void launch_transpose(const uint16_t* x, uint16_t* xt, int BH, int rows, int col
 // Append mode (seqlens non-null, Hkv heads per sequence): only the compressed tokens completed
 // by appending C tokens to sequence b, i.e. n_cmp(seqlens[b]) <= i < n_cmp(seqlens[b] + C)
 // (and i < ncmp), are computed and written; no other row is touched.
+// With x2 non-null a second operand set (x2, wt2, xc2, xct2; same shapes) is compressed in the
+// same launch (keys and values together: twice the workgroups in flight).
 void launch_compress(const uint16_t* x, const uint16_t* wt, uint16_t* xc, uint16_t* xct, int BH,
                      int T, int D, int l, int d, int ncmp, int rows_alloc, int ncp, bool tiled,
-                     hipStream_t s, const int32_t* seqlens = nullptr, int C = 0, int Hkv = 1);
+                     hipStream_t s, const int32_t* seqlens = nullptr, int C = 0, int Hkv = 1,
+                     const uint16_t* x2 = nullptr, const uint16_t* wt2 = nullptr,
+                     uint16_t* xc2 = nullptr, uint16_t* xct2 = nullptr);
 
 // Append mode for few tokens, keys and values in one go (index 0 keys, 1 values): the same
 // tokens as launch_compress's append mode, at most `per` per sequence-head, gathered over all

@@ -143,8 +143,17 @@ __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x
                                                        int T, int l, int d, int ncmp,
                                                        int rows_alloc, int ncp, int tiled,
                                                        const int32_t* __restrict__ seqlens,
-                                                       int C, int Hkv) {
+                                                       int C, int Hkv, const u16* __restrict__ x2,
+                                                       const u16* __restrict__ wt2,
+                                                       u16* __restrict__ xc2,
+                                                       u16* __restrict__ xct2) {
   constexpr int CT = D / 64;  // 16-wide feature tiles per wave
+  if (blockIdx.z == 1) {  // the second operand set (values, when keys and values share a launch)
+    x = x2;
+    wt = wt2;
+    xc = xc2;
+    xct = xct2;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
   const long bh = blockIdx.y;
@@ -425,18 +434,20 @@ void launch_compress_few(const uint16_t* const x[2], const uint16_t* const wt[2]
 
 void launch_compress(const uint16_t* x, const uint16_t* wt, uint16_t* xc, uint16_t* xct, int BH,
                      int T, int D, int l, int d, int ncmp, int rows_alloc, int ncp, bool tiled,
-                     hipStream_t s, const int32_t* seqlens, int C, int Hkv) {
+                     hipStream_t s, const int32_t* seqlens, int C, int Hkv, const uint16_t* x2,
+                     const uint16_t* wt2, uint16_t* xc2, uint16_t* xct2) {
   int rows = rows_alloc > ncp ? rows_alloc : ncp;
   // append mode: at most C / d + 1 tokens are completed per sequence
   if (seqlens != nullptr) rows = C / d + 1 < ncmp ? C / d + 1 : ncmp;
   if (rows <= 0) return;
-  dim3 grid((rows + 63) / 64, BH);
+  dim3 grid((rows + 63) / 64, BH, x2 != nullptr ? 2 : 1);
   if (D == 128)
     compress_kernel<128><<<grid, 256, 0, s>>>(x, wt, xc, xct, T, l, d, ncmp, rows_alloc, ncp,
-                                              tiled ? 1 : 0, seqlens, C, Hkv);
+                                              tiled ? 1 : 0, seqlens, C, Hkv, x2, wt2, xc2,
+                                              xct2);
   else
     compress_kernel<64><<<grid, 256, 0, s>>>(x, wt, xc, xct, T, l, d, ncmp, rows_alloc, ncp,
-                                             tiled ? 1 : 0, seqlens, C, Hkv);
+                                             tiled ? 1 : 0, seqlens, C, Hkv, x2, wt2, xc2, xct2);
 }
 
 }  // namespace nsa

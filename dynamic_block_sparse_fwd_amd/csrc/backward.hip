@@ -695,38 +695,72 @@ __global__ __launch_bounds__(256) void bwd_cmp_reduce_kernel(BwdArgs a) {
   a.dvc[e] = sv;
 }
 
-// dK[s] += sum over the compressed tokens i covering s of dKc[i] W[s - i d]^T (same for V);
-// one thread per (sequence-head, token, feature).
+// dK[s] += sum over the compressed tokens i covering s of dKc[i] W[s - i d]^T (same for V), as
+// one matrix-core GEMM per residue r = s mod d: token s = u d + r receives
+// sum_q dKc[u - q] W[r + q d]^T over q = 0 .. ceil(l / d) - 1 (terms with u - q outside
+// [0, n_cmp) or r + q d >= l drop out), so every output row has one writer.  The fp32 dKc
+// enters the matrix core as a bf16 pair (hi + lo, 2^-17 relative), the weight exactly.
+// Workgroup: 64 values of u x D features of one (sequence-head, residue) for keys (z = 0) or
+// values (z = 1); wave w owns features [w D/4, (w+1) D/4).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_cmp_dx_kernel(BwdArgs a) {
-  const long e = (long)blockIdx.x * 256 + threadIdx.x;
-  const long n = (long)a.B * a.Hkv * a.T * D;
-  if (e >= n) return;
-  const int f = (int)(e % D);
-  const long r = e / D;
-  const int s = (int)(r % a.T);
-  const long bg = r / a.T;
-  int i0 = s - a.l + 1 <= 0 ? 0 : (s - a.l + 1 + a.d - 1) / a.d;
-  int i1 = s / a.d;
-  i1 = i1 < a.ncmp - 1 ? i1 : a.ncmp - 1;
-  float gk = 0.f, gv = 0.f;
-  for (int i = i0; i <= i1; ++i) {
-    const int j = s - i * a.d;
-    const float* ck = a.dkc + (bg * a.NCP + i) * D;
-    const float* cv = a.dvc + (bg * a.NCP + i) * D;
-    const u16* wkr = a.wk + ((long)j * D + f) * D;
-    const u16* wvr = a.wv + ((long)j * D + f) * D;
-    for (int c = 0; c < D; c += 8) {
-      const bf16x8 wk8 = load8(wkr + c), wv8 = load8(wvr + c);
+  constexpr int CT = D / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const int u0 = blockIdx.x * 64;
+  const int r = (int)(blockIdx.y % a.d);
+  const long bg = blockIdx.y / a.d;
+  const int kv = blockIdx.z;
+  const float* dxc = (kv ? a.dvc : a.dkc) + bg * (long)a.NCP * D;
+  const u16* w = kv ? a.wv : a.wk;
+  float* dx = (kv ? a.dv : a.dk) + bg * (long)a.T * D;
+  f32x4 acc[CT][4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        gk = fmaf(ck[c + u], (float)wk8[u], gk);
-        gv = fmaf(cv[c + u], (float)wv8[u], gv);
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) acc[ct][it] = zero4();
+  for (int q = 0; r + q * a.d < a.l; ++q) {
+    const int j = r + q * a.d;
+    for (int kk = 0; kk < D / 32; ++kk) {
+      bf16x8 bw[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        bw[ct] = load8(w + ((long)j * D + wave * (D / 4) + ct * 16 + r16) * D + 32 * kk + 8 * g4);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int i = u0 + it * 16 + r16 - q;
+        bf16x8 hi, lo;
+        if (i >= 0 && i < a.ncmp) {
+          const float4* src = reinterpret_cast<const float4*>(dxc + (long)i * D + 32 * kk + 8 * g4);
+          const float4 x0 = src[0], x1 = src[1];
+          const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            hi[e] = (__bf16)xv[e];
+            lo[e] = (__bf16)(xv[e] - (float)hi[e]);
+          }
+        } else {
+          hi = zero8();
+          lo = zero8();
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          acc[ct][it] = mfma16x16x32(hi, bw[ct], acc[ct][it]);
+          acc[ct][it] = mfma16x16x32(lo, bw[ct], acc[ct][it]);
+        }
       }
     }
   }
-  a.dk[r * D + f] += gk;
-  a.dv[r * D + f] += gv;
+  // lane holds C[u = u0 + it*16 + 4*g4 + e][feature wave*D/4 + ct*16 + r16]
+#pragma unroll
+  for (int it = 0; it < 4; ++it)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const long s = (long)(u0 + it * 16 + 4 * g4 + e) * a.d + r;
+      if (s >= a.T) continue;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) dx[s * D + wave * (D / 4) + ct * 16 + r16] += acc[ct][it][e];
+    }
 }
 
 // dW[j][e][c] = sum over (sequence-head, token i) of x[i d + j][e] dXc[i][c]: 64 x 64 output
@@ -801,8 +835,8 @@ static void launch_bwd_d(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) {
   if (a.ncmp > 0) {
     const long nr = (long)a.B * a.Hkv * a.NCP * D;
     bwd_cmp_reduce_kernel<<<(unsigned)((nr + 255) / 256), 256, 0, s>>>(a);
-    const long nx = (long)a.B * a.Hkv * a.T * D;
-    bwd_cmp_dx_kernel<D><<<(unsigned)((nx + 255) / 256), 256, 0, s>>>(a);
+    const int nu = (a.T + a.d - 1) / a.d;  // token s = u d + r for u < nu
+    bwd_cmp_dx_kernel<D><<<dim3((nu + 63) / 64, a.B * a.Hkv * a.d, 2), 256, 0, s>>>(a);
     bwd_cmp_dw_kernel<D><<<dim3(D / 64, D / 64, 2 * a.l), 256, 0, s>>>(a);
   } else {
     launch_fill_zero(a.dwk, (size_t)a.l * D * D, s);

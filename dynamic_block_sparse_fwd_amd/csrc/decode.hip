@@ -478,7 +478,7 @@ __global__ __launch_bounds__(kGrpThreads, 1) void dec_group_kernel(DecodeArgs a)
   __shared__ float lse_s[16];
   __shared__ int sidx[64];
   __shared__ int tl_s[kMaxTiles];
-  __shared__ int tn_s, next_s;
+  __shared__ int tn_s;
   __shared__ float Wm[2][kGrpWaves][16], Wl[2][kGrpWaves][16];
   __shared__ __align__(16) u16 Qs[16][D + 8];  // the group's queries (MFMA B operand rows)
   const GroupLds L = group_lds(D, a.NCH, a.NT, a.nblk);
@@ -692,10 +692,7 @@ __global__ __launch_bounds__(kGrpThreads, 1) void dec_group_kernel(DecodeArgs a)
       if (code >= 0) tl_s[pos] = code;
       base += (int)__popcll(m);
     }
-    if (lane == 0) {
-      tn_s = base;
-      next_s = kGrpWaves;  // entries 0..7 go to waves 0..7, the rest to whichever wave asks
-    }
+    if (lane == 0) tn_s = base;
   }
   lds_barrier();  // tile list ready; the selection state in the shared region is dead
   // compressed output of this thread's pairs: sum over chunks of co * exp2(cm - lse)
@@ -711,8 +708,9 @@ __global__ __launch_bounds__(kGrpThreads, 1) void dec_group_kernel(DecodeArgs a)
     ocmp[i] = o;
   }
 
-  // 3. the tiles: wave w starts on list entry w and takes the next unclaimed entry (an LDS
-  // counter) when it requests its next tile, so a wave held up by slow loads takes fewer
+  // 3. the tiles: wave w takes list entries w, w + 8, ... (a fixed assignment: the same wave
+  // sums the same tiles in the same order on every call, so the output is reproducible bit for
+  // bit; handing entries to whichever wave asks first balanced slow loads for 1.3 us less)
   const int tn = __builtin_amdgcn_readfirstlane(tn_s);
   float mrun[2] = {kNegInf, kNegInf}, lrun[2] = {0.f, 0.f};
   f32x4 O[2][DT];
@@ -729,9 +727,7 @@ __global__ __launch_bounds__(kGrpThreads, 1) void dec_group_kernel(DecodeArgs a)
       const int k0 = (code & 0x3FFFFFFF) * 64;
       const bool in_slc = (code >> 30) & 1, in_win = k0 + 63 >= w0;
       // the next tile; after the last one every row of the "next" load is row t (one line)
-      int en = 0;
-      if (lane == 0) en = atomicAdd(&next_s, 1);
-      en = __builtin_amdgcn_readfirstlane(en);
+      const int en = e + kGrpWaves;  // static round robin: the same wave sums the same tiles
       const bool more = en < tn;
       const int k1 =
           more ? (__builtin_amdgcn_readfirstlane(tl_s[en]) & 0x3FFFFFFF) * 64 : t;

@@ -213,10 +213,8 @@ int nsa_prefill_timed(const nsa_config* cfg, const void* q, const void* k, const
  *   seqlens        int32 [B], 1 <= seqlens[b] <= Lmax (device memory)
  *   gate           fp32 [B, Hq, 3];  out fp32 [B, Hq, D]
  *   sel_idx        int32 [B, Hkv, top_n] or NULL
- * The selected indices are deterministic; the output varies between calls by the bf16 rounding
- * of the probabilities fed to the matrix core (about 1e-4 at unit scale): a group's tiles go to
- * whichever wave asks first, and each wave takes its probabilities against its own running
- * maximum.  Captures into a HIP graph (kernels only, no allocation, no memset).
+ * Deterministic: the same inputs give the same output and indices bit for bit.  Captures into a
+ * HIP graph (kernels only, no allocation, no memset).
  * Returns NSA_ERR_UNSUPPORTED when top_n * sel_block / 64 + ceil(window / 64) + 1 > 160
  * (tile table), Lmax > 2^24, or the per-group selection state (chunk statistics, tile
  * references, block scores) outgrows 152 KB of LDS (the workgroup's other LDS and it share

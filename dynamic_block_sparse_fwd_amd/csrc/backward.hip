@@ -5,9 +5,10 @@
 // compressed token passes the gradient unchanged.
 //
 // A position's 16 query heads (G = 16) form one 16-row matrix-core tile.  Per branch:
-//   bwd_q_kernel   query-major, one wave per position: a first pass over the branch's 64-key
-//                  tiles gives the log2-sum-exp2 of the scaled scores and <dO, o> (online
-//                  softmax), a second pass dq += scale * dS K;
+//   bwd_q_kernel   query-major, one wave per position, one online pass over the branch's
+//                  64-key tiles: the log2-sum-exp2 of the scaled scores, <dO, o> and
+//                  dq += scale * dS K (dS taken against the running mean of dP', corrected as
+//                  the mean moves);
 //   bwd_kv_kernel  key-major, one workgroup per 64-key tile (a wave per 16 keys): over the
 //                  positions that see the tile, two positions (32 rows) per step,
 //                  dV += (g P)^T dO and dK += scale * dS^T q;
@@ -54,6 +55,66 @@ struct KeySet {
   __device__ __forceinline__ bool valid(int key) const { return key >= lo && key <= hi; }
 };
 
+// One tile of the query-major online pass.  With e = exp2(s - m) against the running maximum m,
+// l = sum e and c = sum e dP' / l, the running mean of dP' under p (it ends as <dO, o>):
+//   Z = sum_k e_k (dP'_k - c) K_k,  Bk = sum_k e_k K_k,
+// and when c moves from c0 to c1, Z += (c0 - c1) Bk keeps Z referred to the new mean; at the
+// end dq = scale * g * Z / l = scale * sum_k g p_k (dP'_k - <dO, o>) K_k.  The operand rounded
+// to bf16 for the matrix core is e (dP' - c), small where dP' is near its mean, as in the
+// two-pass form dS = p (dP' - <dO, o>); Bk's own rounding enters only through the moves of c.
+// raw: scaled scores (log2 units, -inf where masked), dp: dP' of the tile's 16 keys per lane
+// (key 32 kc + 8 g4 + i of row r16); kfrag(kc, n) gives the A operand K^T[16 n + r16][32 kc +
+// 8 g4 ..].
+struct OnlineDq {
+  float m = -kInf, lsum = 0.f, acc = 0.f, c = 0.f;
+  template <int DT, class KF>
+  __device__ __forceinline__ void step(float* raw, const float* dp, f32x4* Z, f32x4* Bk,
+                                       KF kfrag) {
+    float mx = raw[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, raw[i]);
+    mx = col_max4(mx);
+    const float mn = fmaxf(m, mx);
+    if (mn == -kInf) return;  // nothing visible yet (the same for every head)
+    const float sc = exp2f(m - mn);
+    if (__ballot(sc != 1.f) != 0) {  // uniform: some head's maximum moved
+#pragma unroll
+      for (int n = 0; n < DT; ++n) { Z[n] *= sc; Bk[n] *= sc; }
+    }
+    float ls = 0.f, as = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      raw[i] = exp2f(raw[i] - mn);  // e from here on
+      ls += raw[i];
+      as += raw[i] * dp[i];
+    }
+    lsum = lsum * sc + col_sum4(ls);
+    acc = acc * sc + col_sum4(as);
+    m = mn;
+    const float cn = acc / lsum;  // lsum >= 1: the maximum's own term
+    const float dc = c - cn;
+    c = cn;
+    if (__ballot(dc != 0.f) != 0) {  // uniform
+#pragma unroll
+      for (int n = 0; n < DT; ++n) Z[n] += dc * Bk[n];
+    }
+    bf16x8 xb[2], eb[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      xb[i >> 3][i & 7] = (__bf16)(raw[i] * (dp[i] - cn));
+      eb[i >> 3][i & 7] = (__bf16)raw[i];
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int n = 0; n < DT; ++n) {
+        const bf16x8 kf = kfrag(kc, n);
+        Z[n] = mfma16x16x32(kf, xb[kc], Z[n]);
+        Bk[n] = mfma16x16x32(kf, eb[kc], Bk[n]);
+      }
+  }
+};
+
 }  // namespace
 
 // dO -> bf16 rows; q and dO with the 16 heads of a (position, group) contiguous per feature.
@@ -88,9 +149,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   }
 }
 
-// Query-major pass of branch BR: lse and <dO, o> per (position, head), then dq.
+// Query-major pass of branch BR: lse, <dO, o> and dq per (position, head), one pass.
 template <int D, int BR>
-__global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdArgs a) {
   constexpr int DC = D / 32, DT = D / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
@@ -166,70 +227,37 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdArgs a) {
       }
   };
 
-  // pass 1: online log2-sum-exp2 and sum of p * dP'
-  float m = -kInf, lsum = 0.f, acc = 0.f;
+  f32x4 Z[DT], Bk[DT];
+#pragma unroll
+  for (int n = 0; n < DT; ++n) { Z[n] = zero4(); Bk[n] = zero4(); }
+  OnlineDq st;
   for (int e = 0; e < ntiles; ++e) {
     const int base = tile_base(e);
     if (base < 0) continue;
     float raw[16], dp[16];
     tile(base, raw, dp);
-    float mx = raw[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, raw[i]);
-    mx = col_max4(mx);
-    const float mn = fmaxf(m, mx);
-    if (mn == -kInf) continue;  // nothing visible yet (the same for every head)
-    const float sc = exp2f(m - mn);
-    float ls = 0.f, as = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = exp2f(raw[i] - mn);
-      ls += p;
-      as += p * dp[i];
-    }
-    lsum = lsum * sc + col_sum4(ls);
-    acc = acc * sc + col_sum4(as);
-    m = mn;
+    st.step<DT>(raw, dp, Z, Bk, [&](int kc, int n) {
+      return load8(kcols + (long)(16 * n + r16) * pitch + base + 32 * kc + 8 * g4);
+    });
   }
-  const bool any = lsum > 0.f;
-  const float lse2 = any ? m + __log2f(lsum) : kInf;  // no key: every p is 0
-  const float dl = any ? acc / lsum : 0.f;
+  const bool any = st.lsum > 0.f;
+  const float lse2 = any ? st.m + __log2f(st.lsum) : kInf;  // no key: every p is 0
+  const float dl = any ? st.c : 0.f;
   if (g4 == 0) {
     const long o = (long)BR * a.B * a.T * Hq + myrow;
     a.lse[o] = lse2;
     a.dlt[o] = dl;
     a.dgate[myrow * 3 + BR] = dl;
   }
-
-  // pass 2: dq^T += K^T dS^T
+  const float f = any ? a.scale * gt / st.lsum : 0.f;
   f32x4 dq[DT];
 #pragma unroll
-  for (int n = 0; n < DT; ++n) dq[n] = zero4();
-  if (any) {
-    for (int e = 0; e < ntiles; ++e) {
-      const int base = tile_base(e);
-      if (base < 0) continue;
-      float raw[16], dp[16];
-      tile(base, raw, dp);
-      float ds[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ds[i] = gt * exp2f(raw[i] - lse2) * (dp[i] - dl);
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const bf16x8 pb = pack8(ds + 8 * kc);
-#pragma unroll
-        for (int n = 0; n < DT; ++n)
-          dq[n] = mfma16x16x32(
-              load8(kcols + (long)(16 * n + r16) * pitch + base + 32 * kc + 8 * g4), pb, dq[n]);
-      }
-    }
-  }
+  for (int n = 0; n < DT; ++n) dq[n] = Z[n] * f;
   // lane holds dq^T[feature 16 n + 4 g4 + i][head r16]
   float* dqp = a.dq + myrow * D;
 #pragma unroll
   for (int n = 0; n < DT; ++n) {
-    float4 v = make_float4(a.scale * dq[n][0], a.scale * dq[n][1], a.scale * dq[n][2],
-                           a.scale * dq[n][3]);
+    float4 v = make_float4(dq[n][0], dq[n][1], dq[n][2], dq[n][3]);
     float4* dst = reinterpret_cast<float4*>(dqp + 16 * n + 4 * g4);
     if constexpr (BR != kBrCmp) {
       const float4 o = *dst;
@@ -317,59 +345,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_shared_kernel(BwdArgs a) {
       }
   };
 
-  // pass 1: online log2-sum-exp2 and sum of p * dP'
-  float m = -kInf, lsum = 0.f, acc = 0.f;
-  {
-    KTileRegs<D, NT> kr, vr;
-    if (kt0 <= kt1) {
-      kr.load(krows, (long)kt0 * 64, klim);
-      vr.load(vrows, (long)kt0 * 64, klim);
-    }
-    for (int kt = kt0; kt <= kt1; ++kt) {
-      kr.store(Ks);
-      vr.store(Vr);
-      lds_barrier();
-      if (kt < kt1) {
-        kr.load(krows, (long)(kt + 1) * 64, klim);
-        vr.load(vrows, (long)(kt + 1) * 64, klim);
-      }
-      float raw[16], dp[16];
-      tile(kt * 64, raw, dp);
-      float mx = raw[0];
+  // one online pass (OnlineDq): the three tiles of each step staged once
+  f32x4 Z[DT], Bk[DT];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, raw[i]);
-      mx = col_max4(mx);
-      const float mn = fmaxf(m, mx);
-      if (mn != -kInf) {  // uniform per wave (every head shares the key mask)
-        const float sc = exp2f(m - mn);
-        float ls = 0.f, as = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = exp2f(raw[i] - mn);
-          ls += p;
-          as += p * dp[i];
-        }
-        lsum = lsum * sc + col_sum4(ls);
-        acc = acc * sc + col_sum4(as);
-        m = mn;
-      }
-      lds_barrier();
-    }
-  }
-  const bool any = lsum > 0.f;
-  const float lse2 = any ? m + __log2f(lsum) : kInf;
-  const float dl = any ? acc / lsum : 0.f;
-  if (live && g4 == 0) {
-    const long o = (long)BR * a.B * a.T * Hq + myrow;
-    a.lse[o] = lse2;
-    a.dlt[o] = dl;
-    a.dgate[myrow * 3 + BR] = dl;
-  }
-
-  // pass 2: dq^T += K^T dS^T
-  f32x4 dq[DT];
-#pragma unroll
-  for (int n = 0; n < DT; ++n) dq[n] = zero4();
+  for (int n = 0; n < DT; ++n) { Z[n] = zero4(); Bk[n] = zero4(); }
+  OnlineDq st;
   {
     KTileRegs<D, NT> kr, vr;
     VTileRegs<D, NT> tr;
@@ -388,30 +368,32 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_shared_kernel(BwdArgs a) {
         vr.load(vrows, (long)(kt + 1) * 64, klim);
         tr.load(kcols, pitch, (long)(kt + 1) * 64);
       }
-      if (any) {
-        float raw[16], dp[16];
-        tile(kt * 64, raw, dp);
-        float ds[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ds[i] = gt * exp2f(raw[i] - lse2) * (dp[i] - dl);
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          const bf16x8 pb = pack8(ds + 8 * kc);
-          const int ch = ((4 * kc + g4) ^ (r16 & 7)) * 8;
-#pragma unroll
-          for (int n = 0; n < DT; ++n)
-            dq[n] = mfma16x16x32(load8(&Kt[16 * n + r16][ch]), pb, dq[n]);
-        }
-      }
+      float raw[16], dp[16];
+      tile(kt * 64, raw, dp);
+      st.step<DT>(raw, dp, Z, Bk, [&](int kc, int n) {
+        return load8(&Kt[16 * n + r16][((4 * kc + g4) ^ (r16 & 7)) * 8]);
+      });
       lds_barrier();
     }
   }
+  const bool any = st.lsum > 0.f;
+  const float lse2 = any ? st.m + __log2f(st.lsum) : kInf;
+  const float dl = any ? st.c : 0.f;
+  if (live && g4 == 0) {
+    const long o = (long)BR * a.B * a.T * Hq + myrow;
+    a.lse[o] = lse2;
+    a.dlt[o] = dl;
+    a.dgate[myrow * 3 + BR] = dl;
+  }
+  const float f = any ? a.scale * gt / st.lsum : 0.f;
+  f32x4 dq[DT];
+#pragma unroll
+  for (int n = 0; n < DT; ++n) dq[n] = Z[n] * f;
   if (!live) return;
   float* dqp = a.dq + myrow * D;
 #pragma unroll
   for (int n = 0; n < DT; ++n) {
-    float4 v = make_float4(a.scale * dq[n][0], a.scale * dq[n][1], a.scale * dq[n][2],
-                           a.scale * dq[n][3]);
+    float4 v = make_float4(dq[n][0], dq[n][1], dq[n][2], dq[n][3]);
     float4* dst = reinterpret_cast<float4*>(dqp + 16 * n + 4 * g4);
     if constexpr (BR != kBrCmp) {
       const float4 o = *dst;

@@ -54,7 +54,18 @@ CASES = [
     ("no_compressed_T20", 1, 20, 1, 128, {}),
     # an adaptive top-p selection: index rows of varying length, -1 padded
     ("topp0.4_T800_D128", 1, 800, 2, 128, dict(top_p=0.4)),
+    # values with a large common part: dP' = dO . v sits near its mean <dO, o> for every key,
+    # so dS = p (dP' - <dO, o>) is a small difference of large terms
+    ("v_offset4_T600_D128", 1, 600, 1, 128, dict(v_offset=4.0)),
+    # peaked attention (queries scaled by 4): the running maxima move often and p is nearly
+    # one-hot
+    ("peaked_q4_T600_D64", 1, 600, 2, 64, dict(q_scale=4.0)),
 ]
+
+
+def shifted_bf16(bits, scale=1.0, offset=0.0):
+    """bf16 bits of scale * x + offset, rounded to bf16 (an input transform)."""
+    return S.f32_to_bf16_bits(S.bf16_bits_to_f32(bits) * np.float32(scale) + np.float32(offset))
 
 
 @pytest.mark.parametrize("name,B,T,Hkv,D,extra", CASES, ids=[c[0] for c in CASES])
@@ -63,8 +74,14 @@ def test_backward_parity(name, B, T, Hkv, D, extra):
     nsa.load_library()
     print("case backward", name, flush=True)
     G = 16
+    extra = dict(extra)
+    v_offset, q_scale = extra.pop("v_offset", 0.0), extra.pop("q_scale", 1.0)
     ocfg = O.NsaCfg(B, T, Hkv, G, D, **extra)
     x = S.nsa_prefill_inputs(91 + len(name), B, T, Hkv, G, D)
+    if v_offset:
+        x["v"] = shifted_bf16(x["v"], offset=v_offset)
+    if q_scale != 1.0:
+        x["q"] = shifted_bf16(x["q"], scale=q_scale)
     dout = S.upstream_grad(92 + len(name), (B, T, Hkv * G, D))
     kc = O.compress(x["k"], x["wk"], ocfg.cmp_len, ocfg.cmp_stride)
     vc = O.compress(x["v"], x["wv"], ocfg.cmp_len, ocfg.cmp_stride)

@@ -42,22 +42,29 @@ def poisoned_caches(cfg, kc, vc, seqlens):
     return kp, vt
 
 
-def gpu_decode(cfg, x, kc, vc, seqlens):
+def gpu_decode(cfg, x, kc, vc, seqlens, repeat=False):
+    """nsa_decode on the device; repeat: call it a second time on the same buffers and require
+    the same output and indices bit for bit (decode is deterministic)."""
     import dynamic_block_sparse_fwd_amd as nsa
     nsa.load_library()
     c = nsa.NsaConfig(cfg.B, cfg.T, cfg.Hkv, cfg.G, cfg.D, cfg.cmp_len, cfg.cmp_stride,
                       cfg.sel_block, cfg.top_n, cfg.n_local, cfg.window, cfg.scale,
                       cfg.top_p)
     kp, vt = poisoned_caches(cfg, kc, vc, seqlens)
-    out, idx = nsa.nsa_decode(c, to_dev(x["q"]), to_dev(x["kcache"]), to_dev(x["vcache"]),
-                              to_dev(kp), to_dev(vt), to_dev(np.asarray(seqlens, np.int32)),
-                              to_dev(x["gate"]))
+    args = (to_dev(x["q"]), to_dev(x["kcache"]), to_dev(x["vcache"]), to_dev(kp), to_dev(vt),
+            to_dev(np.asarray(seqlens, np.int32)), to_dev(x["gate"]))
+    out, idx = nsa.nsa_decode(c, *args)
+    if repeat:
+        out2, idx2 = nsa.nsa_decode(c, *args)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, idx2), "decode indices differ between two calls"
+        assert torch.equal(out, out2), "decode output differs between two calls"
     torch.cuda.synchronize()
     return out.cpu().numpy(), idx.cpu().numpy()
 
 
-def check_decode(cfg, x, kc, vc, seqlens, what):
-    gout, gidx = gpu_decode(cfg, x, kc, vc, seqlens)
+def check_decode(cfg, x, kc, vc, seqlens, what, repeat=False):
+    gout, gidx = gpu_decode(cfg, x, kc, vc, seqlens, repeat)
     ora = O.nsa_decode(cfg, x["q"], x["kcache"], x["vcache"], kc, vc, seqlens, x["gate"],
                        want_scores=True)
     rows_t = np.asarray(seqlens) - 1
@@ -104,7 +111,7 @@ def test_decode_parity(name, B, L, Hkv, G, D, seqlens, extra):
     x = S.nsa_decode_inputs(30 + len(name), B, L, Hkv, G, D)
     kc = O.compress(x["kcache"], x["wk"], 32, 16)
     vc = O.compress(x["vcache"], x["wv"], 32, 16)
-    check_decode(cfg, x, kc, vc, seqlens, name)
+    check_decode(cfg, x, kc, vc, seqlens, name, repeat=True)
 
 
 def test_decode_equals_prefill_last_row_on_gpu():
@@ -126,13 +133,14 @@ def test_decode_equals_prefill_last_row_on_gpu():
 
 
 def test_decode_64k_batch32_all_rows():
-    """The 64k decode workload: batch 32, 4 KV heads x group 16, D=128, every sequence full."""
+    """The 64k decode workload: batch 32, 4 KV heads x group 16, D=128, every sequence full;
+    two calls on the same buffers give the same result bit for bit."""
     B, L, Hkv, G, D = 32, 65536, 4, 16, 128
     cfg = O.NsaCfg(B, L, Hkv, G, D)
     x = S.nsa_decode_inputs(3, B, L, Hkv, G, D)
     kc = O.compress(x["kcache"], x["wk"], 32, 16)
     vc = O.compress(x["vcache"], x["wv"], 32, 16)
-    check_decode(cfg, x, kc, vc, [L] * B, "decode 64k x 32")
+    check_decode(cfg, x, kc, vc, [L] * B, "decode 64k x 32", repeat=True)
 
 
 def test_decode_1m_planted_recall():

@@ -115,11 +115,12 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
     for (int rt = 0; rt < RTW; ++rt) {
       if (!full) {  // a real (uniform) branch: full tiles skip the masking arithmetic
         __asm__ volatile("" ::: "memory");
+        // key kt*64 + 32*(e>>3) + 8*g4 + (e&7) is visible iff its offset from the lane's first
+        // key is below lim (one subtraction per lane, constant offsets per element)
+        const int lim = nvis[rt] - (kt * 64 + 8 * g4);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kt * 64 + 32 * (e >> 3) + 8 * g4 + (e & 7);
-          raw[rt][e] = key < nvis[rt] ? raw[rt][e] : kNegInf;
-        }
+        for (int e = 0; e < 16; ++e)
+          raw[rt][e] = 32 * (e >> 3) + (e & 7) < lim ? raw[rt][e] : kNegInf;
       }
       float tm = raw[rt][0];
 #pragma unroll
@@ -276,11 +277,9 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
         for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(raw[rt][kc2 * 8 + e], sl, -rlse[rt]));
         if (!full) {
           __asm__ volatile("" ::: "memory");
+          const int lim = nvis[rt] - (kt * 64 + 32 * kc2 + 8 * g4);  // key offsets e < lim
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int key = kt * 64 + 32 * kc2 + 8 * g4 + e;
-            pv[e] = key < nvis[rt] ? pv[e] : 0.f;
-          }
+          for (int e = 0; e < 8; ++e) pv[e] = e < lim ? pv[e] : 0.f;
         }
         if (ps_zero) {  // uniform: a row of this wave drops p' from P V (rare)
 #pragma unroll
@@ -289,7 +288,29 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
 #pragma unroll
           for (int e = 0; e < 8; ++e) pbt[rt][kc2][e] = (__bf16)pv[e];
         }
-        if constexpr (FAST) {
+        if constexpr (FAST && G == 16) {
+          const float cA = (pv[0] + pv[1]) + pv[2] + 0.5f * pv[3];
+          const float cB = (pv[4] + pv[5]) + pv[6] + 0.5f * pv[7];
+          const float h3 = 0.5f * pv[3];
+          const float h7 = 0.5f * pv[7];
+          // the four sums over the row's 16 lanes (the group's heads) at once: each step pairs
+          // lanes that keep complementary halves of the values and adds what the partner sends;
+          // lane r16 ends with the sum of value r16 / 4 (cA, cB, h3, h7), every block through
+          // the same association
+          const bool hi = r16 >= 8, b2 = (r16 & 4) != 0;
+          float x = hi ? h3 : cA, u = hi ? h7 : cB;
+          x += dpp_f<kDppMirror>(hi ? cA : h3);  // partner 15 - r16
+          u += dpp_f<kDppMirror>(hi ? cB : h7);
+          float v = b2 ? u : x;
+          v += dpp_f<kDppHalfMirror>(b2 ? x : u);  // partner 7 - r16 of its half
+          v += xor_lane_f<2>(v);
+          v += xor_lane_f<1>(v);
+          if ((r16 & 3) == 0) {
+            const int tq = r / G, jl = 8 * kc2 + 2 * g4, which = r16 >> 2;
+            float* dst = which < 2 ? &Cb[tq][jl + which] : &Hb[tq][jl + which - 1];
+            *dst = v;
+          }
+        } else if constexpr (FAST) {
           const float cA = head_sum<G>((pv[0] + pv[1]) + pv[2] + 0.5f * pv[3]);
           const float cB = head_sum<G>((pv[4] + pv[5]) + pv[6] + 0.5f * pv[7]);
           const float h3 = head_sum<G>(0.5f * pv[3]);

@@ -99,90 +99,145 @@ struct TopList {
   }
 };
 
-// One wave scores 64 queries (four 16-query sub-tiles, one query block) against every past
-// block key on the matrix core: each 16-block tile of kbar (bf16 hi and lo parts) is loaded
-// once and multiplies all four sub-tiles.  Every lane keeps the top KS of its four blocks per
-// tile for its queries; the four lanes of a query then merge.  The ascending index list is
-// written.
+// One workgroup scores 512 consecutive queries (8 waves x four 16-query sub-tiles) against every
+// past block key on the matrix core.  Each 16-block tile of kbar (bf16 hi and lo parts) is
+// staged in LDS once for the eight waves (double-buffered, one barrier per tile; its rows
+// chunk-swizzled so the 16 rows one operand read touches fall on distinct banks) and multiplies
+// all of a wave's sub-tiles, as four independent accumulation chains; three tiles' loads are in
+// flight.  Every lane keeps the top KS of its four blocks per tile for its queries; the four
+// lanes of a query then merge.  The ascending index list is written.
+constexpr int kGateWaves = 8;
+
+template <int D>
+__device__ __forceinline__ int gate_swz(int row) { return row & (D / 8 - 1); }
+
 template <int D, int KS>
-__global__ __launch_bounds__(256) void moba_gate_kernel(MobaArgs a) {
-  constexpr int NU = 4;
+__global__ __launch_bounds__(kGateWaves * 64) void moba_gate_kernel(MobaArgs a) {
+  constexpr int NU = 4, DC = D / 8;
+  __shared__ __align__(16) u16 kbs[2][2][16][D];  // [buffer][hi, lo][block of the tile][feature]
   const int h = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
-  const int t0 = (blockIdx.x * 4 + wave) * 64;
-  if (t0 >= a.T) return;
-  const int bq = t0 / a.block;  // the wave's 64 queries share one block (block % 64 == 0)
+  const int tw = blockIdx.x * kGateWaves * 64;  // the workgroup's first query
+  const int t0 = tw + wave * 64;
+  const bool live = t0 < a.T;  // dead waves still pass the barriers
+  const int bq = live ? t0 / a.block : 0;  // the wave's 64 queries share one block
+  const int tlast = (tw + kGateWaves * 64 < a.T ? tw + kGateWaves * 64 : a.T) - 1;
+  const int bq_max = tlast / a.block;  // the largest bq of the workgroup
   const long bh = (long)b * a.H + h;
   const int K = a.top_k;
   const int nsel = bq < K ? bq : K;
+  const bool scoring = live && K > 0 && bq > K;  // uniform per wave
   int chosen[NU][KS];
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
     for (int s = 0; s < KS; ++s) chosen[u][s] = s;  // bq <= top_k: blocks 0 .. bq-1
-  if (K > 0 && bq > K) {
+  if (K > 0 && bq_max > K) {  // uniform per workgroup
     bf16x8 qf[NU][D / 32];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const u16* qp = a.q + (((long)b * a.T + t0 + 16 * u + r16) * a.H + h) * D + 8 * g4;
+      const int tq = scoring ? t0 + 16 * u + r16 : 0;
+      const u16* qp = a.q + (((long)b * a.T + tq) * a.H + h) * D + 8 * g4;
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) qf[u][c] = load8(qp + 32 * c);
     }
+    // staging: thread -> (hi/lo part, row, 16-byte chunk); 4 D threads stage a tile (past the
+    // last block the last one is loaded again, so the loads are unconditional)
+    const bool stager = tid < 4 * D;
+    const int spart = tid / (16 * DC), srow = (tid / DC) % 16, sch = tid % DC;
+    const u16* sbase = (spart ? a.kb_lo : a.kb_hi) + bh * a.nb * D + 8 * sch;
+    auto fetch = [&](int jt) -> u32x4 {
+      int jr = jt * 16 + srow;
+      jr = jr < bq_max ? jr : bq_max - 1;
+      return *reinterpret_cast<const u32x4*>(sbase + (long)jr * D);
+    };
+    const int nt = (bq_max + 15) / 16;
+    // one sweep over the tiles: visit(jt, x) receives, per sub-tile u, the scores x[u][i] of
+    // block jt * 16 + 4 g4 + i for this lane's query (-inf past the wave's own past blocks)
+    auto sweep = [&](auto visit) {
+      // three tiles' loads in flight (an L2 round trip outlasts one tile's products)
+      const u32x4 z4 = {0u, 0u, 0u, 0u};
+      u32x4 p0 = stager ? fetch(0) : z4, p1 = stager ? fetch(1) : z4, p2 = stager ? fetch(2) : z4;
+      for (int jt = 0; jt < nt; ++jt) {
+        const int buf = jt & 1;
+        if (stager)
+          *reinterpret_cast<u32x4*>(&kbs[buf][spart][srow][8 * (sch ^ gate_swz<D>(srow))]) = p0;
+        __syncthreads();  // tile jt staged; tile jt - 1's buffer is free again
+        p0 = p1;
+        p1 = p2;
+        if (stager) p2 = fetch(jt + 3);
+        if (scoring && jt * 16 < bq) {  // uniform per wave
+          bf16x8 kh[D / 32], kl[D / 32];
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c) {
+            const int ch = 8 * ((4 * c + g4) ^ gate_swz<D>(r16));
+            kh[c] = load8(&kbs[buf][0][r16][ch]);
+            kl[c] = load8(&kbs[buf][1][r16][ch]);
+          }
+          f32x4 acc[NU];
+#pragma unroll
+          for (int u = 0; u < NU; ++u) acc[u] = zero4();
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+              acc[u] = mfma16x16x32(kh[c], qf[u][c], acc[u]);
+              acc[u] = mfma16x16x32(kl[c], qf[u][c], acc[u]);
+            }
+          float x[NU][4];
+#pragma unroll
+          for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              x[u][i] = jt * 16 + 4 * g4 + i < bq ? acc[u][i] : kNegInf;
+          visit(jt, x);
+        }
+      }
+    };
     TopList<KS> lst[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) lst[u].init();
-    const u16* hib = a.kb_hi + bh * a.nb * D + 8 * g4;
-    const u16* lob = a.kb_lo + bh * a.nb * D + 8 * g4;
-    for (int jt = 0; jt * 16 < bq; ++jt) {
-      int jr = jt * 16 + r16;
-      jr = jr < bq ? jr : bq - 1;
-      bf16x8 kh[D / 32], kl[D / 32];
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        kh[c] = load8(hib + (long)jr * D + 32 * c);
-        kl[c] = load8(lob + (long)jr * D + 32 * c);
-      }
+    sweep([&](int jt, float (&x)[NU][4]) {
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        f32x4 acc = zero4();
+        // an insert that does not beat the list's last entry changes nothing; the inserts run
+        // only when some lane of the wave needs one
+        const float mx = fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3]));
+        if (__ballot(mx > lst[u].v[KS - 1]) != 0) {  // uniform
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) {
-          acc = mfma16x16x32(kh[c], qf[u][c], acc);
-          acc = mfma16x16x32(kl[c], qf[u][c], acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = jt * 16 + 4 * g4 + i;
-          lst[u].insert(j < bq ? acc[i] : kNegInf, j);
+          for (int i = 0; i < 4; ++i) lst[u].insert(x[u][i], jt * 16 + 4 * g4 + i);
         }
       }
-    }
-    // merge the four lanes (L, L^16, L^32, L^48) that hold one query's candidates
+    });
+    if (scoring) {
+      // merge the four lanes (L, L^16, L^32, L^48) that hold one query's candidates
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
+      for (int u = 0; u < NU; ++u) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if (s < K) {
-          const uint64_t mine =
-              lst[u].v[0] == kNegInf ? 0 : signed_rank_key(lst[u].v[0], lst[u].j[0]);
-          const uint64_t m = col_max4_u64(mine);
-          if (mine == m) lst[u].pop();
-          chosen[u][s] = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFu));
-        }
-      }
-      // ascending order of the K chosen blocks
-#pragma unroll
-      for (int x = 0; x < KS; ++x)
-#pragma unroll
-        for (int y = 0; y + 1 < KS; ++y)
-          if (y + 1 < K && chosen[u][y] > chosen[u][y + 1]) {
-            const int tmp = chosen[u][y];
-            chosen[u][y] = chosen[u][y + 1];
-            chosen[u][y + 1] = tmp;
+        for (int s = 0; s < KS; ++s) {
+          if (s < K) {
+            const uint64_t mine =
+                lst[u].v[0] == kNegInf ? 0 : signed_rank_key(lst[u].v[0], lst[u].j[0]);
+            const uint64_t m = col_max4_u64(mine);
+            if (mine == m) lst[u].pop();
+            chosen[u][s] = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFu));
           }
+        }
+        // ascending order of the K chosen blocks
+#pragma unroll
+        for (int x = 0; x < KS; ++x)
+#pragma unroll
+          for (int y = 0; y + 1 < KS; ++y)
+            if (y + 1 < K && chosen[u][y] > chosen[u][y + 1]) {
+              const int tmp = chosen[u][y];
+              chosen[u][y] = chosen[u][y + 1];
+              chosen[u][y + 1] = tmp;
+            }
+      }
     }
   }
+  if (!live) return;  // after the workgroup's last barrier
   if (g4 == 0) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -592,9 +647,9 @@ static void launch_moba_k(const MobaArgs& a, hipStream_t s, hipEvent_t* ev) {
     if (ev != nullptr) (void)hipEventRecord(ev[i], s);
   };
   const long rows = (long)a.B * a.T * a.H;
-  const dim3 gp(a.nb, a.B * a.H), gg((a.T / 64 + 3) / 4, a.H, a.B);
+  const dim3 gp(a.nb, a.B * a.H), gg((a.T + kGateWaves * 64 - 1) / (kGateWaves * 64), a.H, a.B);
   moba_pool_kernel<D><<<gp, 256, 0, s>>>(a);
-  moba_gate_kernel<D, KS><<<gg, 256, 0, s>>>(a);
+  moba_gate_kernel<D, KS><<<gg, kGateWaves * 64, 0, s>>>(a);
   mark(1);
   moba_count_kernel<KS><<<dim3(kMobaChunks, a.H, a.B), kCountThreads,
                           (size_t)a.nb * sizeof(int), s>>>(a);

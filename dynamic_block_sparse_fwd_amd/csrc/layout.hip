@@ -129,7 +129,7 @@ void launch_cmp_cache_layout(const uint16_t* kc, const uint16_t* vtiles, uint16_
 
 // Computes the transposed tile  C^T[c][i] = sum_k Wt[c][k] * X_i[k]  where X_i is the l*D
 // contiguous elements of x starting at token i*d (the l tokens of compressed token i), so the
-// A operand is the weight and the B operand the token window; both are 16-byte loads.
+// A operand is the weight and the B operand the token window, both staged in LDS.
 // Workgroup: 64 compressed tokens x D features; wave w owns features [w*D/4, (w+1)*D/4).
 // Half-width of the band around a bf16 rounding midpoint inside which an fp32 accumulation is
 // re-done in fp64 (absolute below 1, relative above).  fp32 accumulation errors of these sums
@@ -178,28 +178,65 @@ __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = zero4();
 
-  if (ihi > 0) {
-    long xrow[4];
+  if (ihi > 0) {  // uniform
+    // A GEMM over k = l*D in 64-wide steps: the 64 token windows (each l*D contiguous elements
+    // of x) and the weight rows are staged in LDS once per step for the four waves
+    // (double-buffered, one barrier per step; 16-byte chunks swizzled by row so the 16 rows an
+    // operand read touches fall on distinct banks), the next step's loads in flight.
+    __shared__ __align__(16) u16 xs[2][64][64];
+    __shared__ __align__(16) u16 ws[2][D][64];
+    constexpr int XQ = 64 * 8 / 256, WQ = D * 8 / 256;  // 16-byte chunks per thread
+    const int tid = threadIdx.x;
+    const u16* xsrc[XQ];
+    const u16* wsrc[WQ];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      int i = i0 + it * 16 + r16;
+    for (int r = 0; r < XQ; ++r) {
+      const int q = tid + 256 * r, tok = q / 8, ch = q % 8;
+      int i = i0 + tok;
       i = i < ihi ? i : ihi - 1;  // clamp: rows past ihi are computed and discarded
-      xrow[it] = (long)i * d * D;
+      xsrc[r] = xb + (long)i * d * D + 8 * ch;
     }
-    const u16* wrow[CT];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) wrow[ct] = wt + (long)(wave * (D / 4) + ct * 16 + r16) * K;
-    for (int k0 = 0; k0 < K; k0 += 32) {
-      const int ko = k0 + 8 * g4;
-      bf16x8 bx[4], aw[CT];
+    for (int r = 0; r < WQ; ++r) {
+      const int q = tid + 256 * r;
+      wsrc[r] = wt + (long)(q / 8) * K + 8 * (q % 8);
+    }
+    u32x4 px[XQ], pw[WQ];
+    auto fetch = [&](int k0) {
 #pragma unroll
-      for (int it = 0; it < 4; ++it) bx[it] = load8(xb + xrow[it] + ko);
+      for (int r = 0; r < XQ; ++r) px[r] = *reinterpret_cast<const u32x4*>(xsrc[r] + k0);
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) aw[ct] = load8(wrow[ct] + ko);
+      for (int r = 0; r < WQ; ++r) pw[r] = *reinterpret_cast<const u32x4*>(wsrc[r] + k0);
+    };
+    const int nks = K / 64;
+    fetch(0);
+    for (int ks = 0; ks < nks; ++ks) {
+      const int buf = ks & 1;
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
+      for (int r = 0; r < XQ; ++r) {
+        const int q = tid + 256 * r, tok = q / 8, ch = q % 8;
+        *reinterpret_cast<u32x4*>(&xs[buf][tok][8 * (ch ^ (tok & 7))]) = px[r];
+      }
 #pragma unroll
-        for (int it = 0; it < 4; ++it) acc[ct][it] = mfma16x16x32(aw[ct], bx[it], acc[ct][it]);
+      for (int r = 0; r < WQ; ++r) {
+        const int q = tid + 256 * r, f = q / 8, ch = q % 8;
+        *reinterpret_cast<u32x4*>(&ws[buf][f][8 * (ch ^ (f & 7))]) = pw[r];
+      }
+      __syncthreads();  // step ks staged; step ks - 1's buffer is free again
+      fetch(64 * (ks + 1 < nks ? ks + 1 : ks));  // the last step loads itself again
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int ch = 8 * ((4 * kc + g4) ^ (r16 & 7));
+        bf16x8 bx[4], aw[CT];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) bx[it] = load8(&xs[buf][it * 16 + r16][ch]);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) aw[ct] = load8(&ws[buf][wave * (D / 4) + ct * 16 + r16][ch]);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int it = 0; it < 4; ++it) acc[ct][it] = mfma16x16x32(aw[ct], bx[it], acc[ct][it]);
+      }
     }
   }
   // Exact rounding.  The fp32 sum of l*D products carries a small accumulation error; where

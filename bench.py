@@ -294,26 +294,11 @@ def decode_kv_bytes(idx, seqlens, L, D, l=32, d=16, beta=64, w=512):
     return cmp_b * per_tok, tok_b * per_tok
 
 
-def bench_decode(args, B=32, L=65536, Hkv=4, G=16, D=128, seed=3, calls=20):
-    import torch
-
-    import dynamic_block_sparse_fwd_amd as nsa
-    import synth_inputs as S
-
-    cfg = nsa.NsaConfig(B, L, Hkv, G, D, top_p=args.top_p)
-    t0 = time.time()
-    x = S.nsa_decode_inputs(seed, B, L, Hkv, G, D)
-    print("[bench] decode inputs generated in %.1fs" % (time.time() - t0), file=sys.stderr,
-          flush=True)
-    dev = torch.device("cuda:0")
-    d = {k: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).to(dev)
-         for k, v in x.items()}
-    kc = nsa.nsa_compress(cfg, d["kcache"], d["wk"])
-    vc = nsa.nsa_compress_tiles(cfg, d["vcache"], d["wv"])
-    out = torch.empty((B, Hkv * G, D), dtype=torch.float32, device=dev)
-    idx = torch.empty((B, Hkv, cfg.top_n), dtype=torch.int32, device=dev)
-    ws = torch.empty(nsa.decode_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
-    flush = torch.zeros(1 << 28, dtype=torch.int32, device=dev)  # 1 GiB
+def time_decode(nsa, cfg, d, kc, vc, out, idx, ws, calls, flush):
+    """Median per-call time of nsa_decode (ms) with one event pair around each call, and the
+    median of each stage from the instrumented twin; 1 GiB is READ between calls to evict the
+    256 MB Infinity Cache (a write sweep would leave dirty lines whose write-back competes with
+    the call)."""
     nst = len(nsa.DECODE_STAGES)
 
     def call(events=None):
@@ -322,11 +307,10 @@ def bench_decode(args, B=32, L=65536, Hkv=4, G=16, D=128, seed=3, calls=20):
 
     for _ in range(3):
         call()
+    import torch
     ev = HipEvents(calls * (nst + 1))
     torch.cuda.synchronize()
     for c in range(calls):
-        # evict the 256 MB Infinity Cache between calls (outside the events) by READING 1 GiB:
-        # a write sweep would leave dirty lines whose write-back competes with the call
         flush.sum()
         call(ev.group(c * (nst + 1), nst + 1))
     torch.cuda.synchronize()
@@ -347,7 +331,66 @@ def bench_decode(args, B=32, L=65536, Hkv=4, G=16, D=128, seed=3, calls=20):
         ev2.record(2 * c + 1, stream)
     torch.cuda.synchronize()
     plain = [ev2.elapsed_ms(2 * c, 2 * c + 1) for c in range(calls)]
-    ms = float(np.median(plain))
+    med = {nm: float(np.median(v)) for nm, v in stage_ms.items()}
+    return float(np.median(plain)), float(np.median(per_call)), med
+
+
+def decode_result(workload, B, ms, ms_ev, med, idx, seqlens, L, D, calls):
+    cmp_bytes, tok_bytes = decode_kv_bytes(idx, seqlens, L, D)
+    kv = cmp_bytes + tok_bytes
+    return {
+        "workload": workload,
+        "blocks_per_row": round(float((idx >= 0).sum(-1).mean()), 3),
+        "us_per_step": round(ms * 1e3, 2),
+        "us_per_step_with_stage_events": round(ms_ev * 1e3, 2),
+        "tok_s": round(B / (ms * 1e-3), 1),
+        "kv_bytes": kv,
+        "kv_gbs": round(kv / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(kv / (ms * 1e-3) / HBM_PEAK, 4),
+        "stages_us": {nm: round(v * 1e3, 2) for nm, v in med.items()},
+        # the whole call is the unit of the decode roofline: every kernel streams HBM, and the
+        # bytes are the unique K/V the step must read (compressed cache + selected and window
+        # tokens), over the call's event-timed duration
+        "roofline": {"bound": "hbm", "kernel": "nsa_decode (whole call)",
+                     "achieved": round(kv / (ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": round(kv / (ms * 1e-3) / HBM_PEAK, 4),
+                     "traffic": None},
+        "compressed_stream": {"bytes": cmp_bytes,
+                              "gbs": round(cmp_bytes / (med["cmp_stream"] * 1e-3) / 1e9, 1),
+                              "traffic": measured_traffic("dec_cmp_kernel")},
+        "timing": "median of %d calls, HIP events around each call, 1 GiB read between "
+                  "calls to evict the Infinity Cache" % calls,
+    }
+
+
+def bench_decode(args, B=32, L=65536, Hkv=4, G=16, D=128, seed=3, calls=20):
+    import torch
+
+    import dynamic_block_sparse_fwd_amd as nsa
+    import synth_inputs as S
+
+    cfg = nsa.NsaConfig(B, L, Hkv, G, D, top_p=args.top_p)
+    t0 = time.time()
+    x = S.nsa_decode_inputs(seed, B, L, Hkv, G, D)
+    print("[bench] decode inputs generated in %.1fs" % (time.time() - t0), file=sys.stderr,
+          flush=True)
+    dev = torch.device("cuda:0")
+    d = {k: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).to(dev)
+         for k, v in x.items()}
+    kc = nsa.nsa_compress(cfg, d["kcache"], d["wk"])
+    vc = nsa.nsa_compress_tiles(cfg, d["vcache"], d["wv"])
+    out = torch.empty((B, Hkv * G, D), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, Hkv, cfg.top_n), dtype=torch.int32, device=dev)
+    ws = torch.empty(nsa.decode_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    flush = torch.zeros(1 << 28, dtype=torch.int32, device=dev)  # 1 GiB
+    ms, ms_ev, med = time_decode(nsa, cfg, d, kc, vc, out, idx, ws, calls, flush)
+
+    def call():
+        nsa.nsa_decode(cfg, d["q"], d["kcache"], d["vcache"], kc, vc, d["seqlens"], d["gate"],
+                       out=out, sel_idx=idx, ws=ws)
+
+    stream = torch.cuda.current_stream().cuda_stream
     # a generation step: nsa_cache_append of the newest token (here the last cached one,
     # rewritten with its own values at position L-1, which also completes compressed token
     # n_cmp(L) - 1: the 1-in-16 steps that emit one), then the decode
@@ -385,34 +428,128 @@ def bench_decode(args, B=32, L=65536, Hkv=4, G=16, D=128, seed=3, calls=20):
         ev4.record(2 * c + 1, stream)
     torch.cuda.synchronize()
     app0_ms = float(np.median([ev4.elapsed_ms(2 * c, 2 * c + 1) for c in range(calls)]))
-    cmp_bytes, tok_bytes = decode_kv_bytes(idx.cpu().numpy(), x["seqlens"], L, D)
-    kv = cmp_bytes + tok_bytes
-    med = {nm: float(np.median(v)) for nm, v in stage_ms.items()}
-    res = {
-        "workload": "nsa_decode B=%d L=%d Hkv=%d G=%d D=%d top16 window512%s" % (
-            B, L, Hkv, G, D, " top_p=%g" % args.top_p if args.top_p > 0 else ""),
-        "blocks_per_row": round(float((idx >= 0).sum(-1).float().mean()), 3),
-        "us_per_step": round(ms * 1e3, 2),
-        "us_per_step_with_stage_events": round(float(np.median(per_call)) * 1e3, 2),
-        "tok_s": round(B / (ms * 1e-3), 1),
-        "kv_bytes": kv,
-        "kv_gbs": round(kv / (ms * 1e-3) / 1e9, 1),
-        "hbm_frac": round(kv / (ms * 1e-3) / HBM_PEAK, 4),
-        "stages_us": {nm: round(v * 1e3, 2) for nm, v in med.items()},
-        "append_us": round(app_ms * 1e3, 2),
-        "append_us_no_emission": round(app0_ms * 1e3, 2),
-        "generation_step_us": round(gen_ms * 1e3, 2),
-        "roofline": {"bound": "hbm", "kernel": "dec_cmp (compressed-cache stream)",
-                     "achieved": round(cmp_bytes / (med["cmp_stream"] * 1e-3) / 1e9, 1),
-                     "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": round(cmp_bytes / (med["cmp_stream"] * 1e-3) / HBM_PEAK, 4),
-                     "traffic": measured_traffic("dec_cmp_kernel")},
-        "timing": "median of %d calls, HIP events around each call, 1 GiB read between "
-                  "calls to evict the Infinity Cache" % calls,
-    }
+    res = decode_result("nsa_decode B=%d L=%d Hkv=%d G=%d D=%d top16 window512%s" % (
+        B, L, Hkv, G, D, " top_p=%g" % args.top_p if args.top_p > 0 else ""),
+        B, ms, ms_ev, med, idx.cpu().numpy(), x["seqlens"], L, D, calls)
+    res["append_us"] = round(app_ms * 1e3, 2)
+    res["append_us_no_emission"] = round(app0_ms * 1e3, 2)
+    res["generation_step_us"] = round(gen_ms * 1e3, 2)
     del d, kc, vc, out, idx, ws, flush, aws
     torch.cuda.empty_cache()
     return res, x
+
+
+def planted_decode_inputs_device(seed, B, L, Hkv, G, D, n_plant=16, shift=2.0, beta=64):
+    """The long-context planted decode inputs drawn on the device (a host draw of 2 x 1G bf16
+    values takes about a minute): q, K/V caches ~ N(0,1) bf16 from a seeded torch generator;
+    per KV head, n_plant distinct blocks from [1, nblk - 3] (a seeded CPU permutation) whose 64
+    keys get + shift * unit(sum of the group's queries), re-rounded to bf16; gates sigmoid(N(0,1)).
+    Returns the device tensors and the planted block ids [B, Hkv, n_plant] (sorted)."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    Hq = Hkv * G
+    q = torch.randn((B, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+    kc = torch.empty((B, Hkv, L, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    for b in range(B):  # per sequence: bounds the fp32 temporary
+        kc[b] = torch.randn((Hkv, L, D), generator=g, device=dev).to(torch.bfloat16)
+        vc[b] = torch.randn((Hkv, L, D), generator=g, device=dev).to(torch.bfloat16)
+    gate = torch.sigmoid(torch.randn((B, Hq, 3), generator=g, device=dev))
+    nblk = L // beta
+    gc = torch.Generator()
+    gc.manual_seed(seed)
+    planted = np.empty((B, Hkv, n_plant), dtype=np.int64)
+    dirn = q.float().view(B, Hkv, G, D).sum(2)
+    dirn = dirn / dirn.norm(dim=-1, keepdim=True)
+    for b in range(B):
+        for h in range(Hkv):
+            blocks = torch.sort(1 + torch.randperm(nblk - 3, generator=gc)[:n_plant]).values
+            planted[b, h] = blocks.numpy()
+            rows = (blocks.view(-1, 1) * beta + torch.arange(beta).view(1, -1)).reshape(-1)
+            rows = rows.to(dev)
+            kc[b, h, rows] = (kc[b, h, rows].float() + shift * dirn[b, h]).to(torch.bfloat16)
+    seqlens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    return dict(q=q, kcache=kc, vcache=vc, gate=gate, seqlens=seqlens), planted
+
+
+def bench_decode_planted(args, B=1, L=1 << 20, Hkv=8, G=8, D=128, seed=5, calls=20):
+    """Long-context decode with planted structure: batch 1, 1M cached tokens, 8 KV heads x
+    group 8, mean-pooled compressor (a random one would hide the plant), top-16, window 512."""
+    import torch
+
+    import dynamic_block_sparse_fwd_amd as nsa
+    import synth_inputs as S
+
+    cfg = nsa.NsaConfig(B, L, Hkv, G, D, top_p=args.top_p)
+    t0 = time.time()
+    d, planted = planted_decode_inputs_device(seed, B, L, Hkv, G, D)
+    dev = d["q"].device
+    mp = torch.from_numpy(S.mean_pool_weights(32, D).view(np.int16)).to(dev)
+    kc = nsa.nsa_compress(cfg, d["kcache"], mp)
+    vc = nsa.nsa_compress_tiles(cfg, d["vcache"], mp)
+    torch.cuda.synchronize()
+    print("[bench] planted 1M decode inputs drawn on the device in %.1fs" % (time.time() - t0),
+          file=sys.stderr, flush=True)
+    out = torch.empty((B, Hkv * G, D), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, Hkv, cfg.top_n), dtype=torch.int32, device=dev)
+    ws = torch.empty(nsa.decode_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    flush = torch.zeros(1 << 28, dtype=torch.int32, device=dev)  # 1 GiB
+    ms, ms_ev, med = time_decode(nsa, cfg, d, kc, vc, out, idx, ws, calls, flush)
+    gidx = idx.cpu().numpy()
+    nblk = L // 64
+    hits = total = 0
+    for b in range(B):
+        for h in range(Hkv):
+            free = [int(j) for j in gidx[b, h] if j >= 0 and j not in (0, nblk - 2, nblk - 1)]
+            hits += len(set(free) & set(planted[b, h].tolist()))
+            total += len(free)
+    res = decode_result("nsa_decode planted B=%d L=%d Hkv=%d G=%d D=%d top16 window512, "
+                        "mean-pool compressor" % (B, L, Hkv, G, D),
+                        B, ms, ms_ev, med, gidx, [L] * B, L, D, calls)
+    res["planted_recall"] = round(hits / max(total, 1), 4)
+    res["inputs"] = ("q, K/V caches ~ N(0,1) bf16 drawn on the device (seeded torch generator); "
+                     "16 planted blocks per KV head shifted +2 sigma toward the group's query "
+                     "direction")
+    host = None
+    if not args.no_cpu_baseline:
+        host = {k: v.cpu() for k, v in d.items()}
+    del d, kc, vc, out, idx, ws, flush
+    torch.cuda.empty_cache()
+    return res, host
+
+
+def cpu_baseline_decode_planted(host, L=1 << 20, Hkv=8, G=8, D=128, reps=3):
+    """fp64 oracle decode of the planted 1M-token step on the same inputs (copied from the
+    device; the compressed caches built by the oracle's own compression, untimed)."""
+    import oracle as O
+    import synth_inputs as S
+
+    def bits(t):
+        import torch
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 \
+            else t.numpy()
+
+    q, kcache, vcache = bits(host["q"]), bits(host["kcache"]), bits(host["vcache"])
+    gate = host["gate"].numpy()
+    mp = S.mean_pool_weights(32, D)
+    t0 = time.perf_counter()
+    kc = O.compress(kcache, mp, 32, 16)
+    vc = O.compress(vcache, mp, 32, 16)
+    t_cmp = time.perf_counter() - t0
+    cfg = O.NsaCfg(1, L, Hkv, G, D)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        O.nsa_decode(cfg, q, kcache, vcache, kc, vc, [L], gate)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    return {"value": 1 / dt, "unit": "tok/s", "cores": O.threads(), "kind": "oracle",
+            "sample": "fp64 oracle decode of the whole step (batch 1, all 64 heads), median of "
+                      "%d runs; its compressed caches built by the oracle's compression first "
+                      "(%.1fs, untimed)" % (reps, t_cmp)}
 
 
 def backward_flops(B, T, Hkv, G, D, l=32, d=16):
@@ -672,6 +809,35 @@ def cpu_baseline_moba(x, T=131072, H=32, D=128, rows=24576):
 
 # ----------------------------------------------------------------------------- main
 
+def host_info():
+    """What the numbers were measured with: the host CPU model and thread count (the oracle
+    baseline runs there), the library's source digest and, when the tree is a git checkout, its
+    commit."""
+    import hashlib
+    import subprocess
+
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    try:
+        sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                             text=True, timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        sha = None
+    return {"cpu_model": model, "cpu_count": os.cpu_count(), "git_sha": sha,
+            "library_source_sha256": h.hexdigest()[:16]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -681,12 +847,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-decode-1m", action="store_true",
+                    help="skip the planted 1M-token decode workload")
     ap.add_argument("--no-moba", action="store_true")
     ap.add_argument("--moba-seq", type=int, default=131072,
                     help="MoBA sequence length for --only moba (beyond 128k: device-drawn inputs)")
     ap.add_argument("--chunk", type=int, default=8192,
                     help="chunk length for --only chunked (a multiple of 64)")
-    ap.add_argument("--only", choices=("prefill", "decode", "moba", "chunked", "backward"),
+    ap.add_argument("--only", choices=("prefill", "decode", "decode_1m", "moba", "chunked",
+                                       "backward"),
                     help="run one workload and print its result alone (for profiling runs)")
     ap.add_argument("--top-p", type=float, default=0.0,
                     help="adaptive top-p block selection for the NSA workloads (0: fixed top-16)")
@@ -705,6 +874,12 @@ def main():
     if args.only == "decode":
         dec, _ = bench_decode(args)
         print(json.dumps({"decode": dec}), flush=True)
+        return
+    if args.only == "decode_1m":
+        dec, host = bench_decode_planted(args)
+        if host is not None:
+            dec["cpu_baseline"] = cpu_baseline_decode_planted(host)
+        print(json.dumps({"decode_1m": dec}), flush=True)
         return
     if args.only == "backward":
         print(json.dumps({"backward": bench_backward(args)}), flush=True)
@@ -745,6 +920,7 @@ def main():
     }
     if args.top_p > 0:
         line["config"]["top_p"] = args.top_p
+    line["host"] = host_info()
     if args.only == "prefill":
         print(json.dumps(line), flush=True)
         return
@@ -757,6 +933,12 @@ def main():
             dec["cpu_baseline"] = cpu_baseline_decode(xd)
         del xd
         line["decode"] = dec
+    if not args.no_decode_1m:
+        dec, host = bench_decode_planted(args)
+        if host is not None:
+            dec["cpu_baseline"] = cpu_baseline_decode_planted(host)
+        del host
+        line["decode_1m"] = dec
     if not args.no_moba:
         mo, xm = bench_moba(args)
         if not args.no_cpu_baseline:

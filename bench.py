@@ -274,23 +274,32 @@ def cpu_baseline_prefill(x, T, rows=1024):
 
 # ----------------------------------------------------------------------------- decode
 
-def decode_kv_bytes(idx, seqlens, L, D, l=32, d=16, beta=64, w=512):
+def decode_kv_bytes(idx, seqlens, L, D, l=32, d=16, beta=64, w=512, n_local=2, fixed=False):
     """Unique K+V bytes one decode step must read: every visible compressed token, and the
-    union of the selected blocks' and the window's tokens (causal), per (sequence, KV group)."""
+    union of the selected blocks' and the window's tokens (causal), per (sequence, KV group).
+    fixed=True also returns the bytes of the window's and the forced blocks' tokens (block 0 and
+    the n_local most recent), which do not depend on the selection."""
     B, Hkv, _ = idx.shape
     cmp_b = 0
     tok_b = 0
+    fix_b = 0
     for b in range(B):
         t = int(seqlens[b]) - 1
         nvis = (t - l + 1) // d + 1 if t >= l - 1 else 0
+        bcur = t // beta
         for h in range(Hkv):
             toks = set(range(max(0, t - w + 1), t + 1))
+            for j in {0} | set(range(max(0, bcur - n_local + 1), bcur + 1)):
+                toks.update(range(j * beta, min((j + 1) * beta, t + 1)))
+            fix_b += len(toks)
             for j in idx[b, h]:
                 if j >= 0:
                     toks.update(range(j * beta, min((j + 1) * beta, t + 1)))
             tok_b += len(toks)
             cmp_b += nvis
     per_tok = 2 * D * 2  # K and V, bf16
+    if fixed:
+        return cmp_b * per_tok, tok_b * per_tok, fix_b * per_tok
     return cmp_b * per_tok, tok_b * per_tok
 
 
@@ -338,6 +347,7 @@ def time_decode(nsa, cfg, d, kc, vc, out, idx, ws, calls, flush):
 def decode_result(workload, B, ms, ms_ev, med, idx, seqlens, L, D, calls):
     cmp_bytes, tok_bytes = decode_kv_bytes(idx, seqlens, L, D)
     kv = cmp_bytes + tok_bytes
+    first = next(iter(med))  # the compressed-cache stream
     return {
         "workload": workload,
         "blocks_per_row": round(float((idx >= 0).sum(-1).mean()), 3),
@@ -357,7 +367,7 @@ def decode_result(workload, B, ms, ms_ev, med, idx, seqlens, L, D, calls):
                      "frac": round(kv / (ms * 1e-3) / HBM_PEAK, 4),
                      "traffic": None},
         "compressed_stream": {"bytes": cmp_bytes,
-                              "gbs": round(cmp_bytes / (med["cmp_stream"] * 1e-3) / 1e9, 1),
+                              "gbs": round(cmp_bytes / (med[first] * 1e-3) / 1e9, 1),
                               "traffic": measured_traffic("dec_cmp_kernel")},
         "timing": "median of %d calls, HIP events around each call, 1 GiB read between "
                   "calls to evict the Infinity Cache" % calls,

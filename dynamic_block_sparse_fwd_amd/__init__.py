@@ -320,7 +320,7 @@ def nsa_prefill_stages(cfg: NsaConfig, stages: int, q, k, v, wk, wv, gate, out=N
     return out, sel_idx
 
 
-DECODE_STAGES = ("cmp_stream", "select_attend")
+DECODE_STAGES = ("cmp_stream", "select", "group")
 
 
 def nsa_decode(cfg: NsaConfig, q, kcache, vcache, kcmp, vcmp, seqlens, gate, out=None,

@@ -53,13 +53,10 @@ int check_nsa(const nsa_config* c) {
   return NSA_OK;
 }
 
-// Decode builds each group's list of selected/window tiles in a fixed 160-entry table.
-int decode_max_tiles(const nsa_config* c) {
-  return c->top_n * (c->sel_block / 64) + (c->window + 63) / 64 + 1;
-}
-
 struct DecodeShape {
   int ncmp, nblk, NCH, NT, NBT;
+  int SB, NSL, KF;
+  int ntile;  // most tiles a group's list can hold: window, forced and other selected blocks
 };
 
 DecodeShape decode_shape(const nsa_config* c) {
@@ -70,22 +67,26 @@ DecodeShape decode_shape(const nsa_config* c) {
   p.NCH = (p.ncmp + chunk - 1) / chunk;
   p.NT = (p.ncmp + 63) / 64;
   p.NBT = (63 * c->cmp_stride + c->cmp_len - 1) / c->sel_block + 2;
+  const int per = c->sel_block / 64;
+  p.SB = decode_slice_blocks(c->cmp_len, c->cmp_stride, c->sel_block);
+  p.NSL = (p.nblk + p.SB - 1) / p.SB;
+  p.KF = std::max(1, c->top_n - 1 - c->n_local);
+  // the list: every tile when all blocks fit, else the window's and the selected blocks' tiles
+  p.ntile = std::max(c->top_n * per, (c->window + 63) / 64 + 1 + c->top_n * per);
   return p;
 }
 
-// Decode stages per-chunk statistics and the group's block scores in LDS (160 KB) and
-// addresses a cache row with 32-bit offsets.
+// Decode addresses a cache row with 32-bit offsets, keeps a group's tile list in a 256-entry
+// LDS table, stages a group's selection candidates in LDS and launches grids of (slot, KV head,
+// sequence) or (KV head, sequence).
 int check_nsa_decode(const nsa_config* c) {
   int st = check_nsa_base(c);
   if (st != NSA_OK) return st;
   if (c->T > (1 << 24)) return NSA_ERR_UNSUPPORTED;
-  if (decode_max_tiles(c) > decode_max_tile_list()) return NSA_ERR_UNSUPPORTED;
+  if (c->B > 65535 || c->Hkv > 65535) return NSA_ERR_UNSUPPORTED;
   const DecodeShape p = decode_shape(c);
-  // 160 KB of LDS per workgroup, 4 KB of it static
-  // dynamic LDS of the per-group workgroup; with its static LDS (under 8 KB) it must fit the
-  // 160 KB of a workgroup
-  if (decode_group_lds_bytes(c->D, p.NCH, p.NT, p.nblk) > kMaxDecodeDynLds)
-    return NSA_ERR_UNSUPPORTED;
+  if (p.ntile > kDecodeMaxList) return NSA_ERR_UNSUPPORTED;
+  if ((long)p.NSL * p.KF > decode_max_candidates(c->D)) return NSA_ERR_UNSUPPORTED;
   return NSA_OK;
 }
 
@@ -193,7 +194,7 @@ BackwardPlan plan_backward(const nsa_config* c) {
 }
 
 struct DecodePlan {
-  size_t cm, cl, co, tref, cb, idx, total;
+  size_t cm, cl, co, tref, cb, sS, cand, ocmp, idx, total;
   DecodeShape sh;
 };
 
@@ -210,6 +211,9 @@ DecodePlan plan_decode(const nsa_config* c) {
   p.co = off;   off += align_up(BKV * nch * 16 * c->D * F);
   p.tref = off; off += align_up(BKV * nt * 16 * F);
   p.cb = off;   off += align_up(BKV * nt * d.NBT * 16 * F);
+  p.sS = off;   off += align_up(BKV * d.NSL * d.SB * F);
+  p.cand = off; off += align_up(BKV * d.NSL * d.KF * sizeof(uint64_t));
+  p.ocmp = off; off += align_up(BKV * 16 * c->D * F);
   p.idx = off;  off += align_up(BKV * c->top_n * 4);
   p.total = off;
   return p;
@@ -642,10 +646,14 @@ static int decode_impl(const nsa_config* c, const void* q, const void* kcache,
   a.co = reinterpret_cast<float*>(base + p.co);
   a.tref = reinterpret_cast<float*>(base + p.tref);
   a.cb = reinterpret_cast<float*>(base + p.cb);
+  a.sS = reinterpret_cast<float*>(base + p.sS);
+  a.cand = reinterpret_cast<uint64_t*>(base + p.cand);
+  a.ocmp = reinterpret_cast<float*>(base + p.ocmp);
   a.B = c->B; a.L = c->T; a.Hkv = c->Hkv; a.G = c->G; a.D = c->D;
   a.l = c->cmp_len; a.d = c->cmp_stride; a.beta = c->sel_block; a.top_n = c->top_n;
   a.n_local = c->n_local; a.window = c->window; a.top_p = c->top_p;
   a.ncmp = p.sh.ncmp; a.nblk = p.sh.nblk; a.NCH = p.sh.NCH; a.NT = p.sh.NT; a.NBT = p.sh.NBT;
+  a.SB = p.sh.SB; a.NSL = p.sh.NSL; a.KF = p.sh.KF;
   a.scale_log2 = c->scale * 1.4426950408889634f;
   (void)hipGetLastError();
   launch_decode(a, stream, ev);

@@ -2,16 +2,22 @@
 // article: decode loads only the compressed, the selected and the window KV, saving HBM
 // bandwidth; podcast notes EP94 section 6: one shared selection per GQA group, so one KV read
 // serves the group's heads).  Every phase streams HBM; the matrix core does the contractions
-// with the group's heads as the 16 MFMA rows.
+// with the group's heads as the 16 MFMA rows.  Three launches:
 //
 //   dec_cmp_kernel     split-K over the compressed cache: each wave streams TPW 64-token tiles
 //                      with register prefetch and an online softmax; per 1024-token chunk, per
 //                      head, (max, sum, unnormalised output); per tile, the probability mass of
 //                      every selection block it touches, relative to a per-tile reference
-//   dec_group_kernel   one workgroup per (sequence, group): per-head log-sum-exp, every group
-//                      block score, the top-n (forced block 0 + local blocks), the list of
-//                      selected and window tiles (each tile read once, feeding whichever branch
-//                      uses it), the merge of all partials and the gate
+//   dec_select_kernel  per 256-block slice of a group (so a long sequence spreads its selection
+//                      over many workgroups): the per-head log-sum-exp, the group block scores,
+//                      the slice's best free blocks, and the normalised compressed output of a
+//                      share of the heads
+//   dec_group_kernel   per group: the slices' candidates merged into the top-n (forced blocks
+//                      added, ascending, written out); the window's, forced and other selected
+//                      tiles, each read once and feeding both branches that use it; the merge
+//                      and the gate
+// Tile work is assigned in a fixed order and every sum runs in a fixed order, so the output is
+// the same bit for bit on every call.
 #include "attn_tile.h"
 #include "dev_common.h"
 #include "kernels.h"
@@ -20,7 +26,6 @@ namespace nsa {
 
 constexpr int TPW = 4;               // 64-token tiles per wave in dec_cmp
 constexpr int CHUNK = 4 * TPW * 64;  // compressed tokens per dec_cmp workgroup
-constexpr int kMaxTiles = 160;       // selected + window tiles per group
 
 // One 64-key tile of a [rows, D] K/V cache pair in registers: K in MFMA A-operand order, V in
 // the gather order of the transposing LDS store.  Rows past `last` are clamped to it.
@@ -217,23 +222,297 @@ __device__ __forceinline__ int block_tok_hi(int j, int beta, int d) {
   return ((j + 1) * beta - 1) / d;
 }
 
+// ------------------------------------------------------------------ block masses
+
+// Masses of block j for heads 4*hq .. 4*hq + 3.  Every index is clamped so the loads are
+// unconditional (no branch around them).
+//  generic: the (at most) first two tiles the block touches, from tile ta; `ntile` is the
+//    number of tiles it really touches (0 when none of its compressed tokens is visible);
+//  FAST (sel_block = 4 * stride, cmp_len = 2 * stride): block j spans compressed tokens
+//    4j - 1 .. 4j + 3, all in tile T = j / 16 except for j = 16 T, whose half-weight first token
+//    is the previous tile's carry slot 16.  m0 = tile T's slot j - 16 T, m1 = tile T - 1's carry:
+//    the 16 blocks of one wave instruction share that address, so it costs one 64-byte request.
+struct BlockMass {
+  f32x4 m0, m1;
+  int ta, tb, ntile;  // generic: first tile, -, tiles touched; FAST: tile of m0, tile of m1,
+                      // (m0 used) | 2 (m1 used)
+};
+
+template <bool FAST>
+__device__ __forceinline__ BlockMass fetch_block(const DecodeArgs& a, long bkv, int j, int nvis,
+                                                 int hq) {
+  BlockMass r;
+  if constexpr (FAST) {
+    const int T = j >> 4;
+    const int tmax = a.NT > 0 ? a.NT - 1 : 0;
+    const int Tm = T < tmax ? T : tmax, Tc = T > 0 ? (T - 1 < tmax ? T - 1 : tmax) : 0;
+    const bool first = (j & 15) == 0;
+    const bool main_ok = (first ? 4 * j : 4 * j - 1) <= nvis - 1;
+    const bool carry_ok = first && j > 0 && 4 * j - 1 <= nvis - 1;
+    r.m0 = *reinterpret_cast<const f32x4*>(a.cb + ((bkv * a.NT + Tm) * a.NBT + (j - 16 * T)) * 16 +
+                                           4 * hq);
+    r.m1 = *reinterpret_cast<const f32x4*>(a.cb + ((bkv * a.NT + Tc) * a.NBT + 16) * 16 + 4 * hq);
+    r.ta = Tm;
+    r.tb = Tc;
+    r.ntile = (main_ok ? 1 : 0) | (carry_ok ? 2 : 0);
+  } else {
+    const int lo = block_tok_lo(j, a.beta, a.l, a.d);
+    int hi = block_tok_hi(j, a.beta, a.d);
+    hi = hi < nvis - 1 ? hi : nvis - 1;
+    const int ta = (lo < nvis - 1 ? lo : nvis - 1) / 64;
+    const int tb = hi / 64 > ta ? ta + 1 : ta;
+    auto entry = [&](int T) {
+      int jj = j - (T * 64 * a.d) / a.beta;
+      jj = jj < 0 ? 0 : (jj < a.NBT ? jj : a.NBT - 1);
+      return ((bkv * a.NT + T) * a.NBT + jj) * 16 + 4 * hq;
+    };
+    r.m0 = *reinterpret_cast<const f32x4*>(a.cb + entry(ta));
+    r.m1 = *reinterpret_cast<const f32x4*>(a.cb + entry(tb));
+    r.ta = ta;
+    r.tb = tb;
+    r.ntile = lo <= hi ? hi / 64 - lo / 64 + 1 : 0;
+  }
+  return r;
+}
+
+// Group score share of one tile: masses times w = exp2(tref - lse), the per-head normalisation
+// of the compressed softmax (w per tile and head, computed once).
+__device__ __forceinline__ float mass_score(const f32x4& m, const float* w) {
+  return (m[0] * w[0] + m[1] * w[1]) + (m[2] * w[2] + m[3] * w[3]);
+}
+
+
+constexpr int kSelThreads = 256;             // one selection slice
+constexpr int kSelWaves = kSelThreads / 64;  // tile slots of a tile worker
+constexpr int kSliceTiles = 64;              // tile weights a selection slice holds
+constexpr uint32_t kCodeSlc = 1u << 30, kCodeWin = 1u << 29, kCodeTile = (1u << 29) - 1;
+
+int decode_slice_blocks(int l, int d, int beta) {
+  // the blocks j0 .. j0 + sb - 1 touch compressed tokens (j0 beta - l + 1) / d .. ((j0 + sb)
+  // beta - 1) / d: at most (sb beta + l) / d + 1 tokens, i.e. that / 64 + 2 tiles
+  int sb = 256;
+  while (sb > 1 && ((long)sb * beta + l) / d + 1 > (long)(kSliceTiles - 2) * 64) sb /= 2;
+  return sb;
+}
+
+// Per-sequence selection geometry of one decode query.
+struct DecRow {
+  int t, nb, nvis, nch, bcur, flo, kfree, wt0, wt1, w0;
+  bool top_p, all;
+};
+
+__device__ __forceinline__ DecRow dec_row(const DecodeArgs& a, int b) {
+  DecRow r;
+  r.t = a.seqlens[b] - 1;
+  r.nb = r.t / a.beta + 1;
+  r.nvis = n_visible(r.t, a.l, a.d, a.ncmp);
+  r.nch = (r.nvis + CHUNK - 1) / CHUNK;
+  r.top_p = a.top_p > 0.f;
+  r.all = r.nb <= a.top_n && !r.top_p;  // every block is selected
+  r.bcur = r.nb - 1;
+  r.flo = r.bcur - a.n_local + 1 > 1 ? r.bcur - a.n_local + 1 : 1;  // forced: 0, flo .. bcur
+  r.kfree = a.top_n - 1 - a.n_local;
+  r.w0 = r.t - a.window + 1;
+  r.wt0 = (r.w0 > 0 ? r.w0 : 0) / 64;
+  r.wt1 = r.t / 64;
+  return r;
+}
+
+// The group's queries (rows of the MFMA B operand) into LDS, one 16-byte octet per thread;
+// rows past G are zero.
+template <int D>
+__device__ __forceinline__ void stage_queries(const DecodeArgs& a, int b, int kvh,
+                                              u16 (*Qs)[D + 8]) {
+  for (int e = threadIdx.x; e < 16 * (D / 8); e += kSelThreads) {
+    const int qh = e / (D / 8), qc = (e % (D / 8)) * 8;
+    *reinterpret_cast<bf16x8*>(&Qs[qh][qc]) =
+        qh < a.G ? load8(a.q + ((long)b * a.Hkv * a.G + kvh * a.G + qh) * D + qc) : zero8();
+  }
+}
+
+// Running softmax state of one wave over its tiles, for NBR branches.
+template <int D, int NBR>
+struct WaveSoftmax {
+  float m[NBR], l[NBR];
+  f32x4 O[NBR][D / 16];
+};
+
+// One wave's pass over the tile list entries first, first + stride, ... (< n): each tile's K
+// and V read once, feeding every branch whose mask its code allows (branch 0: selected keys
+// <= t; branch 1: window keys w0 .. t); the next tile's K in flight during this tile's softmax
+// and P V, its V after them.  Codes: tile index | kCodeSlc | kCodeWin.
+template <int D, int NBR>
+__device__ void wave_tiles(const DecodeArgs& a, long bkv, const DecRow& r, const int* list,
+                           int n, int first, int stride, const u16 (*Qs)[D + 8],
+                           u16 (*Vt)[64], WaveSoftmax<D, NBR>& st) {
+  constexpr int DT = D / 16;
+  const int lane = threadIdx.x & 63, g4 = lane >> 4, r16 = lane & 15;
+  const float sl = a.scale_log2;
+  const u16* kcb = a.kcache + bkv * (long)a.L * D;
+  const u16* vcb = a.vcache + bkv * (long)a.L * D;
+#pragma unroll
+  for (int br = 0; br < NBR; ++br) {
+    st.m[br] = kNegInf;
+    st.l[br] = 0.f;
+#pragma unroll
+    for (int n2 = 0; n2 < DT; ++n2) st.O[br][n2] = zero4();
+  }
+  if (first >= n) return;  // uniform per wave
+  int e = first;
+  DecTile<D> kv;
+  kv.load(kcb, vcb, (int)(list[e] & kCodeTile) * 64, r.t, lane);
+  for (;;) {
+    const uint32_t code = (uint32_t)__builtin_amdgcn_readfirstlane(list[e]);
+    const int k0 = (int)(code & kCodeTile) * 64;
+    const bool in_slc = code & kCodeSlc, in_win = code & kCodeWin;
+    const int en = e + stride;
+    const bool more = en < n;
+    // after the last tile every row of the "next" load is row t (one line, in bounds)
+    const int k1 = more ? (int)((uint32_t)__builtin_amdgcn_readfirstlane(list[en]) & kCodeTile) * 64
+                        : r.t;
+    const int last1 = more ? r.t : k1;
+    f32x4 acc[4];
+    {
+      bf16x8 qf[D / 32];
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) qf[c] = load8(&Qs[r16][32 * c + 8 * g4]);
+      kv.scores(qf, acc);
+    }
+    __asm__ volatile("" ::: "memory");  // the previous tile's Vt reads stay before these writes
+    kv.stage(Vt, lane);
+    __asm__ volatile("" ::: "memory");  // Vt is this wave's own: LDS keeps its order
+    kv.load_k(kcb, k1, last1, lane);
+#pragma unroll
+    for (int br = 0; br < NBR; ++br) {
+      float p[16];
+      float tm = kNegInf;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + lane_key(q4, i, g4);
+          const bool ok = br == 0 ? (in_slc && key <= r.t)
+                                  : (in_win && key <= r.t && key >= r.w0);
+          const float x = ok ? acc[q4][i] : kNegInf;
+          p[q4 * 4 + i] = x;
+          tm = fmaxf(tm, x);
+        }
+      tm = col_max4(tm);
+      const float mn = fmaxf(st.m[br], tm);
+      const float ms = mn == kNegInf ? 0.f : mn * sl;
+      const float alpha = fast_exp2(fmaf(st.m[br], sl, -ms));
+      st.m[br] = mn;
+      float ls = 0.f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        p[q] = fast_exp2(fmaf(p[q], sl, -ms));
+        ls += p[q];
+      }
+      st.l[br] = fmaf(st.l[br], alpha, col_sum4(ls));
+#pragma unroll
+      for (int n2 = 0; n2 < DT; ++n2) st.O[br][n2] *= alpha;
+      tile_pv<D>(Vt, p, g4, r16, st.O[br]);
+    }
+    kv.load_v(vcb, k1, last1, lane);
+    if (!more) break;
+    e = en;
+  }
+}
+
+// The four waves' states of branch br merged into one record (16 maxima in scaled log2 units,
+// 16 sums, 16 x D outputs relative to the maxima), summed in wave order.  Reuses `region`
+// (the waves' Vt tiles: every wave must be past its tile loop, which the first barrier
+// ensures).
+template <int D, int NBR>
+__device__ void write_record(const WaveSoftmax<D, NBR>& st, int br, float sl, float* region,
+                             float* rec) {
+  constexpr int DT = D / 16, OP = D + 4;
+  __shared__ float Wm[kSelWaves][16], Wl[kSelWaves][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  __syncthreads();  // region free (tile loops or an earlier branch's reads done)
+  if (g4 == 0) {
+    Wm[wave][r16] = st.m[br];
+    Wl[wave][r16] = st.l[br];
+  }
+  __syncthreads();
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) M = fmaxf(M, Wm[w][r16]);
+  const float f = st.m[br] == kNegInf ? 0.f : fast_exp2((st.m[br] - M) * sl);
+#pragma unroll
+  for (int n2 = 0; n2 < DT; ++n2)
+    *reinterpret_cast<f32x4*>(&region[(wave * 16 + r16) * OP + 16 * n2 + 4 * g4]) =
+        f * st.O[br][n2];
+  __syncthreads();
+  for (int e = tid; e < 16 * D; e += kSelThreads) {
+    const int o = (e / D) * OP + e % D;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) v += region[w * 16 * OP + o];
+    rec[32 + e] = v;
+  }
+  if (tid < 16) {
+    float Mh = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) Mh = fmaxf(Mh, Wm[w][tid]);
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w)
+      if (Wm[w][tid] != kNegInf) L += Wl[w][tid] * fast_exp2((Wm[w][tid] - Mh) * sl);
+    rec[tid] = Mh == kNegInf ? kNegInf : Mh * sl;
+    rec[16 + tid] = L;
+  }
+}
+
+// Fixed tiles of one group: the window's tiles and the forced blocks' tiles (or, when every
+// block fits in top_n, all tiles), known before the selection; flagged with the branches they
+// feed.  Written to list by the first wave; returns the count (lane-uniform).
+__device__ int fixed_tile_list(const DecodeArgs& a, const DecRow& r, int* list, int lane) {
+  const int per = a.beta / 64;
+  const int tl = r.t / 64;  // last tile at or before t
+  if (r.all) {
+    for (int i = lane; i <= tl; i += 64)
+      list[i] = (int)(i | kCodeSlc | (i >= r.wt0 ? kCodeWin : 0u));
+    return tl + 1;
+  }
+  const int nw = r.wt1 - r.wt0 + 1;
+  for (int i = lane; i < nw; i += 64) {
+    const int tile = r.wt0 + i, jb = tile / per;
+    const bool forced = jb == 0 || (jb >= r.flo && jb <= r.bcur);
+    list[i] = (int)(tile | kCodeWin | (forced ? kCodeSlc : 0u));
+  }
+  // forced blocks' tiles outside the window: block 0, then flo .. bcur
+  const int nf = (1 + (r.bcur - r.flo + 1)) * per;
+  int base = nw;
+  for (int i0 = 0; i0 < nf; i0 += 64) {
+    const int i = i0 + lane;
+    int code = -1;
+    if (i < nf) {
+      const int jb = i < per ? 0 : r.flo + (i - per) / per;
+      const int tile = jb * per + i % per;
+      if (tile <= tl && (tile < r.wt0 || tile > r.wt1)) code = (int)(tile | kCodeSlc);
+    }
+    const uint64_t m = __ballot(code >= 0);
+    const int pos = base + (int)__popcll(m & ((1ull << lane) - 1ull));
+    if (code >= 0) list[pos] = code;
+    base += (int)__popcll(m);
+  }
+  return base;
+}
+
 // ------------------------------------------------------------------ phase 1: compressed stream
 
 // FAST: sel_block = 4 * stride and cmp_len = 2 * stride, where block j receives
 // p(4j-1)/2 + p(4j) + p(4j+1) + p(4j+2) + p(4j+3)/2: the lane holding keys 4jl..4jl+3 of a
 // tile forms the block's core, and the half-token carries cross lanes by shuffles.
+// The compressed chunk of dec_cmp_kernel (see there).
 template <int D, bool FAST>
-__global__ __launch_bounds__(256, FAST ? 2 : 1) void dec_cmp_kernel(DecodeArgs a) {
+__device__ __forceinline__ void cmp_chunk(const DecodeArgs& a, int b, int kvh, long bkv, int chunk,
+                                          int nvis, float* Ob, float (*Wm)[16], float (*Wl)[16],
+                                          float (*Pw)[FAST ? 1 : 16][64]) {
   constexpr int DT = D / 16, OP = D + 4;
-  __shared__ __align__(16) float Ob[4 * 16 * OP];
-  __shared__ float Wm[4][16], Wl[4][16];
-  __shared__ float Pw[FAST ? 1 : 4][FAST ? 1 : 16][64];
-  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int t = a.seqlens[b] - 1;
-  const int nvis = n_visible(t, a.l, a.d, a.ncmp);
   const int c0 = chunk * CHUNK;
-  const long bkv = (long)b * a.Hkv + kvh;
-  if (c0 >= nvis) return;  // uniform across the workgroup
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
   const u16* kcb = a.kc + bkv * a.ncmp * D;
@@ -372,288 +651,291 @@ __global__ __launch_bounds__(256, FAST ? 2 : 1) void dec_cmp_kernel(DecodeArgs a
   }
 }
 
-// ------------------------------------------------------------------ phase 2: one workgroup per group
 
-// Masses of block j for heads 4*hq .. 4*hq + 3.  Every index is clamped so the loads are
-// unconditional (no branch around them).
-//  generic: the (at most) first two tiles the block touches, from tile ta; `ntile` is the
-//    number of tiles it really touches (0 when none of its compressed tokens is visible);
-//  FAST (sel_block = 4 * stride, cmp_len = 2 * stride): block j spans compressed tokens
-//    4j - 1 .. 4j + 3, all in tile T = j / 16 except for j = 16 T, whose half-weight first token
-//    is the previous tile's carry slot 16.  m0 = tile T's slot j - 16 T, m1 = tile T - 1's carry:
-//    the 16 blocks of one wave instruction share that address, so it costs one 64-byte request.
-struct BlockMass {
-  f32x4 m0, m1;
-  int ta, tb, ntile;  // generic: first tile, -, tiles touched; FAST: tile of m0, tile of m1,
-                      // (m0 used) | 2 (m1 used)
-};
+// Workgroup `chunk` of a group streams the compressed tokens chunk * CHUNK .. + CHUNK - 1 that
+// are visible.
+template <int D, bool FAST>
+__global__ __launch_bounds__(256, FAST ? 2 : 1) void dec_cmp_kernel(DecodeArgs a) {
+  __shared__ __align__(16) float Ob[4 * 16 * (D + 4)];  // the waves' compressed partials
+  __shared__ float Wm[4][16], Wl[4][16];
+  __shared__ float Pw[FAST ? 1 : 4][FAST ? 1 : 16][64];
+  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int nvis = n_visible(a.seqlens[b] - 1, a.l, a.d, a.ncmp);
+  const long bkv = (long)b * a.Hkv + kvh;
+  if (chunk * CHUNK < nvis) cmp_chunk<D, FAST>(a, b, kvh, bkv, chunk, nvis, Ob, Wm, Wl, Pw);
+}
 
-template <bool FAST>
-__device__ __forceinline__ BlockMass fetch_block(const DecodeArgs& a, long bkv, int j, int nvis,
-                                                 int hq) {
-  BlockMass r;
+// ------------------------------------------------------------------ phase 2: selection slices
+
+constexpr int kLseRegs = 4;  // chunk statistics per thread held in registers (<= 64 chunks)
+
+// One selection slice: the group block scores of blocks j0 .. j1-1 (the tile masses of the
+// compressed stream rescaled by exp2(tref - lse), summed over the group's heads; four lanes per
+// block, four heads each), written out, and the slice's best free blocks by (score desc, index
+// asc).  Every load the slice needs (chunk statistics, tile references, block masses) is issued
+// up front, before the per-head log-sum-exp they wait on is reduced.  Slice 0 also posts the
+// log-sum-exp for the merge, and each running slice normalises the compressed output of its
+// share of the heads (heads s, s + nrun, ...: the chunk partials of one head weighted by
+// exp2(chunk max - lse)).  Runs before the selection of the group is known, so every slice
+// of every group is independent.
+template <int D, bool FAST>
+__device__ void select_slice(const DecodeArgs& a, long bkv, int b, int s, unsigned char* smem) {
+  const DecRow r = dec_row(a, b);
+  const int j0 = s * a.SB;
+  const bool ranks = !r.all && j0 < r.nb;  // uniform
+  if (!ranks && s != 0) return;
+  const int j1 = j0 + a.SB < r.nb ? j0 + a.SB : r.nb;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  float* lse_s = reinterpret_cast<float*>(smem);  // [16]
+  float* trs = lse_s + 16;                        // [kSliceTiles][16]
+  float* Ss = trs + kSliceTiles * 16;             // [SB]
+  f32x4* red = reinterpret_cast<f32x4*>(Ss + 256);  // [parts][span] compressed-output partials
+  const bool scored = r.nvis > 0;
+  const int ntv = (r.nvis + 63) / 64;
+  // tiles the slice's blocks read: from the one holding block j0's first compressed token (or
+  // the carry of the tile before) to the one holding block j1-1's last visible token
+  int tlo, thi;
   if constexpr (FAST) {
-    const int T = j >> 4;
-    const int tmax = a.NT > 0 ? a.NT - 1 : 0;
-    const int Tm = T < tmax ? T : tmax, Tc = T > 0 ? (T - 1 < tmax ? T - 1 : tmax) : 0;
-    const bool first = (j & 15) == 0;
-    const bool main_ok = (first ? 4 * j : 4 * j - 1) <= nvis - 1;
-    const bool carry_ok = first && j > 0 && 4 * j - 1 <= nvis - 1;
-    r.m0 = *reinterpret_cast<const f32x4*>(a.cb + ((bkv * a.NT + Tm) * a.NBT + (j - 16 * T)) * 16 +
-                                           4 * hq);
-    r.m1 = *reinterpret_cast<const f32x4*>(a.cb + ((bkv * a.NT + Tc) * a.NBT + 16) * 16 + 4 * hq);
-    r.ta = Tm;
-    r.tb = Tc;
-    r.ntile = (main_ok ? 1 : 0) | (carry_ok ? 2 : 0);
+    tlo = (j0 >> 4) > 0 ? (j0 >> 4) - 1 : 0;
+    thi = (j1 - 1) >> 4;
   } else {
-    const int lo = block_tok_lo(j, a.beta, a.l, a.d);
-    int hi = block_tok_hi(j, a.beta, a.d);
-    hi = hi < nvis - 1 ? hi : nvis - 1;
-    const int ta = (lo < nvis - 1 ? lo : nvis - 1) / 64;
-    const int tb = hi / 64 > ta ? ta + 1 : ta;
-    auto entry = [&](int T) {
-      int jj = j - (T * 64 * a.d) / a.beta;
-      jj = jj < 0 ? 0 : (jj < a.NBT ? jj : a.NBT - 1);
-      return ((bkv * a.NT + T) * a.NBT + jj) * 16 + 4 * hq;
-    };
-    r.m0 = *reinterpret_cast<const f32x4*>(a.cb + entry(ta));
-    r.m1 = *reinterpret_cast<const f32x4*>(a.cb + entry(tb));
-    r.ta = ta;
-    r.tb = tb;
-    r.ntile = lo <= hi ? hi / 64 - lo / 64 + 1 : 0;
+    tlo = block_tok_lo(j0, a.beta, a.l, a.d) / 64;
+    thi = block_tok_hi(j1 - 1, a.beta, a.d) / 64;
   }
-  return r;
+  thi = thi < ntv - 1 ? thi : ntv - 1;
+  const int ntr = ranks && scored && thi >= tlo ? (thi - tlo + 1) * 16 : 0;
+  // 1. loads: chunk statistics of head h = tid / 16 (chunks sub, sub + 16, ...), the slice's
+  // tile references, its blocks' masses (every index clamped: no load under a branch)
+  const int h = tid >> 4, sub = tid & 15;
+  const long cbase = bkv * a.NCH * 16 + h;
+  const int clast = r.nch > 0 ? r.nch - 1 : 0;
+  float vm[kLseRegs], vl[kLseRegs];
+#pragma unroll
+  for (int i = 0; i < kLseRegs; ++i) {
+    const int c = sub + 16 * i, cc = c < clast ? c : clast;
+    vm[i] = a.cm[cbase + cc * 16];
+    vl[i] = a.cl[cbase + cc * 16];
+  }
+  f32x4 trv[kSliceTiles * 16 / kSelThreads / 4];
+#pragma unroll
+  for (int i = 0; i < kSliceTiles * 16 / kSelThreads / 4; ++i) {
+    const int e = 4 * (tid + kSelThreads * i);
+    const int ee = e < ntr ? e : 0;
+    trv[i] = *reinterpret_cast<const f32x4*>(a.tref + (bkv * a.NT + tlo) * 16 + ee);
+  }
+  const int hq = tid & 3;
+  constexpr int kPass = 256 / (kSelThreads / 4);  // block passes of a 256-block slice
+  BlockMass bm[kPass];
+  if (ranks && scored) {
+#pragma unroll
+    for (int u = 0; u < kPass; ++u) {
+      const int j = j0 + (tid >> 2) + (kSelThreads / 4) * u;
+      bm[u] = fetch_block<FAST>(a, bkv, j < j1 ? j : j1 - 1, r.nvis, hq);
+    }
+  }
+  // compressed output of this slice's heads: pair = (head of the slice, feature quad); with few
+  // pairs the chunks are split over `parts` threads per pair, with many (one slice for every
+  // head) the pairs take several passes.  The first batch of loads is issued now.
+  const int nrun = ranks ? (r.nb + a.SB - 1) / a.SB : 1;
+  const int hps = s < a.G ? (a.G - 1 - s) / nrun + 1 : 0;
+  const int npair = hps * (D / 4);
+  int parts = 1;
+  while (parts < 8 && 2 * parts * npair <= kSelThreads) parts *= 2;
+  const int npass = (npair + kSelThreads - 1) / kSelThreads;
+  struct OcMap { int pair, part, oh, of; bool on; };
+  auto oc_map = [&](int pass) {
+    OcMap m;
+    const int base = pass * kSelThreads;
+    const int span = npair - base < kSelThreads ? npair - base : kSelThreads;
+    m.pair = base + tid % span;
+    m.part = tid / span;
+    m.on = m.part < parts;
+    m.oh = s + nrun * (m.pair / (D / 4));
+    m.of = 4 * (m.pair % (D / 4));
+    return m;
+  };
+  constexpr int kOcBatch = 8;
+  f32x4 ocv[kOcBatch];
+  float ocm[kOcBatch];
+  auto oc_load = [&](const OcMap& m, int c0) {
+#pragma unroll
+    for (int u = 0; u < kOcBatch; ++u) {
+      const int c = c0 + u * parts, cc = c < clast ? c : clast;
+      const long ci = (bkv * a.NCH + cc) * 16 + m.oh;
+      ocv[u] = *reinterpret_cast<const f32x4*>(a.co + ci * D + m.of);
+      ocm[u] = c < r.nch ? a.cm[ci] : kNegInf;
+    }
+  };
+  if (npass > 0) {
+    const OcMap m = oc_map(0);
+    if (m.on) oc_load(m, m.part);
+  }
+  // 2. per-head log-sum-exp2 (16 lanes per head); heads past G get +inf: their weights vanish
+  float M = kNegInf;
+#pragma unroll
+  for (int i = 0; i < kLseRegs; ++i)
+    if (sub + 16 * i < r.nch) M = fmaxf(M, vm[i]);
+  for (int c = sub + 16 * kLseRegs; c < r.nch; c += 16) M = fmaxf(M, a.cm[cbase + c * 16]);
+  M = group_max<16>(M);
+  float Ls = 0.f;
+#pragma unroll
+  for (int i = 0; i < kLseRegs; ++i)
+    if (sub + 16 * i < r.nch) Ls += vl[i] * fast_exp2(vm[i] - M);
+  for (int c = sub + 16 * kLseRegs; c < r.nch; c += 16)
+    Ls += a.cl[cbase + c * 16] * fast_exp2(a.cm[cbase + c * 16] - M);
+  Ls = group_sum<16>(Ls);
+  const float lse = M == kNegInf ? __builtin_inff() : M + __log2f(Ls);
+  if (sub == 0) lse_s[h] = lse;
+  lds_barrier();
+  // the compressed output of this slice's heads, summed over the parts in order
+  for (int pass = 0; pass < npass; ++pass) {
+    const OcMap m = oc_map(pass);
+    if (m.on) {
+      if (pass > 0) oc_load(m, m.part);
+      const float lh = lse_s[m.oh];
+      f32x4 o = zero4();
+      for (int c0 = m.part;; c0 += kOcBatch * parts) {
+#pragma unroll
+        for (int u = 0; u < kOcBatch; ++u)  // a select: a chunk not written this call may hold NaN
+          o += ocm[u] == kNegInf ? zero4() : ocv[u] * fast_exp2(ocm[u] - lh);
+        if (c0 + kOcBatch * parts >= r.nch) break;
+        oc_load(m, c0 + kOcBatch * parts);
+      }
+      red[tid] = o;  // tid = part * span + local pair
+    }
+    lds_barrier();
+    if (m.on && m.part == 0) {
+      const int span = npair - pass * kSelThreads < kSelThreads ? npair - pass * kSelThreads
+                                                                  : kSelThreads;
+      f32x4 o = red[tid];
+      for (int q = 1; q < parts; ++q) o += red[q * span + tid];
+      *reinterpret_cast<f32x4*>(a.ocmp + (bkv * 16 + m.oh) * D + m.of) = o;
+    }
+    lds_barrier();  // red is reused by the next pass
+  }
+  if (!ranks) return;  // slice 0 of a group whose blocks all fit: only the compressed output
+  if (tid < 16 && tid >= a.G) lse_s[tid] = __builtin_inff();  // idle heads weigh nothing
+  lds_barrier();
+  // 3. tile weights exp2(tref - lse), then the block scores
+#pragma unroll
+  for (int i = 0; i < kSliceTiles * 16 / kSelThreads / 4; ++i) {
+    const int e = 4 * (tid + kSelThreads * i);
+    if (e < ntr) {
+      f32x4 w;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = fast_exp2(trv[i][q] - lse_s[(e + q) & 15]);
+      *reinterpret_cast<f32x4*>(trs + e) = w;
+    }
+  }
+  lds_barrier();
+  if (scored) {
+#pragma unroll
+    for (int u = 0; u < kPass; ++u) {
+      const int j = j0 + (tid >> 2) + (kSelThreads / 4) * u;
+      float S = 0.f;
+      if constexpr (FAST) {
+        if (bm[u].ntile & 1) S = mass_score(bm[u].m0, trs + (bm[u].ta - tlo) * 16 + 4 * hq);
+        if (bm[u].ntile & 2) S += mass_score(bm[u].m1, trs + (bm[u].tb - tlo) * 16 + 4 * hq);
+      } else {
+        if (bm[u].ntile >= 1) S = mass_score(bm[u].m0, trs + (bm[u].ta - tlo) * 16 + 4 * hq);
+        if (bm[u].ntile >= 2) S += mass_score(bm[u].m1, trs + (bm[u].ta + 1 - tlo) * 16 + 4 * hq);
+        for (int T = bm[u].ta + 2; T < bm[u].ta + bm[u].ntile; ++T) {  // wide blocks only
+          const int jj = j - (T * 64 * a.d) / a.beta;
+          const f32x4 m = *reinterpret_cast<const f32x4*>(
+              a.cb + ((bkv * a.NT + T) * a.NBT + jj) * 16 + 4 * hq);
+          S += mass_score(m, trs + (T - tlo) * 16 + 4 * hq);
+        }
+      }
+      S = group_sum<4>(S);  // the four lanes of a block hold the same j
+      if (hq == 0 && j < j1) Ss[j - j0] = S;
+    }
+  } else {
+    for (int j = j0 + tid; j < j1; j += kSelThreads) Ss[j - j0] = 0.f;
+  }
+  lds_barrier();
+  for (int j = j0 + tid; j < j1; j += kSelThreads) a.sS[bkv * a.NSL * a.SB + j] = Ss[j - j0];
+  if (wave == 0) {
+    const int lo = j0 > 1 ? j0 : 1;
+    const int hi = j1 < r.flo ? j1 : r.flo;  // free blocks: 1 .. flo - 1
+    const uint64_t key =
+        wave_topk([&](int j) { return rank_key(Ss[j - j0], j); }, lo, hi, a.KF, lane);
+    if (lane < a.KF) a.cand[(bkv * a.NSL + s) * a.KF + lane] = key;
+  }
 }
 
-// Group score share of one tile: masses times w = exp2(tref - lse), the per-head normalisation
-// of the compressed softmax (w per tile and head, computed once).
-__device__ __forceinline__ float mass_score(const f32x4& m, const float* w) {
-  return (m[0] * w[0] + m[1] * w[1]) + (m[2] * w[2] + m[3] * w[3]);
+// Selection slices of every group (see select_slice).
+template <int D, bool FAST>
+__global__ __launch_bounds__(kSelThreads) void dec_select_kernel(DecodeArgs a) {
+  __shared__ __align__(16) unsigned char smem[(16 + kSliceTiles * 16 + 256) * 4 +
+                                               kSelThreads * 16];
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  select_slice<D, FAST>(a, (long)b * a.Hkv + kvh, b, blockIdx.x, smem);
 }
+
+// ------------------------------------------------------------------ phase 3: one workgroup per group
 
 constexpr int kGrpWaves = 8;
 constexpr int kGrpThreads = 64 * kGrpWaves;
-constexpr int kGrpLanes = kGrpThreads / 4;  // blocks per pass (four lanes per block)
-constexpr int kGrpUnroll = 8;               // passes whose loads are in flight together
-constexpr int kCoRegs = 4;                  // compressed-output chunks prefetched in registers
 
-// Dynamic LDS of dec_group_kernel: one region reused by the three phases (selection state,
-// per-wave V^T tiles, per-wave partial outputs), then the compressed chunk weights.
-struct GroupLds {
-  size_t cm, cl, tr, S, keys, region, wc, total;
-};
-__host__ __device__ inline GroupLds group_lds(int D, int nch, int nt, int nblk) {
-  auto up = [](size_t x) { return (x + 15) & ~(size_t)15; };
-  GroupLds g{};
-  size_t o = 0;
-  g.cm = o;   o = up(o + (size_t)nch * 16 * 4);
-  g.cl = o;   o = up(o + (size_t)nch * 16 * 4);
-  g.tr = o;   o = up(o + (size_t)nt * 16 * 4);
-  g.S = o;    o = up(o + (size_t)nblk * 4);
-  g.keys = o; o = up(o + (size_t)kGrpWaves * 64 * 8);
-  const size_t tiles = (size_t)kGrpWaves * D * 64 * 2;
-  const size_t merge = (size_t)2 * kGrpWaves * 16 * (D + 4) * 4;
-  g.region = o > tiles ? o : tiles;
-  g.region = g.region > merge ? g.region : merge;
-  g.wc = g.region;
-  g.total = up(g.wc + (size_t)nch * 16 * 4);
-  return g;
-}
-
-// One workgroup per (sequence, group), after the compressed stream:
-//  1. the window's tiles (known before any selection) are requested at once, one per wave;
-//  2. per-head log-sum-exp of the compressed softmax, every group block score (the tile masses
-//     of the compressed stream rescaled by exp2(tref - lse), summed over the group's heads), the
-//     top-n with block 0 and the local blocks forced (each wave ranks an eighth of the blocks,
-//     one wave merges), the compressed output normalised and weighted;
-//  3. the tile list: window tiles first, then selected tiles outside the window, each tile once
-//     and marked with the branches it feeds; the waves take turns over it (the next tile's K in
-//     flight during this tile's softmax and P V, its V after them);
-//  4. the waves' partials merged per branch in LDS and the gate applied:
-//     out = g0 * o_cmp + g1 * o_slc + g2 * o_win.
-template <int D, bool FAST>
-__global__ __launch_bounds__(kGrpThreads, 1) void dec_group_kernel(DecodeArgs a) {
-  constexpr int DT = D / 16, OP = D + 4;
-  extern __shared__ __align__(16) unsigned char gsm[];
-  __shared__ float lse_s[16];
+// The rest of a group's step, after the slices: their candidates merged into the top-n (forced
+// blocks added, ascending, written out); one tile list with every tile the step reads once --
+// the window's (flagged for the selected branch when their block is selected), then the forced
+// and the other selected blocks' tiles outside the window; the waves take entries w, w + 8, ...
+// (a fixed assignment, so the output is reproducible bit for bit), each tile feeding both
+// branches; the waves' partials merged in LDS, added to the slices' compressed output under the
+// gate: out = g0 o_cmp + g1 o_slc + g2 o_win.
+template <int D>
+__global__ __launch_bounds__(kGrpThreads) void dec_group_kernel(DecodeArgs a) {
+  constexpr int OP = D + 4;
+  constexpr int PQ = 16 * D / kGrpThreads;  // (head, feature) pairs per thread
+  extern __shared__ __align__(16) unsigned char smem[];
+  u16(*Qs)[D + 8] = reinterpret_cast<u16(*)[D + 8]>(smem);
+  int* list = reinterpret_cast<int*>(smem + 16 * (D + 8) * 2);
+  unsigned char* region = smem + 16 * (D + 8) * 2 + kDecodeMaxList * 4;
+  u16(*Vt)[D][64] = reinterpret_cast<u16(*)[D][64]>(region);
   __shared__ int sidx[64];
-  __shared__ int tl_s[kMaxTiles];
-  __shared__ int tn_s;
-  __shared__ float Wm[2][kGrpWaves][16], Wl[2][kGrpWaves][16];
-  __shared__ __align__(16) u16 Qs[16][D + 8];  // the group's queries (MFMA B operand rows)
-  const GroupLds L = group_lds(D, a.NCH, a.NT, a.nblk);
-  float* scm = reinterpret_cast<float*>(gsm + L.cm);
-  float* scl = reinterpret_cast<float*>(gsm + L.cl);
-  float* trs = reinterpret_cast<float*>(gsm + L.tr);
-  float* Ss = reinterpret_cast<float*>(gsm + L.S);
-  uint64_t* Kw = reinterpret_cast<uint64_t*>(gsm + L.keys);
-  u16(*Vt)[D][64] = reinterpret_cast<u16(*)[D][64]>(gsm);
-  float* Ob = reinterpret_cast<float*>(gsm);  // [2][waves][16][OP]
-  float* wc = reinterpret_cast<float*>(gsm + L.wc);
-
+  __shared__ int n_s;
+  __shared__ float Wm[kGrpWaves][16], Wl[kGrpWaves][16], Ls[2][16];
   const int kvh = blockIdx.x, b = blockIdx.y;
   const long bkv = (long)b * a.Hkv + kvh;
+  const DecRow r = dec_row(a, b);
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, r16 = lane & 15;
-  const int t = a.seqlens[b] - 1;
-  const int nb = t / a.beta + 1;
-  const int nvis = n_visible(t, a.l, a.d, a.ncmp);
-  const int nch = (nvis + CHUNK - 1) / CHUNK;
-  const int ntv = (nvis + 63) / 64;
-  const bool top_p = a.top_p > 0.f;
-  const bool all = nb <= a.top_n && !top_p;  // uniform: every block is selected
-  const bool scored = !all && nvis > 0;  // uniform
-  const float sl = a.scale_log2;
-  const int w0 = t - a.window + 1;
-  const int wt0 = (w0 > 0 ? w0 : 0) / 64, wt1 = t / 64, nwin = wt1 - wt0 + 1;
-  const u16* kcb = a.kcache + bkv * (long)a.L * D;
-  const u16* vcb = a.vcache + bkv * (long)a.L * D;
-
-  // the group's queries, one 16-byte octet per thread (16 heads x D / 8 octets <= 512 threads),
-  // stored to LDS with the first statistics: the waves re-read their fragments per tile
-  // instead of holding them in registers
-  const int qh = tid / (D / 8), qc = (tid % (D / 8)) * 8;
-  const bool qlive = tid < 16 * (D / 8) && qh < a.G;
-  const bf16x8 qv =
-      load8(a.q + ((long)b * a.Hkv * a.G + kvh * a.G + (qlive ? qh : 0)) * D + (qlive ? qc : 0));
-
-  // 2. selection.  Loads first (chunk statistics, tile references, compressed outputs of the
-  // first chunks, the first block masses), then the LDS stores that wait for them.
-  const int hq = tid & 3, jq = tid >> 2;
-  const bool many = nch * 16 > kGrpThreads;  // uniform: beyond 32 chunks, a loop below
-  const int ce = tid < nch * 16 ? tid : 0;
-  const float cmv = a.cm[bkv * a.NCH * 16 + ce], clv = a.cl[bkv * a.NCH * 16 + ce];
-  // tile references: one f32x4 per thread up to 128 tiles (clamped, stored below), a loop beyond
-  const bool tr_loop = ntv * 4 > kGrpThreads;  // uniform
-  const f32x4 trv = *reinterpret_cast<const f32x4*>(
-      a.tref + bkv * a.NT * 16 + 4 * (tid < ntv * 4 ? tid : 0));
-  // the loads above are waited for first: keep them ahead of the prefetches below (the counter
-  // of loads in flight retires in order, so waiting for a later load waits for every earlier one)
-  __asm__ volatile("" ::: "memory");
-  BlockMass bm[kGrpUnroll];
-#pragma unroll
-  for (int u = 0; u < kGrpUnroll; ++u) {
-    const int j = jq + kGrpLanes * u;
-    bm[u] = fetch_block<FAST>(a, bkv, j < nb ? j : nb - 1, nvis, hq);
+  for (int e = tid; e < 16 * (D / 8); e += kGrpThreads) {
+    const int qh = e / (D / 8), qc = (e % (D / 8)) * 8;
+    *reinterpret_cast<bf16x8*>(&Qs[qh][qc]) =
+        qh < a.G ? load8(a.q + ((long)b * a.Hkv * a.G + kvh * a.G + qh) * D + qc) : zero8();
   }
-  __asm__ volatile("" ::: "memory");
-  if (!many && tid < nch * 16) {
-    scm[tid] = cmv;
-    scl[tid] = clv;
+  // the slices' candidates into LDS (the region the tiles use later), loads issued together
+  uint64_t* ck = reinterpret_cast<uint64_t*>(region);
+  const int nsl = (r.nb + a.SB - 1) / a.SB;
+  if (!r.all) {
+    const uint64_t* cb = a.cand + bkv * a.NSL * a.KF;
+    for (int i = tid; i < nsl * a.KF; i += kGrpThreads) ck[i] = cb[i];
   }
-  if (tid < 16 * (D / 8)) *reinterpret_cast<bf16x8*>(&Qs[qh][qc]) = qlive ? qv : zero8();
-  if (many)
-    for (int e = tid; e < nch * 16; e += kGrpThreads) {
-      scm[e] = a.cm[bkv * a.NCH * 16 + e];
-      scl[e] = a.cl[bkv * a.NCH * 16 + e];
-    }
-  if (tr_loop) {
-    for (int e = tid; e < ntv * 4; e += kGrpThreads)
-      *reinterpret_cast<f32x4*>(trs + 4 * e) =
-          *reinterpret_cast<const f32x4*>(a.tref + bkv * a.NT * 16 + 4 * e);
-  } else if (tid < ntv * 4) {
-    *reinterpret_cast<f32x4*>(trs + 4 * tid) = trv;
-  }
-  lds_barrier();
-  if (tid < 256) {  // 16 lanes per head
-    const int h = tid >> 4, sub = tid & 15;
-    float M = kNegInf;
-    for (int c = sub; c < nch; c += 16) M = fmaxf(M, scm[c * 16 + h]);
-    M = group_max<16>(M);
-    float Ls = 0.f;
-    for (int c = sub; c < nch; c += 16) Ls += scl[c * 16 + h] * fast_exp2(scm[c * 16 + h] - M);
-    Ls = group_sum<16>(Ls);
-    // heads past G get +inf: their weights vanish
-    if (sub == 0) lse_s[h] = (M == kNegInf || h >= a.G) ? __builtin_inff() : M + __log2f(Ls);
-  }
-  lds_barrier();
-  // chunk weights exp2(cm - lse); tile weights exp2(tref - lse) in place of the references
-  for (int e = tid; e < nch * 16; e += kGrpThreads) wc[e] = fast_exp2(scm[e] - lse_s[e & 15]);
-  for (int e = tid; e < ntv * 16; e += kGrpThreads) trs[e] = fast_exp2(trs[e] - lse_s[e & 15]);
-  lds_barrier();
-  if (scored) {
-    for (int j0 = jq;; j0 += kGrpLanes * kGrpUnroll) {
-#pragma unroll
-      for (int u = 0; u < kGrpUnroll; ++u) {
-        const int j = j0 + kGrpLanes * u;
-        float S = 0.f;
-        if constexpr (FAST) {
-          // main + carry equals the generic carry + main bit for bit (one commutative add)
-          if (bm[u].ntile & 1) S = mass_score(bm[u].m0, trs + bm[u].ta * 16 + 4 * hq);
-          if (bm[u].ntile & 2) S += mass_score(bm[u].m1, trs + bm[u].tb * 16 + 4 * hq);
-        } else {
-          if (bm[u].ntile >= 1) S = mass_score(bm[u].m0, trs + bm[u].ta * 16 + 4 * hq);
-          if (bm[u].ntile >= 2) S += mass_score(bm[u].m1, trs + (bm[u].ta + 1) * 16 + 4 * hq);
-          for (int T = bm[u].ta + 2; T < bm[u].ta + bm[u].ntile; ++T) {  // wide blocks only
-            const int jj = j - (T * 64 * a.d) / a.beta;
-            const f32x4 m = *reinterpret_cast<const f32x4*>(
-                a.cb + ((bkv * a.NT + T) * a.NBT + jj) * 16 + 4 * hq);
-            S += mass_score(m, trs + T * 16 + 4 * hq);
-          }
-        }
-        S = group_sum<4>(S);
-        if (hq == 0 && j < nb) Ss[j] = S;
-      }
-      const int jn = j0 + kGrpLanes * kGrpUnroll;
-      if (jn - jq >= nb) break;  // uniform
-#pragma unroll
-      for (int u = 0; u < kGrpUnroll; ++u) {
-        const int j = jn + kGrpLanes * u;
-        bm[u] = fetch_block<FAST>(a, bkv, j < nb ? j : nb - 1, nvis, hq);
-      }
-    }
-  } else if (!all) {
-    for (int j = tid; j < nb; j += kGrpThreads) Ss[j] = 0.f;
-  }
-  // compressed outputs of the first chunks for this thread's output pairs p = tid + 512 i
-  // (head p / D, feature p % D), in flight during the top-n.  (The window's K/V tiles are not
-  // requested here: with every group doing so at once, a wave stalls issuing them while memory
-  // is busy, and the whole workgroup waits for it at the next barrier.)
-  constexpr int PPT = 16 * D / kGrpThreads;
-  float cov[PPT][kCoRegs];
-#pragma unroll
-  for (int i = 0; i < PPT; ++i)
-#pragma unroll
-    for (int c = 0; c < kCoRegs; ++c) {
-      const int cc = c < a.NCH ? c : 0;
-      cov[i][c] = a.co[(bkv * a.NCH + cc) * 16 * D + tid + kGrpThreads * i];
-    }
-  lds_barrier();  // scores and chunk weights in LDS (the loads stay in flight)
-  const int bcur = nb - 1;
-  const int flo = bcur - a.n_local + 1 > 1 ? bcur - a.n_local + 1 : 1;  // forced: 0, flo..bcur
-  const int kfree = a.top_n - 1 - a.n_local;
-  // top-n in two levels: waves 0-3 (one per SIMD) each rank a quarter of the free blocks
-  // 1 .. flo-1, then wave 0 ranks their 4 * kfree winners
-  constexpr int kRankWaves = 4;
-  if (!all && wave < kRankWaves) {  // uniform
-    const int span = (flo - 1 + kRankWaves - 1) / kRankWaves;
-    const int lo = 1 + wave * span;
-    const int hi = lo + span < flo ? lo + span : flo;
-    const uint64_t key =
-        wave_topk([&](int j) { return rank_key(Ss[j], j); }, lo, hi, kfree, lane);
-    if (lane < kfree) Kw[wave * kfree + lane] = key;
-  }
-  lds_barrier();
+  __syncthreads();
   if (wave == 0) {
     int32_t* orow = a.idx + bkv * a.top_n;
-    if (all) {
+    if (r.all) {
       if (lane < a.top_n) {
-        const int el = lane < nb ? lane : -1;
+        const int el = lane < r.nb ? lane : -1;
         orow[lane] = el;
         sidx[lane] = el;
       }
     } else {
-      uint64_t key =
-          wave_topk([&](int i) { return Kw[i]; }, 0, kRankWaves * kfree, kfree, lane);
-      if (top_p) {
-        float forced = Ss[0];
-        for (int j = flo; j <= bcur; ++j) forced += Ss[j];
-        key = top_p_cut(key, kfree, forced, nvis > 0 ? a.top_p * (float)a.G : 0.f, lane);
+      uint64_t key = wave_topk([&](int i) { return ck[i]; }, 0, nsl * a.KF, r.kfree, lane);
+      if (r.top_p) {
+        const float* S = a.sS + bkv * a.NSL * a.SB;
+        float forced = S[0];
+        for (int j = r.flo; j <= r.bcur; ++j) forced += S[j];
+        key = top_p_cut(key, r.kfree, forced, r.nvis > 0 ? a.top_p * (float)a.G : 0.f, lane);
       }
       int el = key != 0 ? rank_key_index(key) : 0x7FFFFFFF;
-      if (lane == kfree) el = 0;
-      if (lane > kfree && lane <= kfree + bcur - flo + 1) el = flo + (lane - kfree - 1);
+      if (lane >= r.kfree) el = 0x7FFFFFFF;
+      if (lane == r.kfree) el = 0;
+      if (lane > r.kfree && lane <= r.kfree + r.bcur - r.flo + 1) el = r.flo + (lane - r.kfree - 1);
       int rank = 0;
       for (int o = 0; o < a.top_n; ++o)  // the whole wave is active here
         rank += (__builtin_amdgcn_readlane(el, o) < el) ? 1 : 0;
@@ -669,204 +951,130 @@ __global__ __launch_bounds__(kGrpThreads, 1) void dec_group_kernel(DecodeArgs a)
       }
     }
     __asm__ volatile("" ::: "memory");  // sidx written by this wave before its reads
-    // 3. tile list: the window tiles, flagged when their block is selected, then the tiles of
-    // selected blocks outside the window, at or before t
-    const int per = a.beta / 64;
-    for (int i = lane; i < nwin; i += 64) {
-      const int tile = wt0 + i, jw = tile / per;
-      bool in = false;
-      for (int e = 0; e < a.top_n; ++e) in |= sidx[e] == jw;
-      tl_s[i] = tile | (in ? 1 << 30 : 0);
-    }
-    const int nsel = a.top_n * per;
-    int base = nwin;
-    for (int i0 = 0; i0 < nsel; i0 += 64) {
-      const int i = i0 + lane;
-      int code = -1;
-      if (i < nsel) {
-        const int jb = sidx[i / per], tile = jb * per + i % per;
-        if (jb >= 0 && tile * 64 <= t && (tile < wt0 || tile > wt1)) code = tile | (1 << 30);
-      }
-      const uint64_t m = __ballot(code >= 0);
-      const int pos = base + (int)__popcll(m & ((1ull << lane) - 1ull));
-      if (code >= 0) tl_s[pos] = code;
-      base += (int)__popcll(m);
-    }
-    if (lane == 0) tn_s = base;
-  }
-  lds_barrier();  // tile list ready; the selection state in the shared region is dead
-  // compressed output of this thread's pairs: sum over chunks of co * exp2(cm - lse)
-  float ocmp[PPT];
-#pragma unroll
-  for (int i = 0; i < PPT; ++i) {
-    const int h = (tid + kGrpThreads * i) / D;
-    float o = 0.f;
-#pragma unroll
-    for (int c = 0; c < kCoRegs; ++c) o += c < nch ? cov[i][c] * wc[c * 16 + h] : 0.f;
-    for (int c = kCoRegs; c < nch; ++c)  // long contexts only
-      o += a.co[(bkv * a.NCH + c) * 16 * D + tid + kGrpThreads * i] * wc[c * 16 + h];
-    ocmp[i] = o;
-  }
-
-  // 3. the tiles: wave w takes list entries w, w + 8, ... (a fixed assignment: the same wave
-  // sums the same tiles in the same order on every call, so the output is reproducible bit for
-  // bit; handing entries to whichever wave asks first balanced slow loads for 1.3 us less)
-  const int tn = __builtin_amdgcn_readfirstlane(tn_s);
-  float mrun[2] = {kNegInf, kNegInf}, lrun[2] = {0.f, 0.f};
-  f32x4 O[2][DT];
-#pragma unroll
-  for (int br = 0; br < 2; ++br)
-#pragma unroll
-    for (int n = 0; n < DT; ++n) O[br][n] = zero4();
-  if (wave < tn) {  // uniform per wave
-    int e = wave;
-    DecTile<D> kv;
-    kv.load(kcb, vcb, (tl_s[e] & 0x3FFFFFFF) * 64, t, lane);
-    for (;;) {
-      const int code = __builtin_amdgcn_readfirstlane(tl_s[e]);
-      const int k0 = (code & 0x3FFFFFFF) * 64;
-      const bool in_slc = (code >> 30) & 1, in_win = k0 + 63 >= w0;
-      // the next tile; after the last one every row of the "next" load is row t (one line)
-      const int en = e + kGrpWaves;  // static round robin: the same wave sums the same tiles
-      const bool more = en < tn;
-      const int k1 =
-          more ? (__builtin_amdgcn_readfirstlane(tl_s[en]) & 0x3FFFFFFF) * 64 : t;
-      const int last1 = more ? t : k1;
-      f32x4 acc[4];
-      {
-        bf16x8 qf[D / 32];
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) qf[c] = load8(&Qs[r16][32 * c + 8 * g4]);
-        kv.scores(qf, acc);
-      }
-      __asm__ volatile("" ::: "memory");  // the previous tile's Vt reads stay before these writes
-      kv.stage(Vt[wave], lane);
-      __asm__ volatile("" ::: "memory");  // Vt[wave] is this wave's own: LDS keeps its order
-      kv.load_k(kcb, k1, last1, lane);
-#pragma unroll
-      for (int br = 0; br < 2; ++br) {
-        float p[16];
-        float tm = kNegInf;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = k0 + lane_key(q4, i, g4);
-            const bool ok = br == 0 ? (in_slc && key <= t) : (in_win && key <= t && key >= w0);
-            const float r = ok ? acc[q4][i] : kNegInf;
-            p[q4 * 4 + i] = r;
-            tm = fmaxf(tm, r);
+    // the window's and forced blocks' tiles, then the other selected blocks' tiles: flagged in
+    // the window, appended outside it
+    int base = fixed_tile_list(a, r, list, lane);
+    if (!r.all) {
+      const int per = a.beta / 64, ns = a.top_n * per, tl = r.t / 64;
+      for (int i0 = 0; i0 < ns; i0 += 64) {
+        const int i = i0 + lane;
+        int code = -1;
+        if (i < ns) {
+          const int jb = sidx[i / per], tile = jb * per + i % per;
+          const bool forced = jb == 0 || (jb >= r.flo && jb <= r.bcur);
+          if (jb >= 0 && !forced && tile <= tl) {
+            if (tile >= r.wt0 && tile <= r.wt1)
+              list[tile - r.wt0] |= (int)kCodeSlc;  // distinct tiles: one lane per entry
+            else
+              code = (int)(tile | kCodeSlc);
           }
-        tm = col_max4(tm);
-        const float mn = fmaxf(mrun[br], tm);
-        const float ms = mn == kNegInf ? 0.f : mn * sl;
-        const float alpha = fast_exp2(fmaf(mrun[br], sl, -ms));
-        mrun[br] = mn;
-        float ls = 0.f;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          p[q] = fast_exp2(fmaf(p[q], sl, -ms));
-          ls += p[q];
         }
-        lrun[br] = fmaf(lrun[br], alpha, col_sum4(ls));
-#pragma unroll
-        for (int n = 0; n < DT; ++n) O[br][n] *= alpha;
-        tile_pv<D>(Vt[wave], p, g4, r16, O[br]);
+        const uint64_t m = __ballot(code >= 0);
+        const int pos = base + (int)__popcll(m & ((1ull << lane) - 1ull));
+        if (code >= 0) list[pos] = code;
+        base += (int)__popcll(m);
       }
-      kv.load_v(vcb, k1, last1, lane);
-      if (!more) break;
-      e = en;
     }
+    if (lane == 0) n_s = base;
   }
-  if (g4 == 0) {
-#pragma unroll
-    for (int br = 0; br < 2; ++br) { Wm[br][wave][r16] = mrun[br]; Wl[br][wave][r16] = lrun[br]; }
-  }
-  __syncthreads();  // Vt reads done; maxima posted
-  // 4. partials rescaled to the workgroup maximum of each branch, summed through LDS
+  __syncthreads();  // the list is posted and the candidates' LDS is free for the tiles
+  const int n = __builtin_amdgcn_readfirstlane(n_s);
+  WaveSoftmax<D, 2> st;
+  wave_tiles<D, 2>(a, bkv, r, list, n, wave, kGrpWaves, Qs, Vt[wave], st);
+  // the waves' partials of each branch rescaled to the workgroup maximum and summed through LDS
+  // (one branch at a time); thread tid keeps the sums of pairs tid + 512 q (head, feature)
+  float* Ob = reinterpret_cast<float*>(region);  // [waves][16][OP]
+  const float sl = a.scale_log2;
+  float ob[2][PQ];
 #pragma unroll
   for (int br = 0; br < 2; ++br) {
+    __syncthreads();  // the tiles' (or the previous branch's) LDS reads are done
+    if (g4 == 0) {
+      Wm[wave][r16] = st.m[br];
+      Wl[wave][r16] = st.l[br];
+    }
+    __syncthreads();
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kGrpWaves; ++w) M = fmaxf(M, Wm[br][w][r16]);
-    const float f =
-        Wm[br][wave][r16] == kNegInf ? 0.f : fast_exp2((Wm[br][wave][r16] - M) * sl);
+    for (int w = 0; w < kGrpWaves; ++w) M = fmaxf(M, Wm[w][r16]);
+    const float f = st.m[br] == kNegInf ? 0.f : fast_exp2((st.m[br] - M) * sl);
 #pragma unroll
-    for (int n = 0; n < DT; ++n)
-      *reinterpret_cast<f32x4*>(&Ob[((br * kGrpWaves + wave) * 16 + r16) * OP + 16 * n + 4 * g4]) =
-          f * O[br][n];
-  }
-  __syncthreads();
+    for (int n2 = 0; n2 < D / 16; ++n2)
+      *reinterpret_cast<f32x4*>(&Ob[(wave * 16 + r16) * OP + 16 * n2 + 4 * g4]) = f * st.O[br][n2];
+    if (tid < 16) {  // lanes 0..15 of wave 0 own rows 0..15: M is row tid's maximum
+      float L = 0.f;
 #pragma unroll
-  for (int i = 0; i < PPT; ++i) {
-    const int pr = tid + kGrpThreads * i;
-    const int h = pr / D, dd = pr % D;
-    if (h >= a.G) continue;
-    float ob[2];
-#pragma unroll
-    for (int br = 0; br < 2; ++br) {
-      float M = kNegInf;
-#pragma unroll
-      for (int w = 0; w < kGrpWaves; ++w) M = fmaxf(M, Wm[br][w][h]);
-      float Lb = 0.f, o = 0.f;
-#pragma unroll
-      for (int w = 0; w < kGrpWaves; ++w) {
-        if (Wm[br][w][h] != kNegInf) Lb += Wl[br][w][h] * fast_exp2((Wm[br][w][h] - M) * sl);
-        o += Ob[((br * kGrpWaves + w) * 16 + h) * OP + dd];
-      }
-      ob[br] = Lb > 0.f ? o / Lb : 0.f;
+      for (int w = 0; w < kGrpWaves; ++w)
+        if (Wm[w][tid] != kNegInf) L += Wl[w][tid] * fast_exp2((Wm[w][tid] - M) * sl);
+      Ls[br][tid] = L;
     }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < PQ; ++q) {
+      const int pr = tid + kGrpThreads * q, h = pr / D, dd = pr % D;
+      float o = 0.f;
+#pragma unroll
+      for (int w = 0; w < kGrpWaves; ++w) o += Ob[(w * 16 + h) * OP + dd];
+      ob[br][q] = o;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < PQ; ++q) {
+    const int pr = tid + kGrpThreads * q, h = pr / D, dd = pr % D;
+    if (h >= a.G) continue;
+    const float ls = Ls[0][h], lw = Ls[1][h];
     const long head = (long)b * a.Hkv * a.G + kvh * a.G + h;
     const float* g = a.gate + head * 3;
-    a.out[head * D + dd] = g[0] * ocmp[i] + g[1] * ob[0] + g[2] * ob[1];
+    a.out[head * D + dd] = g[0] * a.ocmp[(bkv * 16 + h) * D + dd] +
+                           g[1] * (ls > 0.f ? ob[0][q] / ls : 0.f) +
+                           g[2] * (lw > 0.f ? ob[1][q] / lw : 0.f);
   }
 }
 
 // ------------------------------------------------------------------ launcher
 
 int decode_chunk_tokens() { return CHUNK; }
-int decode_max_tile_list() { return kMaxTiles; }
-size_t decode_group_lds_bytes(int D, int nch, int nt, int nblk) {
-  return group_lds(D, nch, nt, nblk).total;
+
+// Dynamic LDS of the per-group kernel: the group's queries, its tile list, and one V^T tile per
+// wave (the candidates before, the partial merge after reuse the tiles' space).
+static size_t group_lds(int D) {
+  const size_t tiles = (size_t)kGrpWaves * D * 64 * 2;
+  const size_t merge = (size_t)kGrpWaves * 16 * (D + 4) * 4;
+  const size_t cand = (size_t)decode_max_candidates(D) * 8;
+  size_t region = tiles > merge ? tiles : merge;
+  region = region > cand ? region : cand;
+  return (size_t)16 * (D + 8) * 2 + kDecodeMaxList * 4 + region;
 }
 
-void launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
+template <int D, bool FAST>
+static void launch_decode_t(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
   auto mark = [&](int i) {
     if (ev != nullptr) (void)hipEventRecord(ev[i], s);
   };
-  const bool fast = a.beta == 4 * a.d && a.l == 2 * a.d && a.NBT >= 17;
-  const size_t lds = decode_group_lds_bytes(a.D, a.NCH, a.NT, a.nblk);
-  const void* gk =
-      a.D == 128 ? (fast ? reinterpret_cast<const void*>(dec_group_kernel<128, true>)
-                         : reinterpret_cast<const void*>(dec_group_kernel<128, false>))
-                 : (fast ? reinterpret_cast<const void*>(dec_group_kernel<64, true>)
-                         : reinterpret_cast<const void*>(dec_group_kernel<64, false>));
-  // opt in to the accepted maximum (not this launch's size: concurrent calls on other host
-  // threads may need more); the attribute is per device, so it is set on every launch
+  const size_t lds = group_lds(D);
+  // opt in to the dynamic LDS beyond 64 KB; the attribute is per device, so it is set on every
+  // launch
   if (lds > 64 * 1024)
-    (void)hipFuncSetAttribute(gk, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)kMaxDecodeDynLds);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(dec_group_kernel<D>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   mark(0);
-  if (a.NCH > 0) {
-    const dim3 g1(a.NCH, a.Hkv, a.B);
-    if (a.D == 128) {
-      if (fast) dec_cmp_kernel<128, true><<<g1, 256, 0, s>>>(a);
-      else dec_cmp_kernel<128, false><<<g1, 256, 0, s>>>(a);
-    } else {
-      if (fast) dec_cmp_kernel<64, true><<<g1, 256, 0, s>>>(a);
-      else dec_cmp_kernel<64, false><<<g1, 256, 0, s>>>(a);
-    }
-  }
+  if (a.NCH > 0) dec_cmp_kernel<D, FAST><<<dim3(a.NCH, a.Hkv, a.B), 256, 0, s>>>(a);
   mark(1);
-  const dim3 g2(a.Hkv, a.B);
-  if (a.D == 128) {
-    if (fast) dec_group_kernel<128, true><<<g2, kGrpThreads, lds, s>>>(a);
-    else dec_group_kernel<128, false><<<g2, kGrpThreads, lds, s>>>(a);
-  } else {
-    if (fast) dec_group_kernel<64, true><<<g2, kGrpThreads, lds, s>>>(a);
-    else dec_group_kernel<64, false><<<g2, kGrpThreads, lds, s>>>(a);
-  }
+  dec_select_kernel<D, FAST><<<dim3(a.NSL, a.Hkv, a.B), kSelThreads, 0, s>>>(a);
   mark(2);
+  dec_group_kernel<D><<<dim3(a.Hkv, a.B), kGrpThreads, lds, s>>>(a);
+  mark(3);
+}
+
+void launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {
+  const bool fast = a.beta == 4 * a.d && a.l == 2 * a.d && a.NBT >= 17;
+  if (a.D == 128) {
+    if (fast) launch_decode_t<128, true>(a, s, ev);
+    else launch_decode_t<128, false>(a, s, ev);
+  } else {
+    if (fast) launch_decode_t<64, true>(a, s, ev);
+    else launch_decode_t<64, false>(a, s, ev);
+  }
 }
 
 }  // namespace nsa

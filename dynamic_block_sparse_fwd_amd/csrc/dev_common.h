@@ -135,6 +135,11 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Max / sum over the whole wave (rows, then across the four rows), returned in every lane; the
+// order of the additions is fixed, so the result is the same on every call.
+__device__ __forceinline__ float wave_max_f(float v) { return col_max4(group_max<16>(v)); }
+__device__ __forceinline__ float wave_sum_f(float v) { return col_sum4(group_sum<16>(v)); }
+
 // Unsigned max over the whole wave, returned in every lane.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, xor_lane_u32<1>(v));

@@ -48,9 +48,14 @@ struct DecodeArgs {
   float* co;    // [B*Hkv, NCH, 16, D] unnormalised output
   float* tref;  // [B*Hkv, NT, 16] per 64-token tile: reference of its block masses (log2)
   float* cb;    // [B*Hkv, NT, NBT, 16] block masses of each tile, relative to exp2(tref)
+  float* sS;        // [B*Hkv, NSL * SB] group block scores, written by the selection slices
+  uint64_t* cand;   // [B*Hkv, NSL, KF] each slice's best free blocks (rank keys, 0 = none)
+  float* ocmp;      // [B*Hkv, 16, D] compressed-branch output, normalised by the selection slices
   int B, L, Hkv, G, D;
   int l, d, beta, top_n, n_local, window;
   int ncmp, nblk, NCH, NT, NBT;
+  int SB, NSL;  // blocks per selection slice, slices per group
+  int KF;       // free blocks per group: top_n - 1 - n_local (at least 1)
   float scale_log2;
   float top_p;  // 0: fixed top_n; else the adaptive cut at top_p * G
 };
@@ -58,10 +63,12 @@ struct DecodeArgs {
 // ev: nullptr or NSA_DECODE_NSTAGES + 1 events recorded around the stages.
 void launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev);
 int decode_chunk_tokens();
-int decode_max_tile_list();
-// dynamic LDS of the per-group kernel (selection state, per-wave tiles, partials)
-size_t decode_group_lds_bytes(int D, int nch, int nt, int nblk);
-constexpr size_t kMaxDecodeDynLds = 152 * 1024;  // accepted maximum of the above
+constexpr int kDecodeMaxList = 256;  // tiles of a group's tile list
+// blocks per selection slice: at most 256, and few enough that the compressed-token tiles the
+// slice's blocks touch fit the slice's 64-tile weight table
+int decode_slice_blocks(int l, int d, int beta);
+// candidates (slices x free blocks) the per-group kernel stages in LDS
+__host__ __device__ constexpr int decode_max_candidates(int D) { return 4 * D * 64 * 2 / 8; }
 
 // Backward of the prefill layer (G = 16).
 struct BwdArgs {

@@ -215,10 +215,11 @@ int nsa_prefill_timed(const nsa_config* cfg, const void* q, const void* k, const
  *   sel_idx        int32 [B, Hkv, top_n] or NULL
  * Deterministic: the same inputs give the same output and indices bit for bit.  Captures into a
  * HIP graph (kernels only, no allocation, no memset).
- * Returns NSA_ERR_UNSUPPORTED when top_n * sel_block / 64 + ceil(window / 64) + 1 > 160
- * (tile table), Lmax > 2^24, or the per-group selection state (chunk statistics, tile
- * references, block scores) outgrows 152 KB of LDS (the workgroup's other LDS and it share
- * 160 KB).
+ * Returns NSA_ERR_UNSUPPORTED when Lmax > 2^24, B or Hkv > 65535, when the per-slice
+ * candidates outgrow the LDS that stages them, ceil(ceil(Lmax / sel_block) / S) *
+ * max(1, top_n - 1 - n_local) > 16 * D (S = 256 selection blocks per slice for the default
+ * geometry; about 10M tokens at D = 128, 5M at D = 64), or when a group's tile list outgrows
+ * 256 entries: ceil(window / 64) + 1 + top_n * sel_block / 64 > 256.
  */
 int nsa_decode(const nsa_config* cfg, const void* q, const void* kcache, const void* vcache,
                const void* kcmp, const void* vcmp, const int32_t* seqlens, const float* gate,
@@ -226,10 +227,11 @@ int nsa_decode(const nsa_config* cfg, const void* q, const void* kcache, const v
 
 /*
  * Instrumented nsa_decode: identical work, plus events[s] recorded before stage s and
- * events[NSA_DECODE_NSTAGES] after the last.  Stages: 0 compressed-cache stream, 1 per group:
- * block scores, selection, selected + window tiles, merge and gate.  For measurement only.
+ * events[NSA_DECODE_NSTAGES] after the last.  Stages: 0 compressed-cache stream, 1 block scores,
+ * per-slice ranking and the compressed output, 2 per group: top-n, the window's and selected
+ * tiles, merge and gate.  For measurement only.
  */
-#define NSA_DECODE_NSTAGES 2
+#define NSA_DECODE_NSTAGES 3
 int nsa_decode_timed(const nsa_config* cfg, const void* q, const void* kcache,
                      const void* vcache, const void* kcmp, const void* vcmp,
                      const int32_t* seqlens, const float* gate, float* out, int32_t* sel_idx,

@@ -61,6 +61,8 @@ EXPORTS = {
                           [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p,
                                                      ctypes.c_void_p]),
     "nsa_decode": (ctypes.c_int, [ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p]),
+    "nsa_decode_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 11),
+    "nsa_decode_noalloc_max_bytes": (ctypes.c_size_t, []),
     "nsa_decode_timed": (ctypes.c_int, [ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p,
                                                                  ctypes.c_void_p]),
     "nsa_cache_append_workspace_bytes": (ctypes.c_size_t, [ctypes.c_void_p]),
@@ -353,6 +355,33 @@ def nsa_decode(cfg: NsaConfig, q, kcache, vcache, kcmp, vcmp, seqlens, gate, out
         ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream), *extra)
     _check(st, "nsa_decode")
     return out, sel_idx
+
+
+def nsa_decode_noalloc(cfg: NsaConfig, q, kcache, vcache, kcmp, vcmp, seqlens, gate, out,
+                       sel_idx=None, stream=None):
+    """nsa_decode on the library's static per-GPU workspace (no workspace argument; neither the
+    library nor this binding allocates).  out (fp32 [B,Hq,D]) must be given; sel_idx
+    ([B,Hkv,top_n] int32) is optional.  Returns (out, sel_idx)."""
+    torch = _torch()
+    lib = load_library()
+    c = cfg.c()
+    B, L, Hkv, Hq, D = cfg.B, cfg.T, cfg.Hkv, cfg.Hq, cfg.D
+    bt = _bf16_types()
+    st = lib.nsa_decode_noalloc(
+        ctypes.byref(c), _dev(q, "q", bt, (B, Hq, D)), _dev(kcache, "kcache", bt, (B, Hkv, L, D)),
+        _dev(vcache, "vcache", bt, (B, Hkv, L, D)), _dev(kcmp, "kcmp", bt, (B, Hkv, cfg.ncmp, D)),
+        _dev(vcmp, "vcmp", bt, (B, Hkv, cfg.ncmp_tiles, D, 64)),
+        _dev(seqlens, "seqlens", (torch.int32,), (B,)),
+        _dev(gate, "gate", (torch.float32,), (B, Hq, 3)),
+        _dev(out, "out", (torch.float32,), (B, Hq, D)),
+        None if sel_idx is None else _dev(sel_idx, "sel_idx", (torch.int32,), (B, Hkv, cfg.top_n)),
+        _stream(stream))
+    _check(st, "nsa_decode_noalloc")
+    return out, sel_idx
+
+
+def decode_noalloc_max_bytes() -> int:
+    return int(load_library().nsa_decode_noalloc_max_bytes())
 
 
 def nsa_cache_append(cfg: NsaConfig, k_new, v_new, seqlens, wk, wv, kcache, vcache, kcmp,

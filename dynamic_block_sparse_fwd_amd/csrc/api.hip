@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/nsa.h"
 #include "kernels.h"
@@ -665,6 +666,54 @@ int nsa_decode(const nsa_config* c, const void* q, const void* kcache, const voi
                float* out, int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
   return decode_impl(c, q, kcache, vcache, kcmp, vcmp, seqlens, gate, out, sel_idx, ws,
                      ws_bytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+// ---- allocation-free decode
+
+namespace {
+
+// The workspace of nsa_decode_noalloc: one copy per GPU, in the code object's device memory,
+// held until the process ends.  In host code `scratch` names a host-side stand-in; the device
+// address of each GPU's copy comes from hipGetSymbolAddress on that device.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// This GPU's copy of the scratch array (resolved once per device, with that device current);
+// null on failure.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nsa_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int nsa_decode_noalloc(const nsa_config* c, const void* q, const void* kcache, const void* vcache,
+                       const void* kcmp, const void* vcmp, const int32_t* seqlens,
+                       const float* gate, float* out, int32_t* sel_idx, hipStream_t stream) {
+  int st = check_nsa_decode(c);
+  if (st != NSA_OK) return st;
+  if (plan_decode(c).total > kScratchBytes) return NSA_ERR_WORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return NSA_ERR_HIP;
+  return decode_impl(c, q, kcache, vcache, kcmp, vcmp, seqlens, gate, out, sel_idx, ws,
+                     kScratchBytes, stream, nullptr);
 }
 
 int nsa_decode_timed(const nsa_config* c, const void* q, const void* kcache, const void* vcache,

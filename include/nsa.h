@@ -226,6 +226,25 @@ int nsa_decode(const nsa_config* cfg, const void* q, const void* kcache, const v
                float* out, int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * nsa_decode without a workspace argument, for callers that cannot allocate device memory
+ * (code being captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc).  The workspace is a static array of the library, one copy per GPU, of
+ * nsa_decode_noalloc_max_bytes() bytes (64 MiB), held until the process ends; nothing is
+ * allocated or freed by the call.  Arguments, results and errors as nsa_decode, plus
+ * NSA_ERR_WORKSPACE when the configuration needs more workspace than that
+ * (nsa_decode_workspace_bytes(cfg) > nsa_decode_noalloc_max_bytes(); e.g. 64k tokens x batch
+ * 32 x 4 KV heads needs about 15 MB) and NSA_ERR_HIP when the array's device address cannot be
+ * resolved.  Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (concurrent streams or host threads) race.  The array is resolved on the device current at
+ * the call, which must be the device of the pointers and the stream.
+ */
+size_t nsa_decode_noalloc_max_bytes(void);
+int nsa_decode_noalloc(const nsa_config* cfg, const void* q, const void* kcache,
+                       const void* vcache, const void* kcmp, const void* vcmp,
+                       const int32_t* seqlens, const float* gate, float* out, int32_t* sel_idx,
+                       hipStream_t stream);
+
+/*
  * Instrumented nsa_decode: identical work, plus events[s] recorded before stage s and
  * events[NSA_DECODE_NSTAGES] after the last.  Stages: 0 compressed-cache stream, 1 block scores,
  * per-slice ranking and the compressed output, 2 per group: top-n, the window's and selected

@@ -51,6 +51,11 @@ int check_nsa(const nsa_config* c) {
   if (cmp_select_lds_bytes(c->G, (int)nblk) > kMaxDynLds) return NSA_ERR_UNSUPPORTED;
   if (c->top_n * (c->sel_block / 64) > 64) return NSA_ERR_UNSUPPORTED;  // one tile per lane
   if ((long)((c->T + 3) / 4) * c->B * c->Hkv > (1L << 31) - 8) return NSA_ERR_UNSUPPORTED;
+  // block-major selected branch: entries are (row << 6 | slot) in 32 bits, work tiles in a 1-D
+  // grid
+  if ((long)c->B * c->T >= (1L << 25)) return NSA_ERR_UNSUPPORTED;
+  if ((long)c->B * c->T * c->Hkv * c->top_n * (c->sel_block / 64) / kSlcRows >= (1L << 30))
+    return NSA_ERR_UNSUPPORTED;
   return NSA_OK;
 }
 
@@ -137,7 +142,8 @@ MobaPlan plan_moba(const moba_config* c) {
 
 struct PrefillPlan {
   size_t vt, kc, vct, wkt, wvt, idx, total;
-  int ncmp, NCP, TP, nblk;
+  size_t s_rank, s_kt, s_count, s_offset, s_tstart, s_ntiles, s_tile_entry, s_list, s_po, s_ps;
+  int ncmp, NCP, TP, nblk, FS, NTK, s_max_tiles;
 };
 
 PrefillPlan plan_prefill(const nsa_config* c) {
@@ -154,8 +160,40 @@ PrefillPlan plan_prefill(const nsa_config* c) {
   p.wkt = off; off += align_up((size_t)c->cmp_len * c->D * c->D * 2);
   p.wvt = off; off += align_up((size_t)c->cmp_len * c->D * c->D * 2);
   p.idx = off; off += align_up((size_t)c->B * c->T * c->Hkv * c->top_n * 4);
+  // selected branch, block-major part: sized for query rows 0 .. T-1
+  p.FS = c->top_n * (c->sel_block / 64);
+  p.NTK = p.TP / 64;
+  const size_t nent = (size_t)BH * c->T * p.FS;
+  const size_t nsub = (size_t)kSlcChunks * BH * p.NTK;
+  p.s_max_tiles = (int)(nent / kSlcRows + nsub + 1);
+  p.s_rank = off;       off += align_up(nent * 4);
+  p.s_kt = off;         off += align_up(nent * 4);
+  p.s_count = off;      off += align_up(nsub * 4);
+  p.s_offset = off;     off += align_up((nsub + 1) * 4);
+  p.s_tstart = off;     off += align_up(nsub * 4);
+  p.s_ntiles = off;     off += align_up(4);
+  p.s_tile_entry = off; off += align_up((size_t)p.s_max_tiles * 4);
+  p.s_list = off;       off += align_up(nent * 4);
+  p.s_po = off;         off += align_up(nent * 16 * c->D * 2);
+  p.s_ps = off;         off += align_up(nent * 16 * 4 * 4);
   p.total = off;
   return p;
+}
+
+void set_selected_ws(PrefillArgs& a, const PrefillPlan& p, char* base) {
+  a.s_rank = reinterpret_cast<int32_t*>(base + p.s_rank);
+  a.s_kt = reinterpret_cast<int32_t*>(base + p.s_kt);
+  a.s_count = reinterpret_cast<int32_t*>(base + p.s_count);
+  a.s_offset = reinterpret_cast<int32_t*>(base + p.s_offset);
+  a.s_tstart = reinterpret_cast<int32_t*>(base + p.s_tstart);
+  a.s_ntiles = reinterpret_cast<int32_t*>(base + p.s_ntiles);
+  a.s_tile_entry = reinterpret_cast<int32_t*>(base + p.s_tile_entry);
+  a.s_list = reinterpret_cast<int32_t*>(base + p.s_list);
+  a.s_po = reinterpret_cast<_Float16*>(base + p.s_po);
+  a.s_ps = reinterpret_cast<float*>(base + p.s_ps);
+  a.FS = p.FS;
+  a.NTK = p.NTK;
+  a.s_max_tiles = p.s_max_tiles;
 }
 
 struct BackwardPlan {
@@ -368,6 +406,7 @@ static int prefill_run(const nsa_config* c, unsigned stages, const void* q, cons
   a.ncmp = p.ncmp; a.NCP = p.NCP; a.TP = p.TP; a.nblk = p.nblk;
   a.scale_log2 = c->scale * 1.4426950408889634f;
   a.fuse_window = s_cmp && s_win;  // one query tile, out written once
+  set_selected_ws(a, p, base);
   mark(2);
   if (s_cmp) launch_cmp_select(a, stream);
   mark(3);
@@ -455,6 +494,8 @@ int nsa_prefill_chunk(const nsa_config* c, int32_t P, int32_t C, const void* q,
   a.nblk = (Tend + c->sel_block - 1) / c->sel_block;
   a.scale_log2 = c->scale * 1.4426950408889634f;
   a.fuse_window = 1;
+  set_selected_ws(a, p, base);
+  a.NTK = a.TP / 64;  // key tiles of this chunk's keys; the lists are sized for the capacity
   (void)hipGetLastError();
   launch_transpose(static_cast<const uint16_t*>(vcache), vt, BH, Tend, c->D, a.TP, stream, c->T);
   launch_cmp_cache_layout(static_cast<const uint16_t*>(kcmp), static_cast<const uint16_t*>(vcmp),

@@ -24,7 +24,24 @@ struct PrefillArgs {
   float scale_log2;     // softmax scale * log2(e)
   float top_p;          // 0: fixed top_n; else the adaptive cut at top_p * G
   int fuse_window;      // cmp_select also runs the window branch and writes out once
+  // Selected branch, block-major part (workspace).  An "entry" is one selected 64-key tile of one
+  // (row, group) that is not among the tiles the selected kernel shares per eight positions;
+  // row = b * nq + (t - q0), free slot fs = its rank among the row's such tiles (< FS).
+  int32_t* s_rank;       // [B*nq, Hkv, FS] rank of the entry in its sub-list
+  int32_t* s_kt;         // [B*nq, Hkv, FS] key tile of the entry, -1 past the row's entries
+  int32_t* s_count;      // [SC, B*Hkv, NTK] entries per (T-chunk, sequence-group, key tile)
+  int32_t* s_offset;     // [SC * B*Hkv * NTK + 1] sub-list offsets (after the scan)
+  int32_t* s_tstart;     // [SC * B*Hkv * NTK] first work tile of each sub-list
+  int32_t* s_ntiles;     // [1] work tiles in all
+  int32_t* s_tile_entry; // [s_max_tiles] sub-list of each work tile
+  int32_t* s_list;       // [B*nq*Hkv*FS] entries by sub-list: row << 6 | fs
+  _Float16* s_po;        // [B*nq, Hkv, FS, 16, D] partial outputs / (sum * scale), fp16
+  float* s_ps;           // [B*nq, Hkv, FS, 16, 4] partial (max in log2 units, sum, scale, 0)
+  int FS, NTK, s_max_tiles;
 };
+
+constexpr int kSlcChunks = 16;  // T-chunks of the block-major lists (work tiles chunk-major)
+constexpr int kSlcRows = 32;   // positions per block-major work tile
 
 // Row of q/gate/out/idx holding query position t of sequence b.
 __device__ __forceinline__ long prow(const PrefillArgs& a, int b, int t) {

@@ -1,11 +1,9 @@
 // NSA prefill kernels ("Zhang Xiaojun podcast EP94 notes", sections 5 and 6):
 //   cmp_select_kernel: compressed attention + block importance + group top-n selection;
-//   window_kernel:     sliding-window attention;
-//   selected_kernel:   attention over the selected blocks, the group's heads stacked into the
-//                      matrix-core M dimension (section 6: heads of a GQA group share one
-//                      selection, so their queries form one tile against each block).
-// The gate mix is folded into the three output writes: cmp stores g0*o_cmp, window and
-// selected add g2*o_win and g1*o_slc.
+//   window_kernel:     sliding-window attention (when run as a stage of its own).
+// The selected-block branch is in selected.hip.  The gate mix is folded into the output
+// writes: cmp stores g0*o_cmp (+ g2*o_win when the window runs inside it), the window and
+// selected branches add g2*o_win and g1*o_slc.
 #include "attn_tile.h"
 #include "dev_common.h"
 #include "kernels.h"
@@ -557,228 +555,6 @@ __global__ __launch_bounds__(QTile<G>::NW * 64) void window_kernel(PrefillArgs a
 
 // ------------------------------------------------------------------ selected blocks
 
-// One wave per (position, KV group), eight consecutive positions of one group per workgroup:
-// the group's heads form the 16 MFMA rows.  The forced blocks (block 0 and the local blocks,
-// one 64-key tile each at the benchmark geometry) are common to the eight positions, so up to
-// three of their tiles are staged in LDS once per workgroup; every other selected tile is
-// gathered straight from global memory (16-byte loads), the next tile's K and V in flight
-// while the current one computes.  A wave's tiles (in index-list order) are listed once, lane
-// e holding the first key of tile e or -1 (padding, a block outside [0, nblk), a tile past t);
-// tiles it shares with the workgroup are taken from LDS (as often as they occur), the rest
-// are visited in order through the ballot mask.
-// Workgroups are dealt to the 8 XCDs round-robin; the linear index is remapped so that XCD x
-// runs a contiguous 1/8 of the (sequence, group, position) range: the waves that share an
-// XCD's L2 then read the same group's K/V at nearby positions.
-constexpr int kSelWaves = 8;   // positions per workgroup
-constexpr int kSelShared = 3;  // tiles staged in LDS per workgroup
-
-template <int D, int G>
-__global__ __launch_bounds__(kSelWaves * 64, 1) void selected_kernel(PrefillArgs a) {
-  constexpr int DT = D / 16, NK = D / 8, NV = D / 8, NT = kSelWaves * 64;
-  __shared__ __align__(16) u16 Ksh[kSelShared][64][D];
-  __shared__ __align__(16) u16 Vsh[kSelShared][D][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g4 = lane >> 4, r16 = lane & 15;
-  const int ntb = (a.nq + kSelWaves - 1) / kSelWaves;
-  const int per_xcd = gridDim.x / 8;  // the grid is padded to a multiple of 8
-  const int w = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  const int stream = w / ntb;
-  if (stream >= a.B * a.Hkv) return;  // uniform
-  const int t0 = a.q0 + (w % ntb) * kSelWaves;
-  const int t = t0 + wave;
-  const bool act = t < a.T;
-  const int kvh = stream % a.Hkv, b = stream / a.Hkv;
-  const long bkv = (long)b * a.Hkv + kvh;
-  const int Hq = a.Hkv * G;
-  const bool hlive = r16 < G;
-  const int head = kvh * G + (hlive ? r16 : 0);
-  const float sl = a.scale_log2;
-  const u16* kb = a.k + bkv * (long)a.ldk * D;
-  const u16* vtb = a.vt + bkv * (long)D * a.TP;
-
-  // The workgroup's shared tiles: tiles of the current block up to t0, of the other local
-  // blocks, then block 0's first tile (uniform; t0 .. t0+7 share one block since the block
-  // size is a multiple of 64 and t0 of 8).
-  int sh[kSelShared];
-  int nsh = 0;
-  {
-    const int bcur = t0 / a.beta, per = a.beta >> 6;
-    for (int f = bcur; f >= 0 && f > bcur - a.n_local && nsh < kSelShared; --f)
-      for (int u = 0; u < per && nsh < kSelShared; ++u)
-        if (f * a.beta + 64 * u <= t0) sh[nsh++] = f * a.beta + 64 * u;
-    if (nsh < kSelShared && bcur - a.n_local >= 0) sh[nsh++] = 0;
-  }
-
-  int my_key0 = -1;
-  if (act) {
-    const int per = a.beta >> 6;
-    const int32_t* irow = a.idx + (prow(a, b, t) * a.Hkv + kvh) * a.top_n;
-    if (lane < a.top_n * per) {
-      const int j = irow[lane / per];
-      const int k0 = j * a.beta + 64 * (lane % per);
-      if (j >= 0 && j < a.nblk && k0 <= t) my_key0 = k0;
-    }
-  }
-  uint64_t todo = __ballot(my_key0 >= 0);  // wave-uniform: gathered tiles still to visit
-  int shcnt[kSelShared];
-#pragma unroll
-  for (int i = 0; i < kSelShared; ++i) {
-    const uint64_t m = i < nsh ? __ballot(my_key0 == sh[i]) : 0ull;
-    shcnt[i] = (int)__popcll(m);
-    todo &= ~m;
-  }
-  const int ntile = (int)__popcll(todo);
-
-  bf16x8 qf[D / 32];
-  {
-    const u16* qp = a.q + (prow(a, b, act ? t : a.q0) * Hq + head) * D;
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) qf[c] = hlive ? load8(qp + 32 * c + 8 * g4) : zero8();
-  }
-  const int tmax = a.T - 1;
-  u32x4 kr[NK], vr[NV];
-  auto load_k = [&](int k0) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      int row = k0 + 32 * (q >> 1) + perm_key(r16, q & 1);
-      row = row < tmax ? row : tmax;
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c)
-        kr[q * (D / 32) + c] =
-            *reinterpret_cast<const u32x4*>(kb + ((uint32_t)row * D + 8 * g4 + 32 * c));
-    }
-  };
-  auto load_v = [&](int k0) {
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int n = 0; n < DT; ++n)
-        vr[kc * DT + n] = *reinterpret_cast<const u32x4*>(
-            vtb + ((uint32_t)(16 * n + r16) * a.TP + k0 + 32 * kc + 8 * g4));
-  };
-  for (int i = 0; i < nsh; ++i) {  // uniform
-    KTileRegs<D, NT> sk;
-    VTileRegs<D, NT> sv;
-    sk.load(kb, sh[i], tmax);
-    sv.load(vtb, a.TP, sh[i]);
-    sk.store(Ksh[i]);
-    sv.store(Vsh[i]);
-  }
-  __syncthreads();
-  if (!act) return;  // after the workgroup's only barrier
-  // the first gathered tile's K is in flight while the shared tiles compute (its V follows:
-  // both at once would not fit the register budget)
-  int key0 = 0;
-  if (ntile > 0) {
-    key0 = __builtin_amdgcn_readlane(my_key0, __builtin_ctzll(todo));
-    todo &= todo - 1;
-  }
-  load_k(key0);
-
-  float mrun = kNegInf, lrun = 0.f;
-  f32x4 O[DT];
-#pragma unroll
-  for (int n = 0; n < DT; ++n) O[n] = zero4();
-  // masking, online softmax and the rescale of O; returns P^T fragments for the P V product
-  auto softmax_step = [&](float* z, int k0, bf16x8* pb) {
-    if (k0 + 63 > t) {  // the diagonal tile (uniform branch)
-      __asm__ volatile("" ::: "memory");
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = k0 + 32 * (q >> 1) + 8 * g4 + 4 * (q & 1) + e;
-          z[q * 4 + e] = key <= t ? z[q * 4 + e] : kNegInf;
-        }
-    }
-    float tm = z[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) tm = fmaxf(tm, z[e]);
-    tm = col_max4(tm);  // finite: every tile used holds a key <= t
-    const bool move = tm * sl > mrun * sl + kLazyLog2;
-    if (__ballot(move) != 0) {  // uniform: lazy rescale
-      const float mn = move ? tm : mrun;
-      const float alpha = move ? fast_exp2((mrun - mn) * sl) : 1.f;
-      mrun = mn;
-      lrun *= alpha;
-#pragma unroll
-      for (int n = 0; n < DT; ++n) O[n] *= alpha;
-    }
-    const float msl = mrun * sl;
-    float sum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float p = fast_exp2(fmaf(z[e], sl, -msl));
-      sum += p;
-      pb[e >> 3][e & 7] = (__bf16)p;
-    }
-    lrun += sum;
-  };
-
-  // shared tiles, from LDS
-  for (int i = 0; i < nsh; ++i)
-    for (int c = 0; c < shcnt[i]; ++c) {
-      float z[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 acc = score_subtile<D>(Ksh[i], qf, q >> 1, q & 1, g4, r16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) z[q * 4 + e] = acc[e];
-      }
-      bf16x8 pb[2];
-      softmax_step(z, sh[i], pb);
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) pv_chunk<D>(Vsh[i], pb[kc], kc, g4, r16, O);
-    }
-
-  load_v(key0);
-
-  // gathered tiles
-  for (int it = 0; it < ntile; ++it) {
-    // the last tile re-fetches itself: unconditional loads keep the wait counts exact (a load
-    // under a branch makes the join wait for every load in flight)
-    const int knext = todo ? __builtin_amdgcn_readlane(my_key0, __builtin_ctzll(todo)) : key0;
-    todo &= todo - 1;
-    float z[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c)
-        acc = mfma16x16x32(__builtin_bit_cast(bf16x8, kr[q * (D / 32) + c]), qf[c], acc);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) z[q * 4 + e] = acc[e];
-    }
-    load_k(knext);
-    bf16x8 pb[2];
-    softmax_step(z, key0, pb);
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int n = 0; n < DT; ++n)
-        O[n] = mfma16x16x32(__builtin_bit_cast(bf16x8, vr[kc * DT + n]), pb[kc], O[n]);
-    load_v(knext);
-    key0 = knext;
-  }
-
-  const float L = col_sum4(lrun);
-  if (hlive) {
-    const long rowoff = prow(a, b, t) * Hq + head;
-    const float gs = L > 0.f ? a.gate[rowoff * 3 + 1] / L : 0.f;
-    float* op = a.out + rowoff * D;
-#pragma unroll
-    for (int n = 0; n < DT; ++n) {
-      float4* dst = reinterpret_cast<float4*>(op + 16 * n + 4 * g4);
-      float4 v = *dst;
-      v.x += gs * O[n][0];
-      v.y += gs * O[n][1];
-      v.z += gs * O[n][2];
-      v.w += gs * O[n][3];
-      *dst = v;
-    }
-  }
-}
-
 // ------------------------------------------------------------------ launchers
 
 template <int G>
@@ -812,11 +588,8 @@ static void launch_prefill_all(const PrefillArgs& a, int which, hipStream_t s) {
       cmp_select_kernel<D, G, true><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, lds, s>>>(a);
     else
       cmp_select_kernel<D, G, false><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, lds, s>>>(a);
-  } else if (which == 1) {
-    window_kernel<D, G><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, 0, s>>>(a);
   } else {
-    const long nwg = (long)((a.nq + kSelWaves - 1) / kSelWaves) * a.Hkv * a.B;
-    selected_kernel<D, G><<<dim3((unsigned)((nwg + 7) / 8 * 8)), kSelWaves * 64, 0, s>>>(a);
+    window_kernel<D, G><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, 0, s>>>(a);
   }
 }
 
@@ -838,6 +611,5 @@ static void dispatch(const PrefillArgs& a, int which, hipStream_t s) {
 
 void launch_cmp_select(const PrefillArgs& a, hipStream_t s) { dispatch(a, 0, s); }
 void launch_window(const PrefillArgs& a, hipStream_t s) { dispatch(a, 1, s); }
-void launch_selected(const PrefillArgs& a, hipStream_t s) { dispatch(a, 2, s); }
 
 }  // namespace nsa

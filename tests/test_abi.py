@@ -85,8 +85,11 @@ def test_null_config_and_status_strings(lib):
 def test_workspace_sizes_are_plausible(lib):
     c = cfgB()
     ws = lib.nsa_prefill_workspace_bytes(ctypes.byref(c.c()))
-    # transposed V (64 MiB) + compressed caches + weights + indices, well under 1 GiB
-    assert 64 << 20 < ws < 1 << 30
+    # the selected branch's block-major partials, one per (row, group, slot): 16 heads x D fp16
+    # outputs + 16 x 4 fp32 statistics; besides them transposed V (64 MiB), compressed caches,
+    # weights, indices and the entry lists, well under 1 GiB
+    partials = c.B * c.T * c.Hkv * c.top_n * (c.sel_block // 64) * (16 * c.D * 2 + 16 * 16)
+    assert partials + (64 << 20) < ws < partials + (1 << 30)
     assert lib.nsa_num_compressed(65536, 32, 16) == 4095
     assert lib.nsa_num_compressed(31, 32, 16) == 0
     assert lib.nsa_num_compressed_tiles(65536, 32, 16) == 64

@@ -135,7 +135,7 @@ MobaPlan plan_moba(const moba_config* c) {
   p.list = off;   off += align_up(entries * 4 + 4);
   // one spare slot each: the merge loads slot 0 unconditionally, also when top_k = 0
   p.po = off;     off += align_up((entries + 1) * c->D * 2);  // fp16
-  p.pml = off;    off += align_up((entries + 1) * 2 * 4);
+  p.pml = off;    off += align_up((entries + 1) * 4 * 4);
   p.total = off;
   return p;
 }

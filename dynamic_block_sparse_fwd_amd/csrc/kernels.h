@@ -144,8 +144,8 @@ struct MobaArgs {
   int32_t* ntiles;     // [1] total tiles
   int32_t* tile_entry; // [max_tiles] the list each 128-row tile belongs to
   int32_t* list;       // [B*T*H*top_k] (t << 4 | slot)
-  _Float16* po;        // [B*T*H, top_k, D] partial outputs, normalised by their own sum (fp16)
-  float* pml;          // [B*T*H, top_k, 2] partial (max, sum), log2 units
+  _Float16* po;        // [B*T*H, top_k, D] partial outputs / (own sum * scale), fp16
+  float* pml;          // [B*T*H, top_k, 4] partial (max in log2 units, sum, scale, 0)
   int B, T, H, D, block, top_k, nb, max_tiles;
   float scale_log2;
 };

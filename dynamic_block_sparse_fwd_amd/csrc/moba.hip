@@ -467,22 +467,31 @@ __global__ __launch_bounds__(256) void moba_block_kernel(MobaArgs a) {
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
     const float L = col_sum4(lrun[rt]);
+    // stored normalised by the partial's own sum (a convex combination of value rows) and by
+    // the power of two at or above its largest magnitude, so fp16 keeps any bf16 value range
+    // (|v| up to 3e38, or far below fp16's normal range) at full relative precision
+    float mx = 0.f;
+#pragma unroll
+    for (int nn = 0; nn < DT; ++nn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) mx = fmaxf(mx, fabsf(O[rt][nn][q]));
+    const float inv = 1.0f / L;  // a chosen past block always has visible keys: L > 0
+    int ex = 0;
+    (void)frexpf(col_max4(mx) * inv, &ex);  // = f 2^ex, f in [0.5, 1); 0 gives ex = 0
+    ex = ex < -126 ? -126 : (ex > 127 ? 127 : ex);  // scale and 1 / scale both finite
+    const float w = inv * ldexpf(1.f, -ex);          // exact power-of-two factor
     if (rt_t[rt] >= 0) {
       const long slot = (((long)b * a.T + rt_t[rt]) * a.H + h) * a.top_k + rt_s[rt];
-      // stored normalised by the partial's own sum: a convex combination of value rows, well
-      // inside fp16's range whatever the headroom of the lazily rescaled sum
       _Float16* op = a.po + slot * D;
-      const float inv = 1.0f / L;  // a chosen past block always has visible keys: L > 0
 #pragma unroll
       for (int nn = 0; nn < DT; ++nn) {
-        const h16x4 v = {(_Float16)(O[rt][nn][0] * inv), (_Float16)(O[rt][nn][1] * inv),
-                         (_Float16)(O[rt][nn][2] * inv), (_Float16)(O[rt][nn][3] * inv)};
+        const h16x4 v = {(_Float16)(O[rt][nn][0] * w), (_Float16)(O[rt][nn][1] * w),
+                         (_Float16)(O[rt][nn][2] * w), (_Float16)(O[rt][nn][3] * w)};
         *reinterpret_cast<h16x4*>(op + 16 * nn + 4 * g4) = v;
       }
-      if (g4 == 0) {
-        a.pml[slot * 2 + 0] = mrun[rt] * a.scale_log2;
-        a.pml[slot * 2 + 1] = L;
-      }
+      if (g4 == 0)
+        *reinterpret_cast<f32x4*>(a.pml + slot * 4) =
+            f32x4{mrun[rt] * a.scale_log2, L, ldexpf(1.f, ex), 0.f};
     }
   }
 }
@@ -594,13 +603,15 @@ __global__ __launch_bounds__(256) void moba_own_kernel(MobaArgs a) {
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
     const long row = ((long)b * a.T + row_t[rt]) * a.H + h;
-    float pm[KS], pl[KS];
+    float pm[KS], pl[KS], ps[KS];
     float4 pv[KS][DT];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {  // every load unconditional (slot index clamped)
       const long slot = row * K + (s < slast ? s : slast);
-      pm[s] = a.pml[slot * 2];
-      pl[s] = a.pml[slot * 2 + 1];
+      const f32x4 st = *reinterpret_cast<const f32x4*>(a.pml + slot * 4);
+      pm[s] = st[0];
+      pl[s] = st[1];
+      ps[s] = st[2];
       const _Float16* op = a.po + slot * D;
 #pragma unroll
       for (int nn = 0; nn < DT; ++nn) {
@@ -621,15 +632,17 @@ __global__ __launch_bounds__(256) void moba_own_kernel(MobaArgs a) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const bool ok = s < nsel;
-      // the partials are normalised: weight = their sum relative to the common max
+      // the partials are normalised: weight = their sum relative to the common max (times the
+      // power-of-two scale of the stored outputs)
       const float f = ok ? pl[s] * fast_exp2(pm[s] - M) : 0.f;
+      const float fo = f * (ok ? ps[s] : 0.f);
       L += f;
 #pragma unroll
       for (int nn = 0; nn < DT; ++nn) {
-        acc[nn].x += ok ? f * pv[s][nn].x : 0.f;
-        acc[nn].y += ok ? f * pv[s][nn].y : 0.f;
-        acc[nn].z += ok ? f * pv[s][nn].z : 0.f;
-        acc[nn].w += ok ? f * pv[s][nn].w : 0.f;
+        acc[nn].x += ok ? fo * pv[s][nn].x : 0.f;
+        acc[nn].y += ok ? fo * pv[s][nn].y : 0.f;
+        acc[nn].z += ok ? fo * pv[s][nn].z : 0.f;
+        acc[nn].w += ok ? fo * pv[s][nn].w : 0.f;
       }
     }
     const float inv = 1.0f / L;

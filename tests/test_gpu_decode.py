@@ -100,6 +100,10 @@ DECODE_CASES = [
     ("topp1_G1_D64_block128", 2, 2500, 2, 1, 64, [2500, 1300],
      dict(top_p=1.0, sel_block=128, top_n=6, window=200)),
     ("topp_tiny_G16_D128", 3, 3000, 2, 16, 128, [3000, 1000, 40], dict(top_p=1e-6)),
+    # other compression geometries (the generic block-mass path)
+    ("cmp16x16_G4_D64", 2, 2100, 2, 4, 64, [2100, 1100], dict(cmp_len=16, cmp_stride=16)),
+    ("cmp48x16_G16_D128", 2, 2000, 1, 16, 128, [2000, 47], dict(cmp_len=48, cmp_stride=16)),
+    ("cmp64x32_G8_D128", 2, 3000, 2, 8, 128, [3000, 1500], dict(cmp_len=64, cmp_stride=32)),
 ]
 
 
@@ -108,9 +112,9 @@ DECODE_CASES = [
 def test_decode_parity(name, B, L, Hkv, G, D, seqlens, extra):
     print("case", name, flush=True)
     cfg = O.NsaCfg(B, L, Hkv, G, D, **extra)
-    x = S.nsa_decode_inputs(30 + len(name), B, L, Hkv, G, D)
-    kc = O.compress(x["kcache"], x["wk"], 32, 16)
-    vc = O.compress(x["vcache"], x["wv"], 32, 16)
+    x = S.nsa_decode_inputs(30 + len(name), B, L, Hkv, G, D, l=cfg.cmp_len)
+    kc = O.compress(x["kcache"], x["wk"], cfg.cmp_len, cfg.cmp_stride)
+    vc = O.compress(x["vcache"], x["wv"], cfg.cmp_len, cfg.cmp_stride)
     check_decode(cfg, x, kc, vc, seqlens, name, repeat=True)
 
 

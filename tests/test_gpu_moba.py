@@ -106,3 +106,25 @@ def test_moba_1m_sampled_rows():
                                      rng.choice(np.arange(2048, T - 64), 3072 - 2048 - 64,
                                                 replace=False)])).astype(np.int32)
     check_moba(cfg, x, np.zeros_like(rows), rows, gout, gidx, "moba 1M")
+
+
+def scaled_bits(bits, e):
+    """bf16 bit patterns times 2**e, exactly (a power of two moves only the exponent, which
+    stays in range here)."""
+    f = S.bf16_bits_to_f32(bits).astype(np.float64) * (2.0 ** e)
+    return S.f32_to_bf16_bits(f.astype(np.float32))
+
+
+@pytest.mark.parametrize("e", [20, -20])
+def test_moba_value_range(e):
+    """Values far outside fp16's range (x 2^20: up to ~4e6) or deep below its normal range
+    (x 2^-20: ~1e-6): the partial outputs the block-major kernel stores in fp16 carry a
+    power-of-two scale, so the output equals 2^e times the unscaled oracle output."""
+    B, T, H, D, block, top_k = 1, 2048, 2, 128, 256, 3
+    cfg = O.MobaCfg(B, T, H, D, block=block, top_k=top_k)
+    x = S.moba_inputs(77, B, T, H, D)
+    xs = dict(x, v=scaled_bits(x["v"], e))
+    gout, gidx = gpu_moba(cfg, xs)
+    assert np.isfinite(gout).all()
+    rb, rt = np.zeros(T, np.int32), np.arange(T, dtype=np.int32)
+    check_moba(cfg, x, rb, rt, gout * (2.0 ** -e), gidx, "moba v x 2^%d" % e)

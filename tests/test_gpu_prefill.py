@@ -78,6 +78,11 @@ CASES = [
     ("topp1_G1_D64_nolocal", 2, 700, 2, 1, 64, dict(top_p=1.0, top_n=4, n_local=0, window=100)),
     # p below any forced mass: only block 0 and the local blocks are kept
     ("topp_tiny_G4_D128", 1, 1300, 2, 4, 128, dict(top_p=1e-6)),
+    # other compression geometries (the generic importance path): l = d, l = 3 d, and l = 2 d
+    # with a selection block of only two strides
+    ("cmp16x16_G4_D64", 1, 1500, 2, 4, 64, dict(cmp_len=16, cmp_stride=16)),
+    ("cmp48x16_G16_D128", 1, 1300, 1, 16, 128, dict(cmp_len=48, cmp_stride=16)),
+    ("cmp64x32_G8_D64", 1, 2100, 2, 8, 64, dict(cmp_len=64, cmp_stride=32)),
 ]
 
 
@@ -86,7 +91,7 @@ def test_prefill_parity_all_rows(name, B, T, Hkv, G, D, extra):
     print("case", name, flush=True)
     cfg = O.NsaCfg(B, T, Hkv, G, D, **extra)
     seed = 1 if name == CASES[0][0] else zlib.crc32(name.encode()) % 1000 + 10
-    x = S.nsa_prefill_inputs(seed, B, T, Hkv, G, D)
+    x = S.nsa_prefill_inputs(seed, B, T, Hkv, G, D, l=cfg.cmp_len)
     gout, gidx = run_gpu_prefill(cfg, x)
     rb, rt = all_rows(cfg)
     compare_prefill(cfg, x, rb, rt, gout, gidx, name)
@@ -225,3 +230,20 @@ def test_prefill_window_and_selected_stages_against_oracle():
     o_s2, _ = nsa.nsa_prefill_stages(c, nsa.STAGE_SELECTED, d["q"], d["k"], d["v"], None, None,
                                      d["gate"], sel_idx=to_dev(idx2))
     check_close(o_s2.cpu().numpy()[0], g[..., 1:2] * ora2["o_slc"], "selected stage, holes")
+
+
+@pytest.mark.parametrize("e", [20, -20])
+def test_prefill_value_range(e):
+    """Values far outside fp16's range (x 2^20) or deep below its normal range (x 2^-20): the
+    selected branch's block-major partials are stored in fp16 with a power-of-two scale per
+    head, so every branch (compression is linear and the scaling exact) and the output equal
+    2^e times the unscaled run, whose oracle output they are compared with."""
+    B, T, Hkv, G, D = 1, 2048, 2, 16, 128
+    cfg = O.NsaCfg(B, T, Hkv, G, D)
+    x = S.nsa_prefill_inputs(78, B, T, Hkv, G, D)
+    f = S.bf16_bits_to_f32(x["v"]).astype(np.float64) * (2.0 ** e)
+    xs = dict(x, v=S.f32_to_bf16_bits(f.astype(np.float32)))
+    gout, gidx = run_gpu_prefill(cfg, xs)
+    assert np.isfinite(gout).all()
+    rb, rt = all_rows(cfg)
+    compare_prefill(cfg, x, rb, rt, gout * (2.0 ** -e), gidx, "prefill v x 2^%d" % e)

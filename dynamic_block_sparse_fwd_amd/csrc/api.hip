@@ -197,18 +197,20 @@ void set_selected_ws(PrefillArgs& a, const PrefillPlan& p, char* base) {
 }
 
 struct BackwardPlan {
-  size_t kt, kc, kct, vc, wkt, wvt, dob, dot, qt, lse, dlt, pk, pv, dkc, dvc, total;
+  size_t kt, kc, kct, vc, wkt, wvt, dob, dot, qt, lse, dlt, pk, pv, dkc, dvc, psk, psv, total;
   int ncmp, NCP, TP, nblk, PC, NPC;
 };
 
 BackwardPlan plan_backward(const nsa_config* c) {
   BackwardPlan p{};
   const size_t BH = (size_t)c->B * c->Hkv, rows = (size_t)c->B * c->T * c->Hkv * c->G;
+  const size_t rows16 = (size_t)c->B * c->T * c->Hkv * 16;  // 16-row tiles per position
   p.ncmp = nsa_num_compressed(c->T, c->cmp_len, c->cmp_stride);
   p.NCP = round64(p.ncmp);
   p.TP = round64(c->T);
   p.nblk = (c->T + c->sel_block - 1) / c->sel_block;
-  // positions per chunk of the compressed key pass: about 16 chunks, at least 256 positions
+  // positions per chunk of the compressed and selected key passes: about 16 chunks, at least
+  // 256 positions
   p.PC = std::max(256, round64((c->T + 15) / 16));
   p.NPC = (c->T + p.PC - 1) / p.PC;
   const size_t cmpn = BH * (size_t)std::max(p.NCP, 64) * c->D;
@@ -220,14 +222,16 @@ BackwardPlan plan_backward(const nsa_config* c) {
   p.wkt = off; off += align_up((size_t)c->cmp_len * c->D * c->D * 2);
   p.wvt = off; off += align_up((size_t)c->cmp_len * c->D * c->D * 2);
   p.dob = off; off += align_up(rows * c->D * 2);
-  p.dot = off; off += align_up(rows * c->D * 2);
-  p.qt = off;  off += align_up(rows * c->D * 2);
+  p.dot = off; off += align_up(rows16 * c->D * 2);
+  p.qt = off;  off += align_up(rows16 * c->D * 2);
   p.lse = off; off += align_up(3 * rows * 4);
   p.dlt = off; off += align_up(3 * rows * 4);
   p.pk = off;  off += align_up((size_t)p.NPC * cmpn * 4);
   p.pv = off;  off += align_up((size_t)p.NPC * cmpn * 4);
   p.dkc = off; off += align_up(cmpn * 4);
   p.dvc = off; off += align_up(cmpn * 4);
+  p.psk = off; off += align_up((size_t)p.NPC * BH * c->T * c->D * 4);
+  p.psv = off; off += align_up((size_t)p.NPC * BH * c->T * c->D * 4);
   p.total = off;
   return p;
 }
@@ -566,13 +570,7 @@ int nsa_cache_append(const nsa_config* c, int32_t C, const void* k_new, const vo
   return hip_status();
 }
 
-// The backward runs a position's 16 heads as one matrix-core tile.
-static int check_nsa_backward(const nsa_config* c) {
-  int st = check_nsa(c);
-  if (st != NSA_OK) return st;
-  if (c->G != 16) return NSA_ERR_UNSUPPORTED;
-  return NSA_OK;
-}
+static int check_nsa_backward(const nsa_config* c) { return check_nsa(c); }
 
 size_t nsa_backward_workspace_bytes(const nsa_config* cfg) {
   if (check_nsa_backward(cfg) != NSA_OK) return 0;
@@ -609,9 +607,10 @@ static int backward_impl(const nsa_config* c, const void* q, const void* k, cons
   a.kt = u16p(p.kt); a.kc = u16p(p.kc); a.kct = u16p(p.kct); a.vc = u16p(p.vc);
   a.dob = u16p(p.dob); a.dot = u16p(p.dot); a.qt = u16p(p.qt);
   a.lse = f32p(p.lse); a.dlt = f32p(p.dlt); a.pk = f32p(p.pk); a.pv = f32p(p.pv);
-  a.dkc = f32p(p.dkc); a.dvc = f32p(p.dvc);
+  a.dkc = f32p(p.dkc); a.dvc = f32p(p.dvc); a.psk = f32p(p.psk); a.psv = f32p(p.psv);
   a.dq = dq; a.dk = dk; a.dv = dv; a.dwk = dwk; a.dwv = dwv; a.dgate = dgate;
-  a.B = c->B; a.T = c->T; a.Hkv = c->Hkv; a.D = c->D; a.l = c->cmp_len; a.d = c->cmp_stride;
+  a.B = c->B; a.T = c->T; a.Hkv = c->Hkv; a.G = c->G; a.D = c->D;
+  a.l = c->cmp_len; a.d = c->cmp_stride;
   a.beta = c->sel_block; a.top_n = c->top_n; a.window = c->window;
   a.ncmp = p.ncmp; a.NCP = p.NCP; a.TP = p.TP; a.nblk = p.nblk; a.PC = p.PC; a.NPC = p.NPC;
   a.scale = c->scale;

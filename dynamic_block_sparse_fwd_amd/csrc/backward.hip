@@ -4,21 +4,25 @@
 // selection is an input: a discrete choice, it passes no gradient, and the bf16 rounding of a
 // compressed token passes the gradient unchanged.
 //
-// A position's 16 query heads (G = 16) form one 16-row matrix-core tile.  Per branch:
-//   bwd_q_kernel   query-major, one wave per position, one online pass over the branch's
+// A position's G query heads form one 16-row matrix-core tile (rows G .. 15 repeat head G - 1
+// with a zero gate and zero transposed operands, and write nothing).  Per branch:
+//   bwd_q_kernel / bwd_q_shared_kernel
+//                  query-major, one wave per position, one online pass over the branch's
 //                  64-key tiles: the log2-sum-exp2 of the scaled scores, <dO, o> and
 //                  dq += scale * dS K (dS taken against the running mean of dP', corrected as
-//                  the mean moves);
-//   bwd_kv_kernel  key-major, one workgroup per 64-key tile (a wave per 16 keys): over the
-//                  positions that see the tile, two positions (32 rows) per step,
-//                  dV += (g P)^T dO and dK += scale * dS^T q;
+//                  the mean moves); the compressed and window passes stage each key tile in
+//                  LDS once for 8 neighbouring positions;
+//   bwd_kv_kernel  key-major, one workgroup per 64- or 128-key tile (a wave per 16 keys): over
+//                  the positions that see the tile, two positions (32 rows) per step staged in
+//                  LDS, dV += (g P)^T dO and dK += scale * dS^T q;
 // the compressed branch's key gradients then go back through the compressor
 // (bwd_cmp_dx_kernel: dK, dV; bwd_cmp_dw_kernel: dWk, dWv).  No atomics: every output element
-// has one writer per launch, and launches that add to the same output run in order, except
-// the selected branch's key-major pass, whose position chunks add into dK, dV atomically.
-// Operands reach the matrix core straight from global memory (no LDS), in the layouts the
-// preparation kernel writes: dO in bf16, and q and dO with the 16 heads of a position
-// contiguous per feature (the B operand of the key-major products).
+// has one writer per launch and launches that add to the same output run in order.  The
+// compressed and selected key-major passes split the positions into chunks that write fp32
+// partials of their own; a reduction adds the chunks in chunk order, so two calls on the same
+// inputs give the same bits.  dO enters the matrix core in bf16; q and dO are also kept with
+// the 16 rows of a (position, group) contiguous per feature (the B operand of the key-major
+// products).
 #include "attn_tile.h"
 #include "kernels.h"
 
@@ -117,7 +121,8 @@ struct OnlineDq {
 
 }  // namespace
 
-// dO -> bf16 rows; q and dO with the 16 heads of a (position, group) contiguous per feature.
+// dO -> bf16 rows; q and dO with the G heads of a (position, group) contiguous per feature,
+// zero in the 16 - G pad rows.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   const long e = (long)blockIdx.x * 256 + threadIdx.x;
   const long n = (long)a.B * a.T * a.Hkv * a.D;
@@ -125,14 +130,18 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   const int D = a.D;
   const int dd = (int)(e % D);
   const long r = e / D;  // (b, t, g)
-  const long row0 = r * 16;  // first head row of [B, T, Hq] (Hq = 16 Hkv)
+  const int G = a.G;
+  const long row0 = r * G;  // first head row of [B, T, Hq] (Hq = G Hkv)
   u16 qh[16], dh[16];
 #pragma unroll
   for (int h = 0; h < 16; ++h) {
-    const float dv = a.dout[(row0 + h) * D + dd];
-    dh[h] = f32_to_bf16(dv);
-    qh[h] = a.q[(row0 + h) * D + dd];
-    a.dob[(row0 + h) * D + dd] = dh[h];
+    dh[h] = 0;
+    qh[h] = 0;
+    if (h < G) {
+      dh[h] = f32_to_bf16(a.dout[(row0 + h) * D + dd]);
+      qh[h] = a.q[(row0 + h) * D + dd];
+      a.dob[(row0 + h) * D + dd] = dh[h];
+    }
   }
   u16* dt = a.dot + (r * D + dd) * 16;
   u16* qt = a.qt + (r * D + dd) * 16;
@@ -157,10 +166,10 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdArgs a) {
   const int g4 = lane >> 4, r16 = lane & 15;
   const int t = blockIdx.x * 4 + wave, g = blockIdx.y, b = blockIdx.z;
   if (t >= a.T) return;  // uniform per wave; no barrier in this kernel
-  const int Hq = a.Hkv * 16;
+  const int Hq = a.Hkv * a.G;
   const long bg = (long)b * a.Hkv + g;
-  const long rowq = ((long)b * a.T + t) * Hq + g * 16;  // head 0 of this position and group
-  const long myrow = rowq + r16;
+  const bool head = r16 < a.G;  // rows G .. 15 repeat head G - 1 and write nothing
+  const long myrow = ((long)b * a.T + t) * Hq + g * a.G + (head ? r16 : a.G - 1);
   bf16x8 qf[DC], df[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
@@ -243,7 +252,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdArgs a) {
   const bool any = st.lsum > 0.f;
   const float lse2 = any ? st.m + __log2f(st.lsum) : kInf;  // no key: every p is 0
   const float dl = any ? st.c : 0.f;
-  if (g4 == 0) {
+  if (g4 == 0 && head) {
     const long o = (long)BR * a.B * a.T * Hq + myrow;
     a.lse[o] = lse2;
     a.dlt[o] = dl;
@@ -253,6 +262,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(BwdArgs a) {
   f32x4 dq[DT];
 #pragma unroll
   for (int n = 0; n < DT; ++n) dq[n] = Z[n] * f;
+  if (!head) return;
   // lane holds dq^T[feature 16 n + 4 g4 + i][head r16]
   float* dqp = a.dq + myrow * D;
 #pragma unroll
@@ -286,9 +296,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_shared_kernel(BwdArgs a) {
   const bool live = t < a.T;  // dead waves still pass the barriers
   const int tq = live ? t : a.T - 1;
   const int tlastw = tfirst + NW - 1 < a.T - 1 ? tfirst + NW - 1 : a.T - 1;
-  const int Hq = a.Hkv * 16;
+  const int Hq = a.Hkv * a.G;
   const long bg = (long)b * a.Hkv + g;
-  const long myrow = ((long)b * a.T + tq) * Hq + g * 16 + r16;
+  const bool head = r16 < a.G;  // rows G .. 15 repeat head G - 1 and write nothing
+  const long myrow = ((long)b * a.T + tq) * Hq + g * a.G + (head ? r16 : a.G - 1);
   bf16x8 qf[DC], df[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
@@ -379,7 +390,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_shared_kernel(BwdArgs a) {
   const bool any = st.lsum > 0.f;
   const float lse2 = any ? st.m + __log2f(st.lsum) : kInf;
   const float dl = any ? st.c : 0.f;
-  if (live && g4 == 0) {
+  if (live && head && g4 == 0) {
     const long o = (long)BR * a.B * a.T * Hq + myrow;
     a.lse[o] = lse2;
     a.dlt[o] = dl;
@@ -389,7 +400,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_shared_kernel(BwdArgs a) {
   f32x4 dq[DT];
 #pragma unroll
   for (int n = 0; n < DT; ++n) dq[n] = Z[n] * f;
-  if (!live) return;
+  if (!live || !head) return;
   float* dqp = a.dq + myrow * D;
 #pragma unroll
   for (int n = 0; n < DT; ++n) {
@@ -437,7 +448,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(BwdArgs a) {
   const int kb = blockIdx.x * 16 * NW;
   const long bg = blockIdx.y;
   const int b = (int)(bg / a.Hkv), g = (int)(bg % a.Hkv);
-  const int Hq = a.Hkv * 16;
+  const int Hq = a.Hkv * a.G;
   const float sl = a.scale_log2;
   const u16* krows;
   const u16* vrows;
@@ -463,7 +474,6 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(BwdArgs a) {
   f32x4 dK[DT], dV[DT];
 #pragma unroll
   for (int n = 0; n < DT; ++n) { dK[n] = zero4(); dV[n] = zero4(); }
-  int seen = 0;  // selected branch: positions gathered by this workgroup (uniform)
   const long bto = (long)BR * a.B * a.T * Hq;
 
   // global -> registers for the pair (ta, tb); tb < 0: rows 16-31 repeat ta's (masked later)
@@ -479,7 +489,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(BwdArgs a) {
       if (region < 2) {
         const int row = w / (D / 8), ch = w % (D / 8);
         const int pos = row < 16 ? ta : tb2;
-        const long qrow = ((long)b * a.T + pos) * Hq + g * 16 + (row & 15);
+        const int h = (row & 15) < a.G ? (row & 15) : a.G - 1;
+        const long qrow = ((long)b * a.T + pos) * Hq + g * a.G + h;
         src = (region == 0 ? a.q : a.dob) + qrow * D + 8 * ch;
       } else {
         const int f = w / 4, part = w % 4;
@@ -492,8 +503,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(BwdArgs a) {
     if (tid < 96) {
       const int kind = tid / 32, row = tid % 32;
       const int pos = row < 16 ? ta : tb2;
-      const long hrow = ((long)b * a.T + pos) * Hq + g * 16 + (row & 15);
-      pst = kind == 0 ? a.lse[bto + hrow] : kind == 1 ? a.dlt[bto + hrow] : a.gate[hrow * 3 + BR];
+      const bool hd = (row & 15) < a.G;  // pad rows: a zero gate cancels every term
+      const long hrow = ((long)b * a.T + pos) * Hq + g * a.G + (hd ? (row & 15) : a.G - 1);
+      pst = kind == 0 ? a.lse[bto + hrow] : kind == 1 ? a.dlt[bto + hrow]
+                      : hd ? a.gate[hrow * 3 + BR] : 0.f;
     }
   };
   auto stash = [&]() {
@@ -604,6 +617,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(BwdArgs a) {
     const int jb = kb / a.beta;
     const int c_lo = (int)blockIdx.z * a.PC > kb ? (int)blockIdx.z * a.PC : kb;
     const int c_hi = ((int)blockIdx.z + 1) * a.PC < a.T ? ((int)blockIdx.z + 1) * a.PC : a.T;
+    if (c_lo >= c_hi) return;  // uniform: no position of this chunk sees the tile
     for (int c0 = c_lo; c0 < c_hi; c0 += 256) {
       const int t = c0 + tid;
       bool sel = false;
@@ -626,13 +640,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(BwdArgs a) {
         x = plist[2 * e];
         y = 2 * e + 1 < tot ? plist[2 * e + 1] : -1;
       });
-      seen += tot;
       __syncthreads();  // plist and wcount are rewritten by the next round
     }
   }
 
-  if constexpr (BR == kBrSlc)
-    if (seen == 0) return;  // uniform: nothing to add
   // lane holds dK[key kb + 16 wave + 4 g4 + i][feature 16 n + r16]
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -647,20 +658,35 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(BwdArgs a) {
       }
     } else {
       if (key >= a.T) continue;
-      const long o = (bg * a.T + key) * D;
+      // selected: the chunk's own partial (every chunk that reaches the tile writes one, zero
+      // when none of its positions chose the block)
+      const long o = BR == kBrSlc ? (((long)blockIdx.z * a.B * a.Hkv + bg) * a.T + key) * D
+                                  : (bg * a.T + key) * D;
+      float* dk = BR == kBrSlc ? a.psk : a.dk;
+      float* dv = BR == kBrSlc ? a.psv : a.dv;
 #pragma unroll
       for (int n = 0; n < DT; ++n) {
-        const float kv = a.scale * dK[n][i], vv = dV[n][i];
-        if constexpr (BR == kBrSlc) {  // position chunks of one tile add concurrently
-          unsafeAtomicAdd(a.dk + o + 16 * n + r16, kv);
-          unsafeAtomicAdd(a.dv + o + 16 * n + r16, vv);
-        } else {
-          a.dk[o + 16 * n + r16] = kv;
-          a.dv[o + 16 * n + r16] = vv;
-        }
+        dk[o + 16 * n + r16] = a.scale * dK[n][i];
+        dv[o + 16 * n + r16] = dV[n][i];
       }
     }
   }
+}
+
+// dK, dV += the selected branch's position-chunk partials, in chunk order from the first chunk
+// that reaches the key's 64-key tile (the chunks that wrote one).
+__global__ __launch_bounds__(256) void bwd_slc_reduce_kernel(BwdArgs a) {
+  const long n = (long)a.B * a.Hkv * a.T * a.D;
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  const int key = (int)((e / a.D) % a.T);
+  float sk = 0.f, sv = 0.f;
+  for (int z = (key & ~63) / a.PC; z < a.NPC; ++z) {
+    sk += a.psk[(long)z * n + e];
+    sv += a.psv[(long)z * n + e];
+  }
+  a.dk[e] += sk;
+  a.dv[e] += sv;
 }
 
 // dKc, dVc = sum of the position-chunk partials (chunk order).
@@ -811,6 +837,8 @@ static void launch_bwd_d(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) {
   const int nkt = (a.T + 63) / 64;
   bwd_kv_kernel<D, kBrWin, 8><<<dim3((a.T + 127) / 128, a.B * a.Hkv, 1), 512, 0, s>>>(a);
   bwd_kv_kernel<D, kBrSlc, 4><<<dim3(nkt, a.B * a.Hkv, a.NPC), 256, 0, s>>>(a);
+  const long nk = (long)a.B * a.Hkv * a.T * D;
+  bwd_slc_reduce_kernel<<<(unsigned)((nk + 255) / 256), 256, 0, s>>>(a);
   if (a.ncmp > 0)
     bwd_kv_kernel<D, kBrCmp, 8><<<dim3((a.NCP + 127) / 128, a.B * a.Hkv, a.NPC), 512, 0, s>>>(a);
   mark(4);

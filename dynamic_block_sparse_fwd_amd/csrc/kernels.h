@@ -103,7 +103,8 @@ struct BwdArgs {
   const uint16_t* kct;    // [B*Hkv, D, NCP] compressed keys, transposed
   const uint16_t* vc;     // [B*Hkv, NCP, D] compressed values
   uint16_t* dob;          // [B, T, Hq, D] dout in bf16
-  uint16_t* dot;          // [B, T, Hkv, D, 16] dout, the 16 heads contiguous per feature
+  uint16_t* dot;          // [B, T, Hkv, D, 16] dout, the G heads contiguous per feature, then
+                          // 16 - G zeros
   uint16_t* qt;           // [B, T, Hkv, D, 16] q, the same
   float* lse;             // [3, B, T, Hq] per branch: log2-sum-exp2 of the scaled scores
   float* dlt;             // [3, B, T, Hq] per branch: <dout, o_branch>
@@ -111,6 +112,8 @@ struct BwdArgs {
   float* pv;              // [NPC, B*Hkv, NCP, D] compressed-value gradient, the same
   float* dkc;             // [B*Hkv, NCP, D]
   float* dvc;             // [B*Hkv, NCP, D]
+  float* psk;             // [NPC, B*Hkv, T, D] selected-branch key gradient, per position chunk
+  float* psv;             // [NPC, B*Hkv, T, D] selected-branch value gradient, the same
   // outputs
   float* dq;              // [B, T, Hq, D]
   float* dk;              // [B, Hkv, T, D]
@@ -118,8 +121,8 @@ struct BwdArgs {
   float* dwk;             // [l, D, D]
   float* dwv;             // [l, D, D]
   float* dgate;           // [B, T, Hq, 3]
-  int B, T, Hkv, D, l, d, beta, top_n, window;
-  int ncmp, NCP, TP, nblk, PC, NPC;  // PC positions per chunk of the compressed key pass
+  int B, T, Hkv, G, D, l, d, beta, top_n, window;
+  int ncmp, NCP, TP, nblk, PC, NPC;  // PC positions per chunk of the key-major passes
   float scale, scale_log2;
 };
 

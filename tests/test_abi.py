@@ -201,8 +201,10 @@ def test_backward_rejects_before_any_launch(lib):
     c = nsa.NsaConfig(1, 2048, 2, 16, 128).c()
     assert lib.nsa_backward_workspace_bytes(ctypes.byref(c)) > 0
     args = [fake] * 15
-    # G other than 16
-    bad = nsa.NsaConfig(1, 2048, 2, 8, 128).c()
+    # every group size the forward takes; an unsupported one is rejected
+    for G in (1, 2, 4, 8):
+        assert lib.nsa_backward_workspace_bytes(ctypes.byref(nsa.NsaConfig(1, 2048, 2, G, 64).c()))
+    bad = nsa.NsaConfig(1, 2048, 2, 3, 128).c()
     assert lib.nsa_backward_workspace_bytes(ctypes.byref(bad)) == 0
     assert lib.nsa_backward(ctypes.byref(bad), *args, 1 << 40, None) == nsa.NSA_ERR_UNSUPPORTED
     # a null input or output, a misaligned pointer, a small workspace

@@ -6,7 +6,7 @@ probabilities and the score gradients rounded to bf16) with fp32 accumulation.  
 alone gives every term of every gradient a relative error of up to 2^-9 (about 2e-3), and
 sums of such terms keep that relative size, so each gradient is held to an error relative to
 its own scale: mean |err| <= 4e-3 * mean |ref| (2^-8) and max |err| <= 1e-2 * max |ref|
-(per tensor)."""
+(per tensor).  Two calls on the same inputs must give the same bits (no atomics)."""
 import numpy as np
 import pytest
 
@@ -45,8 +45,13 @@ def check_grad(name, got, ref, what):
 
 
 CASES = [
-    # name, B, T, Hkv, D, extra
+    # name, B, T, Hkv, D, extra (G = 16 unless given)
     ("T700_Hkv2_D64", 1, 700, 2, 64, {}),
+    # smaller groups: rows G .. 15 of each 16-row tile are padding
+    ("G8_T650_Hkv2_D128", 1, 650, 2, 128, dict(G=8)),
+    ("G4_B2_T700_D64", 2, 700, 1, 64, dict(G=4, top_p=0.5)),
+    ("G1_T500_Hkv3_D64", 1, 500, 3, 64, dict(G=1)),
+    ("G2_T520_D128_block128", 1, 520, 2, 128, dict(G=2, sel_block=128, top_n=5, window=100)),
     ("B2_T530_D128", 2, 530, 1, 128, {}),
     ("block128_top6_win200_D64", 1, 900, 1, 64, dict(sel_block=128, top_n=6, window=200)),
     ("top5_local1_win100_D128", 1, 1100, 1, 128, dict(top_n=5, n_local=1, window=100)),
@@ -73,8 +78,8 @@ def test_backward_parity(name, B, T, Hkv, D, extra):
     import dynamic_block_sparse_fwd_amd as nsa
     nsa.load_library()
     print("case backward", name, flush=True)
-    G = 16
     extra = dict(extra)
+    G = extra.pop("G", 16)
     v_offset, q_scale = extra.pop("v_offset", 0.0), extra.pop("q_scale", 1.0)
     ocfg = O.NsaCfg(B, T, Hkv, G, D, **extra)
     x = S.nsa_prefill_inputs(91 + len(name), B, T, Hkv, G, D)
@@ -95,9 +100,12 @@ def test_backward_parity(name, B, T, Hkv, D, extra):
     cfg = nsa.NsaConfig(B, T, Hkv, G, D, ocfg.cmp_len, ocfg.cmp_stride, ocfg.sel_block,
                         ocfg.top_n, ocfg.n_local, ocfg.window, ocfg.scale)
     d = {k_: to_dev(v_) for k_, v_ in x.items()}
-    got = nsa.nsa_backward(cfg, d["q"], d["k"], d["v"], d["wk"], d["wv"], d["gate"], to_dev(idx),
-                           to_dev(dout))
+    args = (cfg, d["q"], d["k"], d["v"], d["wk"], d["wv"], d["gate"], to_dev(idx), to_dev(dout))
+    got = nsa.nsa_backward(*args)
+    again = nsa.nsa_backward(*args)  # deterministic: the same bits on a second call
     torch.cuda.synchronize()
+    for n in got:
+        assert torch.equal(got[n], again[n]), "%s: %s differs between two calls" % (name, n)
     msg = []
     for n in ("dq", "dk", "dv", "dwk", "dwv", "dgate"):
         mx, mean = check_grad(n, got[n].cpu().numpy(), ref[n], name)

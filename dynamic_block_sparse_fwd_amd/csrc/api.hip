@@ -17,7 +17,6 @@ namespace {
 
 
 constexpr size_t kAlign = 256;
-constexpr size_t kMaxDynLds = 64 * 1024;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int round64(int x) { return (x + 63) / 64 * 64; }
@@ -41,14 +40,21 @@ int check_nsa_base(const nsa_config* c) {
   return NSA_OK;
 }
 
-// Prefill keeps one query tile's block scores in LDS and lists a row's selected 64-key tiles
-// one per lane.
+// Prefill lists a row's selected 64-key tiles one per lane and counts the selected branch's
+// entries per 64-key tile in LDS (4 bytes per tile of the sequence, 64 KB at 2^20 tokens).  A
+// query tile's block scores stay in LDS while they fit; longer sequences select on the fly,
+// with the open block sums of the generic geometry in a ring of kCmpRing slots.
+constexpr int kCmpRing = 128;
+
 int check_nsa(const nsa_config* c) {
   int st = check_nsa_base(c);
   if (st != NSA_OK) return st;
+  if (c->T > (1 << 20)) return NSA_ERR_UNSUPPORTED;
   const long nblk = ((long)c->T + c->sel_block - 1) / c->sel_block;
-  if (nblk > 2048) return NSA_ERR_UNSUPPORTED;
-  if (cmp_select_lds_bytes(c->G, (int)nblk) > kMaxDynLds) return NSA_ERR_UNSUPPORTED;
+  const bool fast = c->sel_block == 4 * c->cmp_stride && c->cmp_len == 2 * c->cmp_stride;
+  if (cmp_select_streams(c->G, (int)nblk) && !fast &&
+      (64L * c->cmp_stride + 2L * c->cmp_len) / c->sel_block + 6 > kCmpRing)
+    return NSA_ERR_UNSUPPORTED;
   if (c->top_n * (c->sel_block / 64) > 64) return NSA_ERR_UNSUPPORTED;  // one tile per lane
   if ((long)((c->T + 3) / 4) * c->B * c->Hkv > (1L << 31) - 8) return NSA_ERR_UNSUPPORTED;
   // block-major selected branch: entries are (row << 6 | slot) in 32 bits, work tiles in a 1-D

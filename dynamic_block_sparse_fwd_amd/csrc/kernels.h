@@ -213,5 +213,7 @@ void launch_window(const PrefillArgs& a, hipStream_t s);
 void launch_selected(const PrefillArgs& a, hipStream_t s);
 
 size_t cmp_select_lds_bytes(int G, int nblk);
+// true when a query tile's block scores do not fit in LDS and the selection streams
+bool cmp_select_streams(int G, int nblk);
 
 }  // namespace nsa

@@ -55,7 +55,70 @@ __device__ __forceinline__ float head_sum(float v) {
   else return group_sum<G>(v);
 }
 
-template <int D, int G, bool FAST>
+// Shift a wave-wide 64-bit value up by one lane (lane e receives lane e - 1's; lane 0 its own).
+__device__ __forceinline__ uint64_t shfl_up1_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)v, 1);
+  const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(v >> 32), 1);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Streaming selection (sequences too long for a query tile's block scores to fit in LDS): a
+// block's group score is final once the key-tile walk has passed its last compressed token, and
+// is then offered at once to the position's running top list, kept sorted in LDS (list[e] =
+// the e-th best free block's rank key so far, 0 = empty); the forced blocks' total is summed in
+// block order for the top-p cut.  Called by a whole wave: block j in the lanes with `have`
+// (ascending with the lane), score s.  Rank keys are unique, so the final list is the same
+// set, in the same order, as a top-k over all scores at the end.
+__device__ __forceinline__ void stream_offer(const PrefillArgs& a, int t, uint64_t* list,
+                                             float* forced_sum, int j, bool have, float s,
+                                             int lane) {
+  const bool top_p = a.top_p > 0.f;
+  const int bcur = t / a.beta;
+  if (bcur + 1 <= a.top_n && !top_p) return;  // every visible block is chosen anyway
+  const int flo = bcur - a.n_local + 1 > 1 ? bcur - a.n_local + 1 : 1;
+  const int kfree = a.top_n - 1 - a.n_local;
+  if (top_p) {
+    uint64_t fm = __ballot(have && (j == 0 || (j >= flo && j <= bcur)));
+    if (fm != 0) {  // uniform
+      float f = *forced_sum;
+      while (fm != 0) {
+        const int src = (int)__builtin_ctzll(fm);
+        fm &= fm - 1;
+        f += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), src));
+      }
+      if (lane == 0) *forced_sum = f;
+    }
+  }
+  if (kfree <= 0) return;
+  const uint64_t key = have && j >= 1 && j < flo ? rank_key(s, j) : 0;
+  uint64_t mine = lane < kfree ? list[lane] : 0;
+  uint64_t thr = readlane_u64(mine, kfree - 1);
+  uint64_t pass = __ballot(key > thr);
+  if (pass == 0) return;  // uniform
+  while (pass != 0) {
+    const int src = (int)__builtin_ctzll(pass);
+    pass &= pass - 1;
+    const uint64_t x = readlane_u64(key, src);
+    if (x <= thr) continue;  // uniform: an earlier insertion raised the bar
+    const int pos = (int)__popcll(__ballot(lane < kfree && mine > x));
+    const uint64_t up = shfl_up1_u64(mine);
+    if (lane > pos && lane < kfree) mine = up;
+    if (lane == pos) mine = x;
+    thr = readlane_u64(mine, kfree - 1);
+  }
+  if (lane < kfree) list[lane] = mine;
+}
+
+// Ring of partially summed block scores (generic geometry, streaming selection): block j at
+// slot j mod kRing.
+constexpr int kRing = 128;
+
+template <int D, int G, bool FAST, bool STREAM>
 __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select_kernel(PrefillArgs a) {
   using QT = QTile<G>;
   constexpr int NT = QT::NW * 64, TQ = QT::TQ, RTW = QT::RTW, DT = D / 16;
@@ -65,7 +128,12 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
   __shared__ float Cb[FAST ? TQ : 1][16];   // fast path: block cores of the tile
   __shared__ float Hb[FAST ? TQ : 1][17];   // fast path: half-key carries into blocks 0..16
   __shared__ float Pc[TQ];                  // fast path: carry into the tile's first block
-  extern __shared__ float Sb[];             // [TQ][nblk] group block scores
+  // streaming selection: per position its running top list and forced total; generic path:
+  // the ring of open block sums
+  __shared__ uint64_t Lk[STREAM ? TQ : 1][64];
+  __shared__ float Fm[STREAM ? TQ : 1];
+  __shared__ float Sr[STREAM && !FAST ? TQ : 1][kRing];
+  extern __shared__ float Sb[];             // [TQ][nblk] group block scores (not streaming)
 
   const int tile = gridDim.x - 1 - blockIdx.x;  // longest rows first
   const int kvh = blockIdx.y, b = blockIdx.z;
@@ -91,8 +159,16 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
   const u16* kc = a.kc + bkv * (long)a.NCP * D;
   const u16* vct = a.vct + bkv * (long)D * a.NCP;
 
-  for (int e = threadIdx.x; e < TQ * nblk; e += NT) Sb[e] = 0.f;
+  if constexpr (STREAM) {
+    for (int e = threadIdx.x; e < TQ * 64; e += NT) Lk[e / 64][e % 64] = 0;
+    if constexpr (!FAST)
+      for (int e = threadIdx.x; e < TQ * kRing; e += NT) Sr[e / kRing][e % kRing] = 0.f;
+    if (threadIdx.x < TQ) Fm[threadIdx.x] = 0.f;
+  } else {
+    for (int e = threadIdx.x; e < TQ * nblk; e += NT) Sb[e] = 0.f;
+  }
   if (threadIdx.x < TQ) Pc[threadIdx.x] = 0.f;
+  int jemit = 0;  // streaming, generic path: blocks below jemit are final and offered
 
   // Pass 1: per-row max and sum of exp2 (per lane; merged over the row's four lanes below).
   float mrun[RTW], lrun[RTW];
@@ -331,7 +407,18 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
     }
     pv_tiles<D, RTW>(Vs, pbt, g4, r16, O);
     __syncthreads();
-    if constexpr (FAST) {
+    if constexpr (FAST && STREAM) {
+      // blocks 16*kt .. 16*kt + 15 are complete (core + carry, as below): offered per position
+      for (int tq = wave; tq < TQ; tq += QT::NW) {
+        if (t0 + tq >= a.T) break;  // uniform
+        const int j = 16 * kt + lane;
+        const bool have = lane < 16 && j < nblk;
+        float sv = 0.f;
+        if (have) sv = Cb[tq][lane] + (lane == 0 ? Pc[tq] : Hb[tq][lane]);
+        if (lane == 0) Pc[tq] = Hb[tq][16];
+        stream_offer(a, t0 + tq, Lk[tq], &Fm[tq], j, have, sv, lane);
+      }
+    } else if constexpr (FAST) {
       // blocks 16*kt .. 16*kt + 15 are complete: core + carry (the carry of the first block
       // comes from the previous tile)
       for (int pr = threadIdx.x; pr < TQ * 16; pr += NT) {
@@ -357,17 +444,59 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
         if (ilo < k0) ilo = k0;
         int ihi = (be - 1) / a.d;
         if (ihi > k0 + 63) ihi = k0 + 63;
-        float sv = Sb[tq * nblk + j];
+        float* slot = STREAM ? &Sr[tq][j & (kRing - 1)] : &Sb[tq * nblk + j];
+        float sv = *slot;
         for (int i = ilo; i <= ihi; ++i) {
           const int s0 = i * a.d, s1 = s0 + a.l;
           const int ov = (s1 < be ? s1 : be) - (s0 > bs ? s0 : bs);
           if (ov > 0) sv += Mb[tq][i - k0] * ((float)ov * inv_l);
         }
-        Sb[tq * nblk + j] = sv;
+        *slot = sv;
+      }
+      if constexpr (STREAM) {
+        // no later tile adds to the blocks below the next tile's first block: offer them and
+        // clear their slots
+        int jend = (int)(((long)(kt + 1) * 64 * a.d) / a.beta);
+        jend = jend < nblk ? jend : nblk;
+        __syncthreads();
+        for (int tq = wave; tq < TQ; tq += QT::NW) {
+          if (t0 + tq >= a.T) break;  // uniform
+          for (int j0 = jemit; j0 < jend; j0 += 64) {
+            const int j = j0 + lane;
+            const bool have = j < jend;
+            float sv = 0.f;
+            if (have) {
+              sv = Sr[tq][j & (kRing - 1)];
+              Sr[tq][j & (kRing - 1)] = 0.f;
+            }
+            stream_offer(a, t0 + tq, Lk[tq], &Fm[tq], j, have, sv, lane);
+          }
+        }
+        jemit = jend > jemit ? jend : jemit;
       }
     }
   }
-  if constexpr (FAST) {
+  if constexpr (STREAM) {
+    __syncthreads();
+    // the rest of the blocks up to the tile's last position's: the block after the last tile
+    // has only its carry (fast path) or the ring's sum (generic path), the ones after it
+    // nothing visible
+    const int jfirst = FAST ? 16 * nkt : jemit;
+    const int bmax = tlast / a.beta;
+    for (int tq = wave; tq < TQ; tq += QT::NW) {
+      if (t0 + tq >= a.T) break;  // uniform
+      for (int j0 = jfirst; j0 <= bmax; j0 += 64) {
+        const int j = j0 + lane;
+        const bool have = j <= bmax && j < nblk;
+        float sv = 0.f;
+        if (have) {
+          if constexpr (FAST) sv = (j == 16 * nkt && nkt > 0) ? 0.f + Pc[tq] : 0.f;
+          else sv = Sr[tq][j & (kRing - 1)];
+        }
+        stream_offer(a, t0 + tq, Lk[tq], &Fm[tq], j, have, sv, lane);
+      }
+    }
+  } else if constexpr (FAST) {
     __syncthreads();
     // the block after the last tile only has its carry
     if (threadIdx.x < TQ && t0 + (int)threadIdx.x < a.T && 16 * nkt < nblk && nkt > 0)
@@ -408,12 +537,21 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
     // forced: block 0 and the local blocks flo..bcur; free candidates 1 .. flo-1
     const int flo = bcur - a.n_local + 1 > 1 ? bcur - a.n_local + 1 : 1;
     const int kfree = a.top_n - 1 - a.n_local;
-    const float* srow = Sb + tq * nblk;
     // lane e < kfree receives the e-th winner among the free blocks (0 past the last one)
-    uint64_t key = wave_topk([&](int j) { return rank_key(srow[j], j); }, 1, flo, kfree, lane);
+    uint64_t key;
+    float forced = 0.f;
+    if constexpr (STREAM) {
+      key = lane < kfree ? Lk[tq][lane] : 0;
+      forced = Fm[tq];
+    } else {
+      const float* srow = Sb + tq * nblk;
+      key = wave_topk([&](int j) { return rank_key(srow[j], j); }, 1, flo, kfree, lane);
+      if (top_p) {
+        forced = srow[0];
+        for (int j = flo; j <= bcur; ++j) forced += srow[j];
+      }
+    }
     if (top_p) {
-      float forced = srow[0];
-      for (int j = flo; j <= bcur; ++j) forced += srow[j];
       const bool seen = t >= a.l - 1;  // a compressed token is visible: total importance G
       key = top_p_cut(key, kfree, forced, seen ? a.top_p * (float)a.G : 0.f, lane);
     }
@@ -572,22 +710,29 @@ size_t cmp_select_lds_bytes(int G, int nblk) {
   }
 }
 
+bool cmp_select_streams(int G, int nblk) { return cmp_select_lds_bytes(G, nblk) > 64 * 1024; }
+
 template <int D, int G>
 static void launch_prefill_all(const PrefillArgs& a, int which, hipStream_t s) {
   using QT = QTile<G>;
   const int ntile = (a.nq + QT::TQ - 1) / QT::TQ;
-  if (which == 0) {
+  const bool fast = a.beta == 4 * a.d && a.l == 2 * a.d;
+  if (which == 0 && cmp_select_streams(G, a.nblk)) {
+    const dim3 grid(ntile, a.Hkv, a.B);
+    if (fast) cmp_select_kernel<D, G, true, true><<<grid, QT::NW * 64, 0, s>>>(a);
+    else cmp_select_kernel<D, G, false, true><<<grid, QT::NW * 64, 0, s>>>(a);
+  } else if (which == 0) {
     const size_t lds = cmp_lds<G>(a.nblk);
-    const bool fast = a.beta == 4 * a.d && a.l == 2 * a.d;
     // opt in to the largest dynamic LDS any launch may use (64 KB, the validated limit); the
     // attribute is per device, so it is set on every launch rather than once per process
-    (void)hipFuncSetAttribute(fast ? reinterpret_cast<const void*>(&cmp_select_kernel<D, G, true>)
-                                   : reinterpret_cast<const void*>(&cmp_select_kernel<D, G, false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
+    (void)hipFuncSetAttribute(
+        fast ? reinterpret_cast<const void*>(&cmp_select_kernel<D, G, true, false>)
+             : reinterpret_cast<const void*>(&cmp_select_kernel<D, G, false, false>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024);
     if (fast)
-      cmp_select_kernel<D, G, true><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, lds, s>>>(a);
+      cmp_select_kernel<D, G, true, false><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, lds, s>>>(a);
     else
-      cmp_select_kernel<D, G, false><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, lds, s>>>(a);
+      cmp_select_kernel<D, G, false, false><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, lds, s>>>(a);
   } else {
     window_kernel<D, G><<<dim3(ntile, a.Hkv, a.B), QT::NW * 64, 0, s>>>(a);
   }

@@ -99,8 +99,11 @@ const char* nsa_status_string(int status);
 
 /* Host-only checks; no device is touched.  NSA_ERR_UNSUPPORTED when: D not 64/128;
  * G not in {1,2,4,8,16}; sel_block not a positive multiple of 64; top_n < 1 + n_local or
- * top_n > 64; T / sel_block > 2048 (prefill selection buffer); top_n * sel_block / 64 > 64
- * (prefill tiles of a row); cmp_len < cmp_stride. */
+ * top_n > 64; T > 2^20 (the prefill counts selected entries per 64-key tile in LDS);
+ * top_n * sel_block / 64 > 64 (prefill tiles of a row); cmp_len < cmp_stride; and, when a
+ * query tile's block scores outgrow LDS (the selection then streams) in a geometry other than
+ * sel_block = 4 cmp_stride, cmp_len = 2 cmp_stride: (64 cmp_stride + 2 cmp_len) / sel_block
+ * + 6 > 128. */
 int nsa_validate(const nsa_config* cfg);
 int moba_validate(const moba_config* cfg);
 

@@ -151,6 +151,60 @@ def test_prefill_chunks(name, B, L, Hkv, G, D, bounds, extra):
               "near-ties %d" % (name, P, E, mx, mean, acc), flush=True)
 
 
+def test_prefill_chunk_1m_tail():
+    """Chunked prefill at the largest capacity, 2^20 tokens (1 KV head x group 16, D = 128):
+    the last 2048 positions from full caches, 16384 selection blocks (the selection streams).
+    The compressed caches are the oracle's compression; queries and gates are drawn for the
+    chunk's positions only (the oracle reads the rows it is asked for).  Sampled rows against
+    the oracle, selection bit-exact under the near-tie rule."""
+    nsa = _nsa()
+    B, L, Hkv, G, D = 1, 1 << 20, 1, 16, 128
+    P, C = L - 2048, 2048
+    Hq = Hkv * G
+    print("case chunk 1M tail", flush=True)
+    cfg = nsa.NsaConfig(B, L, Hkv, G, D)
+    ocfg = O.NsaCfg(B, L, Hkv, G, D)
+    wstd = 1.0 / np.sqrt(32 * D)
+    k = S.normal_bf16(61, "k", (B, Hkv, L, D))
+    v = S.normal_bf16(61, "v", (B, Hkv, L, D))
+    wk = S.normal_bf16(61, "wk", (32, D, D), std=wstd)
+    wv = S.normal_bf16(61, "wv", (32, D, D), std=wstd)
+    qc = S.normal_bf16(61, "q", (B, C, Hq, D))
+    gc = S.gates(61, (B, C, Hq, 3))
+    kc = O.compress(k, wk, 32, 16)
+    vc = O.compress(v, wv, 32, 16)
+    n = kc.shape[2]
+    assert n == cfg.ncmp
+    nt = cfg.ncmp_tiles
+    vt = np.zeros((B, Hkv, nt * 64, D), dtype=np.uint16)
+    vt[:, :, :n] = vc
+    vt = np.ascontiguousarray(vt.reshape(B, Hkv, nt, 64, D).transpose(0, 1, 2, 4, 3))
+    out, idx = nsa.nsa_prefill_chunk(cfg, P, to_dev(qc), to_dev(k), to_dev(v), to_dev(kc),
+                                     to_dev(vt), to_dev(gc))
+    torch.cuda.synchronize()
+    out, idx = out.cpu().numpy(), idx.cpu().numpy()
+    q = np.zeros((B, L, Hq, D), dtype=np.uint16)
+    q[:, P:] = qc
+    gate = np.zeros((B, L, Hq, 3), dtype=np.float32)
+    gate[:, P:] = gc
+    rng = np.random.default_rng(61)
+    rt = np.unique(np.r_[np.arange(P, P + 32), rng.choice(np.arange(P, L), 96, replace=False),
+                         np.arange(L - 32, L)]).astype(np.int32)
+    rb = np.zeros_like(rt)
+    ora = O.nsa_prefill_rows(ocfg, q, k, v, kc, vc, gate, rb, rt, want_scores=True)
+    gi = idx[0, rt - P]
+    rerun, acc = check_nsa_idx(gi, ora, rt, ocfg.sel_block, ocfg.top_n, ocfg.n_local,
+                               ocfg.top_p)
+    ref = ora["out"].copy()
+    if rerun:
+        rr = np.array(rerun)
+        ref[rr] = O.nsa_prefill_rows(ocfg, q, k, v, kc, vc, gate, rb[rr], rt[rr],
+                                     idx_in=gi[rr])["out"]
+    mx, mean = check_close(out[0, rt - P], ref, "chunk 1M tail")
+    print("chunk 1M tail: %d rows, max-abs %.2e mean-abs %.2e near-ties %d" % (
+        len(rt), mx, mean, acc), flush=True)
+
+
 def test_generation_loop():
     """Chunked prefill of 1024 tokens for two sequences, then 24 decode steps in which each
     sequence appends its newest token and decodes it; the second sequence starts 40 tokens

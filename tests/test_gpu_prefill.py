@@ -166,6 +166,36 @@ def test_prefill_64k_sampled_rows():
     compare_prefill(cfg, x, np.zeros_like(rt), rt, gout, gidx, "prefill 64k")
 
 
+STREAM_CASES = [
+    # name, T, Hkv, G, D, extra: more selection blocks than a query tile's block scores can
+    # keep in LDS (64 KB / 4 bytes / positions per tile: 2048 blocks for G >= 4, 1024 for
+    # G = 1), so the selection streams
+    ("G16_T140000_D128", 140000, 1, 16, 128, {}),
+    ("G16_T140000_D64_topp0.5", 140000, 1, 16, 64, dict(top_p=0.5)),
+    ("G1_T70000_Hkv2_D64", 70000, 2, 1, 64, {}),
+    ("G4_T140000_cmp48x16_D64", 140000, 1, 4, 64, dict(cmp_len=48, cmp_stride=16)),
+    ("G8_T140000_cmp64x32_topp0.3", 140000, 1, 8, 128,
+     dict(cmp_len=64, cmp_stride=32, top_p=0.3)),
+]
+
+
+@pytest.mark.parametrize("name,T,Hkv,G,D,extra", STREAM_CASES, ids=[c[0] for c in STREAM_CASES])
+def test_prefill_streaming_selection(name, T, Hkv, G, D, extra):
+    """Long sequences: the top list of every position is built while the compressed keys are
+    walked; checked on the first 64 positions, the positions around block edges where the
+    forced set moves, a seeded random sample and the last 64."""
+    print("case stream", name, flush=True)
+    cfg = O.NsaCfg(1, T, Hkv, G, D, **extra)
+    x = S.nsa_prefill_inputs(50 + len(name), 1, T, Hkv, G, D, l=cfg.cmp_len)
+    gout, gidx = run_gpu_prefill(cfg, x)
+    rng = np.random.default_rng(len(name))
+    edges = np.array([1023, 1024, 1087, 4095, 4096, 65535, 65536, 65600, 131071, 131072])
+    rt = np.unique(np.concatenate([np.arange(64), edges[edges < T],
+                                   rng.choice(np.arange(64, T - 64), 240, replace=False),
+                                   np.arange(T - 64, T)])).astype(np.int32)
+    compare_prefill(cfg, x, np.zeros_like(rt), rt, gout, gidx, name)
+
+
 def _stage_inputs(cfg, x):
     nsa = _nsa()
     c = nsa.NsaConfig(cfg.B, cfg.T, cfg.Hkv, cfg.G, cfg.D, cfg.cmp_len, cfg.cmp_stride,

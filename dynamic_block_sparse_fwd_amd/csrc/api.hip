@@ -110,8 +110,7 @@ int check_moba(const moba_config* c) {
   if (c->D != 64 && c->D != 128) return NSA_ERR_UNSUPPORTED;
   if (c->block % 64 != 0 || c->T % c->block != 0) return NSA_ERR_UNSUPPORTED;
   if (c->top_k > 8) return NSA_ERR_UNSUPPORTED;
-  if (c->T / c->block > 16384) return NSA_ERR_UNSUPPORTED;  // per-head block counts in LDS
-  if ((long)c->T > (1L << 27)) return NSA_ERR_UNSUPPORTED;
+  if ((long)c->T > (1L << 27)) return NSA_ERR_UNSUPPORTED;  // list entries are t << 4 | slot
   if ((long)c->B * c->H * (c->T / 64) > (1L << 31) - 8) return NSA_ERR_UNSUPPORTED;  // 1-D grid
   return NSA_OK;
 }
@@ -119,11 +118,20 @@ int check_moba(const moba_config* c) {
 struct MobaPlan {
   size_t vt, hi, lo, count, rank, offset, tstart, ntiles, tile_entry, idx, list, po, pml, total;
   int nb, max_tiles;
+  int Hc;  // heads per pass
 };
+
+// Heads per pass: all of them while a pass has at most 2^24 query rows (B T Hc), else fewer, so
+// that the per-(query, slot) partials stay within 2^24 (top_k) entries.
+int moba_heads_per_pass(const moba_config* c) {
+  const long cap = (1L << 24) / ((long)c->B * c->T);
+  return (int)std::min<long>(c->H, std::max<long>(1, cap));
+}
 
 MobaPlan plan_moba(const moba_config* c) {
   MobaPlan p{};
-  const size_t BH = (size_t)c->B * c->H, rows = BH * c->T;
+  p.Hc = moba_heads_per_pass(c);
+  const size_t BH = (size_t)c->B * p.Hc, rows = BH * c->T;
   p.nb = c->T / c->block;
   const size_t entries = rows * c->top_k;
   p.max_tiles = (int)(entries / 128 + BH * p.nb + 1);
@@ -137,7 +145,7 @@ MobaPlan plan_moba(const moba_config* c) {
   p.tstart = off; off += align_up(BH * p.nb * 4);
   p.ntiles = off; off += align_up(4);
   p.tile_entry = off; off += align_up((size_t)p.max_tiles * 4);
-  p.idx = off;    off += align_up(rows * (c->top_k + 1) * 4);
+  p.idx = off;    off += align_up((size_t)c->B * c->T * c->H * (c->top_k + 1) * 4);  // all heads
   p.list = off;   off += align_up(entries * 4 + 4);
   // one spare slot each: the merge loads slot 0 unconditionally, also when top_k = 0
   p.po = off;     off += align_up((entries + 1) * c->D * 2);  // fp16
@@ -812,14 +820,22 @@ static int moba_impl(const moba_config* c, const void* q, const void* k, const v
   a.po = reinterpret_cast<_Float16*>(base + p.po);
   a.pml = reinterpret_cast<float*>(base + p.pml);
   a.idx = sel_idx ? sel_idx : reinterpret_cast<int32_t*>(base + p.idx);
-  a.B = c->B; a.T = c->T; a.H = c->H; a.D = c->D; a.block = c->block; a.top_k = c->top_k;
-  a.nb = p.nb; a.max_tiles = p.max_tiles;
+  a.B = c->B; a.T = c->T; a.D = c->D; a.block = c->block; a.top_k = c->top_k;
+  a.nb = p.nb; a.max_tiles = p.max_tiles; a.Hs = c->H;
   a.scale_log2 = c->scale * 1.4426950408889634f;
   (void)hipGetLastError();
   if (ev != nullptr) (void)hipEventRecord(ev[0], stream);
-  launch_transpose(static_cast<const uint16_t*>(v), reinterpret_cast<uint16_t*>(base + p.vt),
-                   c->B * c->H, c->T, c->D, c->T, stream);
-  launch_moba(a, stream, ev);
+  // heads in passes of Hc; with events, the stage marks are those of the last pass
+  for (int h0 = 0; h0 < c->H; h0 += p.Hc) {
+    a.h0 = h0;
+    a.H = std::min(p.Hc, c->H - h0);
+    const size_t head = (size_t)c->T * c->D;  // elements of one (sequence, head) of v
+    for (int b = 0; b < c->B; ++b)
+      launch_transpose(static_cast<const uint16_t*>(v) + ((size_t)b * c->H + h0) * head,
+                       reinterpret_cast<uint16_t*>(base + p.vt) + (size_t)b * a.H * head, a.H,
+                       c->T, c->D, c->T, stream);
+    launch_moba(a, stream, ev);
+  }
   return hip_status();
 }
 

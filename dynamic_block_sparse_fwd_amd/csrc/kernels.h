@@ -130,13 +130,16 @@ struct BwdArgs {
 void launch_backward(const BwdArgs& a, hipStream_t s, hipEvent_t* ev);
 
 constexpr int kMobaChunks = 8;  // T-chunks per head counted by separate workgroups
+constexpr int kMobaCountBlocks = 16384;  // blocks per counting workgroup (64 KB of LDS)
 
+// One pass over H of the caller's Hs heads; the workspace arrays (from vt on) hold this pass's
+// heads only.
 struct MobaArgs {
-  const uint16_t* q;   // [B, T, H, D]
-  const uint16_t* k;   // [B, H, T, D]
+  const uint16_t* q;   // [B, T, Hs, D]
+  const uint16_t* k;   // [B, Hs, T, D]
   const uint16_t* vt;  // [B*H, D, T] values, keys contiguous
-  float* out;          // [B, T, H, D]
-  int32_t* idx;        // [B, T, H, top_k + 1]
+  float* out;          // [B, T, Hs, D]
+  int32_t* idx;        // [B, T, Hs, top_k + 1]
   uint16_t* kb_hi;     // [B*H, nb, D] block key mean, bf16 high part
   uint16_t* kb_lo;     // [B*H, nb, D] bf16 of the remainder
   int32_t* count;      // [B*H*nb, kMobaChunks] queries of each T-chunk that chose each block,
@@ -150,6 +153,7 @@ struct MobaArgs {
   _Float16* po;        // [B*T*H, top_k, D] partial outputs / (own sum * scale), fp16
   float* pml;          // [B*T*H, top_k, 4] partial (max in log2 units, sum, scale, 0)
   int B, T, H, D, block, top_k, nb, max_tiles;
+  int Hs, h0;  // heads of the caller's q, k, out, idx; first head of this pass (H heads)
   float scale_log2;
 };
 

@@ -24,6 +24,15 @@ namespace nsa {
 
 constexpr int MOBA_ROWS = 128;  // gathered queries per block-major tile
 
+// A call runs its heads in chunks (a.H heads from a.h0 of a.Hs).  q, k, out and the index
+// list are addressed with the caller's head count; the workspace arrays hold the chunk's heads.
+__device__ __forceinline__ long moba_gbh(const MobaArgs& a, int b, int h) {
+  return (long)b * a.Hs + a.h0 + h;  // (sequence, head) of the caller's k
+}
+__device__ __forceinline__ long moba_grow(const MobaArgs& a, int b, long t, int h) {
+  return ((long)b * a.T + t) * a.Hs + a.h0 + h;  // row of the caller's q, out, index list
+}
+
 // kbar of one block: 16-byte loads, each thread sums 8 features over a stride of rows; the
 // row groups are then added in a fixed order (fp32), and kbar is split into bf16 hi + lo.
 template <int D>
@@ -33,7 +42,8 @@ __global__ __launch_bounds__(256) void moba_pool_kernel(MobaArgs a) {
   const int j = blockIdx.x;
   const long bh = blockIdx.y;
   const int dc = threadIdx.x % DC, p = threadIdx.x / DC;
-  const u16* src = a.k + (bh * a.T + (long)j * a.block) * D + 8 * dc;
+  const long gbh = moba_gbh(a, (int)(bh / a.H), (int)(bh % a.H));
+  const u16* src = a.k + (gbh * a.T + (long)j * a.block) * D + 8 * dc;
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int r = p; r < a.block; r += NP) {
@@ -138,7 +148,7 @@ __global__ __launch_bounds__(kGateWaves * 64) void moba_gate_kernel(MobaArgs a) 
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int tq = scoring ? t0 + 16 * u + r16 : 0;
-      const u16* qp = a.q + (((long)b * a.T + tq) * a.H + h) * D + 8 * g4;
+      const u16* qp = a.q + moba_grow(a, b, tq, h) * D + 8 * g4;
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) qf[u][c] = load8(qp + 32 * c);
     }
@@ -241,8 +251,7 @@ __global__ __launch_bounds__(kGateWaves * 64) void moba_gate_kernel(MobaArgs a) 
   if (g4 == 0) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const long row = ((long)b * a.T + t0 + 16 * u + r16) * a.H + h;
-      int32_t* orow = a.idx + row * (K + 1);
+      int32_t* orow = a.idx + moba_grow(a, b, t0 + 16 * u + r16, h) * (K + 1);
 #pragma unroll
       for (int s = 0; s < KS; ++s)
         if (s < nsel) orow[s] = chosen[u][s];
@@ -252,21 +261,25 @@ __global__ __launch_bounds__(kGateWaves * 64) void moba_gate_kernel(MobaArgs a) 
   }
 }
 
-// Per (sequence, head, T-chunk): how many of the chunk's queries chose each block, and every
-// (query, slot)'s rank among them, counted with LDS atomics (no global atomics).  Each thread
-// takes kCountRows rows per pass with every index load issued before the atomics.
+// Per (sequence, head, T-chunk, range of kMobaCountBlocks blocks): how many of the chunk's
+// queries chose each block of the range, and every such (query, slot)'s rank among them,
+// counted with LDS atomics (no global atomics).  Each thread takes kCountRows rows per pass
+// with every index load issued before the atomics.
 constexpr int kCountThreads = 1024, kCountRows = 8;
 
 template <int KS>
 __global__ __launch_bounds__(kCountThreads) void moba_count_kernel(MobaArgs a) {
-  extern __shared__ int cnt[];  // [nb]
-  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  extern __shared__ int cnt[];  // [blocks of the range]
+  const int nr = (a.nb + kMobaCountBlocks - 1) / kMobaCountBlocks;
+  const int chunk = blockIdx.x, h = (int)blockIdx.y / nr, b = blockIdx.z;
+  const int jlo = ((int)blockIdx.y % nr) * kMobaCountBlocks;
+  const int jhi = jlo + kMobaCountBlocks < a.nb ? jlo + kMobaCountBlocks : a.nb;
   const long bh = (long)b * a.H + h;
   const int K = a.top_k;
   const int slast = K > 0 ? K - 1 : 0;
   const int cl = (a.T + kMobaChunks - 1) / kMobaChunks;
   const int tbeg = chunk * cl, tend = tbeg + cl < a.T ? tbeg + cl : a.T;
-  for (int j = threadIdx.x; j < a.nb; j += kCountThreads) cnt[j] = 0;
+  for (int j = threadIdx.x; j < jhi - jlo; j += kCountThreads) cnt[j] = 0;
   __syncthreads();
   for (int t0 = tbeg + threadIdx.x; t0 < tend; t0 += kCountThreads * kCountRows) {
     int jb[kCountRows][KS];
@@ -274,7 +287,7 @@ __global__ __launch_bounds__(kCountThreads) void moba_count_kernel(MobaArgs a) {
     for (int u = 0; u < kCountRows; ++u) {
       int t = t0 + u * kCountThreads;
       t = t < tend ? t : tend - 1;
-      const int32_t* orow = a.idx + (((long)b * a.T + t) * a.H + h) * (K + 1);
+      const int32_t* orow = a.idx + moba_grow(a, b, t, h) * (K + 1);
 #pragma unroll
       for (int s = 0; s < KS; ++s) jb[u][s] = orow[s < slast ? s : slast];
     }
@@ -286,12 +299,13 @@ __global__ __launch_bounds__(kCountThreads) void moba_count_kernel(MobaArgs a) {
       const long row = ((long)b * a.T + t) * a.H + h;
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        if (s < nsel) a.rank[row * K + s] = atomicAdd(&cnt[jb[u][s]], 1);
+        if (s < nsel && jb[u][s] >= jlo && jb[u][s] < jhi)
+          a.rank[row * K + s] = atomicAdd(&cnt[jb[u][s] - jlo], 1);
     }
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < a.nb; j += kCountThreads)
-    a.count[(bh * a.nb + j) * kMobaChunks + chunk] = cnt[j];
+  for (int j = threadIdx.x; j < jhi - jlo; j += kCountThreads)
+    a.count[(bh * a.nb + jlo + j) * kMobaChunks + chunk] = cnt[j];
 }
 
 // Exclusive prefix sums of the list lengths and of their 128-row tile counts (one workgroup);
@@ -361,7 +375,7 @@ __global__ __launch_bounds__(256) void moba_fill_kernel(MobaArgs a) {
   const int nsel = bq < a.top_k ? bq : a.top_k;
   const int chunk = t / ((a.T + kMobaChunks - 1) / kMobaChunks);
   const long bh = (long)b * a.H + h;
-  const int32_t* irow = a.idx + row * (a.top_k + 1);
+  const int32_t* irow = a.idx + moba_grow(a, b, t, h) * (a.top_k + 1);
   for (int s = 0; s < nsel; ++s) {
     const long e = bh * a.nb + irow[s];
     a.list[a.offset[e] + a.count[e * kMobaChunks + chunk] + a.rank[row * a.top_k + s]] =
@@ -400,11 +414,11 @@ __global__ __launch_bounds__(256) void moba_block_kernel(MobaArgs a) {
     const int en = r < cnt ? a.list[base + r] : -1;
     rt_t[rt] = en >= 0 ? (en >> 4) : -1;
     rt_s[rt] = en >= 0 ? (en & 15) : 0;
-    const u16* qp = a.q + (((long)b * a.T + (en >= 0 ? rt_t[rt] : 0)) * a.H + h) * D + 8 * g4;
+    const u16* qp = a.q + moba_grow(a, b, en >= 0 ? rt_t[rt] : 0, h) * D + 8 * g4;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) qf[rt][c] = en >= 0 ? load8(qp + 32 * c) : zero8();
   }
-  const u16* kb = a.k + bh * (long)a.T * D;
+  const u16* kb = a.k + moba_gbh(a, b, h) * (long)a.T * D;
   const u16* vtb = a.vt + bh * (long)D * a.T;
   float mrun[RTW], lrun[RTW];
   f32x4 O[RTW][DT];
@@ -520,11 +534,11 @@ __global__ __launch_bounds__(256) void moba_own_kernel(MobaArgs a) {
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
     row_t[rt] = t0 + (wave * RTW + rt) * 16 + r16;
-    const u16* qp = a.q + (((long)b * a.T + row_t[rt]) * a.H + h) * D + 8 * g4;
+    const u16* qp = a.q + moba_grow(a, b, row_t[rt], h) * D + 8 * g4;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) qf[rt][c] = load8(qp + 32 * c);
   }
-  const u16* kb = a.k + bh * (long)a.T * D;
+  const u16* kb = a.k + moba_gbh(a, b, h) * (long)a.T * D;
   const u16* vtb = a.vt + bh * (long)D * a.T;
   float mrun[RTW], lrun[RTW];
   f32x4 O[RTW][DT];
@@ -646,7 +660,7 @@ __global__ __launch_bounds__(256) void moba_own_kernel(MobaArgs a) {
       }
     }
     const float inv = 1.0f / L;
-    float* dst = a.out + row * D;
+    float* dst = a.out + moba_grow(a, b, row_t[rt], h) * D;
 #pragma unroll
     for (int nn = 0; nn < DT; ++nn)
       *reinterpret_cast<float4*>(dst + 16 * nn + 4 * g4) =
@@ -664,8 +678,10 @@ static void launch_moba_k(const MobaArgs& a, hipStream_t s, hipEvent_t* ev) {
   moba_pool_kernel<D><<<gp, 256, 0, s>>>(a);
   moba_gate_kernel<D, KS><<<gg, kGateWaves * 64, 0, s>>>(a);
   mark(1);
-  moba_count_kernel<KS><<<dim3(kMobaChunks, a.H, a.B), kCountThreads,
-                          (size_t)a.nb * sizeof(int), s>>>(a);
+  const int nr = (a.nb + kMobaCountBlocks - 1) / kMobaCountBlocks;
+  const int cblk = a.nb < kMobaCountBlocks ? a.nb : kMobaCountBlocks;
+  moba_count_kernel<KS><<<dim3(kMobaChunks, a.H * nr, a.B), kCountThreads,
+                          (size_t)cblk * sizeof(int), s>>>(a);
   moba_scan_kernel<<<1, 1024, 0, s>>>(a);
   moba_fill_kernel<<<(int)((rows + 255) / 256), 256, 0, s>>>(a);
   mark(2);

@@ -360,8 +360,11 @@ int nsa_backward_timed(const nsa_config* cfg, const void* q, const void* k, cons
  *   q bf16 [B, T, H, D]; k, v bf16 [B, H, T, D]; out fp32 [B, T, H, D]
  *   sel_idx int32 [B, T, H, top_k + 1] or NULL: chosen blocks incl. the own block,
  *           ascending, -1 padded
+ * The heads run in passes of max(1, min(H, 2^24 / (B T))) heads (one pass up to 2^24 query
+ * rows): the workspace holds one pass's per-(query, slot) partials, fp16, about
+ * B T Hpass top_k (2 D + 16) bytes, plus the values transposed for one pass.
  * NSA_ERR_UNSUPPORTED (moba_validate) unless D is 64 or 128, block is a multiple of 64 that
- * divides T, top_k <= 8, T <= 2^27 and T / block <= 16384.
+ * divides T, top_k <= 8 and T <= 2^27.
  */
 int moba_prefill(const moba_config* cfg, const void* q, const void* k, const void* v,
                  float* out, int32_t* sel_idx, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -369,7 +372,8 @@ int moba_prefill(const moba_config* cfg, const void* q, const void* k, const voi
 /*
  * Instrumented moba_prefill: identical work, plus events[s] recorded before stage s and
  * events[NSA_MOBA_NSTAGES] after the last.  Stages: 0 value transpose, pooling and gating,
- * 1 per-block query lists, 2 block-major attention, 3 own block and merge.
+ * 1 per-block query lists, 2 block-major attention, 3 own block and merge.  With several head
+ * passes, stages 1-3 are the last pass's and stage 0 also spans every earlier pass.
  */
 #define NSA_MOBA_NSTAGES 4
 int moba_prefill_timed(const moba_config* cfg, const void* q, const void* k, const void* v,

@@ -50,6 +50,23 @@ def normal_bf16(seed: int, slot: str, shape, std: float = 1.0, chunk: int = 1 <<
     return out.reshape(shape)
 
 
+def normal_bf16_device(seed: int, slot: str, shape, device, chunk: int = 1 << 28):
+    """N(0, 1) bf16 drawn on a torch device with its Philox generator seeded seed * 16 + slot,
+    in chunks of `chunk` fp32 draws rounded to bf16 (round to nearest even) -- for inputs too
+    large to draw on the host (tens of GB).  Not the same values as normal_bf16."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 16 + SLOT[slot])
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    flat = out.view(-1)
+    n = flat.numel()
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        flat[s:e] = torch.randn(e - s, generator=g, device=device, dtype=torch.float32)
+    return out
+
+
 def upstream_grad(seed: int, shape) -> np.ndarray:
     """Gradient of the loss with respect to the layer output: N(0, 1) in fp32."""
     g = _gen(seed, "dout")

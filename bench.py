@@ -31,10 +31,14 @@ HBM_PEAK = 8.0e12         # bytes/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "dynamic_block_sparse_fwd_amd", "csrc")
 # the sources a kernel's code object depends on (its translation unit, shared headers, flags)
+_HDRS = ["attn_tile.h", "dev_common.h", "kernels.h", "../build.py"]
 KERNEL_SOURCES = {
-    "selected_kernel": ["prefill.hip", "attn_tile.h", "dev_common.h", "kernels.h", "../build.py"],
-    "dec_cmp_kernel": ["decode.hip", "attn_tile.h", "dev_common.h", "kernels.h", "../build.py"],
-    "moba_block_kernel": ["moba.hip", "attn_tile.h", "dev_common.h", "kernels.h", "../build.py"],
+    "cmp_select_kernel": ["prefill.hip"] + _HDRS,
+    "slc_block_kernel": ["selected.hip"] + _HDRS,
+    "selected_kernel": ["selected.hip"] + _HDRS,
+    "dec_cmp_kernel": ["decode.hip"] + _HDRS,
+    "moba_block_kernel": ["moba.hip"] + _HDRS,
+    "moba_own_kernel": ["moba.hip"] + _HDRS,
 }
 
 
@@ -166,6 +170,25 @@ def prefill_flops(B, T, Hkv, G, D, l=32, d=16, slc_keys=None):
     return per
 
 
+def cmp_select_performed_flops(B, T, Hkv, G, D, l=32, d=16, window=512):
+    """Matrix-core FLOPs the compressed-attention kernel issues (fused window, G = 16: query
+    tiles of 8 positions x 16 heads): per tile, two score passes and one P V product over the
+    64-key tiles of the compressed tokens the tile's last position sees, and score + P V over
+    the 64-key tiles that cover the tile's windows.  Masked keys inside a tile count: the
+    matrix core computes them."""
+    TQ = 8
+    rows = TQ * G
+    ncmp = (T - l) // d + 1 if T >= l else 0
+    t0 = np.arange(0, T, TQ, dtype=np.int64)
+    tl = np.minimum(t0 + TQ - 1, T - 1)
+    nvis = np.where(tl >= l - 1, np.minimum((tl - l) // d + 1, ncmp), 0)
+    nkt = (nvis + 63) // 64
+    kw0 = np.maximum(t0 - window + 1, 0) // 64
+    nwt = tl // 64 - kw0 + 1
+    tile = 2.0 * rows * 64 * D  # one 64-key product of the tile's rows
+    return float(B * Hkv * tile * (3 * nkt + 2 * nwt).sum())
+
+
 # ----------------------------------------------------------------------------- prefill
 
 def bench_prefill(args):
@@ -234,11 +257,19 @@ def bench_prefill(args):
     res = dict(
         ms_per_step=ms, events_ms_per_step=total_ev, tok_s=B * T / (ms * 1e-3),
         algorithmic_tflop=F / 1e12, mfma_frac=F / (ms * 1e-3) / MFMA_PEAK_BF16, stages=stages,
-        roofline={"bound": "mfma", "kernel": dom,
-                  "achieved": flops[dom] / (stage_ms[dom] * 1e-3) / 1e12,
+        # the dominant single kernel: the compressed-attention kernel (with the fused window and
+        # the selection) is one launch; the selected stage is five (lists, block-major tiles,
+        # merge), each shorter
+        roofline={"bound": "mfma", "kernel": "cmp_select_kernel",
+                  "achieved": flops["cmp_select"] / (stage_ms["cmp_select"] * 1e-3) / 1e12,
                   "peak": MFMA_PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                  "frac": flops[dom] / (stage_ms[dom] * 1e-3) / MFMA_PEAK_BF16,
-                  "traffic": measured_traffic("selected_kernel") if dom == "selected" else None},
+                  "frac": flops["cmp_select"] / (stage_ms["cmp_select"] * 1e-3) / MFMA_PEAK_BF16,
+                  "traffic": measured_traffic("cmp_select_kernel")},
+        longest_stage=dom,
+        cmp_select_performed={
+            "tflop": cmp_select_performed_flops(B, T, Hkv, G, D) / 1e12,
+            "mfma_frac": cmp_select_performed_flops(B, T, Hkv, G, D)
+                         / (stage_ms["cmp_select"] * 1e-3) / MFMA_PEAK_BF16},
         # the selected branch gathers a 64-key K+V tile per (position, group, selected block):
         # its bound is the cache hierarchy's gather bandwidth, reported beside the MFMA figure
         selected_gather={"bytes": gbytes, "gbs": gbytes / (stage_ms["selected"] * 1e-3) / 1e9},
@@ -752,11 +783,8 @@ def bench_moba(args, B=1, T=131072, H=32, D=128, seed=4, calls=5):
         d = {k: torch.from_numpy(v.view(np.int16)).to(dev) for k, v in x.items()}
     else:
         x = None
-        g = torch.Generator(device=dev)
-        g.manual_seed(seed)
         shapes = {"q": (B, T, H, D), "k": (B, H, T, D), "v": (B, H, T, D)}
-        d = {k: torch.randn(sh, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-             for k, sh in shapes.items()}
+        d = {k: S.normal_bf16_device(seed, k, sh, dev) for k, sh in shapes.items()}
     print("[bench] MoBA inputs generated in %.1fs" % (time.time() - t0), file=sys.stderr,
           flush=True)
     out = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
@@ -779,20 +807,36 @@ def bench_moba(args, B=1, T=131072, H=32, D=128, seed=4, calls=5):
            for i, nm in enumerate(nsa.MOBA_STAGES)}
     ms = float(np.median(tot))
     f_att, f_gate, pairs = moba_work(T, H, D)
+    passes = -(-H // max(1, min(H, (1 << 24) // (B * T))))
     res = {
         "workload": "moba_prefill B=%d T=%d H=%d D=%d block 512 top-3 + own" % (B, T, H, D),
         "ms_per_step": round(ms, 4),
         "tok_s": round(B * T / (ms * 1e-3), 1),
         "algorithmic_tflop": round((f_att + f_gate) / 1e12, 4),
         "mfma_frac_total": round((f_att + f_gate) / (ms * 1e-3) / MFMA_PEAK_BF16, 4),
-        "stages_ms": {k: round(v, 4) for k, v in stg.items()},
-        "roofline": {"bound": "mfma", "kernel": "block_attn + own_merge (attention)",
-                     "achieved": round(f_att / ((stg["block_attn"] + stg["own_merge"]) * 1e-3) / 1e12, 2),
-                     "peak": MFMA_PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                     "frac": round(f_att / ((stg["block_attn"] + stg["own_merge"]) * 1e-3) / MFMA_PEAK_BF16, 4),
-                     "traffic": None},
-        "timing": "median of %d calls, HIP events around each stage" % calls,
+        "head_passes": passes,
     }
+    traffic = {"moba_block_kernel": measured_traffic("moba_block_kernel"),
+               "moba_own_kernel": measured_traffic("moba_own_kernel")}
+    if passes == 1:
+        att_ms = stg["block_attn"] + stg["own_merge"]
+        res["stages_ms"] = {k: round(v, 4) for k, v in stg.items()}
+        res["roofline"] = {"bound": "mfma", "kernel": "block_attn + own_merge (attention)",
+                           "achieved": round(f_att / (att_ms * 1e-3) / 1e12, 2),
+                           "peak": MFMA_PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                           "frac": round(f_att / (att_ms * 1e-3) / MFMA_PEAK_BF16, 4),
+                           "traffic": traffic}
+    else:
+        # the heads run in several passes and the stage events of a call mark only the last
+        # pass (stage 0 spans the earlier ones): the roofline is the whole call's
+        res["stages_ms_last_pass"] = {k: round(v, 4) for k, v in stg.items() if k != "pool_gate"}
+        res["roofline"] = {"bound": "mfma", "kernel": "moba_prefill (whole call: gate and "
+                                                      "attention, %d head passes)" % passes,
+                           "achieved": round((f_att + f_gate) / (ms * 1e-3) / 1e12, 2),
+                           "peak": MFMA_PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                           "frac": round((f_att + f_gate) / (ms * 1e-3) / MFMA_PEAK_BF16, 4),
+                           "traffic": None}
+    res["timing"] = "median of %d calls, HIP events around each stage" % calls
     del d, out, idx, ws
     torch.cuda.empty_cache()
     return res, x
@@ -862,6 +906,10 @@ def main():
     ap.add_argument("--no-moba", action="store_true")
     ap.add_argument("--moba-seq", type=int, default=131072,
                     help="MoBA sequence length for --only moba (beyond 128k: device-drawn inputs)")
+    ap.add_argument("--moba-heads", type=int, default=32, help="MoBA heads for --only moba")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the rows beyond the headline workloads (MoBA at 10M tokens, the "
+                         "backward, the chunked prefill)")
     ap.add_argument("--chunk", type=int, default=8192,
                     help="chunk length for --only chunked (a multiple of 64)")
     ap.add_argument("--only", choices=("prefill", "decode", "decode_1m", "moba", "chunked",
@@ -898,7 +946,7 @@ def main():
         print(json.dumps({"chunked": bench_chunked(args)}), flush=True)
         return
     if args.only == "moba":
-        mo, _ = bench_moba(args, T=args.moba_seq)
+        mo, _ = bench_moba(args, T=args.moba_seq, H=args.moba_heads)
         print(json.dumps({"moba": mo}), flush=True)
         return
     pre, x = bench_prefill(args)
@@ -926,7 +974,10 @@ def main():
                     "stages": pre["stages"],
                     "selected_gather": {"bytes": pre["selected_gather"]["bytes"],
                                         "gbs": round(pre["selected_gather"]["gbs"], 1)},
-                    "blocks_per_row": round(pre["blocks_per_row"], 3)},
+                    "blocks_per_row": round(pre["blocks_per_row"], 3),
+                    "longest_stage": pre["longest_stage"],
+                    "cmp_select_performed": {k: round(v, 4) for k, v in
+                                             pre["cmp_select_performed"].items()}},
     }
     if args.top_p > 0:
         line["config"]["top_p"] = args.top_p
@@ -955,6 +1006,12 @@ def main():
             mo["cpu_baseline"] = cpu_baseline_moba(xm)
         del xm
         line["moba"] = mo
+    if not args.no_next:
+        # rows beyond the headline workloads, timed in the same run
+        nxt = {"moba_10m": bench_moba(args, T=10 * (1 << 20), H=4, seed=10, calls=3)[0]}
+        nxt["backward_64k"] = bench_backward(args)
+        nxt["chunked_prefill_64k"] = bench_chunked(args)
+        line["next_rows"] = nxt
     print(json.dumps(line), flush=True)
 
 

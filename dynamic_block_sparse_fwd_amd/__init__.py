@@ -13,7 +13,8 @@ import os
 from dataclasses import dataclass
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libnsa.so")
+# NSA_LIBRARY: another build of the library (the host-side sanitizer run of the tests)
+LIB_PATH = os.environ.get("NSA_LIBRARY") or os.path.join(_PKG, "libnsa.so")
 
 NSA_OK = 0
 NSA_ERR_INVALID_ARG = -1

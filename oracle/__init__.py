@@ -44,8 +44,12 @@ class _MobaCfg(ctypes.Structure):
 def _load():
     global _lib
     if _lib is None:
-        build(force=False)
-        _lib = ctypes.CDLL(_LIB)
+        alt = os.environ.get("NSA_ORACLE_LIB")  # another build of nsa_oracle.c (sanitizer runs)
+        if alt:
+            _lib = ctypes.CDLL(alt)
+        else:
+            build(force=False)
+            _lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         _lib.onsa_compress.argtypes = [ctypes.c_int] * 6 + [P, P, P, P]
         _lib.onsa_compress.restype = None

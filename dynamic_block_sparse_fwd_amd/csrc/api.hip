@@ -68,6 +68,7 @@ int check_nsa(const nsa_config* c) {
 struct DecodeShape {
   int ncmp, nblk, NCH, NT, NBT;
   int SB, NSL, KF;
+  int NG;     // tile workgroups per group of the last phase
   int ntile;  // most tiles a group's list can hold: window, forced and other selected blocks
 };
 
@@ -83,6 +84,9 @@ DecodeShape decode_shape(const nsa_config* c) {
   p.SB = decode_slice_blocks(c->cmp_len, c->cmp_stride, c->sel_block);
   p.NSL = (p.nblk + p.SB - 1) / p.SB;
   p.KF = std::max(1, c->top_n - 1 - c->n_local);
+  // about 512 tile workgroups in all, at most 8 per group (the merge's limit)
+  p.NG = (int)std::min<long>(8, std::max<long>(1, (512 + (long)c->B * c->Hkv - 1) /
+                                                      ((long)c->B * c->Hkv)));
   // the list: every tile when all blocks fit, else the window's and the selected blocks' tiles
   p.ntile = std::max(c->top_n * per, (c->window + 63) / 64 + 1 + c->top_n * per);
   return p;
@@ -251,7 +255,7 @@ BackwardPlan plan_backward(const nsa_config* c) {
 }
 
 struct DecodePlan {
-  size_t cm, cl, co, tref, cb, sS, cand, ocmp, idx, total;
+  size_t cm, cl, co, tref, cb, sS, cand, ocmp, grec, idx, total;
   DecodeShape sh;
 };
 
@@ -271,6 +275,7 @@ DecodePlan plan_decode(const nsa_config* c) {
   p.sS = off;   off += align_up(BKV * d.NSL * d.SB * F);
   p.cand = off; off += align_up(BKV * d.NSL * d.KF * sizeof(uint64_t));
   p.ocmp = off; off += align_up(BKV * 16 * c->D * F);
+  p.grec = off; off += align_up(BKV * d.NG * 2 * (32 + 16 * (size_t)c->D) * F);
   p.idx = off;  off += align_up(BKV * c->top_n * 4);
   p.total = off;
   return p;
@@ -704,11 +709,12 @@ static int decode_impl(const nsa_config* c, const void* q, const void* kcache,
   a.sS = reinterpret_cast<float*>(base + p.sS);
   a.cand = reinterpret_cast<uint64_t*>(base + p.cand);
   a.ocmp = reinterpret_cast<float*>(base + p.ocmp);
+  a.grec = reinterpret_cast<float*>(base + p.grec);
   a.B = c->B; a.L = c->T; a.Hkv = c->Hkv; a.G = c->G; a.D = c->D;
   a.l = c->cmp_len; a.d = c->cmp_stride; a.beta = c->sel_block; a.top_n = c->top_n;
   a.n_local = c->n_local; a.window = c->window; a.top_p = c->top_p;
   a.ncmp = p.sh.ncmp; a.nblk = p.sh.nblk; a.NCH = p.sh.NCH; a.NT = p.sh.NT; a.NBT = p.sh.NBT;
-  a.SB = p.sh.SB; a.NSL = p.sh.NSL; a.KF = p.sh.KF;
+  a.SB = p.sh.SB; a.NSL = p.sh.NSL; a.KF = p.sh.KF; a.NG = p.sh.NG;
   a.scale_log2 = c->scale * 1.4426950408889634f;
   (void)hipGetLastError();
   launch_decode(a, stream, ev);

@@ -2,7 +2,7 @@
 // article: decode loads only the compressed, the selected and the window KV, saving HBM
 // bandwidth; podcast notes EP94 section 6: one shared selection per GQA group, so one KV read
 // serves the group's heads).  Every phase streams HBM; the matrix core does the contractions
-// with the group's heads as the 16 MFMA rows.  Three launches:
+// with the group's heads as the 16 MFMA rows.  Four launches:
 //
 //   dec_cmp_kernel     split-K over the compressed cache: each wave streams TPW 64-token tiles
 //                      with register prefetch and an online softmax; per 1024-token chunk, per
@@ -12,10 +12,12 @@
 //                      over many workgroups): the per-head log-sum-exp, the group block scores,
 //                      the slice's best free blocks, and the normalised compressed output of a
 //                      share of the heads
-//   dec_group_kernel   per group: the slices' candidates merged into the top-n (forced blocks
-//                      added, ascending, written out); the window's, forced and other selected
-//                      tiles, each read once and feeding both branches that use it; the merge
-//                      and the gate
+//   dec_tiles_kernel   NG workgroups per group: the slices' candidates merged into the top-n
+//                      (forced blocks added, ascending, written out); the window's, forced and
+//                      other selected tiles, each read once and feeding both branches that use
+//                      it, dealt out over the group's waves; per branch one partial record per
+//                      workgroup
+//   dec_merge_kernel   per group: the records merged in workgroup order, and the gate
 // Tile work is assigned in a fixed order and every sum runs in a fixed order, so the output is
 // the same bit for bit on every call.
 #include "attn_tile.h"
@@ -873,22 +875,21 @@ __global__ __launch_bounds__(kSelThreads) void dec_select_kernel(DecodeArgs a) {
   select_slice<D, FAST>(a, (long)b * a.Hkv + kvh, b, blockIdx.x, smem);
 }
 
-// ------------------------------------------------------------------ phase 3: one workgroup per group
+// ------------------------------------------------------------------ phase 3: tiles, then merge
 
-constexpr int kGrpWaves = 8;
-constexpr int kGrpThreads = 64 * kGrpWaves;
+constexpr int kTileWaves = kSelWaves;  // waves of a tile workgroup (write_record's count)
+constexpr int kTileThreads = kSelThreads;
 
-// The rest of a group's step, after the slices: their candidates merged into the top-n (forced
-// blocks added, ascending, written out); one tile list with every tile the step reads once --
-// the window's (flagged for the selected branch when their block is selected), then the forced
-// and the other selected blocks' tiles outside the window; the waves take entries w, w + 8, ...
-// (a fixed assignment, so the output is reproducible bit for bit), each tile feeding both
-// branches; the waves' partials merged in LDS, added to the slices' compressed output under the
-// gate: out = g0 o_cmp + g1 o_slc + g2 o_win.
+// The rest of a group's step, after the slices, spread over NG workgroups per group: each
+// merges the slices' candidates into the top-n (forced blocks added; the first workgroup
+// writes the ascending row out) and builds the same tile list with every tile the step reads
+// once -- the window's (flagged for the selected branch when their block is selected), then
+// the forced and the other selected blocks' tiles outside the window; wave w of workgroup g
+// takes entries g W + w, g W + w + NG W, ... (a fixed assignment, so the output is
+// reproducible bit for bit), each tile feeding both branches; per branch the workgroup's
+// waves are merged into one record (maxima, sums, outputs relative to the maxima).
 template <int D>
-__global__ __launch_bounds__(kGrpThreads) void dec_group_kernel(DecodeArgs a) {
-  constexpr int OP = D + 4;
-  constexpr int PQ = 16 * D / kGrpThreads;  // (head, feature) pairs per thread
+__global__ __launch_bounds__(kTileThreads) void dec_tiles_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   u16(*Qs)[D + 8] = reinterpret_cast<u16(*)[D + 8]>(smem);
   int* list = reinterpret_cast<int*>(smem + 16 * (D + 8) * 2);
@@ -896,14 +897,12 @@ __global__ __launch_bounds__(kGrpThreads) void dec_group_kernel(DecodeArgs a) {
   u16(*Vt)[D][64] = reinterpret_cast<u16(*)[D][64]>(region);
   __shared__ int sidx[64];
   __shared__ int n_s;
-  __shared__ float Wm[kGrpWaves][16], Wl[kGrpWaves][16], Ls[2][16];
-  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int ng = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const long bkv = (long)b * a.Hkv + kvh;
   const DecRow r = dec_row(a, b);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g4 = lane >> 4, r16 = lane & 15;
-  for (int e = tid; e < 16 * (D / 8); e += kGrpThreads) {
+  for (int e = tid; e < 16 * (D / 8); e += kTileThreads) {
     const int qh = e / (D / 8), qc = (e % (D / 8)) * 8;
     *reinterpret_cast<bf16x8*>(&Qs[qh][qc]) =
         qh < a.G ? load8(a.q + ((long)b * a.Hkv * a.G + kvh * a.G + qh) * D + qc) : zero8();
@@ -913,15 +912,16 @@ __global__ __launch_bounds__(kGrpThreads) void dec_group_kernel(DecodeArgs a) {
   const int nsl = (r.nb + a.SB - 1) / a.SB;
   if (!r.all) {
     const uint64_t* cb = a.cand + bkv * a.NSL * a.KF;
-    for (int i = tid; i < nsl * a.KF; i += kGrpThreads) ck[i] = cb[i];
+    for (int i = tid; i < nsl * a.KF; i += kTileThreads) ck[i] = cb[i];
   }
   __syncthreads();
   if (wave == 0) {
+    const bool writer = ng == 0;
     int32_t* orow = a.idx + bkv * a.top_n;
     if (r.all) {
       if (lane < a.top_n) {
         const int el = lane < r.nb ? lane : -1;
-        orow[lane] = el;
+        if (writer) orow[lane] = el;
         sidx[lane] = el;
       }
     } else {
@@ -942,11 +942,11 @@ __global__ __launch_bounds__(kGrpThreads) void dec_group_kernel(DecodeArgs a) {
       const bool valid = lane < a.top_n && el != 0x7FFFFFFF;
       const int nsel = (int)__popcll(__ballot(valid));
       if (valid) {
-        orow[rank] = el;
+        if (writer) orow[rank] = el;
         sidx[rank] = el;
       }
       if (lane >= nsel && lane < a.top_n) {
-        orow[lane] = -1;
+        if (writer) orow[lane] = -1;
         sidx[lane] = -1;
       }
     }
@@ -980,54 +980,72 @@ __global__ __launch_bounds__(kGrpThreads) void dec_group_kernel(DecodeArgs a) {
   __syncthreads();  // the list is posted and the candidates' LDS is free for the tiles
   const int n = __builtin_amdgcn_readfirstlane(n_s);
   WaveSoftmax<D, 2> st;
-  wave_tiles<D, 2>(a, bkv, r, list, n, wave, kGrpWaves, Qs, Vt[wave], st);
-  // the waves' partials of each branch rescaled to the workgroup maximum and summed through LDS
-  // (one branch at a time); thread tid keeps the sums of pairs tid + 512 q (head, feature)
-  float* Ob = reinterpret_cast<float*>(region);  // [waves][16][OP]
-  const float sl = a.scale_log2;
-  float ob[2][PQ];
-#pragma unroll
-  for (int br = 0; br < 2; ++br) {
-    __syncthreads();  // the tiles' (or the previous branch's) LDS reads are done
-    if (g4 == 0) {
-      Wm[wave][r16] = st.m[br];
-      Wl[wave][r16] = st.l[br];
-    }
-    __syncthreads();
+  wave_tiles<D, 2>(a, bkv, r, list, n, ng * kTileWaves + wave, a.NG * kTileWaves, Qs,
+                   Vt[wave], st);
+  float* rec = a.grec + (bkv * a.NG + ng) * 2 * (32 + 16 * D);
+  write_record<D, 2>(st, 0, a.scale_log2, reinterpret_cast<float*>(region), rec);
+  write_record<D, 2>(st, 1, a.scale_log2, reinterpret_cast<float*>(region), rec + 32 + 16 * D);
+}
+
+// Per group: the NG tile workgroups' records of each branch merged in workgroup order, then
+// the gate: out = g0 o_cmp + g1 o_slc + g2 o_win (o_cmp normalised by the selection slices).
+// Threads 0..31 turn the records' maxima and sums into per-(branch, head) weights first, so
+// that every output's loads are issued together.
+constexpr int kMergeMaxNG = 8;
+
+template <int D>
+__global__ __launch_bounds__(256) void dec_merge_kernel(DecodeArgs a) {
+  constexpr int RS = 32 + 16 * D;  // floats of one record
+  constexpr int PT = 16 * D / 256;  // (head, feature) pairs per thread
+  __shared__ float W[2][16][kMergeMaxNG];  // weight of record g relative to the common max, / L
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const long bkv = (long)b * a.Hkv + kvh;
+  const float* recs = a.grec + bkv * a.NG * 2 * RS;
+  const int tid = threadIdx.x;
+  if (tid < 32) {
+    const int br = tid >> 4, h = tid & 15;
+    float m[kMergeMaxNG];
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kGrpWaves; ++w) M = fmaxf(M, Wm[w][r16]);
-    const float f = st.m[br] == kNegInf ? 0.f : fast_exp2((st.m[br] - M) * sl);
-#pragma unroll
-    for (int n2 = 0; n2 < D / 16; ++n2)
-      *reinterpret_cast<f32x4*>(&Ob[(wave * 16 + r16) * OP + 16 * n2 + 4 * g4]) = f * st.O[br][n2];
-    if (tid < 16) {  // lanes 0..15 of wave 0 own rows 0..15: M is row tid's maximum
-      float L = 0.f;
-#pragma unroll
-      for (int w = 0; w < kGrpWaves; ++w)
-        if (Wm[w][tid] != kNegInf) L += Wl[w][tid] * fast_exp2((Wm[w][tid] - M) * sl);
-      Ls[br][tid] = L;
+    for (int g = 0; g < kMergeMaxNG; ++g) {
+      m[g] = g < a.NG ? recs[(g * 2 + br) * RS + h] : kNegInf;
+      M = fmaxf(M, m[g]);
     }
-    __syncthreads();
+    float L = 0.f, w[kMergeMaxNG];
 #pragma unroll
-    for (int q = 0; q < PQ; ++q) {
-      const int pr = tid + kGrpThreads * q, h = pr / D, dd = pr % D;
-      float o = 0.f;
+    for (int g = 0; g < kMergeMaxNG; ++g) {
+      w[g] = m[g] == kNegInf ? 0.f : fast_exp2(m[g] - M);
+      L += g < a.NG ? w[g] * recs[(g * 2 + br) * RS + 16 + h] : 0.f;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-      for (int w = 0; w < kGrpWaves; ++w) o += Ob[(w * 16 + h) * OP + dd];
-      ob[br][q] = o;
+    for (int g = 0; g < kMergeMaxNG; ++g) W[br][h][g] = w[g] * inv;
+  }
+  __syncthreads();
+  float acc[PT][2];
+#pragma unroll
+  for (int q = 0; q < PT; ++q) acc[q][0] = acc[q][1] = 0.f;
+#pragma unroll
+  for (int g = 0; g < kMergeMaxNG; ++g) {
+    if (g >= a.NG) break;  // uniform
+#pragma unroll
+    for (int br = 0; br < 2; ++br) {
+      const float* rc = recs + (g * 2 + br) * RS + 32;
+#pragma unroll
+      for (int q = 0; q < PT; ++q) {
+        const int pr = tid + 256 * q, h = pr / D;
+        acc[q][br] += W[br][h][g] * rc[pr];
+      }
     }
   }
 #pragma unroll
-  for (int q = 0; q < PQ; ++q) {
-    const int pr = tid + kGrpThreads * q, h = pr / D, dd = pr % D;
+  for (int q = 0; q < PT; ++q) {
+    const int pr = tid + 256 * q, h = pr / D, dd = pr % D;
     if (h >= a.G) continue;
-    const float ls = Ls[0][h], lw = Ls[1][h];
     const long head = (long)b * a.Hkv * a.G + kvh * a.G + h;
     const float* g = a.gate + head * 3;
-    a.out[head * D + dd] = g[0] * a.ocmp[(bkv * 16 + h) * D + dd] +
-                           g[1] * (ls > 0.f ? ob[0][q] / ls : 0.f) +
-                           g[2] * (lw > 0.f ? ob[1][q] / lw : 0.f);
+    a.out[head * D + dd] = g[0] * a.ocmp[(bkv * 16 + h) * D + dd] + g[1] * acc[q][0] +
+                           g[2] * acc[q][1];
   }
 }
 
@@ -1035,11 +1053,11 @@ __global__ __launch_bounds__(kGrpThreads) void dec_group_kernel(DecodeArgs a) {
 
 int decode_chunk_tokens() { return CHUNK; }
 
-// Dynamic LDS of the per-group kernel: the group's queries, its tile list, and one V^T tile per
-// wave (the candidates before, the partial merge after reuse the tiles' space).
+// Dynamic LDS of a tile workgroup: the group's queries, its tile list, and one V^T tile per
+// wave (the candidates before, the records' merge after reuse the tiles' space).
 static size_t group_lds(int D) {
-  const size_t tiles = (size_t)kGrpWaves * D * 64 * 2;
-  const size_t merge = (size_t)kGrpWaves * 16 * (D + 4) * 4;
+  const size_t tiles = (size_t)kTileWaves * D * 64 * 2;
+  const size_t merge = (size_t)kTileWaves * 16 * (D + 4) * 4;
   const size_t cand = (size_t)decode_max_candidates(D) * 8;
   size_t region = tiles > merge ? tiles : merge;
   region = region > cand ? region : cand;
@@ -1055,15 +1073,17 @@ static void launch_decode_t(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) 
   // opt in to the dynamic LDS beyond 64 KB; the attribute is per device, so it is set on every
   // launch
   if (lds > 64 * 1024)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(dec_group_kernel<D>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(dec_tiles_kernel<D>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   mark(0);
   if (a.NCH > 0) dec_cmp_kernel<D, FAST><<<dim3(a.NCH, a.Hkv, a.B), 256, 0, s>>>(a);
   mark(1);
   dec_select_kernel<D, FAST><<<dim3(a.NSL, a.Hkv, a.B), kSelThreads, 0, s>>>(a);
   mark(2);
-  dec_group_kernel<D><<<dim3(a.Hkv, a.B), kGrpThreads, lds, s>>>(a);
+  dec_tiles_kernel<D><<<dim3(a.NG, a.Hkv, a.B), kTileThreads, lds, s>>>(a);
   mark(3);
+  dec_merge_kernel<D><<<dim3(a.Hkv, a.B), 256, 0, s>>>(a);
+  mark(4);
 }
 
 void launch_decode(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) {

@@ -68,11 +68,14 @@ struct DecodeArgs {
   float* sS;        // [B*Hkv, NSL * SB] group block scores, written by the selection slices
   uint64_t* cand;   // [B*Hkv, NSL, KF] each slice's best free blocks (rank keys, 0 = none)
   float* ocmp;      // [B*Hkv, 16, D] compressed-branch output, normalised by the selection slices
+  float* grec;      // [B*Hkv, NG, 2, 32 + 16 D] per tile workgroup and branch: 16 maxima (scaled
+                    // log2), 16 sums, 16 x D outputs relative to the maxima
   int B, L, Hkv, G, D;
   int l, d, beta, top_n, n_local, window;
   int ncmp, nblk, NCH, NT, NBT;
   int SB, NSL;  // blocks per selection slice, slices per group
   int KF;       // free blocks per group: top_n - 1 - n_local (at least 1)
+  int NG;       // tile workgroups per group
   float scale_log2;
   float top_p;  // 0: fixed top_n; else the adaptive cut at top_p * G
 };
@@ -87,7 +90,7 @@ int decode_slice_blocks(int l, int d, int beta);
 // candidates (slices x free blocks) the per-group kernel stages in LDS
 __host__ __device__ constexpr int decode_max_candidates(int D) { return 4 * D * 64 * 2 / 8; }
 
-// Backward of the prefill layer (G = 16).
+// Backward of the prefill layer.
 struct BwdArgs {
   const uint16_t* q;      // [B, T, Hq, D]
   const uint16_t* k;      // [B, Hkv, T, D]

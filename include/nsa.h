@@ -250,10 +250,11 @@ int nsa_decode_noalloc(const nsa_config* cfg, const void* q, const void* kcache,
 /*
  * Instrumented nsa_decode: identical work, plus events[s] recorded before stage s and
  * events[NSA_DECODE_NSTAGES] after the last.  Stages: 0 compressed-cache stream, 1 block scores,
- * per-slice ranking and the compressed output, 2 per group: top-n, the window's and selected
- * tiles, merge and gate.  For measurement only.
+ * per-slice ranking and the compressed output, 2 top-n and the window's and selected tiles,
+ * spread over several workgroups per group, 3 per group: merge of their partials and gate.
+ * For measurement only.
  */
-#define NSA_DECODE_NSTAGES 3
+#define NSA_DECODE_NSTAGES 4
 int nsa_decode_timed(const nsa_config* cfg, const void* q, const void* kcache,
                      const void* vcache, const void* kcmp, const void* vcmp,
                      const int32_t* seqlens, const float* gate, float* out, int32_t* sel_idx,

@@ -69,6 +69,7 @@ struct DecodeShape {
   int ncmp, nblk, NCH, NT, NBT;
   int SB, NSL, KF;
   int NG;     // tile workgroups per group of the last phase
+  int NGW;    // of them, the ones that take the window's and forced tiles
   int ntile;  // most tiles a group's list can hold: window, forced and other selected blocks
 };
 
@@ -84,9 +85,11 @@ DecodeShape decode_shape(const nsa_config* c) {
   p.SB = decode_slice_blocks(c->cmp_len, c->cmp_stride, c->sel_block);
   p.NSL = (p.nblk + p.SB - 1) / p.SB;
   p.KF = std::max(1, c->top_n - 1 - c->n_local);
-  // about 512 tile workgroups in all, at most 8 per group (the merge's limit)
-  p.NG = (int)std::min<long>(8, std::max<long>(1, (512 + (long)c->B * c->Hkv - 1) /
+  // about 512 tile workgroups in all, at least 2 and at most 8 per group (the merge's limit);
+  // a quarter of them (at least one) take the tiles known before the selection
+  p.NG = (int)std::min<long>(8, std::max<long>(2, (512 + (long)c->B * c->Hkv - 1) /
                                                       ((long)c->B * c->Hkv)));
+  p.NGW = std::max(1, p.NG / 4);
   // the list: every tile when all blocks fit, else the window's and the selected blocks' tiles
   p.ntile = std::max(c->top_n * per, (c->window + 63) / 64 + 1 + c->top_n * per);
   return p;
@@ -714,7 +717,7 @@ static int decode_impl(const nsa_config* c, const void* q, const void* kcache,
   a.l = c->cmp_len; a.d = c->cmp_stride; a.beta = c->sel_block; a.top_n = c->top_n;
   a.n_local = c->n_local; a.window = c->window; a.top_p = c->top_p;
   a.ncmp = p.sh.ncmp; a.nblk = p.sh.nblk; a.NCH = p.sh.NCH; a.NT = p.sh.NT; a.NBT = p.sh.NBT;
-  a.SB = p.sh.SB; a.NSL = p.sh.NSL; a.KF = p.sh.KF; a.NG = p.sh.NG;
+  a.SB = p.sh.SB; a.NSL = p.sh.NSL; a.KF = p.sh.KF; a.NG = p.sh.NG; a.NGW = p.sh.NGW;
   a.scale_log2 = c->scale * 1.4426950408889634f;
   (void)hipGetLastError();
   launch_decode(a, stream, ev);

@@ -12,10 +12,11 @@
 //                      over many workgroups): the per-head log-sum-exp, the group block scores,
 //                      the slice's best free blocks, and the normalised compressed output of a
 //                      share of the heads
-//   dec_tiles_kernel   NG workgroups per group: the slices' candidates merged into the top-n
-//                      (forced blocks added, ascending, written out); the window's, forced and
-//                      other selected tiles, each read once and feeding both branches that use
-//                      it, dealt out over the group's waves; per branch one partial record per
+//   dec_tiles_kernel   NG workgroups per group: NGW of them take the window's and the forced
+//                      blocks' tiles (known before the selection) at once, the others merge the
+//                      slices' candidates into the top-n (forced blocks added, ascending,
+//                      written out) and take the other selected blocks' tiles; tiles dealt out
+//                      over the waves of each kind; per branch one partial record per
 //                      workgroup
 //   dec_merge_kernel   per group: the records merged in workgroup order, and the gate
 // Tile work is assigned in a fixed order and every sum runs in a fixed order, so the output is
@@ -880,14 +881,15 @@ __global__ __launch_bounds__(kSelThreads) void dec_select_kernel(DecodeArgs a) {
 constexpr int kTileWaves = kSelWaves;  // waves of a tile workgroup (write_record's count)
 constexpr int kTileThreads = kSelThreads;
 
-// The rest of a group's step, after the slices, spread over NG workgroups per group: each
-// merges the slices' candidates into the top-n (forced blocks added; the first workgroup
-// writes the ascending row out) and builds the same tile list with every tile the step reads
-// once -- the window's (flagged for the selected branch when their block is selected), then
-// the forced and the other selected blocks' tiles outside the window; wave w of workgroup g
-// takes entries g W + w, g W + w + NG W, ... (a fixed assignment, so the output is
-// reproducible bit for bit), each tile feeding both branches; per branch the workgroup's
-// waves are merged into one record (maxima, sums, outputs relative to the maxima).
+// The rest of a group's step, after the slices, spread over NG workgroups per group in two
+// kinds.  The first NGW take the tiles known before the selection -- the window's, then the
+// forced blocks' outside it (or every tile when all blocks fit) -- and start on them at once.
+// The others merge the slices' candidates into the top-n (forced blocks added; the first of
+// them writes the ascending row out) and take the other selected blocks' tiles, inside the
+// window or not, for the selected branch only.  Within a kind, wave w of its workgroup g takes
+// entries g W + w, g W + w + n W, ... (a fixed assignment, so the output is reproducible bit
+// for bit); per branch the workgroup's waves are merged into one record (maxima, sums,
+// outputs relative to the maxima).
 template <int D>
 __global__ __launch_bounds__(kTileThreads) void dec_tiles_kernel(DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -907,81 +909,81 @@ __global__ __launch_bounds__(kTileThreads) void dec_tiles_kernel(DecodeArgs a) {
     *reinterpret_cast<bf16x8*>(&Qs[qh][qc]) =
         qh < a.G ? load8(a.q + ((long)b * a.Hkv * a.G + kvh * a.G + qh) * D + qc) : zero8();
   }
-  // the slices' candidates into LDS (the region the tiles use later), loads issued together
-  uint64_t* ck = reinterpret_cast<uint64_t*>(region);
-  const int nsl = (r.nb + a.SB - 1) / a.SB;
-  if (!r.all) {
-    const uint64_t* cb = a.cand + bkv * a.NSL * a.KF;
-    for (int i = tid; i < nsl * a.KF; i += kTileThreads) ck[i] = cb[i];
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const bool writer = ng == 0;
-    int32_t* orow = a.idx + bkv * a.top_n;
-    if (r.all) {
-      if (lane < a.top_n) {
-        const int el = lane < r.nb ? lane : -1;
-        if (writer) orow[lane] = el;
-        sidx[lane] = el;
-      }
-    } else {
-      uint64_t key = wave_topk([&](int i) { return ck[i]; }, 0, nsl * a.KF, r.kfree, lane);
-      if (r.top_p) {
-        const float* S = a.sS + bkv * a.NSL * a.SB;
-        float forced = S[0];
-        for (int j = r.flo; j <= r.bcur; ++j) forced += S[j];
-        key = top_p_cut(key, r.kfree, forced, r.nvis > 0 ? a.top_p * (float)a.G : 0.f, lane);
-      }
-      int el = key != 0 ? rank_key_index(key) : 0x7FFFFFFF;
-      if (lane >= r.kfree) el = 0x7FFFFFFF;
-      if (lane == r.kfree) el = 0;
-      if (lane > r.kfree && lane <= r.kfree + r.bcur - r.flo + 1) el = r.flo + (lane - r.kfree - 1);
-      int rank = 0;
-      for (int o = 0; o < a.top_n; ++o)  // the whole wave is active here
-        rank += (__builtin_amdgcn_readlane(el, o) < el) ? 1 : 0;
-      const bool valid = lane < a.top_n && el != 0x7FFFFFFF;
-      const int nsel = (int)__popcll(__ballot(valid));
-      if (valid) {
-        if (writer) orow[rank] = el;
-        sidx[rank] = el;
-      }
-      if (lane >= nsel && lane < a.top_n) {
-        if (writer) orow[lane] = -1;
-        sidx[lane] = -1;
-      }
+  const bool fixed_kind = ng < a.NGW;  // uniform per workgroup
+  if (fixed_kind) {
+    // the window's and forced blocks' tiles (all tiles when every block fits)
+    if (wave == 0) {
+      const int nf = fixed_tile_list(a, r, list, lane);
+      if (lane == 0) n_s = nf;
     }
-    __asm__ volatile("" ::: "memory");  // sidx written by this wave before its reads
-    // the window's and forced blocks' tiles, then the other selected blocks' tiles: flagged in
-    // the window, appended outside it
-    int base = fixed_tile_list(a, r, list, lane);
+    __syncthreads();
+  } else {
+    // the slices' candidates into LDS (the region the tiles use later), loads issued together
+    uint64_t* ck = reinterpret_cast<uint64_t*>(region);
+    const int nsl = (r.nb + a.SB - 1) / a.SB;
     if (!r.all) {
-      const int per = a.beta / 64, ns = a.top_n * per, tl = r.t / 64;
-      for (int i0 = 0; i0 < ns; i0 += 64) {
-        const int i = i0 + lane;
-        int code = -1;
-        if (i < ns) {
-          const int jb = sidx[i / per], tile = jb * per + i % per;
-          const bool forced = jb == 0 || (jb >= r.flo && jb <= r.bcur);
-          if (jb >= 0 && !forced && tile <= tl) {
-            if (tile >= r.wt0 && tile <= r.wt1)
-              list[tile - r.wt0] |= (int)kCodeSlc;  // distinct tiles: one lane per entry
-            else
-              code = (int)(tile | kCodeSlc);
-          }
-        }
-        const uint64_t m = __ballot(code >= 0);
-        const int pos = base + (int)__popcll(m & ((1ull << lane) - 1ull));
-        if (code >= 0) list[pos] = code;
-        base += (int)__popcll(m);
-      }
+      const uint64_t* cb = a.cand + bkv * a.NSL * a.KF;
+      for (int i = tid; i < nsl * a.KF; i += kTileThreads) ck[i] = cb[i];
     }
-    if (lane == 0) n_s = base;
+    __syncthreads();
+    if (wave == 0) {
+      const bool writer = ng == a.NGW;
+      int32_t* orow = a.idx + bkv * a.top_n;
+      int base = 0;
+      if (r.all) {
+        if (lane < a.top_n && writer) orow[lane] = lane < r.nb ? lane : -1;
+      } else {
+        uint64_t key = wave_topk([&](int i) { return ck[i]; }, 0, nsl * a.KF, r.kfree, lane);
+        if (r.top_p) {
+          const float* S = a.sS + bkv * a.NSL * a.SB;
+          float forced = S[0];
+          for (int j = r.flo; j <= r.bcur; ++j) forced += S[j];
+          key = top_p_cut(key, r.kfree, forced, r.nvis > 0 ? a.top_p * (float)a.G : 0.f, lane);
+        }
+        int el = key != 0 ? rank_key_index(key) : 0x7FFFFFFF;
+        if (lane >= r.kfree) el = 0x7FFFFFFF;
+        if (lane == r.kfree) el = 0;
+        if (lane > r.kfree && lane <= r.kfree + r.bcur - r.flo + 1) el = r.flo + (lane - r.kfree - 1);
+        int rank = 0;
+        for (int o = 0; o < a.top_n; ++o)  // the whole wave is active here
+          rank += (__builtin_amdgcn_readlane(el, o) < el) ? 1 : 0;
+        const bool valid = lane < a.top_n && el != 0x7FFFFFFF;
+        const int nsel = (int)__popcll(__ballot(valid));
+        if (valid) {
+          if (writer) orow[rank] = el;
+          sidx[rank] = el;
+        }
+        if (lane >= nsel && lane < a.top_n) {
+          if (writer) orow[lane] = -1;
+          sidx[lane] = -1;
+        }
+        __asm__ volatile("" ::: "memory");  // sidx written by this wave before its reads
+        // the tiles of the selected blocks other than the forced ones, for the selected branch
+        const int per = a.beta / 64, ns = a.top_n * per, tl = r.t / 64;
+        for (int i0 = 0; i0 < ns; i0 += 64) {
+          const int i = i0 + lane;
+          int code = -1;
+          if (i < ns) {
+            const int jb = sidx[i / per], tile = jb * per + i % per;
+            const bool forced = jb == 0 || (jb >= r.flo && jb <= r.bcur);
+            if (jb >= 0 && !forced && tile <= tl) code = (int)(tile | kCodeSlc);
+          }
+          const uint64_t m = __ballot(code >= 0);
+          const int pos = base + (int)__popcll(m & ((1ull << lane) - 1ull));
+          if (code >= 0) list[pos] = code;
+          base += (int)__popcll(m);
+        }
+      }
+      if (lane == 0) n_s = base;
+    }
+    __syncthreads();  // the list is posted and the candidates' LDS is free for the tiles
   }
-  __syncthreads();  // the list is posted and the candidates' LDS is free for the tiles
   const int n = __builtin_amdgcn_readfirstlane(n_s);
+  const int g0 = fixed_kind ? ng : ng - a.NGW;                 // this workgroup's index in its kind
+  const int gn = fixed_kind ? a.NGW : a.NG - a.NGW;           // workgroups of its kind
   WaveSoftmax<D, 2> st;
-  wave_tiles<D, 2>(a, bkv, r, list, n, ng * kTileWaves + wave, a.NG * kTileWaves, Qs,
-                   Vt[wave], st);
+  wave_tiles<D, 2>(a, bkv, r, list, n, g0 * kTileWaves + wave, gn * kTileWaves, Qs, Vt[wave],
+                   st);
   float* rec = a.grec + (bkv * a.NG + ng) * 2 * (32 + 16 * D);
   write_record<D, 2>(st, 0, a.scale_log2, reinterpret_cast<float*>(region), rec);
   write_record<D, 2>(st, 1, a.scale_log2, reinterpret_cast<float*>(region), rec + 32 + 16 * D);

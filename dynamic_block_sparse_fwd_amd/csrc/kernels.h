@@ -76,6 +76,7 @@ struct DecodeArgs {
   int SB, NSL;  // blocks per selection slice, slices per group
   int KF;       // free blocks per group: top_n - 1 - n_local (at least 1)
   int NG;       // tile workgroups per group
+  int NGW;      // of them, the ones that take the window's and forced tiles
   float scale_log2;
   float top_p;  // 0: fixed top_n; else the adaptive cut at top_p * G
 };

@@ -58,6 +58,8 @@ EXPORTS = {
     "nsa_prefill": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p]),
     "nsa_prefill_stages": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint] + [ctypes.c_void_p] * 9
                            + [ctypes.c_size_t, ctypes.c_void_p]),
+    "nsa_prefill_diag": (ctypes.c_int, [ctypes.c_void_p] * 12 + [ctypes.c_size_t,
+                                                                 ctypes.c_void_p]),
     "nsa_prefill_timed": (ctypes.c_int,
                           [ctypes.c_void_p] * 10 + [ctypes.c_size_t, ctypes.c_void_p,
                                                      ctypes.c_void_p]),
@@ -288,6 +290,38 @@ def nsa_prefill(cfg: NsaConfig, q, k, v, wk, wv, gate, out=None, sel_idx=None, w
         ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream), *extra)
     _check(st, "nsa_prefill")
     return out, sel_idx
+
+
+def nsa_prefill_diag(cfg: NsaConfig, q, k, v, wk, wv, gate, want_scores=True, ws=None,
+                     stream=None):
+    """nsa_prefill plus its diagnostics: returns (out, sel_idx, lse fp32 [B,T,Hq], scores fp32
+    [B,T,Hkv,nblk] or None).  lse: ln of the compressed branch's softmax sum (-inf with no
+    visible compressed token); scores: the group block scores the selection ranks."""
+    torch = _torch()
+    lib = load_library()
+    c = cfg.c()
+    B, T, Hkv, Hq, D = cfg.B, cfg.T, cfg.Hkv, cfg.Hq, cfg.D
+    nblk = (T + cfg.sel_block - 1) // cfg.sel_block
+    dev = q.device
+    f32 = (torch.float32,)
+    out = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
+    sel_idx = torch.empty((B, T, Hkv, cfg.top_n), dtype=torch.int32, device=dev)
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
+    scores = torch.empty((B, T, Hkv, nblk), dtype=torch.float32, device=dev) if want_scores \
+        else None
+    ws = _workspace(lib.nsa_prefill_workspace_bytes(ctypes.byref(c)), dev, ws)
+    bt = _bf16_types()
+    st = lib.nsa_prefill_diag(
+        ctypes.byref(c), _dev(q, "q", bt, (B, T, Hq, D)), _dev(k, "k", bt, (B, Hkv, T, D)),
+        _dev(v, "v", bt, (B, Hkv, T, D)), _dev(wk, "wk", bt, (cfg.cmp_len, D, D)),
+        _dev(wv, "wv", bt, (cfg.cmp_len, D, D)), _dev(gate, "gate", f32, (B, T, Hq, 3)),
+        _dev(out, "out", f32, (B, T, Hq, D)),
+        _dev(sel_idx, "sel_idx", (torch.int32,), (B, T, Hkv, cfg.top_n)),
+        _dev(lse, "lse", f32, (B, T, Hq)),
+        None if scores is None else _dev(scores, "scores", f32, (B, T, Hkv, nblk)),
+        ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream))
+    _check(st, "nsa_prefill_diag")
+    return out, sel_idx, lse, scores
 
 
 STAGE_CMP_SELECT, STAGE_WINDOW, STAGE_SELECTED = 1, 2, 4

@@ -373,9 +373,13 @@ int nsa_compress_tiles(const nsa_config* c, const void* x, const void* w, void* 
 static int prefill_run(const nsa_config* c, unsigned stages, const void* q, const void* k,
                        const void* v, const void* wk, const void* wv, const float* gate,
                        float* out, int32_t* sel_idx, void* ws, size_t ws_bytes,
-                       hipStream_t stream, hipEvent_t* ev) {
+                       hipStream_t stream, hipEvent_t* ev, float* dlse = nullptr,
+                       float* dscores = nullptr) {
   int st = check_nsa(c);
   if (st != NSA_OK) return st;
+  if (dscores != nullptr &&
+      cmp_select_streams(c->G, (c->T + c->sel_block - 1) / c->sel_block))
+    return NSA_ERR_UNSUPPORTED;  // the selection streams: no block score array to export
   if (stages == 0 || (stages & ~(unsigned)NSA_STAGE_ALL) != 0) return NSA_ERR_INVALID_ARG;
   const bool s_cmp = stages & NSA_STAGE_CMP_SELECT, s_win = stages & NSA_STAGE_WINDOW;
   const bool s_slc = stages & NSA_STAGE_SELECTED;
@@ -432,6 +436,8 @@ static int prefill_run(const nsa_config* c, unsigned stages, const void* q, cons
   a.ncmp = p.ncmp; a.NCP = p.NCP; a.TP = p.TP; a.nblk = p.nblk;
   a.scale_log2 = c->scale * 1.4426950408889634f;
   a.fuse_window = s_cmp && s_win;  // one query tile, out written once
+  a.dlse = dlse;
+  a.dscores = dscores;
   set_selected_ws(a, p, base);
   mark(2);
   if (s_cmp) launch_cmp_select(a, stream);
@@ -463,6 +469,15 @@ int nsa_prefill(const nsa_config* c, const void* q, const void* k, const void* v
                 const void* wv, const float* gate, float* out, int32_t* sel_idx, void* ws,
                 size_t ws_bytes, hipStream_t stream) {
   return prefill_impl(c, q, k, v, wk, wv, gate, out, sel_idx, ws, ws_bytes, stream, nullptr);
+}
+
+int nsa_prefill_diag(const nsa_config* c, const void* q, const void* k, const void* v,
+                     const void* wk, const void* wv, const float* gate, float* out,
+                     int32_t* sel_idx, float* lse, float* scores, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  if ((lse && !aligned16(lse)) || (scores && !aligned16(scores))) return NSA_ERR_INVALID_ARG;
+  return prefill_run(c, NSA_STAGE_ALL, q, k, v, wk, wv, gate, out, sel_idx, ws, ws_bytes, stream,
+                     nullptr, lse, scores);
 }
 
 int nsa_prefill_timed(const nsa_config* c, const void* q, const void* k, const void* v,

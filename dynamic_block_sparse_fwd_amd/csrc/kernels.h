@@ -24,6 +24,9 @@ struct PrefillArgs {
   float scale_log2;     // softmax scale * log2(e)
   float top_p;          // 0: fixed top_n; else the adaptive cut at top_p * G
   int fuse_window;      // cmp_select also runs the window branch and writes out once
+  float* dlse;          // nullable [B, nq, Hq]: ln of the compressed branch's softmax sum
+  float* dscores;       // nullable [B, nq, Hkv, nblk]: group block scores (block scores kept in
+                        // LDS only)
   // Selected branch, block-major part (workspace).  An "entry" is one selected 64-key tile of one
   // (row, group) that is not among the tiles the selected kernel shares per eight positions;
   // row = b * nq + (t - q0), free slot fs = its rank among the row's such tiles (< FS).

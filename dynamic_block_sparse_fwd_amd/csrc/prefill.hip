@@ -219,6 +219,9 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
     const float part = (mrun[rt] == kNegInf) ? 0.f : lrun[rt] * fast_exp2((mrun[rt] - M) * sl);
     const float L = col_sum4(part);
     rlse[rt] = (M == kNegInf) ? 0.f : M * sl + __log2f(L);  // no visible key: p masked to 0
+    if (a.dlse != nullptr && g4 == 0 && row_t[rt] < a.T)  // diagnostics: natural-log lse
+      a.dlse[prow(a, b, row_t[rt]) * (a.Hkv * G) + row_h[rt]] =
+          M == kNegInf ? kNegInf : rlse[rt] * 0.6931471805599453f;
   }
 
   f32x4 O[RTW][DT];
@@ -530,6 +533,12 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
     if (t >= a.T) break;
     const int bcur = t / a.beta, nb = bcur + 1;
     int32_t* orow = a.idx + (prow(a, b, t) * a.Hkv + kvh) * a.top_n;
+    if constexpr (!STREAM) {
+      if (a.dscores != nullptr) {  // diagnostics: the group block scores, 0 past block bcur
+        float* drow = a.dscores + (prow(a, b, t) * a.Hkv + kvh) * nblk;
+        for (int j = lane; j < nblk; j += 64) drow[j] = j <= bcur ? Sb[tq * nblk + j] : 0.f;
+      }
+    }
     if (nb <= a.top_n && !top_p) {
       for (int e = lane; e < a.top_n; e += 64) orow[e] = e < nb ? e : -1;
       continue;

@@ -190,6 +190,23 @@ int nsa_prefill_stages(const nsa_config* cfg, unsigned stages, const void* q, co
                        hipStream_t stream);
 
 /*
+ * nsa_prefill with two diagnostic outputs of the compressed branch and the selection (podcast
+ * notes EP94 sections 5-6), for checking them against a reference:
+ *   lse     fp32 [B, T, Hq] or NULL: ln of sum_i exp(scale q . kc_i) over the row's visible
+ *           compressed tokens (-inf when none is visible)
+ *   scores  fp32 [B, T, Hkv, ceil(T / sel_block)] or NULL: the group block scores the
+ *           selection ranks (sum over the group's heads of each block's share of the
+ *           compressed probabilities), 0 past the row's current block
+ * Every other argument and result as nsa_prefill.  NSA_ERR_UNSUPPORTED when scores is given
+ * and the sequence has more blocks than a query tile's scores can keep in LDS (2048, 1024 at
+ * G = 1: the selection then streams and no score array exists).
+ */
+int nsa_prefill_diag(const nsa_config* cfg, const void* q, const void* k, const void* v,
+                     const void* wk, const void* wv, const float* gate, float* out,
+                     int32_t* sel_idx, float* lse, float* scores, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/*
  * Instrumented nsa_prefill: identical work, plus events[s] recorded on `stream` before stage s
  * and events[NSA_PREFILL_NSTAGES] after the last stage.  Stages: 0 layout (value and weight
  * transposes), 1 block compression of K and V, 2 compressed attention + sliding window + block

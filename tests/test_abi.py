@@ -212,3 +212,18 @@ def test_backward_rejects_before_any_launch(lib):
     a[8] = P(0x1004)
     assert lib.nsa_backward(ctypes.byref(c), *a, 1 << 40, None) == nsa.NSA_ERR_INVALID_ARG
     assert lib.nsa_backward(ctypes.byref(c), *args, 16, None) == nsa.NSA_ERR_WORKSPACE
+
+
+def test_prefill_diag_rejects_before_any_launch(lib):
+    """nsa_prefill_diag: the block scores exist only while a query tile's scores stay in LDS
+    (here 140000 tokens: 2188 blocks, the selection streams), and the diagnostic outputs must be
+    16-byte aligned; both are refused on the host."""
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced
+    args = [fake] * 8
+    long_cfg = nsa.NsaConfig(1, 140000, 1, 16, 128).c()
+    assert lib.nsa_prefill_diag(ctypes.byref(long_cfg), *args, fake, fake, fake, 1 << 40,
+                                None) == nsa.NSA_ERR_UNSUPPORTED
+    c = nsa.NsaConfig(1, 2048, 1, 4, 64).c()
+    assert lib.nsa_prefill_diag(ctypes.byref(c), *args, P(0x1004), None, fake, 1 << 40,
+                                None) == nsa.NSA_ERR_INVALID_ARG

@@ -166,6 +166,75 @@ def test_prefill_64k_sampled_rows():
     compare_prefill(cfg, x, np.zeros_like(rt), rt, gout, gidx, "prefill 64k")
 
 
+DIAG_CASES = [
+    # name, B, T, Hkv, G, D, extra
+    ("G4_D64", 1, 2048, 1, 4, 64, {}),
+    ("G16_D128_B2", 2, 1500, 2, 16, 128, {}),
+    ("G1_D64_cmp48x16", 1, 1800, 2, 1, 64, dict(cmp_len=48, cmp_stride=16)),
+    ("G8_D128_block128", 1, 2100, 1, 8, 128, dict(sel_block=128, top_n=6)),
+]
+
+
+def check_diag(cfg, x, rb, rt, glse, gsc, what):
+    """lse within 1e-5 relative (absolute below 1), block scores within 1e-5 of the group's
+    total importance G, on rows (rb, rt)."""
+    kc = O.compress(x["k"], x["wk"], cfg.cmp_len, cfg.cmp_stride)
+    vc = O.compress(x["v"], x["wv"], cfg.cmp_len, cfg.cmp_stride)
+    ora = O.nsa_prefill_rows(cfg, x["q"], x["k"], x["v"], kc, vc, x["gate"], rb, rt,
+                             branches=True, want_scores=True)
+    ol, os_ = ora["lse"], ora["scores"]
+    none = np.isneginf(ol)
+    assert np.array_equal(np.isneginf(glse), none), "%s: rows without a visible token" % what
+    el = np.abs(glse[~none] - ol[~none]) / np.maximum(1.0, np.abs(ol[~none]))
+    es = np.abs(gsc - os_)
+    assert el.max(initial=0.0) <= 1e-5, "%s: lse rel err %.3g" % (what, el.max())
+    assert es.max() <= 1e-5 * cfg.G, "%s: block score err %.3g" % (what, es.max())
+    print("%s: %d rows, lse max rel err %.2e, block score max err %.2e (G = %d)" % (
+        what, len(rt), el.max(initial=0.0), es.max(), cfg.G), flush=True)
+
+
+@pytest.mark.parametrize("name,B,T,Hkv,G,D,extra", DIAG_CASES, ids=[c[0] for c in DIAG_CASES])
+def test_prefill_diagnostics_lse_and_scores(name, B, T, Hkv, G, D, extra):
+    """The compressed branch's log-sum-exp and the group block scores the selection ranks,
+    exported by nsa_prefill_diag, against the oracle's on every row; the output and indices
+    equal nsa_prefill's bit for bit."""
+    nsa = _nsa()
+    print("case diag", name, flush=True)
+    cfg = O.NsaCfg(B, T, Hkv, G, D, **extra)
+    x = S.nsa_prefill_inputs(60 + len(name), B, T, Hkv, G, D, l=cfg.cmp_len)
+    c = nsa.NsaConfig(B, T, Hkv, G, D, cfg.cmp_len, cfg.cmp_stride, cfg.sel_block, cfg.top_n,
+                      cfg.n_local, cfg.window, cfg.scale, cfg.top_p)
+    d = {k: to_dev(v) for k, v in x.items()}
+    out, idx, lse, sc = nsa.nsa_prefill_diag(c, d["q"], d["k"], d["v"], d["wk"], d["wv"],
+                                              d["gate"])
+    out2, idx2 = nsa.nsa_prefill(c, d["q"], d["k"], d["v"], d["wk"], d["wv"], d["gate"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(idx, idx2)
+    b, t = np.meshgrid(np.arange(B), np.arange(T), indexing="ij")
+    rb, rt = b.ravel().astype(np.int32), t.ravel().astype(np.int32)
+    check_diag(cfg, x, rb, rt, lse.cpu().numpy()[rb, rt], sc.cpu().numpy()[rb, rt], name)
+
+
+def test_prefill_diagnostics_64k_sampled_rows():
+    """The 64k prefill workload's lse and block scores on 1024 sampled rows."""
+    nsa = _nsa()
+    B, T, Hkv, G, D = 1, 65536, 4, 16, 128
+    cfg = O.NsaCfg(B, T, Hkv, G, D)
+    x = S.nsa_prefill_inputs(2, B, T, Hkv, G, D)
+    c = nsa.NsaConfig(B, T, Hkv, G, D)
+    d = {k: to_dev(v) for k, v in x.items()}
+    _, _, lse, sc = nsa.nsa_prefill_diag(c, d["q"], d["k"], d["v"], d["wk"], d["wv"], d["gate"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    rt = np.unique(np.concatenate([np.arange(48), rng.choice(np.arange(48, T), 976,
+                                                             replace=False)])).astype(np.int32)
+    ri = torch.from_numpy(rt.astype(np.int64)).cuda()
+    glse = lse[0].index_select(0, ri).cpu().numpy()
+    gsc = sc[0].index_select(0, ri).cpu().numpy()
+    del d, lse, sc
+    check_diag(cfg, x, np.zeros_like(rt), rt, glse, gsc, "diag 64k")
+
+
 STREAM_CASES = [
     # name, T, Hkv, G, D, extra: more selection blocks than a query tile's block scores can
     # keep in LDS (64 KB / 4 bytes / positions per tile: 2048 blocks for G >= 4, 1024 for

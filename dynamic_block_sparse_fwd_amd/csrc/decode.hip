@@ -1057,7 +1057,7 @@ int decode_chunk_tokens() { return CHUNK; }
 
 // Dynamic LDS of a tile workgroup: the group's queries, its tile list, and one V^T tile per
 // wave (the candidates before, the records' merge after reuse the tiles' space).
-static size_t group_lds(int D) {
+static size_t tile_lds(int D) {
   const size_t tiles = (size_t)kTileWaves * D * 64 * 2;
   const size_t merge = (size_t)kTileWaves * 16 * (D + 4) * 4;
   const size_t cand = (size_t)decode_max_candidates(D) * 8;
@@ -1071,7 +1071,7 @@ static void launch_decode_t(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) 
   auto mark = [&](int i) {
     if (ev != nullptr) (void)hipEventRecord(ev[i], s);
   };
-  const size_t lds = group_lds(D);
+  const size_t lds = tile_lds(D);
   // opt in to the dynamic LDS beyond 64 KB; the attribute is per device, so it is set on every
   // launch
   if (lds > 64 * 1024)

@@ -91,7 +91,7 @@ constexpr int kDecodeMaxList = 256;  // tiles of a group's tile list
 // blocks per selection slice: at most 256, and few enough that the compressed-token tiles the
 // slice's blocks touch fit the slice's 64-tile weight table
 int decode_slice_blocks(int l, int d, int beta);
-// candidates (slices x free blocks) the per-group kernel stages in LDS
+// candidates (slices x free blocks) a tile workgroup stages in LDS
 __host__ __device__ constexpr int decode_max_candidates(int D) { return 4 * D * 64 * 2 / 8; }
 
 // Backward of the prefill layer.

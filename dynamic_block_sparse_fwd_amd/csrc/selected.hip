@@ -128,44 +128,79 @@ __global__ __launch_bounds__(kSlcCountThreads) void slc_count_kernel(PrefillArgs
     a.s_count[((long)c * a.B * a.Hkv + bkv) * a.NTK + i] = cnt[i];
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    v += lane >= o ? u : 0;
+  }
+  return v;
+}
+
 // Exclusive prefix sums of the sub-list lengths and of their kSlcRows-entry tile counts (one
 // workgroup, sub-lists in (chunk, sequence-group, key tile) order), and the sub-list of every
-// work tile.
+// work tile.  4096 consecutive sub-lists per step, four per thread (one 16-byte load; the count
+// is a multiple of kSlcChunks = 16), each step's sums scanned over the waves and added to the
+// running totals of the steps before; the next step's counts are loaded during this one.
 __global__ __launch_bounds__(1024) void slc_scan_kernel(PrefillArgs a) {
-  __shared__ int sc[1024], st[1024];
+  static_assert(kSlcChunks % 4 == 0, "four sub-lists per thread");
+  __shared__ int wc[16], wt[16];
+  __shared__ int carry_c, carry_t;
   const long n = (long)kSlcChunks * a.B * a.Hkv * a.NTK;
-  const long per = (n + 1023) / 1024;
-  const long lo = threadIdx.x * per, hi = lo + per < n ? lo + per : n;
-  int c = 0, tl = 0;
-  for (long e = lo; e < hi; ++e) {
-    const int v = a.s_count[e];
-    c += v;
-    tl += (v + kSlcRows - 1) / kSlcRows;
+  const long n4 = n / 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int4* cnt4 = reinterpret_cast<const int4*>(a.s_count);
+  if (tid == 0) {
+    carry_c = 0;
+    carry_t = 0;
   }
-  sc[threadIdx.x] = c;
-  st[threadIdx.x] = tl;
+  int4 v_next = cnt4[tid < n4 ? tid : n4 - 1];  // every load unconditional (index clamped)
+  for (long base = 0; base < n4; base += 1024) {
+    const long q = base + tid;  // this thread's sub-lists 4 q .. 4 q + 3
+    const bool live = q < n4;
+    const int4 v4 = v_next;
+    const long qn = base + 1024 + tid;
+    v_next = cnt4[qn < n4 ? qn : n4 - 1];
+    const int v[4] = {live ? v4.x : 0, live ? v4.y : 0, live ? v4.z : 0, live ? v4.w : 0};
+    int nt[4], sv = 0, st = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      nt[i] = (v[i] + kSlcRows - 1) / kSlcRows;
+      sv += v[i];
+      st += nt[i];
+    }
+    const int ic = wave_incl_scan(sv, lane), it = wave_incl_scan(st, lane);
+    if (lane == 63) {
+      wc[wave] = ic;
+      wt[wave] = it;
+    }
+    __syncthreads();  // the wave totals (and the carries of the step before) are posted
+    int co = carry_c + ic - sv, to = carry_t + it - st;  // exclusive
+    for (int w = 0; w < wave; ++w) {
+      co += wc[w];
+      to += wt[w];
+    }
+    if (live) {
+      const int4 o4 = {co, co + v[0], co + v[0] + v[1], co + v[0] + v[1] + v[2]};
+      const int4 t4 = {to, to + nt[0], to + nt[0] + nt[1], to + nt[0] + nt[1] + nt[2]};
+      reinterpret_cast<int4*>(a.s_offset)[q] = o4;
+      reinterpret_cast<int4*>(a.s_tstart)[q] = t4;
+      int tt = to;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        for (int k = 0; k < nt[i]; ++k) a.s_tile_entry[tt++] = (int)(4 * q + i);
+    }
+    __syncthreads();  // every thread has read wc, wt and the carries
+    if (tid == 1023) {  // its inclusive sums close the step (0 past the end)
+      carry_c = co + sv;
+      carry_t = to + st;
+    }
+  }
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int vc = threadIdx.x >= o ? sc[threadIdx.x - o] : 0;
-    const int vt = threadIdx.x >= o ? st[threadIdx.x - o] : 0;
-    __syncthreads();
-    sc[threadIdx.x] += vc;
-    st[threadIdx.x] += vt;
-    __syncthreads();
-  }
-  int co = sc[threadIdx.x] - c, to = st[threadIdx.x] - tl;  // exclusive
-  for (long e = lo; e < hi; ++e) {
-    const int v = a.s_count[e];
-    a.s_offset[e] = co;
-    a.s_tstart[e] = to;
-    const int nt = (v + kSlcRows - 1) / kSlcRows;
-    for (int k = 0; k < nt; ++k) a.s_tile_entry[to + k] = (int)e;
-    co += v;
-    to += nt;
-  }
-  if (threadIdx.x == 1023) {
-    a.s_ntiles[0] = st[1023];
-    a.s_offset[n] = sc[1023];
+  if (tid == 0) {
+    a.s_ntiles[0] = carry_t;
+    a.s_offset[n] = carry_c;
   }
 }
 

@@ -1004,6 +1004,17 @@ __global__ __launch_bounds__(256) void dec_merge_kernel(DecodeArgs a) {
   const long bkv = (long)b * a.Hkv + kvh;
   const float* recs = a.grec + bkv * a.NG * 2 * RS;
   const int tid = threadIdx.x;
+  // the compressed output and the gates do not depend on the weights: loaded first
+  float oc[PT], g3[PT][3];
+#pragma unroll
+  for (int q = 0; q < PT; ++q) {
+    const int pr = tid + 256 * q, h = pr / D, dd = pr % D;
+    const int hc = h < a.G ? h : 0;  // rows past G read head 0 (in bounds) and write nothing
+    const long head = (long)b * a.Hkv * a.G + kvh * a.G + hc;
+    oc[q] = a.ocmp[(bkv * 16 + h) * D + dd];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) g3[q][c] = a.gate[head * 3 + c];
+  }
   if (tid < 32) {
     const int br = tid >> 4, h = tid & 15;
     float m[kMergeMaxNG];
@@ -1045,9 +1056,7 @@ __global__ __launch_bounds__(256) void dec_merge_kernel(DecodeArgs a) {
     const int pr = tid + 256 * q, h = pr / D, dd = pr % D;
     if (h >= a.G) continue;
     const long head = (long)b * a.Hkv * a.G + kvh * a.G + h;
-    const float* g = a.gate + head * 3;
-    a.out[head * D + dd] = g[0] * a.ocmp[(bkv * 16 + h) * D + dd] + g[1] * acc[q][0] +
-                           g[2] * acc[q][1];
+    a.out[head * D + dd] = g3[q][0] * oc[q] + g3[q][1] * acc[q][0] + g3[q][2] * acc[q][1];
   }
 }
 

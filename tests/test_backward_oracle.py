@@ -30,7 +30,9 @@ def setup(seed=51, B=1, T=200, Hkv=2, G=2, D=16, **kw):
 
 
 def test_forward_equals_c_oracle():
-    for kw in ({}, dict(top_n=4, n_local=1, window=50), dict(sel_block=128, top_n=3)):
+    for kw in ({}, dict(top_n=4, n_local=1, window=50), dict(sel_block=128, top_n=3),
+               dict(cmp_len=16, cmp_stride=16), dict(cmp_len=48, cmp_stride=16),
+               dict(cmp_len=64, cmp_stride=32)):
         cfg, x, idx, ref = setup(T=300, **kw)
         f = NB.inputs_f64(x)
         out = NB.forward(cfg, f["q"], f["k"], f["v"], f["wk"], f["wv"], f["gate"], idx)
@@ -56,6 +58,31 @@ def test_gradients_match_finite_differences(name):
     fd = (loss(eps) - loss(-eps)) / (2 * eps)
     an = float(np.sum(g * u))
     assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+@pytest.mark.parametrize("l,d", [(16, 16), (48, 16), (64, 32)])
+def test_generic_compressor_gradients_match_finite_differences(l, d):
+    """Compressor geometries other than l = 2 d (l = d, l = 3 d, l = 2 d with d = 32): every
+    gradient against a central finite difference along a random direction, as above."""
+    cfg, x, idx, _ = setup(seed=54 + l + d, T=160, G=2, D=16, top_n=4, n_local=1, window=40,
+                           cmp_len=l, cmp_stride=d)
+    f = NB.inputs_f64(x)
+    dout = S.upstream_grad(55, f["q"].shape).astype(np.float64)
+    grads = NB.backward(cfg, f["q"], f["k"], f["v"], f["wk"], f["wv"], f["gate"], idx, dout,
+                        round_cmp=False)
+    for i, name in enumerate(["q", "k", "v", "wk", "wv", "gate"]):
+        u = np.random.default_rng(56 + i).standard_normal(f[name].shape)
+        eps = 1e-5
+
+        def loss(delta):
+            ff = dict(f)
+            ff[name] = f[name] + delta * u
+            return float(np.sum(dout * NB.forward(cfg, ff["q"], ff["k"], ff["v"], ff["wk"],
+                                                  ff["wv"], ff["gate"], idx, round_cmp=False)))
+
+        fd = (loss(eps) - loss(-eps)) / (2 * eps)
+        an = float(np.sum(grads["d" + name] * u))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (l, d, name, fd, an)
 
 
 def sdpa_grads(q, k, v, dout, scale, window=None):

@@ -65,6 +65,10 @@ CASES = [
     # peaked attention (queries scaled by 4): the running maxima move often and p is nearly
     # one-hot
     ("peaked_q4_T600_D64", 1, 600, 2, 64, dict(q_scale=4.0)),
+    # compressor geometries other than l = 2 d (the generic importance and compression paths)
+    ("cmp16x16_G4_T600_D64", 1, 600, 2, 64, dict(G=4, cmp_len=16, cmp_stride=16)),
+    ("cmp48x16_T650_D128", 1, 650, 1, 128, dict(cmp_len=48, cmp_stride=16)),
+    ("cmp64x32_G8_T700_D64", 1, 700, 2, 64, dict(G=8, cmp_len=64, cmp_stride=32)),
 ]
 
 
@@ -82,7 +86,7 @@ def test_backward_parity(name, B, T, Hkv, D, extra):
     G = extra.pop("G", 16)
     v_offset, q_scale = extra.pop("v_offset", 0.0), extra.pop("q_scale", 1.0)
     ocfg = O.NsaCfg(B, T, Hkv, G, D, **extra)
-    x = S.nsa_prefill_inputs(91 + len(name), B, T, Hkv, G, D)
+    x = S.nsa_prefill_inputs(91 + len(name), B, T, Hkv, G, D, l=ocfg.cmp_len)
     if v_offset:
         x["v"] = shifted_bf16(x["v"], offset=v_offset)
     if q_scale != 1.0:

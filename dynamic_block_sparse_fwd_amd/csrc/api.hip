@@ -164,6 +164,7 @@ MobaPlan plan_moba(const moba_config* c) {
 struct PrefillPlan {
   size_t vt, kc, vct, wkt, wvt, idx, total;
   size_t s_rank, s_kt, s_count, s_offset, s_tstart, s_ntiles, s_tile_entry, s_list, s_po, s_ps;
+  size_t kpmax, kcmax;
   int ncmp, NCP, TP, nblk, FS, NTK, s_max_tiles;
 };
 
@@ -181,6 +182,8 @@ PrefillPlan plan_prefill(const nsa_config* c) {
   p.wkt = off; off += align_up((size_t)c->cmp_len * c->D * c->D * 2);
   p.wvt = off; off += align_up((size_t)c->cmp_len * c->D * c->D * 2);
   p.idx = off; off += align_up((size_t)c->B * c->T * c->Hkv * c->top_n * 4);
+  p.kpmax = off; off += align_up((size_t)BH * p.NCP * 4);
+  p.kcmax = off; off += align_up((size_t)BH * ((p.ncmp + kNormRows - 1) / kNormRows + 1) * 4);
   // selected branch, block-major part: sized for query rows 0 .. T-1
   p.FS = c->top_n * (c->sel_block / 64);
   p.NTK = p.TP / 64;
@@ -202,6 +205,9 @@ PrefillPlan plan_prefill(const nsa_config* c) {
 }
 
 void set_selected_ws(PrefillArgs& a, const PrefillPlan& p, char* base) {
+  a.kpmax = reinterpret_cast<float*>(base + p.kpmax);
+  a.kcmax = reinterpret_cast<float*>(base + p.kcmax);
+  a.NKB = (a.ncmp + kNormRows - 1) / kNormRows;  // a.ncmp is set before this call
   a.s_rank = reinterpret_cast<int32_t*>(base + p.s_rank);
   a.s_kt = reinterpret_cast<int32_t*>(base + p.s_kt);
   a.s_count = reinterpret_cast<int32_t*>(base + p.s_count);

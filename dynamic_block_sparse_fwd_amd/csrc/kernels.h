@@ -27,6 +27,12 @@ struct PrefillArgs {
   float* dlse;          // nullable [B, nq, Hq]: ln of the compressed branch's softmax sum
   float* dscores;       // nullable [B, nq, Hkv, nblk]: group block scores (block scores kept in
                         // LDS only)
+  // Squared norms of the compressed keys as running maxima (workspace), from which the
+  // compressed attention bounds a row's scores: kpmax[j] = max |k_i|^2 over the rows i <= j of
+  // j's kNormRows-row chunk, kcmax[c] = the maximum over chunk c.
+  float* kpmax;         // [B*Hkv, NCP]
+  float* kcmax;         // [B*Hkv, NKB]
+  int NKB;              // chunks of the visible compressed keys: ceil(ncmp / kNormRows)
   // Selected branch, block-major part (workspace).  An "entry" is one selected 64-key tile of one
   // (row, group) that is not among the tiles the selected kernel shares per eight positions;
   // row = b * nq + (t - q0), free slot fs = its rank among the row's such tiles (< FS).
@@ -43,6 +49,7 @@ struct PrefillArgs {
   int FS, NTK, s_max_tiles;
 };
 
+constexpr int kNormRows = 256;  // compressed-key rows per chunk of the norm maxima
 constexpr int kSlcChunks = 16;  // T-chunks of the block-major lists (work tiles chunk-major)
 constexpr int kSlcRows = 32;   // positions per block-major work tile
 

@@ -118,6 +118,46 @@ __device__ __forceinline__ void stream_offer(const PrefillArgs& a, int t, uint64
 // slot j mod kRing.
 constexpr int kRing = 128;
 
+// Squared norms of the compressed keys of one (sequence, KV group) as running maxima within
+// kNormRows-row chunks (kpmax) and per chunk (kcmax): one row per thread, the chunk's prefix a
+// wave scan plus the maxima of the waves before.  Rows at or past ncmp count as zero.  The sums
+// run in a fixed order, so a row's entry depends on the rows up to it only.
+__global__ __launch_bounds__(kNormRows) void kc_norm_kernel(PrefillArgs a) {
+  __shared__ float wmax[kNormRows / 64];
+  const int c = blockIdx.x;
+  const long bkv = (long)blockIdx.z * a.Hkv + blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = c * kNormRows + tid;
+  float sq = 0.f;
+  if (j < a.ncmp) {
+    const u32x4* row = reinterpret_cast<const u32x4*>(a.kc + (bkv * a.NCP + j) * a.D);
+    for (int e = 0; e < a.D / 8; ++e) {
+      const u32x4 w = row[e];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float lo = __uint_as_float(w[h] << 16), hi = __uint_as_float(w[h] & 0xFFFF0000u);
+        sq = fmaf(lo, lo, sq);
+        sq = fmaf(hi, hi, sq);
+      }
+    }
+  }
+  float incl = sq;  // maximum over the wave's rows up to this one
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float u = __shfl_up(incl, o);
+    if (lane >= o) incl = fmaxf(incl, u);
+  }
+  if (lane == 63) wmax[wave] = incl;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) incl = fmaxf(incl, wmax[w]);
+  if (j < a.ncmp) a.kpmax[bkv * a.NCP + j] = incl;
+  if (tid == 0) {
+    float m = wmax[0];
+    for (int w = 1; w < kNormRows / 64; ++w) m = fmaxf(m, wmax[w]);
+    a.kcmax[bkv * a.NKB + c] = m;
+  }
+}
+
 template <int D, int G, bool FAST, bool STREAM>
 __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select_kernel(PrefillArgs a) {
   using QT = QTile<G>;
@@ -170,24 +210,51 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
   if (threadIdx.x < TQ) Pc[threadIdx.x] = 0.f;
   int jemit = 0;  // streaming, generic path: blocks below jemit are final and offered
 
-  // Pass 1: per-row max and sum of exp2 (per lane; merged over the row's four lanes below).
-  float mrun[RTW], lrun[RTW];
+  // Pass 1: the row log-sum-exp of the compressed scores.  Every scaled score z sl of a row is at
+  // most U = |sl| |q| max |k_c| over the compressed keys the tile sees (Cauchy-Schwarz; the
+  // factor 1 + 2^-10 covers the fp32 rounding of the norms and of the products' sums), so the
+  // row sum of exp2(z sl - U) needs no running maximum.  A row whose sum falls below 2^-60 (a
+  // bound loose by more than 60 in log2 units, or non-finite values) sends the workgroup
+  // through the running-maximum form instead.  U depends only on the keys the tile sees, so a
+  // chunked prefill takes the same path, bit for bit, as the whole sequence.
+  float U[RTW];
+  {
+    float km = 0.f;
+    if (nvis_max > 0) {  // uniform
+      const int jl = nvis_max - 1, cl = jl / kNormRows;
+      km = a.kpmax[bkv * a.NCP + jl];
+      for (int i = lane; i < cl; i += 64) km = fmaxf(km, a.kcmax[bkv * a.NKB + i]);
+      km = wave_max_f(km);
+    }
 #pragma unroll
-  for (int rt = 0; rt < RTW; ++rt) { mrun[rt] = kNegInf; lrun[rt] = 0.f; }
+    for (int rt = 0; rt < RTW; ++rt) {
+      float qn = 0.f;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = (float)qf[rt][c][e];
+          qn = fmaf(x, x, qn);
+        }
+      U[rt] = fabsf(sl) * sqrtf(col_sum4(qn) * km) * (1.f + 0x1p-10f);
+    }
+  }
+  float lsum[RTW];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) lsum[rt] = 0.f;
   KTileRegs<D, NT> kr;
   VTileRegs<D, NT> vr;
-  if (nkt > 0) kr.load(kc, 0, a.NCP - 1);
-  for (int kt = 0; kt < nkt; ++kt) {
+  // the compressed keys' scores of one 64-key tile (keys past a row's visible count at -inf)
+  auto tile_scores = [&](int kt, float (*raw)[16]) {
     __syncthreads();
     kr.store(Ks);
     __syncthreads();
     if (kt + 1 < nkt) kr.load(kc, (long)(kt + 1) * 64, a.NCP - 1);
     const bool full = (kt + 1) * 64 <= nvis_lo;
-    float raw[RTW][16];
     score_tiles<D, RTW>(Ks, qf, g4, r16, raw);
+    if (!full) {  // a real (uniform) branch: full tiles skip the masking arithmetic
 #pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
-      if (!full) {  // a real (uniform) branch: full tiles skip the masking arithmetic
+      for (int rt = 0; rt < RTW; ++rt) {
         __asm__ volatile("" ::: "memory");
         // key kt*64 + 32*(e>>3) + 8*g4 + (e&7) is visible iff its offset from the lane's first
         // key is below lim (one subtraction per lane, constant offsets per element)
@@ -196,33 +263,70 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
         for (int e = 0; e < 16; ++e)
           raw[rt][e] = 32 * (e >> 3) + (e & 7) < lim ? raw[rt][e] : kNegInf;
       }
-      float tm = raw[rt][0];
+    }
+  };
+  if (nkt > 0) kr.load(kc, 0, a.NCP - 1);
+  for (int kt = 0; kt < nkt; ++kt) {
+    float raw[RTW][16];
+    tile_scores(kt, raw);
 #pragma unroll
-      for (int e = 1; e < 16; ++e) tm = fmaxf(tm, raw[rt][e]);
-      const float mn = fmaxf(mrun[rt], tm);
-      if (mn != kNegInf) {
-        const float msl = mn * sl;
-        float sum = 0.f;
+    for (int rt = 0; rt < RTW; ++rt) {
+      float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sum += fast_exp2(fmaf(raw[rt][e], sl, -msl));
-        lrun[rt] = lrun[rt] * fast_exp2(fmaf(mrun[rt], sl, -msl)) + sum;
-        mrun[rt] = mn;
-      }
+      for (int e = 0; e < 16; ++e) sum += fast_exp2(fmaf(raw[rt][e], sl, -U[rt]));
+      lsum[rt] += sum;
     }
   }
   // Row log-sum-exp (scaled, log2 units): pass 2 computes the normalised probabilities
   // p = exp2(z - lse) directly, for the block importance (fp32) and the P V product (bf16).
   float rlse[RTW];
+  bool vis[RTW];  // the row sees a compressed key (else p is masked to 0)
+  int loose = 0;
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt) {
-    const float M = col_max4(mrun[rt]);
-    const float part = (mrun[rt] == kNegInf) ? 0.f : lrun[rt] * fast_exp2((mrun[rt] - M) * sl);
-    const float L = col_sum4(part);
-    rlse[rt] = (M == kNegInf) ? 0.f : M * sl + __log2f(L);  // no visible key: p masked to 0
+    const float L = col_sum4(lsum[rt]);
+    vis[rt] = nvis[rt] > 0;
+    rlse[rt] = vis[rt] ? U[rt] + __log2f(L) : 0.f;
+    if (vis[rt] && !(L >= 0x1p-60f)) loose = 1;
+  }
+  if (__syncthreads_or(loose)) {  // uniform: the running-maximum form (per lane, then per row)
+    float mrun[RTW], lrun[RTW];
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) { mrun[rt] = kNegInf; lrun[rt] = 0.f; }
+    if (nkt > 0) kr.load(kc, 0, a.NCP - 1);
+    for (int kt = 0; kt < nkt; ++kt) {
+      float raw[RTW][16];
+      tile_scores(kt, raw);
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt) {
+        float tm = raw[rt][0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) tm = fmaxf(tm, raw[rt][e]);
+        const float mn = fmaxf(mrun[rt], tm);
+        if (mn != kNegInf) {
+          const float msl = mn * sl;
+          float sum = 0.f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sum += fast_exp2(fmaf(raw[rt][e], sl, -msl));
+          lrun[rt] = lrun[rt] * fast_exp2(fmaf(mrun[rt], sl, -msl)) + sum;
+          mrun[rt] = mn;
+        }
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const float M = col_max4(mrun[rt]);
+      const float part = (mrun[rt] == kNegInf) ? 0.f : lrun[rt] * fast_exp2((mrun[rt] - M) * sl);
+      const float L = col_sum4(part);
+      vis[rt] = M != kNegInf;
+      rlse[rt] = vis[rt] ? M * sl + __log2f(L) : 0.f;
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt)
     if (a.dlse != nullptr && g4 == 0 && row_t[rt] < a.T)  // diagnostics: natural-log lse
       a.dlse[prow(a, b, row_t[rt]) * (a.Hkv * G) + row_h[rt]] =
-          M == kNegInf ? kNegInf : rlse[rt] * 0.6931471805599453f;
-  }
+          vis[rt] ? rlse[rt] * 0.6931471805599453f : kNegInf;
 
   f32x4 O[RTW][DT];
 #pragma unroll
@@ -763,7 +867,10 @@ static void dispatch(const PrefillArgs& a, int which, hipStream_t s) {
   else dispatch_g<64>(a, which, s);
 }
 
-void launch_cmp_select(const PrefillArgs& a, hipStream_t s) { dispatch(a, 0, s); }
+void launch_cmp_select(const PrefillArgs& a, hipStream_t s) {
+  if (a.ncmp > 0) kc_norm_kernel<<<dim3(a.NKB, a.Hkv, a.B), kNormRows, 0, s>>>(a);
+  dispatch(a, 0, s);
+}
 void launch_window(const PrefillArgs& a, hipStream_t s) { dispatch(a, 1, s); }
 
 }  // namespace nsa

@@ -143,6 +143,24 @@ def test_prefill_zero_query_ties_bit_exact():
     check_close(gout[0], ora["out"], "zero-q")
 
 
+@pytest.mark.parametrize("G,D", [(16, 128), (4, 64)])
+def test_prefill_loose_score_bound(G, D):
+    """Keys 512 .. 639 scaled by 16 (exact in bf16): a query tile that sees their compressed
+    tokens bounds its scores by |q| times their norm, more than 60 (log2 units) above its actual
+    maximum, so the compressed attention's first pass takes its running-maximum form there,
+    while the tiles before them keep the bounded form.  Every row against the oracle."""
+    T = 1500
+    print("case loose bound G%d D%d" % (G, D), flush=True)
+    cfg = O.NsaCfg(1, T, 2, G, D)
+    x = S.nsa_prefill_inputs(21 + G, 1, T, 2, G, D)
+    k = S.bf16_bits_to_f32(x["k"]).astype(np.float64)
+    k[:, :, 512:640] *= 16.0
+    x["k"] = S.f32_to_bf16_bits(k.astype(np.float32))
+    gout, gidx = run_gpu_prefill(cfg, x)
+    rb, rt = all_rows(cfg)
+    compare_prefill(cfg, x, rb, rt, gout, gidx, "loose bound G%d D%d" % (G, D))
+
+
 def test_prefill_deterministic():
     cfg = O.NsaCfg(1, 3000, 2, 16, 128)
     x = S.nsa_prefill_inputs(9, 1, 3000, 2, 16, 128)

@@ -224,8 +224,9 @@ void set_selected_ws(PrefillArgs& a, const PrefillPlan& p, char* base) {
 }
 
 struct BackwardPlan {
-  size_t kt, kc, kct, vc, wkt, wvt, dob, dot, qt, lse, dlt, pk, pv, dkc, dvc, psk, psv, total;
-  int ncmp, NCP, TP, nblk, PC, NPC;
+  size_t kt, kc, kct, vc, wkt, wvt, dob, dot, qt, lse, dlt, pk, pv, dkc, dvc, psk, psv, sbits;
+  size_t total;
+  int ncmp, NCP, TP, nblk, PC, NPC, SW;
 };
 
 BackwardPlan plan_backward(const nsa_config* c) {
@@ -259,6 +260,8 @@ BackwardPlan plan_backward(const nsa_config* c) {
   p.dvc = off; off += align_up(cmpn * 4);
   p.psk = off; off += align_up((size_t)p.NPC * BH * c->T * c->D * 4);
   p.psv = off; off += align_up((size_t)p.NPC * BH * c->T * c->D * 4);
+  p.SW = (c->T + 31) / 32;
+  p.sbits = off; off += align_up(BH * p.nblk * p.SW * 4);
   p.total = off;
   return p;
 }
@@ -651,6 +654,8 @@ static int backward_impl(const nsa_config* c, const void* q, const void* k, cons
   a.dob = u16p(p.dob); a.dot = u16p(p.dot); a.qt = u16p(p.qt);
   a.lse = f32p(p.lse); a.dlt = f32p(p.dlt); a.pk = f32p(p.pk); a.pv = f32p(p.pv);
   a.dkc = f32p(p.dkc); a.dvc = f32p(p.dvc); a.psk = f32p(p.psk); a.psv = f32p(p.psv);
+  a.selbits = reinterpret_cast<uint32_t*>(base + p.sbits);
+  a.SW = p.SW;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dwk = dwk; a.dwv = dwv; a.dgate = dgate;
   a.B = c->B; a.T = c->T; a.Hkv = c->Hkv; a.G = c->G; a.D = c->D;
   a.l = c->cmp_len; a.d = c->cmp_stride;

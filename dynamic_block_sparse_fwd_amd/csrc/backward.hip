@@ -16,11 +16,12 @@
 //                  the positions that see the tile, two positions (32 rows) per step staged in
 //                  LDS, dV += (g P)^T dO and dK += scale * dS^T q;
 // the compressed branch's key gradients then go back through the compressor
-// (bwd_cmp_dx_kernel: dK, dV; bwd_cmp_dw_kernel: dWk, dWv).  No atomics: every output element
-// has one writer per launch and launches that add to the same output run in order.  The
-// compressed and selected key-major passes split the positions into chunks that write fp32
-// partials of their own; a reduction adds the chunks in chunk order, so two calls on the same
-// inputs give the same bits.  dO enters the matrix core in bf16; q and dO are also kept with
+// (bwd_cmp_dx_kernel: dK, dV; bwd_cmp_dw_kernel: dWk, dWv).  No floating-point atomics: every
+// output element has one writer per launch and launches that add to the same output run in
+// order.  The compressed and selected key-major passes split the positions into chunks that
+// write fp32 partials of their own; a reduction adds the chunks in chunk order, so two calls on
+// the same inputs give the same bits.  The selected pass takes a tile's positions, ascending,
+// from a bitmap of the selection (bwd_selbits_kernel, built with an order-free atomic OR).  dO enters the matrix core in bf16; q and dO are also kept with
 // the 16 rows of a (position, group) contiguous per feature (the B operand of the key-major
 // products).
 #include "attn_tile.h"
@@ -123,6 +124,23 @@ struct OnlineDq {
 
 // dO -> bf16 rows; q and dO with the G heads of a (position, group) contiguous per feature,
 // zero in the 16 - G pad rows.
+// The selection as a bitmap: bit t of row (sequence, group, block j) is set when position t's
+// index row holds j (repeats, holes and blocks out of range ignored).  OR is order-free, so the
+// bitmap is the same on every call; the selected key-major pass reads its positions from it.
+__global__ __launch_bounds__(256) void bwd_selbits_kernel(BwdArgs a) {
+  const long id = (long)blockIdx.x * 256 + threadIdx.x;  // (b * T + t) * Hkv + g
+  if (id >= (long)a.B * a.T * a.Hkv) return;
+  const int g = (int)(id % a.Hkv);
+  const long bt = id / a.Hkv;
+  const int t = (int)(bt % a.T), b = (int)(bt / a.T);
+  const int32_t* ir = a.idx + id * a.top_n;
+  uint32_t* rows = a.selbits + ((long)b * a.Hkv + g) * a.nblk * a.SW + (t >> 5);
+  for (int e = 0; e < a.top_n; ++e) {
+    const int j = ir[e];
+    if (j >= 0 && j < a.nblk) atomicOr(&rows[(long)j * a.SW], 1u << (t & 31));
+  }
+}
+
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   const long e = (long)blockIdx.x * 256 + threadIdx.x;
   const long n = (long)a.B * a.T * a.Hkv * a.D;
@@ -441,8 +459,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(BwdArgs a) {
   constexpr int DC = D / 32, DT = D / 16, NT = NW * 64;
   constexpr int NCH = 16 * D / NT;  // 16-byte chunks per thread per pair (4 arrays of 4D)
   __shared__ PairStage<D> st;
-  __shared__ int plist[256];
-  __shared__ int wcount[4];
+  __shared__ int plist[BR == kBrSlc ? 64 * 32 : 1];
+  __shared__ int ptot;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4, r16 = lane & 15;
   const int kb = blockIdx.x * 16 * NW;
@@ -611,36 +629,43 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(BwdArgs a) {
       y = x + 1 <= t1 ? x + 1 : -1;
     });
   } else {
-    // positions of chunk blockIdx.z at or after kb whose group selected the block of this
-    // tile, gathered 256 at a time (block 0 is selected by every position: without the chunks
-    // its tile alone would walk the whole sequence)
+    // positions of chunk blockIdx.z at or after kb whose group selected the block of this tile
+    // (block 0 is selected by every position: without the chunks its tile alone would walk the
+    // whole sequence), read from the selection bitmap 64 words (2048 positions) at a time: the
+    // first wave turns its words into the ascending list of their set bits
     const int jb = kb / a.beta;
     const int c_lo = (int)blockIdx.z * a.PC > kb ? (int)blockIdx.z * a.PC : kb;
     const int c_hi = ((int)blockIdx.z + 1) * a.PC < a.T ? ((int)blockIdx.z + 1) * a.PC : a.T;
     if (c_lo >= c_hi) return;  // uniform: no position of this chunk sees the tile
-    for (int c0 = c_lo; c0 < c_hi; c0 += 256) {
-      const int t = c0 + tid;
-      bool sel = false;
-      if (t < c_hi) {
-        const int32_t* ir = a.idx + (((long)b * a.T + t) * a.Hkv + g) * a.top_n;
-        for (int e = 0; e < a.top_n; ++e) sel |= ir[e] == jb;
-      }
-      const uint64_t bal = __ballot(sel);
-      if (lane == 0) wcount[wave] = (int)__popcll(bal);
-      __syncthreads();
-      int off = 0, tot = 0;
+    // c_lo is a multiple of 64 (PC and kb are), so every word starts inside the chunk
+    const uint32_t* bits = a.selbits + ((long)bg * a.nblk + jb) * a.SW;
+    for (int p0 = c_lo; p0 < c_hi; p0 += 64 * 32) {
+      if (wave == 0) {
+        const int p = p0 + 32 * lane;  // this lane's word covers positions p .. p + 31
+        uint32_t word = p < c_hi ? bits[p >> 5] : 0u;
+        const int keep = c_hi - p;  // positions of the word inside the chunk
+        if (keep < 32) word &= keep > 0 ? (1u << keep) - 1u : 0u;
+        const int n = __popc(word);
+        int incl = n;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        off += w < wave ? wcount[w] : 0;
-        tot += wcount[w];
+        for (int o = 1; o < 64; o <<= 1) {
+          const int u = __shfl_up(incl, o);
+          incl += lane >= o ? u : 0;
+        }
+        int at = incl - n;
+        while (word != 0u) {
+          plist[at++] = p + (__ffs(word) - 1);
+          word &= word - 1u;
+        }
+        if (lane == 63) ptot = incl;
       }
-      if (sel) plist[off + (int)__popcll(bal & ((1ull << lane) - 1ull))] = t;
       __syncthreads();
+      const int tot = ptot;
       run((tot + 1) / 2, [&](int e, int& x, int& y) {
         x = plist[2 * e];
         y = 2 * e + 1 < tot ? plist[2 * e + 1] : -1;
       });
-      __syncthreads();  // plist and wcount are rewritten by the next round
+      __syncthreads();  // plist and ptot are rewritten by the next round
     }
   }
 
@@ -827,6 +852,9 @@ static void launch_bwd_d(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) {
   };
   const long nprep = (long)a.B * a.T * a.Hkv * D;
   bwd_prep_kernel<<<(unsigned)((nprep + 255) / 256), 256, 0, s>>>(a);
+  launch_fill_zero(reinterpret_cast<float*>(a.selbits), (size_t)a.B * a.Hkv * a.nblk * a.SW, s);
+  const long nsel = (long)a.B * a.T * a.Hkv;
+  bwd_selbits_kernel<<<(unsigned)((nsel + 255) / 256), 256, 0, s>>>(a);
   mark(2);
   const dim3 gq((a.T + 3) / 4, a.Hkv, a.B);
   const dim3 gq8((a.T + 7) / 8, a.Hkv, a.B);

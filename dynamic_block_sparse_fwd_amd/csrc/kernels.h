@@ -128,6 +128,7 @@ struct BwdArgs {
   float* dvc;             // [B*Hkv, NCP, D]
   float* psk;             // [NPC, B*Hkv, T, D] selected-branch key gradient, per position chunk
   float* psv;             // [NPC, B*Hkv, T, D] selected-branch value gradient, the same
+  uint32_t* selbits;      // [B*Hkv, nblk, SW] bit t of row (group, block): position t selected it
   // outputs
   float* dq;              // [B, T, Hq, D]
   float* dk;              // [B, Hkv, T, D]
@@ -137,6 +138,7 @@ struct BwdArgs {
   float* dgate;           // [B, T, Hq, 3]
   int B, T, Hkv, G, D, l, d, beta, top_n, window;
   int ncmp, NCP, TP, nblk, PC, NPC;  // PC positions per chunk of the key-major passes
+  int SW;                            // 32-bit words per bitmap row: ceil(T / 32)
   float scale, scale_log2;
 };
 

@@ -347,10 +347,11 @@ int nsa_prefill_chunk(const nsa_config* cfg, int32_t P, int32_t C, const void* q
  *   ws       at least nsa_backward_workspace_bytes(cfg) bytes
  * Matrix-core operands are bf16 (q, k, v, the compressed tokens as given; dout, the
  * probabilities and the score gradients rounded to bf16), accumulation fp32.  Checks as
- * nsa_prefill (every G it accepts).  Deterministic: no atomics; key gradients that several
- * position chunks contribute to are summed in a fixed chunk order, so two calls on the same
- * inputs give the same bits.  The workspace holds two fp32 [chunks, B, Hkv, T, D] partial
- * arrays (about 16 chunks): 4.3 GB at B = 1, T = 65536, Hkv = 4, D = 128.
+ * nsa_prefill (every G it accepts).  Deterministic: no floating-point atomics; key gradients
+ * that several position chunks contribute to are summed in a fixed chunk order, so two calls
+ * on the same inputs give the same bits.  The workspace holds two fp32 [chunks, B, Hkv, T, D]
+ * partial arrays (about 16 chunks) and a bitmap of the selection (one bit per position and
+ * block): 4.3 GB at B = 1, T = 65536, Hkv = 4, D = 128.
  */
 size_t nsa_backward_workspace_bytes(const nsa_config* cfg);
 int nsa_backward(const nsa_config* cfg, const void* q, const void* k, const void* v,

@@ -1,4 +1,6 @@
 // NSA prefill kernels ("Zhang Xiaojun podcast EP94 notes", sections 5 and 6):
+//   kc_norm_kernel:    maxima of the compressed keys' squared norms (the score bound of the
+//                      compressed attention's first pass);
 //   cmp_select_kernel: compressed attention + block importance + group top-n selection;
 //   window_kernel:     sliding-window attention (when run as a stage of its own).
 // The selected-block branch is in selected.hip.  The gate mix is folded into the output
@@ -214,8 +216,8 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
   // most U = |sl| |q| max |k_c| over the compressed keys the tile sees (Cauchy-Schwarz; the
   // factor 1 + 2^-10 covers the fp32 rounding of the norms and of the products' sums), so the
   // row sum of exp2(z sl - U) needs no running maximum.  A row whose sum falls below 2^-60 (a
-  // bound loose by more than 60 in log2 units, or non-finite values) sends the workgroup
-  // through the running-maximum form instead.  U depends only on the keys the tile sees, so a
+  // bound loose by more than 60 in log2 units) or is not finite and at most 2^100 sends the
+  // workgroup through the running-maximum form instead.  U depends only on the keys the tile sees, so a
   // chunked prefill takes the same path, bit for bit, as the whole sequence.
   float U[RTW];
   {
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(QTile<G>::NW * 64, G == 16 ? 2 : 1) void cmp_select
     const float L = col_sum4(lsum[rt]);
     vis[rt] = nvis[rt] > 0;
     rlse[rt] = vis[rt] ? U[rt] + __log2f(L) : 0.f;
-    if (vis[rt] && !(L >= 0x1p-60f)) loose = 1;
+    if (vis[rt] && !(L >= 0x1p-60f && L <= 0x1p100f)) loose = 1;  // also an overflowed sum
   }
   if (__syncthreads_or(loose)) {  // uniform: the running-maximum form (per lane, then per row)
     float mrun[RTW], lrun[RTW];

@@ -115,13 +115,18 @@ struct TopList {
 // chunk-swizzled so the 16 rows one operand read touches fall on distinct banks) and multiplies
 // all of a wave's sub-tiles, as four independent accumulation chains; three tiles' loads are in
 // flight.  Every lane keeps the top KS of its four blocks per tile for its queries; the four
-// lanes of a query then merge.  The ascending index list is written.
+// lanes of a query then merge.  The ascending index list is written.  An insert that does not
+// beat the list's last entry changes nothing, so inserts run only where some lane of the wave
+// needs one: with few blocks nearly every sub-tile has such a lane (one test per sub-tile, then
+// its four inserts); with many (LATE) a lane's list rarely moves after the first tiles (one test
+// per score).  Either way a lane inserts its scores in block order, so the lists are the same.
 constexpr int kGateWaves = 8;
+constexpr int kGateLateBlocks = 2048;  // blocks per head from which the gate tests per score
 
 template <int D>
 __device__ __forceinline__ int gate_swz(int row) { return row & (D / 8 - 1); }
 
-template <int D, int KS>
+template <int D, int KS, bool LATE>
 __global__ __launch_bounds__(kGateWaves * 64) void moba_gate_kernel(MobaArgs a) {
   constexpr int NU = 4, DC = D / 8;
   __shared__ __align__(16) u16 kbs[2][2][16][D];  // [buffer][hi, lo][block of the tile][feature]
@@ -211,12 +216,17 @@ __global__ __launch_bounds__(kGateWaves * 64) void moba_gate_kernel(MobaArgs a) 
     sweep([&](int jt, float (&x)[NU][4]) {
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        // an insert that does not beat the list's last entry changes nothing; the inserts run
-        // only when some lane of the wave needs one
-        const float mx = fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3]));
-        if (__ballot(mx > lst[u].v[KS - 1]) != 0) {  // uniform
+        if constexpr (LATE) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) lst[u].insert(x[u][i], jt * 16 + 4 * g4 + i);
+          for (int i = 0; i < 4; ++i)
+            if (__ballot(x[u][i] > lst[u].v[KS - 1]) != 0)  // uniform
+              lst[u].insert(x[u][i], jt * 16 + 4 * g4 + i);
+        } else {
+          const float mx = fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3]));
+          if (__ballot(mx > lst[u].v[KS - 1]) != 0) {  // uniform
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lst[u].insert(x[u][i], jt * 16 + 4 * g4 + i);
+          }
         }
       }
     });
@@ -676,7 +686,8 @@ static void launch_moba_k(const MobaArgs& a, hipStream_t s, hipEvent_t* ev) {
   const long rows = (long)a.B * a.T * a.H;
   const dim3 gp(a.nb, a.B * a.H), gg((a.T + kGateWaves * 64 - 1) / (kGateWaves * 64), a.H, a.B);
   moba_pool_kernel<D><<<gp, 256, 0, s>>>(a);
-  moba_gate_kernel<D, KS><<<gg, kGateWaves * 64, 0, s>>>(a);
+  if (a.nb > kGateLateBlocks) moba_gate_kernel<D, KS, true><<<gg, kGateWaves * 64, 0, s>>>(a);
+  else moba_gate_kernel<D, KS, false><<<gg, kGateWaves * 64, 0, s>>>(a);
   mark(1);
   const int nr = (a.nb + kMobaCountBlocks - 1) / kMobaCountBlocks;
   const int cblk = a.nb < kMobaCountBlocks ? a.nb : kMobaCountBlocks;

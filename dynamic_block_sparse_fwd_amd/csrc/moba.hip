@@ -109,9 +109,11 @@ struct TopList {
   }
 };
 
-// One workgroup scores 512 consecutive queries (8 waves x four 16-query sub-tiles) against every
-// past block key on the matrix core.  Each 16-block tile of kbar (bf16 hi and lo parts) is
-// staged in LDS once for the eight waves (double-buffered, one barrier per tile; its rows
+// One workgroup scores 256 consecutive queries (4 waves x four 16-query sub-tiles) against every
+// past block key on the matrix core; three workgroups share a CU, so one waiting at its per-tile
+// barrier leaves the matrix cores to the others.  Each 16-block tile of kbar (bf16 hi and lo
+// parts, two 16-byte pieces per thread) is staged in LDS once for the four waves
+// (double-buffered, one barrier per tile; its rows
 // chunk-swizzled so the 16 rows one operand read touches fall on distinct banks) and multiplies
 // all of a wave's sub-tiles, as four independent accumulation chains; three tiles' loads are in
 // flight.  Every lane keeps the top KS of its four blocks per tile for its queries; the four
@@ -120,14 +122,14 @@ struct TopList {
 // needs one: with few blocks nearly every sub-tile has such a lane (one test per sub-tile, then
 // its four inserts); with many (LATE) a lane's list rarely moves after the first tiles (one test
 // per score).  Either way a lane inserts its scores in block order, so the lists are the same.
-constexpr int kGateWaves = 8;
+constexpr int kGateWaves = 4;
 constexpr int kGateLateBlocks = 2048;  // blocks per head from which the gate tests per score
 
 template <int D>
 __device__ __forceinline__ int gate_swz(int row) { return row & (D / 8 - 1); }
 
 template <int D, int KS, bool LATE>
-__global__ __launch_bounds__(kGateWaves * 64) void moba_gate_kernel(MobaArgs a) {
+__global__ __launch_bounds__(kGateWaves * 64, 3) void moba_gate_kernel(MobaArgs a) {
   constexpr int NU = 4, DC = D / 8;
   __shared__ __align__(16) u16 kbs[2][2][16][D];  // [buffer][hi, lo][block of the tile][feature]
   const int h = blockIdx.y, b = blockIdx.z;
@@ -159,13 +161,20 @@ __global__ __launch_bounds__(kGateWaves * 64) void moba_gate_kernel(MobaArgs a) 
     }
     // staging: thread -> (hi/lo part, row, 16-byte chunk); 4 D threads stage a tile (past the
     // last block the last one is loaded again, so the loads are unconditional)
+    constexpr int NTH = kGateWaves * 64, NST = (4 * D + NTH - 1) / NTH;
     const bool stager = tid < 4 * D;
-    const int spart = tid / (16 * DC), srow = (tid / DC) % 16, sch = tid % DC;
-    const u16* sbase = (spart ? a.kb_lo : a.kb_hi) + bh * a.nb * D + 8 * sch;
-    auto fetch = [&](int jt) -> u32x4 {
-      int jr = jt * 16 + srow;
+    int spart[NST], srow[NST], sch[NST];
+    const u16* sbase[NST];
+#pragma unroll
+    for (int k = 0; k < NST; ++k) {
+      const int c = tid + NTH * k;
+      spart[k] = c / (16 * DC); srow[k] = (c / DC) % 16; sch[k] = c % DC;
+      sbase[k] = (spart[k] ? a.kb_lo : a.kb_hi) + bh * a.nb * D + 8 * sch[k];
+    }
+    auto fetch = [&](int jt, int k) -> u32x4 {
+      int jr = jt * 16 + srow[k];
       jr = jr < bq_max ? jr : bq_max - 1;
-      return *reinterpret_cast<const u32x4*>(sbase + (long)jr * D);
+      return *reinterpret_cast<const u32x4*>(sbase[k] + (long)jr * D);
     };
     const int nt = (bq_max + 15) / 16;
     // one sweep over the tiles: visit(jt, x) receives, per sub-tile u, the scores x[u][i] of
@@ -173,15 +182,28 @@ __global__ __launch_bounds__(kGateWaves * 64) void moba_gate_kernel(MobaArgs a) 
     auto sweep = [&](auto visit) {
       // three tiles' loads in flight (an L2 round trip outlasts one tile's products)
       const u32x4 z4 = {0u, 0u, 0u, 0u};
-      u32x4 p0 = stager ? fetch(0) : z4, p1 = stager ? fetch(1) : z4, p2 = stager ? fetch(2) : z4;
+      u32x4 p0[NST], p1[NST], p2[NST];
+#pragma unroll
+      for (int k = 0; k < NST; ++k) {
+        p0[k] = stager ? fetch(0, k) : z4;
+        p1[k] = stager ? fetch(1, k) : z4;
+        p2[k] = stager ? fetch(2, k) : z4;
+      }
       for (int jt = 0; jt < nt; ++jt) {
         const int buf = jt & 1;
-        if (stager)
-          *reinterpret_cast<u32x4*>(&kbs[buf][spart][srow][8 * (sch ^ gate_swz<D>(srow))]) = p0;
+        if (stager) {
+#pragma unroll
+          for (int k = 0; k < NST; ++k)
+            *reinterpret_cast<u32x4*>(
+                &kbs[buf][spart[k]][srow[k]][8 * (sch[k] ^ gate_swz<D>(srow[k]))]) = p0[k];
+        }
         __syncthreads();  // tile jt staged; tile jt - 1's buffer is free again
-        p0 = p1;
-        p1 = p2;
-        if (stager) p2 = fetch(jt + 3);
+#pragma unroll
+        for (int k = 0; k < NST; ++k) {
+          p0[k] = p1[k];
+          p1[k] = p2[k];
+          if (stager) p2[k] = fetch(jt + 3, k);
+        }
         if (scoring && jt * 16 < bq) {  // uniform per wave
           bf16x8 kh[D / 32], kl[D / 32];
 #pragma unroll

@@ -868,7 +868,8 @@ static void launch_bwd_d(const BwdArgs& a, hipStream_t s, hipEvent_t* ev) {
   const long nk = (long)a.B * a.Hkv * a.T * D;
   bwd_slc_reduce_kernel<<<(unsigned)((nk + 255) / 256), 256, 0, s>>>(a);
   if (a.ncmp > 0)
-    bwd_kv_kernel<D, kBrCmp, 8><<<dim3((a.NCP + 127) / 128, a.B * a.Hkv, a.NPC), 512, 0, s>>>(a);
+    // 64 compressed keys per workgroup (two workgroups per CU); the window pass keeps 128
+    bwd_kv_kernel<D, kBrCmp, 4><<<dim3((a.NCP + 63) / 64, a.B * a.Hkv, a.NPC), 256, 0, s>>>(a);
   mark(4);
   if (a.ncmp > 0) {
     const long nr = (long)a.B * a.Hkv * a.NCP * D;

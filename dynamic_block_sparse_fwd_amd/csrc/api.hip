@@ -555,14 +555,28 @@ int nsa_prefill_chunk(const nsa_config* c, int32_t P, int32_t C, const void* q,
   return hip_status();
 }
 
-// Appends that complete at most this many compressed tokens per sequence-head use one
-// workgroup per token; longer ones the 64-token tile compressor.
+// Appends that complete at most split_tokens(cfg) compressed tokens per sequence-head compress
+// with the split reduction (the completed tokens of all sequence-heads gathered into 64-row
+// tiles, the l*D reduction split over workgroups, fp32 partials summed in split order): its
+// partials take at most kSplitPartBytes of workspace, and at least kFewTokens tokens per
+// sequence-head are allowed.  Longer appends use the 64-token tile compressor, whose long
+// reduction per workgroup needs many workgroups to fill the GPU.
 constexpr int kFewTokens = 4;
+constexpr size_t kSplitPartBytes = (size_t)64 << 20;
+
+static int split_tokens(const nsa_config* c) {
+  const size_t one = few_part_bytes(c->B * c->Hkv, c->D, c->cmp_len, 1);
+  const int ncap = nsa_num_compressed(c->T, c->cmp_len, c->cmp_stride);
+  long n = one > 0 ? (long)(kSplitPartBytes / one) : kFewTokens;
+  n = std::max<long>(n, kFewTokens);
+  n = std::min<long>(n, std::max(ncap, kFewTokens));
+  return (int)n;
+}
 
 size_t nsa_cache_append_workspace_bytes(const nsa_config* c) {
   if (check_compress(c) != NSA_OK) return 0;
   return 2 * align_up((size_t)c->cmp_len * c->D * c->D * 2) +
-         align_up(few_part_bytes(c->B * c->Hkv, c->D, c->cmp_len, kFewTokens));
+         align_up(few_part_bytes(c->B * c->Hkv, c->D, c->cmp_len, split_tokens(c)));
 }
 
 int nsa_cache_append(const nsa_config* c, int32_t C, const void* k_new, const void* v_new,
@@ -589,7 +603,7 @@ int nsa_cache_append(const nsa_config* c, int32_t C, const void* k_new, const vo
                      kc16, vc16, seqlens, BH, c->Hkv, C, c->T, c->D, stream);
   // at most C / d + 1 compressed tokens per sequence-head are completed
   const int per = C / c->cmp_stride + 1 < ncap ? C / c->cmp_stride + 1 : ncap;
-  if (ncap > 0 && per <= kFewTokens) {
+  if (ncap > 0 && per <= split_tokens(c)) {
     char* base = static_cast<char*>(ws);
     uint16_t* wkt = reinterpret_cast<uint16_t*>(base);
     uint16_t* wvt = reinterpret_cast<uint16_t*>(base + align_up((size_t)LD * c->D * 2));

@@ -294,7 +294,10 @@ int nsa_decode_timed(const nsa_config* cfg, const void* q, const void* kcache,
  *   kcache, vcache bf16 [B, Hkv, Lmax, D]           updated in place
  *   kcmp           bf16 [B, Hkv, n_cmp(Lmax), D]     compressed keys, updated in place
  *   vcmp           bf16 [B, Hkv, nt(Lmax), D, 64]    compressed values in tiles, updated in place
- *   ws             at least nsa_cache_append_workspace_bytes(cfg) bytes (transposed weights)
+ *   ws             at least nsa_cache_append_workspace_bytes(cfg) bytes (transposed weights
+ *                  and the fp32 partials of the split compressor, at most 64 MB of them;
+ *                  appends completing more compressed tokens per sequence-head than those
+ *                  partials hold use the tile compressor)
  * Exactly the compressed tokens i with n_cmp(seqlens[b]) <= i < n_cmp(seqlens[b] + C) are
  * written, each equal bit for bit to nsa_compress / nsa_compress_tiles of the full cache; no
  * other compressed token and no cache row outside the appended positions is touched.  With

@@ -47,11 +47,20 @@ struct PrefillArgs {
   _Float16* s_po;        // [B*nq, Hkv, FS, 16, D] partial outputs / (sum * scale), fp16
   float* s_ps;           // [B*nq, Hkv, FS, 16, 4] partial (max in log2 units, sum, scale, 0)
   int FS, NTK, s_max_tiles;
+  int SC;  // T-chunks of the lists: slc_chunks(nq, NTK, top_n beta / 64), set at launch
 };
 
 constexpr int kNormRows = 256;  // compressed-key rows per chunk of the norm maxima
-constexpr int kSlcChunks = 16;  // T-chunks of the block-major lists (work tiles chunk-major)
-constexpr int kSlcRows = 32;   // positions per block-major work tile
+constexpr int kSlcChunks = 16;  // most T-chunks of the block-major lists (work tiles chunk-major)
+constexpr int kSlcRows = 32;    // positions per block-major work tile
+// T-chunks of the lists for nq query rows, ntk key tiles and `per` selected tiles per row: as
+// many as keep a sub-list about one work tile long (nq per / (ntk kSlcRows) entries in all per
+// key tile), a multiple of 4 in [4, kSlcChunks]
+__host__ __device__ constexpr int slc_chunks(long nq, int ntk, int per) {
+  const long c = nq * per / ((long)kSlcRows * (ntk > 0 ? ntk : 1));
+  const long c4 = c / 4 * 4;
+  return c4 < 4 ? 4 : (c4 > kSlcChunks ? kSlcChunks : (int)c4);
+}
 
 // Row of q/gate/out/idx holding query position t of sequence b.
 __device__ __forceinline__ long prow(const PrefillArgs& a, int b, int t) {

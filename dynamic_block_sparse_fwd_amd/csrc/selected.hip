@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kSlcCountThreads) void slc_count_kernel(PrefillArgs
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const long bkv = (long)b * a.Hkv + kvh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int cl = (a.nq + kSlcChunks - 1) / kSlcChunks;
+  const int cl = (a.nq + a.SC - 1) / a.SC;
   const int r0 = c * cl, r1 = r0 + cl < a.nq ? r0 + cl : a.nq;
   for (int i = threadIdx.x; i < a.NTK; i += kSlcCountThreads) cnt[i] = 0;
   __syncthreads();
@@ -141,13 +141,14 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 // Exclusive prefix sums of the sub-list lengths and of their kSlcRows-entry tile counts (one
 // workgroup, sub-lists in (chunk, sequence-group, key tile) order), and the sub-list of every
 // work tile.  4096 consecutive sub-lists per step, four per thread (one 16-byte load; the count
-// is a multiple of kSlcChunks = 16), each step's sums scanned over the waves and added to the
-// running totals of the steps before; the next step's counts are loaded during this one.
+// is a multiple of the T-chunk count, itself a multiple of 4), each step's sums scanned over the
+// waves and added to the running totals of the steps before; the next step's counts are loaded
+// during this one.
 __global__ __launch_bounds__(1024) void slc_scan_kernel(PrefillArgs a) {
   static_assert(kSlcChunks % 4 == 0, "four sub-lists per thread");
   __shared__ int wc[16], wt[16];
   __shared__ int carry_c, carry_t;
-  const long n = (long)kSlcChunks * a.B * a.Hkv * a.NTK;
+  const long n = (long)a.SC * a.B * a.Hkv * a.NTK;
   const long n4 = n / 4;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int4* cnt4 = reinterpret_cast<const int4*>(a.s_count);
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(256) void slc_fill_kernel(PrefillArgs a) {
   const int kvh = (int)(rg % a.Hkv);
   const long row = rg / a.Hkv;
   const int b = (int)(row / a.nq), r = (int)(row % a.nq);
-  const int c = r / ((a.nq + kSlcChunks - 1) / kSlcChunks);
+  const int c = r / ((a.nq + a.SC - 1) / a.SC);
   const long e = ((long)c * a.B * a.Hkv + (long)b * a.Hkv + kvh) * a.NTK + kt;
   a.s_list[a.s_offset[e] + a.s_rank[id]] = (int)(row << 6) | fs;
 }
@@ -516,7 +517,7 @@ __global__ __launch_bounds__(kSelWaves * 64, 1) void selected_kernel(PrefillArgs
 
 template <int D, int G>
 static void launch_selected_t(const PrefillArgs& a, hipStream_t s) {
-  slc_count_kernel<<<dim3(kSlcChunks, a.Hkv, a.B), kSlcCountThreads, a.NTK * sizeof(int), s>>>(a);
+  slc_count_kernel<<<dim3(a.SC, a.Hkv, a.B), kSlcCountThreads, a.NTK * sizeof(int), s>>>(a);
   slc_scan_kernel<<<1, 1024, 0, s>>>(a);
   const long nent = (long)a.B * a.nq * a.Hkv * a.FS;
   slc_fill_kernel<<<dim3((unsigned)((nent + 255) / 256)), 256, 0, s>>>(a);
@@ -536,7 +537,9 @@ static void launch_selected_g(const PrefillArgs& a, hipStream_t s) {
   }
 }
 
-void launch_selected(const PrefillArgs& a, hipStream_t s) {
+void launch_selected(const PrefillArgs& a0, hipStream_t s) {
+  PrefillArgs a = a0;
+  a.SC = slc_chunks(a.nq, a.NTK, a.top_n * (a.beta / 64));  // per (sequence, group) sub-lists
   if (a.D == 128) launch_selected_g<128>(a, s);
   else launch_selected_g<64>(a, s);
 }

@@ -136,6 +136,35 @@ void launch_cmp_cache_layout(const uint16_t* kc, const uint16_t* vtiles, uint16_
 // are around 1e-6 of the operand scale; 2^-16 leaves a wide margin and flags about 1% of outputs.
 constexpr float kMidTol = 1.0f / 65536.0f;
 
+// The fp64 dot product of the l*D elements at xp and wp (bf16; every product exact in fp64),
+// summed by the whole wave, then its round-to-odd fp32 image (whose bf16 rounding equals the
+// correctly rounded fp64 value).  Each lane sums elements 8 lane + 512 j in ascending j; the
+// loads of eight j at a time are issued together, so one recomputation waits for one load
+// round trip per 4096 elements instead of one per 512.
+__device__ __forceinline__ float exact_dot_rto(const u16* xp, const u16* wp, int K, int lane) {
+  double s = 0.0;
+  for (int kb = 0; kb < K; kb += 4096) {
+    bf16x8 xv[8], wv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int k = kb + 512 * j + 8 * lane;
+      k = k < K ? k : 0;  // past the end: an in-bounds load whose products are skipped
+      xv[j] = load8(xp + k);
+      wv[j] = load8(wp + k);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (kb + 512 * j + 8 * lane < K)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s += (double)(float)xv[j][q] * (double)(float)wv[j][q];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  float f = __double2float_rz(s);
+  if ((double)f != s) f = __uint_as_float(__float_as_uint(f) | 1u);  // round to odd
+  return f;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x,
                                                        const u16* __restrict__ wt,
@@ -182,10 +211,13 @@ __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x
     // A GEMM over k = l*D in 64-wide steps: the 64 token windows (each l*D contiguous elements
     // of x) and the weight rows are staged in LDS once per step for the four waves
     // (double-buffered, one barrier per step; 16-byte chunks swizzled by row so the 16 rows an
-    // operand read touches fall on distinct banks), the next step's loads in flight.
+    // operand read touches fall on distinct banks).  The loads of the next NPF steps are in
+    // flight in NPF register sets (a step's compute is far shorter than a load's latency, so
+    // one set in flight left the loop waiting on every load).
     __shared__ __align__(16) u16 xs[2][64][64];
     __shared__ __align__(16) u16 ws[2][D][64];
     constexpr int XQ = 64 * 8 / 256, WQ = D * 8 / 256;  // 16-byte chunks per thread
+    constexpr int NPF = 3;                               // register sets of steps in flight
     const int tid = threadIdx.x;
     const u16* xsrc[XQ];
     const u16* wsrc[WQ];
@@ -201,80 +233,52 @@ __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x
       const int q = tid + 256 * r;
       wsrc[r] = wt + (long)(q / 8) * K + 8 * (q % 8);
     }
-    u32x4 px[XQ], pw[WQ];
-    auto fetch = [&](int k0) {
-#pragma unroll
-      for (int r = 0; r < XQ; ++r) px[r] = *reinterpret_cast<const u32x4*>(xsrc[r] + k0);
-#pragma unroll
-      for (int r = 0; r < WQ; ++r) pw[r] = *reinterpret_cast<const u32x4*>(wsrc[r] + k0);
-    };
     const int nks = K / 64;
-    fetch(0);
-    for (int ks = 0; ks < nks; ++ks) {
-      const int buf = ks & 1;
+    u32x4 px[NPF][XQ], pw[NPF][WQ];
+    auto fetch = [&](int set, int step) {  // step clamped: past the end it reloads the last
+      const int k0 = 64 * (step < nks ? step : nks - 1);
 #pragma unroll
-      for (int r = 0; r < XQ; ++r) {
-        const int q = tid + 256 * r, tok = q / 8, ch = q % 8;
-        *reinterpret_cast<u32x4*>(&xs[buf][tok][8 * (ch ^ (tok & 7))]) = px[r];
-      }
+      for (int r = 0; r < XQ; ++r) px[set][r] = *reinterpret_cast<const u32x4*>(xsrc[r] + k0);
 #pragma unroll
-      for (int r = 0; r < WQ; ++r) {
-        const int q = tid + 256 * r, f = q / 8, ch = q % 8;
-        *reinterpret_cast<u32x4*>(&ws[buf][f][8 * (ch ^ (f & 7))]) = pw[r];
-      }
-      __syncthreads();  // step ks staged; step ks - 1's buffer is free again
-      fetch(64 * (ks + 1 < nks ? ks + 1 : ks));  // the last step loads itself again
+      for (int r = 0; r < WQ; ++r) pw[set][r] = *reinterpret_cast<const u32x4*>(wsrc[r] + k0);
+    };
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const int ch = 8 * ((4 * kc + g4) ^ (r16 & 7));
-        bf16x8 bx[4], aw[CT];
+    for (int p = 0; p < NPF; ++p) fetch(p, p);
+    for (int ks0 = 0; ks0 < nks; ks0 += NPF) {
 #pragma unroll
-        for (int it = 0; it < 4; ++it) bx[it] = load8(&xs[buf][it * 16 + r16][ch]);
+      for (int p = 0; p < NPF; ++p) {
+        const int ks = ks0 + p;
+        if (ks >= nks) break;  // uniform
+        const int buf = ks & 1;
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) aw[ct] = load8(&ws[buf][wave * (D / 4) + ct * 16 + r16][ch]);
+        for (int r = 0; r < XQ; ++r) {
+          const int q = tid + 256 * r, tok = q / 8, ch = q % 8;
+          *reinterpret_cast<u32x4*>(&xs[buf][tok][8 * (ch ^ (tok & 7))]) = px[p][r];
+        }
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
+        for (int r = 0; r < WQ; ++r) {
+          const int q = tid + 256 * r, f = q / 8, ch = q % 8;
+          *reinterpret_cast<u32x4*>(&ws[buf][f][8 * (ch ^ (f & 7))]) = pw[p][r];
+        }
+        __syncthreads();  // step ks staged; step ks - 1's buffer is free again
+        fetch(p, ks + NPF);
 #pragma unroll
-          for (int it = 0; it < 4; ++it) acc[ct][it] = mfma16x16x32(aw[ct], bx[it], acc[ct][it]);
+        for (int kc = 0; kc < 2; ++kc) {
+          const int ch = 8 * ((4 * kc + g4) ^ (r16 & 7));
+          bf16x8 bx[4], aw[CT];
+#pragma unroll
+          for (int it = 0; it < 4; ++it) bx[it] = load8(&xs[buf][it * 16 + r16][ch]);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            aw[ct] = load8(&ws[buf][wave * (D / 4) + ct * 16 + r16][ch]);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+              acc[ct][it] = mfma16x16x32(aw[ct], bx[it], acc[ct][it]);
+        }
       }
     }
-  }
-  // Exact rounding.  The fp32 sum of l*D products carries a small accumulation error; where
-  // it lies within kMidTol of a bf16 rounding midpoint the rounding direction is not settled
-  // by fp32, so the whole wave recomputes that element in fp64 (exact products, fp64 sum) and
-  // replaces it by its round-to-odd fp32 image, whose bf16 rounding equals the correctly
-  // rounded fp64 value.  Every other element already rounds like the exact sum.
-  if (ihi > 0) {
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int it = 0; it < 4; ++it)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v = acc[ct][it][e];
-          const float mid = __uint_as_float((__float_as_uint(v) & 0xFFFF0000u) | 0x8000u);
-          const float tol = kMidTol * fmaxf(1.f, fabsf(v));
-          uint64_t pending = __ballot(fabsf(v - mid) < tol && (i0 + it * 16 + r16) < ihi);
-          while (pending) {
-            const int src = __builtin_ctzll(pending);
-            pending &= pending - 1;
-            const int c = wave * (D / 4) + ct * 16 + 4 * (src >> 4) + e;
-            const int i = i0 + it * 16 + (src & 15);
-            const u16* xp = xb + (long)i * d * D;
-            const u16* wp = wt + (long)c * K;
-            double s = 0.0;
-            for (int k = 8 * lane; k < K; k += 512) {
-              const bf16x8 xv = load8(xp + k), wv = load8(wp + k);
-#pragma unroll
-              for (int q = 0; q < 8; ++q) s += (double)(float)xv[q] * (double)(float)wv[q];
-            }
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-            float f = __double2float_rz(s);
-            if ((double)f != s) f = __uint_as_float(__float_as_uint(f) | 1u);  // round to odd
-            if (lane == src) acc[ct][it][e] = f;
-          }
-        }
   }
   // lane holds C^T[c = base + 4*g4 + e][i = i0 + it*16 + r16]
 #pragma unroll
@@ -300,6 +304,50 @@ __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x
         const long es = tiled ? 64 : ncp;
 #pragma unroll
         for (int e = 0; e < 4; ++e) xct[o + e * es] = h[e];
+      }
+    }
+  }
+  // Exact rounding.  The fp32 sum of l*D products carries a small accumulation error; where
+  // it lies within kMidTol of a bf16 rounding midpoint the rounding direction is not settled
+  // by fp32, so the whole wave recomputes that element in fp64 (exact products, fp64 sum) and
+  // its owner lane stores again the bf16 rounding of the round-to-odd fp32 image, which equals
+  // the correctly rounded fp64 value.  Every other element already rounds like the exact sum.
+  // The flags of the wave's CT x 16 accumulator slots go to LDS first, so the recomputation
+  // loop below is not unrolled over the slots.
+  if (ihi > 0) {  // uniform
+    __shared__ uint64_t flags[4][CT * 16];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = acc[ct][it][e];
+          const float mid = __uint_as_float((__float_as_uint(v) & 0xFFFF0000u) | 0x8000u);
+          const float tol = kMidTol * fmaxf(1.f, fabsf(v));
+          const uint64_t m = __ballot(fabsf(v - mid) < tol && (i0 + it * 16 + r16) < ihi);
+          if (lane == 0) flags[wave][(ct * 4 + it) * 4 + e] = m;
+        }
+    __asm__ volatile("" ::: "memory");  // the wave's own LDS writes come before its reads
+    for (int slot = 0; slot < CT * 16; ++slot) {
+      const uint64_t fl = flags[wave][slot];  // the same in every lane: made scalar
+      uint64_t pending =
+          ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(fl >> 32)) << 32) |
+          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)fl);
+      const int ct = slot >> 4, it = (slot >> 2) & 3, e = slot & 3;
+      while (pending) {
+        const int src = __builtin_ctzll(pending);
+        pending &= pending - 1;
+        const int c = wave * (D / 4) + ct * 16 + 4 * (src >> 4) + e;
+        const int i = i0 + it * 16 + (src & 15);
+        const float f = exact_dot_rto(xb + (long)i * d * D, wt + (long)c * K, K, lane);
+        if (lane == src) {
+          const u16 h = f32_to_bf16(f);
+          if (xc != nullptr && i < rows_alloc) xc[(bh * rows_alloc + i) * D + c] = h;
+          if (xct != nullptr && i < ncp)
+            xct[tiled ? ((bh * (ncp >> 6) + (i >> 6)) * D + c) * 64 + (i & 63)
+                      : (bh * D + c) * (long)ncp + i] = h;
+        }
       }
     }
   }
@@ -413,16 +461,7 @@ __global__ __launch_bounds__(256) void compress_finish_kernel(FewArgs a) {
     const int src = __builtin_ctzll(pending);
     pending &= pending - 1;
     const u16* wp = a.wt[kv] + (long)(c - lane + src) * K;
-    double s = 0.0;
-    for (int k = 8 * lane; k < K; k += 512) {
-      const bf16x8 xv = load8(xp + k), wv = load8(wp + k);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) s += (double)(float)xv[q] * (double)(float)wv[q];
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-    float f = __double2float_rz(s);
-    if ((double)f != s) f = __uint_as_float(__float_as_uint(f) | 1u);  // round to odd
+    const float f = exact_dot_rto(xp, wp, K, lane);
     if (lane == src) v = f;
   }
   const u16 h = f32_to_bf16(v);

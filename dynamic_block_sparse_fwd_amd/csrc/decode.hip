@@ -991,8 +991,9 @@ __global__ __launch_bounds__(kTileThreads) void dec_tiles_kernel(DecodeArgs a) {
 
 // Per group: the NG tile workgroups' records of each branch merged in workgroup order, then
 // the gate: out = g0 o_cmp + g1 o_slc + g2 o_win (o_cmp normalised by the selection slices).
-// Threads 0..31 turn the records' maxima and sums into per-(branch, head) weights first, so
-// that every output's loads are issued together.
+// Every thread issues its loads of the records' outputs, the compressed output and the gates
+// first; meanwhile threads 0..31 turn the records' maxima and sums into per-(branch, head)
+// weights.
 constexpr int kMergeMaxNG = 8;
 
 template <int D>
@@ -1014,6 +1015,16 @@ __global__ __launch_bounds__(256) void dec_merge_kernel(DecodeArgs a) {
     oc[q] = a.ocmp[(bkv * 16 + h) * D + dd];
 #pragma unroll
     for (int c = 0; c < 3; ++c) g3[q][c] = a.gate[head * 3 + c];
+  }
+  // the records' outputs do not depend on the weights either: in flight across the barrier
+  float ro[kMergeMaxNG][2][PT];
+#pragma unroll
+  for (int g = 0; g < kMergeMaxNG; ++g) {
+    if (g >= a.NG) break;  // uniform
+#pragma unroll
+    for (int br = 0; br < 2; ++br)
+#pragma unroll
+      for (int q = 0; q < PT; ++q) ro[g][br][q] = recs[(g * 2 + br) * RS + 32 + tid + 256 * q];
   }
   if (tid < 32) {
     const int br = tid >> 4, h = tid & 15;
@@ -1043,11 +1054,10 @@ __global__ __launch_bounds__(256) void dec_merge_kernel(DecodeArgs a) {
     if (g >= a.NG) break;  // uniform
 #pragma unroll
     for (int br = 0; br < 2; ++br) {
-      const float* rc = recs + (g * 2 + br) * RS + 32;
 #pragma unroll
       for (int q = 0; q < PT; ++q) {
         const int pr = tid + 256 * q, h = pr / D;
-        acc[q][br] += W[br][h][g] * rc[pr];
+        acc[q][br] += W[br][h][g] * ro[g][br][q];
       }
     }
   }

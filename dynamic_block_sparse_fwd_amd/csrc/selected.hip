@@ -68,12 +68,28 @@ __device__ __forceinline__ int sel_tile_key(const PrefillArgs& a, int b, int kvh
   return k0;
 }
 
-// Lane's tile key if it is not one of the shared tiles, else -1.
-__device__ __forceinline__ int free_tile_key(const PrefillArgs& a, int b, int kvh, int t,
-                                             int lane) {
-  const int t0 = a.q0 + ((t - a.q0) / kSelWaves) * kSelWaves;
-  const SelShared sh = sel_shared(a, t0);
-  int k0 = sel_tile_key(a, b, kvh, t, lane);
+// Lane e < top_n * per of a position's index row: its block slot e / per and its sub-tile
+// e % per, the same for every position (computed once per lane).
+struct LaneTile {
+  int slot, sub;
+  bool on;
+};
+
+__device__ __forceinline__ LaneTile lane_tile(const PrefillArgs& a, int lane) {
+  const int per = a.beta >> 6;
+  return LaneTile{lane / per, lane % per, lane < a.top_n * per};
+}
+
+// The lane's tile key of position t, whose index row is `row` (as sel_tile_key), if it is not
+// one of the tiles `sh` shared by t's workgroup of the position-major kernel, else -1.
+__device__ __forceinline__ int free_tile_key(const PrefillArgs& a, const int32_t* row, int t,
+                                             const LaneTile& lt, const SelShared& sh) {
+  int k0 = -1;
+  if (lt.on) {
+    const int j = row[lt.slot];
+    const int kk = j * a.beta + 64 * lt.sub;
+    if (j >= 0 && j < a.nblk && kk <= t) k0 = kk;
+  }
 #pragma unroll
   for (int i = 0; i < kSelShared; ++i)
     if (i < sh.n && k0 == sh.key(i)) k0 = -1;
@@ -91,36 +107,49 @@ constexpr int kSlcCountThreads = 1024;
 // Per (T-chunk, group, sequence): one wave per position lists its free tiles (their rank among
 // the row's free tiles is the slot fs); every entry's rank among the chunk's entries of its key
 // tile comes from LDS counters (no global atomics), the counts per key tile are written out.
+// A wave takes the kSelWaves positions that share one workgroup of the position-major kernel
+// at a time: their shared tiles (scalar arithmetic with divisions) are found once, and their
+// index loads are in flight together.
 __global__ __launch_bounds__(kSlcCountThreads) void slc_count_kernel(PrefillArgs a) {
   extern __shared__ int cnt[];  // [NTK]
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const long bkv = (long)b * a.Hkv + kvh;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // positions: uniform
+  const LaneTile lt = lane_tile(a, lane);
   const int cl = (a.nq + a.SC - 1) / a.SC;
   const int r0 = c * cl, r1 = r0 + cl < a.nq ? r0 + cl : a.nq;
   for (int i = threadIdx.x; i < a.NTK; i += kSlcCountThreads) cnt[i] = 0;
   __syncthreads();
-  constexpr int W = kSlcCountThreads / 64, U = 4;  // positions per wave and pass
-  for (int rb = r0 + wave; rb < r1; rb += W * U) {  // wave-uniform
+  constexpr int W = kSlcCountThreads / 64, U = kSelWaves;
+  // position groups (rows r = U g .. U g + U - 1, relative to q0) overlapping [r0, r1)
+  // consecutive positions: index rows si ints apart, entry rows ss apart
+  const int si = a.Hkv * a.top_n, ss = a.Hkv * a.FS;
+  for (int g = r0 / U + wave; g * U < r1; g += W) {  // wave-uniform
+    const int rg = g * U;
+    const SelShared sh = sel_shared(a, a.q0 + rg);
+    const int32_t* irow = a.idx + (prow(a, b, a.q0 + rg) * a.Hkv + kvh) * a.top_n;
+    const long sbase = (((long)b * a.nq + rg) * a.Hkv + kvh) * a.FS;
     int k0[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {  // the index loads of U positions in flight together
-      const int r = rb + W * u;
-      k0[u] = r < r1 ? free_tile_key(a, b, kvh, a.q0 + r, lane) : -1;
+    for (int u = 0; u < U; ++u) {
+      const int r = rg + u;
+      k0[u] = r >= r0 && r < r1 ? free_tile_key(a, irow + u * si, a.q0 + r, lt, sh) : -1;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int r = rb + W * u;
-      if (r >= r1) break;  // uniform
+      const int r = rg + u;
+      if (r < r0 || r >= r1) continue;  // uniform
       const uint64_t m = __ballot(k0[u] >= 0);
       const int nfree = (int)__popcll(m);
-      const long base = (((long)b * a.nq + r) * a.Hkv + kvh) * a.FS;
+      int32_t* rk = a.s_rank + sbase + u * ss;
+      int32_t* kt = a.s_kt + sbase + u * ss;
       if (k0[u] >= 0) {
         const int fs = lanes_below(m, lane);
-        a.s_rank[base + fs] = atomicAdd(&cnt[k0[u] >> 6], 1);
-        a.s_kt[base + fs] = k0[u] >> 6;
+        rk[fs] = atomicAdd(&cnt[k0[u] >> 6], 1);
+        kt[fs] = k0[u] >> 6;
       }
-      if (lane >= nfree && lane < a.FS) a.s_kt[base + lane] = -1;
+      if (lane >= nfree && lane < a.FS) kt[lane] = -1;
     }
   }
   __syncthreads();

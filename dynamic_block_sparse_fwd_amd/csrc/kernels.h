@@ -44,7 +44,9 @@ struct PrefillArgs {
   int32_t* s_ntiles;     // [1] work tiles in all
   int32_t* s_tile_entry; // [s_max_tiles] sub-list of each work tile
   int32_t* s_list;       // [B*nq*Hkv*FS] entries by sub-list: row << 6 | fs
-  _Float16* s_po;        // [B*nq, Hkv, FS, 16, D] partial outputs / (sum * scale), fp16
+  _Float16* s_po;        // [B*nq, Hkv, FS, 16, D] partial outputs / (sum * scale), fp16;
+                         // the 8 values at 32 p + 8 g of a row are columns 32 p + 4 g ..
+                         // + 3 and 32 p + 16 + 4 g .. + 3 (g < 4)
   float* s_ps;           // [B*nq, Hkv, FS, 16, 4] partial (max in log2 units, sum, scale, 0)
   int FS, NTK, s_max_tiles;
   int SC;  // T-chunks of the lists: slc_chunks(nq, NTK, top_n beta / 64), set at launch

@@ -358,12 +358,18 @@ __global__ __launch_bounds__(256) void slc_block_kernel(PrefillArgs a) {
       const float scale = ldexpf(1.f, ex);
       const float w = inv * ldexpf(1.f, -ex);  // exact power-of-two factor
       const long slot = ((row * a.Hkv + kvh) * a.FS + fs) * 16 + r16;
+      // the lane's output quads of column tiles 2 p and 2 p + 1 in one 16-byte piece at
+      // 32 p + 8 g4 of the row (the merge reads them back whole)
       _Float16* op = a.s_po + slot * D;
 #pragma unroll
-      for (int n = 0; n < DT; ++n) {
-        const h16x4 v = {(_Float16)(O[r][n][0] * w), (_Float16)(O[r][n][1] * w),
-                         (_Float16)(O[r][n][2] * w), (_Float16)(O[r][n][3] * w)};
-        *reinterpret_cast<h16x4*>(op + 16 * n + 4 * g4) = v;
+      for (int p2 = 0; p2 < DT / 2; ++p2) {
+        h16x8 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] = (_Float16)(O[r][2 * p2][q] * w);
+          v[4 + q] = (_Float16)(O[r][2 * p2 + 1][q] * w);
+        }
+        *reinterpret_cast<h16x8*>(op + 32 * p2 + 8 * g4) = v;
       }
       if (g4 == 0) *reinterpret_cast<f32x4*>(a.s_ps + slot * 4) = f32x4{msl[r], L[r], scale, 0.f};
     }
@@ -440,15 +446,15 @@ __global__ __launch_bounds__(kSelWaves * 64, 1) void selected_kernel(PrefillArgs
   // outputs, in flight while the shared tiles compute (slot 0 always exists in the layout, and
   // is unused when the row has no partial)
   const long pslot = ((long)(b * a.nq + (t - a.q0)) * a.Hkv + kvh) * a.FS;
-  auto load_part = [&](int fs, float4& st, h16x4* ov) {
+  auto load_part = [&](int fs, float4& st, h16x8* ov) {
     const long slot = (pslot + fs) * 16 + r16;
     st = *reinterpret_cast<const float4*>(a.s_ps + slot * 4);
 #pragma unroll
-    for (int n = 0; n < DT; ++n)
-      ov[n] = *reinterpret_cast<const h16x4*>(a.s_po + slot * D + 16 * n + 4 * g4);
+    for (int p2 = 0; p2 < DT / 2; ++p2)
+      ov[p2] = *reinterpret_cast<const h16x8*>(a.s_po + slot * D + 32 * p2 + 8 * g4);
   };
   float4 st;
-  h16x4 ov[DT];
+  h16x8 ov[DT / 2];
   load_part(0, st, ov);
 
   float mrun = kNegInf, lrun = 0.f;
@@ -509,9 +515,9 @@ __global__ __launch_bounds__(kSelWaves * 64, 1) void selected_kernel(PrefillArgs
   float L = col_sum4(lrun);
   for (int fs = 0; fs < nfree; ++fs) {
     const float4 cs = st;
-    h16x4 cv[DT];
+    h16x8 cv[DT / 2];
 #pragma unroll
-    for (int n = 0; n < DT; ++n) cv[n] = ov[n];
+    for (int p2 = 0; p2 < DT / 2; ++p2) cv[p2] = ov[p2];
     load_part(fs + 1 < nfree ? fs + 1 : fs, st, ov);  // unconditional: the last re-fetches itself
     const float mn = fmaxf(msl, cs.x);
     const float a1 = msl == kNegInf ? 0.f : fast_exp2(msl - mn);
@@ -520,7 +526,8 @@ __global__ __launch_bounds__(kSelWaves * 64, 1) void selected_kernel(PrefillArgs
 #pragma unroll
     for (int n = 0; n < DT; ++n)
 #pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) O[n][i2] = O[n][i2] * a1 + (float)cv[n][i2] * w2;
+      for (int i2 = 0; i2 < 4; ++i2)
+        O[n][i2] = O[n][i2] * a1 + (float)cv[n >> 1][4 * (n & 1) + i2] * w2;
     L = L * a1 + cs.y * a2;
     msl = mn;
   }

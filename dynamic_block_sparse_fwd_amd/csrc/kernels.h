@@ -177,7 +177,8 @@ struct MobaArgs {
   int32_t* ntiles;     // [1] total tiles
   int32_t* tile_entry; // [max_tiles] the list each 128-row tile belongs to
   int32_t* list;       // [B*T*H*top_k] (t << 4 | slot)
-  _Float16* po;        // [B*T*H, top_k, D] partial outputs / (own sum * scale), fp16
+  _Float16* po;        // [B*T*H, top_k, D] partial outputs / (own sum * scale), fp16;
+                       // values 32 p + 8 g .. + 7: columns 32 p + 4 g .. + 3, 32 p + 16 + 4 g .. + 3
   float* pml;          // [B*T*H, top_k, 4] partial (max in log2 units, sum, scale, 0)
   int B, T, H, D, block, top_k, nb, max_tiles;
   int Hs, h0;  // heads of the caller's q, k, out, idx; first head of this pass (H heads)

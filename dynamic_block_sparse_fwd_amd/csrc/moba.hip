@@ -528,12 +528,18 @@ __global__ __launch_bounds__(256) void moba_block_kernel(MobaArgs a) {
     const float w = inv * ldexpf(1.f, -ex);          // exact power-of-two factor
     if (rt_t[rt] >= 0) {
       const long slot = (((long)b * a.T + rt_t[rt]) * a.H + h) * a.top_k + rt_s[rt];
+      // the lane's output quads of column tiles 2 p and 2 p + 1 in one 16-byte piece at
+      // 32 p + 8 g4 of the slot (moba_own_kernel reads them back whole)
       _Float16* op = a.po + slot * D;
 #pragma unroll
-      for (int nn = 0; nn < DT; ++nn) {
-        const h16x4 v = {(_Float16)(O[rt][nn][0] * w), (_Float16)(O[rt][nn][1] * w),
-                         (_Float16)(O[rt][nn][2] * w), (_Float16)(O[rt][nn][3] * w)};
-        *reinterpret_cast<h16x4*>(op + 16 * nn + 4 * g4) = v;
+      for (int p2 = 0; p2 < DT / 2; ++p2) {
+        h16x8 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] = (_Float16)(O[rt][2 * p2][q] * w);
+          v[4 + q] = (_Float16)(O[rt][2 * p2 + 1][q] * w);
+        }
+        *reinterpret_cast<h16x8*>(op + 32 * p2 + 8 * g4) = v;
       }
       if (g4 == 0)
         *reinterpret_cast<f32x4*>(a.pml + slot * 4) =
@@ -660,9 +666,10 @@ __global__ __launch_bounds__(256) void moba_own_kernel(MobaArgs a) {
       ps[s] = st[2];
       const _Float16* op = a.po + slot * D;
 #pragma unroll
-      for (int nn = 0; nn < DT; ++nn) {
-        const h16x4 v = *reinterpret_cast<const h16x4*>(op + 16 * nn + 4 * g4);
-        pv[s][nn] = make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+      for (int p2 = 0; p2 < DT / 2; ++p2) {
+        const h16x8 v = *reinterpret_cast<const h16x8*>(op + 32 * p2 + 8 * g4);
+        pv[s][2 * p2] = make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+        pv[s][2 * p2 + 1] = make_float4((float)v[4], (float)v[5], (float)v[6], (float)v[7]);
       }
     }
     float M = mrun[rt];

@@ -883,13 +883,26 @@ def host_info():
     for f in sorted(os.listdir(CSRC)):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + fh.read())
+    digest = h.hexdigest()[:16]
     try:
         sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
                              text=True, timeout=10).stdout.strip() or None
     except (OSError, subprocess.SubprocessError):
         sha = None
+    sha_from = "git" if sha else None
+    if sha is None:  # a copy of the tree without .git: the commit recorded at build time
+        try:
+            with open(os.path.join(ROOT, "dynamic_block_sparse_fwd_amd",
+                                   "libnsa.buildinfo.json")) as fh:
+                info = json.load(fh)
+            if info.get("library_source_sha256") == digest and info.get("git_sha"):
+                sha = info["git_sha"]
+                sha_from = ("build record, sources modified since that commit"
+                            if info.get("csrc_modified_since_commit") else "build record")
+        except (OSError, ValueError):
+            pass
     return {"cpu_model": model, "cpu_count": os.cpu_count(), "git_sha": sha,
-            "library_source_sha256": h.hexdigest()[:16]}
+            "git_sha_source": sha_from, "library_source_sha256": digest}
 
 
 def main():

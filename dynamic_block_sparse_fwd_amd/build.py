@@ -24,6 +24,43 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
+BUILD_INFO = os.path.join(PKG, "libnsa.buildinfo.json")
+
+
+def source_digest() -> str:
+    """sha256 (first 16 hex digits) over every file of csrc/, names and contents, in name order."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(PKG, "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _write_build_info() -> None:
+    """Record the commit the library was built from (when the tree is a git checkout), so that a
+    copy of the tree without its history can still name it; the source digest ties the record
+    to the sources it describes."""
+    import json
+
+    sha, dirty = None, None
+    try:
+        sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                             text=True, timeout=10).stdout.strip() or None
+        if sha:
+            st = subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--",
+                                 os.path.join(PKG, "csrc")], capture_output=True, text=True,
+                                timeout=10).stdout
+            dirty = bool(st.strip())
+    except (OSError, subprocess.SubprocessError):
+        pass
+    with open(BUILD_INFO, "w") as fh:
+        json.dump({"git_sha": sha, "csrc_modified_since_commit": dirty,
+                   "library_source_sha256": source_digest()}, fh)
+
+
 def build(verbose: bool = False) -> str:
     """Compile every kernel source and the C-ABI layer into one shared library."""
     objs = []
@@ -52,6 +89,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     subprocess.check_call(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
+    _write_build_info()
     return LIB
 
 

@@ -387,6 +387,8 @@ __device__ void wave_tiles(const DecodeArgs& a, long bkv, const DecRow& r, const
     kv.load_k(kcb, k1, last1, lane);
 #pragma unroll
     for (int br = 0; br < NBR; ++br) {
+      // a branch the tile does not feed (uniform) would only add masked zeros: skipped
+      if (!(br == 0 ? in_slc : in_win)) continue;
       float p[16];
       float tm = kNegInf;
 #pragma unroll

@@ -92,14 +92,12 @@ struct DecTile {
       const int x = it * 64 + lane, kq = x & 15, dc = x >> 4;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16, d = 8 * dc + e;
-        const uint32_t h0 = (v[it * 4 + 0][e >> 1] >> sh) & 0xFFFFu;
-        const uint32_t h1 = (v[it * 4 + 1][e >> 1] >> sh) & 0xFFFFu;
-        const uint32_t h2 = (v[it * 4 + 2][e >> 1] >> sh) & 0xFFFFu;
-        const uint32_t h3 = (v[it * 4 + 3][e >> 1] >> sh) & 0xFFFFu;
+        // the e-th features of keys 4 kq .. 4 kq + 3 paired by byte permutes: bytes 0,1 (even
+        // e) or 2,3 (odd e) of the lower key's word, then the same of the upper key's
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u, d = 8 * dc + e;
         uint2 pk;
-        pk.x = h0 | (h1 << 16);
-        pk.y = h2 | (h3 << 16);
+        pk.x = __builtin_amdgcn_perm(v[it * 4 + 1][e >> 1], v[it * 4 + 0][e >> 1], sel);
+        pk.y = __builtin_amdgcn_perm(v[it * 4 + 3][e >> 1], v[it * 4 + 2][e >> 1], sel);
         *reinterpret_cast<uint2*>(&Vt[d][(((kq >> 1) ^ (d & 7)) * 8) + (kq & 1) * 4]) = pk;
       }
     }

@@ -123,11 +123,17 @@ class HipEvents:
 
 # ----------------------------------------------------------------------------- work counts
 
-def gather_bytes(B, T, Hkv, D, beta=64, n=16):
-    """K+V bytes the selected branch gathers: one bf16 K and V row per (position, KV group,
-    selected key), causal keys of the selected blocks only."""
-    _, slc, _ = prefill_pairs(T, beta=beta, n=n)
-    return B * Hkv * slc * 2 * D * 2
+def selected_traffic(stage_ms):
+    """HBM bytes of the selected stage's two heavy launches (block-major tiles and the merge)
+    from the committed counters, over the stage's time: the bound of the block-major design,
+    whose q reads and partials are traffic of the design rather than of the method.  None while
+    the counters are stale."""
+    t1, t2 = measured_traffic("slc_block_kernel"), measured_traffic("selected_kernel")
+    if t1 is None or t2 is None or stage_ms <= 0:
+        return {"bytes": None, "gbs": None, "hbm_frac": None}
+    gbs = (t1 + t2) / (stage_ms * 1e-3)
+    return {"bytes": t1 + t2, "gbs": round(gbs / 1e9, 1), "hbm_frac": round(gbs / HBM_PEAK, 4),
+            "kernels": ["slc_block_kernel", "selected_kernel"]}
 
 
 def prefill_pairs(T, l=32, d=16, beta=64, n=16, n_local=2, w=512):
@@ -248,7 +254,6 @@ def bench_prefill(args):
     flops["cmp_select"] += flops["window"]
     flops["window"] = 0.0
     dom = max(stage_ms, key=lambda k: stage_ms[k])
-    gbytes = gather_bytes(B, T, Hkv, D) if slc_keys is None else slc_keys * 2 * D * 2
     stages = {nm: {"ms": round(stage_ms[nm], 4),
                    "tflops": round(flops[nm] / (stage_ms[nm] * 1e-3) / 1e12, 2)
                    if flops.get(nm, 0) > 0 and stage_ms[nm] > 0 else None}
@@ -270,9 +275,8 @@ def bench_prefill(args):
             "tflop": cmp_select_performed_flops(B, T, Hkv, G, D) / 1e12,
             "mfma_frac": cmp_select_performed_flops(B, T, Hkv, G, D)
                          / (stage_ms["cmp_select"] * 1e-3) / MFMA_PEAK_BF16},
-        # the selected branch gathers a 64-key K+V tile per (position, group, selected block):
-        # its bound is the cache hierarchy's gather bandwidth, reported beside the MFMA figure
-        selected_gather={"bytes": gbytes, "gbs": gbytes / (stage_ms["selected"] * 1e-3) / 1e9},
+        # the selected branch is bound by HBM: its counted bytes over the stage's time
+        selected_traffic=selected_traffic(stage_ms["selected"]),
         blocks_per_row=blocks_per_row,
     )
     del d, out, idx, ws
@@ -985,8 +989,7 @@ def main():
                     "algorithmic_tflop": round(pre["algorithmic_tflop"], 4),
                     "instrumented_ms_per_step": round(pre["events_ms_per_step"], 4),
                     "stages": pre["stages"],
-                    "selected_gather": {"bytes": pre["selected_gather"]["bytes"],
-                                        "gbs": round(pre["selected_gather"]["gbs"], 1)},
+                    "selected_traffic": pre["selected_traffic"],
                     "blocks_per_row": round(pre["blocks_per_row"], 3),
                     "longest_stage": pre["longest_stage"],
                     "cmp_select_performed": {k: round(v, 4) for k, v in

@@ -104,7 +104,7 @@ __device__ __forceinline__ int lanes_below(uint64_t m, int lane) {
 
 constexpr int kSlcCountThreads = 1024;
 
-// Per (T-chunk, group, sequence): one wave per position lists its free tiles (their rank among
+// Per (T-chunk, group, sequence): the free tiles of every position are listed (their rank among
 // the row's free tiles is the slot fs); every entry's rank among the chunk's entries of its key
 // tile comes from LDS counters (no global atomics), the counts per key tile are written out.
 // A wave takes the kSelWaves positions that share one workgroup of the position-major kernel

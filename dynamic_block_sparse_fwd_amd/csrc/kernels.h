@@ -54,7 +54,7 @@ struct PrefillArgs {
 
 constexpr int kNormRows = 256;  // compressed-key rows per chunk of the norm maxima
 constexpr int kSlcChunks = 16;  // most T-chunks of the block-major lists (work tiles chunk-major)
-constexpr int kSlcRows = 32;    // positions per block-major work tile
+constexpr int kSlcRows = 64;    // positions per block-major work tile
 // T-chunks of the lists for nq query rows, ntk key tiles and `per` selected tiles per row: as
 // many as keep a sub-list about one work tile long (nq per / (ntk kSlcRows) entries in all per
 // key tile), a multiple of 4 in [4, kSlcChunks]

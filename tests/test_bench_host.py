@@ -1,5 +1,6 @@
 """Host logic of bench.py, on the CPU: the work counts that its rates divide by, checked against
-the key sets the oracle actually attends over, and the one-GPU rule."""
+the key sets the oracle actually attends over, the one-GPU rule, the counter-traffic and
+commit records and when they are reported."""
 import os
 import subprocess
 import sys
@@ -65,3 +66,49 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_traffic_is_reported_only_for_the_sources_it_was_measured_on(tmp_path, monkeypatch):
+    """measured_traffic scales the committed counters by the copy calibration while the
+    kernel's source digest matches, and reports nothing once it does not; the selected stage's
+    rate follows the same rule."""
+    import json
+
+    tr = {"copy_calibration": {"fetch_counter_bytes_per_byte": 0.5,
+                               "write_counter_bytes_per_byte": 1.0},
+          "kernels": {k: {"fetch_kib_per_dispatch": 1000.0, "write_kib_per_dispatch": 500.0,
+                          "source_sha256": bench.source_digest(k)}
+                      for k in ("slc_block_kernel", "selected_kernel")}}
+    path = tmp_path / "traffic.json"
+    path.write_text(json.dumps(tr))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
+    expect = int(round(1000.0 * 1024 / 0.5 + 500.0 * 1024))
+    assert bench.measured_traffic("slc_block_kernel") == expect
+    sel = bench.selected_traffic(2.0)
+    assert sel["bytes"] == 2 * expect
+    assert abs(sel["gbs"] - 2 * expect / 2e-3 / 1e9) < 0.1
+    tr["kernels"]["selected_kernel"]["source_sha256"] = "0" * 64
+    path.write_text(json.dumps(tr))
+    assert bench.measured_traffic("selected_kernel") is None
+    assert bench.selected_traffic(2.0)["bytes"] is None
+
+
+def test_host_info_names_the_commit_from_the_build_record(tmp_path, monkeypatch):
+    """Outside a git checkout the bench takes the commit from the record the build wrote beside
+    the library, and only while the record's source digest equals the sources'."""
+    import json
+    import shutil
+
+    pkg = tmp_path / "dynamic_block_sparse_fwd_amd"
+    shutil.copytree(bench.CSRC, pkg / "csrc")
+    digest = bench.host_info()["library_source_sha256"]
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))  # no .git there
+    monkeypatch.setattr(bench, "CSRC", str(pkg / "csrc"))
+    rec = pkg / "libnsa.buildinfo.json"
+    rec.write_text(json.dumps({"git_sha": "abc123", "csrc_modified_since_commit": False,
+                               "library_source_sha256": digest}))
+    info = bench.host_info()
+    assert info["git_sha"] == "abc123" and info["git_sha_source"] == "build record"
+    rec.write_text(json.dumps({"git_sha": "abc123", "csrc_modified_since_commit": False,
+                               "library_source_sha256": "stale"}))
+    assert bench.host_info()["git_sha"] is None

@@ -18,7 +18,8 @@
 //                      written out) and take the other selected blocks' tiles; tiles dealt out
 //                      over the waves of each kind; per branch one partial record per
 //                      workgroup
-//   dec_merge_kernel   per group: the records merged in workgroup order, and the gate
+//   dec_merge_kernel   per group (over four workgroups): the records merged in workgroup order,
+//                      and the gate
 // Tile work is assigned in a fixed order and every sum runs in a fixed order, so the output is
 // the same bit for bit on every call.
 #include "attn_tile.h"
@@ -993,15 +994,19 @@ __global__ __launch_bounds__(kTileThreads) void dec_tiles_kernel(DecodeArgs a) {
 // the gate: out = g0 o_cmp + g1 o_slc + g2 o_win (o_cmp normalised by the selection slices).
 // Every thread issues its loads of the records' outputs, the compressed output and the gates
 // first; meanwhile threads 0..31 turn the records' maxima and sums into per-(branch, head)
-// weights.
+// weights.  A group's (head, feature) outputs are split over kMergeSplit workgroups (each
+// computes the weights itself), so that a small batch still spreads its merge over the GPU.
 constexpr int kMergeMaxNG = 8;
+constexpr int kMergeSplit = 4;
 
 template <int D>
 __global__ __launch_bounds__(256) void dec_merge_kernel(DecodeArgs a) {
   constexpr int RS = 32 + 16 * D;  // floats of one record
-  constexpr int PT = 16 * D / 256;  // (head, feature) pairs per thread
+  constexpr int PW = 16 * D / kMergeSplit;  // (head, feature) pairs per workgroup
+  constexpr int PT = PW / 256;               // ... per thread
+  static_assert(PT * 256 * kMergeSplit == 16 * D, "pairs must split evenly");
   __shared__ float W[2][16][kMergeMaxNG];  // weight of record g relative to the common max, / L
-  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int kvh = blockIdx.x, b = blockIdx.y, p0 = blockIdx.z * PW;
   const long bkv = (long)b * a.Hkv + kvh;
   const float* recs = a.grec + bkv * a.NG * 2 * RS;
   const int tid = threadIdx.x;
@@ -1009,7 +1014,7 @@ __global__ __launch_bounds__(256) void dec_merge_kernel(DecodeArgs a) {
   float oc[PT], g3[PT][3];
 #pragma unroll
   for (int q = 0; q < PT; ++q) {
-    const int pr = tid + 256 * q, h = pr / D, dd = pr % D;
+    const int pr = p0 + tid + 256 * q, h = pr / D, dd = pr % D;
     const int hc = h < a.G ? h : 0;  // rows past G read head 0 (in bounds) and write nothing
     const long head = (long)b * a.Hkv * a.G + kvh * a.G + hc;
     oc[q] = a.ocmp[(bkv * 16 + h) * D + dd];
@@ -1024,7 +1029,8 @@ __global__ __launch_bounds__(256) void dec_merge_kernel(DecodeArgs a) {
 #pragma unroll
     for (int br = 0; br < 2; ++br)
 #pragma unroll
-      for (int q = 0; q < PT; ++q) ro[g][br][q] = recs[(g * 2 + br) * RS + 32 + tid + 256 * q];
+      for (int q = 0; q < PT; ++q)
+        ro[g][br][q] = recs[(g * 2 + br) * RS + 32 + p0 + tid + 256 * q];
   }
   if (tid < 32) {
     const int br = tid >> 4, h = tid & 15;
@@ -1056,14 +1062,14 @@ __global__ __launch_bounds__(256) void dec_merge_kernel(DecodeArgs a) {
     for (int br = 0; br < 2; ++br) {
 #pragma unroll
       for (int q = 0; q < PT; ++q) {
-        const int pr = tid + 256 * q, h = pr / D;
+        const int pr = p0 + tid + 256 * q, h = pr / D;
         acc[q][br] += W[br][h][g] * ro[g][br][q];
       }
     }
   }
 #pragma unroll
   for (int q = 0; q < PT; ++q) {
-    const int pr = tid + 256 * q, h = pr / D, dd = pr % D;
+    const int pr = p0 + tid + 256 * q, h = pr / D, dd = pr % D;
     if (h >= a.G) continue;
     const long head = (long)b * a.Hkv * a.G + kvh * a.G + h;
     a.out[head * D + dd] = g3[q][0] * oc[q] + g3[q][1] * acc[q][0] + g3[q][2] * acc[q][1];
@@ -1103,7 +1109,7 @@ static void launch_decode_t(const DecodeArgs& a, hipStream_t s, hipEvent_t* ev) 
   mark(2);
   dec_tiles_kernel<D><<<dim3(a.NG, a.Hkv, a.B), kTileThreads, lds, s>>>(a);
   mark(3);
-  dec_merge_kernel<D><<<dim3(a.Hkv, a.B), 256, 0, s>>>(a);
+  dec_merge_kernel<D><<<dim3(a.Hkv, a.B, kMergeSplit), 256, 0, s>>>(a);
   mark(4);
 }
 

@@ -608,8 +608,9 @@ int nsa_cache_append(const nsa_config* c, int32_t C, const void* k_new, const vo
     uint16_t* wkt = reinterpret_cast<uint16_t*>(base);
     uint16_t* wvt = reinterpret_cast<uint16_t*>(base + align_up((size_t)LD * c->D * 2));
     float* part = reinterpret_cast<float*>(base + 2 * align_up((size_t)LD * c->D * 2));
-    launch_transpose(static_cast<const uint16_t*>(wk), wkt, 1, LD, c->D, LD, stream);
-    launch_transpose(static_cast<const uint16_t*>(wv), wvt, 1, LD, c->D, LD, stream);
+    launch_append_weights(static_cast<const uint16_t*>(wk), static_cast<const uint16_t*>(wv),
+                          wkt, wvt, LD, c->D, seqlens, c->B, C, c->cmp_len, c->cmp_stride, ncap,
+                          stream);
     const uint16_t* xs[2] = {kc16, vc16};
     const uint16_t* wts[2] = {wkt, wvt};
     uint16_t* xcs[2] = {static_cast<uint16_t*>(kcmp), nullptr};
@@ -620,8 +621,9 @@ int nsa_cache_append(const nsa_config* c, int32_t C, const void* k_new, const vo
   } else if (ncap > 0) {
     uint16_t* wkt = static_cast<uint16_t*>(ws);
     uint16_t* wvt = wkt + align_up((size_t)LD * c->D * 2) / 2;
-    launch_transpose(static_cast<const uint16_t*>(wk), wkt, 1, LD, c->D, LD, stream);
-    launch_transpose(static_cast<const uint16_t*>(wv), wvt, 1, LD, c->D, LD, stream);
+    launch_append_weights(static_cast<const uint16_t*>(wk), static_cast<const uint16_t*>(wv),
+                          wkt, wvt, LD, c->D, seqlens, c->B, C, c->cmp_len, c->cmp_stride, ncap,
+                          stream);
     // keys (row-major) and values (tiles) in one launch
     launch_compress(kc16, wkt, static_cast<uint16_t*>(kcmp), nullptr, BH, c->T, c->D,
                     c->cmp_len, c->cmp_stride, ncap, ncap, 64 * ((ncap + 63) / 64), true, stream,

@@ -197,6 +197,13 @@ void launch_fill_zero(float* p, size_t n, hipStream_t s);
 void launch_transpose(const uint16_t* x, uint16_t* xt, int BH, int rows, int cols, int rows_pad,
                       hipStream_t s, int ld_rows = -1);
 
+// The compressor weights wk, wv [rows = l*D, cols = D] -> wkt, wvt [cols, rows] in one launch,
+// skipped (every workgroup returns) when an append of C tokens at seqlens [B] completes no
+// compressed token below the capacity ncap.
+void launch_append_weights(const uint16_t* wk, const uint16_t* wv, uint16_t* wkt, uint16_t* wvt,
+                           int rows, int cols, const int32_t* seqlens, int B, int C, int l,
+                           int d, int ncap, hipStream_t s);
+
 // Compressed tokens of x [BH, T, D] with the transposed weight wt [D, l*D]:
 //   xc  (nullable) [BH, rows_alloc, D] row-major, rows n_cmp..rows_alloc-1 zero;
 //   xct (nullable) [BH, D, ncp] transposed, or with `tiled` [BH, ncp / 64, D, 64] (64-token

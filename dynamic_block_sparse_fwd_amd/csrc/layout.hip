@@ -11,12 +11,11 @@ namespace nsa {
 // `rows` are written as zero.
 constexpr int kTP = 72;  // LDS row pitch in bf16 (16-byte aligned rows)
 
-__global__ __launch_bounds__(256) void transpose_kernel(const u16* __restrict__ x,
-                                                        u16* __restrict__ xt, int rows,
-                                                        int cols, int rows_pad, int ld_rows) {
-  __shared__ __align__(16) u16 tile[64][kTP];
-  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  const long bh = blockIdx.z;
+// One 64 x 64 tile of x [bh][rows][cols] (row pitch `cols`, ld_rows rows per bh) into
+// xt [bh][cols][rows_pad], rows past `rows` as zeros; 256 threads, through LDS.
+__device__ __forceinline__ void transpose_tile(const u16* __restrict__ x, u16* __restrict__ xt,
+                                               int rows, int cols, int rows_pad, int ld_rows,
+                                               long bh, int r0, int c0, u16 (*tile)[kTP]) {
   const int tid = threadIdx.x;
   const int ch = tid & 7;
 #pragma unroll
@@ -38,6 +37,45 @@ __global__ __launch_bounds__(256) void transpose_kernel(const u16* __restrict__ 
     *reinterpret_cast<u32x4*>(xt + (bh * cols + c0 + c) * rows_pad + r0 + 8 * ch) =
         u32x4{w[0], w[1], w[2], w[3]};
   }
+}
+
+__global__ __launch_bounds__(256) void transpose_kernel(const u16* __restrict__ x,
+                                                        u16* __restrict__ xt, int rows,
+                                                        int cols, int rows_pad, int ld_rows) {
+  __shared__ __align__(16) u16 tile[64][kTP];
+  transpose_tile(x, xt, rows, cols, rows_pad, ld_rows, blockIdx.z, blockIdx.x * 64,
+                 blockIdx.y * 64, tile);
+}
+
+// The two compressor weights [l*D, D] transposed in one launch (blockIdx.z: keys, values) for
+// an append of C tokens per sequence at the device-side lengths `seqlens`; when no sequence
+// completes a compressed token (15 of 16 single-token steps) nothing reads them, and every
+// workgroup leaves at once.
+__global__ __launch_bounds__(256) void append_weights_kernel(
+    const u16* __restrict__ wk, const u16* __restrict__ wv, u16* __restrict__ wkt,
+    u16* __restrict__ wvt, int rows, int cols, const int32_t* __restrict__ seqlens, int B, int C,
+    int l, int d, int ncap) {
+  __shared__ __align__(16) u16 tile[64][kTP];
+  int any = 0;
+  for (int b = threadIdx.x; b < B; b += 256) {
+    const int s0 = seqlens[b], s1 = s0 + C;
+    int n0 = s0 >= l ? (s0 - l) / d + 1 : 0, n1 = s1 >= l ? (s1 - l) / d + 1 : 0;
+    n0 = n0 < ncap ? n0 : ncap;
+    n1 = n1 < ncap ? n1 : ncap;
+    any |= n1 > n0;
+  }
+  if (!__syncthreads_or(any)) return;  // uniform
+  const bool v = blockIdx.z == 1;
+  transpose_tile(v ? wv : wk, v ? wvt : wkt, rows, cols, rows, rows, 0, blockIdx.x * 64,
+                 blockIdx.y * 64, tile);
+}
+
+void launch_append_weights(const uint16_t* wk, const uint16_t* wv, uint16_t* wkt, uint16_t* wvt,
+                           int rows, int cols, const int32_t* seqlens, int B, int C, int l,
+                           int d, int ncap, hipStream_t s) {
+  append_weights_kernel<<<dim3(rows / 64, cols / 64, 2), 256, 0, s>>>(wk, wv, wkt, wvt, rows,
+                                                                        cols, seqlens, B, C, l,
+                                                                        d, ncap);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float4* __restrict__ p, long n4) {

@@ -398,6 +398,8 @@ __global__ __launch_bounds__(256) void compress_kernel(const u16* __restrict__ x
 // n_cmp(seqlens[b] + C).  The l*D reduction is split in `ks`-long pieces over blockIdx.y, each
 // writing fp32 partials part[split][slot][D]; compress_finish_kernel sums them in split order
 // and rounds like compress_kernel.  blockIdx.z: 0 keys, 1 values.
+constexpr int kFewMaxSplits = 16;  // splits of the l*D reduction: few_splits gives at most 16
+
 struct FewArgs {
   const u16* x[2];   // caches [BH, T, D]
   const u16* wt[2];  // transposed weights [D, l*D]
@@ -450,17 +452,35 @@ __global__ __launch_bounds__(256) void compress_split_kernel(FewArgs a) {
   for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
     for (int it = 0; it < 4; ++it) acc[ct][it] = zero4();
-  for (int k0 = k_lo; k0 < k_hi; k0 += 32) {
-    const int ko = k0 + 8 * g4;
-    bf16x8 bx[4], aw[CT];
+  // eight 32-wide k-steps at a time, their loads issued together (a split is a short chain of
+  // steps, each with little to compute: one round trip per eight steps instead of per step)
+  constexpr int KS = 8;
+  for (int kb = k_lo; kb < k_hi; kb += KS * 32) {
+    bf16x8 bx[KS][4], aw[KS][CT];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) bx[it] = load8(xb + xrow[it] + ko);
+    for (int st = 0; st < KS; ++st) {
+      // past the split's end: an in-bounds load of its first step, its weight taken as zero
+      // (the products are then exact zeros and the sums unchanged; no branch, so the loads of
+      // all KS steps stay ahead of the products)
+      const bool in = kb + 32 * st < k_hi;
+      const int ko = (in ? kb + 32 * st : k_lo) + 8 * g4;
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) aw[ct] = load8(wrow[ct] + ko);
+      for (int it = 0; it < 4; ++it) bx[st][it] = load8(xb + xrow[it] + ko);
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+      for (int ct = 0; ct < CT; ++ct) {
+        const bf16x8 w = load8(wrow[ct] + ko);
+        aw[st][ct] = in ? w : zero8();
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the scheduler keeps every load above the products
 #pragma unroll
-      for (int it = 0; it < 4; ++it) acc[ct][it] = mfma16x16x32(aw[ct], bx[it], acc[ct][it]);
+    for (int st = 0; st < KS; ++st) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+          acc[ct][it] = mfma16x16x32(aw[st][ct], bx[st][it], acc[ct][it]);
+    }
   }
   // lane holds C^T[c = base + 4*g4 + e][slot = g0 + it*16 + r16]
   float* pb = a.part + ((long)(kv * a.nsplit + sp) * a.nslots) * D;
@@ -489,8 +509,15 @@ __global__ __launch_bounds__(256) void compress_finish_kernel(FewArgs a) {
   const int i = few_token(a, slot, &bh);
   if (i < 0) return;  // uniform per wave
   const float* pb = a.part + ((long)kv * a.nsplit * a.nslots + slot) * D + c;
+  // every split's partial loaded at once (at most kFewMaxSplits), then summed in split order
+  float pv[kFewMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < kFewMaxSplits; ++sp)
+    pv[sp] = pb[(long)(sp < a.nsplit ? sp : a.nsplit - 1) * a.nslots * D];
   float v = 0.f;
-  for (int sp = 0; sp < a.nsplit; ++sp) v += pb[(long)sp * a.nslots * D];
+#pragma unroll
+  for (int sp = 0; sp < kFewMaxSplits; ++sp)
+    if (sp < a.nsplit) v += pv[sp];
   const int K = a.l * D;
   const u16* xp = a.x[kv] + ((long)bh * a.T + (long)i * a.d) * D;
   const float mid = __uint_as_float((__float_as_uint(v) & 0xFFFF0000u) | 0x8000u);
@@ -508,7 +535,7 @@ __global__ __launch_bounds__(256) void compress_finish_kernel(FewArgs a) {
     a.xct[kv][(((long)bh * (a.ncp >> 6) + (i >> 6)) * D + c) * 64 + (i & 63)] = h;
 }
 
-int few_splits(int K, int* ks) {
+int few_splits(int K, int* ks) {  // at most kFewMaxSplits
   int k = (K + 15) / 16;
   k = (k + 31) / 32 * 32;
   *ks = k;

@@ -80,13 +80,13 @@ __device__ __forceinline__ LaneTile lane_tile(const PrefillArgs& a, int lane) {
   return LaneTile{lane / per, lane % per, lane < a.top_n * per};
 }
 
-// The lane's tile key of position t, whose index row is `row` (as sel_tile_key), if it is not
-// one of the tiles `sh` shared by t's workgroup of the position-major kernel, else -1.
-__device__ __forceinline__ int free_tile_key(const PrefillArgs& a, const int32_t* row, int t,
+// The lane's tile key of position t, given the block j its index row holds in the lane's slot
+// (as sel_tile_key), if it is not one of the tiles `sh` shared by t's workgroup of the
+// position-major kernel, else -1.
+__device__ __forceinline__ int free_tile_key(const PrefillArgs& a, int j, int t,
                                              const LaneTile& lt, const SelShared& sh) {
   int k0 = -1;
   if (lt.on) {
-    const int j = row[lt.slot];
     const int kk = j * a.beta + 64 * lt.sub;
     if (j >= 0 && j < a.nblk && kk <= t) k0 = kk;
   }
@@ -130,11 +130,21 @@ __global__ __launch_bounds__(kSlcCountThreads) void slc_count_kernel(PrefillArgs
     const SelShared sh = sel_shared(a, a.q0 + rg);
     const int32_t* irow = a.idx + (prow(a, b, a.q0 + rg) * a.Hkv + kvh) * a.top_n;
     const long sbase = (((long)b * a.nq + rg) * a.Hkv + kvh) * a.FS;
+    // the U index loads unconditional (rows outside [r0, r1) clamped into it, lanes past the
+    // row's slots at slot 0) and issued together before any of them is used
+    int jv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int r = rg + u;
+      r = r < r0 ? r0 : (r < r1 ? r : r1 - 1);
+      jv[u] = irow[(r - rg) * si + (lt.on ? lt.slot : 0)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     int k0[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int r = rg + u;
-      k0[u] = r >= r0 && r < r1 ? free_tile_key(a, irow + u * si, a.q0 + r, lt, sh) : -1;
+      k0[u] = r >= r0 && r < r1 ? free_tile_key(a, jv[u], a.q0 + r, lt, sh) : -1;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {

@@ -1025,27 +1025,34 @@ __global__ __launch_bounds__(256) void dec_merge_kernel(DecodeArgs a) {
   float ro[kMergeMaxNG][2][PT];
 #pragma unroll
   for (int g = 0; g < kMergeMaxNG; ++g) {
-    if (g >= a.NG) break;  // uniform
+    const int gc = g < a.NG ? g : a.NG - 1;  // unconditional loads: the record index clamped
 #pragma unroll
     for (int br = 0; br < 2; ++br)
 #pragma unroll
       for (int q = 0; q < PT; ++q)
-        ro[g][br][q] = recs[(g * 2 + br) * RS + 32 + p0 + tid + 256 * q];
+        ro[g][br][q] = recs[(gc * 2 + br) * RS + 32 + p0 + tid + 256 * q];
   }
   if (tid < 32) {
     const int br = tid >> 4, h = tid & 15;
-    float m[kMergeMaxNG];
+    // every record's maximum and sum loaded unconditionally (record index clamped), together
+    float m[kMergeMaxNG], sm[kMergeMaxNG];
+#pragma unroll
+    for (int g = 0; g < kMergeMaxNG; ++g) {
+      const float* rg = recs + ((g < a.NG ? g : a.NG - 1) * 2 + br) * RS;
+      m[g] = rg[h];
+      sm[g] = rg[16 + h];
+    }
     float M = kNegInf;
 #pragma unroll
     for (int g = 0; g < kMergeMaxNG; ++g) {
-      m[g] = g < a.NG ? recs[(g * 2 + br) * RS + h] : kNegInf;
+      m[g] = g < a.NG ? m[g] : kNegInf;
       M = fmaxf(M, m[g]);
     }
     float L = 0.f, w[kMergeMaxNG];
 #pragma unroll
     for (int g = 0; g < kMergeMaxNG; ++g) {
       w[g] = m[g] == kNegInf ? 0.f : fast_exp2(m[g] - M);
-      L += g < a.NG ? w[g] * recs[(g * 2 + br) * RS + 16 + h] : 0.f;
+      L += g < a.NG ? w[g] * sm[g] : 0.f;
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll

@@ -410,6 +410,15 @@ struct FewArgs {
   int T, l, d, ncmp, rows_alloc, ncp, C, Hkv, per, nslots, ks, nsplit;
 };
 
+// Token of `slot` given its sequence's length s0 before the append (-1 when dead).
+__device__ __forceinline__ int few_token_at(const FewArgs& a, int slot, int s0) {
+  const int q = slot % a.per, s1 = s0 + a.C;
+  const int ilo = s0 >= a.l ? (s0 - a.l) / a.d + 1 : 0;
+  int ihi = s1 >= a.l ? (s1 - a.l) / a.d + 1 : 0;
+  ihi = ihi < a.ncmp ? ihi : a.ncmp;
+  return ilo + q < ihi ? ilo + q : -1;
+}
+
 __device__ __forceinline__ int few_token(const FewArgs& a, int slot, int* bh_out) {
   const int bh = slot / a.per, q = slot % a.per;
   const int s0 = a.seqlens[bh / a.Hkv], s1 = s0 + a.C;
@@ -431,16 +440,24 @@ __global__ __launch_bounds__(256) void compress_split_kernel(FewArgs a) {
   const int k_lo = sp * a.ks, k_hi = k_lo + a.ks < K ? k_lo + a.ks : K;
   {  // every wave finds the same answer: a workgroup whose 64 slots are all dead leaves
     int bh;
-    const bool live = g0 + lane < a.nslots && few_token(a, g0 + lane, &bh) >= 0;
+    const int sl = g0 + lane < a.nslots ? g0 + lane : a.nslots - 1;
+    const bool live = g0 + lane < a.nslots && few_token(a, sl, &bh) >= 0;
     if (__ballot(live) == 0ull) return;
   }
   long xrow[4];
+  int s0v[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {  // the four length loads in flight together (slot clamped)
+    const int slot = g0 + it * 16 + r16, sc = slot < a.nslots ? slot : a.nslots - 1;
+    s0v[it] = a.seqlens[(sc / a.per) / a.Hkv];
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int slot = g0 + it * 16 + r16;
-    int bh = 0, i = -1;
-    if (slot < a.nslots) i = few_token(a, slot, &bh);
-    if (i < 0) { bh = 0; i = 0; }  // dead slot: reads tokens 0 .. l-1 of head 0, discarded
+    const int slot = g0 + it * 16 + r16, sc = slot < a.nslots ? slot : a.nslots - 1;
+    int bh = sc / a.per;
+    int i = few_token_at(a, sc, s0v[it]);
+    if (slot >= a.nslots || i < 0) { bh = 0; i = 0; }  // dead: tokens 0 .. l-1 of head 0, discarded
     xrow[it] = ((long)bh * a.T + (long)i * a.d) * D;
   }
   const u16* xb = a.x[kv];

@@ -396,23 +396,39 @@ __global__ __launch_bounds__(1024) void moba_scan_kernel(MobaArgs a) {
 }
 
 // Places every (query, slot) at its block's list offset + its chunk's offset in the list + its
-// rank among the chunk's queries.
+// rank among the chunk's queries.  KS >= top_k slots per row: the row's block indices are
+// loaded together, then every slot's offset, chunk offset and rank together (indices clamped
+// into range, so no load waits behind a per-slot condition); only the stores are conditional.
+template <int KS>
 __global__ __launch_bounds__(256) void moba_fill_kernel(MobaArgs a) {
   const long row = (long)blockIdx.x * 256 + threadIdx.x;  // (b, t, h)
-  if (row >= (long)a.B * a.T * a.H) return;
+  if (row >= (long)a.B * a.T * a.H || a.nb == 0) return;  // nb = 0: no query selects a block
   const int h = (int)(row % a.H);
   const long bt = row / a.H;
   const int t = (int)(bt % a.T), b = (int)(bt / a.T);
+  const int K = a.top_k, slast = K > 0 ? K - 1 : 0;
   const int bq = t / a.block;
-  const int nsel = bq < a.top_k ? bq : a.top_k;
+  const int nsel = bq < K ? bq : K;
   const int chunk = t / ((a.T + kMobaChunks - 1) / kMobaChunks);
   const long bh = (long)b * a.H + h;
-  const int32_t* irow = a.idx + moba_grow(a, b, t, h) * (a.top_k + 1);
-  for (int s = 0; s < nsel; ++s) {
-    const long e = bh * a.nb + irow[s];
-    a.list[a.offset[e] + a.count[e * kMobaChunks + chunk] + a.rank[row * a.top_k + s]] =
-        (t << 4) | s;
+  const int32_t* irow = a.idx + moba_grow(a, b, t, h) * (K + 1);  // K + 1 entries
+  int jb[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int v = irow[s < K ? s : K];
+    jb[s] = v < 0 ? 0 : (v < a.nb ? v : a.nb - 1);
   }
+  int off[KS], cnt[KS], rk[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const long e = bh * a.nb + jb[s];
+    off[s] = a.offset[e];
+    cnt[s] = a.count[e * kMobaChunks + chunk];
+    rk[s] = a.rank[row * K + (s < slast ? s : slast)];  // K = 0: the spare slot 0
+  }
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    if (s < nsel) a.list[off[s] + cnt[s] + rk[s]] = (t << 4) | s;
 }
 
 template <int D>
@@ -723,7 +739,7 @@ static void launch_moba_k(const MobaArgs& a, hipStream_t s, hipEvent_t* ev) {
   moba_count_kernel<KS><<<dim3(kMobaChunks, a.H * nr, a.B), kCountThreads,
                           (size_t)cblk * sizeof(int), s>>>(a);
   moba_scan_kernel<<<1, 1024, 0, s>>>(a);
-  moba_fill_kernel<<<(int)((rows + 255) / 256), 256, 0, s>>>(a);
+  moba_fill_kernel<KS><<<(int)((rows + 255) / 256), 256, 0, s>>>(a);
   mark(2);
   if (a.max_tiles > 0) moba_block_kernel<D><<<(a.max_tiles + 7) / 8 * 8, 256, 0, s>>>(a);
   mark(3);

@@ -340,58 +340,86 @@ __global__ __launch_bounds__(kCountThreads) void moba_count_kernel(MobaArgs a) {
     a.count[(bh * a.nb + jlo + j) * kMobaChunks + chunk] = cnt[j];
 }
 
-// Exclusive prefix sums of the list lengths and of their 128-row tile counts (one workgroup);
-// each list's chunk counts become the chunk offsets inside the list, and every tile records
-// its list.
-__device__ __forceinline__ int list_len(const MobaArgs& a, int e) {
-  int v = 0;
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int moba_wave_scan(int v, int lane) {
 #pragma unroll
-  for (int c = 0; c < kMobaChunks; ++c) v += a.count[(long)e * kMobaChunks + c];
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    v += lane >= o ? u : 0;
+  }
   return v;
 }
 
+// Exclusive prefix sums of the list lengths and of their 128-row tile counts (one workgroup);
+// each list's chunk counts become the chunk offsets inside the list, and every tile records
+// its list.  1024 consecutive lists per step, one per thread (its kMobaChunks counts in two
+// 16-byte loads), each step's sums scanned over the waves and added to the running totals of
+// the steps before; the next step's counts are loaded during this one.
 __global__ __launch_bounds__(1024) void moba_scan_kernel(MobaArgs a) {
-  __shared__ int sc[1024], st[1024];
-  const int n = a.B * a.H * a.nb;
-  const int per = (n + 1023) / 1024;
-  const int lo = threadIdx.x * per, hi = lo + per < n ? lo + per : n;
-  int c = 0, tl = 0;
-  for (int e = lo; e < hi; ++e) {
-    const int v = list_len(a, e);
-    c += v;
-    tl += (v + MOBA_ROWS - 1) / MOBA_ROWS;
-  }
-  sc[threadIdx.x] = c;
-  st[threadIdx.x] = tl;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int vc = threadIdx.x >= o ? sc[threadIdx.x - o] : 0;
-    const int vt = threadIdx.x >= o ? st[threadIdx.x - o] : 0;
-    __syncthreads();
-    sc[threadIdx.x] += vc;
-    st[threadIdx.x] += vt;
-    __syncthreads();
-  }
-  int co = sc[threadIdx.x] - c, to = st[threadIdx.x] - tl;  // exclusive
-  for (int e = lo; e < hi; ++e) {
-    int run = 0;
-#pragma unroll
-    for (int ch = 0; ch < kMobaChunks; ++ch) {
-      int32_t* cc = a.count + (long)e * kMobaChunks + ch;
-      const int v = *cc;
-      *cc = run;
-      run += v;
+  static_assert(kMobaChunks == 8, "a list's chunk counts are two 16-byte loads");
+  __shared__ int wc[16], wt[16];
+  __shared__ int carry_c, carry_t;
+  const long n = (long)a.B * a.H * a.nb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (n == 0) {  // no lists (T < block)
+    if (tid == 0) {
+      a.ntiles[0] = 0;
+      a.offset[0] = 0;
     }
-    a.offset[e] = co;
-    a.tstart[e] = to;
-    const int nt = (run + MOBA_ROWS - 1) / MOBA_ROWS;
-    for (int k = 0; k < nt; ++k) a.tile_entry[to + k] = e;
-    co += run;
-    to += nt;
+    return;
   }
-  if (threadIdx.x == 1023) {
-    a.ntiles[0] = st[1023];
-    a.offset[n] = sc[1023];  // end of the last list
+  int4* cnt4 = reinterpret_cast<int4*>(a.count);  // list e: cnt4[2 e], cnt4[2 e + 1]
+  if (tid == 0) {
+    carry_c = 0;
+    carry_t = 0;
+  }
+  const long e0 = tid < n ? tid : n - 1;  // every load unconditional (index clamped)
+  int4 n0 = cnt4[2 * e0], n1 = cnt4[2 * e0 + 1];
+  for (long base = 0; base < n; base += 1024) {
+    const long e = base + tid;
+    const bool live = e < n;
+    const int4 c0 = n0, c1 = n1;
+    const long en = base + 1024 + tid < n ? base + 1024 + tid : n - 1;
+    n0 = cnt4[2 * en];
+    n1 = cnt4[2 * en + 1];
+    const int v[kMobaChunks] = {live ? c0.x : 0, live ? c0.y : 0, live ? c0.z : 0,
+                                live ? c0.w : 0, live ? c1.x : 0, live ? c1.y : 0,
+                                live ? c1.z : 0, live ? c1.w : 0};
+    int r[kMobaChunks], sv = 0;
+#pragma unroll
+    for (int c = 0; c < kMobaChunks; ++c) {
+      r[c] = sv;
+      sv += v[c];
+    }
+    const int nt = (sv + MOBA_ROWS - 1) / MOBA_ROWS;
+    const int ic = moba_wave_scan(sv, lane), it = moba_wave_scan(nt, lane);
+    if (lane == 63) {
+      wc[wave] = ic;
+      wt[wave] = it;
+    }
+    __syncthreads();  // the wave totals (and the carries of the step before) are posted
+    int co = carry_c + ic - sv, to = carry_t + it - nt;  // exclusive
+    for (int w = 0; w < wave; ++w) {
+      co += wc[w];
+      to += wt[w];
+    }
+    if (live) {
+      cnt4[2 * e] = int4{r[0], r[1], r[2], r[3]};
+      cnt4[2 * e + 1] = int4{r[4], r[5], r[6], r[7]};
+      a.offset[e] = co;
+      a.tstart[e] = to;
+      for (int k = 0; k < nt; ++k) a.tile_entry[to + k] = (int)e;
+    }
+    __syncthreads();  // every thread has read wc, wt and the carries
+    if (tid == 1023) {  // its inclusive sums close the step (0 past the end)
+      carry_c = co + sv;
+      carry_t = to + nt;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    a.ntiles[0] = carry_t;
+    a.offset[n] = carry_c;  // end of the last list
   }
 }
 

@@ -171,7 +171,7 @@ struct MobaArgs {
   uint16_t* kb_lo;     // [B*H, nb, D] bf16 of the remainder
   int32_t* count;      // [B*H*nb, kMobaChunks] queries of each T-chunk that chose each block,
                        // turned into chunk offsets inside the block's list by the scan
-  int32_t* rank;       // [B*T*H, top_k] position of each (query, slot) in its block's list
+  int32_t* rank;       // [B*H*T, top_k] position of each (query, slot) in its block's list
   int32_t* offset;     // [B*H*nb + 1] list offsets (exclusive prefix of the list lengths)
   int32_t* tstart;     // [B*H*nb] first 128-row tile of each list
   int32_t* ntiles;     // [1] total tiles

@@ -328,11 +328,11 @@ __global__ __launch_bounds__(kCountThreads) void moba_count_kernel(MobaArgs a) {
       const int t = t0 + u * kCountThreads;
       const int bq = t / a.block;
       const int nsel = t < tend ? (bq < K ? bq : K) : 0;
-      const long row = ((long)b * a.T + t) * a.H + h;
+      const long rrow = bh * a.T + t;  // rank rows are head-major: the stores are contiguous
 #pragma unroll
       for (int s = 0; s < KS; ++s)
         if (s < nsel && jb[u][s] >= jlo && jb[u][s] < jhi)
-          a.rank[row * K + s] = atomicAdd(&cnt[jb[u][s] - jlo], 1);
+          a.rank[rrow * K + s] = atomicAdd(&cnt[jb[u][s] - jlo], 1);
     }
   }
   __syncthreads();
@@ -429,16 +429,17 @@ __global__ __launch_bounds__(1024) void moba_scan_kernel(MobaArgs a) {
 // into range, so no load waits behind a per-slot condition); only the stores are conditional.
 template <int KS>
 __global__ __launch_bounds__(256) void moba_fill_kernel(MobaArgs a) {
-  const long row = (long)blockIdx.x * 256 + threadIdx.x;  // (b, t, h)
-  if (row >= (long)a.B * a.T * a.H || a.nb == 0) return;  // nb = 0: no query selects a block
-  const int h = (int)(row % a.H);
-  const long bt = row / a.H;
-  const int t = (int)(bt % a.T), b = (int)(bt / a.T);
+  // (b, h, t), t fastest: a wave's rows share a head, so their ranks are contiguous and their
+  // entries of one block land close together in its list
+  const long row = (long)blockIdx.x * 256 + threadIdx.x;
+  if (row >= (long)a.B * a.H * a.T || a.nb == 0) return;  // nb = 0: no query selects a block
+  const int t = (int)(row % a.T);
+  const long bh = row / a.T;
+  const int h = (int)(bh % a.H), b = (int)(bh / a.H);
   const int K = a.top_k, slast = K > 0 ? K - 1 : 0;
   const int bq = t / a.block;
   const int nsel = bq < K ? bq : K;
   const int chunk = t / ((a.T + kMobaChunks - 1) / kMobaChunks);
-  const long bh = (long)b * a.H + h;
   const int32_t* irow = a.idx + moba_grow(a, b, t, h) * (K + 1);  // K + 1 entries
   int jb[KS];
 #pragma unroll
